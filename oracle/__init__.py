@@ -1,0 +1,119 @@
+"""Python entry to the float64 CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the library.  The wrappers only widen
+the stored input values to float64 and marshal pointers; all arithmetic is in
+``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11"]
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Oracle:
+    """ctypes binding of one build of ``oracle.c`` (the default build, or a
+    variant that a test compiles from edited source)."""
+
+    def __init__(self, libpath: str):
+        lib = ctypes.CDLL(libpath)
+        i64, dp = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_scan_f64.argtypes = [i64] * 5 + [dp] * 10
+        lib.oracle_scan_f64.restype = ctypes.c_int
+        lib.oracle_ssd_f64.argtypes = [i64] * 6 + [dp] * 10
+        lib.oracle_ssd_f64.restype = ctypes.c_int
+        self.lib = lib
+
+    def scan(self, u, delta, A, B, C, D=None, z=None, h0=None):
+        """Selective scan in float64. Returns (y, h_last) as float64 arrays.
+
+        u, delta, z: (batch, dim, L); B, C: (batch, G, N, L); A: (dim, N);
+        D: (dim,); h0: (batch, dim, N).
+        """
+        u, delta, A, B, C, D, z, h0 = map(f64, (u, delta, A, B, C, D, z, h0))
+        batch, dim, L = u.shape
+        G, N = B.shape[1], B.shape[2]
+        assert delta.shape == u.shape and A.shape == (dim, N) and C.shape == B.shape
+        assert B.shape == (batch, G, N, L)
+        assert z is None or z.shape == u.shape
+        assert h0 is None or h0.shape == (batch, dim, N)
+        y = np.zeros_like(u)
+        h = np.zeros((batch, dim, N))
+        rc = self.lib.oracle_scan_f64(batch, dim, N, L, G, _ptr(u), _ptr(delta), _ptr(A),
+                                      _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                      _ptr(y), _ptr(h))
+        if rc != 0:
+            raise ValueError("oracle_scan_f64 rejected the shapes")
+        return y, h
+
+    def ssd(self, x, dt, A, B, C, D=None, z=None, h0=None):
+        """Scalar-decay SSD recurrence in float64. Returns (y, h_last).
+
+        x, z: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N);
+        A, D: (H,); h0, h_last: (batch, H, P, N).
+        """
+        x, dt, A, B, C, D, z, h0 = map(f64, (x, dt, A, B, C, D, z, h0))
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (batch, L, H) and B.shape == (batch, L, G, N)
+        assert C.shape == B.shape and A.shape == (H,)
+        assert h0 is None or h0.shape == (batch, H, P, N)
+        y = np.zeros_like(x)
+        h = np.zeros((batch, H, P, N))
+        rc = self.lib.oracle_ssd_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A),
+                                     _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                                     _ptr(y), _ptr(h))
+        if rc != 0:
+            raise ValueError("oracle_ssd_f64 rejected the shapes")
+        return y, h
+
+
+def _load() -> Oracle:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = Oracle(_LIB)
+    return _lib
+
+
+def f64(a):
+    """Widen a stored tensor/array (f32, bf16 or f64) to a contiguous float64 array."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (bf16 has no numpy dtype)
+        import torch
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def scan(u, delta, A, B, C, D=None, z=None, h0=None):
+    """Selective scan in float64 with the default build; see ``Oracle.scan``."""
+    return _load().scan(u, delta, A, B, C, D, z, h0)
+
+
+def ssd(x, dt, A, B, C, D=None, z=None, h0=None):
+    """Scalar-decay SSD in float64 with the default build; see ``Oracle.ssd``."""
+    return _load().ssd(x, dt, A, B, C, D, z, h0)

@@ -1,0 +1,137 @@
+/*
+ * CPU oracle for the selective scan and its scalar-decay (SSD) variant.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may call this code.  It shares no source,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * Plain, slow, single-threaded, float64 throughout, libm exp.  Every loop is
+ * the definition written out; nothing is blocked, fused or reordered.
+ *
+ * What is computed (page titles and sections are those of the pages that
+ * define the method):
+ *   - "We brought Mamba to Trainium", section "Mamba: bringing an unsupported
+ *     model to the chip": the running state is updated every step,
+ *     h_t = Abar_t * h_{t-1} + Bbar_t * x_t, and read out as y_t = sum_n C_t h_t.
+ *   - "Mamba-3 NKI Kernels for AWS Neuron", section "How it works", Phase 0:
+ *     the decay is alpha = exp(dt * A); the input weight is gamma = lam * dt,
+ *     which is dt for the plain (lam = 1) form used here, so Bbar_t x_t is
+ *     dt_t * B_t * x_t.
+ *   - same page and section, Phase 5: the D skip is added, then the silu gate
+ *     is applied: y = (C.h + D x) * silu(z), silu(z) = z / (1 + exp(-z)).
+ *   - the state before the first step is h0 (zero when h0 is NULL); h_last is
+ *     the state after the last step, before the readout.
+ *
+ * Parity of this code is pinned by the CPU tests (closed forms, brute force,
+ * a hand-derived worked example, invariants); it is never compared with
+ * itself.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * Selective scan.
+ *   u, delta, z : (batch, dim, seqlen)          y    : (batch, dim, seqlen)
+ *   B, C        : (batch, ngroups, dstate, seqlen)
+ *   A           : (dim, dstate)                  Dskip: (dim)         (nullable)
+ *   h0, h_last  : (batch, dim, dstate)           (h0 and h_last nullable)
+ * Channel d reads group g = d / (dim / ngroups).
+ * Returns 0, or -1 on a bad shape.
+ */
+int oracle_scan_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                    int64_t ngroups, const double *u, const double *delta,
+                    const double *A, const double *B, const double *C,
+                    const double *Dskip, const double *z, const double *h0,
+                    double *y, double *h_last)
+{
+    if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0 || ngroups < 1 ||
+        dim % ngroups != 0 || dstate > 4096)
+        return -1;
+    double h[4096];
+    const int64_t dpg = dim / ngroups;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t g = d / dpg;
+            for (int64_t n = 0; n < dstate; ++n)
+                h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t i = (b * dim + d) * seqlen + t;
+                const double dl = delta[i];
+                const double x = u[i];
+                double acc = 0.0;
+                for (int64_t n = 0; n < dstate; ++n) {
+                    const int64_t j = ((b * ngroups + g) * dstate + n) * seqlen + t;
+                    const double abar = exp(dl * A[d * dstate + n]);
+                    h[n] = abar * h[n] + dl * B[j] * x;
+                    acc += C[j] * h[n];
+                }
+                if (Dskip) acc += Dskip[d] * x;
+                if (z) acc *= silu(z[i]);
+                y[i] = acc;
+            }
+            if (h_last)
+                for (int64_t n = 0; n < dstate; ++n)
+                    h_last[(b * dim + d) * dstate + n] = h[n];
+        }
+    }
+    return 0;
+}
+
+/*
+ * Scalar-decay (SSD) form: one decay per (batch, time, head), shared by the
+ * head's headdim x dstate states.  This is the recurrence the chunked SSD of
+ * "Mamba-3 NKI Kernels for AWS Neuron" (section "Kernel details",
+ * mamba3_siso_ssd_kernel, Mamba-2 structure) reaches, with the trapezoidal
+ * and rotary extras switched off.  It takes no chunk argument: chunking only
+ * reorganises the arithmetic.
+ *   x, z, y : (batch, seqlen, nheads, headdim)   dt : (batch, seqlen, nheads)
+ *   B, C    : (batch, seqlen, ngroups, dstate)    A, Dskip : (nheads)
+ *   h0, h_last : (batch, nheads, headdim, dstate)
+ * Head h reads group g = h / (nheads / ngroups).
+ */
+int oracle_ssd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int64_t ngroups, const double *x, const double *dt,
+                   const double *A, const double *B, const double *C,
+                   const double *Dskip, const double *z, const double *h0,
+                   double *y, double *h_last)
+{
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1 ||
+        ngroups < 1 || nheads % ngroups != 0 || headdim * dstate > 65536)
+        return -1;
+    static double H[65536];
+    const int64_t hpg = nheads / ngroups;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t hd = 0; hd < nheads; ++hd) {
+            const int64_t g = hd / hpg;
+            for (int64_t k = 0; k < headdim * dstate; ++k)
+                H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const double d = dt[(b * seqlen + t) * nheads + hd];
+                const double alpha = exp(d * A[hd]);
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = ((b * seqlen + t) * nheads + hd) * headdim + p;
+                    const double xv = x[i];
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        double *hp = &H[p * dstate + n];
+                        *hp = alpha * *hp + d * Bt[n] * xv;
+                        acc += Ct[n] * *hp;
+                    }
+                    if (Dskip) acc += Dskip[hd] * xv;
+                    if (z) acc *= silu(z[i]);
+                    y[i] = acc;
+                }
+            }
+            if (h_last)
+                for (int64_t k = 0; k < headdim * dstate; ++k)
+                    h_last[(b * nheads + hd) * headdim * dstate + k] = H[k];
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,332 @@
+"""Pins for the float64 CPU oracle.
+
+Each ``check_*`` function takes an ``Oracle``-like object (``.scan`` and
+``.ssd``) and raises ``AssertionError`` if the oracle disagrees with something
+fixed independently of it: a closed form, a brute-force materialised sum, a
+hand-derived worked example, a different algorithm for the same quantity, or an
+invariant of the recurrence.  ``test_oracle_pins.py`` runs them on the oracle;
+``test_oracle_mutants.py`` runs them on copies of the oracle with planted
+mistakes and requires every mistake to be caught.
+
+Definitions followed (page titles and sections):
+  * "We brought Mamba to Trainium", section "Mamba: bringing an unsupported
+    model to the chip": h_t = Abar_t h_{t-1} + Bbar_t x_t, y_t = sum_n C_t h_t.
+  * "Mamba-3 NKI Kernels for AWS Neuron", section "How it works": Phase 0
+    alpha = exp(dt*A) and input weight dt (lam = 1); Phase 5 D skip then silu
+    gate.  Section "Kernel details" (mamba3_siso_ssd_kernel): chunked SSD with
+    the Mamba-2 structure; section "Repository layout": segsum and causal masks.
+  * "We brought Mamba to Trainium", section "We built the parallel scan": the
+    recurrence is associative, so it can be split and recombined.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+RTOL = 1e-12
+
+
+def _close(got, want, rtol=RTOL, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    scale = max(1.0, float(np.max(np.abs(want))) if want.size else 1.0)
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= rtol * scale, f"{what}: max abs err {err:.3e} (scale {scale:.3e})"
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _rand_scan(rng, batch, dim, N, L, G, a_scale=1.0):
+    u = rng.standard_normal((batch, dim, L))
+    delta = np.exp(rng.uniform(math.log(1e-2), math.log(0.5), (batch, dim, L)))
+    A = -a_scale * np.exp(rng.uniform(math.log(0.3), math.log(3.0), (dim, N)))
+    B = rng.standard_normal((batch, G, N, L))
+    C = rng.standard_normal((batch, G, N, L))
+    D = rng.standard_normal(dim)
+    z = rng.standard_normal((batch, dim, L))
+    return u, delta, A, B, C, D, z
+
+
+def _rand_ssd(rng, batch, L, H, P, N, G):
+    x = rng.standard_normal((batch, L, H, P))
+    dt = np.exp(rng.uniform(math.log(1e-2), math.log(0.5), (batch, L, H)))
+    A = -np.exp(rng.uniform(0.0, math.log(8.0), H))
+    B = rng.standard_normal((batch, L, G, N))
+    C = rng.standard_normal((batch, L, G, N))
+    D = rng.standard_normal(H)
+    z = rng.standard_normal((batch, L, H, P))
+    return x, dt, A, B, C, D, z
+
+
+# --------------------------------------------------------------------------
+# Selective scan
+# --------------------------------------------------------------------------
+
+def check_scan_hand_example(orc):
+    """Hand-derived worked example (tests/golden/scan_hand_example.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "scan_hand_example.json")))
+    i, e = g["inputs"], g["expected"]
+    arr = {k: np.array(v, dtype=np.float64) for k, v in i.items() if not k.endswith("exact")}
+    y, h = orc.scan(arr["u"], arr["delta"], arr["A"], arr["B"], arr["C"], arr["D"])
+    _close(y, e["y"], what="hand y")
+    _close(h, e["h_last"], what="hand h_last")
+    yg, hg = orc.scan(arr["u"], arr["delta"], arr["A"], arr["B"], arr["C"], arr["D"],
+                      arr["z_gated_case"])
+    _close(yg, e["y_gated"], what="hand gated y")
+    _close(hg, e["h_last"], what="hand gated h_last (the gate does not touch the state)")
+
+
+def check_scan_a_zero_prefix_sum(orc):
+    """A = 0: no decay, so the state is a running (prefix) sum of dt*B*x."""
+    rng = np.random.default_rng(11)
+    batch, dim, N, L, G = 2, 4, 5, 37, 2
+    u, delta, _, B, C, D, z = _rand_scan(rng, batch, dim, N, L, G)
+    A = np.zeros((dim, N))
+    y, h = orc.scan(u, delta, A, B, C, D, z)
+    g_of_d = np.arange(dim) // (dim // G)
+    Bd = B[:, g_of_d]                      # (batch, dim, N, L)
+    Cd = C[:, g_of_d]
+    contrib = delta[:, :, None, :] * Bd * u[:, :, None, :]
+    hs = np.cumsum(contrib, axis=-1)       # (batch, dim, N, L)
+    want = (np.sum(Cd * hs, axis=2) + D[None, :, None] * u) * _silu(z)
+    _close(y, want, what="A=0 y")
+    _close(h, hs[..., -1], what="A=0 h_last")
+
+
+def check_scan_constant_coeff_geometric(orc):
+    """Constant dt, x, B, C: geometric series h_t = dt B x (1 - r^(t+1)) / (1 - r)."""
+    dim, N, L = 3, 4, 50
+    dl, xi = 0.07, 1.3
+    A = np.array([[-0.5, -1.0, -2.0, -4.0],
+                  [-0.1, -0.2, -3.0, -0.7],
+                  [-1.5, -0.05, -0.9, -6.0]])
+    beta = np.array([0.9, -0.4, 1.7, 0.3])
+    gam = np.array([1.1, 0.6, -0.8, 2.0])
+    Dk = np.array([0.3, -1.2, 0.0])
+    u = np.full((1, dim, L), xi)
+    delta = np.full((1, dim, L), dl)
+    B = np.broadcast_to(beta[None, None, :, None], (1, 1, N, L)).copy()
+    C = np.broadcast_to(gam[None, None, :, None], (1, 1, N, L)).copy()
+    y, h = orc.scan(u, delta, A, B, C, Dk)
+    t = np.arange(L)
+    r = np.exp(dl * A)                                     # (dim, N)
+    geo = (1.0 - r[:, :, None] ** (t + 1)) / (1.0 - r[:, :, None])
+    hs = dl * beta[None, :, None] * xi * geo               # (dim, N, L)
+    want = np.einsum("n,dnt->dt", gam, hs) + Dk[:, None] * xi
+    _close(y[0], want, what="geometric y")
+    _close(h[0], hs[..., -1], what="geometric h_last")
+
+
+def check_scan_l1(orc):
+    """L = 1 from a zero state: y0 = dt0 x0 sum_n C0 B0 + D x0, h = dt0 B0 x0."""
+    rng = np.random.default_rng(12)
+    batch, dim, N, G = 3, 4, 6, 1
+    u, delta, A, B, C, D, z = _rand_scan(rng, batch, dim, N, 1, G)
+    y, h = orc.scan(u, delta, A, B, C, D, z)
+    cb = np.sum(C[:, 0, :, 0] * B[:, 0, :, 0], axis=1)   # (batch,)
+    want = (delta[..., 0] * u[..., 0] * cb[:, None] + D[None, :] * u[..., 0]) * _silu(z[..., 0])
+    _close(y[..., 0], want, what="L=1 y")
+    _close(h, delta[..., 0, None] * B[:, 0, None, :, 0] * u[..., 0, None], what="L=1 h_last")
+
+
+def check_scan_bruteforce(orc):
+    """Materialised quadratic form on tiny inputs, pure Python loops:
+    y_t = sum_{s<=t} sum_n C_t[n] (prod_{k=s+1..t} exp(dt_k A[n])) dt_s B_s[n] x_s + D x_t,
+    then the gate; h_last[n] is the same sum at t = L-1 without C."""
+    rng = np.random.default_rng(13)
+    for (batch, dim, N, L, G) in [(2, 3, 4, 9, 1), (1, 2, 3, 13, 2), (1, 1, 2, 24, 1)]:
+        u, delta, A, B, C, D, z = _rand_scan(rng, batch, dim, N, L, G)
+        y, h = orc.scan(u, delta, A, B, C, D, z)
+        dpg = dim // G
+        want_y = np.zeros((batch, dim, L))
+        want_h = np.zeros((batch, dim, N))
+        for b in range(batch):
+            for d in range(dim):
+                g = d // dpg
+                for t in range(L):
+                    acc = 0.0
+                    for s in range(t + 1):
+                        for n in range(N):
+                            prod = 1.0
+                            for k in range(s + 1, t + 1):
+                                prod *= math.exp(delta[b, d, k] * A[d, n])
+                            acc += C[b, g, n, t] * prod * delta[b, d, s] * B[b, g, n, s] * u[b, d, s]
+                    acc += D[d] * u[b, d, t]
+                    want_y[b, d, t] = acc * z[b, d, t] / (1.0 + math.exp(-z[b, d, t]))
+                for n in range(N):
+                    acc = 0.0
+                    for s in range(L):
+                        prod = 1.0
+                        for k in range(s + 1, L):
+                            prod *= math.exp(delta[b, d, k] * A[d, n])
+                        acc += prod * delta[b, d, s] * B[b, g, n, s] * u[b, d, s]
+                    want_h[b, d, n] = acc
+        _close(y, want_y, rtol=1e-11, what=f"brute y {(batch, dim, N, L, G)}")
+        _close(h, want_h, rtol=1e-11, what=f"brute h {(batch, dim, N, L, G)}")
+
+
+def check_scan_invariants(orc):
+    """Causality, linearity in x (no gate) and split continuation through h0."""
+    rng = np.random.default_rng(14)
+    batch, dim, N, L, G = 2, 3, 5, 41, 1
+    u, delta, A, B, C, D, z = _rand_scan(rng, batch, dim, N, L, G)
+    y, h = orc.scan(u, delta, A, B, C, D, z)
+    # causality: changing x at t0 leaves y_{<t0} unchanged and changes y_{t0}
+    t0 = 17
+    u2 = u.copy()
+    u2[:, :, t0] += 1.0
+    y2, _ = orc.scan(u2, delta, A, B, C, D, z)
+    assert np.array_equal(y2[..., :t0], y[..., :t0]), "causality"
+    assert np.all(y2[..., t0] != y[..., t0]), "x_t0 must reach y_t0"
+    # linearity in x without the gate
+    v = rng.standard_normal(u.shape)
+    ya, ha = orc.scan(u, delta, A, B, C, D)
+    yb, hb = orc.scan(v, delta, A, B, C, D)
+    yc, hc = orc.scan(2.0 * u - 3.0 * v, delta, A, B, C, D)
+    _close(yc, 2.0 * ya - 3.0 * yb, rtol=1e-11, what="linearity y")
+    _close(hc, 2.0 * ha - 3.0 * hb, rtol=1e-11, what="linearity h")
+    # split continuation: [0, L1) then [L1, L) from the first part's h_last
+    for L1 in (1, 20, L - 1):
+        yl, hl = orc.scan(u[..., :L1], delta[..., :L1], A, B[..., :L1], C[..., :L1], D, z[..., :L1])
+        yr, hr = orc.scan(u[..., L1:], delta[..., L1:], A, B[..., L1:], C[..., L1:], D,
+                          z[..., L1:], h0=hl)
+        _close(np.concatenate([yl, yr], axis=-1), y, what=f"split y at {L1}")
+        _close(hr, h, what=f"split h_last at {L1}")
+    # the gate: z = 0 zeroes y, and never touches the state
+    y0, h0 = orc.scan(u, delta, A, B, C, D, np.zeros_like(z))
+    assert np.all(y0 == 0.0), "silu(0) = 0"
+    _close(h0, h, rtol=0.0, what="gate leaves the state alone")
+
+
+# --------------------------------------------------------------------------
+# Scalar-decay SSD
+# --------------------------------------------------------------------------
+
+def check_ssd_hand_example(orc):
+    """Hand-derived worked example (tests/golden/ssd_hand_example.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "ssd_hand_example.json")))
+    i, e = g["inputs"], g["expected"]
+    arr = {k: np.array(v, dtype=np.float64) for k, v in i.items() if not k.endswith("exact")}
+    y, h = orc.ssd(arr["x"], arr["dt"], arr["A"], arr["B"], arr["C"], arr["D"])
+    _close(y, e["y"], what="hand ssd y")
+    _close(h, e["h_last"], what="hand ssd h_last")
+
+
+def chunked_ssd_numpy(x, dt, A, B, C, D, z, Q):
+    """The chunked (Mamba-2 structured) SSD written with matrices in float64.
+
+    Per chunk of Q steps (the last chunk may be shorter), with a_t the inclusive
+    cumulative sum of dt*A inside the chunk:
+      intra-chunk  Y_diag[t] = sum_{s<=t} (C_t . B_s) exp(a_t - a_s) dt_s x_s
+      state in     Y_off[t]  = exp(a_t) C_t . H_prev
+      state out    H_new     = exp(a_last) H_prev + sum_s exp(a_last - a_s) dt_s x_s B_s^T
+    This is a different algorithm from the step-by-step recurrence; both must
+    give the same numbers.
+    """
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    hpg = H // G
+    y = np.zeros_like(x)
+    hl = np.zeros((batch, H, P, N))
+    for b in range(batch):
+        for hd in range(H):
+            g = hd // hpg
+            Hs = np.zeros((P, N))
+            for c0 in range(0, L, Q):
+                c1 = min(L, c0 + Q)
+                Xc = x[b, c0:c1, hd, :]                 # (q, P)
+                dtc = dt[b, c0:c1, hd]                  # (q,)
+                Bc = B[b, c0:c1, g, :]                  # (q, N)
+                Cc = C[b, c0:c1, g, :]
+                a = np.cumsum(dtc * A[hd])              # (q,)
+                seg = a[:, None] - a[None, :]           # segsum a_t - a_s
+                q = c1 - c0
+                causal = np.tril(np.ones((q, q), dtype=bool))
+                Lmat = np.where(causal, np.exp(np.where(causal, seg, 0.0)), 0.0)
+                G_cb = Cc @ Bc.T                        # (q, q)
+                Ydiag = (G_cb * Lmat * dtc[None, :]) @ Xc
+                Yoff = np.exp(a)[:, None] * (Cc @ Hs.T)
+                decay_end = np.exp(a[-1] - a)           # (q,)
+                Hs = np.exp(a[-1]) * Hs + (Xc * (decay_end * dtc)[:, None]).T @ Bc
+                yc = Ydiag + Yoff
+                if D is not None:
+                    yc = yc + D[hd] * Xc
+                if z is not None:
+                    yc = yc * _silu(z[b, c0:c1, hd, :])
+                y[b, c0:c1, hd, :] = yc
+            hl[b, hd] = Hs
+    return y, hl
+
+
+def check_ssd_chunked_equals_recurrence(orc):
+    """The chunked matrix form (chunk 1, 3, 16, 64; ragged tails) equals the oracle."""
+    rng = np.random.default_rng(21)
+    for (batch, L, H, P, N, G) in [(2, 70, 4, 3, 5, 2), (1, 64, 2, 4, 8, 1), (1, 5, 1, 2, 3, 1)]:
+        x, dt, A, B, C, D, z = _rand_ssd(rng, batch, L, H, P, N, G)
+        y, h = orc.ssd(x, dt, A, B, C, D, z)
+        for Q in (1, 3, 16, 64):
+            yc, hc = chunked_ssd_numpy(x, dt, A, B, C, D, z, Q)
+            _close(y, yc, rtol=1e-11, what=f"chunked y Q={Q} {(batch, L, H, P, N, G)}")
+            _close(h, hc, rtol=1e-11, what=f"chunked h Q={Q} {(batch, L, H, P, N, G)}")
+
+
+def check_ssd_equals_scan_broadcast(orc):
+    """SSD is the selective scan with A[d=(h,p), n] = A_h and dt broadcast over p."""
+    rng = np.random.default_rng(22)
+    batch, L, H, P, N, G = 2, 29, 4, 3, 5, 2
+    x, dt, A, B, C, D, z = _rand_ssd(rng, batch, L, H, P, N, G)
+    y, h = orc.ssd(x, dt, A, B, C, D, z)
+    dim = H * P
+    u = x.reshape(batch, L, dim).transpose(0, 2, 1).copy()
+    delta = np.repeat(dt, P, axis=2).transpose(0, 2, 1).copy()
+    Asc = np.repeat(A, P)[:, None] * np.ones((1, N))
+    Bsc = B.transpose(0, 2, 3, 1).copy()
+    Csc = C.transpose(0, 2, 3, 1).copy()
+    zsc = z.reshape(batch, L, dim).transpose(0, 2, 1).copy()
+    ys, hs = orc.scan(u, delta, Asc, Bsc, Csc, np.repeat(D, P), zsc)
+    _close(y, ys.transpose(0, 2, 1).reshape(batch, L, H, P), what="ssd vs scan y")
+    _close(h, hs.reshape(batch, H, P, N), what="ssd vs scan h")
+
+
+def check_ssd_invariants(orc):
+    """Split continuation through h0, causality, and the zero-dt identity."""
+    rng = np.random.default_rng(23)
+    batch, L, H, P, N, G = 2, 33, 2, 3, 4, 1
+    x, dt, A, B, C, D, z = _rand_ssd(rng, batch, L, H, P, N, G)
+    y, h = orc.ssd(x, dt, A, B, C, D, z)
+    for L1 in (1, 16, 32):
+        yl, hl = orc.ssd(x[:, :L1], dt[:, :L1], A, B[:, :L1], C[:, :L1], D, z[:, :L1])
+        yr, hr = orc.ssd(x[:, L1:], dt[:, L1:], A, B[:, L1:], C[:, L1:], D, z[:, L1:], h0=hl)
+        _close(np.concatenate([yl, yr], axis=1), y, what=f"ssd split y at {L1}")
+        _close(hr, h, what=f"ssd split h at {L1}")
+    x2 = x.copy()
+    x2[:, 10] += 1.0
+    y2, _ = orc.ssd(x2, dt, A, B, C, D, z)
+    assert np.array_equal(y2[:, :10], y[:, :10]), "ssd causality"
+    # dt = 0 everywhere: no decay and no input, so the state stays h0 and y = C.h0 + D x
+    h0 = rng.standard_normal((batch, H, P, N))
+    y3, h3 = orc.ssd(x, np.zeros_like(dt), A, B, C, D, None, h0=h0)
+    want = np.einsum("blgn,bhpn->blhp", C[:, :, [0]], h0) + D[None, None, :, None] * x
+    _close(y3, want, what="dt=0 y")
+    _close(h3, h0, rtol=0.0, what="dt=0 h")
+
+
+ALL_CHECKS = [
+    check_scan_hand_example,
+    check_scan_a_zero_prefix_sum,
+    check_scan_constant_coeff_geometric,
+    check_scan_l1,
+    check_scan_bruteforce,
+    check_scan_invariants,
+    check_ssd_hand_example,
+    check_ssd_chunked_equals_recurrence,
+    check_ssd_equals_scan_broadcast,
+    check_ssd_invariants,
+]

@@ -1,0 +1,65 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require the
+pins to catch every one of them.  This shows the pins constrain each term of
+the definition: the decay and its sign, the dt on the input, the readout order,
+B versus C, the D skip, the gate and its order, the group index, the B/C
+layout, the initial state and the final state."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, [(old, new), ...]) -- every ``old`` must occur in oracle.c.
+MUTANTS = [
+    ("decay_sign", [("exp(dl * A[d * dstate + n])", "exp(-dl * A[d * dstate + n])")]),
+    ("no_dt_on_input", [("h[n] = abar * h[n] + dl * B[j] * x;", "h[n] = abar * h[n] + B[j] * x;")]),
+    ("readout_before_update", [(
+        "h[n] = abar * h[n] + dl * B[j] * x;\n                    acc += C[j] * h[n];",
+        "acc += C[j] * h[n];\n                    h[n] = abar * h[n] + dl * B[j] * x;")]),
+    ("b_c_swapped", [("dl * B[j] * x", "dl * C[j] * x"), ("acc += C[j] * h[n];", "acc += B[j] * h[n];")]),
+    ("no_dskip", [("if (Dskip) acc += Dskip[d] * x;", "")]),
+    ("sigmoid_gate", [("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));")]),
+    ("gate_before_dskip", [(
+        "if (Dskip) acc += Dskip[d] * x;\n                if (z) acc *= silu(z[i]);",
+        "if (z) acc *= silu(z[i]);\n                if (Dskip) acc += Dskip[d] * x;")]),
+    ("group_index", [("const int64_t g = d / dpg;", "const int64_t g = d % ngroups;")]),
+    ("bc_layout_transposed", [("((b * ngroups + g) * dstate + n) * seqlen + t",
+                               "((b * ngroups + g) * seqlen + t) * dstate + n")]),
+    ("h0_ignored", [("h[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;", "h[n] = 0.0;")]),
+    ("dt_times_a_off_by_one", [("const double dl = delta[i];",
+                                "const double dl = delta[t + 1 < seqlen ? i + 1 : i];")]),
+    ("ssd_decay_sign", [("exp(d * A[hd])", "exp(-d * A[hd])")]),
+    ("ssd_no_dt_on_input", [("*hp = alpha * *hp + d * Bt[n] * xv;", "*hp = alpha * *hp + Bt[n] * xv;")]),
+    ("ssd_no_dskip", [("if (Dskip) acc += Dskip[hd] * xv;", "")]),
+    ("ssd_wrong_state_index", [("double *hp = &H[p * dstate + n];", "double *hp = &H[n * headdim + p];")]),
+    ("ssd_group_index", [("const int64_t g = hd / hpg;", "const int64_t g = hd % ngroups;")]),
+    ("ssd_h0_ignored", [("H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;", "H[k] = 0.0;")]),
+]
+
+
+def _build(tmp_path, name, edits):
+    src = open(SRC).read()
+    for old, new in edits:
+        assert old in src, f"mutant {name}: pattern not found: {old!r}"
+        src = src.replace(old, new)
+    c = tmp_path / f"{name}.c"
+    c.write_text(src)
+    so = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", *oracle._CFLAGS, str(c), "-o", str(so), "-lm"])
+    return oracle.Oracle(str(so))
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, edits):
+    orc = _build(tmp_path, name, edits)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(orc)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no pin catches the planted mistake {name!r}"
