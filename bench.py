@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Selective-scan benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one ``ssm_scan_fwd`` call over the whole workload (every step of the
+hot path: stream the inputs, discretise, recur, read out, D skip, gate, write y
+and h_last), with the inputs already resident in HBM.  The headline workload is
+the large-channel long scan (batch 4, 5120 channels, 16 states, 4096 steps,
+bf16 storage, float32 arithmetic).  Prints one JSON line.
+
+Besides the headline, the line carries:
+  * ``roofline``: the dominant kernel (the scan sweep) against the bound that
+    limits it, from HIP events recorded on the launch stream around the timed
+    region;
+  * ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
+    same workload (single thread);
+  * ``workloads``: the other named workloads (the tiny, page-1 and long-prefill
+    scans and the chunked SSD), timed the same way, for context.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks and unit counts.
+HBM_PEAK_GBS = 8000.0
+N_CU, CLOCK_GHZ, SIMD_PER_CU, LANES_PER_SIMD = 256, 2.4, 4, 16
+# Non-packed fp32 VALU issue capacity: one lane-op per lane per clock.
+VALU_SLOTS_PER_S = N_CU * SIMD_PER_CU * LANES_PER_SIMD * CLOCK_GHZ * 1e9   # 3.93e13
+FP32_NONPACKED_TFLOPS = 2 * VALU_SLOTS_PER_S / 1e12                        # 78.6 (FMA = 2)
+BF16_MFMA_TFLOPS = 2500.0
+# Issue cost of one v_exp_f32 / v_rcp_f32 in full-rate VALU slots on gfx950
+# (measured: see the exp-rate probe summary under profiles/).
+TRANS_SLOTS = 2.0
+
+HEADLINE = "large_channel_4x5120x4096_bf16"
+
+
+def scan_alu_slots_per_element(N: int, has_z: bool, has_d: bool) -> float:
+    """VALU slots the method itself needs per (batch, channel, step) element.
+
+    Per state: exp(dt A) (1 transcendental), its argument dt*A (1 mul), the
+    input term (dt u) B (1 mul), the update a h + bx (1 fma) and the readout
+    C h (1 fma).  Per element: dt*u (1 mul), D u (1 fma), and the gate
+    z * 1/(1 + exp(-z)) (exp + rcp transcendentals, 3 mul/add).
+    """
+    full = 4 * N + 1 + (1 if has_d else 0) + (3 if has_z else 0)
+    trans = N + (2 if has_z else 0)
+    return full + TRANS_SLOTS * trans
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-context", action="store_true", help="skip the other named workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import state_space_model_ssm_amd as ssm
+    from state_space_model_ssm_amd.synth import WORKLOADS, ScanShape, SsdShape, make_scan_inputs, make_ssd_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def time_calls(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def scan_runner(s: ScanShape, host):
+        d = {k: (None if v is None else v.to(dev)) for k, v in host.items()}
+        y = torch.empty((s.batch, s.dim, s.seqlen), dtype=d["u"].dtype, device=dev)
+        h = torch.empty((s.batch, s.dim, s.dstate), dtype=torch.float32, device=dev)
+        dims = ssm.ScanDims(batch=s.batch, dim=s.dim, dstate=s.dstate, seqlen=s.seqlen,
+                            ngroups=s.ngroups, in_dtype=ssm.SSM_BF16 if s.dtype == "bf16" else ssm.SSM_F32,
+                            out_dtype=ssm.SSM_BF16 if s.dtype == "bf16" else ssm.SSM_F32,
+                            n_chunks=0, flags=0, workspace=None, workspace_bytes=0)
+        chunks = ssm.scan_resolved_chunks(dims)
+        need = ssm.scan_workspace_size(dims)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def fn():
+            ssm.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], y=y, h_last=h,
+                         workspace=ws, stream=stream)
+        return fn, chunks
+
+    def ssd_runner(s: SsdShape, host):
+        d = {k: (None if v is None else v.to(dev)) for k, v in host.items()}
+        y = torch.empty((s.batch, s.seqlen, s.nheads, s.headdim), dtype=torch.bfloat16, device=dev)
+        h = torch.empty((s.batch, s.nheads, s.headdim, s.dstate), dtype=torch.float32, device=dev)
+
+        def fn():
+            ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], y=y, h_last=h,
+                                stream=stream)
+        return fn
+
+    # ---- headline ------------------------------------------------------------
+    s = WORKLOADS[args.workload]
+    if not isinstance(s, ScanShape):
+        raise SystemExit("the headline workload must be a selective scan")
+    host = make_scan_inputs(s)
+    fn, chunks = scan_runner(s, host)
+    ms, wall = time_calls(fn, args.steps, args.warmup)
+    sec = ms / 1e3
+    gelem = s.elements / sec / 1e9
+    mbytes = s.metric_bytes()
+    hbm_gbs = mbytes / sec / 1e9
+    has_z, has_d = host["z"] is not None, host["D"] is not None
+    slots = scan_alu_slots_per_element(s.dstate, has_z, has_d) * s.elements
+    alu_tflops = 2 * slots / sec / 1e12
+    t_hbm = mbytes / (HBM_PEAK_GBS * 1e9)
+    t_alu = slots / VALU_SLOTS_PER_S
+    if t_alu >= t_hbm:
+        roof = {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(FP32_NONPACKED_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_NONPACKED_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "scan_chunk_kernel<bf16,bf16,16,sweep>" if s.dtype == "bf16" else "scan_chunk_kernel<f32,f32,16,sweep>"
+    roof["hbm_gbs"] = round(hbm_gbs, 1)
+    roof["hbm_frac"] = round(hbm_gbs / HBM_PEAK_GBS, 4)
+    roof["alu_model_us"] = round(t_alu * 1e6, 2)
+    roof["hbm_model_us"] = round(t_hbm * 1e6, 2)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- context: the other named workloads ------------------------------------
+    context = {}
+    if not args.no_context:
+        for name, w in WORKLOADS.items():
+            if name == args.workload:
+                continue
+            if isinstance(w, ScanShape):
+                f, k = scan_runner(w, make_scan_inputs(w))
+                reps = 200 if w.elements < 1 << 22 else 20
+                wms, _ = time_calls(f, reps, 5)
+                context[name] = {"ms": round(wms, 5), "Gelem/s": round(w.elements / wms / 1e6, 2),
+                                 "hbm_GB/s": round(w.metric_bytes() / wms / 1e6, 1), "n_chunks": k}
+            else:
+                f = ssd_runner(w, make_ssd_inputs(w))
+                wms, _ = time_calls(f, 50, 5)
+                context[name] = {"ms": round(wms, 5), "Gelem/s": round(w.elements / wms / 1e6, 2),
+                                 "hbm_GB/s": round(w.metric_bytes() / wms / 1e6, 1),
+                                 "hbm_GB/s_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6, 1),
+                                 "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2)}
+    torch.cuda.synchronize()
+
+    # ---- CPU baseline: the float64 oracle on a bounded sample ------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        oracle.build(force=False)
+        probe = 16
+        t0 = time.perf_counter()
+        _cpu_slice(oracle, host, s, probe)
+        per_ch = (time.perf_counter() - t0) / probe
+        nch = int(max(probe, min(s.batch * s.dim, args.cpu_seconds / max(per_ch, 1e-9))))
+        t0 = time.perf_counter()
+        _cpu_slice(oracle, host, s, nch)
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": round(nch * s.seqlen / dt_cpu / 1e9, 6), "unit": "Gelem/s", "cores": 1,
+               "kind": "oracle", "seconds": round(dt_cpu, 2),
+               "sample": f"first {nch} of {s.batch * s.dim} channels (batch-major), all {s.seqlen} steps, "
+                         f"single-threaded float64 recurrence"}
+
+    out = {
+        "metric": "selective-scan Gelem/s (B*D*L) + achieved HBM GB/s as % of MI355X peak",
+        "value": round(gelem, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": s.batch, "dim": s.dim, "dstate": s.dstate,
+                   "seqlen": s.seqlen, "ngroups": s.ngroups, "io_dtype": s.dtype, "gate": has_z,
+                   "dskip": has_d, "n_chunks": chunks, "seed": s.seed,
+                   "metric_bytes": mbytes, "parallelism": "none (1 GPU)"},
+        "hbm_GB/s": round(hbm_gbs, 1),
+        "hbm_pct_of_peak": round(100 * hbm_gbs / HBM_PEAK_GBS, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "workloads": context,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def ssd_flops(w) -> float:
+    """Matrix-core flops of the chunked SSD per call (the s2-s6 contractions)."""
+    Q, P, N = w.chunk, w.headdim, w.dstate
+    chunks = -(-w.seqlen // Q)
+    per_bc = 2 * Q * Q * N                       # C B^T, once per (batch, chunk) and group
+    per_bch = 2 * Q * Q * P + 2 * N * P * Q + 2 * Q * N * P   # M X, chunk state, C S^T
+    return w.batch * chunks * (per_bc * w.ngroups + per_bch * w.nheads)
+
+
+def _cpu_slice(oracle, host, s, nch):
+    """Run the oracle on the first nch (batch, channel) rows of the workload."""
+    import numpy as np
+    done = 0
+    b = 0
+    while done < nch:
+        take = min(nch - done, s.dim)
+        sl = {"u": host["u"][b:b + 1, :take], "delta": host["delta"][b:b + 1, :take],
+              "A": host["A"][:take], "B": host["B"][b:b + 1], "C": host["C"][b:b + 1],
+              "D": None if host["D"] is None else host["D"][:take],
+              "z": None if host["z"] is None else host["z"][b:b + 1, :take]}
+        if s.ngroups != 1:
+            raise SystemExit("cpu baseline sample assumes one group")
+        oracle.scan(sl["u"], sl["delta"], sl["A"], sl["B"], sl["C"], sl["D"], sl["z"])
+        done += take
+        b += 1
+
+
+if __name__ == "__main__":
+    main()

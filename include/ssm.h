@@ -1,0 +1,200 @@
+/*
+ * libssm: selective scan and scalar-decay chunked SSD forward on AMD MI355X
+ * (gfx950).  Plain C ABI: device pointers, sizes, a HIP stream; no torch types.
+ *
+ * Sources of the definitions (page titles, then the section):
+ *   [Mamba on Trainium]  "We brought Mamba to Trainium - and mapped where
+ *                        custom kernels actually help"
+ *   [Mamba-3 NKI]        "Mamba-3 NKI Kernels for AWS Neuron"
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; scratch memory ("workspace") is
+ *     passed in by the caller through the dims struct.
+ *   - Every tensor is dense, row-major, with the last listed index contiguous.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *     A kernel fault surfaces at the caller's next synchronisation.
+ *   - All argument checks run on the host before any HIP call.  A call that
+ *     fails a check returns a negative ssm_status_t, launches nothing and
+ *     writes nothing; ssm_last_error() then holds a one-line reason (per
+ *     host thread).  SSM_ERR_HIP is returned when a launch itself fails.
+ *   - Pointers must be aligned to their element size (4 bytes for float32,
+ *     2 for bfloat16), and more where an entry point says so; otherwise
+ *     SSM_ERR_ALIGN.
+ *   - Unsupported sizes return SSM_ERR_UNSUPPORTED; there is no fallback path.
+ *   - Indices and offsets are 64-bit throughout.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from libssm.so; nothing else is. */
+#define SSM_API __attribute__((visibility("default")))
+
+/* Storage dtypes. Arithmetic is float32 in every kernel. */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  SSM_ERR_SHAPE = -2,       /* negative size, ngroups does not divide, ...   */
+  SSM_ERR_DTYPE = -3,       /* dtype code is not an ssm_dtype_t              */
+  SSM_ERR_ALIGN = -4,       /* pointer not aligned to its element size       */
+  SSM_ERR_UNSUPPORTED = -5, /* valid but not implemented (e.g. dstate = 12)  */
+  SSM_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required    */
+  SSM_ERR_HIP = -7          /* a HIP launch failed                           */
+} ssm_status_t;
+
+/* ------------------------------------------------------------------------ */
+/* Selective scan                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sizes of one selective-scan call.
+ *   batch, dim (channels), dstate (N), seqlen (L), ngroups (G; G divides dim,
+ *   channel d reads the B/C of group d / (dim / G)).
+ *   in_dtype : storage dtype of u, delta, B, C, z.
+ *   out_dtype: storage dtype of y.  A, D and h_last are always float32.
+ *   n_chunks : 0 = the library picks; 1 = one sequential pass per channel;
+ *              k > 1 = split L into ceil(L / ceil(L / k)) chunks that run in
+ *              parallel, joined by the (decay product, state) carry.
+ *   flags    : reserved, must be 0.
+ *   workspace, workspace_bytes: caller-owned device scratch of at least
+ *              ssm_scan_workspace_size() bytes (may be NULL when that is 0).
+ * Supported: dstate in {1, 2, 4, 8, 16, 32, 64}; any batch, dim, seqlen >= 0.
+ */
+typedef struct {
+  int64_t batch, dim, dstate, seqlen, ngroups;
+  int32_t in_dtype, out_dtype;
+  int32_t n_chunks;
+  int32_t flags;
+  void *workspace;
+  size_t workspace_bytes;
+} ssm_scan_dims_t;
+
+/*
+ * Workspace the scan needs for `dims` (with n_chunks resolved as the call
+ * would resolve it).  Writes *bytes; returns SSM_OK or a check failure.
+ * The chunked carry keeps, per (batch, channel, chunk but the last, state),
+ * the chunk's decay product and its local end state: 8 * batch * dim *
+ * (chunks - 1) * dstate bytes.  One pass (a single chunk) needs none.
+ */
+SSM_API int ssm_scan_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes);
+
+/* The chunk count ssm_scan_fwd uses for `dims` (resolves n_chunks = 0). */
+SSM_API int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks);
+
+/*
+ * Selective-scan forward.
+ *
+ * For every batch b and channel d (state h in R^N, zero before t = 0):
+ *   h_t[n] = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B_t[n] * u_t
+ *   y_t    = (sum_n C_t[n] * h_t[n] + D[d] * u_t) * silu(z_t)
+ * with silu(z) = z / (1 + exp(-z)); the D term is dropped when D is NULL and
+ * the gate when z is NULL.  h_last receives h after the last step.
+ *   [Mamba on Trainium], "Mamba: bringing an unsupported model to the chip":
+ *     the state update h_t = Abar_t h_{t-1} + Bbar_t x_t and readout
+ *     y_t = sum_n C_t h_t, walked along the sequence.
+ *   [Mamba-3 NKI], "How it works", Phase 0: decay alpha = exp(dt * A) and
+ *     input weight gamma = lam * dt, here with lam = 1 (so Bbar x = dt B x);
+ *     Phase 5: the D skip connection, then the silu gate.
+ *   [Mamba on Trainium], "We built the parallel scan": the recurrence is
+ *     associative, which the chunked carry (n_chunks > 1) relies on.
+ *
+ * Layouts (in_dtype unless noted):
+ *   u, delta, z : (batch, dim, seqlen)         z nullable
+ *   A           : (dim, dstate) float32
+ *   B, C        : (batch, ngroups, dstate, seqlen)
+ *   D           : (dim) float32                nullable
+ *   y           : (batch, dim, seqlen) out_dtype
+ *   h_last      : (batch, dim, dstate) float32  nullable
+ * y and h_last must not overlap any input.  bfloat16 y is rounded to
+ * nearest even from the float32 result.
+ */
+SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, void *y, float *h_last,
+                 const ssm_scan_dims_t *dims, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Scalar-decay chunked SSD                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sizes of one SSD call.
+ *   batch, seqlen (L), nheads (H), headdim (P), dstate (N), ngroups (G; G
+ *   divides H, head h reads group h / (H / G)), chunk (Q).
+ *   in_dtype must be SSM_BF16 (the intra-chunk contractions run on bf16
+ *   matrix cores with float32 accumulation); out_dtype is SSM_BF16 or SSM_F32.
+ *   flags: reserved, must be 0.
+ * Supported: headdim = 64, dstate in {64, 128}, chunk = 64, any seqlen >= 0
+ * (a ragged last chunk is masked).
+ * Alignment: x, z, B, C and h_last must be 16-byte aligned (they are read and
+ * written as 16-byte vectors); dt and y need their element alignment.
+ */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  int32_t in_dtype, out_dtype;
+  int32_t flags;
+  int32_t reserved;
+  void *workspace;
+  size_t workspace_bytes;
+} ssd_dims_t;
+
+/* Workspace the SSD needs for `dims` (currently always 0). */
+SSM_API int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
+
+/*
+ * Scalar-decay SSD forward: the selective scan with one decay per (batch,
+ * time, head), shared by the head's headdim x dstate states, computed chunk by
+ * chunk with matrix-core contractions.
+ *
+ * For every batch b and head h (state S in R^{P x N}, zero before t = 0):
+ *   S_t   = exp(dt_t * A[h]) * S_{t-1} + dt_t * x_t B_t^T
+ *   y_t   = (S_t C_t + D[h] * x_t) * silu(z_t)
+ *   [Mamba-3 NKI], "Kernel details", mamba3_siso_ssd_kernel: a chunked SSD
+ *     with the Mamba-2 structure and chunk size 64 (the trapezoidal and
+ *     rotary Mamba-3 terms are not part of this call);
+ *   [Mamba-3 NKI], "Repository layout": segsum and causal masks;
+ *   [Mamba-3 NKI], "How it works", Phase 0 (alpha = exp(dt * A)) and Phase 5
+ *     (D skip, silu gate);
+ *   [Mamba on Trainium], "We built the parallel scan": the state passes from
+ *     chunk to chunk by the associative (decay, state) combine.
+ *
+ * Layouts:
+ *   x, z    : (batch, seqlen, nheads, headdim) bf16    z nullable
+ *   dt      : (batch, seqlen, nheads) bf16  (already positive: any softplus
+ *             and bias are applied by the caller)
+ *   A, D    : (nheads) float32                          D nullable
+ *   B, C    : (batch, seqlen, ngroups, dstate) bf16
+ *   y       : (batch, seqlen, nheads, headdim) out_dtype
+ *   h_last  : (batch, nheads, headdim, dstate) float32  nullable
+ */
+SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B,
+                    const void *C, const float *D, const void *z, void *y, float *h_last,
+                    const ssd_dims_t *dims, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Static name of a status code ("SSM_OK", "SSM_ERR_SHAPE", ...). */
+SSM_API const char *ssm_status_string(int status);
+
+/* Reason for the last failure on the calling host thread ("" if none).
+ * The pointer stays valid until the next libssm call on that thread. */
+SSM_API const char *ssm_last_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+SSM_API int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,251 @@
+"""Python binding of libssm (include/ssm.h): selective-scan and scalar-decay
+chunked-SSD forward on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libssm.so``.  PyTorch supplies device memory and the current HIP
+stream.  If ``libssm.so`` is missing the calls raise; there is no fallback.
+
+    from state_space_model_ssm_amd import scan_fwd, ssd_chunked_fwd
+    y, h_last = scan_fwd(u, delta, A, B, C, D, z)
+    y, h_last = ssd_chunked_fwd(x, dt, A, B, C, D)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "SSM_F32", "SSM_BF16", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
+    "scan_fwd", "ssd_chunked_fwd", "scan_workspace_size", "scan_resolved_chunks",
+    "ssd_workspace_size", "status_string", "last_error", "version",
+]
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE",
+          -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_UNSUPPORTED", -6: "SSM_ERR_WORKSPACE",
+          -7: "SSM_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssm.so")
+_lib = None
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class ScanDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("n_chunks", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libssm (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m state_space_model_ssm_amd.build` "
+                "(hipcc, gfx950). There is no fallback implementation.")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        L.ssm_scan_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(ScanDims), vp]
+        L.ssm_scan_fwd.restype = i32
+        L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_scan_workspace_size.restype = i32
+        L.ssm_scan_resolved_chunks.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_int32)]
+        L.ssm_scan_resolved_chunks.restype = i32
+        L.ssd_chunked_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_chunked_fwd.restype = i32
+        L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_workspace_size.restype = i32
+        L.ssm_status_string.argtypes = [i32]
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_last_error.argtypes = []
+        L.ssm_last_error.restype = ctypes.c_char_p
+        L.ssm_version.argtypes = []
+        L.ssm_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().ssm_last_error().decode()
+
+
+def version() -> int:
+    return lib().ssm_version()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SsmError(rc, last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.float32:
+        return SSM_F32
+    if t == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _scan_dims(u, B, in_dtype, out_dtype, n_chunks) -> ScanDims:
+    batch, dim, L = u.shape
+    G, N = B.shape[1], B.shape[2]
+    return ScanDims(batch=batch, dim=dim, dstate=N, seqlen=L, ngroups=G, in_dtype=in_dtype,
+                    out_dtype=out_dtype, n_chunks=n_chunks, flags=0, workspace=None,
+                    workspace_bytes=0)
+
+
+def scan_workspace_size(dims: ScanDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssm_scan_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def scan_resolved_chunks(dims: ScanDims) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().ssm_scan_resolved_chunks(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, *, out_dtype=None, n_chunks: int = 0,
+             return_h_last: bool = True, y=None, h_last=None, workspace=None, stream=None):
+    """Selective-scan forward (``ssm_scan_fwd``). Returns ``(y, h_last)``.
+
+    u, delta, z: (batch, dim, L); A: (dim, N) float32; B, C: (batch, G, N, L);
+    D: (dim,) float32.  u/delta/B/C/z share one dtype (float32 or bfloat16);
+    y defaults to that dtype, h_last is float32 (batch, dim, N).
+    """
+    torch = _torch()
+    in_code = _dtype_code(u.dtype)
+    out_dt = u.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != u.dtype:
+            raise TypeError(f"{name} must have dtype {u.dtype}")
+    for name, t in (("A", A), ("D", D)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    batch, dim, L = u.shape
+    N = B.shape[2]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("delta and z must have the shape of u")
+    if B.dim() != 4 or B.shape[0] != batch or B.shape[3] != L or C.shape != B.shape:
+        raise ValueError("B and C must be (batch, ngroups, dstate, seqlen)")
+    if A.shape != (dim, N) or (D is not None and D.shape != (dim,)):
+        raise ValueError("A must be (dim, dstate) and D (dim,)")
+    dims = _scan_dims(u, B, in_code, out_code, n_chunks)
+    need = scan_workspace_size(dims)
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=out_dt, device=u.device)
+    if h_last is None and return_h_last:
+        h_last = torch.empty((batch, dim, N), dtype=torch.float32, device=u.device)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+        dims.workspace = _ptr(workspace)
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+    _check(rc)
+    return y, h_last
+
+
+def _ssd_dims(x, B, chunk, in_dtype, out_dtype) -> SsdDims:
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return SsdDims(batch=batch, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=chunk,
+                   in_dtype=in_dtype, out_dtype=out_dtype, flags=0, reserved=0, workspace=None,
+                   workspace_bytes=0)
+
+
+def ssd_workspace_size(dims: SsdDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssd_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, chunk: int = 64, out_dtype=None,
+                    return_h_last: bool = True, y=None, h_last=None, stream=None):
+    """Scalar-decay chunked SSD forward (``ssd_chunked_fwd``). Returns ``(y, h_last)``.
+
+    x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
+    B, C: (batch, L, G, N) bf16.  h_last is float32 (batch, H, P, N).
+    """
+    torch = _torch()
+    in_code = _dtype_code(x.dtype)
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} must have dtype {x.dtype}")
+    for name, t in (("A", A), ("D", D)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    batch, L, H, P = x.shape
+    N = B.shape[3]
+    if dt.shape != (batch, L, H) or (z is not None and z.shape != x.shape):
+        raise ValueError("dt must be (batch, L, H) and z shaped like x")
+    if B.dim() != 4 or B.shape[:2] != (batch, L) or C.shape != B.shape:
+        raise ValueError("B and C must be (batch, seqlen, ngroups, dstate)")
+    if A.shape != (H,) or (D is not None and D.shape != (H,)):
+        raise ValueError("A and D must be (nheads,)")
+    dims = _ssd_dims(x, B, chunk, in_code, out_code)
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=out_dt, device=x.device)
+    if h_last is None and return_h_last:
+        h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device)
+    rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+    _check(rc)
+    return y, h_last

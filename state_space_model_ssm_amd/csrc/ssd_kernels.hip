@@ -1,0 +1,300 @@
+// Scalar-decay chunked SSD forward for gfx950: bf16 matrix cores (MFMA
+// 16x16x32, float32 accumulation) for the intra-chunk contractions.
+//
+// Structure ("Mamba-3 NKI Kernels for AWS Neuron", section "Kernel details",
+// mamba3_siso_ssd_kernel: the Mamba-2 chunked SSD with chunk 64; section
+// "Repository layout": segsum and causal masks).  For one (batch b, head h)
+// and one chunk of Q = 64 steps, with a_t the inclusive cumulative sum of
+// dt_s * A_h inside the chunk:
+//   G^T[s][t] = B_s . C_t                                  (MFMA, K = N)
+//   M[t][s]   = G^T[s][t] exp(a_t - a_s) dt_s  if s <= t, else 0   (segsum mask)
+//   Y         = diag(exp(a_t)) C S_prev^T  +  M X          (MFMA, K = N and K = Q)
+//   S_new     = exp(a_last) S_prev + sum_s exp(a_last - a_s) dt_s x_s B_s^T  (MFMA, K = Q)
+//   y         = (Y + D_h x) * silu(z)
+// S is the (headdim x dstate) state; passing it from chunk to chunk is the
+// associative (decay, state) combine of "We brought Mamba to Trainium",
+// section "We built the parallel scan", with a scalar decay per head.
+//
+// One workgroup (4 wavefronts) per (b, h) walks the chunks in order and keeps
+// S^T in float32 MFMA accumulators: wavefront w owns the 16 headdim columns
+// p in [16w, 16w+16) for all dstate rows.  Chunk operands are staged in LDS as
+// bf16 (x transposed to [p][s], B also transposed to [n][s]) so that every
+// MFMA operand fragment is one 16-byte (or two 8-byte) LDS read.
+//
+// MFMA 16x16x32 bf16 lane layout (lane l, q = l / 16, i = l % 16):
+//   A fragment: row i, k = 8q .. 8q+7;  B fragment: column i, k = 8q .. 8q+7;
+//   D: column i, rows 4q .. 4q+3.
+// A contraction may permute k as long as both fragments use one permutation:
+// the C S^T product uses k-slot 8q + j -> n = 32kk + 4q + j (j < 4) and
+// n = 32kk + 16 + 4q + j - 4 (j >= 4), which is exactly what two S^T
+// accumulator tiles hold per lane, so S feeds the MFMA without a transpose.
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int Q = 64;   // chunk length
+constexpr int P = 64;   // headdim
+constexpr int QP = Q + 8;  // padded LDS row (bf16 elements) of [.][s] arrays
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+
+__device__ __forceinline__ floatx4 mfma(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {  // 16-byte LDS read
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+__device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) { p[i] = f2bf(v); }
+
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
+template <typename Tout, int N>
+__global__ void __launch_bounds__(256) ssd_chunk_kernel(const SsdParams p) {
+  constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
+  constexpr int NT = N / 16;      // dstate tiles of S^T
+  constexpr int NK = N / 32;      // K steps over dstate
+  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * NP];   // C[t][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];   // B[s][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sBt[N * QP];  // B[n][s]
+  __shared__ __attribute__((aligned(16))) uint16_t sXt[P * QP];  // x[p][s]
+  __shared__ __attribute__((aligned(16))) uint16_t sM[Q * QP];   // M[t][s]
+  __shared__ __attribute__((aligned(16))) float sA[Q];           // a_t
+  __shared__ __attribute__((aligned(16))) float sEa[Q];          // exp(a_t)
+  __shared__ __attribute__((aligned(16))) float sW[Q];           // exp(a_last - a_s) dt_s
+  __shared__ __attribute__((aligned(16))) float sDt[Q];          // dt_s
+  __shared__ float sDecay;                                       // exp(a_last)
+
+  const uint16_t *__restrict__ gx = static_cast<const uint16_t *>(p.x);
+  const uint16_t *__restrict__ gdt = static_cast<const uint16_t *>(p.dt);
+  const uint16_t *__restrict__ gB = static_cast<const uint16_t *>(p.B);
+  const uint16_t *__restrict__ gC = static_cast<const uint16_t *>(p.C);
+  const uint16_t *__restrict__ gz = static_cast<const uint16_t *>(p.z);
+  Tout *__restrict__ gy = static_cast<Tout *>(p.y);
+
+  // Blocks of one batch row share B and C.  Consecutive block ids are dealt
+  // round-robin to the 8 XCDs, so remap ids to give each XCD a contiguous run
+  // of (b, h) pairs and keep a batch row's B/C in one L2.
+  const int64_t nblk = p.batch * p.nheads;
+  int64_t id = blockIdx.x;
+  if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;
+  const int64_t b = id / p.nheads;
+  const int64_t h = id % p.nheads;
+  const int64_t g = h / (p.nheads / p.ngroups);
+  const int64_t L = p.seqlen, H = p.nheads, G = p.ngroups;
+  const float Ah = p.A[h];
+  const float Dh = p.D ? p.D[h] : 0.0f;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int q = lane / 16;
+  const int r16 = lane % 16;
+  const int pcol = wave * 16 + r16;  // this lane's headdim column in S^T and Y
+
+  floatx4 S[NT];  // S^T tiles: rows n = 16 ni + 4q + r, column p = pcol
+#pragma unroll
+  for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c0 = 0; c0 < L; c0 += Q) {
+    // ---- stage the chunk --------------------------------------------------
+    // B and C: Q rows of N bf16, 16-byte vectors.
+#pragma unroll
+    for (int k = 0; k < (Q * N / 8) / 256; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (N / 8);
+      const int nv = (v % (N / 8)) * 8;
+      uint4 cv = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
+      if (c0 + t < L) {
+        const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
+        cv = *reinterpret_cast<const uint4 *>(gC + off);
+        bv = *reinterpret_cast<const uint4 *>(gB + off);
+      }
+      *reinterpret_cast<uint4 *>(&sC[t * NP + nv]) = cv;
+      *reinterpret_cast<uint4 *>(&sB[t * NP + nv]) = bv;
+      const uint16_t *be = reinterpret_cast<const uint16_t *>(&bv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sBt[(nv + j) * QP + t] = be[j];
+    }
+    // x: Q rows of P bf16, stored transposed.
+#pragma unroll
+    for (int k = 0; k < (Q * P / 8) / 256; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (P / 8);
+      const int pv = (v % (P / 8)) * 8;
+      uint4 xv = {0u, 0u, 0u, 0u};
+      if (c0 + t < L) xv = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
+      const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xv);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sXt[(pv + j) * QP + t] = xe[j];
+    }
+    // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
+    if (wave == 0) {
+      const float dtv = (c0 + lane < L) ? bf2f(gdt[(b * L + c0 + lane) * H + h]) : 0.0f;
+      float a = dtv * Ah;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(a, off);
+        if (lane >= off) a += o;
+      }
+      const float alast = __shfl(a, 63);
+      sA[lane] = a;
+      sEa[lane] = fast_exp(a);
+      sW[lane] = fast_exp(alast - a) * dtv;
+      sDt[lane] = dtv;
+      if (lane == 0) sDecay = fast_exp(alast);
+    }
+    __syncthreads();
+
+    // ---- Y_off = diag(exp(a_t)) C S_prev^T ---------------------------------
+    floatx4 Y[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) Y[ti] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const floatx8 sf = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
+                          S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
+      const bf16x8 bfrag = __builtin_convertvector(sf, bf16x8);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        const uint16_t *crow = &sC[(ti * 16 + r16) * NP + 32 * kk + 4 * q];
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(crow));
+        const bf16x4 hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(crow + 16));
+        const bf16x8 afrag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        Y[ti] = mfma(afrag, bfrag, Y[ti]);
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[ti][r] *= sEa[ti * 16 + 4 * q + r];
+    }
+
+    // ---- S_new = exp(a_last) S_prev + B^T (w x) ----------------------------
+    {
+      const float decay = sDecay;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) S[i] *= decay;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int s0 = 32 * kk + 8 * q;
+        const bf16x8 xs = lds8(&sXt[pcol * QP + s0]);
+        floatx8 wx;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wx[j] = static_cast<float>(xs[j]) * sW[s0 + j];
+        const bf16x8 bfrag = __builtin_convertvector(wx, bf16x8);
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          const bf16x8 afrag = lds8(&sBt[(ni * 16 + r16) * QP + s0]);
+          S[ni] = mfma(afrag, bfrag, S[ni]);
+        }
+      }
+    }
+
+    // ---- M = mask(G^T) into LDS: 12 tiles (si, ti), three per wavefront ----
+    // The lower-triangular tiles plus the two upper tiles (1,0) and (3,2) that
+    // the K = 32 steps of Y_diag read; those are written as zeros.
+    {
+      // (si, ti) pairs, four bits each: si | ti << 2, in the order listed above.
+      constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 |
+                                  0xAull << 20 | 0xCull << 24 | 0xDull << 28 | 0xEull << 32 |
+                                  0xFull << 36 | 0x1ull << 40 | 0xBull << 44;
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int code = static_cast<int>((kTiles >> (4 * (wave + 4 * u))) & 0xF);
+        const int si = code & 3;
+        const int ti = code >> 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (si <= ti) {
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) {
+            const bf16x8 afrag = lds8(&sB[(si * 16 + r16) * NP + 32 * kk + 8 * q]);
+            const bf16x8 bfrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
+            acc = mfma(afrag, bfrag, acc);
+          }
+        }
+        const int t = ti * 16 + r16;
+        const float at = sA[t];
+        uint16_t m[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = si * 16 + 4 * q + r;
+          const float v = (s <= t) ? acc[r] * fast_exp(at - sA[s]) * sDt[s] : 0.0f;
+          m[r] = f2bf(v);
+        }
+        *reinterpret_cast<uint2 *>(&sM[t * QP + si * 16 + 4 * q]) = *reinterpret_cast<const uint2 *>(m);
+      }
+    }
+    __syncthreads();
+
+    // ---- Y += M X (causal: K steps at or below the diagonal) ---------------
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (32 * kk < 16 * (ti + 1)) {
+          const bf16x8 afrag = lds8(&sM[(ti * 16 + r16) * QP + 32 * kk + 8 * q]);
+          const bf16x8 bfrag = lds8(&sXt[pcol * QP + 32 * kk + 8 * q]);
+          Y[ti] = mfma(afrag, bfrag, Y[ti]);
+        }
+      }
+    }
+
+    // ---- epilogue: D skip, gate, store y -----------------------------------
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = ti * 16 + 4 * q + r;
+        if (c0 + t < L) {
+          const int64_t off = ((b * L + c0 + t) * H + h) * P + pcol;
+          float yv = Y[ti][r] + Dh * bf2f(sXt[pcol * QP + t]);
+          if (gz) yv *= silu(bf2f(gz[off]));
+          st(gy, off, yv);
+        }
+      }
+    }
+    __syncthreads();  // the next chunk overwrites the LDS operands
+  }
+
+  if (p.h_last) {
+    float *hl = p.h_last + ((b * H + h) * P + pcol) * N;
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
+      *reinterpret_cast<floatx4 *>(hl + ni * 16 + 4 * q) = S[ni];
+  }
+}
+
+template <typename Tout>
+hipError_t launch_typed(const SsdParams &p, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
+  if (p.dstate == 128)
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, 128>), grid, dim3(256), 0, stream, p);
+  else if (p.dstate == 64)
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, 64>), grid, dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream) {
+  if (p.headdim != P || p.chunk != Q) return hipErrorInvalidValue;
+  return out_bf16 ? launch_typed<uint16_t>(p, stream) : launch_typed<float>(p, stream);
+}
+
+}  // namespace ssm

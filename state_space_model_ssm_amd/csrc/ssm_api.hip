@@ -1,0 +1,309 @@
+// C ABI of libssm (declared in include/ssm.h): argument checks, chunk-count
+// resolution, workspace sizing and dispatch to the HIP launchers.
+//
+// Every check runs on the host before any HIP call, so a rejected request
+// launches nothing and writes nothing.
+#include "ssm.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ssm_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SSM_OK;
+}
+
+bool valid_dtype(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
+size_t dtype_size(int32_t t) { return t == SSM_F32 ? 4 : 2; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int32_t kMaxChunks = 4096;
+constexpr int64_t kMaxGridX = 2147483647;
+
+// Byte range [p, p + bytes) of one tensor, for the overlap check.
+struct Span {
+  const void *p;
+  size_t bytes;
+};
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// ---------------------------------------------------------------------------
+// Selective scan
+// ---------------------------------------------------------------------------
+
+int check_scan_dims(const ssm_scan_dims_t *d) {
+  if (!d) return fail(SSM_ERR_NULL, "dims is NULL");
+  if (d->batch < 0 || d->dim < 0 || d->seqlen < 0)
+    return fail(SSM_ERR_SHAPE, "negative size (batch=%lld dim=%lld seqlen=%lld)",
+                (long long)d->batch, (long long)d->dim, (long long)d->seqlen);
+  if (d->dstate < 1) return fail(SSM_ERR_SHAPE, "dstate must be >= 1 (got %lld)", (long long)d->dstate);
+  if (d->ngroups < 1) return fail(SSM_ERR_SHAPE, "ngroups must be >= 1 (got %lld)", (long long)d->ngroups);
+  if (d->dim % d->ngroups != 0)
+    return fail(SSM_ERR_SHAPE, "ngroups (%lld) must divide dim (%lld)", (long long)d->ngroups,
+                (long long)d->dim);
+  if (!valid_dtype(d->in_dtype)) return fail(SSM_ERR_DTYPE, "in_dtype %d is not an ssm_dtype_t", d->in_dtype);
+  if (!valid_dtype(d->out_dtype)) return fail(SSM_ERR_DTYPE, "out_dtype %d is not an ssm_dtype_t", d->out_dtype);
+  if (d->flags != 0) return fail(SSM_ERR_SHAPE, "flags must be 0 (got %d)", d->flags);
+  if (d->n_chunks < 0 || d->n_chunks > kMaxChunks)
+    return fail(SSM_ERR_SHAPE, "n_chunks must be in [0, %d] (got %d)", kMaxChunks, d->n_chunks);
+  const int64_t N = d->dstate;
+  if (N != 1 && N != 2 && N != 4 && N != 8 && N != 16 && N != 32 && N != 64)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (1, 2, 4, 8, 16, 32 or 64)", (long long)N);
+  const int64_t cpb = ssm::scan_channels_per_block(static_cast<int>(N));
+  const int64_t tiles = d->ngroups ? ceil_div(d->dim / d->ngroups, cpb) : 0;
+  if (d->batch > 0 && d->ngroups * tiles > kMaxGridX / d->batch)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * ngroups * channel tiles exceeds the grid limit");
+  return SSM_OK;
+}
+
+// Chunk count the call uses.  0 asks the library: split the sequence only when
+// the channels alone give fewer than ~1024 wavefronts (one per SIMD of the
+// 256-CU part), and keep every chunk at least 64 steps long.
+int32_t resolve_chunks(const ssm_scan_dims_t *d, int64_t *chunk_len) {
+  const int64_t L = d->seqlen;
+  if (L <= 1 || d->batch == 0 || d->dim == 0) {
+    *chunk_len = L > 0 ? L : 1;
+    return 1;
+  }
+  int64_t want = d->n_chunks;
+  if (want == 0) {
+    const int64_t waves = d->batch * d->dim * d->dstate / 64;
+    want = waves >= 1024 ? 1 : ceil_div(1024, waves > 0 ? waves : 1);
+    const int64_t cap = L / 64 > 1 ? L / 64 : 1;
+    if (want > cap) want = cap;
+    if (want > 64) want = 64;
+  }
+  if (want > L) want = L;
+  const int64_t len = ceil_div(L, want);
+  *chunk_len = len;
+  return static_cast<int32_t>(ceil_div(L, len));
+}
+
+size_t scan_workspace(const ssm_scan_dims_t *d, int32_t chunks) {
+  if (chunks <= 1) return 0;
+  return static_cast<size_t>(8) * d->batch * d->dim * (chunks - 1) * d->dstate;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
+  const int rc = check_scan_dims(dims);
+  if (rc != SSM_OK) return rc;
+  int64_t len;
+  *bytes = scan_workspace(dims, resolve_chunks(dims, &len));
+  return ok();
+}
+
+int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks) {
+  if (!n_chunks) return fail(SSM_ERR_NULL, "n_chunks is NULL");
+  const int rc = check_scan_dims(dims);
+  if (rc != SSM_OK) return rc;
+  int64_t len;
+  *n_chunks = resolve_chunks(dims, &len);
+  return ok();
+}
+
+int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, void *y, float *h_last, const ssm_scan_dims_t *dims,
+                 void *stream) {
+  int rc = check_scan_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssm_scan_dims_t &d = *dims;
+  const int64_t n_bdl = d.batch * d.dim * d.seqlen;
+  const int64_t n_bc = d.batch * d.ngroups * d.dstate * d.seqlen;
+  const int64_t n_a = d.dim * d.dstate;
+  const int64_t n_h = d.batch * d.dim * d.dstate;
+  if (n_bdl > 0 && (!u || !delta || !y)) return fail(SSM_ERR_NULL, "u, delta and y are required");
+  if (n_bc > 0 && (!B || !C)) return fail(SSM_ERR_NULL, "B and C are required");
+  if (n_a > 0 && !A) return fail(SSM_ERR_NULL, "A is required");
+  const size_t ei = dtype_size(d.in_dtype), eo = dtype_size(d.out_dtype);
+  if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei))
+    return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
+  if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h_last, 4))
+    return fail(SSM_ERR_ALIGN, "A, D and h_last must be 4-byte aligned");
+  const Span ins[] = {{u, n_bdl * ei}, {delta, n_bdl * ei}, {z, n_bdl * ei}, {B, n_bc * ei},
+                      {C, n_bc * ei},  {A, n_a * 4ull},    {D, d.dim * 4ull}};
+  const Span sy{y, n_bdl * eo}, sh{h_last, n_h * 4ull};
+  for (const Span &s : ins)
+    if (overlap(s, sy) || overlap(s, sh)) return fail(SSM_ERR_SHAPE, "an output overlaps an input");
+  if (overlap(sy, sh)) return fail(SSM_ERR_SHAPE, "y overlaps h_last");
+
+  int64_t chunk_len = 1;
+  const int32_t chunks = resolve_chunks(&d, &chunk_len);
+  const size_t need = scan_workspace(&d, chunks);
+  if (need > 0) {
+    if (!d.workspace || d.workspace_bytes < need)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required for %d chunks (got %zu)", need,
+                  chunks, d.workspace ? d.workspace_bytes : (size_t)0);
+    if (!aligned(d.workspace, 4)) return fail(SSM_ERR_ALIGN, "workspace must be 4-byte aligned");
+    const Span sw{d.workspace, need};
+    for (const Span &s : ins)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an input");
+    if (overlap(sw, sy) || overlap(sw, sh)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
+  }
+  if (d.batch == 0 || d.dim == 0) return ok();
+
+  ssm::ScanParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.A = A;
+  p.D = D;
+  p.y = y;
+  p.h_last = h_last;
+  p.carry = static_cast<float *>(need > 0 ? d.workspace : nullptr);
+  p.batch = d.batch;
+  p.dim = d.dim;
+  p.seqlen = d.seqlen;
+  p.ngroups = d.ngroups;
+  p.dim_per_group = d.dim / d.ngroups;
+  p.chunk_len = chunk_len;
+  p.tiles_per_group = ceil_div(p.dim_per_group, ssm::scan_channels_per_block(static_cast<int>(d.dstate)));
+  p.n_chunks = chunks;
+  p.dstate = static_cast<int32_t>(d.dstate);
+  const hipError_t e = ssm::launch_scan(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Scalar-decay chunked SSD
+// ---------------------------------------------------------------------------
+
+static int check_ssd_dims(const ssd_dims_t *d) {
+  if (!d) return fail(SSM_ERR_NULL, "dims is NULL");
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 0)
+    return fail(SSM_ERR_SHAPE, "negative size (batch=%lld seqlen=%lld nheads=%lld)", (long long)d->batch,
+                (long long)d->seqlen, (long long)d->nheads);
+  if (d->headdim < 1 || d->dstate < 1 || d->chunk < 1)
+    return fail(SSM_ERR_SHAPE, "headdim, dstate and chunk must be >= 1");
+  if (d->ngroups < 1) return fail(SSM_ERR_SHAPE, "ngroups must be >= 1 (got %lld)", (long long)d->ngroups);
+  if (d->nheads % d->ngroups != 0)
+    return fail(SSM_ERR_SHAPE, "ngroups (%lld) must divide nheads (%lld)", (long long)d->ngroups,
+                (long long)d->nheads);
+  if (!valid_dtype(d->in_dtype)) return fail(SSM_ERR_DTYPE, "in_dtype %d is not an ssm_dtype_t", d->in_dtype);
+  if (!valid_dtype(d->out_dtype)) return fail(SSM_ERR_DTYPE, "out_dtype %d is not an ssm_dtype_t", d->out_dtype);
+  if (d->flags != 0 || d->reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (d->in_dtype != SSM_BF16)
+    return fail(SSM_ERR_UNSUPPORTED, "ssd_chunked_fwd takes bf16 inputs only (matrix-core operands)");
+  if (d->headdim != 64) return fail(SSM_ERR_UNSUPPORTED, "headdim %lld not supported (64)", (long long)d->headdim);
+  if (d->dstate != 64 && d->dstate != 128)
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (64 or 128)", (long long)d->dstate);
+  if (d->chunk != 64) return fail(SSM_ERR_UNSUPPORTED, "chunk %lld not supported (64)", (long long)d->chunk);
+  if (d->batch > 0 && d->nheads > kMaxGridX / d->batch)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * nheads exceeds the grid limit");
+  return SSM_OK;
+}
+
+int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
+  const int rc = check_ssd_dims(dims);
+  if (rc != SSM_OK) return rc;
+  *bytes = 0;
+  return ok();
+}
+
+int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                    const float *D, const void *z, void *y, float *h_last, const ssd_dims_t *dims,
+                    void *stream) {
+  const int rc = check_ssd_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssd_dims_t &d = *dims;
+  const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
+  const int64_t n_dt = d.batch * d.seqlen * d.nheads;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const int64_t n_h = d.batch * d.nheads * d.headdim * d.dstate;
+  if (n_x > 0 && (!x || !dt || !y)) return fail(SSM_ERR_NULL, "x, dt and y are required");
+  if (n_bc > 0 && (!B || !C)) return fail(SSM_ERR_NULL, "B and C are required");
+  if (d.nheads > 0 && !A) return fail(SSM_ERR_NULL, "A is required");
+  const size_t eo = dtype_size(d.out_dtype);
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16))
+    return fail(SSM_ERR_ALIGN, "x, z, B and C must be 16-byte aligned");
+  if (!aligned(dt, 2)) return fail(SSM_ERR_ALIGN, "dt must be 2-byte aligned");
+  if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
+  if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
+  if (!aligned(h_last, 16)) return fail(SSM_ERR_ALIGN, "h_last must be 16-byte aligned");
+  const Span ins[] = {{x, n_x * 2ull}, {dt, n_dt * 2ull}, {z, n_x * 2ull}, {B, n_bc * 2ull},
+                      {C, n_bc * 2ull}, {A, d.nheads * 4ull}, {D, d.nheads * 4ull}};
+  const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull};
+  for (const Span &s : ins)
+    if (overlap(s, sy) || overlap(s, sh)) return fail(SSM_ERR_SHAPE, "an output overlaps an input");
+  if (overlap(sy, sh)) return fail(SSM_ERR_SHAPE, "y overlaps h_last");
+  if (d.batch == 0 || d.nheads == 0) return ok();
+
+  ssm::SsdParams p{};
+  p.x = x;
+  p.dt = dt;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.A = A;
+  p.D = D;
+  p.y = y;
+  p.h_last = h_last;
+  p.batch = d.batch;
+  p.seqlen = d.seqlen;
+  p.nheads = d.nheads;
+  p.headdim = d.headdim;
+  p.dstate = d.dstate;
+  p.ngroups = d.ngroups;
+  p.chunk = d.chunk;
+  const hipError_t e = ssm::launch_ssd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssd launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostics
+// ---------------------------------------------------------------------------
+
+const char *ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_NULL: return "SSM_ERR_NULL";
+    case SSM_ERR_SHAPE: return "SSM_ERR_SHAPE";
+    case SSM_ERR_DTYPE: return "SSM_ERR_DTYPE";
+    case SSM_ERR_ALIGN: return "SSM_ERR_ALIGN";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+    case SSM_ERR_WORKSPACE: return "SSM_ERR_WORKSPACE";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP";
+    default: return "SSM_ERR_UNKNOWN";
+  }
+}
+
+const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+int ssm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal declarations of libssm: kernel parameter blocks and the launchers
+// that ssm_api.hip calls after validating a request.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// One selective-scan launch (see ssm_scan_fwd in include/ssm.h for the math).
+struct ScanParams {
+  const void *u, *delta, *B, *C, *z;  // in_dtype
+  const float *A, *D;                 // float32; D nullable
+  void *y;                            // out_dtype
+  float *h_last;                      // nullable
+  float *carry;                       // chunked path: [batch][dim][n_chunks-1][2][dstate]
+  int64_t batch, dim, seqlen, ngroups, dim_per_group;
+  int64_t chunk_len;                  // time steps per chunk
+  int64_t tiles_per_group;            // channel tiles per (batch, group)
+  int32_t n_chunks;                   // resolved chunk count (>= 1)
+  int32_t dstate;
+};
+
+// Channel tile of one workgroup for a given dstate: 256 threads, one state per
+// thread, so 256 / dstate channels.
+int scan_channels_per_block(int dstate);
+
+// Launch the chunk-summary pass (chunks 0 .. n_chunks-2) when n_chunks > 1,
+// then the sweep that writes y and h_last.  Returns a hipError_t.
+hipError_t launch_scan(const ScanParams &p, int in_bf16, int out_bf16, hipStream_t stream);
+
+// One chunked-SSD launch (see ssd_chunked_fwd in include/ssm.h).
+struct SsdParams {
+  const void *x, *dt, *B, *C, *z;     // bf16
+  const float *A, *D;                 // float32; D nullable
+  void *y;                            // out dtype
+  float *h_last;                      // nullable
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+};
+
+hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
+
+}  // namespace ssm

@@ -1,0 +1,166 @@
+"""libssm's C ABI on the host: the library loads, exports exactly what
+include/ssm.h declares, and rejects every bad request before any HIP call.
+
+No kernel is launched here: each call below fails a host-side check, so the
+fake device addresses it passes are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_model_ssm_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+FAKE = 0x7F0000000000  # 256-byte aligned fake device address; never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^SSM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
+
+
+def _exported():
+    out = os.popen(f"nm -D --defined-only {ssm.library_path()}").read()
+    return sorted({l.split()[-1] for l in out.splitlines() if " T " in l})
+
+
+def test_library_loads_and_exports_exactly_the_header():
+    lib = ssm.lib()
+    declared = _declared()
+    assert len(declared) == 8, declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert _exported() == declared
+
+
+def test_version_and_status_strings():
+    assert ssm.version() == 100
+    for code, name in ssm.STATUS.items():
+        assert ssm.status_string(code) == name
+    assert ssm.status_string(-99) == "SSM_ERR_UNKNOWN"
+
+
+def _dims(**kw):
+    base = dict(batch=2, dim=64, dstate=16, seqlen=100, ngroups=1, in_dtype=0, out_dtype=0,
+                n_chunks=0, flags=0, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    return ssm.ScanDims(**base)
+
+
+def _scan(dims, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
+          C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None):
+    return ssm.lib().ssm_scan_fwd(u, delta, A, B, C, D, z, y, h, ctypes.byref(dims), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dim=-3), -2), (dict(seqlen=-1), -2), (dict(dstate=0), -2),
+    (dict(ngroups=0), -2), (dict(dim=64, ngroups=3), -2), (dict(in_dtype=2), -3),
+    (dict(out_dtype=-1), -3), (dict(flags=1), -2), (dict(n_chunks=-1), -2),
+    (dict(n_chunks=5000), -2), (dict(dstate=12), -5), (dict(dstate=128), -5),
+])
+def test_scan_rejects_bad_dims(kw, code):
+    rc = _scan(_dims(**kw))
+    assert rc == code, (rc, ssm.last_error())
+    assert ssm.last_error()
+
+
+def test_scan_rejects_null_and_misaligned():
+    d = _dims()
+    assert _scan(d, u=None) == -1
+    assert _scan(d, B=None) == -1
+    assert _scan(d, A=None) == -1
+    assert _scan(d, y=None) == -1
+    assert ssm.lib().ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, None) == -1
+    assert _scan(d, u=FAKE + 2) == -4                       # f32 input needs 4-byte alignment
+    assert _scan(d, h=FAKE + 0x20000002) == -4
+    assert _scan(_dims(out_dtype=1), y=FAKE + 0x10000001) == -4
+
+
+def test_scan_rejects_overlap():
+    d = _dims()
+    assert _scan(d, y=FAKE + 16) == -2            # y starts inside u
+    assert _scan(d, h=FAKE + 0x10000000 + 64) == -2  # h_last inside y
+
+
+def test_scan_workspace_rules():
+    d = _dims(n_chunks=4)
+    need = ssm.scan_workspace_size(d)
+    assert need == 8 * 2 * 64 * 3 * 16
+    assert ssm.scan_resolved_chunks(d) == 4
+    assert _scan(d) == -6                                      # no workspace
+    d.workspace, d.workspace_bytes = FAKE + 0x30000000, need - 4
+    assert _scan(d) == -6                                      # too small
+    d.workspace_bytes = need
+    d.workspace = FAKE + 0x30000002
+    assert _scan(d) == -4                                      # misaligned
+    d.workspace = FAKE + 8                                     # overlaps u
+    assert _scan(d) == -2
+    assert ssm.scan_workspace_size(_dims(n_chunks=1)) == 0
+
+
+@pytest.mark.parametrize("L,k,expect", [(100, 4, 4), (10, 4, 4), (9, 4, 3), (5, 8, 5), (1, 8, 1),
+                                         (0, 3, 1), (4096, 1, 1), (128, 3, 3)])
+def test_scan_chunk_resolution(L, k, expect):
+    assert ssm.scan_resolved_chunks(_dims(seqlen=L, n_chunks=k)) == expect
+
+
+def test_scan_auto_chunks_keep_big_work_in_one_pass():
+    # enough channels for >= 1024 wavefronts: a single pass
+    assert ssm.scan_resolved_chunks(_dims(batch=8, dim=1536, seqlen=2048)) == 1
+    assert ssm.scan_resolved_chunks(_dims(batch=4, dim=5120, seqlen=4096)) == 1
+    # few channels: split, with chunks of at least 64 steps
+    k = ssm.scan_resolved_chunks(_dims(batch=1, dim=64, seqlen=4096))
+    assert 1 < k <= 64
+    assert ssm.scan_resolved_chunks(_dims(batch=1, dim=64, seqlen=100)) == 1
+
+
+def _sdims(**kw):
+    base = dict(batch=2, seqlen=128, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=64,
+                in_dtype=1, out_dtype=1, flags=0, reserved=0, workspace=None, workspace_bytes=0)
+    base.update(kw)
+    return ssm.SsdDims(**base)
+
+
+def _ssd(dims, x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
+         C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None):
+    return ssm.lib().ssd_chunked_fwd(x, dt, A, B, C, D, z, y, h, ctypes.byref(dims), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(seqlen=-1), -2), (dict(headdim=0), -2), (dict(ngroups=3), -2),
+    (dict(in_dtype=7), -3), (dict(in_dtype=0), -5), (dict(headdim=32), -5), (dict(dstate=96), -5),
+    (dict(chunk=32), -5), (dict(flags=2), -2), (dict(reserved=1), -2),
+])
+def test_ssd_rejects_bad_dims(kw, code):
+    assert _ssd(_sdims(**kw)) == code, ssm.last_error()
+
+
+def test_ssd_rejects_null_misaligned_overlap():
+    d = _sdims()
+    assert _ssd(d, x=None) == -1
+    assert _ssd(d, C=None) == -1
+    assert _ssd(d, x=FAKE + 8) == -4            # x must be 16-byte aligned
+    assert _ssd(d, dt=FAKE + 0x100001) == -4
+    assert _ssd(d, h=FAKE + 0x20000008) == -4   # h_last must be 16-byte aligned
+    assert _ssd(d, y=FAKE + 0x100010) == -2     # y overlaps dt
+    n = ctypes.c_size_t(99)
+    assert ssm.lib().ssd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_empty_inputs_launch_nothing_and_succeed():
+    # batch = 0 or dim = 0: valid, nothing to do, no HIP call is made.
+    assert _scan(_dims(batch=0), u=None, delta=None, B=None, C=None, y=None) == 0
+    assert _scan(_dims(dim=0), u=None, delta=None, A=None, y=None) == 0  # B, C still have elements
+    assert _ssd(_sdims(batch=0), x=None, dt=None, B=None, C=None, y=None) == 0
+    assert _ssd(_sdims(nheads=0), x=None, dt=None, A=None, y=None) == 0
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ssm, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ssm, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        ssm.lib()
