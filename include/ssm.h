@@ -62,8 +62,9 @@ typedef enum {
  *   in_dtype : storage dtype of u, delta, B, C, z.
  *   out_dtype: storage dtype of y.  A, D and h_last are always float32.
  *   n_chunks : 0 = the library picks; 1 = one sequential pass per channel;
- *              k > 1 = split L into ceil(L / ceil(L / k)) chunks that run in
- *              parallel, joined by the (decay product, state) carry.
+ *              k > 1 = split L into chunks of len = 32 * ceil(ceil(L / k) / 32)
+ *              steps (ceil(L / len) <= k chunks) that run in parallel, joined
+ *              by the (decay product, state) carry.
  *   flags    : reserved, must be 0.
  *   workspace, workspace_bytes: caller-owned device scratch of at least
  *              ssm_scan_workspace_size() bytes (may be NULL when that is 0).

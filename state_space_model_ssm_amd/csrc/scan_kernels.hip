@@ -10,14 +10,18 @@
 //   * One thread owns one (channel d, state n) pair and keeps h[n] in a float32
 //     register for its whole time range.  A 256-thread workgroup covers
 //     256 / N channels of one (batch, group), so the B_t/C_t tile it stages in
-//     LDS is shared by every channel of the block.
-//   * Time is walked in tiles of T steps.  Per tile the block stages, in LDS,
-//     delta and w = delta * u for its channels and B, C for its group (the
-//     global loads of tile i+1 are issued into registers before tile i is
-//     computed).  Each thread then runs T steps of the recurrence and writes its
+//     LDS is shared by every channel of the block.  For N >= 16 the N states of
+//     a channel fill whole 16-lane DPP rows.
+//   * Time is walked in tiles of T steps.  Global loads are 16-byte vectors
+//     issued DEPTH tiles ahead into a static register ring.  Per tile the block
+//     writes dt, w = dt * u and D * u for its channels and B, C for its group
+//     into LDS; each thread then runs T steps of the recurrence and writes its
 //     readout partial C_t[n] h_t[n] to LDS; after a barrier the same 256
-//     threads, now one per (channel, step) element, sum the N partials, add the
-//     D skip, apply the gate and store y with coalesced writes.
+//     threads, one per (channel, step) element, sum the N partials, add the D
+//     skip, apply the gate and store y.
+//   * N >= 16: the 16 lanes of a DPP row share one channel, so dt and w reach
+//     them by a row broadcast fused into the multiplies (v_mul_f32_dpp
+//     row_newbcast), from a single LDS word per lane per 16 steps.
 //   * The sequence may be split into chunks that run in parallel (grid.y).
 //     A first pass (SUMMARY) reduces every chunk but the last to the pair
 //     (prod_t exp(dt_t A), local end state); the sweep pass for chunk c folds
@@ -25,8 +29,10 @@
 //     (P1, h1) o (P2, h2) = (P1 P2, P2 h1 + h2)  ("We brought Mamba to
 //     Trainium", section "We built the parallel scan") to get its start state.
 //
-// Padding rule: time steps past the end of a chunk are staged with delta = 0
-// and w = 0, so exp(0) = 1 and the state passes through them unchanged.
+// Padding rule: time steps past the end of a chunk are staged with dt = 0 and
+// w = 0, so exp(0) = 1 and the state passes through them unchanged.
+#include <utility>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -38,10 +44,13 @@ struct alignas(16) F4 {
   float v[4];
 };
 
-__device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t raw(const float *p, int64_t i) { return __float_as_uint(p[i]); }
+__device__ __forceinline__ uint32_t raw(const uint16_t *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float from_raw(uint32_t r, const float *) { return __uint_as_float(r); }
+__device__ __forceinline__ float from_raw(uint32_t r, const uint16_t *) { return __uint_as_float(r << 16); }
 
 __device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
@@ -54,27 +63,130 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
 }
 
+// Value of lane J of this lane's 16-lane DPP row.  Folded by the compiler
+// into the consuming VOP2 instruction (v_mul_f32_dpp ... row_newbcast:J).
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J,
+                                                               0xF, 0xF, false));
+}
+
+// One step of the recurrence on the DPP path: dt and w come from lane J of
+// the row (step J of the current 16-step block).
+template <int J, bool SUMMARY>
+__device__ __forceinline__ void dpp_step(float dl16, float w16, float a2, float bv, float cv, float &h,
+                                         float &prod, float &pr) {
+  const float a = fast_exp2(row_bcast<J>(dl16) * a2);
+  h = fmaf(a, h, row_bcast<J>(w16) * bv);
+  if constexpr (SUMMARY) prod *= a;
+  else pr = cv * h;
+}
+
+// Steps 4G .. 4G+3 of a 16-step block.
+template <int G, bool SUMMARY>
+__device__ __forceinline__ void dpp_group(float dl16, float w16, float a2, const F4 &b4, const F4 &c4,
+                                          F4 &pr, float &h, float &prod) {
+  dpp_step<4 * G + 0, SUMMARY>(dl16, w16, a2, b4.v[0], c4.v[0], h, prod, pr.v[0]);
+  dpp_step<4 * G + 1, SUMMARY>(dl16, w16, a2, b4.v[1], c4.v[1], h, prod, pr.v[1]);
+  dpp_step<4 * G + 2, SUMMARY>(dl16, w16, a2, b4.v[2], c4.v[2], h, prod, pr.v[2]);
+  dpp_step<4 * G + 3, SUMMARY>(dl16, w16, a2, b4.v[3], c4.v[3], h, prod, pr.v[3]);
+}
+
+// Unpack one 16-byte vector of VEC storage elements into floats.
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+  static constexpr int kN = 4;
+  __device__ static void unpack(const uint4 &r, float *o) {
+    o[0] = __uint_as_float(r.x);
+    o[1] = __uint_as_float(r.y);
+    o[2] = __uint_as_float(r.z);
+    o[3] = __uint_as_float(r.w);
+  }
+};
+template <>
+struct Vec<uint16_t> {
+  static constexpr int kN = 8;
+  __device__ static void unpack(const uint4 &r, float *o) {
+    o[0] = bf_lo(r.x); o[1] = bf_hi(r.x);
+    o[2] = bf_lo(r.y); o[3] = bf_hi(r.y);
+    o[4] = bf_lo(r.z); o[5] = bf_hi(r.z);
+    o[6] = bf_lo(r.w); o[7] = bf_hi(r.w);
+  }
+};
+
+// A row segment that is misaligned or crosses the end of the chunk: element
+// loads, zero past t_end, packed into the same 16-byte layout as a vector load.
+__device__ __forceinline__ uint32_t elem_bits(const float *row, int64_t t, int64_t t_end) {
+  return t < t_end ? __float_as_uint(row[t]) : 0u;
+}
+__device__ __forceinline__ uint32_t elem_bits(const uint16_t *row, int64_t t, int64_t t_end) {
+  return t < t_end ? static_cast<uint32_t>(row[t]) : 0u;
+}
+__device__ __forceinline__ uint4 load_seg_tail(const float *row, int64_t t, int64_t t_end) {
+  return uint4{elem_bits(row, t, t_end), elem_bits(row, t + 1, t_end), elem_bits(row, t + 2, t_end),
+               elem_bits(row, t + 3, t_end)};
+}
+__device__ __forceinline__ uint4 load_seg_tail(const uint16_t *row, int64_t t, int64_t t_end) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = elem_bits(row, t + 2 * i, t_end) | (elem_bits(row, t + 2 * i + 1, t_end) << 16);
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
 template <int N>
 struct TileCfg {
   static constexpr int CH = 256 / N;                             // channels per block
   static constexpr int T = N >= 4 ? 32 : (N == 2 ? 16 : 8);      // time steps per tile
-  static constexpr int TP = T + 4;                               // padded LDS row
-  static constexpr int EPT = (CH * T + 255) / 256;               // channel-tile elements / thread
-  static constexpr int BPT = (N * T + 255) / 256;                // B/C-tile elements / thread
+  static constexpr int TP = T + 4;                               // padded LDS row (floats)
+  static constexpr int EPT = (CH * T + 255) / 256;               // epilogue elements / thread
+  static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
 };
 
-template <typename Tin, typename Tout, int N, bool SUMMARY>
+// One block's view of the tensors and its fixed index math.
+template <typename Tin, int N, bool SUMMARY>
+struct Block {
+  using Cfg = TileCfg<N>;
+  static constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT;
+  static constexpr int VEC = Vec<Tin>::kN;          // storage elements per 16-byte vector
+  static constexpr int SEG = (T + VEC - 1) / VEC;   // vectors per tile row
+  static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
+  static constexpr int BC_JOBS = N * SEG;           // (B, C) row segments
+  static constexpr int JOBS = PAIR_JOBS + BC_JOBS;
+  static constexpr int JPT = (JOBS + 255) / 256;    // staging jobs per thread
+};
+
+// Registers holding one tile's global data between its load and its staging.
+template <typename Tin, int N, bool SUMMARY>
+struct TileRegs {
+  using Bk = Block<Tin, N, SUMMARY>;
+  uint4 a[Bk::JPT];   // dt segment, or B segment
+  uint4 b[Bk::JPT];   // u segment, or C segment
+  uint32_t z[Bk::EPT];   // raw storage bits of z; converted in the epilogue
+};
+
+template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z>
 __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
-  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT, BPT = Cfg::BPT;
-  static_assert(T % 4 == 0 && TP % 4 == 0, "tiles are read four steps at a time");
+  using Bk = Block<Tin, N, SUMMARY>;
+  using Regs = TileRegs<Tin, N, SUMMARY>;
+  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT;
+  constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
+  constexpr bool kDpp = Cfg::kDpp;
+  static_assert(T % 4 == 0 && TP % 4 == 0 && (!kDpp || T % 16 == 0), "tile shape");
 
   __shared__ F4 sDl4[CH * TP / 4];
   __shared__ F4 sW4[CH * TP / 4];
+  // D * u is read by the epilogue of tile i while tile i+1 is being staged,
+  // so it alternates between two buffers by tile parity.
+  __shared__ F4 sDu4[SUMMARY ? 1 : 2 * CH * TP / 4];
   __shared__ F4 sB4[N * TP / 4];
   __shared__ F4 sC4[SUMMARY ? 1 : N * TP / 4];
   __shared__ F4 sP4[SUMMARY ? 1 : 256 * TP / 4];
-  float *sDl = sDl4[0].v, *sW = sW4[0].v, *sB = sB4[0].v, *sC = sC4[0].v, *sP = sP4[0].v;
+  float *sDl = sDl4[0].v, *sW = sW4[0].v, *sDu = sDu4[0].v;
+  float *sP = sP4[0].v;
 
   const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
   const Tin *__restrict__ gdl = static_cast<const Tin *>(p.delta);
@@ -82,7 +194,8 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   const Tin *__restrict__ gC = static_cast<const Tin *>(p.C);
   const Tin *__restrict__ gz = static_cast<const Tin *>(p.z);
   Tout *__restrict__ gy = static_cast<Tout *>(p.y);
-  const bool has_z = !SUMMARY && gz != nullptr;
+  constexpr bool has_z = !SUMMARY && HAS_Z;
+  const bool vec_ok = p.vec_ok != 0;
 
   const int tid = threadIdx.x;
   const int n = tid % N;
@@ -100,6 +213,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   const int64_t d0 = g * p.dim_per_group + ch0;
   const int64_t t_begin = static_cast<int64_t>(c) * p.chunk_len;
   const int64_t t_end = min(L, t_begin + p.chunk_len);
+  const int ntiles = static_cast<int>((t_end - t_begin + T - 1) / T);
 
   // ---- this thread's state ------------------------------------------------
   const bool mine = chl < nvalid;
@@ -112,125 +226,218 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     for (int j = 0; j < c; ++j) h = fmaf(cr[j * 2 * N + n], h, cr[j * 2 * N + N + n]);
   }
 
-  // ---- staging / epilogue element map: element k of this thread ------------
-  int col[EPT], loff[EPT];
-  bool act[EPT], inrange[EPT];
-  int64_t gbase[EPT];
-  float dsk[EPT];
+  // ---- staging jobs: job k of this thread loads one row segment of VEC steps
+  // from two tensors: (dt, u) of a channel row, or (B, C) of a state row.
+  // Whether a thread has job k is uniform over its wavefront when the job
+  // count is a multiple of 64, which keeps the loads free of divergence.
+  const Tin *jsrc1[JPT], *jsrc2[JPT];
+  int jkind[JPT], jrow[JPT], jcol[JPT];
+  bool jon[JPT];
+  int64_t jbase[JPT];
+  float jdsk[JPT];
+#pragma unroll
+  for (int k = 0; k < JPT; ++k) {
+    int job = tid + 256 * k;
+    jon[k] = job < Bk::JOBS;
+    if constexpr (Bk::JOBS % 64 == 0)
+      jon[k] = __builtin_amdgcn_readfirstlane(static_cast<int>(jon[k])) != 0;
+    if (!jon[k]) job = 0;
+    const int kind = job < Bk::PAIR_JOBS ? 0 : 1;
+    if (kind == 1) job -= Bk::PAIR_JOBS;
+    jkind[k] = kind;
+    jrow[k] = job / SEG;
+    jcol[k] = (job % SEG) * VEC;
+    if (kind == 0) {
+      // Rows past the group's last channel load a valid row's data; their
+      // states are never written out.
+      const int r = min(jrow[k], nvalid - 1);
+      jbase[k] = (b * p.dim + d0 + r) * L;
+      jdsk[k] = (jrow[k] < nvalid && p.D != nullptr) ? p.D[d0 + jrow[k]] : 0.0f;
+      jsrc1[k] = gdl;
+      jsrc2[k] = gu;
+    } else {
+      jbase[k] = ((b * p.ngroups + g) * N + jrow[k]) * L;
+      jdsk[k] = 0.0f;
+      jsrc1[k] = gB;
+      jsrc2[k] = gC;
+    }
+  }
+  // ---- epilogue element map: element k of this thread is (row, col) of the tile
+  int erow[EPT], ecol[EPT];
+  bool eact[EPT];
+  int64_t ebase[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
-    const int idx = tid + 256 * k;
-    const int row = idx / T;
-    col[k] = idx % T;
-    inrange[k] = idx < CH * T;
-    act[k] = inrange[k] && row < nvalid;
-    loff[k] = row * TP + col[k];
-    gbase[k] = act[k] ? (b * p.dim + d0 + row) * L + col[k] : 0;
-    dsk[k] = (act[k] && p.D != nullptr) ? p.D[d0 + row] : 0.0f;
-  }
-  int bcol[BPT], boff[BPT];
-  bool bin[BPT];
-  int64_t bbase[BPT];
-#pragma unroll
-  for (int k = 0; k < BPT; ++k) {
-    const int idx = tid + 256 * k;
-    const int nn = idx / T;
-    bcol[k] = idx % T;
-    bin[k] = idx < N * T;
-    boff[k] = nn * TP + bcol[k];
-    bbase[k] = bin[k] ? ((b * p.ngroups + g) * N + nn) * L + bcol[k] : 0;
+    const int e = tid + 256 * k;
+    erow[k] = e / T;
+    ecol[k] = e % T;
+    eact[k] = e < CH * T && erow[k] < nvalid;
+    ebase[k] = (b * p.dim + d0 + (eact[k] ? erow[k] : 0)) * L;
   }
 
-  float rdl[EPT], ru[EPT], rz[EPT], rb[BPT], rc[BPT];
-  auto prefetch = [&](int64_t t0) {
+  // Tiles wholly inside [t_begin, t_end) with 16-byte aligned rows load
+  // with branch-free vector loads; the last partial tile (or every tile when
+  // rows are misaligned) loads element by element, zero past t_end.
+  const int nfast = vec_ok ? static_cast<int>((t_end - t_begin) / T) : 0;
+
+  auto prefetch_fast = [&](Regs &R, int ti) __attribute__((always_inline)) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      rdl[k] = 0.0f;
-      ru[k] = 0.0f;
-      rz[k] = 0.0f;
-      if (act[k] && t0 + col[k] < t_end) {
-        rdl[k] = ld(gdl, gbase[k] + t0);
-        ru[k] = ld(gu, gbase[k] + t0);
-        if (has_z) rz[k] = ld(gz, gbase[k] + t0);
+    for (int k = 0; k < JPT; ++k) {
+      if (jon[k]) {
+        const int64_t o = jbase[k] + t0 + jcol[k];
+        R.a[k] = *reinterpret_cast<const uint4 *>(jsrc1[k] + o);
+        R.b[k] = *reinterpret_cast<const uint4 *>(jsrc2[k] + o);
+      }
+    }
+    if constexpr (has_z) {
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) R.z[k] = raw(gz, ebase[k] + t0 + ecol[k]);
+    }
+  };
+
+  auto prefetch_slow = [&](Regs &R, int ti) __attribute__((always_inline)) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      if (jon[k]) {
+        const int64_t t = t0 + jcol[k];
+        R.a[k] = load_seg_tail(jsrc1[k] + jbase[k], t, t_end);
+        R.b[k] = load_seg_tail(jsrc2[k] + jbase[k], t, t_end);
       }
     }
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      rb[k] = 0.0f;
-      rc[k] = 0.0f;
-      if (bin[k] && t0 + bcol[k] < t_end) {
-        rb[k] = ld(gB, bbase[k] + t0);
-        if (!SUMMARY) rc[k] = ld(gC, bbase[k] + t0);
+    for (int k = 0; k < EPT; ++k) {
+      R.z[k] = 0u;
+      if constexpr (has_z) {
+        if (t0 + ecol[k] < t_end) R.z[k] = raw(gz, ebase[k] + t0 + ecol[k]);
       }
     }
   };
 
-  prefetch(t_begin);
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += T) {
-    // ---- stage tile t0 from registers into LDS ----------------------------
-    float du[EPT], zz[EPT];
+  auto stage = [&](const Regs &R, int par) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      if (inrange[k]) {
-        sDl[loff[k]] = rdl[k];
-        sW[loff[k]] = rdl[k] * ru[k];
-      }
-      du[k] = dsk[k] * ru[k];
-      zz[k] = rz[k];
-    }
+    for (int k = 0; k < JPT; ++k) {
+      if (!jon[k]) continue;
+      float va[VEC], vb[VEC];
+      Vec<Tin>::unpack(R.a[k], va);
+      Vec<Tin>::unpack(R.b[k], vb);
+      const int o = jrow[k] * TP + jcol[k];
+      if (jkind[k] == 0) {
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      if (bin[k]) {
-        sB[boff[k]] = rb[k];
-        if (!SUMMARY) sC[boff[k]] = rc[k];
-      }
-    }
-    __syncthreads();
-    if (t0 + T < t_end) prefetch(t0 + T);
-
-    // ---- recurrence over the tile ------------------------------------------
-#pragma unroll
-    for (int tt = 0; tt < T; tt += 4) {
-      const F4 dl4 = sDl4[(chl * TP + tt) / 4];
-      const F4 w4 = sW4[(chl * TP + tt) / 4];
-      const F4 b4 = sB4[(n * TP + tt) / 4];
-      if constexpr (SUMMARY) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = fast_exp2(dl4.v[j] * a2);
-          h = fmaf(a, h, w4.v[j] * b4.v[j]);
-          prod *= a;
+        for (int i = 0; i < VEC; i += 4) {
+          sDl4[(o + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
+          sW4[(o + i) / 4] = F4{{va[i] * vb[i], va[i + 1] * vb[i + 1], va[i + 2] * vb[i + 2], va[i + 3] * vb[i + 3]}};
+          if (!SUMMARY) {
+            const float dk = jdsk[k];
+            sDu4[par * (CH * TP / 4) + (o + i) / 4] = F4{{dk * vb[i], dk * vb[i + 1], dk * vb[i + 2], dk * vb[i + 3]}};
+          }
         }
       } else {
-        const F4 c4 = sC4[(n * TP + tt) / 4];
-        F4 pr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float a = fast_exp2(dl4.v[j] * a2);
-          h = fmaf(a, h, w4.v[j] * b4.v[j]);
-          pr.v[j] = c4.v[j] * h;
+        for (int i = 0; i < VEC; i += 4) {
+          sB4[(o + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
+          if (!SUMMARY) sC4[(o + i) / 4] = F4{{vb[i], vb[i + 1], vb[i + 2], vb[i + 3]}};
         }
-        sP4[((chl * N + n) * TP + tt) / 4] = pr;
       }
     }
-    __syncthreads();
+  };
 
-    // ---- epilogue: sum the N partials, D skip, gate, store y ----------------
+  // T steps of the recurrence for this thread's (channel, state); the readout
+  // partials C_t[n] h_t[n] go to LDS.
+  auto recur = [&]() __attribute__((always_inline)) {
+    if constexpr (kDpp) {
+      const int j = tid % 16;
+#pragma unroll
+      for (int blk16 = 0; blk16 < T / 16; ++blk16) {
+        const float dl16 = sDl[chl * TP + blk16 * 16 + j];
+        const float w16 = sW[chl * TP + blk16 * 16 + j];
+        const int tb = blk16 * 16;
+        const int prow = ((chl * N + n) * TP + tb) / 4;
+        F4 b4[4], c4[4], pr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b4[q] = sB4[(n * TP + tb) / 4 + q];
+          c4[q] = SUMMARY ? F4{} : sC4[(n * TP + tb) / 4 + q];
+        }
+        dpp_group<0, SUMMARY>(dl16, w16, a2, b4[0], c4[0], pr[0], h, prod);
+        dpp_group<1, SUMMARY>(dl16, w16, a2, b4[1], c4[1], pr[1], h, prod);
+        dpp_group<2, SUMMARY>(dl16, w16, a2, b4[2], c4[2], pr[2], h, prod);
+        dpp_group<3, SUMMARY>(dl16, w16, a2, b4[3], c4[3], pr[3], h, prod);
+        if constexpr (!SUMMARY) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < T; tt += 4) {
+        const F4 dl4 = sDl4[(chl * TP + tt) / 4];
+        const F4 w4 = sW4[(chl * TP + tt) / 4];
+        const F4 b4 = sB4[(n * TP + tt) / 4];
+        const F4 c4 = SUMMARY ? F4{} : sC4[(n * TP + tt) / 4];
+        F4 pr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = fast_exp2(dl4.v[i] * a2);
+          h = fmaf(a, h, w4.v[i] * b4.v[i]);
+          if constexpr (SUMMARY) prod *= a;
+          else pr.v[i] = c4.v[i] * h;
+        }
+        if constexpr (!SUMMARY) sP4[((chl * N + n) * TP + tt) / 4] = pr;
+      }
+    }
+  };
+
+  // One tile: stage from registers, recur, epilogue.  `pf` refills R with the
+  // tile DEPTH ahead on the fast path.
+  auto do_tile = [&](Regs &R, int ti, bool pf) __attribute__((always_inline)) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
+    uint32_t zz[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) zz[e] = R.z[e];
+    const int par = ti & 1;
+    stage(R, par);
+    __syncthreads();
+    if (pf && ti + DEPTH < nfast) prefetch_fast(R, ti + DEPTH);
+    recur();
+    __syncthreads();
     if constexpr (!SUMMARY) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        if (act[k] && t0 + col[k] < t_end) {
-          const int row = (tid + 256 * k) / T;
-          const float *pp = sP + row * N * TP + col[k];
+      for (int e = 0; e < EPT; ++e) {
+        if (eact[e] && t0 + ecol[e] < t_end) {
+          const float *pp = sP + erow[e] * N * TP + ecol[e];
           float s = 0.0f;
 #pragma unroll
           for (int nn = 0; nn < N; ++nn) s += pp[nn * TP];
-          float yv = s + du[k];
-          if (has_z) yv *= silu(zz[k]);
-          st(gy, gbase[k] + t0, yv);
+          float yv = s + sDu[par * CH * TP + erow[e] * TP + ecol[e]];
+          if constexpr (has_z) yv *= silu(from_raw(zz[e], gz));
+          st(gy, ebase[e] + t0 + ecol[e], yv);
         }
       }
     }
+  };
+
+  // Fast tiles: tile ti lives in ring slot ti % DEPTH; the loop is unrolled
+  // DEPTH times so every slot index is a compile-time constant.
+  static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
+  Regs ring[DEPTH];
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k)
+    if (k < nfast) prefetch_fast(ring[k], k);
+  for (int ti0 = 0; ti0 < nfast; ti0 += DEPTH) {
+    do_tile(ring[0], ti0, true);
+    if constexpr (DEPTH > 1) {
+      if (ti0 + 1 < nfast) do_tile(ring[1], ti0 + 1, true);
+    }
+    if constexpr (DEPTH > 2) {
+      if (ti0 + 2 < nfast) do_tile(ring[2], ti0 + 2, true);
+    }
+  }
+  // Remaining tiles: element loads, one tile at a time.
+  for (int ti = nfast; ti < ntiles; ++ti) {
+    prefetch_slow(ring[0], ti);
+    do_tile(ring[0], ti, false);
   }
 
   if constexpr (SUMMARY) {
@@ -244,20 +451,28 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   }
 }
 
+// Prefetch depth (tiles in flight per block) by input dtype: bf16 tiles are
+// half the bytes, so they keep one more tile in flight.
+template <typename Tin>
+constexpr int kDepth = sizeof(Tin) == 2 ? 3 : 2;
+
 template <typename Tin, typename Tout, int N>
 hipError_t launch_typed(const ScanParams &p, hipStream_t stream) {
   const int64_t blocks = p.batch * p.ngroups * p.tiles_per_group;
   if (blocks == 0) return hipSuccess;
+  constexpr int kD = kDepth<Tin>;
   if (p.n_chunks > 1) {
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, true>),
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, true, kD, false>),
                        dim3(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks - 1)),
                        dim3(256), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false>),
-                     dim3(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks)),
-                     dim3(256), 0, stream, p);
+  const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks));
+  if (p.z != nullptr)
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -278,6 +493,8 @@ hipError_t launch_n(const ScanParams &p, hipStream_t stream) {
 }  // namespace
 
 int scan_channels_per_block(int dstate) { return dstate > 0 ? 256 / dstate : 0; }
+
+int scan_vector_elems(int in_bf16) { return in_bf16 ? 8 : 4; }
 
 hipError_t launch_scan(const ScanParams &p, int in_bf16, int out_bf16, hipStream_t stream) {
   if (!in_bf16 && !out_bf16) return launch_n<float, float>(p, stream);

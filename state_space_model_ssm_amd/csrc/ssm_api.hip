@@ -98,7 +98,8 @@ int32_t resolve_chunks(const ssm_scan_dims_t *d, int64_t *chunk_len) {
     if (want > 64) want = 64;
   }
   if (want > L) want = L;
-  const int64_t len = ceil_div(L, want);
+  int64_t len = ceil_div(L, want);
+  if (want > 1) len = ceil_div(len, ssm::kScanChunkAlign) * ssm::kScanChunkAlign;
   *chunk_len = len;
   return static_cast<int32_t>(ceil_div(L, len));
 }
@@ -191,6 +192,9 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   p.tiles_per_group = ceil_div(p.dim_per_group, ssm::scan_channels_per_block(static_cast<int>(d.dstate)));
   p.n_chunks = chunks;
   p.dstate = static_cast<int32_t>(d.dstate);
+  const int vec = ssm::scan_vector_elems(d.in_dtype == SSM_BF16);
+  p.vec_ok = (d.seqlen % vec == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(B, 16) &&
+             aligned(C, 16);
   const hipError_t e = ssm::launch_scan(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));

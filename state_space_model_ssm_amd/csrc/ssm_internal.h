@@ -20,11 +20,18 @@ struct ScanParams {
   int64_t tiles_per_group;            // channel tiles per (batch, group)
   int32_t n_chunks;                   // resolved chunk count (>= 1)
   int32_t dstate;
+  int32_t vec_ok;                     // u, delta, B, C rows start 16-byte aligned
 };
+
+// Chunks start on multiples of this many steps (the scan's time tile).
+constexpr int64_t kScanChunkAlign = 32;
 
 // Channel tile of one workgroup for a given dstate: 256 threads, one state per
 // thread, so 256 / dstate channels.
 int scan_channels_per_block(int dstate);
+
+// Storage elements per 16-byte vector load of the scan inputs.
+int scan_vector_elems(int in_bf16);
 
 // Launch the chunk-summary pass (chunks 0 .. n_chunks-2) when n_chunks > 1,
 // then the sweep that writes y and h_last.  Returns a hipError_t.

@@ -102,8 +102,10 @@ def test_scan_workspace_rules():
     assert ssm.scan_workspace_size(_dims(n_chunks=1)) == 0
 
 
-@pytest.mark.parametrize("L,k,expect", [(100, 4, 4), (10, 4, 4), (9, 4, 3), (5, 8, 5), (1, 8, 1),
-                                         (0, 3, 1), (4096, 1, 1), (128, 3, 3)])
+# Chunks are ceil(L / k) steps rounded up to a multiple of 32 (the time tile).
+@pytest.mark.parametrize("L,k,expect", [(100, 4, 4), (10, 4, 1), (9, 4, 1), (5, 8, 1), (1, 8, 1),
+                                         (0, 3, 1), (4096, 1, 1), (128, 3, 2), (1000, 16, 16),
+                                         (300, 7, 5), (4096, 64, 64), (129, 129, 5)])
 def test_scan_chunk_resolution(L, k, expect):
     assert ssm.scan_resolved_chunks(_dims(seqlen=L, n_chunks=k)) == expect
 

@@ -91,7 +91,7 @@ SCAN_CASES = [
     (2, 20, 16, 300, 1, "f32", True, "normal", 3),      # chunked carry
     (2, 20, 16, 301, 1, "f32", True, "normal", 7),      # chunked, ragged chunks
     (1, 16, 16, 1000, 2, "f32", True, "normal", 16),
-    (1, 24, 16, 129, 1, "f32", True, "normal", 129),    # one step per chunk
+    (1, 24, 16, 129, 1, "f32", True, "normal", 129),    # 32-step chunks, ragged last
     (2, 64, 1, 77, 1, "f32", True, "normal", 1),
     (2, 300, 1, 40, 3, "f32", True, "normal", 2),       # 256-channel tiles, ragged
     (2, 70, 2, 65, 1, "f32", True, "normal", 1),
