@@ -31,14 +31,18 @@ sys.path.insert(0, ROOT)
 
 # MI355X published peaks and unit counts.
 HBM_PEAK_GBS = 8000.0
-N_CU, CLOCK_GHZ, SIMD_PER_CU, LANES_PER_SIMD = 256, 2.4, 4, 16
-# Non-packed fp32 VALU issue capacity: one lane-op per lane per clock.
-VALU_SLOTS_PER_S = N_CU * SIMD_PER_CU * LANES_PER_SIMD * CLOCK_GHZ * 1e9   # 3.93e13
-FP32_NONPACKED_TFLOPS = 2 * VALU_SLOTS_PER_S / 1e12                        # 78.6 (FMA = 2)
+N_CU, CLOCK_GHZ = 256, 2.4
+# fp32 VALU issue capacity: 128 lanes per CU per clock for ordinary (not
+# packed) fp32 instructions on gfx950, i.e. the published 157.3 TFLOP/s fp32
+# vector peak with an FMA counted as 2 flops.
+VALU_LANES_PER_CU_CLK = 128
+VALU_SLOTS_PER_S = N_CU * VALU_LANES_PER_CU_CLK * CLOCK_GHZ * 1e9   # 7.86e13
+FP32_VECTOR_TFLOPS = 2 * VALU_SLOTS_PER_S / 1e12                    # 157.3
 BF16_MFMA_TFLOPS = 2500.0
-# Issue cost of one v_exp_f32 / v_rcp_f32 in full-rate VALU slots on gfx950
-# (measured: see the exp-rate probe summary under profiles/).
-TRANS_SLOTS = 2.0
+# Issue cost of one v_exp_f32 / v_rcp_f32 in full-rate VALU slots on gfx950:
+# the transcendental rate is a quarter of the fp32 rate (measured; see the
+# VALU-rate probe summary under profiles/).
+TRANS_SLOTS = 4.0
 
 HEADLINE = "large_channel_4x5120x4096_bf16"
 
@@ -149,8 +153,8 @@ def main():
     t_hbm = mbytes / (HBM_PEAK_GBS * 1e9)
     t_alu = slots / VALU_SLOTS_PER_S
     if t_alu >= t_hbm:
-        roof = {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(FP32_NONPACKED_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_NONPACKED_TFLOPS, 4)}
+        roof = {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(FP32_VECTOR_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_VECTOR_TFLOPS, 4)}
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}

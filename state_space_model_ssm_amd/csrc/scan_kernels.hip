@@ -35,6 +35,16 @@
 
 #include "ssm_internal.h"
 
+#ifndef SCAN_PAIRSUM
+#define SCAN_PAIRSUM 0
+#endif
+#ifndef SCAN_HOIST
+#define SCAN_HOIST 1
+#endif
+#ifndef SCAN_WPE
+#define SCAN_WPE 0
+#endif
+
 namespace ssm {
 namespace {
 
@@ -67,8 +77,13 @@ __device__ __forceinline__ float silu(float z) {
 // into the consuming VOP2 instruction (v_mul_f32_dpp ... row_newbcast:J).
 template <int J>
 __device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J,
-                                                               0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
+}
+
+// Value of lane (i + 8) mod 16 of this lane's row (DPP row_ror:8), folded into
+// the consuming add.
+__device__ __forceinline__ float row_swap8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
 }
 
 // One step of the recurrence on the DPP path: dt and w come from lane J of
@@ -90,6 +105,15 @@ __device__ __forceinline__ void dpp_group(float dl16, float w16, float a2, const
   dpp_step<4 * G + 1, SUMMARY>(dl16, w16, a2, b4.v[1], c4.v[1], h, prod, pr.v[1]);
   dpp_step<4 * G + 2, SUMMARY>(dl16, w16, a2, b4.v[2], c4.v[2], h, prod, pr.v[2]);
   dpp_step<4 * G + 3, SUMMARY>(dl16, w16, a2, b4.v[3], c4.v[3], h, prod, pr.v[3]);
+}
+
+// Decays and input terms of a whole 16-step block, computed ahead of the
+// serial state updates so the transcendental latency overlaps.
+template <int... J>
+__device__ __forceinline__ void dpp_coeffs(float dl16, float w16, float a2, const F4 *b4, float *av,
+                                           float *bx, std::integer_sequence<int, J...>) {
+  ((av[J] = fast_exp2(row_bcast<J>(dl16) * a2)), ...);
+  ((bx[J] = row_bcast<J>(w16) * b4[J / 4].v[J % 4]), ...);
 }
 
 // Unpack one 16-byte vector of VEC storage elements into floats.
@@ -143,6 +167,10 @@ struct TileCfg {
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
   static constexpr int EPT = (CH * T + 255) / 256;               // epilogue elements / thread
   static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
+  // Readout partials per (channel, step) kept in LDS: on the DPP path lanes
+  // n and n+8 of a row first add their products, so half as many.
+  static constexpr bool kPairSum = kDpp && SCAN_PAIRSUM;
+  static constexpr int NP = kPairSum ? N / 2 : N;
 };
 
 // One block's view of the tensors and its fixed index math.
@@ -167,12 +195,17 @@ struct TileRegs {
   uint32_t z[Bk::EPT];   // raw storage bits of z; converted in the epilogue
 };
 
+#if SCAN_WPE > 0
+#define SCAN_KERNEL_ATTRS __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SCAN_WPE, SCAN_WPE)))
+#else
+#define SCAN_KERNEL_ATTRS __launch_bounds__(256)
+#endif
 template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z>
-__global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
+__global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
-  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT;
+  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT, NP = Cfg::NP;
   constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
   constexpr bool kDpp = Cfg::kDpp;
   static_assert(T % 4 == 0 && TP % 4 == 0 && (!kDpp || T % 16 == 0), "tile shape");
@@ -184,7 +217,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   __shared__ F4 sDu4[SUMMARY ? 1 : 2 * CH * TP / 4];
   __shared__ F4 sB4[N * TP / 4];
   __shared__ F4 sC4[SUMMARY ? 1 : N * TP / 4];
-  __shared__ F4 sP4[SUMMARY ? 1 : 256 * TP / 4];
+  __shared__ F4 sP4[SUMMARY ? 1 : CH * NP * TP / 4];
   float *sDl = sDl4[0].v, *sW = sW4[0].v, *sDu = sDu4[0].v;
   float *sP = sP4[0].v;
 
@@ -353,20 +386,44 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
         const float dl16 = sDl[chl * TP + blk16 * 16 + j];
         const float w16 = sW[chl * TP + blk16 * 16 + j];
         const int tb = blk16 * 16;
-        const int prow = ((chl * N + n) * TP + tb) / 4;
+        const int prow = ((chl * NP + (Cfg::kPairSum ? (n / 16) * 8 + j : n)) * TP + tb) / 4;
         F4 b4[4], c4[4], pr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           b4[q] = sB4[(n * TP + tb) / 4 + q];
           c4[q] = SUMMARY ? F4{} : sC4[(n * TP + tb) / 4 + q];
         }
-        dpp_group<0, SUMMARY>(dl16, w16, a2, b4[0], c4[0], pr[0], h, prod);
-        dpp_group<1, SUMMARY>(dl16, w16, a2, b4[1], c4[1], pr[1], h, prod);
-        dpp_group<2, SUMMARY>(dl16, w16, a2, b4[2], c4[2], pr[2], h, prod);
-        dpp_group<3, SUMMARY>(dl16, w16, a2, b4[3], c4[3], pr[3], h, prod);
-        if constexpr (!SUMMARY) {
+        if constexpr (SCAN_HOIST) {
+          float av[16], bx[16];
+          dpp_coeffs(dl16, w16, a2, b4, av, bx, std::make_integer_sequence<int, 16>{});
 #pragma unroll
-          for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
+          for (int i = 0; i < 16; ++i) {
+            h = fmaf(av[i], h, bx[i]);
+            if constexpr (SUMMARY) prod *= av[i];
+            else pr[i / 4].v[i % 4] = c4[i / 4].v[i % 4] * h;
+          }
+        } else {
+          dpp_group<0, SUMMARY>(dl16, w16, a2, b4[0], c4[0], pr[0], h, prod);
+          dpp_group<1, SUMMARY>(dl16, w16, a2, b4[1], c4[1], pr[1], h, prod);
+          dpp_group<2, SUMMARY>(dl16, w16, a2, b4[2], c4[2], pr[2], h, prod);
+          dpp_group<3, SUMMARY>(dl16, w16, a2, b4[3], c4[3], pr[3], h, prod);
+        }
+        if constexpr (!SUMMARY) {
+          if constexpr (Cfg::kPairSum) {
+            // Pair sums over lanes (n, n+8) of the row; lanes 0..7 store them.
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pr[q].v[i] += row_swap8(pr[q].v[i]);
+            }
+            if (j < 8) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
+          }
         }
       }
     } else {
@@ -406,10 +463,10 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         if (eact[e] && t0 + ecol[e] < t_end) {
-          const float *pp = sP + erow[e] * N * TP + ecol[e];
+          const float *pp = sP + erow[e] * NP * TP + ecol[e];
           float s = 0.0f;
 #pragma unroll
-          for (int nn = 0; nn < N; ++nn) s += pp[nn * TP];
+          for (int nn = 0; nn < NP; ++nn) s += pp[nn * TP];
           float yv = s + sDu[par * CH * TP + erow[e] * TP + ecol[e]];
           if constexpr (has_z) yv *= silu(from_raw(zz[e], gz));
           st(gy, ebase[e] + t0 + ecol[e], yv);

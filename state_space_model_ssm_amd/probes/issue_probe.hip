@@ -52,6 +52,48 @@ __global__ void lds_kernel(float *out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = (float)acc;
 }
 
+
+// Throughput of DPP-modified VALU ops: v_mul_f32 with a row_newbcast (or
+// row_ror:8) source, against the same loop without DPP.
+template <int CTRL, bool USE_DPP>
+__global__ void dpp_kernel(float *out, int iters) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 1.0f + 0.001f * (threadIdx.x + j);
+  const float s = 0.9999f + 1e-7f * threadIdx.x;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float src = v[(j + 1) & 7];
+      if (USE_DPP)
+        src = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, 0xF, 0xF, false));
+      v[j] = src * s;
+    }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc += v[j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+template <int CTRL, bool USE_DPP>
+int run_dpp(float *dout, int blocks, int iters, const char *name) {
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return 1;
+  float ms = 0.f;
+  for (int rep = 0; rep < 2; ++rep) {
+    (void)hipEventRecord(e0, 0);
+    hipLaunchKernelGGL((dpp_kernel<CTRL, USE_DPP>), dim3(blocks), dim3(256), 0, 0, dout, iters);
+    if (hipGetLastError() != hipSuccess) return 1;
+    (void)hipEventRecord(e1, 0);
+    (void)hipEventSynchronize(e1);
+    (void)hipEventElapsedTime(&ms, e0, e1);
+  }
+  const double ops = (double)blocks * 256 * iters * 8;
+  printf("%-28s %.3f ms, %.2f T ops/s (%.0f%% of 78.6)\n", name, ms, ops / ms / 1e9, 100.0 * ops / ms / 1e9 / 78.64);
+  return 0;
+}
+
 #define CK(x) do { hipError_t e = (x); if (e != hipSuccess) { printf("HIP error %s line %d\n", hipGetErrorString(e), __LINE__); return 1; } } while (0)
 
 template <int ILP, bool EXP>
@@ -110,6 +152,9 @@ int main() {
   run_valu<4, true>(dout, 256, it / 2, ncu);
   run_valu<4, true>(dout, 512, it / 2, ncu);
   run_valu<8, true>(dout, 256, it / 2, ncu);
+  run_dpp<0x150, false>(dout, ncu * 16, 4096, "v_mul_f32 (no dpp)");
+  run_dpp<0x155, true>(dout, ncu * 16, 4096, "v_mul_f32_dpp row_newbcast");
+  run_dpp<0x128, true>(dout, ncu * 16, 4096, "v_mul_f32_dpp row_ror:8");
   run_lds<true>(dout, ncu * 8, 256, 1024);
   run_lds<false>(dout, ncu * 8, 256, 1024);
   return 0;
