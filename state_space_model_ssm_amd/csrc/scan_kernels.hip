@@ -67,6 +67,17 @@ __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
 }
 
+// Two consecutive elements in one store (the address is 4-byte aligned for
+// bf16, 8-byte for float32: rows of even length from an aligned base).
+__device__ __forceinline__ void st2(float *p, int64_t i, float a, float b) {
+  *reinterpret_cast<float2 *>(p + i) = make_float2(a, b);
+}
+__device__ __forceinline__ void st2(uint16_t *p, int64_t i, float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
+  const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
+  *reinterpret_cast<uint32_t *>(p + i) = lo | (hi << 16);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float silu(float z) {
@@ -165,7 +176,7 @@ struct TileCfg {
   static constexpr int CH = 256 / N;                             // channels per block
   static constexpr int T = N >= 4 ? 32 : (N == 2 ? 16 : 8);      // time steps per tile
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
-  static constexpr int EPT = (CH * T + 255) / 256;               // epilogue elements / thread
+  static constexpr int EPP = (CH * T / 2 + 255) / 256;           // epilogue step pairs / thread
   static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
   // Readout partials per (channel, step) kept in LDS: on the DPP path lanes
   // n and n+8 of a row first add their products, so half as many.
@@ -177,7 +188,7 @@ struct TileCfg {
 template <typename Tin, int N, bool SUMMARY>
 struct Block {
   using Cfg = TileCfg<N>;
-  static constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT;
+  static constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPP = Cfg::EPP;
   static constexpr int VEC = Vec<Tin>::kN;          // storage elements per 16-byte vector
   static constexpr int SEG = (T + VEC - 1) / VEC;   // vectors per tile row
   static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
@@ -192,7 +203,7 @@ struct TileRegs {
   using Bk = Block<Tin, N, SUMMARY>;
   uint4 a[Bk::JPT];   // dt segment, or B segment
   uint4 b[Bk::JPT];   // u segment, or C segment
-  uint32_t z[Bk::EPT];   // raw storage bits of z; converted in the epilogue
+  uint32_t z[2 * Bk::EPP];   // raw storage bits of z; converted in the epilogue
 };
 
 #if SCAN_WPE > 0
@@ -205,7 +216,7 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
-  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPT = Cfg::EPT, NP = Cfg::NP;
+  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPP = Cfg::EPP, NP = Cfg::NP;
   constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
   constexpr bool kDpp = Cfg::kDpp;
   static_assert(T % 4 == 0 && TP % 4 == 0 && (!kDpp || T % 16 == 0), "tile shape");
@@ -296,15 +307,19 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
     }
   }
   // ---- epilogue element map: element k of this thread is (row, col) of the tile
-  int erow[EPT], ecol[EPT];
-  bool eact[EPT];
-  int64_t ebase[EPT];
+  // Epilogue map: pair k of this thread covers steps (ecol, ecol + 1) of
+  // channel row erow of the tile.
+  int erow[EPP], ecol[EPP], eoff[EPP];
+  bool eact[EPP];
+  int64_t ebase[EPP];
 #pragma unroll
-  for (int k = 0; k < EPT; ++k) {
-    const int e = tid + 256 * k;
-    erow[k] = e / T;
-    ecol[k] = e % T;
-    eact[k] = e < CH * T && erow[k] < nvalid;
+  for (int k = 0; k < EPP; ++k) {
+    const int q = tid + 256 * k;
+    erow[k] = q / (T / 2);
+    ecol[k] = 2 * (q % (T / 2));
+    eact[k] = q < CH * T / 2 && erow[k] < nvalid;
+    const int r = q < CH * T / 2 ? erow[k] : 0;  // LDS row read (in range for every thread)
+    eoff[k] = r * TP + ecol[k];
     ebase[k] = (b * p.dim + d0 + (eact[k] ? erow[k] : 0)) * L;
   }
 
@@ -325,7 +340,10 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
     }
     if constexpr (has_z) {
 #pragma unroll
-      for (int k = 0; k < EPT; ++k) R.z[k] = raw(gz, ebase[k] + t0 + ecol[k]);
+      for (int k = 0; k < EPP; ++k) {
+        R.z[2 * k] = raw(gz, ebase[k] + t0 + ecol[k]);
+        R.z[2 * k + 1] = raw(gz, ebase[k] + t0 + ecol[k] + 1);
+      }
     }
   };
 
@@ -340,10 +358,12 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-      R.z[k] = 0u;
+    for (int k = 0; k < EPP; ++k) {
+      R.z[2 * k] = 0u;
+      R.z[2 * k + 1] = 0u;
       if constexpr (has_z) {
-        if (t0 + ecol[k] < t_end) R.z[k] = raw(gz, ebase[k] + t0 + ecol[k]);
+        if (t0 + ecol[k] < t_end) R.z[2 * k] = raw(gz, ebase[k] + t0 + ecol[k]);
+        if (t0 + ecol[k] + 1 < t_end) R.z[2 * k + 1] = raw(gz, ebase[k] + t0 + ecol[k] + 1);
       }
     }
   };
@@ -450,9 +470,9 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
   // tile DEPTH ahead on the fast path.
   auto do_tile = [&](Regs &R, int ti, bool pf) __attribute__((always_inline)) {
     const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
-    uint32_t zz[EPT];
+    uint32_t zz[2 * EPP];
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) zz[e] = R.z[e];
+    for (int e = 0; e < 2 * EPP; ++e) zz[e] = R.z[e];
     const int par = ti & 1;
     stage(R, par);
     __syncthreads();
@@ -460,16 +480,37 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
     recur();
     __syncthreads();
     if constexpr (!SUMMARY) {
+      // Sum the NP partials of two consecutive steps (pairwise tree), add the
+      // D skip, gate, store.  LDS reads are unconditional (in range for every
+      // thread); only the stores depend on the element being live.
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        if (eact[e] && t0 + ecol[e] < t_end) {
-          const float *pp = sP + erow[e] * NP * TP + ecol[e];
-          float s = 0.0f;
+      for (int k = 0; k < EPP; ++k) {
+        float2 v[NP];
 #pragma unroll
-          for (int nn = 0; nn < NP; ++nn) s += pp[nn * TP];
-          float yv = s + sDu[par * CH * TP + erow[e] * TP + ecol[e]];
-          if constexpr (has_z) yv *= silu(from_raw(zz[e], gz));
-          st(gy, ebase[e] + t0 + ecol[e], yv);
+        for (int nn = 0; nn < NP; ++nn)
+          v[nn] = *reinterpret_cast<const float2 *>(sP + (eoff[k] / TP) * NP * TP + nn * TP + ecol[k]);
+#pragma unroll
+        for (int w = NP / 2; w >= 1; w /= 2) {
+#pragma unroll
+          for (int i = 0; i < w; ++i) {
+            v[i].x += v[i + w].x;
+            v[i].y += v[i + w].y;
+          }
+        }
+        const float2 du = *reinterpret_cast<const float2 *>(sDu + par * CH * TP + eoff[k]);
+        float y0 = v[0].x + du.x, y1 = v[0].y + du.y;
+        if constexpr (has_z) {
+          y0 *= silu(from_raw(zz[2 * k], gz));
+          y1 *= silu(from_raw(zz[2 * k + 1], gz));
+        }
+        if (eact[k]) {
+          const int64_t o = ebase[k] + t0 + ecol[k];
+          if (vec_ok && t0 + ecol[k] + 1 < t_end) {
+            st2(gy, o, y0, y1);
+          } else {
+            if (t0 + ecol[k] < t_end) st(gy, o, y0);
+            if (t0 + ecol[k] + 1 < t_end) st(gy, o + 1, y1);
+          }
         }
       }
     }
