@@ -35,16 +35,6 @@
 
 #include "ssm_internal.h"
 
-#ifndef SCAN_PAIRSUM
-#define SCAN_PAIRSUM 0
-#endif
-#ifndef SCAN_HOIST
-#define SCAN_HOIST 1
-#endif
-#ifndef SCAN_WPE
-#define SCAN_WPE 0
-#endif
-
 namespace ssm {
 namespace {
 
@@ -67,17 +57,6 @@ __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
 }
 
-// Two consecutive elements in one store (the address is 4-byte aligned for
-// bf16, 8-byte for float32: rows of even length from an aligned base).
-__device__ __forceinline__ void st2(float *p, int64_t i, float a, float b) {
-  *reinterpret_cast<float2 *>(p + i) = make_float2(a, b);
-}
-__device__ __forceinline__ void st2(uint16_t *p, int64_t i, float a, float b) {
-  const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
-  const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(b));
-  *reinterpret_cast<uint32_t *>(p + i) = lo | (hi << 16);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float silu(float z) {
@@ -89,33 +68,6 @@ __device__ __forceinline__ float silu(float z) {
 template <int J>
 __device__ __forceinline__ float row_bcast(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
-}
-
-// Value of lane (i + 8) mod 16 of this lane's row (DPP row_ror:8), folded into
-// the consuming add.
-__device__ __forceinline__ float row_swap8(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, true));
-}
-
-// One step of the recurrence on the DPP path: dt and w come from lane J of
-// the row (step J of the current 16-step block).
-template <int J, bool SUMMARY>
-__device__ __forceinline__ void dpp_step(float dl16, float w16, float a2, float bv, float cv, float &h,
-                                         float &prod, float &pr) {
-  const float a = fast_exp2(row_bcast<J>(dl16) * a2);
-  h = fmaf(a, h, row_bcast<J>(w16) * bv);
-  if constexpr (SUMMARY) prod *= a;
-  else pr = cv * h;
-}
-
-// Steps 4G .. 4G+3 of a 16-step block.
-template <int G, bool SUMMARY>
-__device__ __forceinline__ void dpp_group(float dl16, float w16, float a2, const F4 &b4, const F4 &c4,
-                                          F4 &pr, float &h, float &prod) {
-  dpp_step<4 * G + 0, SUMMARY>(dl16, w16, a2, b4.v[0], c4.v[0], h, prod, pr.v[0]);
-  dpp_step<4 * G + 1, SUMMARY>(dl16, w16, a2, b4.v[1], c4.v[1], h, prod, pr.v[1]);
-  dpp_step<4 * G + 2, SUMMARY>(dl16, w16, a2, b4.v[2], c4.v[2], h, prod, pr.v[2]);
-  dpp_step<4 * G + 3, SUMMARY>(dl16, w16, a2, b4.v[3], c4.v[3], h, prod, pr.v[3]);
 }
 
 // Decays and input terms of a whole 16-step block, computed ahead of the
@@ -174,21 +126,25 @@ __device__ __forceinline__ uint4 load_seg_tail(const uint16_t *row, int64_t t, i
 template <int N>
 struct TileCfg {
   static constexpr int CH = 256 / N;                             // channels per block
+  static constexpr int CPW = 64 / N;                             // channels per wavefront
   static constexpr int T = N >= 4 ? 32 : (N == 2 ? 16 : 8);      // time steps per tile
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
-  static constexpr int EPP = (CH * T / 2 + 255) / 256;           // epilogue step pairs / thread
+  static constexpr int BS = T < 16 ? T : 16;                     // steps per readout block
+  static constexpr int NB = T / BS;                              // readout blocks per tile
+  static constexpr int OPL = (CPW * BS + 63) / 64;               // readout outputs per lane per block
+  static constexpr int SP_TP = BS + 4;                           // partials of one state (floats)
   static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
-  // Readout partials per (channel, step) kept in LDS: on the DPP path lanes
-  // n and n+8 of a row first add their products, so half as many.
-  static constexpr bool kPairSum = kDpp && SCAN_PAIRSUM;
-  static constexpr int NP = kPairSum ? N / 2 : N;
+  // LDS stride between the partial rows of two channels.  On the DPP path the
+  // readout's 64 lanes read 64 / 16 channel rows of 16 steps each; a stride of
+  // 16 (mod 64 banks) puts them on disjoint banks.
+  static constexpr int PRS = N * SP_TP + (kDpp ? ((16 - (N * SP_TP) % 64) % 64 + 64) % 64 : 0);
 };
 
 // One block's view of the tensors and its fixed index math.
 template <typename Tin, int N, bool SUMMARY>
 struct Block {
   using Cfg = TileCfg<N>;
-  static constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPP = Cfg::EPP;
+  static constexpr int CH = Cfg::CH, T = Cfg::T;
   static constexpr int VEC = Vec<Tin>::kN;          // storage elements per 16-byte vector
   static constexpr int SEG = (T + VEC - 1) / VEC;   // vectors per tile row
   static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
@@ -200,35 +156,41 @@ struct Block {
 // Registers holding one tile's global data between its load and its staging.
 template <typename Tin, int N, bool SUMMARY>
 struct TileRegs {
+  using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
-  uint4 a[Bk::JPT];   // dt segment, or B segment
-  uint4 b[Bk::JPT];   // u segment, or C segment
-  uint32_t z[2 * Bk::EPP];   // raw storage bits of z; converted in the epilogue
+  uint4 a[Bk::JPT];                  // dt segment, or B segment
+  uint4 b[Bk::JPT];                  // u segment, or C segment
+  uint32_t z[Cfg::NB * Cfg::OPL];    // raw storage bits of z; converted in the readout
 };
 
-#if SCAN_WPE > 0
-#define SCAN_KERNEL_ATTRS __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SCAN_WPE, SCAN_WPE)))
-#else
-#define SCAN_KERNEL_ATTRS __launch_bounds__(256)
-#endif
+// Orders this wavefront's LDS accesses: its earlier stores complete before
+// its later loads issue, and the compiler moves no LDS access across.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
 template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z>
-__global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
+__global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
-  constexpr int CH = Cfg::CH, T = Cfg::T, TP = Cfg::TP, EPP = Cfg::EPP, NP = Cfg::NP;
+  constexpr int CH = Cfg::CH, CPW = Cfg::CPW, T = Cfg::T, TP = Cfg::TP, BS = Cfg::BS, NB = Cfg::NB;
+  constexpr int OPL = Cfg::OPL, SP_TP = Cfg::SP_TP, PRS = Cfg::PRS;
   constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
   constexpr bool kDpp = Cfg::kDpp;
-  static_assert(T % 4 == 0 && TP % 4 == 0 && (!kDpp || T % 16 == 0), "tile shape");
+  static_assert(T % BS == 0 && BS % 4 == 0 && TP % 4 == 0 && SP_TP % 4 == 0 && PRS % 4 == 0, "tile shape");
+  static_assert(!kDpp || BS == 16, "DPP readout blocks are 16 steps");
 
-  __shared__ F4 sDl4[CH * TP / 4];
-  __shared__ F4 sW4[CH * TP / 4];
-  // D * u is read by the epilogue of tile i while tile i+1 is being staged,
-  // so it alternates between two buffers by tile parity.
+  // Staged inputs of a tile, double-buffered by tile parity: there is one
+  // barrier per tile, so a wavefront may stage tile i+1 while others still
+  // read tile i (never tile i-1, which the barrier of tile i has retired).
+  __shared__ F4 sDl4[2 * CH * TP / 4];
+  __shared__ F4 sW4[2 * CH * TP / 4];
   __shared__ F4 sDu4[SUMMARY ? 1 : 2 * CH * TP / 4];
-  __shared__ F4 sB4[N * TP / 4];
-  __shared__ F4 sC4[SUMMARY ? 1 : N * TP / 4];
-  __shared__ F4 sP4[SUMMARY ? 1 : CH * NP * TP / 4];
+  __shared__ F4 sB4[2 * N * TP / 4];
+  __shared__ F4 sC4[SUMMARY ? 1 : 2 * N * TP / 4];
+  // Readout partials C_t[n] h_t[n] of one BS-step block.  A channel's rows are
+  // written and read only by the wavefront that owns the channel.
+  __shared__ F4 sP4[SUMMARY ? 1 : CH * PRS / 4];
   float *sDl = sDl4[0].v, *sW = sW4[0].v, *sDu = sDu4[0].v;
   float *sP = sP4[0].v;
 
@@ -244,6 +206,8 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
   const int tid = threadIdx.x;
   const int n = tid % N;
   const int chl = tid / N;
+  const int lane = tid % 64;
+  const int wave = tid / 64;
 
   int64_t blk = blockIdx.x;
   const int64_t tile = blk % p.tiles_per_group;
@@ -306,20 +270,19 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
       jsrc2[k] = gC;
     }
   }
-  // ---- epilogue element map: element k of this thread is (row, col) of the tile
-  // Epilogue map: pair k of this thread covers steps (ecol, ecol + 1) of
-  // channel row erow of the tile.
-  int erow[EPP], ecol[EPP], eoff[EPP];
-  bool eact[EPP];
-  int64_t ebase[EPP];
+
+  // ---- readout map: output k of this lane in a BS-step block is step ej[k]
+  // of channel row erow[k], one of this wavefront's CPW rows.
+  int erow[OPL], ej[OPL];
+  bool eact[OPL];
+  int64_t ebase[OPL];
 #pragma unroll
-  for (int k = 0; k < EPP; ++k) {
-    const int q = tid + 256 * k;
-    erow[k] = q / (T / 2);
-    ecol[k] = 2 * (q % (T / 2));
-    eact[k] = q < CH * T / 2 && erow[k] < nvalid;
-    const int r = q < CH * T / 2 ? erow[k] : 0;  // LDS row read (in range for every thread)
-    eoff[k] = r * TP + ecol[k];
+  for (int k = 0; k < OPL; ++k) {
+    const int o = lane + 64 * k;
+    const bool live = o < CPW * BS;
+    erow[k] = wave * CPW + (live ? o / BS : 0);  // an LDS row of this wave for every lane
+    ej[k] = o % BS;
+    eact[k] = live && erow[k] < nvalid;
     ebase[k] = (b * p.dim + d0 + (eact[k] ? erow[k] : 0)) * L;
   }
 
@@ -340,9 +303,9 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
     }
     if constexpr (has_z) {
 #pragma unroll
-      for (int k = 0; k < EPP; ++k) {
-        R.z[2 * k] = raw(gz, ebase[k] + t0 + ecol[k]);
-        R.z[2 * k + 1] = raw(gz, ebase[k] + t0 + ecol[k] + 1);
+      for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+        for (int k = 0; k < OPL; ++k) R.z[bb * OPL + k] = raw(gz, ebase[k] + t0 + bb * BS + ej[k]);
       }
     }
   };
@@ -358,12 +321,14 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < EPP; ++k) {
-      R.z[2 * k] = 0u;
-      R.z[2 * k + 1] = 0u;
-      if constexpr (has_z) {
-        if (t0 + ecol[k] < t_end) R.z[2 * k] = raw(gz, ebase[k] + t0 + ecol[k]);
-        if (t0 + ecol[k] + 1 < t_end) R.z[2 * k + 1] = raw(gz, ebase[k] + t0 + ecol[k] + 1);
+    for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+      for (int k = 0; k < OPL; ++k) {
+        R.z[bb * OPL + k] = 0u;
+        if constexpr (has_z) {
+          const int64_t t = t0 + bb * BS + ej[k];
+          if (t < t_end) R.z[bb * OPL + k] = raw(gz, ebase[k] + t);
+        }
       }
     }
   };
@@ -377,82 +342,62 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
       Vec<Tin>::unpack(R.b[k], vb);
       const int o = jrow[k] * TP + jcol[k];
       if (jkind[k] == 0) {
+        const int ob = par * CH * TP + o;
 #pragma unroll
         for (int i = 0; i < VEC; i += 4) {
-          sDl4[(o + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
-          sW4[(o + i) / 4] = F4{{va[i] * vb[i], va[i + 1] * vb[i + 1], va[i + 2] * vb[i + 2], va[i + 3] * vb[i + 3]}};
+          sDl4[(ob + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
+          sW4[(ob + i) / 4] = F4{{va[i] * vb[i], va[i + 1] * vb[i + 1], va[i + 2] * vb[i + 2], va[i + 3] * vb[i + 3]}};
           if (!SUMMARY) {
             const float dk = jdsk[k];
-            sDu4[par * (CH * TP / 4) + (o + i) / 4] = F4{{dk * vb[i], dk * vb[i + 1], dk * vb[i + 2], dk * vb[i + 3]}};
+            sDu4[(ob + i) / 4] = F4{{dk * vb[i], dk * vb[i + 1], dk * vb[i + 2], dk * vb[i + 3]}};
           }
         }
       } else {
+        const int ob = par * N * TP + o;
 #pragma unroll
         for (int i = 0; i < VEC; i += 4) {
-          sB4[(o + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
-          if (!SUMMARY) sC4[(o + i) / 4] = F4{{vb[i], vb[i + 1], vb[i + 2], vb[i + 3]}};
+          sB4[(ob + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
+          if (!SUMMARY) sC4[(ob + i) / 4] = F4{{vb[i], vb[i + 1], vb[i + 2], vb[i + 3]}};
         }
       }
     }
   };
 
-  // T steps of the recurrence for this thread's (channel, state); the readout
-  // partials C_t[n] h_t[n] go to LDS.
-  auto recur = [&]() __attribute__((always_inline)) {
+  // Steps blk*BS .. blk*BS+BS-1 of the tile staged in buffer `par` for this
+  // thread's (channel, state); the readout partials go to LDS.
+  auto recur_block = [&](int par, int blk) __attribute__((always_inline)) {
+    const int tb = blk * BS;
+    const int dbase = par * CH * TP + chl * TP + tb;
+    const int bbase = par * N * TP + n * TP + tb;
     if constexpr (kDpp) {
       const int j = tid % 16;
+      const float dl16 = sDl[dbase + j];
+      const float w16 = sW[dbase + j];
+      F4 b4[4], c4[4], pr[4];
 #pragma unroll
-      for (int blk16 = 0; blk16 < T / 16; ++blk16) {
-        const float dl16 = sDl[chl * TP + blk16 * 16 + j];
-        const float w16 = sW[chl * TP + blk16 * 16 + j];
-        const int tb = blk16 * 16;
-        const int prow = ((chl * NP + (Cfg::kPairSum ? (n / 16) * 8 + j : n)) * TP + tb) / 4;
-        F4 b4[4], c4[4], pr[4];
+      for (int q = 0; q < 4; ++q) {
+        b4[q] = sB4[bbase / 4 + q];
+        c4[q] = SUMMARY ? F4{} : sC4[bbase / 4 + q];
+      }
+      float av[16], bx[16];
+      dpp_coeffs(dl16, w16, a2, b4, av, bx, std::make_integer_sequence<int, 16>{});
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          b4[q] = sB4[(n * TP + tb) / 4 + q];
-          c4[q] = SUMMARY ? F4{} : sC4[(n * TP + tb) / 4 + q];
-        }
-        if constexpr (SCAN_HOIST) {
-          float av[16], bx[16];
-          dpp_coeffs(dl16, w16, a2, b4, av, bx, std::make_integer_sequence<int, 16>{});
+      for (int i = 0; i < 16; ++i) {
+        h = fmaf(av[i], h, bx[i]);
+        if constexpr (SUMMARY) prod *= av[i];
+        else pr[i / 4].v[i % 4] = c4[i / 4].v[i % 4] * h;
+      }
+      if constexpr (!SUMMARY) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            h = fmaf(av[i], h, bx[i]);
-            if constexpr (SUMMARY) prod *= av[i];
-            else pr[i / 4].v[i % 4] = c4[i / 4].v[i % 4] * h;
-          }
-        } else {
-          dpp_group<0, SUMMARY>(dl16, w16, a2, b4[0], c4[0], pr[0], h, prod);
-          dpp_group<1, SUMMARY>(dl16, w16, a2, b4[1], c4[1], pr[1], h, prod);
-          dpp_group<2, SUMMARY>(dl16, w16, a2, b4[2], c4[2], pr[2], h, prod);
-          dpp_group<3, SUMMARY>(dl16, w16, a2, b4[3], c4[3], pr[3], h, prod);
-        }
-        if constexpr (!SUMMARY) {
-          if constexpr (Cfg::kPairSum) {
-            // Pair sums over lanes (n, n+8) of the row; lanes 0..7 store them.
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) pr[q].v[i] += row_swap8(pr[q].v[i]);
-            }
-            if (j < 8) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sP4[prow + q] = pr[q];
-          }
-        }
+        for (int q = 0; q < 4; ++q) sP4[(chl * PRS + n * SP_TP) / 4 + q] = pr[q];
       }
     } else {
 #pragma unroll
-      for (int tt = 0; tt < T; tt += 4) {
-        const F4 dl4 = sDl4[(chl * TP + tt) / 4];
-        const F4 w4 = sW4[(chl * TP + tt) / 4];
-        const F4 b4 = sB4[(n * TP + tt) / 4];
-        const F4 c4 = SUMMARY ? F4{} : sC4[(n * TP + tt) / 4];
+      for (int tt = 0; tt < BS; tt += 4) {
+        const F4 dl4 = sDl4[(dbase + tt) / 4];
+        const F4 w4 = sW4[(dbase + tt) / 4];
+        const F4 b4 = sB4[(bbase + tt) / 4];
+        const F4 c4 = SUMMARY ? F4{} : sC4[(bbase + tt) / 4];
         F4 pr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -461,57 +406,59 @@ __global__ void SCAN_KERNEL_ATTRS scan_chunk_kernel(const ScanParams p) {
           if constexpr (SUMMARY) prod *= a;
           else pr.v[i] = c4.v[i] * h;
         }
-        if constexpr (!SUMMARY) sP4[((chl * N + n) * TP + tt) / 4] = pr;
+        if constexpr (!SUMMARY) sP4[(chl * PRS + n * SP_TP + tt) / 4] = pr;
       }
     }
   };
 
-  // One tile: stage from registers, recur, epilogue.  `pf` refills R with the
-  // tile DEPTH ahead on the fast path.
+  // Readout of block blk: sum the N partials of each of this lane's outputs
+  // (pairwise, 16 at a time), add the D skip, gate, store.  LDS reads are
+  // unconditional (rows of this wave for every lane); only stores depend on
+  // the output being live.
+  auto readout_block = [&](int par, int blk, int64_t t0, const uint32_t *zz) __attribute__((always_inline)) {
+    constexpr int G = N < 16 ? N : 16;
+#pragma unroll
+    for (int k = 0; k < OPL; ++k) {
+      const float *row = sP + erow[k] * PRS + ej[k];
+      float acc = 0.0f;
+#pragma unroll
+      for (int g0 = 0; g0 < N; g0 += G) {
+        float v[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) v[i] = row[(g0 + i) * SP_TP];
+#pragma unroll
+        for (int w = G / 2; w >= 1; w /= 2) {
+#pragma unroll
+          for (int i = 0; i < w; ++i) v[i] += v[i + w];
+        }
+        acc = g0 == 0 ? v[0] : acc + v[0];
+      }
+      float y = acc + sDu[par * CH * TP + erow[k] * TP + blk * BS + ej[k]];
+      if constexpr (has_z) y *= silu(from_raw(zz[blk * OPL + k], gz));
+      const int64_t t = t0 + blk * BS + ej[k];
+      if (eact[k] && t < t_end) st(gy, ebase[k] + t, y);
+    }
+  };
+
+  // One tile: stage from registers, one barrier, then per readout block the
+  // recurrence and this wavefront's readout.  `pf` refills R with the tile
+  // DEPTH ahead on the fast path.
   auto do_tile = [&](Regs &R, int ti, bool pf) __attribute__((always_inline)) {
     const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
-    uint32_t zz[2 * EPP];
+    uint32_t zz[NB * OPL];
 #pragma unroll
-    for (int e = 0; e < 2 * EPP; ++e) zz[e] = R.z[e];
+    for (int e = 0; e < NB * OPL; ++e) zz[e] = R.z[e];
     const int par = ti & 1;
     stage(R, par);
     __syncthreads();
     if (pf && ti + DEPTH < nfast) prefetch_fast(R, ti + DEPTH);
-    recur();
-    __syncthreads();
-    if constexpr (!SUMMARY) {
-      // Sum the NP partials of two consecutive steps (pairwise tree), add the
-      // D skip, gate, store.  LDS reads are unconditional (in range for every
-      // thread); only the stores depend on the element being live.
 #pragma unroll
-      for (int k = 0; k < EPP; ++k) {
-        float2 v[NP];
-#pragma unroll
-        for (int nn = 0; nn < NP; ++nn)
-          v[nn] = *reinterpret_cast<const float2 *>(sP + (eoff[k] / TP) * NP * TP + nn * TP + ecol[k]);
-#pragma unroll
-        for (int w = NP / 2; w >= 1; w /= 2) {
-#pragma unroll
-          for (int i = 0; i < w; ++i) {
-            v[i].x += v[i + w].x;
-            v[i].y += v[i + w].y;
-          }
-        }
-        const float2 du = *reinterpret_cast<const float2 *>(sDu + par * CH * TP + eoff[k]);
-        float y0 = v[0].x + du.x, y1 = v[0].y + du.y;
-        if constexpr (has_z) {
-          y0 *= silu(from_raw(zz[2 * k], gz));
-          y1 *= silu(from_raw(zz[2 * k + 1], gz));
-        }
-        if (eact[k]) {
-          const int64_t o = ebase[k] + t0 + ecol[k];
-          if (vec_ok && t0 + ecol[k] + 1 < t_end) {
-            st2(gy, o, y0, y1);
-          } else {
-            if (t0 + ecol[k] < t_end) st(gy, o, y0);
-            if (t0 + ecol[k] + 1 < t_end) st(gy, o + 1, y1);
-          }
-        }
+    for (int bb = 0; bb < NB; ++bb) {
+      recur_block(par, bb);
+      if constexpr (!SUMMARY) {
+        wave_lds_sync();
+        readout_block(par, bb, t0, zz);
+        compiler_fence();
       }
     }
   };
