@@ -132,12 +132,15 @@ struct TileCfg {
   static constexpr int BS = T < 16 ? T : 16;                     // steps per readout block
   static constexpr int NB = T / BS;                              // readout blocks per tile
   static constexpr int OPL = (CPW * BS + 63) / 64;               // readout outputs per lane per block
-  static constexpr int SP_TP = BS + 4;                           // partials of one state (floats)
   static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
-  // LDS stride between the partial rows of two channels.  On the DPP path the
-  // readout's 64 lanes read 64 / 16 channel rows of 16 steps each; a stride of
-  // 16 (mod 64 banks) puts them on disjoint banks.
-  static constexpr int PRS = N * SP_TP + (kDpp ? ((16 - (N * SP_TP) % 64) % 64 + 64) % 64 : 0);
+  // Readout partials of a block live as [channel][step][state]: JS floats per
+  // step (the N states, padded to keep 16-byte rows on distinct banks), RS per
+  // channel.  A recurrence store (one step, lanes over states) then hits
+  // consecutive banks, and RS = min(N, 64) (mod 64) keeps the channel rows a
+  // wavefront stores at once on disjoint banks.
+  static constexpr int JS = N >= 4 ? N + 4 : N;
+  static constexpr int RS_ALIGN = N >= 4 ? (N < 64 ? N : 0) : 4;
+  static constexpr int RS = BS * JS + ((RS_ALIGN - (BS * JS) % 64) % 64 + 64) % 64;
 };
 
 // One block's view of the tensors and its fixed index math.
@@ -163,10 +166,34 @@ struct TileRegs {
   uint32_t z[Cfg::NB * Cfg::OPL];    // raw storage bits of z; converted in the readout
 };
 
-// Orders this wavefront's LDS accesses: its earlier stores complete before
-// its later loads issue, and the compiler moves no LDS access across.
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+#ifndef SCAN_WSYNC
+#define SCAN_WSYNC 1
+#endif
+#ifndef SCAN_PIPE
+#define SCAN_PIPE 1
+#endif
+
+// Orders this wavefront's LDS accesses across lanes.  LDS instructions of one
+// wavefront execute in issue order, so a later load sees an earlier store of
+// any lane of the same wavefront; the fences keep the compiler from moving
+// LDS accesses across.
+__device__ __forceinline__ void wave_lds_sync() {
+#if SCAN_WSYNC
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#else
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
+}
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Operands of one 16-step block on the DPP path: dt and w of step j (lane j
+// of the row), and B, C of this lane's state for the 16 steps.
+struct DppOps {
+  float dl16, w16;
+  F4 b4[4], c4[4];
+};
 
 template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z>
 __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
@@ -174,10 +201,10 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
   constexpr int CH = Cfg::CH, CPW = Cfg::CPW, T = Cfg::T, TP = Cfg::TP, BS = Cfg::BS, NB = Cfg::NB;
-  constexpr int OPL = Cfg::OPL, SP_TP = Cfg::SP_TP, PRS = Cfg::PRS;
+  constexpr int OPL = Cfg::OPL, JS = Cfg::JS, RS = Cfg::RS;
   constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
   constexpr bool kDpp = Cfg::kDpp;
-  static_assert(T % BS == 0 && BS % 4 == 0 && TP % 4 == 0 && SP_TP % 4 == 0 && PRS % 4 == 0, "tile shape");
+  static_assert(T % BS == 0 && BS % 4 == 0 && TP % 4 == 0 && RS % 4 == 0, "tile shape");
   static_assert(!kDpp || BS == 16, "DPP readout blocks are 16 steps");
 
   // Staged inputs of a tile, double-buffered by tile parity: there is one
@@ -190,7 +217,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   __shared__ F4 sC4[SUMMARY ? 1 : 2 * N * TP / 4];
   // Readout partials C_t[n] h_t[n] of one BS-step block.  A channel's rows are
   // written and read only by the wavefront that owns the channel.
-  __shared__ F4 sP4[SUMMARY ? 1 : CH * PRS / 4];
+  __shared__ F4 sP4[SUMMARY ? 1 : CH * RS / 4];
   float *sDl = sDl4[0].v, *sW = sW4[0].v, *sDu = sDu4[0].v;
   float *sP = sP4[0].v;
 
@@ -364,34 +391,46 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   };
 
   // Steps blk*BS .. blk*BS+BS-1 of the tile staged in buffer `par` for this
-  // thread's (channel, state); the readout partials go to LDS.
-  auto recur_block = [&](int par, int blk) __attribute__((always_inline)) {
+  // thread's (channel, state); the readout partials go to LDS.  On the DPP
+  // path the block's operands are loaded first (load_ops), so that they can be
+  // issued ahead of the previous block's readout.
+  auto load_ops = [&](int par, int blk, DppOps &o) __attribute__((always_inline)) {
     const int tb = blk * BS;
     const int dbase = par * CH * TP + chl * TP + tb;
     const int bbase = par * N * TP + n * TP + tb;
+    const int j = tid % 16;
+    o.dl16 = sDl[dbase + j];
+    o.w16 = sW[dbase + j];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o.b4[q] = sB4[bbase / 4 + q];
+      o.c4[q] = SUMMARY ? F4{} : sC4[bbase / 4 + q];
+    }
+  };
+  auto recur_ops = [&](const DppOps &o) __attribute__((always_inline)) {
+    F4 pr[4];
+    float av[16], bx[16];
+    dpp_coeffs(o.dl16, o.w16, a2, o.b4, av, bx, std::make_integer_sequence<int, 16>{});
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h = fmaf(av[i], h, bx[i]);
+      if constexpr (SUMMARY) prod *= av[i];
+      else pr[i / 4].v[i % 4] = o.c4[i / 4].v[i % 4] * h;
+    }
+    if constexpr (!SUMMARY) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sP[chl * RS + i * JS + n] = pr[i / 4].v[i % 4];
+    }
+  };
+  auto recur_block = [&](int par, int blk) __attribute__((always_inline)) {
     if constexpr (kDpp) {
-      const int j = tid % 16;
-      const float dl16 = sDl[dbase + j];
-      const float w16 = sW[dbase + j];
-      F4 b4[4], c4[4], pr[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        b4[q] = sB4[bbase / 4 + q];
-        c4[q] = SUMMARY ? F4{} : sC4[bbase / 4 + q];
-      }
-      float av[16], bx[16];
-      dpp_coeffs(dl16, w16, a2, b4, av, bx, std::make_integer_sequence<int, 16>{});
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        h = fmaf(av[i], h, bx[i]);
-        if constexpr (SUMMARY) prod *= av[i];
-        else pr[i / 4].v[i % 4] = c4[i / 4].v[i % 4] * h;
-      }
-      if constexpr (!SUMMARY) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sP4[(chl * PRS + n * SP_TP) / 4 + q] = pr[q];
-      }
+      DppOps o;
+      load_ops(par, blk, o);
+      recur_ops(o);
     } else {
+      const int tb = blk * BS;
+      const int dbase = par * CH * TP + chl * TP + tb;
+      const int bbase = par * N * TP + n * TP + tb;
 #pragma unroll
       for (int tt = 0; tt < BS; tt += 4) {
         const F4 dl4 = sDl4[(dbase + tt) / 4];
@@ -406,7 +445,10 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
           if constexpr (SUMMARY) prod *= a;
           else pr.v[i] = c4.v[i] * h;
         }
-        if constexpr (!SUMMARY) sP4[(chl * PRS + n * SP_TP + tt) / 4] = pr;
+        if constexpr (!SUMMARY) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sP[chl * RS + (tt + i) * JS + n] = pr.v[i];
+        }
       }
     }
   };
@@ -414,18 +456,40 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   // Readout of block blk: sum the N partials of each of this lane's outputs
   // (pairwise, 16 at a time), add the D skip, gate, store.  LDS reads are
   // unconditional (rows of this wave for every lane); only stores depend on
-  // the output being live.
-  auto readout_block = [&](int par, int blk, int64_t t0, const uint32_t *zz) __attribute__((always_inline)) {
+  // the output being live.  readout_load issues the LDS reads, readout_finish
+  // consumes them.
+  struct Partials {
+    float v[OPL][N];
+    float du[OPL];
+  };
+  auto readout_load = [&](int par, int blk, Partials &P) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < OPL; ++k) {
+      const float *row = sP + erow[k] * RS + ej[k] * JS;
+      if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+          const F4 v4 = *reinterpret_cast<const F4 *>(row + i);
+          P.v[k][i] = v4.v[0];
+          P.v[k][i + 1] = v4.v[1];
+          P.v[k][i + 2] = v4.v[2];
+          P.v[k][i + 3] = v4.v[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) P.v[k][i] = row[i];
+      }
+      P.du[k] = sDu[par * CH * TP + erow[k] * TP + blk * BS + ej[k]];
+    }
+  };
+  auto readout_finish = [&](int blk, int64_t t0, const uint32_t *zz, Partials &P) __attribute__((always_inline)) {
     constexpr int G = N < 16 ? N : 16;
 #pragma unroll
     for (int k = 0; k < OPL; ++k) {
-      const float *row = sP + erow[k] * PRS + ej[k];
       float acc = 0.0f;
 #pragma unroll
       for (int g0 = 0; g0 < N; g0 += G) {
-        float v[G];
-#pragma unroll
-        for (int i = 0; i < G; ++i) v[i] = row[(g0 + i) * SP_TP];
+        float *v = &P.v[k][g0];
 #pragma unroll
         for (int w = G / 2; w >= 1; w /= 2) {
 #pragma unroll
@@ -433,7 +497,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
         }
         acc = g0 == 0 ? v[0] : acc + v[0];
       }
-      float y = acc + sDu[par * CH * TP + erow[k] * TP + blk * BS + ej[k]];
+      float y = acc + P.du[k];
       if constexpr (has_z) y *= silu(from_raw(zz[blk * OPL + k], gz));
       const int64_t t = t0 + blk * BS + ej[k];
       if (eact[k] && t < t_end) st(gy, ebase[k] + t, y);
@@ -452,12 +516,32 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     stage(R, par);
     __syncthreads();
     if (pf && ti + DEPTH < nfast) prefetch_fast(R, ti + DEPTH);
+    if constexpr (SUMMARY) {
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      recur_block(par, bb);
-      if constexpr (!SUMMARY) {
+      for (int bb = 0; bb < NB; ++bb) recur_block(par, bb);
+    } else if constexpr (kDpp && SCAN_PIPE) {
+      // The next block's operands load between this block's partial reads
+      // and the sums that consume them.
+      DppOps o;
+      load_ops(par, 0, o);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        recur_ops(o);
         wave_lds_sync();
-        readout_block(par, bb, t0, zz);
+        Partials P;
+        readout_load(par, bb, P);
+        if (bb + 1 < NB) load_ops(par, bb + 1, o);
+        readout_finish(bb, t0, zz, P);
+        compiler_fence();
+      }
+    } else {
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        recur_block(par, bb);
+        wave_lds_sync();
+        Partials P;
+        readout_load(par, bb, P);
+        readout_finish(bb, t0, zz, P);
         compiler_fence();
       }
     }

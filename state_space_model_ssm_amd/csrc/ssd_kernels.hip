@@ -30,6 +30,13 @@
 // accumulator tiles hold per lane, so S feeds the MFMA without a transpose.
 #include "ssm_internal.h"
 
+#ifndef SSD_PF
+#define SSD_PF 0
+#endif
+#ifndef SSD_WPE
+#define SSD_WPE 2
+#endif
+
 namespace ssm {
 namespace {
 
@@ -63,7 +70,7 @@ __device__ __forceinline__ float silu(float z) {
 }
 
 template <typename Tout, int N>
-__global__ void __launch_bounds__(256) ssd_chunk_kernel(const SsdParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WPE, SSD_WPE))) ssd_chunk_kernel(const SsdParams p) {
   constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
   constexpr int NK = N / 32;      // K steps over dstate
@@ -109,38 +116,86 @@ __global__ void __launch_bounds__(256) ssd_chunk_kernel(const SsdParams p) {
 #pragma unroll
   for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c0 = 0; c0 < L; c0 += Q) {
-    // ---- stage the chunk --------------------------------------------------
-    // B and C: Q rows of N bf16, 16-byte vectors.
+  constexpr int BCK = (Q * N / 8) / 256;  // B/C vectors per thread per chunk
+  constexpr int XK = (Q * P / 8) / 256;   // x vectors per thread per chunk
+  auto load_bc = [&](int64_t c0, uint4 *cv, uint4 *bv) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < (Q * N / 8) / 256; ++k) {
+    for (int k = 0; k < BCK; ++k) {
       const int v = tid + 256 * k;
       const int t = v / (N / 8);
       const int nv = (v % (N / 8)) * 8;
-      uint4 cv = {0u, 0u, 0u, 0u}, bv = {0u, 0u, 0u, 0u};
+      cv[k] = uint4{0u, 0u, 0u, 0u};
+      bv[k] = uint4{0u, 0u, 0u, 0u};
       if (c0 + t < L) {
         const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
-        cv = *reinterpret_cast<const uint4 *>(gC + off);
-        bv = *reinterpret_cast<const uint4 *>(gB + off);
+        cv[k] = *reinterpret_cast<const uint4 *>(gC + off);
+        bv[k] = *reinterpret_cast<const uint4 *>(gB + off);
       }
-      *reinterpret_cast<uint4 *>(&sC[t * NP + nv]) = cv;
-      *reinterpret_cast<uint4 *>(&sB[t * NP + nv]) = bv;
-      const uint16_t *be = reinterpret_cast<const uint16_t *>(&bv);
+    }
+  };
+  auto load_x = [&](int64_t c0, uint4 *xv) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (P / 8);
+      const int pv = (v % (P / 8)) * 8;
+      xv[k] = uint4{0u, 0u, 0u, 0u};
+      if (c0 + t < L) xv[k] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
+    }
+  };
+#if SSD_PF >= 1
+  uint4 xpf[XK];
+  load_x(0, xpf);
+#endif
+#if SSD_PF >= 2
+  uint4 cpf[BCK], bpf[BCK];
+  load_bc(0, cpf, bpf);
+#endif
+
+  for (int64_t c0 = 0; c0 < L; c0 += Q) {
+    // ---- stage the chunk --------------------------------------------------
+    // B and C: Q rows of N bf16, 16-byte vectors.
+    uint4 cvv[BCK], bvv[BCK];
+#if SSD_PF >= 2
+#pragma unroll
+    for (int k = 0; k < BCK; ++k) { cvv[k] = cpf[k]; bvv[k] = bpf[k]; }
+#else
+    load_bc(c0, cvv, bvv);
+#endif
+#pragma unroll
+    for (int k = 0; k < BCK; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (N / 8);
+      const int nv = (v % (N / 8)) * 8;
+      *reinterpret_cast<uint4 *>(&sC[t * NP + nv]) = cvv[k];
+      *reinterpret_cast<uint4 *>(&sB[t * NP + nv]) = bvv[k];
+      const uint16_t *be = reinterpret_cast<const uint16_t *>(&bvv[k]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) sBt[(nv + j) * QP + t] = be[j];
     }
     // x: Q rows of P bf16, stored transposed.
+    uint4 xvv[XK];
+#if SSD_PF >= 1
 #pragma unroll
-    for (int k = 0; k < (Q * P / 8) / 256; ++k) {
+    for (int k = 0; k < XK; ++k) xvv[k] = xpf[k];
+#else
+    load_x(c0, xvv);
+#endif
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
       const int v = tid + 256 * k;
       const int t = v / (P / 8);
       const int pv = (v % (P / 8)) * 8;
-      uint4 xv = {0u, 0u, 0u, 0u};
-      if (c0 + t < L) xv = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
-      const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xv);
+      const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xvv[k]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) sXt[(pv + j) * QP + t] = xe[j];
     }
+#if SSD_PF >= 1
+    if (c0 + Q < L) load_x(c0 + Q, xpf);
+#endif
+#if SSD_PF >= 2
+    if (c0 + Q < L) load_bc(c0 + Q, cpf, bpf);
+#endif
     // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
     if (wave == 0) {
       const float dtv = (c0 + lane < L) ? bf2f(gdt[(b * L + c0 + lane) * H + h]) : 0.0f;

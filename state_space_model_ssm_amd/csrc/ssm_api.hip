@@ -194,7 +194,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   p.dstate = static_cast<int32_t>(d.dstate);
   const int vec = ssm::scan_vector_elems(d.in_dtype == SSM_BF16);
   p.vec_ok = (d.seqlen % vec == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(B, 16) &&
-             aligned(C, 16) && aligned(y, 16);
+             aligned(C, 16);
   const hipError_t e = ssm::launch_scan(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));

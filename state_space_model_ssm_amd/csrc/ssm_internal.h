@@ -20,7 +20,7 @@ struct ScanParams {
   int64_t tiles_per_group;            // channel tiles per (batch, group)
   int32_t n_chunks;                   // resolved chunk count (>= 1)
   int32_t dstate;
-  int32_t vec_ok;                     // u, delta, B, C, y rows start 16-byte aligned
+  int32_t vec_ok;                     // u, delta, B, C rows start 16-byte aligned
 };
 
 // Chunks start on multiples of this many steps (the scan's time tile).
