@@ -30,9 +30,6 @@
 // accumulator tiles hold per lane, so S feeds the MFMA without a transpose.
 #include "ssm_internal.h"
 
-#ifndef SSD_PF
-#define SSD_PF 0
-#endif
 #ifndef SSD_WPE
 #define SSD_WPE 2
 #endif
@@ -116,86 +113,69 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #pragma unroll
   for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int BCK = (Q * N / 8) / 256;  // B/C vectors per thread per chunk
-  constexpr int XK = (Q * P / 8) / 256;   // x vectors per thread per chunk
-  auto load_bc = [&](int64_t c0, uint4 *cv, uint4 *bv) __attribute__((always_inline)) {
+  // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group,
+  // so the transposed copies are written as packed 32-bit step pairs:
+  // consecutive lanes (consecutive tp) hit consecutive LDS banks.
+  constexpr int BJ = (Q / 2) * (N / 8) / 256;  // B/C jobs per thread per chunk
+  constexpr int XJ = (Q / 2) * (P / 8) / 256;  // x jobs per thread per chunk
+  static_assert(BJ >= 1 && XJ == 1 && QP % 2 == 0, "staging map");
+  uint32_t *sBt32 = reinterpret_cast<uint32_t *>(sBt);
+  uint32_t *sXt32 = reinterpret_cast<uint32_t *>(sXt);
+  // Low halves (even elements) or high halves (odd elements) of two words,
+  // step 2tp in the low half of the result.
+  auto pair_lo = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
+  auto pair_hi = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
+  auto put_t = [&](uint32_t *dst, int col0, int tp, const uint4 &r0, const uint4 &r1) __attribute__((always_inline)) {
+    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+    const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-    for (int k = 0; k < BCK; ++k) {
-      const int v = tid + 256 * k;
-      const int t = v / (N / 8);
-      const int nv = (v % (N / 8)) * 8;
-      cv[k] = uint4{0u, 0u, 0u, 0u};
-      bv[k] = uint4{0u, 0u, 0u, 0u};
-      if (c0 + t < L) {
-        const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
-        cv[k] = *reinterpret_cast<const uint4 *>(gC + off);
-        bv[k] = *reinterpret_cast<const uint4 *>(gB + off);
-      }
+    for (int i = 0; i < 4; ++i) {
+      dst[(col0 + 2 * i) * (QP / 2) + tp] = pair_lo(w0[i], w1[i]);
+      dst[(col0 + 2 * i + 1) * (QP / 2) + tp] = pair_hi(w0[i], w1[i]);
     }
   };
-  auto load_x = [&](int64_t c0, uint4 *xv) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < XK; ++k) {
-      const int v = tid + 256 * k;
-      const int t = v / (P / 8);
-      const int pv = (v % (P / 8)) * 8;
-      xv[k] = uint4{0u, 0u, 0u, 0u};
-      if (c0 + t < L) xv[k] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
-    }
-  };
-#if SSD_PF >= 1
-  uint4 xpf[XK];
-  load_x(0, xpf);
-#endif
-#if SSD_PF >= 2
-  uint4 cpf[BCK], bpf[BCK];
-  load_bc(0, cpf, bpf);
-#endif
 
   for (int64_t c0 = 0; c0 < L; c0 += Q) {
     // ---- stage the chunk --------------------------------------------------
-    // B and C: Q rows of N bf16, 16-byte vectors.
-    uint4 cvv[BCK], bvv[BCK];
-#if SSD_PF >= 2
+    // B and C: rows of N bf16, natural layout [t][n] for both, and B also
+    // transposed to [n][t].
 #pragma unroll
-    for (int k = 0; k < BCK; ++k) { cvv[k] = cpf[k]; bvv[k] = bpf[k]; }
-#else
-    load_bc(c0, cvv, bvv);
-#endif
-#pragma unroll
-    for (int k = 0; k < BCK; ++k) {
+    for (int k = 0; k < BJ; ++k) {
       const int v = tid + 256 * k;
-      const int t = v / (N / 8);
-      const int nv = (v % (N / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sC[t * NP + nv]) = cvv[k];
-      *reinterpret_cast<uint4 *>(&sB[t * NP + nv]) = bvv[k];
-      const uint16_t *be = reinterpret_cast<const uint16_t *>(&bvv[k]);
+      const int tp = v % (Q / 2);
+      const int nv = (v / (Q / 2)) * 8;
+      uint4 bv[2], cv[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sBt[(nv + j) * QP + t] = be[j];
+      for (int e = 0; e < 2; ++e) {
+        const int t = 2 * tp + e;
+        bv[e] = uint4{0u, 0u, 0u, 0u};
+        cv[e] = uint4{0u, 0u, 0u, 0u};
+        if (c0 + t < L) {
+          const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
+          bv[e] = *reinterpret_cast<const uint4 *>(gB + off);
+          cv[e] = *reinterpret_cast<const uint4 *>(gC + off);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<uint4 *>(&sB[(2 * tp + e) * NP + nv]) = bv[e];
+        *reinterpret_cast<uint4 *>(&sC[(2 * tp + e) * NP + nv]) = cv[e];
+      }
+      put_t(sBt32, nv, tp, bv[0], bv[1]);
     }
-    // x: Q rows of P bf16, stored transposed.
-    uint4 xvv[XK];
-#if SSD_PF >= 1
+    // x: rows of P bf16, stored transposed [p][t].
+    {
+      const int tp = tid % (Q / 2);
+      const int pv = (tid / (Q / 2)) * 8;
+      uint4 xv[2];
 #pragma unroll
-    for (int k = 0; k < XK; ++k) xvv[k] = xpf[k];
-#else
-    load_x(c0, xvv);
-#endif
-#pragma unroll
-    for (int k = 0; k < XK; ++k) {
-      const int v = tid + 256 * k;
-      const int t = v / (P / 8);
-      const int pv = (v % (P / 8)) * 8;
-      const uint16_t *xe = reinterpret_cast<const uint16_t *>(&xvv[k]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sXt[(pv + j) * QP + t] = xe[j];
+      for (int e = 0; e < 2; ++e) {
+        const int t = 2 * tp + e;
+        xv[e] = uint4{0u, 0u, 0u, 0u};
+        if (c0 + t < L) xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
+      }
+      put_t(sXt32, pv, tp, xv[0], xv[1]);
     }
-#if SSD_PF >= 1
-    if (c0 + Q < L) load_x(c0 + Q, xpf);
-#endif
-#if SSD_PF >= 2
-    if (c0 + Q < L) load_bc(c0 + Q, cpf, bpf);
-#endif
     // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
     if (wave == 0) {
       const float dtv = (c0 + lane < L) ? bf2f(gdt[(b * L + c0 + lane) * H + h]) : 0.0f;
