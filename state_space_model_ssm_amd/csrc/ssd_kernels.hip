@@ -28,10 +28,15 @@
 // the C S^T product uses k-slot 8q + j -> n = 32kk + 4q + j (j < 4) and
 // n = 32kk + 16 + 4q + j - 4 (j >= 4), which is exactly what two S^T
 // accumulator tiles hold per lane, so S feeds the MFMA without a transpose.
+#include <type_traits>
+
 #include "ssm_internal.h"
 
 #ifndef SSD_WPE
 #define SSD_WPE 2
+#endif
+#ifndef SSD_PREFETCH
+#define SSD_PREFETCH 1
 #endif
 
 namespace ssm {
@@ -66,7 +71,23 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-template <typename Tout, int N>
+// Transposed chunk copies ([col][t] for COLS columns, rows of QP bf16): the
+// XOR applied to the index of the 32-bit step pair (t / 2) in row `col`.  A
+// staging store instruction covers 64 / (COLS / 8) consecutive pairs of each
+// of COLS / 8 rows; rows 16 apart get distinct multiples of that span.
+template <int COLS>
+__device__ __forceinline__ int tswz(int col) {
+  constexpr int span = 64 / (COLS / 8);
+  return span * ((col >> 4) & (COLS / 16 - 1));
+}
+
+// Element index of (col, t) in a transposed copy.
+template <int COLS>
+__device__ __forceinline__ int tidx(int col, int t) {
+  return col * QP + 2 * ((t >> 1) ^ tswz<COLS>(col)) + (t & 1);
+}
+
+template <typename Tout, int N, bool HAS_Z>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WPE, SSD_WPE))) ssd_chunk_kernel(const SsdParams p) {
   constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
@@ -113,72 +134,89 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #pragma unroll
   for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group,
-  // so the transposed copies are written as packed 32-bit step pairs:
-  // consecutive lanes (consecutive tp) hit consecutive LDS banks.
+  // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group;
+  // the 8-column groups of a row go to consecutive lanes, so a wavefront's
+  // global loads read whole rows.  The transposed copies ([col][t], 32-bit
+  // step pairs) XOR the pair index with a multiple of the wavefront's tp span
+  // chosen by the row, which spreads one store instruction over all 64 banks;
+  // fragment reads apply the same XOR, and keep 16-byte groups contiguous.
   constexpr int BJ = (Q / 2) * (N / 8) / 256;  // B/C jobs per thread per chunk
-  constexpr int XJ = (Q / 2) * (P / 8) / 256;  // x jobs per thread per chunk
-  static_assert(BJ >= 1 && XJ == 1 && QP % 2 == 0, "staging map");
+  static_assert(BJ >= 1 && (Q / 2) * (P / 8) == 256 && QP % 2 == 0, "staging map");
   uint32_t *sBt32 = reinterpret_cast<uint32_t *>(sBt);
   uint32_t *sXt32 = reinterpret_cast<uint32_t *>(sXt);
-  // Low halves (even elements) or high halves (odd elements) of two words,
-  // step 2tp in the low half of the result.
   auto pair_lo = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
   auto pair_hi = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); };
-  auto put_t = [&](uint32_t *dst, int col0, int tp, const uint4 &r0, const uint4 &r1) __attribute__((always_inline)) {
+  auto put_t = [&](uint32_t *dst, int col0, int tp, const uint4 &r0, const uint4 &r1, auto cols)
+                   __attribute__((always_inline)) {
+    constexpr int COLS = decltype(cols)::value;
     const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
     const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dst[(col0 + 2 * i) * (QP / 2) + tp] = pair_lo(w0[i], w1[i]);
-      dst[(col0 + 2 * i + 1) * (QP / 2) + tp] = pair_hi(w0[i], w1[i]);
+      const int c = col0 + 2 * i;
+      dst[c * (QP / 2) + (tp ^ tswz<COLS>(c))] = pair_lo(w0[i], w1[i]);
+      dst[(c + 1) * (QP / 2) + (tp ^ tswz<COLS>(c + 1))] = pair_hi(w0[i], w1[i]);
     }
   };
 
-  for (int64_t c0 = 0; c0 < L; c0 += Q) {
-    // ---- stage the chunk --------------------------------------------------
-    // B and C: rows of N bf16, natural layout [t][n] for both, and B also
-    // transposed to [n][t].
+  // One chunk's global inputs in registers: loaded a chunk ahead (while the
+  // previous chunk computes), then written to LDS.
+  struct ChunkRegs {
+    uint4 bv[BJ][2], cv[BJ][2];
+    uint4 xv[2];
+    uint32_t dt;  // raw bf16 bits of dt at step `lane` (wavefront 0 uses it)
+  };
+  auto load_chunk = [&](int64_t c0, ChunkRegs &R) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < BJ; ++k) {
       const int v = tid + 256 * k;
-      const int tp = v % (Q / 2);
-      const int nv = (v / (Q / 2)) * 8;
-      uint4 bv[2], cv[2];
+      const int tp = v / (N / 8);
+      const int nv = (v % (N / 8)) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int t = 2 * tp + e;
-        bv[e] = uint4{0u, 0u, 0u, 0u};
-        cv[e] = uint4{0u, 0u, 0u, 0u};
+        R.bv[k][e] = uint4{0u, 0u, 0u, 0u};
+        R.cv[k][e] = uint4{0u, 0u, 0u, 0u};
         if (c0 + t < L) {
           const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
-          bv[e] = *reinterpret_cast<const uint4 *>(gB + off);
-          cv[e] = *reinterpret_cast<const uint4 *>(gC + off);
+          R.bv[k][e] = *reinterpret_cast<const uint4 *>(gB + off);
+          R.cv[k][e] = *reinterpret_cast<const uint4 *>(gC + off);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<uint4 *>(&sB[(2 * tp + e) * NP + nv]) = bv[e];
-        *reinterpret_cast<uint4 *>(&sC[(2 * tp + e) * NP + nv]) = cv[e];
-      }
-      put_t(sBt32, nv, tp, bv[0], bv[1]);
     }
-    // x: rows of P bf16, stored transposed [p][t].
     {
-      const int tp = tid % (Q / 2);
-      const int pv = (tid / (Q / 2)) * 8;
-      uint4 xv[2];
+      const int tp = tid / (P / 8);
+      const int pv = (tid % (P / 8)) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int t = 2 * tp + e;
-        xv[e] = uint4{0u, 0u, 0u, 0u};
-        if (c0 + t < L) xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
+        R.xv[e] = uint4{0u, 0u, 0u, 0u};
+        if (c0 + t < L) R.xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
       }
-      put_t(sXt32, pv, tp, xv[0], xv[1]);
     }
+    // Unconditional load from a clamped step: no branch, so nothing waits
+    // on it (or on the loads before it) until the chunk is staged.
+    R.dt = gdt[(b * L + min(c0 + lane, L - 1)) * H + h];
+  };
+  auto stage_chunk = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
+    // B and C: natural layout [t][n] for both, B also transposed to [n][t].
+#pragma unroll
+    for (int k = 0; k < BJ; ++k) {
+      const int v = tid + 256 * k;
+      const int tp = v / (N / 8);
+      const int nv = (v % (N / 8)) * 8;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<uint4 *>(&sB[(2 * tp + e) * NP + nv]) = R.bv[k][e];
+        *reinterpret_cast<uint4 *>(&sC[(2 * tp + e) * NP + nv]) = R.cv[k][e];
+      }
+      put_t(sBt32, nv, tp, R.bv[k][0], R.bv[k][1], std::integral_constant<int, N>{});
+    }
+    // x transposed to [p][t].
+    put_t(sXt32, (tid % (P / 8)) * 8, tid / (P / 8), R.xv[0], R.xv[1], std::integral_constant<int, P>{});
     // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
     if (wave == 0) {
-      const float dtv = (c0 + lane < L) ? bf2f(gdt[(b * L + c0 + lane) * H + h]) : 0.0f;
+      const float dtv = (c0 + lane < L) ? bf2f(static_cast<uint16_t>(R.dt)) : 0.0f;
       float a = dtv * Ah;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -192,7 +230,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       sDt[lane] = dtv;
       if (lane == 0) sDecay = fast_exp(alast);
     }
+  };
+
+  ChunkRegs R;
+  load_chunk(0, R);
+  for (int64_t c0 = 0; c0 < L; c0 += Q) {
+    stage_chunk(R, c0);
     __syncthreads();
+#if SSD_PREFETCH
+    if (c0 + Q < L) load_chunk(c0 + Q, R);
+#endif
 
     // ---- Y_off = diag(exp(a_t)) C S_prev^T ---------------------------------
     floatx4 Y[4];
@@ -226,14 +273,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int s0 = 32 * kk + 8 * q;
-        const bf16x8 xs = lds8(&sXt[pcol * QP + s0]);
+        const bf16x8 xs = lds8(&sXt[tidx<P>(pcol, s0)]);
         floatx8 wx;
 #pragma unroll
         for (int j = 0; j < 8; ++j) wx[j] = static_cast<float>(xs[j]) * sW[s0 + j];
         const bf16x8 bfrag = __builtin_convertvector(wx, bf16x8);
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) {
-          const bf16x8 afrag = lds8(&sBt[(ni * 16 + r16) * QP + s0]);
+          const bf16x8 afrag = lds8(&sBt[tidx<N>(ni * 16 + r16, s0)]);
           S[ni] = mfma(afrag, bfrag, S[ni]);
         }
       }
@@ -282,13 +329,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       for (int kk = 0; kk < 2; ++kk) {
         if (32 * kk < 16 * (ti + 1)) {
           const bf16x8 afrag = lds8(&sM[(ti * 16 + r16) * QP + 32 * kk + 8 * q]);
-          const bf16x8 bfrag = lds8(&sXt[pcol * QP + 32 * kk + 8 * q]);
+          const bf16x8 bfrag = lds8(&sXt[tidx<P>(pcol, 32 * kk + 8 * q)]);
           Y[ti] = mfma(afrag, bfrag, Y[ti]);
         }
       }
     }
 
     // ---- epilogue: D skip, gate, store y -----------------------------------
+    // The gate's z values are loaded first, all together, from clamped steps,
+    // so the loads are waited for once.
+    uint32_t zr[16];
+    if constexpr (HAS_Z) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t tc = min(c0 + (e / 4) * 16 + 4 * q + (e % 4), L - 1);
+        zr[e] = gz[((b * L + tc) * H + h) * P + pcol];
+      }
+    }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
@@ -296,13 +353,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         const int t = ti * 16 + 4 * q + r;
         if (c0 + t < L) {
           const int64_t off = ((b * L + c0 + t) * H + h) * P + pcol;
-          float yv = Y[ti][r] + Dh * bf2f(sXt[pcol * QP + t]);
-          if (gz) yv *= silu(bf2f(gz[off]));
+          float yv = Y[ti][r] + Dh * bf2f(sXt[tidx<P>(pcol, t)]);
+          if constexpr (HAS_Z) yv *= silu(bf2f(static_cast<uint16_t>(zr[ti * 4 + r])));
           st(gy, off, yv);
         }
       }
     }
     __syncthreads();  // the next chunk overwrites the LDS operands
+#if !SSD_PREFETCH
+    if (c0 + Q < L) load_chunk(c0 + Q, R);
+#endif
   }
 
   if (p.h_last) {
@@ -313,16 +373,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   }
 }
 
+template <typename Tout, int N>
+hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
+  if (p.z != nullptr)
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename Tout>
 hipError_t launch_typed(const SsdParams &p, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
-  if (p.dstate == 128)
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, 128>), grid, dim3(256), 0, stream, p);
-  else if (p.dstate == 64)
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, 64>), grid, dim3(256), 0, stream, p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (p.dstate == 128) return launch_n<Tout, 128>(p, stream);
+  if (p.dstate == 64) return launch_n<Tout, 64>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
