@@ -96,7 +96,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];   // B[s][n]
   __shared__ __attribute__((aligned(16))) uint16_t sBt[N * QP];  // B[n][s]
   __shared__ __attribute__((aligned(16))) uint16_t sXt[P * QP];  // x[p][s]
-  __shared__ __attribute__((aligned(16))) uint16_t sM[Q * QP];   // M[t][s]
+  // M[t][s] (bf16, rows of QP), then the chunk's y[t][p] (Tout, rows of YP).
+  constexpr int YV = 16 / static_cast<int>(sizeof(Tout));   // y elements per 16-byte vector
+  constexpr int YP = P + YV;                                 // padded y row
+  constexpr int YJ = Q * (P / YV) / 256;                     // y vectors per thread per chunk
+  constexpr int SM_BYTES = Q * QP * 2 > Q * YP * static_cast<int>(sizeof(Tout))
+                               ? Q * QP * 2 : Q * YP * static_cast<int>(sizeof(Tout));
+  __shared__ __attribute__((aligned(16))) uint16_t sM[SM_BYTES / 2];
+  Tout *sY = reinterpret_cast<Tout *>(sM);
   __shared__ __attribute__((aligned(16))) float sA[Q];           // a_t
   __shared__ __attribute__((aligned(16))) float sEa[Q];          // exp(a_t)
   __shared__ __attribute__((aligned(16))) float sW[Q];           // exp(a_last - a_s) dt_s
@@ -335,7 +342,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       }
     }
 
-    // ---- epilogue: D skip, gate, store y -----------------------------------
+    // ---- epilogue: D skip and gate in the MFMA layout, then y through LDS ----
     // The gate's z values are loaded first, all together, from clamped steps,
     // so the loads are waited for once.
     uint32_t zr[16];
@@ -346,20 +353,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         zr[e] = gz[((b * L + tc) * H + h) * P + pcol];
       }
     }
+    float yv[16];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = ti * 16 + 4 * q + r;
-        if (c0 + t < L) {
-          const int64_t off = ((b * L + c0 + t) * H + h) * P + pcol;
-          float yv = Y[ti][r] + Dh * bf2f(sXt[tidx<P>(pcol, t)]);
-          if constexpr (HAS_Z) yv *= silu(bf2f(static_cast<uint16_t>(zr[ti * 4 + r])));
-          st(gy, off, yv);
-        }
+        float v = Y[ti][r] + Dh * bf2f(sXt[tidx<P>(pcol, t)]);
+        if constexpr (HAS_Z) v *= silu(bf2f(static_cast<uint16_t>(zr[ti * 4 + r])));
+        yv[ti * 4 + r] = v;
       }
     }
-    __syncthreads();  // the next chunk overwrites the LDS operands
+    __syncthreads();  // every wavefront is done reading M; its buffer takes y
+#pragma unroll
+    for (int e = 0; e < 16; ++e) st(sY, ((e / 4) * 16 + 4 * q + (e % 4)) * YP + pcol, yv[e]);
+    __syncthreads();
+    // y rows of the chunk as 16-byte vectors: P / YV vectors per step.
+#pragma unroll
+    for (int k = 0; k < YJ; ++k) {
+      const int v = tid + 256 * k;
+      const int t = v / (P / YV);
+      const int pv = (v % (P / YV)) * YV;
+      if (c0 + t < L)
+        *reinterpret_cast<uint4 *>(gy + ((b * L + c0 + t) * H + h) * P + pv) =
+            *reinterpret_cast<const uint4 *>(&sY[t * YP + pv]);
+    }
+    // No barrier here: the next chunk's staging writes none of the y buffer,
+    // and every wavefront read its last staged operands before the barrier
+    // above; the y buffer is rewritten (as M) only after the next barrier.
 #if !SSD_PREFETCH
     if (c0 + Q < L) load_chunk(c0 + Q, R);
 #endif
