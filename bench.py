@@ -45,6 +45,24 @@ BF16_MFMA_TFLOPS = 2500.0
 TRANS_SLOTS = 4.0
 
 HEADLINE = "large_channel_4x5120x4096_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch counted by rocprofv3 for this workload's kernel, or
+    None when no count exists or the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f).get(workload)
+        if entry is None:
+            return None
+        with open(os.path.join(ROOT, entry["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != entry["source_sha256"]:
+                return None
+        return int(entry["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
 
 
 def scan_alu_slots_per_element(N: int, has_z: bool, has_d: bool) -> float:
@@ -158,7 +176,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload) if chunks == 1 else None
     roof["kernel"] = "scan_chunk_kernel<bf16,bf16,16,sweep>" if s.dtype == "bf16" else "scan_chunk_kernel<f32,f32,16,sweep>"
     roof["hbm_gbs"] = round(hbm_gbs, 1)
     roof["hbm_frac"] = round(hbm_gbs / HBM_PEAK_GBS, 4)
