@@ -94,7 +94,8 @@ SSM_API int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chu
 /*
  * Selective-scan forward.
  *
- * For every batch b and channel d (state h in R^N, zero before t = 0):
+ * For every batch b and channel d (state h in R^N; before t = 0 it is
+ * h0[b,d,:], or zero when h0 is NULL):
  *   h_t[n] = exp(delta_t * A[d,n]) * h_{t-1}[n] + delta_t * B_t[n] * u_t
  *   y_t    = (sum_n C_t[n] * h_t[n] + D[d] * u_t) * silu(z_t)
  * with silu(z) = z / (1 + exp(-z)); the D term is dropped when D is NULL and
@@ -113,14 +114,19 @@ SSM_API int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chu
  *   A           : (dim, dstate) float32
  *   B, C        : (batch, ngroups, dstate, seqlen)
  *   D           : (dim) float32                nullable
+ *   h0          : (batch, dim, dstate) float32  nullable (initial state)
  *   y           : (batch, dim, seqlen) out_dtype
  *   h_last      : (batch, dim, dstate) float32  nullable
- * y and h_last must not overlap any input.  bfloat16 y is rounded to
- * nearest even from the float32 result.
+ * y and h_last must not overlap any input, with one exception: h_last may be
+ * exactly h0 (the state updated in place, as when a prefill continues from a
+ * cache) when the call runs as one pass (ssm_scan_resolved_chunks() == 1).
+ * With h0 = the h_last of a call on steps [0, L1), a call on [L1, L) continues
+ * that sequence.  bfloat16 y is rounded to nearest even from the float32
+ * result.
  */
 SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B,
-                 const void *C, const float *D, const void *z, void *y, float *h_last,
-                 const ssm_scan_dims_t *dims, void *stream);
+                 const void *C, const float *D, const void *z, const float *h0, void *y,
+                 float *h_last, const ssm_scan_dims_t *dims, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Scalar-decay chunked SSD                                                  */
@@ -135,8 +141,8 @@ SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const
  *   flags: reserved, must be 0.
  * Supported: headdim = 64, dstate in {64, 128}, chunk = 64, any seqlen >= 0
  * (a ragged last chunk is masked).
- * Alignment: x, z, B, C and h_last must be 16-byte aligned (they are read and
- * written as 16-byte vectors); dt and y need their element alignment.
+ * Alignment: x, z, B, C, h0 and h_last must be 16-byte aligned (they are read
+ * and written as 16-byte vectors); dt and y need their element alignment.
  */
 typedef struct {
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
@@ -155,7 +161,8 @@ SSM_API int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
  * time, head), shared by the head's headdim x dstate states, computed chunk by
  * chunk with matrix-core contractions.
  *
- * For every batch b and head h (state S in R^{P x N}, zero before t = 0):
+ * For every batch b and head h (state S in R^{P x N}; before t = 0 it is
+ * h0[b,h,:,:], or zero when h0 is NULL):
  *   S_t   = exp(dt_t * A[h]) * S_{t-1} + dt_t * x_t B_t^T
  *   y_t   = (S_t C_t + D[h] * x_t) * silu(z_t)
  *   [Mamba-3 NKI], "Kernel details", mamba3_siso_ssd_kernel: a chunked SSD
@@ -173,12 +180,15 @@ SSM_API int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
  *             and bias are applied by the caller)
  *   A, D    : (nheads) float32                          D nullable
  *   B, C    : (batch, seqlen, ngroups, dstate) bf16
+ *   h0      : (batch, nheads, headdim, dstate) float32  nullable (initial state)
  *   y       : (batch, seqlen, nheads, headdim) out_dtype
  *   h_last  : (batch, nheads, headdim, dstate) float32  nullable
+ * h0 and h_last must be 16-byte aligned; h_last may be exactly h0 (updated in
+ * place), any other overlap with an input is rejected.
  */
 SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B,
-                    const void *C, const float *D, const void *z, void *y, float *h_last,
-                    const ssd_dims_t *dims, void *stream);
+                    const void *C, const float *D, const void *z, const float *h0, void *y,
+                    float *h_last, const ssd_dims_t *dims, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

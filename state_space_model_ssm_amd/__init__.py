@@ -67,13 +67,13 @@ def lib():
                 "(hipcc, gfx950). There is no fallback implementation.")
         L = ctypes.CDLL(_LIB_PATH)
         vp, i32 = ctypes.c_void_p, ctypes.c_int
-        L.ssm_scan_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(ScanDims), vp]
+        L.ssm_scan_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(ScanDims), vp]
         L.ssm_scan_fwd.restype = i32
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_workspace_size.restype = i32
         L.ssm_scan_resolved_chunks.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_int32)]
         L.ssm_scan_resolved_chunks.restype = i32
-        L.ssd_chunked_fwd.argtypes = [vp] * 9 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_chunked_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(SsdDims), vp]
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
@@ -158,13 +158,14 @@ def scan_resolved_chunks(dims: ScanDims) -> int:
     return n.value
 
 
-def scan_fwd(u, delta, A, B, C, D=None, z=None, *, out_dtype=None, n_chunks: int = 0,
+def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_chunks: int = 0,
              return_h_last: bool = True, y=None, h_last=None, workspace=None, stream=None):
     """Selective-scan forward (``ssm_scan_fwd``). Returns ``(y, h_last)``.
 
     u, delta, z: (batch, dim, L); A: (dim, N) float32; B, C: (batch, G, N, L);
-    D: (dim,) float32.  u/delta/B/C/z share one dtype (float32 or bfloat16);
-    y defaults to that dtype, h_last is float32 (batch, dim, N).
+    D: (dim,) float32; h0: (batch, dim, N) float32 initial state (zero when
+    None).  u/delta/B/C/z share one dtype (float32 or bfloat16); y defaults to
+    that dtype, h_last is float32 (batch, dim, N) and may be h0 itself.
     """
     torch = _torch()
     in_code = _dtype_code(u.dtype)
@@ -184,6 +185,8 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, out_dtype=None, n_chunks: int
         raise ValueError("B and C must be (batch, ngroups, dstate, seqlen)")
     if A.shape != (dim, N) or (D is not None and D.shape != (dim,)):
         raise ValueError("A must be (dim, dstate) and D (dim,)")
+    if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, dim, N)):
+        raise ValueError("h0 must be float32 (batch, dim, dstate)")
     dims = _scan_dims(u, B, in_code, out_code, n_chunks)
     need = scan_workspace_size(dims)
     if y is None:
@@ -196,7 +199,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, out_dtype=None, n_chunks: int
         dims.workspace = _ptr(workspace)
         dims.workspace_bytes = workspace.numel() * workspace.element_size()
     rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                            _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+                            _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last
 
@@ -215,12 +218,13 @@ def ssd_workspace_size(dims: SsdDims) -> int:
     return n.value
 
 
-def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, chunk: int = 64, out_dtype=None,
+def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
                     return_h_last: bool = True, y=None, h_last=None, stream=None):
     """Scalar-decay chunked SSD forward (``ssd_chunked_fwd``). Returns ``(y, h_last)``.
 
     x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
-    B, C: (batch, L, G, N) bf16.  h_last is float32 (batch, H, P, N).
+    B, C: (batch, L, G, N) bf16; h0: (batch, H, P, N) float32 initial state
+    (zero when None).  h_last is float32 (batch, H, P, N) and may be h0 itself.
     """
     torch = _torch()
     in_code = _dtype_code(x.dtype)
@@ -240,12 +244,14 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, chunk: int = 64, out_dtyp
         raise ValueError("B and C must be (batch, seqlen, ngroups, dstate)")
     if A.shape != (H,) or (D is not None and D.shape != (H,)):
         raise ValueError("A and D must be (nheads,)")
+    if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, H, P, N)):
+        raise ValueError("h0 must be float32 (batch, nheads, headdim, dstate)")
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
     if y is None:
         y = torch.empty((batch, L, H, P), dtype=out_dt, device=x.device)
     if h_last is None and return_h_last:
         h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device)
     rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                               _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+                               _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last

@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   const bool mine = chl < nvalid;
   const int64_t d = d0 + chl;
   const float a2 = mine ? p.A[d * N + n] * kLog2e : 0.0f;
-  float h = 0.0f;
+  float h = (!SUMMARY && p.h0 != nullptr && mine) ? p.h0[(b * p.dim + d) * N + n] : 0.0f;
   float prod = 1.0f;
   if (!SUMMARY && c > 0 && mine) {
     const float *cr = p.carry + (b * p.dim + d) * static_cast<int64_t>(p.n_chunks - 1) * (2 * N);

@@ -140,6 +140,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   floatx4 S[NT];  // S^T tiles: rows n = 16 ni + 4q + r, column p = pcol
 #pragma unroll
   for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (p.h0) {
+    const float *h0 = p.h0 + ((b * H + h) * P + pcol) * N;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
+  }
 
   // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group;
   // the 8-column groups of a row go to consecutive lanes, so a wavefront's

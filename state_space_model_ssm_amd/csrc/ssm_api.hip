@@ -132,8 +132,8 @@ int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks) {
 }
 
 int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
-                 const float *D, const void *z, void *y, float *h_last, const ssm_scan_dims_t *dims,
-                 void *stream) {
+                 const float *D, const void *z, const float *h0, void *y, float *h_last,
+                 const ssm_scan_dims_t *dims, void *stream) {
   int rc = check_scan_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssm_scan_dims_t &d = *dims;
@@ -148,17 +148,21 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei))
     return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
   if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
-  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h_last, 4))
-    return fail(SSM_ERR_ALIGN, "A, D and h_last must be 4-byte aligned");
-  const Span ins[] = {{u, n_bdl * ei}, {delta, n_bdl * ei}, {z, n_bdl * ei}, {B, n_bc * ei},
-                      {C, n_bc * ei},  {A, n_a * 4ull},    {D, d.dim * 4ull}};
-  const Span sy{y, n_bdl * eo}, sh{h_last, n_h * 4ull};
-  for (const Span &s : ins)
-    if (overlap(s, sy) || overlap(s, sh)) return fail(SSM_ERR_SHAPE, "an output overlaps an input");
-  if (overlap(sy, sh)) return fail(SSM_ERR_SHAPE, "y overlaps h_last");
-
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(h_last, 4))
+    return fail(SSM_ERR_ALIGN, "A, D, h0 and h_last must be 4-byte aligned");
   int64_t chunk_len = 1;
   const int32_t chunks = resolve_chunks(&d, &chunk_len);
+  const Span ins[] = {{u, n_bdl * ei}, {delta, n_bdl * ei}, {z, n_bdl * ei}, {B, n_bc * ei},
+                      {C, n_bc * ei},  {A, n_a * 4ull},    {D, d.dim * 4ull}};
+  const Span sy{y, n_bdl * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
+  for (const Span &s : ins)
+    if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
+      return fail(SSM_ERR_SHAPE, "an output or h0 overlaps an input");
+  if (overlap(sy, sh) || overlap(sy, s0)) return fail(SSM_ERR_SHAPE, "y overlaps h_last or h0");
+  // h_last may replace h0 in place when one pass reads each state once and
+  // writes it after; chunked passes read h0 from every chunk.
+  if (overlap(s0, sh) && !(h0 == h_last && chunks == 1))
+    return fail(SSM_ERR_SHAPE, "h_last overlaps h0 (only h_last == h0 with one pass is allowed)");
   const size_t need = scan_workspace(&d, chunks);
   if (need > 0) {
     if (!d.workspace || d.workspace_bytes < need)
@@ -168,6 +172,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
     const Span sw{d.workspace, need};
     for (const Span &s : ins)
       if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an input");
+    if (overlap(sw, s0)) return fail(SSM_ERR_SHAPE, "workspace overlaps h0");
     if (overlap(sw, sy) || overlap(sw, sh)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
   }
   if (d.batch == 0 || d.dim == 0) return ok();
@@ -180,6 +185,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   p.z = z;
   p.A = A;
   p.D = D;
+  p.h0 = h0;
   p.y = y;
   p.h_last = h_last;
   p.carry = static_cast<float *>(need > 0 ? d.workspace : nullptr);
@@ -239,8 +245,8 @@ int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
 }
 
 int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
-                    const float *D, const void *z, void *y, float *h_last, const ssd_dims_t *dims,
-                    void *stream) {
+                    const float *D, const void *z, const float *h0, void *y, float *h_last,
+                    const ssd_dims_t *dims, void *stream) {
   const int rc = check_ssd_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssd_dims_t &d = *dims;
@@ -257,13 +263,18 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
   if (!aligned(dt, 2)) return fail(SSM_ERR_ALIGN, "dt must be 2-byte aligned");
   if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
   if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
-  if (!aligned(h_last, 16)) return fail(SSM_ERR_ALIGN, "h_last must be 16-byte aligned");
+  if (!aligned(h0, 16) || !aligned(h_last, 16))
+    return fail(SSM_ERR_ALIGN, "h0 and h_last must be 16-byte aligned");
   const Span ins[] = {{x, n_x * 2ull}, {dt, n_dt * 2ull}, {z, n_x * 2ull}, {B, n_bc * 2ull},
                       {C, n_bc * 2ull}, {A, d.nheads * 4ull}, {D, d.nheads * 4ull}};
-  const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull};
+  const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
   for (const Span &s : ins)
-    if (overlap(s, sy) || overlap(s, sh)) return fail(SSM_ERR_SHAPE, "an output overlaps an input");
-  if (overlap(sy, sh)) return fail(SSM_ERR_SHAPE, "y overlaps h_last");
+    if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
+      return fail(SSM_ERR_SHAPE, "an output or h0 overlaps an input");
+  if (overlap(sy, sh) || overlap(sy, s0)) return fail(SSM_ERR_SHAPE, "y overlaps h_last or h0");
+  // One workgroup per (batch, head) reads its state first and writes it last.
+  if (overlap(s0, sh) && h0 != h_last)
+    return fail(SSM_ERR_SHAPE, "h_last overlaps h0 (only h_last == h0 is allowed)");
   if (d.batch == 0 || d.nheads == 0) return ok();
 
   ssm::SsdParams p{};
@@ -274,6 +285,7 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
   p.z = z;
   p.A = A;
   p.D = D;
+  p.h0 = h0;
   p.y = y;
   p.h_last = h_last;
   p.batch = d.batch;
@@ -308,6 +320,6 @@ const char *ssm_status_string(int status) {
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
 
-int ssm_version(void) { return 100; }
+int ssm_version(void) { return 200; }
 
 }  // extern "C"

@@ -12,6 +12,7 @@ namespace ssm {
 struct ScanParams {
   const void *u, *delta, *B, *C, *z;  // in_dtype
   const float *A, *D;                 // float32; D nullable
+  const float *h0;                    // nullable initial state [batch][dim][dstate]
   void *y;                            // out_dtype
   float *h_last;                      // nullable
   float *carry;                       // chunked path: [batch][dim][n_chunks-1][2][dstate]
@@ -41,6 +42,7 @@ hipError_t launch_scan(const ScanParams &p, int in_bf16, int out_bf16, hipStream
 struct SsdParams {
   const void *x, *dt, *B, *C, *z;     // bf16
   const float *A, *D;                 // float32; D nullable
+  const float *h0;                    // nullable initial state [batch][nheads][headdim][dstate]
   void *y;                            // out dtype
   float *h_last;                      // nullable
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;

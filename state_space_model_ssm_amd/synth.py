@@ -120,6 +120,12 @@ def _store(a: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(torch.float32).to(torch.bfloat16)
 
 
+def make_state(shape, seed: int, scale: float = 1.0) -> torch.Tensor:
+    """Seeded float32 initial state (h0) of the given shape: N(0, scale^2)."""
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy((scale * rng.standard_normal(shape)).astype(np.float32))
+
+
 def make_scan_inputs(s: ScanShape, a_override: Optional[np.ndarray] = None) -> dict:
     """Selective-scan inputs on the host, in the storage dtypes of the C ABI.
 

@@ -38,7 +38,7 @@ def test_library_loads_and_exports_exactly_the_header():
 
 
 def test_version_and_status_strings():
-    assert ssm.version() == 100
+    assert ssm.version() == 200
     for code, name in ssm.STATUS.items():
         assert ssm.status_string(code) == name
     assert ssm.status_string(-99) == "SSM_ERR_UNKNOWN"
@@ -52,8 +52,8 @@ def _dims(**kw):
 
 
 def _scan(dims, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
-          C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None):
-    return ssm.lib().ssm_scan_fwd(u, delta, A, B, C, D, z, y, h, ctypes.byref(dims), None)
+          C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None, h0=None):
+    return ssm.lib().ssm_scan_fwd(u, delta, A, B, C, D, z, h0, y, h, ctypes.byref(dims), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -74,7 +74,7 @@ def test_scan_rejects_null_and_misaligned():
     assert _scan(d, B=None) == -1
     assert _scan(d, A=None) == -1
     assert _scan(d, y=None) == -1
-    assert ssm.lib().ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, None) == -1
+    assert ssm.lib().ssm_scan_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None) == -1
     assert _scan(d, u=FAKE + 2) == -4                       # f32 input needs 4-byte alignment
     assert _scan(d, h=FAKE + 0x20000002) == -4
     assert _scan(_dims(out_dtype=1), y=FAKE + 0x10000001) == -4
@@ -84,6 +84,21 @@ def test_scan_rejects_overlap():
     d = _dims()
     assert _scan(d, y=FAKE + 16) == -2            # y starts inside u
     assert _scan(d, h=FAKE + 0x10000000 + 64) == -2  # h_last inside y
+
+
+def test_scan_h0_rules():
+    H = FAKE + 0x20000000          # h_last; a (2, 64, 16) float32 state is 8 KiB
+    d = _dims(n_chunks=1)
+    assert _scan(d, h=H, h0=H + 2) == -4                     # h0 must be 4-byte aligned
+    assert _scan(d, h=H, h0=FAKE + 0x100) == -2              # h0 inside u
+    assert _scan(d, h=H, h0=FAKE + 0x10000000 + 64) == -2    # h0 inside y
+    assert _scan(d, h=H, h0=H + 64) == -2                    # partial overlap with h_last
+    dk = _dims(n_chunks=4)
+    need = ssm.scan_workspace_size(dk)
+    dk.workspace, dk.workspace_bytes = FAKE + 0x30000000, need
+    assert _scan(dk, h=H, h0=H) == -2                        # in place needs one pass
+    assert _scan(dk, h=H, h0=FAKE + 0x30000000 + 64) == -2   # h0 inside the workspace
+    assert "h0" in ssm.last_error()
 
 
 def test_scan_workspace_rules():
@@ -128,8 +143,8 @@ def _sdims(**kw):
 
 
 def _ssd(dims, x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
-         C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None):
-    return ssm.lib().ssd_chunked_fwd(x, dt, A, B, C, D, z, y, h, ctypes.byref(dims), None)
+         C=FAKE + 0x400000, D=None, z=None, y=FAKE + 0x10000000, h=None, h0=None):
+    return ssm.lib().ssd_chunked_fwd(x, dt, A, B, C, D, z, h0, y, h, ctypes.byref(dims), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -149,6 +164,9 @@ def test_ssd_rejects_null_misaligned_overlap():
     assert _ssd(d, dt=FAKE + 0x100001) == -4
     assert _ssd(d, h=FAKE + 0x20000008) == -4   # h_last must be 16-byte aligned
     assert _ssd(d, y=FAKE + 0x100010) == -2     # y overlaps dt
+    assert _ssd(d, h=FAKE + 0x20000000, h0=FAKE + 0x20000008) == -4   # h0 16-byte aligned
+    assert _ssd(d, h=FAKE + 0x20000000, h0=FAKE + 0x20000100) == -2   # partial overlap
+    assert _ssd(d, h0=FAKE + 0x300000) == -2                          # h0 inside B
     n = ctypes.c_size_t(99)
     assert ssm.lib().ssd_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
 

@@ -21,7 +21,7 @@ import torch
 import oracle
 import state_space_model_ssm_amd as ssm
 from state_space_model_ssm_amd.synth import (WORKLOADS, ScanShape, SsdShape, make_scan_inputs,
-                                             make_ssd_inputs)
+                                             make_ssd_inputs, make_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def _dev(t):
     return None if t is None else t.cuda()
 
 
-def run_scan(inp, out_dtype=None, n_chunks=0, with_h=True):
+def run_scan(inp, out_dtype=None, n_chunks=0, with_h=True, h0=None):
     u = _dev(inp["u"])
     out_dt = u.dtype if out_dtype is None else out_dtype
     y = torch.full(u.shape, float("nan"), dtype=out_dt, device="cuda")
@@ -61,14 +61,23 @@ def run_scan(inp, out_dtype=None, n_chunks=0, with_h=True):
         h = torch.full((u.shape[0], u.shape[1], inp["B"].shape[2]), float("nan"),
                        dtype=torch.float32, device="cuda")
     y, h = ssm.scan_fwd(u, _dev(inp["delta"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
-                        _dev(inp["D"]), _dev(inp["z"]), out_dtype=out_dt, n_chunks=n_chunks,
-                        y=y, h_last=h, return_h_last=with_h)
+                        _dev(inp["D"]), _dev(inp["z"]), h0=_dev(h0), out_dtype=out_dt,
+                        n_chunks=n_chunks, y=y, h_last=h, return_h_last=with_h)
     torch.cuda.synchronize()
     return y.float().cpu(), (None if h is None else h.cpu())
 
 
-def ref_scan(inp):
-    return oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"])
+def ref_scan(inp, h0=None):
+    return oracle.scan(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0=h0)
+
+
+def _scan_steps(inp, t0, t1):
+    """The inputs restricted to steps [t0, t1) (contiguous copies)."""
+    out = dict(inp)
+    for k in ("u", "delta", "z", "B", "C"):
+        if inp[k] is not None:
+            out[k] = inp[k][..., t0:t1].contiguous()
+    return out
 
 
 def tol_for(*dtypes):
@@ -173,6 +182,45 @@ def test_scan_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# Selective scan: initial state h0 and continuation of a split sequence
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,N", [("f32", 16), ("f32", 4), ("bf16", 16), ("bf16", 64)])
+def test_scan_h0(dtype, N):
+    s = ScanShape(2, 50, N, 257, 1, dtype, has_z=True, dskip="normal", a_kind="loguniform",
+                  seed=4100 + N)
+    inp = make_scan_inputs(s)
+    h0 = make_state((2, 50, N), seed=4200 + N)
+    yr, hr = ref_scan(inp, h0=h0)
+    tol = tol_for(dtype)
+    for k in (1, 3, 9):
+        y, h = run_scan(inp, n_chunks=k, h0=h0)
+        assert rel_err(y, yr) <= tol, (k, rel_err(y, yr))
+        assert rel_err(h, hr) <= tol, (k, rel_err(h, hr))
+
+
+@pytest.mark.parametrize("L1", [1, 100, 128, 257])
+def test_scan_split_continuation_in_place(L1):
+    """Steps [0, L1) then [L1, L), the state carried in one tensor updated in
+    place (h_last is h0), equal one call over [0, L)."""
+    L = 300
+    s = ScanShape(2, 40, 16, L, 1, "f32", has_z=True, dskip="normal", a_kind="loguniform", seed=4300)
+    inp = make_scan_inputs(s)
+    yr, hr = ref_scan(inp)
+    a, b = _scan_steps(inp, 0, L1), _scan_steps(inp, L1, L)
+    state = torch.full((2, 40, 16), float("nan"), dtype=torch.float32, device="cuda")
+    ys = []
+    for part, k, h0 in ((a, 4, None), (b, 1, state)):
+        y, _ = ssm.scan_fwd(_dev(part["u"]), _dev(part["delta"]), _dev(part["A"]), _dev(part["B"]),
+                            _dev(part["C"]), _dev(part["D"]), _dev(part["z"]), h0=h0, n_chunks=k,
+                            h_last=state)
+        ys.append(y.cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat(ys, dim=-1), yr) <= TOL_F32
+    assert rel_err(state.cpu(), hr) <= TOL_F32
+
+
+# ---------------------------------------------------------------------------
 # Selective scan: the named workloads at full size
 # ---------------------------------------------------------------------------
 
@@ -216,7 +264,7 @@ def test_scan_named_workload_full_size(name):
 # Scalar-decay chunked SSD
 # ---------------------------------------------------------------------------
 
-def run_ssd(inp, out_dtype=None, with_h=True):
+def run_ssd(inp, out_dtype=None, with_h=True, h0=None):
     x = _dev(inp["x"])
     out_dt = x.dtype if out_dtype is None else out_dtype
     y = torch.full(x.shape, float("nan"), dtype=out_dt, device="cuda")
@@ -225,14 +273,14 @@ def run_ssd(inp, out_dtype=None, with_h=True):
         b, L, H, P = x.shape
         h = torch.full((b, H, P, inp["B"].shape[3]), float("nan"), dtype=torch.float32, device="cuda")
     y, h = ssm.ssd_chunked_fwd(x, _dev(inp["dt"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
-                               _dev(inp["D"]), _dev(inp["z"]), out_dtype=out_dt, y=y, h_last=h,
-                               return_h_last=with_h)
+                               _dev(inp["D"]), _dev(inp["z"]), h0=_dev(h0), out_dtype=out_dt, y=y,
+                               h_last=h, return_h_last=with_h)
     torch.cuda.synchronize()
     return y.float().cpu(), (None if h is None else h.cpu())
 
 
-def ref_ssd(inp):
-    return oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"])
+def ref_ssd(inp, h0=None):
+    return oracle.ssd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0=h0)
 
 
 SSD_CASES = [
@@ -266,6 +314,36 @@ def test_ssd_f32_output_and_empty():
     e = make_ssd_inputs(SsdShape(2, 0, 2, 64, 128, 1, 64, "bf16", seed=32))
     y, h = run_ssd(e)
     assert y.numel() == 0 and torch.all(h == 0)
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_ssd_h0(N):
+    s = SsdShape(2, 200, 4, 64, N, 2, 64, "bf16", has_z=True, dskip="normal", seed=4400 + N)
+    inp = make_ssd_inputs(s)
+    h0 = make_state((2, 4, 64, N), seed=4500 + N, scale=0.5)
+    y, h = run_ssd(inp, h0=h0)
+    yr, hr = ref_ssd(inp, h0=h0)
+    assert rel_err(y, yr) <= TOL_BF16, rel_err(y, yr)
+    assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
+
+
+@pytest.mark.parametrize("L1", [1, 64, 100])
+def test_ssd_split_continuation_in_place(L1):
+    L = 256
+    s = SsdShape(2, L, 4, 64, 128, 1, 64, "bf16", dskip="normal", seed=4600)
+    inp = make_ssd_inputs(s)
+    yr, hr = ref_ssd(inp)
+    state = torch.full((2, 4, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ys = []
+    for t0, t1, h0 in ((0, L1, None), (L1, L, state)):
+        part = {k: (None if v is None else (v[:, t0:t1].contiguous() if k in ("x", "dt", "B", "C", "z") else v))
+                for k, v in inp.items()}
+        y, _ = ssm.ssd_chunked_fwd(_dev(part["x"]), _dev(part["dt"]), _dev(part["A"]), _dev(part["B"]),
+                                   _dev(part["C"]), _dev(part["D"]), _dev(part["z"]), h0=h0, h_last=state)
+        ys.append(y.float().cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat(ys, dim=1), yr) <= TOL_BF16
+    assert rel_err(state.cpu(), hr) <= TOL_BF16
 
 
 def test_ssd_named_workload_full_size():
