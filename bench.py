@@ -210,6 +210,7 @@ def main():
                                  "hbm_GB/s": round(w.metric_bytes() / wms / 1e6, 1),
                                  "hbm_GB/s_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6, 1),
                                  "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2)}
+        context.update(decode_context(ssm, dev, stream, time_calls))
     torch.cuda.synchronize()
 
     # ---- CPU baseline: the float64 oracle on a bounded sample ------------------
@@ -255,6 +256,44 @@ def main():
         "workloads": context,
     }
     print(json.dumps(out), flush=True)
+
+
+def decode_context(ssm, dev, stream, time_calls):
+    """Single-token decode steps at the large workloads' state shapes: the scan
+    step on the large-channel state (batch 4, 5120 channels, 16 states) and
+    the SSD step on the SSD workload's state (batch 32, 32 heads x 64, 128
+    states).  HBM-bound on the state: it is read and written once per step."""
+    import torch
+    from state_space_model_ssm_amd.synth import make_state
+    g = torch.Generator(device="cpu").manual_seed(6)
+    out = {}
+
+    def rnd(*shape, dtype=torch.bfloat16, pos=False):
+        t = torch.randn(*shape, generator=g)
+        return (t.abs() * 0.01 if pos else t).to(dtype).to(dev)
+
+    b, d, n = 4, 5120, 16
+    u, dl, z = rnd(b, d), rnd(b, d, pos=True), rnd(b, d)
+    A = -torch.rand(d, n, generator=g).add(0.5).to(dev)
+    Bm, Cm, D = rnd(b, 1, n), rnd(b, 1, n), torch.ones(d, device=dev)
+    state = make_state((b, d, n), seed=7).to(dev)
+    y = torch.empty(b, d, dtype=torch.bfloat16, device=dev)
+    ms, _ = time_calls(lambda: ssm.scan_step(u, dl, A, Bm, Cm, D, z, state=state, y=y, stream=stream), 200, 10)
+    nbytes = 2 * state.numel() * 4 + 4 * b * d * 2 + b * d * 2
+    out["decode_scan_step_4x5120_n16_bf16"] = {"ms": round(ms, 5), "state_MB": round(state.numel() * 4 / 1e6, 2),
+                                               "hbm_GB/s": round(nbytes / ms / 1e6, 1)}
+    b, H, P, n = 32, 32, 64, 128
+    x, dt, z = rnd(b, H, P), rnd(b, H, pos=True), None
+    Ah = -torch.rand(H, generator=g).add(0.5).to(dev)
+    Bm, Cm, Dh = rnd(b, 1, n), rnd(b, 1, n), torch.ones(H, device=dev)
+    state = make_state((b, H, P, n), seed=8, scale=0.1).to(dev)
+    y = torch.empty(b, H, P, dtype=torch.bfloat16, device=dev)
+    ms, _ = time_calls(lambda: ssm.ssd_step(x, dt, Ah, Bm, Cm, Dh, z, state=state, y=y, stream=stream), 200, 10)
+    nbytes = 2 * state.numel() * 4 + 2 * x.numel() * 2
+    out["decode_ssd_step_32xh32p64_n128_bf16"] = {"ms": round(ms, 5), "state_MB": round(state.numel() * 4 / 1e6, 2),
+                                                  "hbm_GB/s": round(nbytes / ms / 1e6, 1),
+                                                  "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def ssd_flops(w) -> float:

@@ -191,6 +191,70 @@ SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const
                     float *h_last, const ssd_dims_t *dims, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Single-token decode steps (state cache updated in place)                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sizes of one selective-scan decode step.
+ *   batch, dim (channels), dstate (N), ngroups (G divides dim);
+ *   in_dtype: u, delta, B, C, z; out_dtype: y.  flags, reserved: must be 0.
+ * Supported: dstate a power of two up to 256; any batch, dim >= 0.
+ */
+typedef struct {
+  int64_t batch, dim, dstate, ngroups;
+  int32_t in_dtype, out_dtype;
+  int32_t flags, reserved;
+} ssm_step_dims_t;
+
+/*
+ * One decode step of the selective scan: the recurrence of ssm_scan_fwd at a
+ * single token, continuing from the cached state.  For every (b, d):
+ *   state[n] <- exp(delta * A[d,n]) * state[n] + delta * B[n] * u
+ *   y        = (sum_n C[n] * state[n] + D[d] * u) * silu(z)
+ *   [Mamba-3 NKI], "How it works": decode through step() is the direct
+ *     recurrence h_t = alpha h_{t-1} + beta prev_Bx + gamma B_t x_t with
+ *     output C_t^T h_t; here beta = 0 and gamma = delta (lam = 1);
+ *   [Mamba-3 NKI], "Kernel details", mamba3_siso_decode_state_kernel: the
+ *     state update and the output contraction in one kernel.
+ * Layouts: u, delta, z, y (batch, dim); A (dim, dstate) float32;
+ *   B, C (batch, ngroups, dstate); D (dim) float32 nullable; z nullable;
+ *   state (batch, dim, dstate) float32, read and written in place, 16-byte
+ *   aligned when dstate >= 4.  y and the state must not overlap any input.
+ * Equal to ssm_scan_fwd with seqlen 1, h0 = h_last = state.
+ */
+SSM_API int ssm_scan_step(const void *u, const void *delta, const float *A, const void *B,
+                  const void *C, const float *D, const void *z, float *state, void *y,
+                  const ssm_step_dims_t *dims, void *stream);
+
+/*
+ * Sizes of one SSD decode step: batch, nheads (H), headdim (P), dstate (N),
+ * ngroups (G divides H); in_dtype: x, dt, B, C, z; out_dtype: y.
+ * Supported: any headdim >= 1, dstate a power of two up to 256.
+ */
+typedef struct {
+  int64_t batch, nheads, headdim, dstate, ngroups;
+  int32_t in_dtype, out_dtype;
+  int32_t flags, reserved;
+} ssd_step_dims_t;
+
+/*
+ * One decode step of the scalar-decay SSD: for every (b, h, p),
+ *   state[p][n] <- exp(dt[b,h] * A[h]) * state[p][n] + dt[b,h] * x[p] * B[n]
+ *   y[p]        = (sum_n C[n] * state[p][n] + D[h] * x[p]) * silu(z[p])
+ *   [Mamba-3 NKI], "Kernel details", mamba3_siso_decode_state_kernel: the
+ *     per-head state update alpha h + gamma B (x) x and y = C^T h, batched
+ *     over the heads (beta = 0, gamma = dt here).
+ * Layouts: x, z, y (batch, nheads, headdim); dt (batch, nheads);
+ *   A, D (nheads) float32 (D nullable); B, C (batch, ngroups, dstate);
+ *   state (batch, nheads, headdim, dstate) float32, read and written in place,
+ *   16-byte aligned when dstate >= 4.
+ * Equal to ssd_chunked_fwd with seqlen 1, h0 = h_last = state.
+ */
+SSM_API int ssd_step(const void *x, const void *dt, const float *A, const void *B, const void *C,
+             const float *D, const void *z, float *state, void *y, const ssd_step_dims_t *dims,
+             void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */
 

@@ -117,3 +117,22 @@ def scan(u, delta, A, B, C, D=None, z=None, h0=None):
 def ssd(x, dt, A, B, C, D=None, z=None, h0=None):
     """Scalar-decay SSD in float64 with the default build; see ``Oracle.ssd``."""
     return _load().ssd(x, dt, A, B, C, D, z, h0)
+
+
+def scan_step(u, delta, A, B, C, D=None, z=None, state=None):
+    """One decode step of the selective scan: the recurrence at a single token
+    from the cached ``state`` (zero when None), i.e. ``scan`` with seqlen 1 and
+    h0 = state.  u, delta, z: (batch, dim); B, C: (batch, G, N);
+    state: (batch, dim, N).  Returns (y (batch, dim), new state)."""
+    col = lambda a: None if a is None else f64(a)[..., None]
+    y, h = scan(col(u), col(delta), A, col(B), col(C), D, col(z), state)
+    return y[..., 0], h
+
+
+def ssd_step(x, dt, A, B, C, D=None, z=None, state=None):
+    """One decode step of the scalar-decay SSD: ``ssd`` with seqlen 1 and
+    h0 = state.  x, z: (batch, H, P); dt: (batch, H); B, C: (batch, G, N);
+    state: (batch, H, P, N).  Returns (y (batch, H, P), new state)."""
+    row = lambda a: None if a is None else f64(a)[:, None]
+    y, h = ssd(row(x), row(dt), A, row(B), row(C), D, row(z), state)
+    return y[:, 0], h

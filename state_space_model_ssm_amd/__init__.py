@@ -17,8 +17,8 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
-    "scan_fwd", "ssd_chunked_fwd", "scan_workspace_size", "scan_resolved_chunks",
-    "ssd_workspace_size", "status_string", "last_error", "version",
+    "scan_fwd", "ssd_chunked_fwd", "scan_step", "ssd_step", "scan_workspace_size",
+    "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
 
 SSM_F32, SSM_BF16 = 0, 1
@@ -53,6 +53,18 @@ class SsdDims(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class StepDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SsdStepDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -77,6 +89,10 @@ def lib():
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
+        L.ssm_scan_step.argtypes = [vp] * 9 + [ctypes.POINTER(StepDims), vp]
+        L.ssm_scan_step.restype = i32
+        L.ssd_step.argtypes = [vp] * 9 + [ctypes.POINTER(SsdStepDims), vp]
+        L.ssd_step.restype = i32
         L.ssm_status_string.argtypes = [i32]
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -255,3 +271,65 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64,
                                _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last
+
+
+def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None):
+    """One selective-scan decode step (``ssm_scan_step``); ``state`` is updated
+    in place.  Returns y.
+
+    u, delta, z: (batch, dim); A: (dim, N) float32; B, C: (batch, G, N);
+    D: (dim,) float32; state: (batch, dim, N) float32.
+    """
+    torch = _torch()
+    in_code = _dtype_code(u.dtype)
+    out_dt = u.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != u.dtype:
+            raise TypeError(f"{name} must have dtype {u.dtype}")
+    batch, dim = u.shape
+    G, N = B.shape[1], B.shape[2]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("delta and z must have the shape of u")
+    if B.shape != (batch, G, N) or C.shape != B.shape or A.shape != (dim, N):
+        raise ValueError("B, C must be (batch, ngroups, dstate) and A (dim, dstate)")
+    if state.dtype != torch.float32 or state.shape != (batch, dim, N):
+        raise ValueError("state must be float32 (batch, dim, dstate)")
+    if y is None:
+        y = torch.empty((batch, dim), dtype=out_dt, device=u.device)
+    dims = StepDims(batch=batch, dim=dim, dstate=N, ngroups=G, in_dtype=in_code, out_dtype=out_code,
+                    flags=0, reserved=0)
+    _check(lib().ssm_scan_step(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
+    return y
+
+
+def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None):
+    """One scalar-decay SSD decode step (``ssd_step``); ``state`` is updated in
+    place.  Returns y.
+
+    x, z: (batch, H, P); dt: (batch, H); A, D: (H,) float32; B, C: (batch, G, N);
+    state: (batch, H, P, N) float32.
+    """
+    torch = _torch()
+    in_code = _dtype_code(x.dtype)
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("dt", dt), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} must have dtype {x.dtype}")
+    batch, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if dt.shape != (batch, H) or (z is not None and z.shape != x.shape):
+        raise ValueError("dt must be (batch, H) and z shaped like x")
+    if B.shape != (batch, G, N) or C.shape != B.shape or A.shape != (H,):
+        raise ValueError("B, C must be (batch, ngroups, dstate) and A (nheads,)")
+    if state.dtype != torch.float32 or state.shape != (batch, H, P, N):
+        raise ValueError("state must be float32 (batch, nheads, headdim, dstate)")
+    if y is None:
+        y = torch.empty((batch, H, P), dtype=out_dt, device=x.device)
+    dims = SsdStepDims(batch=batch, nheads=H, headdim=P, dstate=N, ngroups=G, in_dtype=in_code,
+                       out_dtype=out_code, flags=0, reserved=0)
+    _check(lib().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                          _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
+    return y

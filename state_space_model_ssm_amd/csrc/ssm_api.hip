@@ -301,6 +301,98 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
 }
 
 // ---------------------------------------------------------------------------
+// Decode steps
+// ---------------------------------------------------------------------------
+
+static bool step_dstate_ok(int64_t n) {
+  return n == 1 || n == 2 || n == 4 || n == 8 || n == 16 || n == 32 || n == 64 || n == 128 || n == 256;
+}
+
+// Shared checks and launch of both decode steps: `chan` channels per batch
+// row, A of `n_a` floats, dt of `n_dt` elements, D of `n_d` floats.
+static int step_common(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                       const float *D, const void *z, float *state, void *y, int64_t batch, int64_t chan,
+                       int64_t dstate, int64_t ngroups, int64_t headdim, int64_t n_a, int64_t n_dt,
+                       int64_t n_d, int32_t in_dtype, int32_t out_dtype, int per_head, void *stream) {
+  const int64_t n_x = batch * chan;
+  const int64_t n_bc = batch * ngroups * dstate;
+  const int64_t n_h = n_x * dstate;
+  if (n_x > 0 && (!u || !delta || !y || !state)) return fail(SSM_ERR_NULL, "input, dt, state and y are required");
+  if (n_bc > 0 && (!B || !C)) return fail(SSM_ERR_NULL, "B and C are required");
+  if (n_a > 0 && !A) return fail(SSM_ERR_NULL, "A is required");
+  const size_t ei = dtype_size(in_dtype), eo = dtype_size(out_dtype);
+  if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei))
+    return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
+  if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
+  if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
+  if (!aligned(state, dstate >= 4 ? 16 : 4))
+    return fail(SSM_ERR_ALIGN, "state must be %d-byte aligned", dstate >= 4 ? 16 : 4);
+  const Span ins[] = {{u, n_x * ei}, {delta, n_dt * ei}, {z, n_x * ei}, {B, n_bc * ei},
+                      {C, n_bc * ei}, {A, n_a * 4ull},  {D, n_d * 4ull}};
+  const Span sy{y, n_x * eo}, ss{state, n_h * 4ull};
+  for (const Span &s : ins)
+    if (overlap(s, sy) || overlap(s, ss)) return fail(SSM_ERR_SHAPE, "y or the state overlaps an input");
+  if (overlap(sy, ss)) return fail(SSM_ERR_SHAPE, "y overlaps the state");
+  const int64_t tpc = dstate < 4 ? 1 : dstate / 4;
+  if (n_x > 0 && ceil_div(n_x, 256) > kMaxGridX / tpc)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * channels exceeds the grid limit");
+  if (n_x == 0) return ok();
+
+  ssm::StepParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.A = A;
+  p.D = D;
+  p.state = state;
+  p.y = y;
+  p.batch = batch;
+  p.dim = chan;
+  p.ngroups = ngroups;
+  p.headdim = headdim;
+  p.dstate = static_cast<int32_t>(dstate);
+  const hipError_t e = ssm::launch_step(p, per_head, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "step launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int ssm_scan_step(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                  const float *D, const void *z, float *state, void *y, const ssm_step_dims_t *dims,
+                  void *stream) {
+  if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+  const ssm_step_dims_t &d = *dims;
+  if (d.batch < 0 || d.dim < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (d.dstate < 1 || d.ngroups < 1) return fail(SSM_ERR_SHAPE, "dstate and ngroups must be >= 1");
+  if (d.dim % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide dim");
+  if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
+  if (d.flags != 0 || d.reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (!step_dstate_ok(d.dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two up to 256)", (long long)d.dstate);
+  return step_common(u, delta, A, B, C, D, z, state, y, d.batch, d.dim, d.dstate, d.ngroups, 1,
+                     d.dim * d.dstate, d.batch * d.dim, d.dim, d.in_dtype, d.out_dtype, 0, stream);
+}
+
+int ssd_step(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
+             const void *z, float *state, void *y, const ssd_step_dims_t *dims, void *stream) {
+  if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+  const ssd_step_dims_t &d = *dims;
+  if (d.batch < 0 || d.nheads < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (d.headdim < 1 || d.dstate < 1 || d.ngroups < 1)
+    return fail(SSM_ERR_SHAPE, "headdim, dstate and ngroups must be >= 1");
+  if (d.nheads % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide nheads");
+  if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
+  if (d.flags != 0 || d.reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (!step_dstate_ok(d.dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two up to 256)", (long long)d.dstate);
+  if (d.nheads > 0 && d.headdim > kMaxGridX / d.nheads) return fail(SSM_ERR_UNSUPPORTED, "too many channels");
+  return step_common(x, dt, A, B, C, D, z, state, y, d.batch, d.nheads * d.headdim, d.dstate, d.ngroups,
+                     d.headdim, d.nheads, d.batch * d.nheads, d.nheads, d.in_dtype, d.out_dtype, 1, stream);
+}
+
+// ---------------------------------------------------------------------------
 // Diagnostics
 // ---------------------------------------------------------------------------
 

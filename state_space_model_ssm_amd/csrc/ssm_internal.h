@@ -50,4 +50,18 @@ struct SsdParams {
 
 hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
 
+// One decode step (see ssm_scan_step and ssd_step in include/ssm.h).  The
+// SSD step is the scan step over channels d = (head, p) with A, dt and D
+// taken per head (headdim channels per head); the scan step has headdim 1.
+struct StepParams {
+  const void *u, *delta, *B, *C, *z;  // in_dtype
+  const float *A, *D;                 // float32; D nullable
+  float *state;                       // [batch][dim][dstate], updated in place
+  void *y;                            // out_dtype
+  int64_t batch, dim, ngroups, headdim;
+  int32_t dstate;
+};
+
+hipError_t launch_step(const StepParams &p, int per_head, int in_bf16, int out_bf16, hipStream_t stream);
+
 }  // namespace ssm

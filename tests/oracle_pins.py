@@ -318,6 +318,45 @@ def check_ssd_invariants(orc):
     _close(h3, h0, rtol=0.0, what="dt=0 h")
 
 
+def check_decode_steps_chain(orc):
+    """A decode step is the recurrence at one token from a cached state: L
+    steps chained through the state reproduce one run over L steps exactly
+    (same float64 operations in the same order), for the scan and the SSD."""
+    rng = np.random.default_rng(77)
+    b, d, n, L = 2, 5, 4, 9
+    u = rng.standard_normal((b, d, L))
+    dl = np.exp(rng.uniform(-5, -1, (b, d, L)))
+    A = -np.exp(rng.uniform(0, 1.5, (d, n)))
+    B = rng.standard_normal((b, 1, n, L))
+    C = rng.standard_normal((b, 1, n, L))
+    D = rng.standard_normal(d)
+    z = rng.standard_normal((b, d, L))
+    h0 = rng.standard_normal((b, d, n))
+    y, h = orc.scan(u, dl, A, B, C, D, z, h0)
+    st, ys = h0, []
+    for t in range(L):
+        yt, st = orc.scan(u[..., t:t + 1], dl[..., t:t + 1], A, B[..., t:t + 1], C[..., t:t + 1], D,
+                          z[..., t:t + 1], st)
+        ys.append(yt)
+    _close(np.concatenate(ys, axis=-1), y, rtol=0.0, what="scan steps chained")
+    _close(st, h, rtol=0.0, what="scan state after chained steps")
+    H, P, N = 3, 4, 8
+    x = rng.standard_normal((b, L, H, P))
+    dt = np.exp(rng.uniform(-4, -1, (b, L, H)))
+    Ah = -np.exp(rng.uniform(0, 2, H))
+    Bs = rng.standard_normal((b, L, 1, N))
+    Cs = rng.standard_normal((b, L, 1, N))
+    Dh = rng.standard_normal(H)
+    S0 = rng.standard_normal((b, H, P, N))
+    y, h = orc.ssd(x, dt, Ah, Bs, Cs, Dh, None, S0)
+    st, ys = S0, []
+    for t in range(L):
+        yt, st = orc.ssd(x[:, t:t + 1], dt[:, t:t + 1], Ah, Bs[:, t:t + 1], Cs[:, t:t + 1], Dh, None, st)
+        ys.append(yt)
+    _close(np.concatenate(ys, axis=1), y, rtol=0.0, what="ssd steps chained")
+    _close(st, h, rtol=0.0, what="ssd state after chained steps")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -329,4 +368,5 @@ ALL_CHECKS = [
     check_ssd_chunked_equals_recurrence,
     check_ssd_equals_scan_broadcast,
     check_ssd_invariants,
+    check_decode_steps_chain,
 ]

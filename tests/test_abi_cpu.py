@@ -31,7 +31,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 8, declared
+    assert len(declared) == 10, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -177,6 +177,52 @@ def test_empty_inputs_launch_nothing_and_succeed():
     assert _scan(_dims(dim=0), u=None, delta=None, A=None, y=None) == 0  # B, C still have elements
     assert _ssd(_sdims(batch=0), x=None, dt=None, B=None, C=None, y=None) == 0
     assert _ssd(_sdims(nheads=0), x=None, dt=None, A=None, y=None) == 0
+
+
+def _step(dims, u=FAKE, dl=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000,
+          D=None, z=None, state=FAKE + 0x20000000, y=FAKE + 0x10000000, ssd=False):
+    f = ssm.lib().ssd_step if ssd else ssm.lib().ssm_scan_step
+    return f(u, dl, A, B, C, D, z, state, y, ctypes.byref(dims), None)
+
+
+def _stepdims(**kw):
+    base = dict(batch=2, dim=64, dstate=16, ngroups=1, in_dtype=0, out_dtype=0, flags=0, reserved=0)
+    base.update(kw)
+    return ssm.StepDims(**base)
+
+
+def _ssdstepdims(**kw):
+    base = dict(batch=2, nheads=4, headdim=64, dstate=128, ngroups=1, in_dtype=1, out_dtype=1, flags=0,
+                reserved=0)
+    base.update(kw)
+    return ssm.SsdStepDims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(dim=65, ngroups=2), -2), (dict(dstate=12), -5), (dict(dstate=512), -5),
+    (dict(in_dtype=5), -3), (dict(flags=1), -2), (dict(reserved=3), -2), (dict(dstate=0), -2),
+])
+def test_scan_step_rejects_bad_dims(kw, code):
+    assert _step(_stepdims(**kw)) == code, ssm.last_error()
+
+
+def test_step_rejects_null_misaligned_overlap():
+    d = _stepdims()
+    assert _step(d, state=None) == -1
+    assert _step(d, B=None) == -1
+    assert _step(d, state=FAKE + 0x20000004) == -4          # 16-byte state rows for dstate >= 4
+    # dstate < 4 needs only 4-byte alignment: this state passes that check and
+    # is then rejected for overlapping B (no call here reaches a launch).
+    assert _step(_stepdims(dstate=2), state=FAKE + 0x300004) == -2
+    assert _step(d, y=FAKE + 0x100) == -2                   # y inside u
+    assert _step(d, state=FAKE + 0x300000) == -2            # state inside B
+    assert _step(d, state=FAKE + 0x10000000 - 64) == -2     # state overlaps y
+    s = _ssdstepdims()
+    assert _step(s, ssd=True, state=FAKE + 0x20000008) == -4
+    assert _step(_ssdstepdims(nheads=6, ngroups=4), ssd=True) == -2
+    assert _step(_ssdstepdims(dstate=96), ssd=True) == -5
+    assert _step(_ssdstepdims(batch=0), ssd=True, u=None, dl=None, B=None, C=None, y=None, state=None) == 0
+    assert _step(_stepdims(dim=0), u=None, dl=None, A=None, y=None, state=None) == 0
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):

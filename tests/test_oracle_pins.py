@@ -15,3 +15,36 @@ def orc():
 @pytest.mark.parametrize("check", oracle_pins.ALL_CHECKS, ids=lambda f: f.__name__)
 def test_pin(orc, check):
     check(orc)
+
+
+def test_step_wrappers_match_the_definition():
+    """oracle.scan_step / ssd_step take one token's slices; chained over L
+    tokens they equal oracle.scan / ssd over L steps from the same state."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    b, d, n, L = 2, 3, 4, 6
+    u, z = rng.standard_normal((b, d, L)), rng.standard_normal((b, d, L))
+    dl = np.exp(rng.uniform(-4, -1, (b, d, L)))
+    A = -np.exp(rng.uniform(0, 1, (d, n)))
+    B, C = rng.standard_normal((b, 2, n, L)), rng.standard_normal((b, 2, n, L))
+    h0 = rng.standard_normal((b, d * 2 // 2, n))
+    D = rng.standard_normal(d)
+    A2 = np.concatenate([A, A]); D2 = np.concatenate([D, D])
+    u2, z2, dl2 = (np.concatenate([a, a], axis=1) for a in (u, z, dl))
+    h02 = np.concatenate([h0, h0], axis=1)
+    y, h = oracle.scan(u2, dl2, A2, B, C, D2, z2, h02)
+    st, ys = h02, []
+    for t in range(L):
+        yt, st = oracle.scan_step(u2[..., t], dl2[..., t], A2, B[..., t], C[..., t], D2, z2[..., t], st)
+        ys.append(yt)
+    assert np.array_equal(np.stack(ys, axis=-1), y) and np.array_equal(st, h)
+    H, P, N = 2, 3, 4
+    x, dt = rng.standard_normal((b, L, H, P)), np.exp(rng.uniform(-3, -1, (b, L, H)))
+    Bs, Cs = rng.standard_normal((b, L, 1, N)), rng.standard_normal((b, L, 1, N))
+    Ah, S0 = -np.exp(rng.uniform(0, 1, H)), rng.standard_normal((b, H, P, N))
+    y, h = oracle.ssd(x, dt, Ah, Bs, Cs, None, None, S0)
+    st, ys = S0, []
+    for t in range(L):
+        yt, st = oracle.ssd_step(x[:, t], dt[:, t], Ah, Bs[:, t], Cs[:, t], None, None, st)
+        ys.append(yt)
+    assert np.array_equal(np.stack(ys, axis=1), y) and np.array_equal(st, h)

@@ -376,3 +376,77 @@ def test_ssd_deterministic():
     a = run_ssd(inp)
     b = run_ssd(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Single-token decode steps (state cache updated in place)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,N,G,has_z", [("f32", 16, 1, True), ("f32", 1, 1, False), ("f32", 4, 2, True),
+                                             ("f32", 64, 1, True), ("f32", 256, 1, False),
+                                             ("bf16", 16, 1, True), ("bf16", 128, 2, True)])
+def test_scan_decode_steps(dtype, N, G, has_z):
+    """Consecutive ssm_scan_step calls from h0 equal one scan over the same
+    steps from h0 (y at every step, and the final state)."""
+    L = 12
+    s = ScanShape(2, 40, N, L, G, dtype, has_z=has_z, dskip="normal", a_kind="loguniform",
+                  seed=4700 + N + G)
+    inp = make_scan_inputs(s)
+    h0 = make_state((2, 40, N), seed=4800 + N)
+    yr, hr = ref_scan(inp, h0=h0)
+    state = h0.cuda().clone()
+    ys = []
+    for t in range(L):
+        tok = {k: (None if inp[k] is None else inp[k][..., t].contiguous().cuda())
+               for k in ("u", "delta", "z", "B", "C")}
+        y = ssm.scan_step(tok["u"], tok["delta"], _dev(inp["A"]), tok["B"], tok["C"], _dev(inp["D"]),
+                          tok["z"], state=state)
+        ys.append(y.float().cpu())
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    assert rel_err(torch.stack(ys, dim=-1), yr) <= tol
+    assert rel_err(state.cpu(), hr) <= tol
+
+
+@pytest.mark.parametrize("P,N,G,has_z", [(64, 128, 1, False), (64, 64, 2, True), (5, 16, 1, True)])
+def test_ssd_decode_steps(P, N, G, has_z):
+    L = 10
+    s = SsdShape(2, L, 4, P, N, G, 64, "bf16", has_z=has_z, dskip="normal", seed=4900 + P + N)
+    inp = make_ssd_inputs(s)
+    S0 = make_state((2, 4, P, N), seed=5000 + N, scale=0.5)
+    yr, hr = ref_ssd(inp, h0=S0)
+    state = S0.cuda().clone()
+    ys = []
+    for t in range(L):
+        tok = {k: (None if inp[k] is None else inp[k][:, t].contiguous().cuda())
+               for k in ("x", "dt", "z", "B", "C")}
+        y = ssm.ssd_step(tok["x"], tok["dt"], _dev(inp["A"]), tok["B"], tok["C"], _dev(inp["D"]), tok["z"],
+                         state=state)
+        ys.append(y.float().cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(ys, dim=1), yr) <= TOL_BF16
+    assert rel_err(state.cpu(), hr) <= TOL_BF16
+
+
+def test_ssd_prefill_then_128_decode_steps():
+    """A 64-token chunked prefill leaves its state in a cache; 128 decode steps
+    continue from it in place.  Every step's y and the final state match one
+    oracle run over all 192 tokens (head dims 32 x 64, dstate 128)."""
+    Lp, Ld = 64, 128
+    s = SsdShape(1, Lp + Ld, 32, 64, 128, 1, 64, "bf16", dskip="ones", seed=5100)
+    inp = make_ssd_inputs(s)
+    yr, hr = ref_ssd(inp)
+    cache = torch.full((1, 32, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
+    pre = {k: (None if v is None else (v[:, :Lp].contiguous() if k in ("x", "dt", "B", "C") else v))
+           for k, v in inp.items()}
+    y0, _ = ssm.ssd_chunked_fwd(_dev(pre["x"]), _dev(pre["dt"]), _dev(pre["A"]), _dev(pre["B"]),
+                                _dev(pre["C"]), _dev(pre["D"]), None, h_last=cache)
+    ys = [y0.float().cpu()]
+    for t in range(Lp, Lp + Ld):
+        tok = {k: inp[k][:, t].contiguous().cuda() for k in ("x", "dt", "B", "C")}
+        y = ssm.ssd_step(tok["x"], tok["dt"], _dev(inp["A"]), tok["B"], tok["C"], _dev(inp["D"]), None,
+                         state=cache)
+        ys.append(y.float().cpu()[:, None])
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat(ys, dim=1), yr) <= TOL_BF16
+    assert rel_err(cache.cpu(), hr) <= TOL_BF16
