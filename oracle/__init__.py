@@ -39,6 +39,8 @@ class Oracle:
         lib.oracle_scan_f64.argtypes = [i64] * 5 + [dp] * 10
         lib.oracle_scan_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.argtypes = [i64] * 6 + [dp] * 10
+        lib.oracle_scan_bwd_f64.argtypes = [i64] * 5 + [dp] * 18
+        lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.restype = ctypes.c_int
         self.lib = lib
 
@@ -63,6 +65,29 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the shapes")
         return y, h
+
+    def scan_bwd(self, u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
+        """Gradients of the selective scan in float64 for upstream gradients dy
+        (batch, dim, L) and dh_last (batch, dim, N; None = zero).  Returns a
+        dict: du, ddelta, dA, dB, dC, and dD / dz / dh0 (dD, dz None when D, z
+        are None)."""
+        u, delta, A, B, C, D, z, h0, dy, dh_last = map(f64, (u, delta, A, B, C, D, z, h0, dy, dh_last))
+        batch, dim, L = u.shape
+        G, N = B.shape[1], B.shape[2]
+        assert delta.shape == u.shape and A.shape == (dim, N) and C.shape == B.shape
+        assert B.shape == (batch, G, N, L) and dy.shape == u.shape
+        assert dh_last is None or dh_last.shape == (batch, dim, N)
+        g = {"du": np.zeros_like(u), "ddelta": np.zeros_like(u), "dA": np.zeros((dim, N)),
+             "dB": np.zeros_like(B), "dC": np.zeros_like(C),
+             "dD": None if D is None else np.zeros(dim), "dz": None if z is None else np.zeros_like(u),
+             "dh0": np.zeros((batch, dim, N))}
+        rc = self.lib.oracle_scan_bwd_f64(batch, dim, N, L, G, _ptr(u), _ptr(delta), _ptr(A), _ptr(B),
+                                          _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last),
+                                          _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                          _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_f64 rejected the shapes")
+        return g
 
     def ssd(self, x, dt, A, B, C, D=None, z=None, h0=None):
         """Scalar-decay SSD recurrence in float64. Returns (y, h_last).
@@ -112,6 +137,11 @@ def _ptr(a):
 def scan(u, delta, A, B, C, D=None, z=None, h0=None):
     """Selective scan in float64 with the default build; see ``Oracle.scan``."""
     return _load().scan(u, delta, A, B, C, D, z, h0)
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
+    """Selective-scan gradients in float64 with the default build; see ``Oracle.scan_bwd``."""
+    return _load().scan_bwd(u, delta, A, B, C, D, z, h0, dy, dh_last)
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, h0=None):

@@ -135,3 +135,118 @@ int oracle_ssd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
     }
     return 0;
 }
+
+/*
+ * Gradients of the selective scan above (reverse mode), float64.
+ *
+ * For a loss with upstream gradients dy (batch, dim, seqlen) on y and dh_last
+ * (batch, dim, dstate; nullable = zero) on h_last, returns the loss gradient
+ * with respect to every input: du, ddelta, dz (batch, dim, seqlen; dz only
+ * when z is given), dA (dim, dstate), dB, dC (batch, ngroups, dstate,
+ * seqlen), dD (dim; when Dskip is given) and dh0 (batch, dim, dstate).
+ *
+ * The pages report that the implementations' gradients are checked against a
+ * reference ("Mamba-3 NKI Kernels for AWS Neuron", section "Correctness",
+ * backward parity) but print no formulas: this is the chain rule applied to
+ * the forward definition, step by step.  With yhat_t = C_t.h_t + D x_t the
+ * output before the gate and lambda_t = dL/dh_t, walking t backwards:
+ *   dyhat_t   = dy_t silu(z_t);   dz_t = dy_t yhat_t silu'(z_t)
+ *   lambda_t  = dyhat_t C_t + abar_{t+1} lambda_{t+1}   (lambda_{L-1} also
+ *               receives dh_last)
+ *   dC_t     += dyhat_t h_t;      dB_t += lambda_t delta_t x_t
+ *   dx_t      = dyhat_t D + sum_n lambda_t delta_t B_t
+ *   ddelta_t  = sum_n lambda_t (B_t x_t + A abar_t h_{t-1})
+ *   dA       += lambda_t delta_t abar_t h_{t-1};   dD += dyhat_t x_t
+ *   dh0       = abar_0 lambda_0
+ * The forward states of one channel are recomputed and kept (seqlen + 1 rows).
+ * Returns 0, -1 on a bad shape, -2 if memory runs out.
+ */
+#include <stdlib.h>
+
+int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                        int64_t ngroups, const double *u, const double *delta,
+                        const double *A, const double *B, const double *C,
+                        const double *Dskip, const double *z, const double *h0,
+                        const double *dy, const double *dh_last,
+                        double *du, double *ddelta, double *dA, double *dB,
+                        double *dC, double *dD, double *dz, double *dh0)
+{
+    if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0 || ngroups < 1 ||
+        dim % ngroups != 0)
+        return -1;
+    const int64_t dpg = dim / ngroups;
+    double *hs = malloc(sizeof(double) * (size_t)((seqlen + 1) * dstate));
+    double *yhat = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+    double *lam = malloc(sizeof(double) * (size_t)dstate);
+    if (!hs || !yhat || !lam) {
+        free(hs); free(yhat); free(lam);
+        return -2;
+    }
+    for (int64_t k = 0; k < dim * dstate; ++k) dA[k] = 0.0;
+    for (int64_t k = 0; k < batch * ngroups * dstate * seqlen; ++k) {
+        dB[k] = 0.0;
+        dC[k] = 0.0;
+    }
+    if (Dskip)
+        for (int64_t d = 0; d < dim; ++d) dD[d] = 0.0;
+
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const int64_t g = d / dpg;
+            /* forward, keeping every state: hs[t + 1] is h after step t */
+            for (int64_t n = 0; n < dstate; ++n)
+                hs[n] = h0 ? h0[(b * dim + d) * dstate + n] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t i = (b * dim + d) * seqlen + t;
+                double acc = 0.0;
+                for (int64_t n = 0; n < dstate; ++n) {
+                    const int64_t j = ((b * ngroups + g) * dstate + n) * seqlen + t;
+                    const double abar = exp(delta[i] * A[d * dstate + n]);
+                    hs[(t + 1) * dstate + n] = abar * hs[t * dstate + n] + delta[i] * B[j] * u[i];
+                    acc += C[j] * hs[(t + 1) * dstate + n];
+                }
+                if (Dskip) acc += Dskip[d] * u[i];
+                yhat[t] = acc;
+            }
+            /* backward */
+            for (int64_t n = 0; n < dstate; ++n)
+                lam[n] = dh_last ? dh_last[(b * dim + d) * dstate + n] : 0.0;
+            for (int64_t t = seqlen - 1; t >= 0; --t) {
+                const int64_t i = (b * dim + d) * seqlen + t;
+                const double dl = delta[i], x = u[i];
+                double dyh = dy[i];
+                if (z) {
+                    const double s = 1.0 / (1.0 + exp(-z[i]));
+                    dyh = dy[i] * z[i] * s;
+                    dz[i] = dy[i] * yhat[t] * s * (1.0 + z[i] * (1.0 - s));
+                }
+                double dx = 0.0, ddl = 0.0;
+                if (Dskip) {
+                    dD[d] += dyh * x;
+                    dx = dyh * Dskip[d];
+                }
+                for (int64_t n = 0; n < dstate; ++n) {
+                    const int64_t j = ((b * ngroups + g) * dstate + n) * seqlen + t;
+                    const double a = A[d * dstate + n];
+                    const double abar = exp(dl * a);
+                    const double hprev = hs[t * dstate + n];
+                    const double l = lam[n] + dyh * C[j];
+                    dC[j] += dyh * hs[(t + 1) * dstate + n];
+                    dB[j] += l * dl * x;
+                    dx += l * dl * B[j];
+                    ddl += l * (B[j] * x + a * abar * hprev);
+                    dA[d * dstate + n] += l * dl * abar * hprev;
+                    lam[n] = abar * l;
+                }
+                du[i] = dx;
+                ddelta[i] = ddl;
+            }
+            for (int64_t n = 0; n < dstate; ++n)
+                dh0[(b * dim + d) * dstate + n] = lam[n];
+        }
+    }
+    free(hs);
+    free(yhat);
+    free(lam);
+    return 0;
+}

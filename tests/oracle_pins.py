@@ -357,6 +357,39 @@ def check_decode_steps_chain(orc):
     _close(st, h, rtol=0.0, what="ssd state after chained steps")
 
 
+def check_scan_bwd_finite_differences(orc):
+    """The backward against central finite differences of the forward, on tiny
+    problems with every optional input present: the gradient of
+    L = sum(dy * y) + sum(dh_last * h_last) with respect to each element of
+    u, delta, A, B, C, D, z and h0 (two group counts)."""
+    names = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "h0": "dh0"}
+    for seed, (b, d, n, L, G) in ((11, (2, 3, 4, 6, 1)), (12, (1, 4, 2, 5, 2))):
+        rng = np.random.default_rng(seed)
+        inp = {"u": rng.standard_normal((b, d, L)), "delta": np.exp(rng.uniform(-3, 0, (b, d, L))),
+               "A": -np.exp(rng.uniform(-1, 1, (d, n))), "B": rng.standard_normal((b, G, n, L)),
+               "C": rng.standard_normal((b, G, n, L)), "D": rng.standard_normal(d),
+               "z": rng.standard_normal((b, d, L)), "h0": rng.standard_normal((b, d, n))}
+        dy, dhl = rng.standard_normal((b, d, L)), rng.standard_normal((b, d, n))
+
+        def loss(v):
+            y, h = orc.scan(v["u"], v["delta"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"])
+            return float(np.sum(dy * y) + np.sum(dhl * h))
+
+        g = orc.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                         inp["h0"], dy, dhl)
+        for k, gk in names.items():
+            fd = np.zeros_like(inp[k])
+            for idx in np.ndindex(inp[k].shape):
+                e = 1e-6 * max(1.0, abs(inp[k][idx]))
+                lo, hi = dict(inp), dict(inp)
+                lo[k], hi[k] = inp[k].copy(), inp[k].copy()
+                lo[k][idx] -= e
+                hi[k][idx] += e
+                fd[idx] = (loss(hi) - loss(lo)) / (2 * e)
+            _close(g[gk], fd, rtol=1e-7, what=f"d{k} against finite differences (seed {seed})")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -369,4 +402,5 @@ ALL_CHECKS = [
     check_ssd_equals_scan_broadcast,
     check_ssd_invariants,
     check_decode_steps_chain,
+    check_scan_bwd_finite_differences,
 ]

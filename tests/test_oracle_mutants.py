@@ -2,7 +2,9 @@
 pins to catch every one of them.  This shows the pins constrain each term of
 the definition: the decay and its sign, the dt on the input, the readout order,
 B versus C, the D skip, the gate and its order, the group index, the B/C
-layout, the initial state and the final state."""
+layout, the initial state and the final state; and each term of the backward
+(the adjoint's decay, the state each gradient uses, the gate derivative, the
+upstream state gradient)."""
 import os
 import subprocess
 
@@ -38,6 +40,16 @@ MUTANTS = [
     ("ssd_wrong_state_index", [("double *hp = &H[p * dstate + n];", "double *hp = &H[n * headdim + p];")]),
     ("ssd_group_index", [("const int64_t g = hd / hpg;", "const int64_t g = hd % ngroups;")]),
     ("ssd_h0_ignored", [("H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;", "H[k] = 0.0;")]),
+    ("bwd_no_decay_in_adjoint", [("lam[n] = abar * l;", "lam[n] = l;")]),
+    ("bwd_dA_uses_new_state", [("dA[d * dstate + n] += l * dl * abar * hprev;",
+                                "dA[d * dstate + n] += l * dl * abar * hs[(t + 1) * dstate + n];")]),
+    ("bwd_ddelta_no_decay_term", [("ddl += l * (B[j] * x + a * abar * hprev);", "ddl += l * (B[j] * x);")]),
+    ("bwd_dC_uses_old_state", [("dC[j] += dyh * hs[(t + 1) * dstate + n];", "dC[j] += dyh * hs[t * dstate + n];")]),
+    ("bwd_gate_derivative", [("dz[i] = dy[i] * yhat[t] * s * (1.0 + z[i] * (1.0 - s));",
+                              "dz[i] = dy[i] * yhat[t] * s;")]),
+    ("bwd_readout_ungated", [("const double l = lam[n] + dyh * C[j];", "const double l = lam[n] + dy[i] * C[j];")]),
+    ("bwd_dh_last_ignored", [("lam[n] = dh_last ? dh_last[(b * dim + d) * dstate + n] : 0.0;", "lam[n] = 0.0;")]),
+    ("bwd_dD_ungated", [("dD[d] += dyh * x;", "dD[d] += dy[i] * x;")]),
 ]
 
 
