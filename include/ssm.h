@@ -128,6 +128,51 @@ SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const
                  const void *C, const float *D, const void *z, const float *h0, void *y,
                  float *h_last, const ssm_scan_dims_t *dims, void *stream);
 
+/*
+ * Workspace ssm_scan_bwd needs for `dims`: the forward state every 16 steps,
+ * 4 * batch * dim * dstate * ceil(seqlen / 16) bytes (n_chunks is ignored).
+ */
+SSM_API int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes);
+
+/*
+ * Selective-scan backward: gradients of a loss L with respect to every input
+ * of ssm_scan_fwd, given dy = dL/dy and dh_last = dL/dh_last.
+ *
+ * The chain rule on the forward above (the pages report gradient checks,
+ * [Mamba-3 NKI] "Correctness", backward parity, but print no backward).  With
+ * yhat = C.h + D u the output before the gate and lambda_t = dL/dh_t, walked
+ * from the last step to the first (lambda after the last step = dh_last):
+ *   dyhat_t  = dy_t silu(z_t),  dz_t = dy_t yhat_t silu'(z_t)
+ *   lambda_t = dyhat_t C_t + exp(delta_{t+1} A) lambda_{t+1}
+ *   du_t     = dyhat_t D + sum_n lambda_t delta_t B_t
+ *   ddelta_t = sum_n lambda_t (B_t u_t + A exp(delta_t A) h_{t-1})
+ *   dB_t     = sum over the group's channels of lambda_t delta_t u_t
+ *   dC_t     = sum over the group's channels of dyhat_t h_t
+ *   dA       = sum over batch and steps of lambda_t delta_t exp(delta_t A) h_{t-1}
+ *   dD       = sum over batch and steps of dyhat_t u_t;   dh0 = exp(delta_0 A) lambda_0
+ * The forward is recomputed (from h0, checkpointed every 16 steps in the
+ * workspace); nothing from the forward call is needed.
+ *
+ * Inputs: as ssm_scan_fwd (dims, u, delta, A, B, C, D, z, h0), plus
+ *   dy      : (batch, dim, seqlen) out_dtype
+ *   dh_last : (batch, dim, dstate) float32, nullable (zero)
+ * Outputs (overwritten):
+ *   du, ddelta : (batch, dim, seqlen) in_dtype
+ *   dz         : (batch, dim, seqlen) in_dtype, required when z is given
+ *   dA         : (dim, dstate) float32
+ *   dB, dC     : (batch, ngroups, dstate, seqlen) float32
+ *   dD         : (dim) float32, required when D is given (ignored otherwise)
+ *   dh0        : (batch, dim, dstate) float32, nullable
+ * No output may overlap an input, another output or the workspace.  dA, dB,
+ * dC and dD are accumulated with float32 atomics: their summation order, and
+ * so their last bits, vary between calls; the other outputs are
+ * deterministic.  Supported sizes are those of ssm_scan_fwd.
+ */
+SSM_API int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, const float *h0, const void *dy,
+                 const float *dh_last, void *du, void *ddelta, float *dA, float *dB, float *dC,
+                 float *dD, void *dz, float *dh0, const ssm_scan_dims_t *dims, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Scalar-decay chunked SSD                                                  */
 /* ------------------------------------------------------------------------ */

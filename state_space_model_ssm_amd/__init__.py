@@ -17,7 +17,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
-    "scan_fwd", "ssd_chunked_fwd", "scan_step", "ssd_step", "scan_workspace_size",
+    "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "scan_step", "ssd_step", "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
 
@@ -89,6 +89,10 @@ def lib():
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
+        L.ssm_scan_bwd.argtypes = [vp] * 18 + [ctypes.POINTER(ScanDims), vp]
+        L.ssm_scan_bwd.restype = i32
+        L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_scan_bwd_workspace_size.restype = i32
         L.ssm_scan_step.argtypes = [vp] * 9 + [ctypes.POINTER(StepDims), vp]
         L.ssm_scan_step.restype = i32
         L.ssd_step.argtypes = [vp] * 9 + [ctypes.POINTER(SsdStepDims), vp]
@@ -218,6 +222,49 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_ch
                             _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last
+
+
+def scan_bwd_workspace_size(dims: ScanDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssm_scan_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, workspace=None, stream=None):
+    """Selective-scan backward (``ssm_scan_bwd``): gradients of a loss with
+    upstream gradients dy (shaped like y, in y's dtype) and dh_last (float32,
+    optional).  Returns a dict du, ddelta (u's dtype), dA, dB, dC (float32),
+    dD (float32, when D is given), dz (u's dtype, when z is given) and dh0
+    (float32)."""
+    torch = _torch()
+    in_code = _dtype_code(u.dtype)
+    out_code = _dtype_code(dy.dtype)
+    batch, dim, L = u.shape
+    G, N = B.shape[1], B.shape[2]
+    if dy.shape != u.shape or (dh_last is not None and dh_last.shape != (batch, dim, N)):
+        raise ValueError("dy must be shaped like u and dh_last (batch, dim, dstate)")
+    if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, dim, N)):
+        raise ValueError("h0 must be float32 (batch, dim, dstate)")
+    dims = _scan_dims(u, B, in_code, out_code, 0)
+    need = scan_bwd_workspace_size(dims)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+        dims.workspace = _ptr(workspace)
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    f32 = torch.float32
+    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+         "dA": torch.empty((dim, N), dtype=f32, device=u.device),
+         "dB": torch.empty(B.shape, dtype=f32, device=u.device),
+         "dC": torch.empty(C.shape, dtype=f32, device=u.device),
+         "dD": None if D is None else torch.empty((dim,), dtype=f32, device=u.device),
+         "dz": None if z is None else torch.empty_like(u),
+         "dh0": torch.empty((batch, dim, N), dtype=f32, device=u.device)}
+    _check(lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
+                              _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
+                              _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
+                              ctypes.byref(dims), _stream(stream)))
+    return g
 
 
 def _ssd_dims(x, B, chunk, in_dtype, out_dtype) -> SsdDims:

@@ -1,0 +1,295 @@
+// Selective-scan backward for gfx950 (CDNA4, wave64).
+//
+// The forward ("We brought Mamba to Trainium", section "Mamba: bringing an
+// unsupported model to the chip"; discretisation and gate from "Mamba-3 NKI
+// Kernels for AWS Neuron", section "How it works", Phases 0 and 5) is
+//   h_t = exp(dt_t A) h_{t-1} + dt_t B_t u_t,   y_t = (C_t.h_t + D u_t) silu(z_t).
+// The pages check gradients (same page, section "Correctness") but print no
+// backward; this is the chain rule on that forward.  With lambda_t = dL/dh_t
+// walked backwards from dh_last:
+//   dyhat_t  = dy_t silu(z_t),   dz_t = dy_t yhat_t silu'(z_t)
+//   lambda_t = dyhat_t C_t + exp(dt_{t+1} A) lambda_{t+1}
+//   dC_t += dyhat_t h_t          dB_t += lambda_t dt_t u_t      (over channels)
+//   du_t  = dyhat_t D + sum_n lambda_t dt_t B_t
+//   ddt_t = sum_n lambda_t (B_t u_t + A exp(dt_t A) h_{t-1})
+//   dA   += lambda_t dt_t exp(dt_t A) h_{t-1}     dD += dyhat_t u_t
+//   dh0   = exp(dt_0 A) lambda_0
+//
+// Decomposition: the forward kernel in checkpoint mode first stores h every
+// kScanCkptStep = 16 steps.  Here one 256-thread workgroup takes a tile of
+// 256 / N channels (one (channel, state) per thread, as in the forward) and
+// walks 16-step time tiles from the last to the first: stage the tile's
+// inputs in LDS, recompute its 16 states from the checkpoint (kept in
+// registers), read out yhat when there is a gate, then run the adjoint
+// backwards.  Sums over states (du, ddt) go through LDS partials
+// [channel][step][state]; sums over the workgroup's channels (dB, dC) through
+// [step][state][channel] and are then added to the float32 outputs with
+// atomics, as are dA and dD (so their summation order is not fixed).
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kT = static_cast<int>(kScanCkptStep);  // steps per tile
+
+__device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
+  p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+}
+
+template <int N>
+struct BwdCfg {
+  static constexpr int CH = 256 / N;            // channels per workgroup
+  static constexpr int TP = kT + 1;             // staged row (floats): odd, so rows hit distinct banks
+  static constexpr int JS = N >= 4 ? N + 4 : N; // state partials of one step
+  static constexpr int RS_ALIGN = N >= 4 ? (N < 64 ? N : 0) : 4;
+  static constexpr int RS = kT * JS + ((RS_ALIGN - (kT * JS) % 64) % 64 + 64) % 64;  // per channel
+  static constexpr int CS = CH + 4;             // channel partials of one (step, state)
+  static constexpr int PAIRS_CT = CH * kT;      // (channel, step) sums per tile
+  static constexpr int PAIRS_NT = N * kT;       // (state, step) sums per tile
+};
+
+template <typename Tin, typename Tout, int N, bool HAS_Z>
+__global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
+  using Cfg = BwdCfg<N>;
+  constexpr int CH = Cfg::CH, TP = Cfg::TP, JS = Cfg::JS, RS = Cfg::RS, CS = Cfg::CS;
+
+  __shared__ float sDl[CH * TP], sU[CH * TP], sDy[CH * TP], sZ[HAS_Z ? CH * TP : 1];
+  __shared__ float sB[N * TP], sC[N * TP];
+  __shared__ __attribute__((aligned(16))) float sQ[CH * RS];          // [channel][step][state]
+  __shared__ __attribute__((aligned(16))) float sR[kT * N * CS];      // [step][state][channel]
+
+  const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
+  const Tin *__restrict__ gdl = static_cast<const Tin *>(p.delta);
+  const Tin *__restrict__ gB = static_cast<const Tin *>(p.B);
+  const Tin *__restrict__ gC = static_cast<const Tin *>(p.C);
+  const Tin *__restrict__ gz = static_cast<const Tin *>(p.z);
+  const Tout *__restrict__ gdy = static_cast<const Tout *>(p.dy);
+
+  const int tid = threadIdx.x;
+  const int n = tid % N;
+  const int chl = tid / N;
+  int64_t blk = blockIdx.x;
+  const int64_t tile = blk % p.tiles_per_group;
+  blk /= p.tiles_per_group;
+  const int64_t g = blk % p.ngroups;
+  const int64_t b = blk / p.ngroups;
+  const int64_t L = p.seqlen;
+  const int64_t ch0 = tile * CH;
+  const int nvalid = static_cast<int>(min(static_cast<int64_t>(CH), p.dim_per_group - ch0));
+  const int64_t d0 = g * p.dim_per_group + ch0;
+  const int64_t ntiles = (L + kT - 1) / kT;
+  const bool mine = chl < nvalid;
+  const int64_t d = d0 + (mine ? chl : 0);
+  const float a_n = mine ? p.A[d * N + n] : 0.0f;
+  const float a2 = a_n * kLog2e;
+
+  float lam = (mine && p.dh_last != nullptr) ? p.dh_last[(b * p.dim + d) * N + n] : 0.0f;
+  float dA_acc = 0.0f;
+  float dD_acc[(Cfg::PAIRS_CT + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) dD_acc[k] = 0.0f;
+
+  for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
+    const int64_t t0 = ti * kT;
+    __syncthreads();  // the previous tile is done with every LDS buffer
+    // ---- stage the tile: rows of 16 steps, zero past the end ---------------
+    for (int e = tid; e < CH * kT; e += 256) {
+      const int r = e / kT, t = e % kT;
+      const int64_t row = (b * p.dim + d0 + min(r, nvalid - 1)) * L;
+      const bool in = t0 + t < L;
+      sDl[r * TP + t] = in ? ld(gdl, row + t0 + t) : 0.0f;
+      sU[r * TP + t] = in ? ld(gu, row + t0 + t) : 0.0f;
+      sDy[r * TP + t] = (in && r < nvalid) ? ld(gdy, row + t0 + t) : 0.0f;
+      if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(gz, row + t0 + t) : 0.0f;
+    }
+    for (int e = tid; e < N * kT; e += 256) {
+      const int r = e / kT, t = e % kT;
+      const int64_t row = ((b * p.ngroups + g) * N + r) * L;
+      const bool in = t0 + t < L;
+      sB[r * TP + t] = in ? ld(gB, row + t0 + t) : 0.0f;
+      sC[r * TP + t] = in ? ld(gC, row + t0 + t) : 0.0f;
+    }
+    const float h_start = mine ? p.ckpt[((b * p.dim + d) * ntiles + ti) * N + n] : 0.0f;
+    __syncthreads();
+
+    // ---- recompute the tile's states; readout partials for the gate --------
+    float hist[kT];
+    {
+      float h = h_start;
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        const float dl = sDl[chl * TP + t];
+        h = fmaf(__builtin_amdgcn_exp2f(dl * a2), h, dl * sU[chl * TP + t] * sB[n * TP + t]);
+        hist[t] = h;
+        if constexpr (HAS_Z) sQ[chl * RS + t * JS + n] = sC[n * TP + t] * h;
+      }
+    }
+    // ---- per (channel, step): dyhat (and dz, from yhat) --------------------
+    if constexpr (HAS_Z) __syncthreads();
+#pragma unroll
+    for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
+      const int e = tid + 256 * k;
+      if (e < Cfg::PAIRS_CT) {
+        const int r = e / kT, t = e % kT;
+        const float uu = sU[r * TP + t];
+        const float dy = sDy[r * TP + t];
+        const float dskip = (p.D != nullptr && r < nvalid) ? p.D[d0 + r] : 0.0f;
+        float dyh = dy;
+        if constexpr (HAS_Z) {
+          float yhat = dskip * uu;
+#pragma unroll
+          for (int i = 0; i < N; ++i) yhat += sQ[r * RS + t * JS + i];
+          const float zz = sZ[r * TP + t];
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+          dyh = dy * zz * sg;
+          if (r < nvalid && t0 + t < L)
+            st(static_cast<Tin *>(p.dz), (b * p.dim + d0 + r) * L + t0 + t,
+               dy * yhat * sg * (1.0f + zz * (1.0f - sg)));
+        }
+        dD_acc[k] = fmaf(dyh, uu, dD_acc[k]);
+        // sDy now holds dyhat; the reader of (r, t) wrote it and no one else
+        // reads sDy[r][t] before the barrier below.
+        sDy[r * TP + t] = dyh;
+      }
+    }
+    __syncthreads();
+
+    // ---- adjoint, backwards through the tile --------------------------------
+    float pdu[kT], pddl[kT], pdB[kT], pdC[kT];
+#pragma unroll
+    for (int t = kT - 1; t >= 0; --t) {
+      const float dl = sDl[chl * TP + t];
+      const float uu = sU[chl * TP + t];
+      const float dyh = sDy[chl * TP + t];
+      const float bv = sB[n * TP + t];
+      const float cv = sC[n * TP + t];
+      const float a = __builtin_amdgcn_exp2f(dl * a2);
+      const float hprev = t > 0 ? hist[t - 1] : h_start;
+      const float l = fmaf(dyh, cv, lam);
+      pdC[t] = mine ? dyh * hist[t] : 0.0f;
+      pdB[t] = mine ? l * dl * uu : 0.0f;
+      pdu[t] = l * dl * bv;
+      pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
+      dA_acc = fmaf(l * dl * a, hprev, dA_acc);
+      lam = a * l;
+    }
+
+    // ---- reductions: (du over states, dB over channels), then (ddt, dC) ---
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+#pragma unroll
+      for (int t = 0; t < kT; ++t) {
+        sQ[chl * RS + t * JS + n] = phase == 0 ? pdu[t] : pddl[t];
+        sR[(t * N + n) * CS + chl] = phase == 0 ? pdB[t] : pdC[t];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
+        const int e = tid + 256 * k;
+        if (e < Cfg::PAIRS_CT) {
+          const int r = e / kT, t = e % kT;
+          float s = 0.0f;
+#pragma unroll
+          for (int i = 0; i < N; ++i) s += sQ[r * RS + t * JS + i];
+          if (r < nvalid && t0 + t < L) {
+            const int64_t o = (b * p.dim + d0 + r) * L + t0 + t;
+            if (phase == 0) {
+              const float dskip = p.D != nullptr ? p.D[d0 + r] : 0.0f;
+              st(static_cast<Tin *>(p.du), o, fmaf(sDy[r * TP + t], dskip, s));
+            } else {
+              st(static_cast<Tin *>(p.ddelta), o, s);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < (Cfg::PAIRS_NT + 255) / 256; ++k) {
+        const int e = tid + 256 * k;
+        if (e < Cfg::PAIRS_NT) {
+          const int t = e / N, nn = e % N;
+          float s = 0.0f;
+#pragma unroll
+          for (int i = 0; i < CH; ++i) s += sR[(t * N + nn) * CS + i];
+          if (t0 + t < L)
+            atomicAdd((phase == 0 ? p.dB : p.dC) + ((b * p.ngroups + g) * N + nn) * L + t0 + t, s);
+        }
+      }
+      if (phase == 0) __syncthreads();
+    }
+  }
+
+  if (mine) {
+    if (p.dh0 != nullptr) p.dh0[(b * p.dim + d) * N + n] = lam;
+    atomicAdd(p.dA + d * N + n, dA_acc);
+  }
+  if (p.dD != nullptr) {
+#pragma unroll
+    for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
+      const int e = tid + 256 * k;
+      if (e < Cfg::PAIRS_CT && e / kT < nvalid) atomicAdd(p.dD + d0 + e / kT, dD_acc[k]);
+    }
+  }
+}
+
+__global__ void zero_kernel(float *p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0.0f;
+}
+
+hipError_t zero(float *p, int64_t n, hipStream_t stream) {
+  if (p == nullptr || n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int64_t blocks = want < 8192 ? want : 8192;
+  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, int N>
+hipError_t launch_bwd_n(const ScanBwdParams &p, hipStream_t stream) {
+  const int64_t blocks = p.batch * p.ngroups * p.tiles_per_group;
+  if (blocks == 0) return hipSuccess;
+  if (p.z != nullptr)
+    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tout, N, true>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tout, N, false>), dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_bwd_typed(const ScanBwdParams &p, hipStream_t stream) {
+  switch (p.dstate) {
+    case 1: return launch_bwd_n<Tin, Tout, 1>(p, stream);
+    case 2: return launch_bwd_n<Tin, Tout, 2>(p, stream);
+    case 4: return launch_bwd_n<Tin, Tout, 4>(p, stream);
+    case 8: return launch_bwd_n<Tin, Tout, 8>(p, stream);
+    case 16: return launch_bwd_n<Tin, Tout, 16>(p, stream);
+    case 32: return launch_bwd_n<Tin, Tout, 32>(p, stream);
+    case 64: return launch_bwd_n<Tin, Tout, 64>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hipStream_t stream) {
+  hipError_t e;
+  if ((e = zero(p.dA, p.dim * p.dstate, stream)) != hipSuccess) return e;
+  if ((e = zero(p.dB, p.batch * p.ngroups * p.dstate * p.seqlen, stream)) != hipSuccess) return e;
+  if ((e = zero(p.dC, p.batch * p.ngroups * p.dstate * p.seqlen, stream)) != hipSuccess) return e;
+  if ((e = zero(p.dD, p.D != nullptr ? p.dim : 0, stream)) != hipSuccess) return e;
+  if (!in_bf16 && !out_bf16) return launch_bwd_typed<float, float>(p, stream);
+  if (!in_bf16 && out_bf16) return launch_bwd_typed<float, uint16_t>(p, stream);
+  if (in_bf16 && !out_bf16) return launch_bwd_typed<uint16_t, float>(p, stream);
+  return launch_bwd_typed<uint16_t, uint16_t>(p, stream);
+}
+
+}  // namespace ssm

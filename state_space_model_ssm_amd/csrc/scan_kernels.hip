@@ -195,7 +195,10 @@ struct DppOps {
   F4 b4[4], c4[4];
 };
 
-template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z>
+// SUMMARY: no readout; reduce the chunk to (decay product, end state).
+// CKPT (with SUMMARY, one chunk): instead store the state at every
+// kScanCkptStep-step boundary, from h0, for the backward pass.
+template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z, bool CKPT = false>
 __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
@@ -254,7 +257,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   const bool mine = chl < nvalid;
   const int64_t d = d0 + chl;
   const float a2 = mine ? p.A[d * N + n] * kLog2e : 0.0f;
-  float h = (!SUMMARY && p.h0 != nullptr && mine) ? p.h0[(b * p.dim + d) * N + n] : 0.0f;
+  float h = ((!SUMMARY || CKPT) && p.h0 != nullptr && mine) ? p.h0[(b * p.dim + d) * N + n] : 0.0f;
   float prod = 1.0f;
   if (!SUMMARY && c > 0 && mine) {
     const float *cr = p.carry + (b * p.dim + d) * static_cast<int64_t>(p.n_chunks - 1) * (2 * N);
@@ -422,7 +425,13 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
       for (int i = 0; i < 16; ++i) sP[chl * RS + i * JS + n] = pr[i / 4].v[i % 4];
     }
   };
-  auto recur_block = [&](int par, int blk) __attribute__((always_inline)) {
+  auto recur_block = [&](int par, int blk, int64_t t0) __attribute__((always_inline)) {
+    if constexpr (CKPT) {
+      static_assert(kScanCkptStep % BS == 0 || BS % kScanCkptStep == 0, "checkpoint grid");
+      const int64_t ts = t0 + blk * BS;
+      if (mine && ts < t_end && (ts - t_begin) % kScanCkptStep == 0)
+        p.carry[((b * p.dim + d) * ((L + kScanCkptStep - 1) / kScanCkptStep) + ts / kScanCkptStep) * N + n] = h;
+    }
     if constexpr (kDpp) {
       DppOps o;
       load_ops(par, blk, o);
@@ -518,7 +527,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     if (pf && ti + DEPTH < nfast) prefetch_fast(R, ti + DEPTH);
     if constexpr (SUMMARY) {
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) recur_block(par, bb);
+      for (int bb = 0; bb < NB; ++bb) recur_block(par, bb, t0);
     } else if constexpr (kDpp && SCAN_PIPE) {
       // The next block's operands load between this block's partial reads
       // and the sums that consume them.
@@ -537,7 +546,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     } else {
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        recur_block(par, bb);
+        recur_block(par, bb, t0);
         wave_lds_sync();
         Partials P;
         readout_load(par, bb, P);
@@ -569,7 +578,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     do_tile(ring[0], ti, false);
   }
 
-  if constexpr (SUMMARY) {
+  if constexpr (SUMMARY && !CKPT) {
     if (mine) {
       float *cr = p.carry + ((b * p.dim + d) * static_cast<int64_t>(p.n_chunks - 1) + c) * (2 * N);
       cr[n] = prod;
@@ -605,6 +614,15 @@ hipError_t launch_typed(const ScanParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename Tin, int N>
+hipError_t launch_ckpt_n(const ScanParams &p, hipStream_t stream) {
+  const int64_t blocks = p.batch * p.ngroups * p.tiles_per_group;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tin, N, true, kDepth<Tin>, false, true>),
+                     dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename Tin, typename Tout>
 hipError_t launch_n(const ScanParams &p, hipStream_t stream) {
   switch (p.dstate) {
@@ -624,6 +642,17 @@ hipError_t launch_n(const ScanParams &p, hipStream_t stream) {
 int scan_channels_per_block(int dstate) { return dstate > 0 ? 256 / dstate : 0; }
 
 int scan_vector_elems(int in_bf16) { return in_bf16 ? 8 : 4; }
+
+hipError_t launch_scan_ckpt(const ScanParams &p, int in_bf16, hipStream_t stream) {
+  switch (p.dstate) {
+#define SSM_CKPT_CASE(NN) \
+    case NN: return in_bf16 ? launch_ckpt_n<uint16_t, NN>(p, stream) : launch_ckpt_n<float, NN>(p, stream);
+    SSM_CKPT_CASE(1) SSM_CKPT_CASE(2) SSM_CKPT_CASE(4) SSM_CKPT_CASE(8) SSM_CKPT_CASE(16)
+    SSM_CKPT_CASE(32) SSM_CKPT_CASE(64)
+#undef SSM_CKPT_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_scan(const ScanParams &p, int in_bf16, int out_bf16, hipStream_t stream) {
   if (!in_bf16 && !out_bf16) return launch_n<float, float>(p, stream);

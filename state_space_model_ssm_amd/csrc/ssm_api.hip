@@ -208,6 +208,129 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
 }
 
 // ---------------------------------------------------------------------------
+// Selective-scan backward
+// ---------------------------------------------------------------------------
+
+static size_t scan_bwd_workspace(const ssm_scan_dims_t *d) {
+  return 4ull * d->batch * d->dim * d->dstate * ceil_div(d->seqlen, ssm::kScanCkptStep);
+}
+
+int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
+  const int rc = check_scan_dims(dims);
+  if (rc != SSM_OK) return rc;
+  *bytes = scan_bwd_workspace(dims);
+  return ok();
+}
+
+int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
+                 void *du, void *ddelta, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
+                 const ssm_scan_dims_t *dims, void *stream) {
+  int rc = check_scan_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssm_scan_dims_t &d = *dims;
+  const int64_t n_bdl = d.batch * d.dim * d.seqlen;
+  const int64_t n_bc = d.batch * d.ngroups * d.dstate * d.seqlen;
+  const int64_t n_a = d.dim * d.dstate;
+  const int64_t n_h = d.batch * d.dim * d.dstate;
+  if (n_bdl > 0 && (!u || !delta || !dy || !du || !ddelta))
+    return fail(SSM_ERR_NULL, "u, delta, dy, du and ddelta are required");
+  if (n_bc > 0 && (!B || !C || !dB || !dC)) return fail(SSM_ERR_NULL, "B, C, dB and dC are required");
+  if (n_a > 0 && (!A || !dA)) return fail(SSM_ERR_NULL, "A and dA are required");
+  if (n_bdl > 0 && z && !dz) return fail(SSM_ERR_NULL, "dz is required when z is given");
+  if (d.dim > 0 && D && !dD) return fail(SSM_ERR_NULL, "dD is required when D is given");
+  if (!z) dz = nullptr;
+  if (!D) dD = nullptr;
+  const size_t ei = dtype_size(d.in_dtype), eo = dtype_size(d.out_dtype);
+  if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei) ||
+      !aligned(du, ei) || !aligned(ddelta, ei) || !aligned(dz, ei))
+    return fail(SSM_ERR_ALIGN, "input-dtype pointers must be aligned to %zu bytes", ei);
+  if (!aligned(dy, eo)) return fail(SSM_ERR_ALIGN, "dy must be aligned to %zu bytes", eo);
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(dh_last, 4) || !aligned(dA, 4) ||
+      !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4))
+    return fail(SSM_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+  const Span ins[] = {{u, n_bdl * ei},  {delta, n_bdl * ei}, {z, n_bdl * ei},   {B, n_bc * ei},
+                      {C, n_bc * ei},   {A, n_a * 4ull},     {D, d.dim * 4ull}, {h0, n_h * 4ull},
+                      {dy, n_bdl * eo}, {dh_last, n_h * 4ull}};
+  const Span outs[] = {{du, n_bdl * ei}, {ddelta, n_bdl * ei}, {dz, n_bdl * ei},  {dA, n_a * 4ull},
+                       {dB, n_bc * 4ull}, {dC, n_bc * 4ull},    {dD, d.dim * 4ull}, {dh0, n_h * 4ull}};
+  for (const Span &o : outs) {
+    for (const Span &i : ins)
+      if (overlap(o, i)) return fail(SSM_ERR_SHAPE, "a gradient output overlaps an input");
+    for (const Span &o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return fail(SSM_ERR_SHAPE, "two gradient outputs overlap");
+  }
+  const size_t need = scan_bwd_workspace(&d);
+  if (need > 0) {
+    if (!d.workspace || d.workspace_bytes < need)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required for the state checkpoints (got %zu)",
+                  need, d.workspace ? d.workspace_bytes : (size_t)0);
+    if (!aligned(d.workspace, 4)) return fail(SSM_ERR_ALIGN, "workspace must be 4-byte aligned");
+    const Span sw{d.workspace, need};
+    for (const Span &s : ins)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an input");
+    for (const Span &s : outs)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
+  }
+  // An empty batch or channel set still zeroes dA, dB, dC and dD (sums over
+  // nothing); the kernels then launch no workgroup.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t tiles = ceil_div(d.dim / d.ngroups, ssm::scan_channels_per_block(static_cast<int>(d.dstate)));
+  ssm::ScanParams f{};
+  f.u = u;
+  f.delta = delta;
+  f.B = B;
+  f.C = C;
+  f.A = A;
+  f.h0 = h0;
+  f.carry = static_cast<float *>(d.workspace);
+  f.batch = d.batch;
+  f.dim = d.dim;
+  f.seqlen = d.seqlen;
+  f.ngroups = d.ngroups;
+  f.dim_per_group = d.dim / d.ngroups;
+  f.chunk_len = d.seqlen > 0 ? d.seqlen : 1;
+  f.tiles_per_group = tiles;
+  f.n_chunks = 1;
+  f.dstate = static_cast<int32_t>(d.dstate);
+  const int vec = ssm::scan_vector_elems(d.in_dtype == SSM_BF16);
+  f.vec_ok = (d.seqlen % vec == 0) && aligned(u, 16) && aligned(delta, 16) && aligned(B, 16) && aligned(C, 16);
+  hipError_t e = hipSuccess;
+  if (need > 0) e = ssm::launch_scan_ckpt(f, d.in_dtype == SSM_BF16, st);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "checkpoint launch failed: %s", hipGetErrorString(e));
+  ssm::ScanBwdParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.A = A;
+  p.D = D;
+  p.dy = dy;
+  p.dh_last = dh_last;
+  p.du = du;
+  p.ddelta = ddelta;
+  p.dz = dz;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dh0 = dh0;
+  p.ckpt = static_cast<const float *>(d.workspace);
+  p.batch = d.batch;
+  p.dim = d.dim;
+  p.seqlen = d.seqlen;
+  p.ngroups = d.ngroups;
+  p.dim_per_group = d.dim / d.ngroups;
+  p.tiles_per_group = tiles;
+  p.dstate = static_cast<int32_t>(d.dstate);
+  e = ssm::launch_scan_bwd(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16, st);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Scalar-decay chunked SSD
 // ---------------------------------------------------------------------------
 

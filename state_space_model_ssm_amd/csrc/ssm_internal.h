@@ -27,6 +27,9 @@ struct ScanParams {
 // Chunks start on multiples of this many steps (the scan's time tile).
 constexpr int64_t kScanChunkAlign = 32;
 
+// The backward pass keeps the forward state every kScanCkptStep steps.
+constexpr int64_t kScanCkptStep = 16;
+
 // Channel tile of one workgroup for a given dstate: 256 threads, one state per
 // thread, so 256 / dstate channels.
 int scan_channels_per_block(int dstate);
@@ -37,6 +40,30 @@ int scan_vector_elems(int in_bf16);
 // Launch the chunk-summary pass (chunks 0 .. n_chunks-2) when n_chunks > 1,
 // then the sweep that writes y and h_last.  Returns a hipError_t.
 hipError_t launch_scan(const ScanParams &p, int in_bf16, int out_bf16, hipStream_t stream);
+
+// Forward pass of one chunk (p.n_chunks == 1) from h0 that stores the state
+// at every kScanCkptStep-step boundary t into
+// p.carry[(batch*dim + d) * ceil(L / kScanCkptStep) + t / kScanCkptStep][n].
+hipError_t launch_scan_ckpt(const ScanParams &p, int in_bf16, hipStream_t stream);
+
+// The selective-scan backward (see ssm_scan_bwd in include/ssm.h): the
+// checkpoint pass stores the forward state every kScanCkptStep steps into
+// ckpt; the backward kernel walks 16-step tiles from the last to the first.
+struct ScanBwdParams {
+  const void *u, *delta, *B, *C, *z;  // in_dtype
+  const float *A, *D;                 // float32; D nullable
+  const void *dy;                     // out_dtype
+  const float *dh_last;               // nullable
+  void *du, *ddelta, *dz;             // in_dtype; dz only with z
+  float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
+  const float *ckpt;                  // [batch][dim][ceil(L / kScanCkptStep)][dstate]
+  int64_t batch, dim, seqlen, ngroups, dim_per_group, tiles_per_group;
+  int32_t dstate;
+};
+
+// Zero dA, dB, dC, dD, then run the backward kernel (the checkpoint pass must
+// have run on the same stream).
+hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hipStream_t stream);
 
 // One chunked-SSD launch (see ssd_chunked_fwd in include/ssm.h).
 struct SsdParams {

@@ -31,7 +31,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 10, declared
+    assert len(declared) == 12, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -223,6 +223,34 @@ def test_step_rejects_null_misaligned_overlap():
     assert _step(_ssdstepdims(dstate=96), ssd=True) == -5
     assert _step(_ssdstepdims(batch=0), ssd=True, u=None, dl=None, B=None, C=None, y=None, state=None) == 0
     assert _step(_stepdims(dim=0), u=None, dl=None, A=None, y=None, state=None) == 0
+
+
+def _bwd(dims, **kw):
+    a = dict(u=FAKE, dl=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000, C=FAKE + 0x400000, D=None,
+             z=None, h0=None, dy=FAKE + 0x500000, dhl=None, du=FAKE + 0x10000000, ddl=FAKE + 0x11000000,
+             dA=FAKE + 0x12000000, dB=FAKE + 0x13000000, dC=FAKE + 0x14000000, dD=None, dz=None, dh0=None)
+    a.update(kw)
+    return ssm.lib().ssm_scan_bwd(a["u"], a["dl"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["dy"],
+                                  a["dhl"], a["du"], a["ddl"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                  a["dh0"], ctypes.byref(dims), None)
+
+
+def test_scan_bwd_rules():
+    d = _dims(seqlen=100)
+    need = ssm.scan_bwd_workspace_size(d)
+    assert need == 4 * 2 * 64 * 16 * 7          # a state every 16 steps: ceil(100 / 16) = 7
+    assert _bwd(d) == -6                          # no workspace
+    d.workspace, d.workspace_bytes = FAKE + 0x30000000, need
+    assert _bwd(d, dy=None) == -1
+    assert _bwd(d, dB=None) == -1
+    assert _bwd(d, z=FAKE + 0x600000) == -1      # dz required with z
+    assert _bwd(d, D=FAKE + 0x700000) == -1      # dD required with D
+    assert _bwd(d, du=FAKE + 0x10000002) == -4   # f32 gradient needs 4-byte alignment
+    assert _bwd(d, du=FAKE + 0x100) == -2        # du inside u
+    assert _bwd(d, dB=FAKE + 0x10000000 + 64) == -2   # two outputs overlap
+    assert _bwd(d, dh0=FAKE + 0x30000000 + 8) == -2   # output inside the workspace
+    assert _bwd(_dims(dstate=12)) == -5
+    assert "overlap" in ssm.last_error() or ssm.last_error()
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
