@@ -39,6 +39,8 @@ class Oracle:
         lib.oracle_scan_f64.argtypes = [i64] * 5 + [dp] * 10
         lib.oracle_scan_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.argtypes = [i64] * 6 + [dp] * 10
+        lib.oracle_ssd_trap_f64.argtypes = [i64] * 6 + [dp] * 11
+        lib.oracle_ssd_trap_f64.restype = ctypes.c_int
         lib.oracle_scan_bwd_f64.argtypes = [i64] * 5 + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.restype = ctypes.c_int
@@ -64,6 +66,26 @@ class Oracle:
                                       _ptr(y), _ptr(h))
         if rc != 0:
             raise ValueError("oracle_scan_f64 rejected the shapes")
+        return y, h
+
+    def ssd_trap(self, x, dt, lam, A, B, C, D=None, z=None, h0=None):
+        """Trapezoidal (three-term) SSD in float64. Returns (y, h_last).
+
+        x, z: (batch, L, H, P); dt, lam: (batch, L, H); B, C: (batch, L, G, N);
+        A, D: (H,); h0, h_last: (batch, H, P, N).
+        """
+        x, dt, lam, A, B, C, D, z, h0 = map(f64, (x, dt, lam, A, B, C, D, z, h0))
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (batch, L, H) and lam.shape == dt.shape and A.shape == (H,)
+        assert B.shape == (batch, L, G, N) and C.shape == B.shape
+        assert h0 is None or h0.shape == (batch, H, P, N)
+        y = np.zeros_like(x)
+        h = np.zeros((batch, H, P, N))
+        rc = self.lib.oracle_ssd_trap_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(lam), _ptr(A),
+                                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h))
+        if rc != 0:
+            raise ValueError("oracle_ssd_trap_f64 rejected the shapes")
         return y, h
 
     def scan_bwd(self, u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
@@ -142,6 +164,11 @@ def scan(u, delta, A, B, C, D=None, z=None, h0=None):
 def scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
     """Selective-scan gradients in float64 with the default build; see ``Oracle.scan_bwd``."""
     return _load().scan_bwd(u, delta, A, B, C, D, z, h0, dy, dh_last)
+
+
+def ssd_trap(x, dt, lam, A, B, C, D=None, z=None, h0=None):
+    """Trapezoidal SSD in float64 with the default build; see ``Oracle.ssd_trap``."""
+    return _load().ssd_trap(x, dt, lam, A, B, C, D, z, h0)
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, h0=None):

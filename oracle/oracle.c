@@ -250,3 +250,67 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
     free(lam);
     return 0;
 }
+
+/*
+ * Trapezoidal (Mamba-3 SISO) form of the scalar-decay SSD, float64.
+ *
+ * "Mamba-3 NKI Kernels for AWS Neuron": section "How it works", Phase 0 gives
+ * the per-token coefficients alpha = exp(dt A), gamma = lam dt and
+ * beta = (dt - gamma) alpha (lam already through its sigmoid, dt through its
+ * softplus); the decode path is the three-term recurrence of its Eq. 9,
+ *   H_t = alpha_t H_{t-1} + beta_t (B_{t-1} x_{t-1}) + gamma_t (B_t x_t),
+ * read out as y_t = C_t . H_t; Phase 5 adds the D skip and the silu gate.
+ * Before the first token H is h0 (zero when NULL) and the previous input
+ * B_{-1} x_{-1} is zero.  h_last is H after the last token.
+ *   lam : (batch, seqlen, nheads); other layouts as oracle_ssd_f64.
+ * Returns 0, or -1 on a bad shape.
+ */
+int oracle_ssd_trap_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t ngroups, const double *x, const double *dt,
+                        const double *lam, const double *A, const double *B, const double *C,
+                        const double *Dskip, const double *z, const double *h0,
+                        double *y, double *h_last)
+{
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1 ||
+        ngroups < 1 || nheads % ngroups != 0 || headdim * dstate > 65536)
+        return -1;
+    static double H[65536], prev[65536];
+    const int64_t hpg = nheads / ngroups;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t hd = 0; hd < nheads; ++hd) {
+            const int64_t g = hd / hpg;
+            for (int64_t k = 0; k < headdim * dstate; ++k) {
+                H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;
+                prev[k] = 0.0;
+            }
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const double d = dt[(b * seqlen + t) * nheads + hd];
+                const double lm = lam[(b * seqlen + t) * nheads + hd];
+                const double alpha = exp(d * A[hd]);
+                const double gamma = lm * d;
+                const double beta = (d - gamma) * alpha;
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = ((b * seqlen + t) * nheads + hd) * headdim + p;
+                    const double xv = x[i];
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const int64_t k = p * dstate + n;
+                        const double bx = Bt[n] * xv;
+                        H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;
+                        prev[k] = bx;
+                        acc += Ct[n] * H[k];
+                    }
+                    if (Dskip) acc += Dskip[hd] * xv;
+                    if (z) acc *= silu(z[i]);
+                    y[i] = acc;
+                }
+            }
+            if (h_last)
+                for (int64_t k = 0; k < headdim * dstate; ++k)
+                    h_last[(b * nheads + hd) * headdim * dstate + k] = H[k];
+        }
+    }
+    return 0;
+}

@@ -390,6 +390,57 @@ def check_scan_bwd_finite_differences(orc):
             _close(g[gk], fd, rtol=1e-7, what=f"d{k} against finite differences (seed {seed})")
 
 
+def _trap_inputs(rng, b, L, H, P, N, G):
+    return {"x": rng.standard_normal((b, L, H, P)), "dt": np.exp(rng.uniform(-3, 0, (b, L, H))),
+            "lam": rng.uniform(0, 1, (b, L, H)), "A": -np.exp(rng.uniform(-1, 1, H)),
+            "B": rng.standard_normal((b, L, G, N)), "C": rng.standard_normal((b, L, G, N)),
+            "D": rng.standard_normal(H), "z": rng.standard_normal((b, L, H, P)),
+            "h0": rng.standard_normal((b, H, P, N))}
+
+
+def check_ssd_trap_lam_one_is_ssd(orc):
+    """lam = 1: gamma = dt and beta = 0, so the three-term recurrence is the
+    plain scalar-decay SSD (equal up to the order of one product's rounding)."""
+    rng = np.random.default_rng(61)
+    v = _trap_inputs(rng, 2, 9, 3, 4, 5, 1)
+    one = np.ones_like(v["lam"])
+    y, h = orc.ssd_trap(v["x"], v["dt"], one, v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"])
+    yr, hr = orc.ssd(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"])
+    _close(y, yr, rtol=1e-13, what="trapezoidal at lam = 1 vs SSD")
+    _close(h, hr, rtol=1e-13, what="trapezoidal h_last at lam = 1 vs SSD")
+
+
+def check_ssd_trap_single_ssd_form(orc):
+    """Against the single-SSD form written out independently: the input of
+    step s reaches step t > s with weight scale_s = gamma_s + dt_{s+1} (1 -
+    lam_{s+1}) times the decay exp(sum_{k=s+1..t} dt_k A), and its own step
+    with gamma_t (the diagonal correction); h0 decays from before step 0."""
+    rng = np.random.default_rng(62)
+    b, L, H, P, N, G = 2, 11, 4, 3, 5, 2
+    v = _trap_inputs(rng, b, L, H, P, N, G)
+    y, h = orc.ssd_trap(v["x"], v["dt"], v["lam"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"])
+    hpg = H // G
+    for bb in range(b):
+        for hd in range(H):
+            g = hd // hpg
+            dt, lam = v["dt"][bb, :, hd], v["lam"][bb, :, hd]
+            la = dt * v["A"][hd]                                  # log decay of each step
+            gam = lam * dt
+            nxt = np.append(dt[1:] * (1 - lam[1:]), 0.0)
+            scale = gam + nxt
+            for t in range(L):
+                state = np.exp(np.sum(la[:t + 1])) * v["h0"][bb, hd]     # (P, N)
+                for s in range(t + 1):
+                    w = gam[s] if s == t else scale[s] * np.exp(np.sum(la[s + 1:t + 1]))
+                    state = state + w * np.outer(v["x"][bb, s, hd], v["B"][bb, s, g])
+                yt = state @ v["C"][bb, t, g] + v["D"][hd] * v["x"][bb, t, hd]
+                zt = v["z"][bb, t, hd]
+                yt = yt * zt / (1 + np.exp(-zt))
+                _close(y[bb, t, hd], yt, what=f"single-SSD form y (b{bb} h{hd} t{t})")
+                if t == L - 1:
+                    _close(h[bb, hd], state, what=f"single-SSD form h_last (b{bb} h{hd})")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -403,4 +454,6 @@ ALL_CHECKS = [
     check_ssd_invariants,
     check_decode_steps_chain,
     check_scan_bwd_finite_differences,
+    check_ssd_trap_lam_one_is_ssd,
+    check_ssd_trap_single_ssd_form,
 ]

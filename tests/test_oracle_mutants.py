@@ -40,6 +40,12 @@ MUTANTS = [
     ("ssd_wrong_state_index", [("double *hp = &H[p * dstate + n];", "double *hp = &H[n * headdim + p];")]),
     ("ssd_group_index", [("const int64_t g = hd / hpg;", "const int64_t g = hd % ngroups;")]),
     ("ssd_h0_ignored", [("H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;", "H[k] = 0.0;")]),
+    ("trap_no_beta_term", [("H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;",
+                            "H[k] = alpha * H[k] + gamma * bx;")]),
+    ("trap_beta_without_decay", [("const double beta = (d - gamma) * alpha;", "const double beta = d - gamma;")]),
+    ("trap_gamma_ignores_lam", [("const double gamma = lm * d;", "const double gamma = d;")]),
+    ("trap_prev_updated_first", [("H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;\n                        prev[k] = bx;",
+                                  "prev[k] = bx;\n                        H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;")]),
     ("bwd_no_decay_in_adjoint", [("lam[n] = abar * l;", "lam[n] = l;")]),
     ("bwd_dA_uses_new_state", [("dA[d * dstate + n] += l * dl * abar * hprev;",
                                 "dA[d * dstate + n] += l * dl * abar * hs[(t + 1) * dstate + n];")]),
