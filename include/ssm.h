@@ -235,6 +235,32 @@ SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const
                     const void *C, const float *D, const void *z, const float *h0, void *y,
                     float *h_last, const ssd_dims_t *dims, void *stream);
 
+/*
+ * Trapezoidal (Mamba-3 SISO) form of the SSD, chunked.  Per token
+ *   alpha_t = exp(dt_t A[h]),  gamma_t = lam_t dt_t,  beta_t = (dt_t - gamma_t) alpha_t
+ *   S_t = alpha_t S_{t-1} + beta_t x_{t-1} B_{t-1}^T + gamma_t x_t B_t^T
+ *   y_t = (S_t C_t + D[h] x_t) * silu(z_t)
+ * with the previous-token term zero before the first token.
+ *   [Mamba-3 NKI], "How it works", Phase 0: alpha, gamma = lam dt and
+ *     beta = (dt - gamma) alpha (lam after its sigmoid, dt after its
+ *     softplus: both are applied by the caller); the step form is its Eq. 9;
+ *   [Mamba-3 NKI], "Kernel details", mamba3_siso_ssd_kernel: chunked in the
+ *     single-SSD form, the input of step s weighted by scale_s = gamma_s +
+ *     dt_{s+1} (1 - lam_{s+1}) at later steps, plus a diagonal correction
+ *     (weight gamma_s at its own step), chunk 64.
+ * Arguments, layouts and supported sizes are those of ssd_chunked_fwd, plus
+ *   lam : (batch, seqlen, nheads) bf16, 2-byte aligned.
+ * h0 is the state S before the first token; the previous-token term of the
+ * first token is zero, so a call continues an earlier one exactly only when
+ * that one's last token has lam = 1.  h_last is S after the last token.
+ * The rotary and normalisation steps that precede the SSD core in Mamba-3
+ * are not part of this call.
+ */
+SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A,
+                         const void *B, const void *C, const float *D, const void *z,
+                         const float *h0, void *y, float *h_last, const ssd_dims_t *dims,
+                         void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Single-token decode steps (state cache updated in place)                  */
 /* ------------------------------------------------------------------------ */

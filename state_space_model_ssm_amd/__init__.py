@@ -17,7 +17,8 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
-    "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "scan_step", "ssd_step", "scan_workspace_size",
+    "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
+    "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
 
@@ -86,6 +87,8 @@ def lib():
         L.ssm_scan_resolved_chunks.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_int32)]
         L.ssm_scan_resolved_chunks.restype = i32
         L.ssd_chunked_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_trap_chunked_fwd.argtypes = [vp] * 11 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_trap_chunked_fwd.restype = ctypes.c_int
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
@@ -281,9 +284,10 @@ def ssd_workspace_size(dims: SsdDims) -> int:
     return n.value
 
 
-def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
+def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
                     return_h_last: bool = True, y=None, h_last=None, stream=None):
-    """Scalar-decay chunked SSD forward (``ssd_chunked_fwd``). Returns ``(y, h_last)``.
+    """Scalar-decay chunked SSD forward, plain (lam None: ``ssd_chunked_fwd``)
+    or trapezoidal (``ssd_trap_chunked_fwd``). Returns ``(y, h_last)``.
 
     x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
     B, C: (batch, L, G, N) bf16; h0: (batch, H, P, N) float32 initial state
@@ -303,6 +307,8 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64,
     N = B.shape[3]
     if dt.shape != (batch, L, H) or (z is not None and z.shape != x.shape):
         raise ValueError("dt must be (batch, L, H) and z shaped like x")
+    if lam is not None and (lam.shape != dt.shape or lam.dtype != x.dtype):
+        raise ValueError("lam must be shaped and typed like dt")
     if B.dim() != 4 or B.shape[:2] != (batch, L) or C.shape != B.shape:
         raise ValueError("B and C must be (batch, seqlen, ngroups, dstate)")
     if A.shape != (H,) or (D is not None and D.shape != (H,)):
@@ -314,10 +320,33 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64,
         y = torch.empty((batch, L, H, P), dtype=out_dt, device=x.device)
     if h_last is None and return_h_last:
         h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device)
-    rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                               _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+    if lam is None:
+        rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
+    else:
+        rc = lib().ssd_trap_chunked_fwd(_ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                        _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims),
+                                        _stream(stream))
     _check(rc)
     return y, h_last
+
+
+def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, **kw):
+    """Scalar-decay chunked SSD forward (``ssd_chunked_fwd``). Returns ``(y, h_last)``.
+
+    x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
+    B, C: (batch, L, G, N) bf16; h0: (batch, H, P, N) float32 initial state
+    (zero when None).  h_last is float32 (batch, H, P, N) and may be h0 itself.
+    Keywords: h0, chunk, out_dtype, return_h_last, y, h_last, stream.
+    """
+    return _ssd_call(x, dt, None, A, B, C, D, z, **kw)
+
+
+def ssd_trap_chunked_fwd(x, dt, lam, A, B, C, D=None, z=None, **kw):
+    """Trapezoidal (Mamba-3 SISO) chunked SSD (``ssd_trap_chunked_fwd``):
+    lam (batch, L, H) bf16 in [0, 1] (after its sigmoid).  Otherwise as
+    ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
+    return _ssd_call(x, dt, lam, A, B, C, D, z, **kw)
 
 
 def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None):

@@ -87,7 +87,11 @@ __device__ __forceinline__ int tidx(int col, int t) {
   return col * QP + 2 * ((t >> 1) ^ tswz<COLS>(col)) + (t & 1);
 }
 
-template <typename Tout, int N, bool HAS_Z>
+// TRAP: the trapezoidal (Mamba-3 SISO) three-term form.  Its chunked form is
+// this SSD with the input of step s weighted by scale_s = gamma_s +
+// dt_{s+1} (1 - lam_{s+1}) wherever it reaches a later step, and by
+// gamma_s = lam_s dt_s at its own step (the diagonal of M).
+template <typename Tout, int N, bool HAS_Z, bool TRAP = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WPE, SSD_WPE))) ssd_chunk_kernel(const SsdParams p) {
   constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
@@ -106,8 +110,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   Tout *sY = reinterpret_cast<Tout *>(sM);
   __shared__ __attribute__((aligned(16))) float sA[Q];           // a_t
   __shared__ __attribute__((aligned(16))) float sEa[Q];          // exp(a_t)
-  __shared__ __attribute__((aligned(16))) float sW[Q];           // exp(a_last - a_s) dt_s
-  __shared__ __attribute__((aligned(16))) float sDt[Q];          // dt_s
+  __shared__ __attribute__((aligned(16))) float sW[Q];           // exp(a_last - a_s) w_s
+  __shared__ __attribute__((aligned(16))) float sDt[Q];          // w_s: dt_s (scale_s when TRAP)
+  __shared__ __attribute__((aligned(16))) float sGam[TRAP ? Q : 1];  // gamma_s (TRAP)
   __shared__ float sDecay;                                       // exp(a_last)
 
   const uint16_t *__restrict__ gx = static_cast<const uint16_t *>(p.x);
@@ -115,6 +120,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   const uint16_t *__restrict__ gB = static_cast<const uint16_t *>(p.B);
   const uint16_t *__restrict__ gC = static_cast<const uint16_t *>(p.C);
   const uint16_t *__restrict__ gz = static_cast<const uint16_t *>(p.z);
+  const uint16_t *__restrict__ glam = static_cast<const uint16_t *>(p.lam);
   Tout *__restrict__ gy = static_cast<Tout *>(p.y);
 
   // Blocks of one batch row share B and C.  Consecutive block ids are dealt
@@ -177,6 +183,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
     uint4 bv[BJ][2], cv[BJ][2];
     uint4 xv[2];
     uint32_t dt;  // raw bf16 bits of dt at step `lane` (wavefront 0 uses it)
+    uint32_t lam, dtn, lamn;  // TRAP: lam at step `lane`, dt and lam at step `lane` + 1
   };
   auto load_chunk = [&](int64_t c0, ChunkRegs &R) __attribute__((always_inline)) {
 #pragma unroll
@@ -209,6 +216,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
     // Unconditional load from a clamped step: no branch, so nothing waits
     // on it (or on the loads before it) until the chunk is staged.
     R.dt = gdt[(b * L + min(c0 + lane, L - 1)) * H + h];
+    if constexpr (TRAP) {
+      R.lam = glam[(b * L + min(c0 + lane, L - 1)) * H + h];
+      R.dtn = gdt[(b * L + min(c0 + lane + 1, L - 1)) * H + h];
+      R.lamn = glam[(b * L + min(c0 + lane + 1, L - 1)) * H + h];
+    }
   };
   auto stage_chunk = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
     // B and C: natural layout [t][n] for both, B also transposed to [n][t].
@@ -236,16 +248,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         if (lane >= off) a += o;
       }
       const float alast = __shfl(a, 63);
+      float w = dtv;
+      if constexpr (TRAP) {
+        // Weight of this step's input wherever it reaches a later step; the
+        // step after the sequence has dt = 0, so the last step keeps gamma.
+        const float gam = (c0 + lane < L) ? bf2f(static_cast<uint16_t>(R.lam)) * dtv : 0.0f;
+        const bool nx = c0 + lane + 1 < L;
+        const float dtn = nx ? bf2f(static_cast<uint16_t>(R.dtn)) : 0.0f;
+        const float lamn = nx ? bf2f(static_cast<uint16_t>(R.lamn)) : 0.0f;
+        w = gam + dtn * (1.0f - lamn);
+        sGam[lane] = gam;
+      }
       sA[lane] = a;
       sEa[lane] = fast_exp(a);
-      sW[lane] = fast_exp(alast - a) * dtv;
-      sDt[lane] = dtv;
+      sW[lane] = fast_exp(alast - a) * w;
+      sDt[lane] = w;
       if (lane == 0) sDecay = fast_exp(alast);
     }
   };
 
   ChunkRegs R;
-  load_chunk(0, R);
+  if (L > 0) load_chunk(0, R);  // an empty sequence reads nothing (its step indexes would be -1)
   for (int64_t c0 = 0; c0 < L; c0 += Q) {
     stage_chunk(R, c0);
     __syncthreads();
@@ -326,7 +349,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = si * 16 + 4 * q + r;
-          const float v = (s <= t) ? acc[r] * fast_exp(at - sA[s]) * sDt[s] : 0.0f;
+          const float ws = TRAP ? (s < t ? sDt[s] : sGam[s]) : sDt[s];
+          const float v = (s <= t) ? acc[r] * fast_exp(at - sA[s]) * ws : 0.0f;
           m[r] = f2bf(v);
         }
         *reinterpret_cast<uint2 *>(&sM[t * QP + si * 16 + 4 * q]) = *reinterpret_cast<const uint2 *>(m);
@@ -399,20 +423,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   }
 }
 
-template <typename Tout, int N>
+template <typename Tout, int N, bool TRAP>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
   if (p.z != nullptr)
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, true, TRAP>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, false, TRAP>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename Tout>
 hipError_t launch_typed(const SsdParams &p, hipStream_t stream) {
-  if (p.dstate == 128) return launch_n<Tout, 128>(p, stream);
-  if (p.dstate == 64) return launch_n<Tout, 64>(p, stream);
+  if (p.lam != nullptr) {
+    if (p.dstate == 128) return launch_n<Tout, 128, true>(p, stream);
+    if (p.dstate == 64) return launch_n<Tout, 64, true>(p, stream);
+  } else {
+    if (p.dstate == 128) return launch_n<Tout, 128, false>(p, stream);
+    if (p.dstate == 64) return launch_n<Tout, 64, false>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

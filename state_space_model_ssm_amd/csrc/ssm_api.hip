@@ -367,9 +367,9 @@ int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
   return ok();
 }
 
-int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
-                    const float *D, const void *z, const float *h0, void *y, float *h_last,
-                    const ssd_dims_t *dims, void *stream) {
+static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, const float *A, const void *B,
+                   const void *C, const float *D, const void *z, const float *h0, void *y, float *h_last,
+                   const ssd_dims_t *dims, void *stream) {
   const int rc = check_ssd_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssd_dims_t &d = *dims;
@@ -383,13 +383,14 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
   const size_t eo = dtype_size(d.out_dtype);
   if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16))
     return fail(SSM_ERR_ALIGN, "x, z, B and C must be 16-byte aligned");
-  if (!aligned(dt, 2)) return fail(SSM_ERR_ALIGN, "dt must be 2-byte aligned");
+  if (trap && n_dt > 0 && !lam) return fail(SSM_ERR_NULL, "lam is required");
+  if (!aligned(dt, 2) || !aligned(lam, 2)) return fail(SSM_ERR_ALIGN, "dt and lam must be 2-byte aligned");
   if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
   if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
   if (!aligned(h0, 16) || !aligned(h_last, 16))
     return fail(SSM_ERR_ALIGN, "h0 and h_last must be 16-byte aligned");
   const Span ins[] = {{x, n_x * 2ull}, {dt, n_dt * 2ull}, {z, n_x * 2ull}, {B, n_bc * 2ull},
-                      {C, n_bc * 2ull}, {A, d.nheads * 4ull}, {D, d.nheads * 4ull}};
+                      {C, n_bc * 2ull}, {A, d.nheads * 4ull}, {D, d.nheads * 4ull}, {lam, n_dt * 2ull}};
   const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
@@ -403,6 +404,7 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
   ssm::SsdParams p{};
   p.x = x;
   p.dt = dt;
+  p.lam = trap ? lam : nullptr;
   p.B = B;
   p.C = C;
   p.z = z;
@@ -421,6 +423,18 @@ int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B
   const hipError_t e = ssm::launch_ssd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssd launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                    const float *D, const void *z, const float *h0, void *y, float *h_last,
+                    const ssd_dims_t *dims, void *stream) {
+  return ssd_run(x, dt, nullptr, false, A, B, C, D, z, h0, y, h_last, dims, stream);
+}
+
+int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A, const void *B,
+                         const void *C, const float *D, const void *z, const float *h0, void *y,
+                         float *h_last, const ssd_dims_t *dims, void *stream) {
+  return ssd_run(x, dt, lam, true, A, B, C, D, z, h0, y, h_last, dims, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -68,6 +68,7 @@ hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hi
 // One chunked-SSD launch (see ssd_chunked_fwd in include/ssm.h).
 struct SsdParams {
   const void *x, *dt, *B, *C, *z;     // bf16
+  const void *lam;                    // bf16 (batch, seqlen, nheads); non-null = trapezoidal form
   const float *A, *D;                 // float32; D nullable
   const float *h0;                    // nullable initial state [batch][nheads][headdim][dstate]
   void *y;                            // out dtype

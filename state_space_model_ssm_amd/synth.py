@@ -126,6 +126,15 @@ def make_state(shape, seed: int, scale: float = 1.0) -> torch.Tensor:
     return torch.from_numpy((scale * rng.standard_normal(shape)).astype(np.float32))
 
 
+def make_lam(shape, seed: int) -> torch.Tensor:
+    """Seeded trapezoid weights lam = sigmoid(N(0, 1)) per (batch, time, head),
+    stored as bf16 (the Phase-0 sigmoid of "Mamba-3 NKI Kernels for AWS Neuron",
+    section "How it works", applied on the host)."""
+    rng = np.random.default_rng(seed)
+    v = 1.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+    return _store(v, "bf16")
+
+
 def make_scan_inputs(s: ScanShape, a_override: Optional[np.ndarray] = None) -> dict:
     """Selective-scan inputs on the host, in the storage dtypes of the C ABI.
 

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import state_space_model_ssm_amd as ssm
-from state_space_model_ssm_amd.synth import (WORKLOADS, ScanShape, SsdShape, make_scan_inputs,
+from state_space_model_ssm_amd.synth import (WORKLOADS, ScanShape, SsdShape, make_lam, make_scan_inputs,
                                              make_ssd_inputs, make_state)
 
 pytestmark = pytest.mark.gpu
@@ -525,3 +525,78 @@ def test_scan_backward_empty_sequence():
     torch.cuda.synchronize()
     assert torch.equal(g["dh0"].cpu(), dhl)
     assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Trapezoidal (Mamba-3 SISO) SSD
+# ---------------------------------------------------------------------------
+
+TRAP_CASES = [
+    # (batch, L, H, N, G, has_z, dskip, h0)
+    (1, 64, 1, 128, 1, False, "ones", False),
+    (2, 256, 4, 128, 1, False, "ones", True),
+    (2, 200, 4, 128, 2, True, "normal", False),    # ragged last chunk: lookahead across chunk ends
+    (1, 1, 2, 128, 1, True, "normal", True),       # L = 1
+    (3, 130, 3, 64, 1, False, "normal", True),
+    (2, 65, 4, 64, 4, True, "none", False),        # one step past a chunk
+]
+
+
+def run_trap(inp, lam, h0=None, out_dtype=None):
+    x = _dev(inp["x"])
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    b, L, H, P = x.shape
+    y = torch.full(x.shape, float("nan"), dtype=out_dt, device="cuda")
+    h = torch.full((b, H, P, inp["B"].shape[3]), float("nan"), dtype=torch.float32, device="cuda")
+    y, h = ssm.ssd_trap_chunked_fwd(x, _dev(inp["dt"]), _dev(lam), _dev(inp["A"]), _dev(inp["B"]),
+                                    _dev(inp["C"]), _dev(inp["D"]), _dev(inp["z"]), h0=_dev(h0),
+                                    out_dtype=out_dt, y=y, h_last=h)
+    torch.cuda.synchronize()
+    return y.float().cpu(), h.cpu()
+
+
+@pytest.mark.parametrize("case", TRAP_CASES, ids=lambda c: "b{}l{}h{}n{}g{}_z{}_{}_h0{}".format(*c))
+def test_ssd_trap_small(case):
+    batch, L, H, N, G, has_z, dskip, with_h0 = case
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip=dskip, seed=6000 + L + H)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((batch, L, H), seed=6100 + L)
+    h0 = make_state((batch, H, 64, N), seed=6200 + N, scale=0.5) if with_h0 else None
+    y, h = run_trap(inp, lam, h0)
+    yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
+    assert rel_err(y, yr) <= TOL_BF16, rel_err(y, yr)
+    assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
+
+
+def test_ssd_trap_lam_one_equals_ssd_bitwise():
+    """lam = 1 makes every weight dt: the trapezoidal kernel then computes the
+    same values as the plain SSD kernel, bit for bit."""
+    s = SsdShape(2, 200, 4, 64, 128, 1, 64, "bf16", has_z=True, dskip="normal", seed=6300)
+    inp = make_ssd_inputs(s)
+    one = torch.ones((2, 200, 4), dtype=torch.bfloat16)
+    a = run_trap(inp, one)
+    b = run_ssd(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_ssd_trap_named_workload_full_size():
+    """The SSD workload's shapes (batch 32, 256 steps, 32 heads x 64, dstate
+    128) with trapezoid weights; 48 sampled (batch, head) pairs checked."""
+    s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(s)
+    lam = make_lam((s.batch, s.seqlen, s.nheads), seed=6400)
+    y, h = run_trap(inp, lam)
+    assert not torch.isnan(y).any() and not torch.isnan(h).any()
+    rng = np.random.default_rng(6401)
+    pairs = rng.choice(s.batch * s.nheads, size=48, replace=False)
+    ys, yrs, hs, hrs = [], [], [], []
+    for i in sorted(int(v) for v in pairs):
+        b, hd = divmod(i, s.nheads)
+        sl = dict(x=inp["x"][b:b + 1, :, hd:hd + 1], dt=inp["dt"][b:b + 1, :, hd:hd + 1],
+                  lam=lam[b:b + 1, :, hd:hd + 1], A=inp["A"][hd:hd + 1], B=inp["B"][b:b + 1],
+                  C=inp["C"][b:b + 1], D=None if inp["D"] is None else inp["D"][hd:hd + 1])
+        yr, hr = oracle.ssd_trap(sl["x"], sl["dt"], sl["lam"], sl["A"], sl["B"], sl["C"], sl["D"])
+        ys.append(y[b, :, hd].numpy()); yrs.append(yr[0, :, 0])
+        hs.append(h[b, hd].numpy()); hrs.append(hr[0, 0])
+    assert rel_err(np.stack(ys), np.stack(yrs)) <= TOL_BF16
+    assert rel_err(np.stack(hs), np.stack(hrs)) <= TOL_BF16
