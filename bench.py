@@ -211,6 +211,7 @@ def main():
                                  "hbm_GB/s_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6, 1),
                                  "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2)}
         context.update(decode_context(ssm, dev, stream, time_calls))
+        context.update(extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs))
     torch.cuda.synchronize()
 
     # ---- CPU baseline: the float64 oracle on a bounded sample ------------------
@@ -256,6 +257,37 @@ def main():
         "workloads": context,
     }
     print(json.dumps(out), flush=True)
+
+
+def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs):
+    """The scan backward on the long-prefill and large-channel workloads, and
+    the trapezoidal SSD on the SSD workload's shapes."""
+    import torch
+    from state_space_model_ssm_amd.synth import make_lam
+    out = {}
+    for name in ("long_prefill_8x1536x2048_f32", "large_channel_4x5120x4096_bf16"):
+        w = WORKLOADS[name]
+        d = {k: (None if v is None else v.to(dev)) for k, v in make_scan_inputs(w).items()}
+        g = torch.Generator(device="cpu").manual_seed(9)
+        dy = torch.randn(w.batch, w.dim, w.seqlen, generator=g).to(d["u"].dtype).to(dev)
+        dims = ssm._scan_dims(d["u"], d["B"], ssm._dtype_code(d["u"].dtype), ssm._dtype_code(dy.dtype), 0)
+        ws = torch.empty(max(ssm.scan_bwd_workspace_size(dims), 1), dtype=torch.uint8, device=dev)
+        ms, _ = time_calls(lambda: ssm.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                                dy=dy, workspace=ws, stream=stream), 5, 1)
+        out["backward_" + name] = {"ms": round(ms, 4), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                   "workspace_MB": round(ws.numel() / 1e6, 1)}
+        del d, dy, ws
+    w = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    d = {k: (None if v is None else v.to(dev)) for k, v in make_ssd_inputs(w).items()}
+    lam = make_lam((w.batch, w.seqlen, w.nheads), seed=10).to(dev)
+    y = torch.empty_like(d["x"])
+    h = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    ms, _ = time_calls(lambda: ssm.ssd_trap_chunked_fwd(d["x"], d["dt"], lam, d["A"], d["B"], d["C"], d["D"],
+                                                        d["z"], y=y, h_last=h, stream=stream), 50, 5)
+    nbytes = w.metric_bytes() + w.hlast_bytes() + lam.numel() * 2
+    out["ssd_trap_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                              "hbm_GB/s_with_h_last": round(nbytes / ms / 1e6, 1)}
+    return out
 
 
 def decode_context(ssm, dev, stream, time_calls):
