@@ -42,25 +42,55 @@ __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
 }
 
+struct alignas(16) F4 {
+  float v[4];
+};
+
 template <int N>
 struct BwdCfg {
   static constexpr int CH = 256 / N;            // channels per workgroup
-  static constexpr int TP = kT + 1;             // staged row (floats): odd, so rows hit distinct banks
+  static constexpr int TP = kT + 4;             // staged row (floats): 16-byte rows on distinct banks
   static constexpr int JS = N >= 4 ? N + 4 : N; // state partials of one step
-  static constexpr int RS_ALIGN = N >= 4 ? (N < 64 ? N : 0) : 4;
-  static constexpr int RS = kT * JS + ((RS_ALIGN - (kT * JS) % 64) % 64 + 64) % 64;  // per channel
+  static constexpr int RS_ALIGN = N < 64 ? N : 0;
+  // Per channel; below 4 states a row is read one float at a time, so a
+  // minimal pad does.
+  static constexpr int RS = N >= 4 ? kT * JS + ((RS_ALIGN - (kT * JS) % 64) % 64 + 64) % 64 : kT * JS + 4;
   static constexpr int CS = CH + 4;             // channel partials of one (step, state)
   static constexpr int PAIRS_CT = CH * kT;      // (channel, step) sums per tile
   static constexpr int PAIRS_NT = N * kT;       // (state, step) sums per tile
 };
+
+// Sum of M consecutive LDS floats (16-byte reads when M is a multiple of 4;
+// the row is then 16-byte aligned), pairwise.
+template <int M>
+__device__ __forceinline__ float sum_row(const float *row) {
+  float v[M];
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < M; i += 4) {
+      const F4 q = *reinterpret_cast<const F4 *>(row + i);
+      v[i] = q.v[0]; v[i + 1] = q.v[1]; v[i + 2] = q.v[2]; v[i + 3] = q.v[3];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] = row[i];
+  }
+#pragma unroll
+  for (int w = 1; w < M; w *= 2) {
+#pragma unroll
+    for (int i = 0; i + w < M; i += 2 * w) v[i] += v[i + w];
+  }
+  return v[0];
+}
 
 template <typename Tin, typename Tout, int N, bool HAS_Z>
 __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
   using Cfg = BwdCfg<N>;
   constexpr int CH = Cfg::CH, TP = Cfg::TP, JS = Cfg::JS, RS = Cfg::RS, CS = Cfg::CS;
 
-  __shared__ float sDl[CH * TP], sU[CH * TP], sDy[CH * TP], sZ[HAS_Z ? CH * TP : 1];
-  __shared__ float sB[N * TP], sC[N * TP];
+  __shared__ F4 sDl4[CH * TP / 4], sU4[CH * TP / 4], sDy4[CH * TP / 4], sZ4[HAS_Z ? CH * TP / 4 : 1];
+  __shared__ F4 sB4[N * TP / 4], sC4[N * TP / 4];
+  float *sDl = sDl4[0].v, *sU = sU4[0].v, *sDy = sDy4[0].v, *sZ = sZ4[0].v, *sB = sB4[0].v, *sC = sC4[0].v;
   __shared__ __attribute__((aligned(16))) float sQ[CH * RS];          // [channel][step][state]
   __shared__ __attribute__((aligned(16))) float sR[kT * N * CS];      // [step][state][channel]
 
@@ -123,11 +153,17 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     {
       float h = h_start;
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        const float dl = sDl[chl * TP + t];
-        h = fmaf(__builtin_amdgcn_exp2f(dl * a2), h, dl * sU[chl * TP + t] * sB[n * TP + t]);
-        hist[t] = h;
-        if constexpr (HAS_Z) sQ[chl * RS + t * JS + n] = sC[n * TP + t] * h;
+      for (int t4 = 0; t4 < kT; t4 += 4) {
+        const F4 dl4 = sDl4[(chl * TP + t4) / 4], u4 = sU4[(chl * TP + t4) / 4], b4 = sB4[(n * TP + t4) / 4];
+        F4 c4 = {};
+        if constexpr (HAS_Z) c4 = sC4[(n * TP + t4) / 4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float dl = dl4.v[i];
+          h = fmaf(__builtin_amdgcn_exp2f(dl * a2), h, dl * u4.v[i] * b4.v[i]);
+          hist[t4 + i] = h;
+          if constexpr (HAS_Z) sQ[chl * RS + (t4 + i) * JS + n] = c4.v[i] * h;
+        }
       }
     }
     // ---- per (channel, step): dyhat (and dz, from yhat) --------------------
@@ -142,9 +178,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
         const float dskip = (p.D != nullptr && r < nvalid) ? p.D[d0 + r] : 0.0f;
         float dyh = dy;
         if constexpr (HAS_Z) {
-          float yhat = dskip * uu;
-#pragma unroll
-          for (int i = 0; i < N; ++i) yhat += sQ[r * RS + t * JS + i];
+          const float yhat = fmaf(dskip, uu, sum_row<N>(sQ + r * RS + t * JS));
           const float zz = sZ[r * TP + t];
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
           dyh = dy * zz * sg;
@@ -163,21 +197,23 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     // ---- adjoint, backwards through the tile --------------------------------
     float pdu[kT], pddl[kT], pdB[kT], pdC[kT];
 #pragma unroll
-    for (int t = kT - 1; t >= 0; --t) {
-      const float dl = sDl[chl * TP + t];
-      const float uu = sU[chl * TP + t];
-      const float dyh = sDy[chl * TP + t];
-      const float bv = sB[n * TP + t];
-      const float cv = sC[n * TP + t];
-      const float a = __builtin_amdgcn_exp2f(dl * a2);
-      const float hprev = t > 0 ? hist[t - 1] : h_start;
-      const float l = fmaf(dyh, cv, lam);
-      pdC[t] = mine ? dyh * hist[t] : 0.0f;
-      pdB[t] = mine ? l * dl * uu : 0.0f;
-      pdu[t] = l * dl * bv;
-      pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
-      dA_acc = fmaf(l * dl * a, hprev, dA_acc);
-      lam = a * l;
+    for (int t4 = kT - 4; t4 >= 0; t4 -= 4) {
+      const F4 dl4 = sDl4[(chl * TP + t4) / 4], u4 = sU4[(chl * TP + t4) / 4], dy4 = sDy4[(chl * TP + t4) / 4];
+      const F4 b4 = sB4[(n * TP + t4) / 4], c4 = sC4[(n * TP + t4) / 4];
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const int t = t4 + i;
+        const float dl = dl4.v[i], uu = u4.v[i], dyh = dy4.v[i], bv = b4.v[i], cv = c4.v[i];
+        const float a = __builtin_amdgcn_exp2f(dl * a2);
+        const float hprev = t > 0 ? hist[t - 1] : h_start;
+        const float l = fmaf(dyh, cv, lam);
+        pdC[t] = mine ? dyh * hist[t] : 0.0f;
+        pdB[t] = mine ? l * dl * uu : 0.0f;
+        pdu[t] = l * dl * bv;
+        pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
+        dA_acc = fmaf(l * dl * a, hprev, dA_acc);
+        lam = a * l;
+      }
     }
 
     // ---- reductions: (du over states, dB over channels), then (ddt, dC) ---
@@ -194,9 +230,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
         const int e = tid + 256 * k;
         if (e < Cfg::PAIRS_CT) {
           const int r = e / kT, t = e % kT;
-          float s = 0.0f;
-#pragma unroll
-          for (int i = 0; i < N; ++i) s += sQ[r * RS + t * JS + i];
+          const float s = sum_row<N>(sQ + r * RS + t * JS);
           if (r < nvalid && t0 + t < L) {
             const int64_t o = (b * p.dim + d0 + r) * L + t0 + t;
             if (phase == 0) {
@@ -213,9 +247,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
         const int e = tid + 256 * k;
         if (e < Cfg::PAIRS_NT) {
           const int t = e / N, nn = e % N;
-          float s = 0.0f;
-#pragma unroll
-          for (int i = 0; i < CH; ++i) s += sR[(t * N + nn) * CS + i];
+          const float s = sum_row<CH>(sR + (t * N + nn) * CS);
           if (t0 + t < L)
             atomicAdd((phase == 0 ? p.dB : p.dC) + ((b * p.ngroups + g) * N + nn) * L + t0 + t, s);
         }
