@@ -79,68 +79,87 @@ __device__ __forceinline__ void dpp_coeffs(float dl16, float w16, float a2, cons
   ((bx[J] = row_bcast<J>(w16) * b4[J / 4].v[J % 4]), ...);
 }
 
-// Unpack one 16-byte vector of VEC storage elements into floats.
-template <typename T>
-struct Vec;
-template <>
-struct Vec<float> {
-  static constexpr int kN = 4;
-  __device__ static void unpack(const uint4 &r, float *o) {
-    o[0] = __uint_as_float(r.x);
-    o[1] = __uint_as_float(r.y);
-    o[2] = __uint_as_float(r.z);
-    o[3] = __uint_as_float(r.w);
-  }
-};
-template <>
-struct Vec<uint16_t> {
-  static constexpr int kN = 8;
-  __device__ static void unpack(const uint4 &r, float *o) {
-    o[0] = bf_lo(r.x); o[1] = bf_hi(r.x);
-    o[2] = bf_lo(r.y); o[3] = bf_hi(r.y);
-    o[4] = bf_lo(r.z); o[5] = bf_hi(r.z);
-    o[6] = bf_lo(r.w); o[7] = bf_hi(r.w);
-  }
+// W 32-bit words of one row segment, loaded as a single vector.
+template <int W>
+struct alignas(4 * W) Words {
+  uint32_t v[W];
 };
 
+// Unpack the storage elements held in W words into floats.
+__device__ __forceinline__ void unpack(const uint32_t *w, int nw, float *o, const float *) {
+  for (int i = 0; i < nw; ++i) o[i] = __uint_as_float(w[i]);
+}
+__device__ __forceinline__ void unpack(const uint32_t *w, int nw, float *o, const uint16_t *) {
+  for (int i = 0; i < nw; ++i) {
+    o[2 * i] = bf_lo(w[i]);
+    o[2 * i + 1] = bf_hi(w[i]);
+  }
+}
+
 // A row segment that is misaligned or crosses the end of the chunk: element
-// loads, zero past t_end, packed into the same 16-byte layout as a vector load.
+// loads, zero past t_end, packed into the same words as a vector load.
 __device__ __forceinline__ uint32_t elem_bits(const float *row, int64_t t, int64_t t_end) {
   return t < t_end ? __float_as_uint(row[t]) : 0u;
 }
 __device__ __forceinline__ uint32_t elem_bits(const uint16_t *row, int64_t t, int64_t t_end) {
   return t < t_end ? static_cast<uint32_t>(row[t]) : 0u;
 }
-__device__ __forceinline__ uint4 load_seg_tail(const float *row, int64_t t, int64_t t_end) {
-  return uint4{elem_bits(row, t, t_end), elem_bits(row, t + 1, t_end), elem_bits(row, t + 2, t_end),
-               elem_bits(row, t + 3, t_end)};
-}
-__device__ __forceinline__ uint4 load_seg_tail(const uint16_t *row, int64_t t, int64_t t_end) {
-  uint32_t w[4];
+template <int W>
+__device__ __forceinline__ Words<W> load_seg_tail(const float *row, int64_t t, int64_t t_end) {
+  Words<W> r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = elem_bits(row, t + 2 * i, t_end) | (elem_bits(row, t + 2 * i + 1, t_end) << 16);
-  return uint4{w[0], w[1], w[2], w[3]};
+  for (int i = 0; i < W; ++i) r.v[i] = elem_bits(row, t + i, t_end);
+  return r;
 }
+template <int W>
+__device__ __forceinline__ Words<W> load_seg_tail(const uint16_t *row, int64_t t, int64_t t_end) {
+  Words<W> r;
+#pragma unroll
+  for (int i = 0; i < W; ++i)
+    r.v[i] = elem_bits(row, t + 2 * i, t_end) | (elem_bits(row, t + 2 * i + 1, t_end) << 16);
+  return r;
+}
+
+#ifndef SCAN_DPP_T
+#define SCAN_DPP_T 32
+#endif
+#ifndef SCAN_DPP_VEC
+#define SCAN_DPP_VEC 4
+#endif
+#ifndef SCAN_WAVES16
+#define SCAN_WAVES16 4
+#endif
 
 template <int N>
 struct TileCfg {
+  static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
   static constexpr int CH = 256 / N;                             // channels per block
   static constexpr int CPW = 64 / N;                             // channels per wavefront
-  static constexpr int T = N >= 4 ? 32 : (N == 2 ? 16 : 8);      // time steps per tile
+  // Time steps per tile.
+  static constexpr int T = kDpp ? SCAN_DPP_T : (N >= 4 ? 32 : (N == 2 ? 16 : 8));
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
   static constexpr int BS = T < 16 ? T : 16;                     // steps per readout block
   static constexpr int NB = T / BS;                              // readout blocks per tile
   static constexpr int OPL = (CPW * BS + 63) / 64;               // readout outputs per lane per block
-  static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
   // Readout partials of a block live as [channel][step][state]: JS floats per
-  // step (the N states, padded to keep 16-byte rows on distinct banks), RS per
-  // channel.  A recurrence store (one step, lanes over states) then hits
-  // consecutive banks, and RS = min(N, 64) (mod 64) keeps the channel rows a
-  // wavefront stores at once on disjoint banks.
-  static constexpr int JS = N >= 4 ? N + 4 : N;
+  // step, RS per channel.  A recurrence store (one step, lanes over states)
+  // hits consecutive banks, and RS = min(N, 64) (mod 64) keeps the channel
+  // rows a wavefront stores at once on disjoint banks.  A reader lane sums one
+  // (channel, step) row in 16-byte groups; the 16 lanes of a 16-step block
+  // would hit the same banks, so on the DPP path each lane visits the groups
+  // of its row in the order q ^ swz(step) (kSwz, unpadded rows; the pairwise
+  // sum pairs the same groups in any such order, so the result is unchanged),
+  // and otherwise rows are padded by 4 floats.
+  static constexpr bool kSwz = kDpp;
+  static constexpr int G = N / 4;                                // 16-byte groups per row
+  static constexpr int JS = kSwz ? N : (N >= 4 ? N + 4 : N);
   static constexpr int RS_ALIGN = N >= 4 ? (N < 64 ? N : 0) : 4;
   static constexpr int RS = BS * JS + ((RS_ALIGN - (BS * JS) % 64) % 64 + 64) % 64;
+  __device__ static int swz(int step) { return kSwz ? (step / (16 / G)) % G : 0; }
+  // Wavefronts per SIMD the register allocation aims at: for N = 16 the
+  // block's LDS (39.5 KiB) allows four blocks per CU, so registers are held
+  // to 128 per lane to match.
+  static constexpr int kWaves = N == 16 ? SCAN_WAVES16 : 1;
 };
 
 // One block's view of the tensors and its fixed index math.
@@ -148,8 +167,11 @@ template <typename Tin, int N, bool SUMMARY>
 struct Block {
   using Cfg = TileCfg<N>;
   static constexpr int CH = Cfg::CH, T = Cfg::T;
-  static constexpr int VEC = Vec<Tin>::kN;          // storage elements per 16-byte vector
-  static constexpr int SEG = (T + VEC - 1) / VEC;   // vectors per tile row
+  // Storage elements per staging load: two on the DPP path (one load per
+  // thread and tile), else one 16-byte vector.
+  static constexpr int VEC = Cfg::kDpp ? SCAN_DPP_VEC : 16 / static_cast<int>(sizeof(Tin));
+  static constexpr int WORDS = VEC * static_cast<int>(sizeof(Tin)) / 4;  // 32-bit words per load
+  static constexpr int SEG = (T + VEC - 1) / VEC;   // loads per tile row
   static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
   static constexpr int BC_JOBS = N * SEG;           // (B, C) row segments
   static constexpr int JOBS = PAIR_JOBS + BC_JOBS;
@@ -161,8 +183,8 @@ template <typename Tin, int N, bool SUMMARY>
 struct TileRegs {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
-  uint4 a[Bk::JPT];                  // dt segment, or B segment
-  uint4 b[Bk::JPT];                  // u segment, or C segment
+  Words<Bk::WORDS> a[Bk::JPT];       // dt segment, or B segment
+  Words<Bk::WORDS> b[Bk::JPT];       // u segment, or C segment
   uint32_t z[Cfg::NB * Cfg::OPL];    // raw storage bits of z; converted in the readout
 };
 
@@ -188,6 +210,21 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// Store M consecutive floats to LDS (M a multiple of 4 at a 16-byte aligned
+// address, or M == 2 at an 8-byte aligned one).
+struct alignas(8) F2 {
+  float v[2];
+};
+template <int M>
+__device__ __forceinline__ void store_row(float *dst, const float *v) {
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < M; i += 4) *reinterpret_cast<F4 *>(dst + i) = F4{{v[i], v[i + 1], v[i + 2], v[i + 3]}};
+  } else {
+    *reinterpret_cast<F2 *>(dst) = F2{{v[0], v[1]}};
+  }
+}
+
 // Operands of one 16-step block on the DPP path: dt and w of step j (lane j
 // of the row), and B, C of this lane's state for the 16 steps.
 struct DppOps {
@@ -199,13 +236,14 @@ struct DppOps {
 // CKPT (with SUMMARY, one chunk): instead store the state at every
 // kScanCkptStep-step boundary, from h0, for the backward pass.
 template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z, bool CKPT = false>
-__global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileCfg<N>::kWaves)))
+scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
   constexpr int CH = Cfg::CH, CPW = Cfg::CPW, T = Cfg::T, TP = Cfg::TP, BS = Cfg::BS, NB = Cfg::NB;
   constexpr int OPL = Cfg::OPL, JS = Cfg::JS, RS = Cfg::RS;
-  constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT;
+  constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT, WORDS = Bk::WORDS;
   constexpr bool kDpp = Cfg::kDpp;
   static_assert(T % BS == 0 && BS % 4 == 0 && TP % 4 == 0 && RS % 4 == 0, "tile shape");
   static_assert(!kDpp || BS == 16, "DPP readout blocks are 16 steps");
@@ -327,8 +365,8 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     for (int k = 0; k < JPT; ++k) {
       if (jon[k]) {
         const int64_t o = jbase[k] + t0 + jcol[k];
-        R.a[k] = *reinterpret_cast<const uint4 *>(jsrc1[k] + o);
-        R.b[k] = *reinterpret_cast<const uint4 *>(jsrc2[k] + o);
+        R.a[k] = *reinterpret_cast<const Words<WORDS> *>(jsrc1[k] + o);
+        R.b[k] = *reinterpret_cast<const Words<WORDS> *>(jsrc2[k] + o);
       }
     }
     if constexpr (has_z) {
@@ -346,8 +384,8 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     for (int k = 0; k < JPT; ++k) {
       if (jon[k]) {
         const int64_t t = t0 + jcol[k];
-        R.a[k] = load_seg_tail(jsrc1[k] + jbase[k], t, t_end);
-        R.b[k] = load_seg_tail(jsrc2[k] + jbase[k], t, t_end);
+        R.a[k] = load_seg_tail<WORDS>(jsrc1[k] + jbase[k], t, t_end);
+        R.b[k] = load_seg_tail<WORDS>(jsrc2[k] + jbase[k], t, t_end);
       }
     }
 #pragma unroll
@@ -364,31 +402,29 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   };
 
   auto stage = [&](const Regs &R, int par) __attribute__((always_inline)) {
+    static_assert(VEC % 4 == 0 || VEC == 2, "staging store width");
 #pragma unroll
     for (int k = 0; k < JPT; ++k) {
       if (!jon[k]) continue;
       float va[VEC], vb[VEC];
-      Vec<Tin>::unpack(R.a[k], va);
-      Vec<Tin>::unpack(R.b[k], vb);
+      unpack(R.a[k].v, WORDS, va, gu);
+      unpack(R.b[k].v, WORDS, vb, gu);
       const int o = jrow[k] * TP + jcol[k];
       if (jkind[k] == 0) {
         const int ob = par * CH * TP + o;
+        float vw[VEC], vd[VEC];
 #pragma unroll
-        for (int i = 0; i < VEC; i += 4) {
-          sDl4[(ob + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
-          sW4[(ob + i) / 4] = F4{{va[i] * vb[i], va[i + 1] * vb[i + 1], va[i + 2] * vb[i + 2], va[i + 3] * vb[i + 3]}};
-          if (!SUMMARY) {
-            const float dk = jdsk[k];
-            sDu4[(ob + i) / 4] = F4{{dk * vb[i], dk * vb[i + 1], dk * vb[i + 2], dk * vb[i + 3]}};
-          }
+        for (int i = 0; i < VEC; ++i) {
+          vw[i] = va[i] * vb[i];
+          vd[i] = jdsk[k] * vb[i];
         }
+        store_row<VEC>(sDl + ob, va);
+        store_row<VEC>(sW + ob, vw);
+        if (!SUMMARY) store_row<VEC>(sDu + ob, vd);
       } else {
         const int ob = par * N * TP + o;
-#pragma unroll
-        for (int i = 0; i < VEC; i += 4) {
-          sB4[(ob + i) / 4] = F4{{va[i], va[i + 1], va[i + 2], va[i + 3]}};
-          if (!SUMMARY) sC4[(ob + i) / 4] = F4{{vb[i], vb[i + 1], vb[i + 2], vb[i + 3]}};
-        }
+        store_row<VEC>(sB4[0].v + ob, va);
+        if (!SUMMARY) store_row<VEC>(sC4[0].v + ob, vb);
       }
     }
   };
@@ -463,7 +499,7 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   };
 
   // Readout of block blk: sum the N partials of each of this lane's outputs
-  // (pairwise, 16 at a time), add the D skip, gate, store.  LDS reads are
+  // (pairwise), add the D skip, gate, store.  LDS reads are
   // unconditional (rows of this wave for every lane); only stores depend on
   // the output being live.  readout_load issues the LDS reads, readout_finish
   // consumes them.
@@ -476,13 +512,14 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     for (int k = 0; k < OPL; ++k) {
       const float *row = sP + erow[k] * RS + ej[k] * JS;
       if constexpr (N % 4 == 0) {
+        const int f = Cfg::swz(ej[k]);
 #pragma unroll
-        for (int i = 0; i < N; i += 4) {
-          const F4 v4 = *reinterpret_cast<const F4 *>(row + i);
-          P.v[k][i] = v4.v[0];
-          P.v[k][i + 1] = v4.v[1];
-          P.v[k][i + 2] = v4.v[2];
-          P.v[k][i + 3] = v4.v[3];
+        for (int q = 0; q < N / 4; ++q) {
+          const F4 v4 = *reinterpret_cast<const F4 *>(row + 4 * (q ^ f));
+          P.v[k][4 * q] = v4.v[0];
+          P.v[k][4 * q + 1] = v4.v[1];
+          P.v[k][4 * q + 2] = v4.v[2];
+          P.v[k][4 * q + 3] = v4.v[3];
         }
       } else {
 #pragma unroll
@@ -492,21 +529,15 @@ __global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
     }
   };
   auto readout_finish = [&](int blk, int64_t t0, const uint32_t *zz, Partials &P) __attribute__((always_inline)) {
-    constexpr int G = N < 16 ? N : 16;
 #pragma unroll
     for (int k = 0; k < OPL; ++k) {
-      float acc = 0.0f;
+      float *v = P.v[k];
 #pragma unroll
-      for (int g0 = 0; g0 < N; g0 += G) {
-        float *v = &P.v[k][g0];
+      for (int w = N / 2; w >= 1; w /= 2) {
 #pragma unroll
-        for (int w = G / 2; w >= 1; w /= 2) {
-#pragma unroll
-          for (int i = 0; i < w; ++i) v[i] += v[i + w];
-        }
-        acc = g0 == 0 ? v[0] : acc + v[0];
+        for (int i = 0; i < w; ++i) v[i] += v[i + w];
       }
-      float y = acc + P.du[k];
+      float y = v[0] + P.du[k];
       if constexpr (has_z) y *= silu(from_raw(zz[blk * OPL + k], gz));
       const int64_t t = t0 + blk * BS + ej[k];
       if (eact[k] && t < t_end) st(gy, ebase[k] + t, y);
