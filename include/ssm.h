@@ -129,8 +129,12 @@ SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const
                  float *h_last, const ssm_scan_dims_t *dims, void *stream);
 
 /*
- * Workspace ssm_scan_bwd needs for `dims`: the forward state every 16 steps,
- * 4 * batch * dim * dstate * ceil(seqlen / 16) bytes (n_chunks is ignored).
+ * Workspace ssm_scan_bwd needs for `dims` (n_chunks is ignored), 4 bytes per
+ * float: the forward state every 16 steps, batch * dim * dstate *
+ * ceil(seqlen / 16) floats; the dB and dC terms of every tile of
+ * 256 / dstate channels, 2 * batch * ngroups * ceil(dim / ngroups /
+ * (256 / dstate)) * dstate * seqlen floats; and per-batch dA and dD terms,
+ * batch * dim * (dstate + 1) floats.
  */
 SSM_API int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes);
 
@@ -163,10 +167,10 @@ SSM_API int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *byt
  *   dB, dC     : (batch, ngroups, dstate, seqlen) float32
  *   dD         : (dim) float32, required when D is given (ignored otherwise)
  *   dh0        : (batch, dim, dstate) float32, nullable
- * No output may overlap an input, another output or the workspace.  dA, dB,
- * dC and dD are accumulated with float32 atomics: their summation order, and
- * so their last bits, vary between calls; the other outputs are
- * deterministic.  Supported sizes are those of ssm_scan_fwd.
+ * No output may overlap an input, another output or the workspace.  The sums
+ * over channels (dB, dC) and over batch rows (dA, dD) are formed per channel
+ * tile or batch row in the workspace and then added in a fixed order, so every
+ * output is deterministic.  Supported sizes are those of ssm_scan_fwd.
  */
 SSM_API int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
                  const void *C, const float *D, const void *z, const float *h0, const void *dy,

@@ -23,8 +23,10 @@
 // registers), read out yhat when there is a gate, then run the adjoint
 // backwards.  Sums over states (du, ddt) go through LDS partials
 // [channel][step][state]; sums over the workgroup's channels (dB, dC) through
-// [step][state][channel] and are then added to the float32 outputs with
-// atomics, as are dA and dD (so their summation order is not fixed).
+// [step][state][channel]; each workgroup writes its channel sums of every
+// step to the workspace, as it writes its per-batch dA and dD terms, and a
+// reduction kernel then adds those over channel tiles (dB, dC) or batch rows
+// (dA, dD) in a fixed order.  No atomics: every output is deterministic.
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -249,7 +251,8 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
           const int t = e / N, nn = e % N;
           const float s = sum_row<CH>(sR + (t * N + nn) * CS);
           if (t0 + t < L)
-            atomicAdd((phase == 0 ? p.dB : p.dC) + ((b * p.ngroups + g) * N + nn) * L + t0 + t, s);
+            (phase == 0 ? p.part_dB : p.part_dC)[(((b * p.ngroups + g) * p.tiles_per_group + tile) * N + nn) * L +
+                                                 t0 + t] = s;
         }
       }
       if (phase == 0) __syncthreads();
@@ -258,28 +261,49 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
 
   if (mine) {
     if (p.dh0 != nullptr) p.dh0[(b * p.dim + d) * N + n] = lam;
-    atomicAdd(p.dA + d * N + n, dA_acc);
+    p.part_dA[(b * p.dim + d) * N + n] = dA_acc;
   }
   if (p.dD != nullptr) {
+    // This batch row's dD term per channel: the kT step positions of a
+    // channel, summed pairwise through LDS.
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
       const int e = tid + 256 * k;
-      if (e < Cfg::PAIRS_CT && e / kT < nvalid) atomicAdd(p.dD + d0 + e / kT, dD_acc[k]);
+      if (e < Cfg::PAIRS_CT) sQ[e] = dD_acc[k];
     }
+    __syncthreads();
+    if (tid < nvalid) p.part_dD[b * p.dim + d0 + tid] = sum_row<kT>(sQ + tid * kT);
   }
 }
 
-__global__ void zero_kernel(float *p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    p[i] = 0.0f;
+// out[o][i] = sum over j < J of in[o][j][i], for o < outer, i < inner: four
+// interleaved partial sums in j, combined pairwise (a fixed order).
+__global__ void __launch_bounds__(256) reduce_mid_kernel(const float *__restrict__ in, float *__restrict__ out,
+                                                         int64_t outer, int64_t J, int64_t inner) {
+  const int64_t total = outer * inner;
+  for (int64_t x = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; x < total;
+       x += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t o = x / inner, i = x % inner;
+    const float *src = in + o * J * inner + i;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t j = 0;
+    for (; j + 4 <= J; j += 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += src[(j + k) * inner];
+    }
+    for (int k = 0; j < J; ++j, ++k) acc[k] += src[j * inner];
+    out[x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
 }
 
-hipError_t zero(float *p, int64_t n, hipStream_t stream) {
-  if (p == nullptr || n <= 0) return hipSuccess;
-  const int64_t want = (n + 255) / 256;
-  const int64_t blocks = want < 8192 ? want : 8192;
-  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p, n);
+hipError_t reduce_mid(const float *in, float *out, int64_t outer, int64_t J, int64_t inner, hipStream_t stream) {
+  const int64_t total = outer * inner;
+  if (out == nullptr || total <= 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int64_t blocks = want < 16384 ? want : 16384;
+  hipLaunchKernelGGL(reduce_mid_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, in, out, outer,
+                     J, inner);
   return hipGetLastError();
 }
 
@@ -314,14 +338,16 @@ hipError_t launch_bwd_typed(const ScanBwdParams &p, hipStream_t stream) {
 
 hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hipStream_t stream) {
   hipError_t e;
-  if ((e = zero(p.dA, p.dim * p.dstate, stream)) != hipSuccess) return e;
-  if ((e = zero(p.dB, p.batch * p.ngroups * p.dstate * p.seqlen, stream)) != hipSuccess) return e;
-  if ((e = zero(p.dC, p.batch * p.ngroups * p.dstate * p.seqlen, stream)) != hipSuccess) return e;
-  if ((e = zero(p.dD, p.D != nullptr ? p.dim : 0, stream)) != hipSuccess) return e;
-  if (!in_bf16 && !out_bf16) return launch_bwd_typed<float, float>(p, stream);
-  if (!in_bf16 && out_bf16) return launch_bwd_typed<float, uint16_t>(p, stream);
-  if (in_bf16 && !out_bf16) return launch_bwd_typed<uint16_t, float>(p, stream);
-  return launch_bwd_typed<uint16_t, uint16_t>(p, stream);
+  if (!in_bf16 && !out_bf16) e = launch_bwd_typed<float, float>(p, stream);
+  else if (!in_bf16 && out_bf16) e = launch_bwd_typed<float, uint16_t>(p, stream);
+  else if (in_bf16 && !out_bf16) e = launch_bwd_typed<uint16_t, float>(p, stream);
+  else e = launch_bwd_typed<uint16_t, uint16_t>(p, stream);
+  if (e != hipSuccess) return e;
+  const int64_t bg = p.batch * p.ngroups, nl = p.dstate * p.seqlen;
+  if ((e = reduce_mid(p.part_dB, p.dB, bg, p.tiles_per_group, nl, stream)) != hipSuccess) return e;
+  if ((e = reduce_mid(p.part_dC, p.dC, bg, p.tiles_per_group, nl, stream)) != hipSuccess) return e;
+  if ((e = reduce_mid(p.part_dA, p.dA, 1, p.batch, p.dim * p.dstate, stream)) != hipSuccess) return e;
+  return reduce_mid(p.part_dD, p.D != nullptr ? p.dD : nullptr, 1, p.batch, p.dim, stream);
 }
 
 }  // namespace ssm

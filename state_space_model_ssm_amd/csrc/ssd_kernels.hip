@@ -38,6 +38,9 @@
 #ifndef SSD_PREFETCH
 #define SSD_PREFETCH 1
 #endif
+#ifndef SSD_H0_WAIT
+#define SSD_H0_WAIT 1
+#endif
 
 namespace ssm {
 namespace {
@@ -151,6 +154,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #pragma unroll
     for (int i = 0; i < NT; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
   }
+#if SSD_H0_WAIT
+  // Retire the initial-state loads here (s_waitcnt vmcnt(0)).  Otherwise they
+  // may count as outstanding at the top of the chunk loop, and the first use
+  // of S in every chunk would wait for all loads in flight, prefetches included.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
 
   // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group;
   // the 8-column groups of a row go to consecutive lanes, so a wavefront's

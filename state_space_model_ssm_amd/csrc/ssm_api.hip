@@ -211,9 +211,25 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
 // Selective-scan backward
 // ---------------------------------------------------------------------------
 
-static size_t scan_bwd_workspace(const ssm_scan_dims_t *d) {
-  return 4ull * d->batch * d->dim * d->dstate * ceil_div(d->seqlen, ssm::kScanCkptStep);
+// Backward workspace, in floats: the state checkpoints, then the dB and dC
+// terms of every channel tile, then the per-batch dA and dD terms.
+struct BwdWorkspace {
+  size_t ckpt, part_bc, part_a, part_d;
+  size_t bytes() const { return 4 * (ckpt + 2 * part_bc + part_a + part_d); }
+};
+
+static BwdWorkspace scan_bwd_layout(const ssm_scan_dims_t *d) {
+  const int64_t tiles =
+      d->ngroups > 0 ? ceil_div(d->dim / d->ngroups, ssm::scan_channels_per_block(static_cast<int>(d->dstate))) : 0;
+  BwdWorkspace w;
+  w.ckpt = static_cast<size_t>(d->batch * d->dim * d->dstate * ceil_div(d->seqlen, ssm::kScanCkptStep));
+  w.part_bc = static_cast<size_t>(d->batch * d->ngroups * tiles * d->dstate * d->seqlen);
+  w.part_a = static_cast<size_t>(d->batch * d->dim * d->dstate);
+  w.part_d = static_cast<size_t>(d->batch * d->dim);
+  return w;
 }
+
+static size_t scan_bwd_workspace(const ssm_scan_dims_t *d) { return scan_bwd_layout(d).bytes(); }
 
 int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes) {
   if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
@@ -264,7 +280,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
   const size_t need = scan_bwd_workspace(&d);
   if (need > 0) {
     if (!d.workspace || d.workspace_bytes < need)
-      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required for the state checkpoints (got %zu)",
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required for checkpoints and partial sums (got %zu)",
                   need, d.workspace ? d.workspace_bytes : (size_t)0);
     if (!aligned(d.workspace, 4)) return fail(SSM_ERR_ALIGN, "workspace must be 4-byte aligned");
     const Span sw{d.workspace, need};
@@ -273,8 +289,8 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
     for (const Span &s : outs)
       if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
   }
-  // An empty batch or channel set still zeroes dA, dB, dC and dD (sums over
-  // nothing); the kernels then launch no workgroup.
+  // An empty batch or channel set still writes zeros to dA and dD (sums over
+  // nothing); the backward kernel then launches no workgroup.
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t tiles = ceil_div(d.dim / d.ngroups, ssm::scan_channels_per_block(static_cast<int>(d.dstate)));
   ssm::ScanParams f{};
@@ -318,6 +334,12 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
   p.dD = dD;
   p.dh0 = dh0;
   p.ckpt = static_cast<const float *>(d.workspace);
+  const BwdWorkspace wl = scan_bwd_layout(&d);
+  float *ws = static_cast<float *>(d.workspace);
+  p.part_dB = ws + wl.ckpt;
+  p.part_dC = p.part_dB + wl.part_bc;
+  p.part_dA = p.part_dC + wl.part_bc;
+  p.part_dD = p.part_dA + wl.part_a;
   p.batch = d.batch;
   p.dim = d.dim;
   p.seqlen = d.seqlen;

@@ -57,12 +57,16 @@ struct ScanBwdParams {
   void *du, *ddelta, *dz;             // in_dtype; dz only with z
   float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
   const float *ckpt;                  // [batch][dim][ceil(L / kScanCkptStep)][dstate]
+  // Workspace for the sums: per channel tile, dB and dC terms
+  // [batch][ngroups][tiles_per_group][dstate][L]; per batch row, dA terms
+  // [batch][dim][dstate] and dD terms [batch][dim].
+  float *part_dB, *part_dC, *part_dA, *part_dD;
   int64_t batch, dim, seqlen, ngroups, dim_per_group, tiles_per_group;
   int32_t dstate;
 };
 
-// Zero dA, dB, dC, dD, then run the backward kernel (the checkpoint pass must
-// have run on the same stream).
+// Run the backward kernel (the checkpoint pass must have run on the same
+// stream), then reduce its per-tile and per-batch terms into dB, dC, dA, dD.
 hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hipStream_t stream);
 
 // One chunked-SSD launch (see ssd_chunked_fwd in include/ssm.h).

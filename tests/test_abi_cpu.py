@@ -263,7 +263,10 @@ def _bwd(dims, **kw):
 def test_scan_bwd_rules():
     d = _dims(seqlen=100)
     need = ssm.scan_bwd_workspace_size(d)
-    assert need == 4 * 2 * 64 * 16 * 7          # a state every 16 steps: ceil(100 / 16) = 7
+    ckpt = 2 * 64 * 16 * 7                        # a state every 16 steps: ceil(100 / 16) = 7
+    terms_bc = 2 * (2 * 1 * 4 * 16 * 100)         # dB, dC terms of 4 tiles of 16 channels
+    terms_ad = 2 * 64 * (16 + 1)                  # per-batch dA and dD terms
+    assert need == 4 * (ckpt + terms_bc + terms_ad)
     assert _bwd(d) == -6                          # no workspace
     d.workspace, d.workspace_bytes = FAKE + 0x30000000, need
     assert _bwd(d, dy=None) == -1

@@ -459,7 +459,7 @@ def test_ssd_prefill_then_128_decode_steps():
 # Gradients are compared tensor by tensor with the float64 oracle backward,
 # max|g - g_ref| / max|g_ref|, against the forward's bars: 1e-5 for float32
 # (measured worst case 1.4e-6, on dA, which sums every step of every batch
-# row in float32 atomics of any order) and 2e-2 with bf16 storage.
+# row in float32) and 2e-2 with bf16 storage.
 TOL_BWD_F32 = 1e-5
 
 BWD_CASES = [
@@ -501,7 +501,7 @@ def test_scan_backward(case):
 
 def test_scan_backward_medium_bf16():
     """A larger bf16 case (2 x 256 channels x 1024 steps, gate and D skip):
-    dB and dC sum 256 channels per group through the atomics."""
+    dB and dC sum 16 channel tiles of 16 channels per group."""
     s = ScanShape(2, 256, 16, 1024, 1, "bf16", has_z=True, dskip="normal", a_kind="neg_n1", seed=5600)
     inp = make_scan_inputs(s)
     dy = make_state((2, 256, 1024), seed=5601).to(torch.bfloat16)
@@ -512,6 +512,21 @@ def test_scan_backward_medium_bf16():
     for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
         err = rel_err(g[k].float().cpu(), ref[k])
         assert err <= TOL_BF16, (k, err)
+
+
+def test_scan_backward_deterministic():
+    """Two calls give bitwise equal gradients: the sums over channel tiles and
+    batch rows run in a fixed order."""
+    s = ScanShape(3, 96, 16, 300, 2, "f32", has_z=True, dskip="normal", a_kind="loguniform", seed=5650)
+    inp = make_scan_inputs(s)
+    dy = make_state((3, 96, 300), seed=5651)
+    dhl = make_state((3, 96, 16), seed=5652)
+    args = [_dev(inp[k]) for k in ("u", "delta", "A", "B", "C", "D", "z")]
+    g1 = ssm.scan_bwd(*args, dy=_dev(dy), dh_last=_dev(dhl))
+    g2 = ssm.scan_bwd(*args, dy=_dev(dy), dh_last=_dev(dhl))
+    torch.cuda.synchronize()
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        assert torch.equal(g1[k], g2[k]), k
 
 
 def test_scan_backward_empty_sequence():
