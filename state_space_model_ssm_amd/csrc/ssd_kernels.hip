@@ -70,6 +70,19 @@ __device__ __forceinline__ bf16x8 lds8(const uint16_t *p) {  // 16-byte LDS read
 __device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) { p[i] = f2bf(v); }
 
+// Value of lane (l - N) of this lane's 16-lane row, or 0 when that lane is
+// outside the row (DPP row_shr with bound_ctrl).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+
+// Value of lane J (wave-uniform).
+template <int J>
+__device__ __forceinline__ float lane_value(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), J));
+}
+
 __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
@@ -250,13 +263,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
     // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
     if (wave == 0) {
       const float dtv = (c0 + lane < L) ? bf2f(static_cast<uint16_t>(R.dt)) : 0.0f;
+      // Inclusive prefix sum over the 64 lanes: within each 16-lane row by
+      // DPP row shifts (lanes shifted in from outside the row read 0), then
+      // the totals of the rows below, read from lanes 15, 31 and 47.
       float a = dtv * Ah;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(a, off);
-        if (lane >= off) a += o;
-      }
-      const float alast = __shfl(a, 63);
+      a += row_shr<1>(a);
+      a += row_shr<2>(a);
+      a += row_shr<4>(a);
+      a += row_shr<8>(a);
+      const float r0 = lane_value<15>(a), r1 = lane_value<31>(a), r2 = lane_value<47>(a);
+      a += (lane >= 16 ? r0 : 0.0f) + (lane >= 32 ? r1 : 0.0f) + (lane >= 48 ? r2 : 0.0f);
+      const float alast = lane_value<63>(a);
       float w = dtv;
       if constexpr (TRAP) {
         // Weight of this step's input wherever it reaches a later step; the
@@ -305,8 +322,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
     }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
+      const floatx4 ea = *reinterpret_cast<const floatx4 *>(&sEa[ti * 16 + 4 * q]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Y[ti][r] *= sEa[ti * 16 + 4 * q + r];
+      for (int r = 0; r < 4; ++r) Y[ti][r] *= ea[r];
     }
 
     // ---- S_new = exp(a_last) S_prev + B^T (w x) ----------------------------
@@ -318,9 +336,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       for (int kk = 0; kk < 2; ++kk) {
         const int s0 = 32 * kk + 8 * q;
         const bf16x8 xs = lds8(&sXt[tidx<P>(pcol, s0)]);
+        const floatx4 w0 = *reinterpret_cast<const floatx4 *>(&sW[s0]);
+        const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sW[s0 + 4]);
         floatx8 wx;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) wx[j] = static_cast<float>(xs[j]) * sW[s0 + j];
+        for (int j = 0; j < 4; ++j) {
+          wx[j] = static_cast<float>(xs[j]) * w0[j];
+          wx[j + 4] = static_cast<float>(xs[j + 4]) * w1[j];
+        }
         const bf16x8 bfrag = __builtin_convertvector(wx, bf16x8);
 #pragma unroll
         for (int ni = 0; ni < NT; ++ni) {
@@ -354,12 +377,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         }
         const int t = ti * 16 + r16;
         const float at = sA[t];
+        const int sb = si * 16 + 4 * q;
+        const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sA[sb]);
+        const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
+        floatx4 gm4 = dt4;
+        if constexpr (TRAP) gm4 = *reinterpret_cast<const floatx4 *>(&sGam[sb]);
         uint16_t m[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int s = si * 16 + 4 * q + r;
-          const float ws = TRAP ? (s < t ? sDt[s] : sGam[s]) : sDt[s];
-          const float v = (s <= t) ? acc[r] * fast_exp(at - sA[s]) * ws : 0.0f;
+          const int s = sb + r;
+          const float ws = s < t ? dt4[r] : gm4[r];
+          const float v = (s <= t) ? acc[r] * fast_exp(at - as4[r]) * ws : 0.0f;
           m[r] = f2bf(v);
         }
         *reinterpret_cast<uint2 *>(&sM[t * QP + si * 16 + 4 * q]) = *reinterpret_cast<const uint2 *>(m);
