@@ -200,7 +200,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   };
 
   // One chunk's global inputs in registers: loaded a chunk ahead (while the
-  // previous chunk computes), then written to LDS.
+  // previous chunk computes), then written to LDS.  Steps past the end of the
+  // sequence load copies of the last step: their dt is taken as 0, so they
+  // reach no output row that is stored and add nothing to the state (their
+  // weights in M and in the state update are 0).  The loads are branch-free.
   struct ChunkRegs {
     uint4 bv[BJ][2], cv[BJ][2];
     uint4 xv[2];
@@ -215,14 +218,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       const int nv = (v % (N / 8)) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int t = 2 * tp + e;
-        R.bv[k][e] = uint4{0u, 0u, 0u, 0u};
-        R.cv[k][e] = uint4{0u, 0u, 0u, 0u};
-        if (c0 + t < L) {
-          const int64_t off = ((b * L + c0 + t) * G + g) * N + nv;
-          R.bv[k][e] = *reinterpret_cast<const uint4 *>(gB + off);
-          R.cv[k][e] = *reinterpret_cast<const uint4 *>(gC + off);
-        }
+        const int64_t tc = min(c0 + 2 * tp + e, L - 1);
+        const int64_t off = ((b * L + tc) * G + g) * N + nv;
+        R.bv[k][e] = *reinterpret_cast<const uint4 *>(gB + off);
+        R.cv[k][e] = *reinterpret_cast<const uint4 *>(gC + off);
       }
     }
     {
@@ -230,9 +229,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       const int pv = (tid % (P / 8)) * 8;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int t = 2 * tp + e;
-        R.xv[e] = uint4{0u, 0u, 0u, 0u};
-        if (c0 + t < L) R.xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + c0 + t) * H + h) * P + pv);
+        const int64_t tc = min(c0 + 2 * tp + e, L - 1);
+        R.xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + tc) * H + h) * P + pv);
       }
     }
     // Unconditional load from a clamped step: no branch, so nothing waits
