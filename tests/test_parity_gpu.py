@@ -110,6 +110,7 @@ SCAN_CASES = [
     (2, 6, 64, 97, 2, "f32", True, "normal", 3),
     (2, 50, 16, 257, 1, "bf16", True, "normal", 1),
     (2, 50, 16, 257, 1, "bf16", True, "ones", 4),
+    (2, 50, 16, 264, 1, "bf16", True, "normal", 1),     # vector tiles, then an element tail
     (1, 12, 64, 130, 1, "bf16", False, "normal", 1),
 ]
 
@@ -125,6 +126,27 @@ def test_scan_small(case):
     tol = tol_for(dtype)
     assert rel_err(y, yr) <= tol, rel_err(y, yr)
     assert rel_err(h, hr) <= tol, rel_err(h, hr)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_misaligned_rows(dtype):
+    """Inputs one element past a 16-byte boundary (L a multiple of the vector
+    width): the library must take the element path for every tile."""
+    s = ScanShape(2, 40, 16, 128, 1, dtype, has_z=True, dskip="normal", seed=91)
+    inp = make_scan_inputs(s)
+
+    def shifted(t):
+        flat = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
+        v = flat[1:1 + t.numel()].view(t.shape)
+        v.copy_(t.to("cuda"))
+        return v
+
+    y, h = ssm.scan_fwd(shifted(inp["u"]), shifted(inp["delta"]), _dev(inp["A"]), shifted(inp["B"]),
+                        shifted(inp["C"]), _dev(inp["D"]), shifted(inp["z"]))
+    torch.cuda.synchronize()
+    yr, hr = ref_scan(inp)
+    assert rel_err(y.float().cpu(), yr) <= tol_for(dtype)
+    assert rel_err(h.cpu(), hr) <= tol_for(dtype)
 
 
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "bf16"), ("bf16", "f32")])
