@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cold-reps", type=int, default=30,
+                    help="calls timed one at a time after a 512 MiB cache flush (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -126,6 +128,31 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
+
+    flush = {}
+
+    def time_cold(fn, reps):
+        """Cold-cache timing: before each call, overwrite a 512 MiB buffer on
+        the same stream (evicting L2 and the 256 MB Infinity Cache), then time
+        that one call with events.  Returns the median and the 10th/90th
+        percentiles in ms."""
+        if "buf" not in flush:
+            flush["buf"] = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn()
+        ts = []
+        for i in range(reps):
+            flush["buf"].fill_(float(i))
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        pick = lambda q: ts[min(len(ts) - 1, int(q * (len(ts) - 1) + 0.5))]
+        return {"median_ms": round(pick(0.5), 5), "p10_ms": round(pick(0.1), 5), "p90_ms": round(pick(0.9), 5),
+                "reps": reps}
 
     def scan_runner(s: ScanShape, host):
         d = {k: (None if v is None else v.to(dev)) for k, v in host.items()}
@@ -182,6 +209,7 @@ def main():
     roof["hbm_frac"] = round(hbm_gbs / HBM_PEAK_GBS, 4)
     roof["alu_model_us"] = round(t_alu * 1e6, 2)
     roof["hbm_model_us"] = round(t_hbm * 1e6, 2)
+    cold = time_cold(fn, args.cold_reps) if args.cold_reps > 0 else None
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -209,7 +237,11 @@ def main():
                 context[name] = {"ms": round(wms, 5), "Gelem/s": round(w.elements / wms / 1e6, 2),
                                  "hbm_GB/s": round(w.metric_bytes() / wms / 1e6, 1),
                                  "hbm_GB/s_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6, 1),
+                                 "hbm_frac_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6 /
+                                                               HBM_PEAK_GBS, 4),
                                  "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2)}
+                if args.cold_reps > 0:
+                    context[name]["cold"] = time_cold(f, args.cold_reps)
         context.update(decode_context(ssm, dev, stream, time_calls))
         context.update(extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs))
     torch.cuda.synchronize()
@@ -253,6 +285,7 @@ def main():
         "hbm_pct_of_peak": round(100 * hbm_gbs / HBM_PEAK_GBS, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
+        "cold": cold,
         "cpu_baseline": cpu,
         "workloads": context,
     }
