@@ -19,9 +19,9 @@
 // kScanCkptStep = 16 steps.  Here one 256-thread workgroup takes a tile of
 // 256 / N channels (one (channel, state) per thread, as in the forward) and
 // walks 16-step time tiles from the last to the first: stage the tile's
-// inputs in LDS, recompute its 16 states from the checkpoint (kept in
-// registers), read out yhat when there is a gate, then run the adjoint
-// backwards.  Sums over states (du, ddt) go through LDS partials
+// inputs in LDS (loaded into registers one tile ahead), recompute its 16
+// states and decays from the checkpoint (kept in registers), read out yhat
+// when there is a gate, then run the adjoint backwards.  Sums over states (du, ddt) go through LDS partials
 // [channel][step][state]; sums over the workgroup's channels (dB, dC) through
 // [step][state][channel]; each workgroup writes its channel sums of every
 // step to the workspace, as it writes its per-batch dA and dD terms, and a
@@ -33,6 +33,7 @@ namespace ssm {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
 constexpr int kT = static_cast<int>(kScanCkptStep);  // steps per tile
 
 __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
@@ -127,31 +128,105 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
 #pragma unroll
   for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) dD_acc[k] = 0.0f;
 
+  // A tile's global inputs, loaded one tile ahead into registers (in storage
+  // form, converted when staged) when they take at most a few registers per
+  // thread (N >= 8); the loads read clamped, always valid steps and rows, so
+  // they are branch-free, and staging zeroes what lies past the end.
+  constexpr int PE = (Cfg::PAIRS_CT + 255) / 256;   // (channel, step) elements per thread
+  constexpr int PB = (Cfg::PAIRS_NT + 255) / 256;   // (state, step) elements per thread
+  constexpr bool kPrefetch = PE <= 2 && PB <= 4;
+  struct TileIn {
+    Tin dl[PE], u[PE], z[PE], bb[PB], cc[PB];
+    Tout dy[PE];
+    float h0;
+  };
+  auto load_tile = [&](int64_t ti, TileIn &R) __attribute__((always_inline)) {
+    const int64_t t0 = ti * kT;
+#pragma unroll
+    for (int k = 0; k < PE; ++k) {
+      const int e = tid + 256 * k;
+      if (Cfg::PAIRS_CT % 256 != 0 && e >= Cfg::PAIRS_CT) continue;  // uniform per wavefront
+      const int r = e / kT, t = e % kT;
+      const int64_t at = (b * p.dim + d0 + min(r, nvalid - 1)) * L + min(t0 + t, L - 1);
+      R.dl[k] = gdl[at];
+      R.u[k] = gu[at];
+      R.dy[k] = gdy[at];
+      if constexpr (HAS_Z) R.z[k] = gz[at];
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int e = tid + 256 * k;
+      if (Cfg::PAIRS_NT % 256 != 0 && e >= Cfg::PAIRS_NT) continue;
+      const int r = e / kT, t = e % kT;
+      const int64_t at = ((b * p.ngroups + g) * N + r) * L + min(t0 + t, L - 1);
+      R.bb[k] = gB[at];
+      R.cc[k] = gC[at];
+    }
+    R.h0 = p.ckpt[((b * p.dim + d) * ntiles + ti) * N + n];
+  };
+  auto stage_tile = [&](int64_t ti, const TileIn &R) __attribute__((always_inline)) {
+    const int64_t t0 = ti * kT;
+#pragma unroll
+    for (int k = 0; k < PE; ++k) {
+      const int e = tid + 256 * k;
+      if (Cfg::PAIRS_CT % 256 != 0 && e >= Cfg::PAIRS_CT) continue;
+      const int r = e / kT, t = e % kT;
+      const bool in = t0 + t < L;
+      sDl[r * TP + t] = in ? ld(R.dl + k, 0) : 0.0f;
+      sU[r * TP + t] = in ? ld(R.u + k, 0) : 0.0f;
+      sDy[r * TP + t] = (in && r < nvalid) ? ld(R.dy + k, 0) : 0.0f;
+      if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(R.z + k, 0) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < PB; ++k) {
+      const int e = tid + 256 * k;
+      if (Cfg::PAIRS_NT % 256 != 0 && e >= Cfg::PAIRS_NT) continue;
+      const int r = e / kT, t = e % kT;
+      const bool in = t0 + t < L;
+      sB[r * TP + t] = in ? ld(R.bb + k, 0) : 0.0f;
+      sC[r * TP + t] = in ? ld(R.cc + k, 0) : 0.0f;
+    }
+  };
+  TileIn R;
+  if constexpr (kPrefetch) {
+    if (ntiles > 0) load_tile(ntiles - 1, R);
+  }
+
   for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
     const int64_t t0 = ti * kT;
     __syncthreads();  // the previous tile is done with every LDS buffer
     // ---- stage the tile: rows of 16 steps, zero past the end ---------------
-    for (int e = tid; e < CH * kT; e += 256) {
-      const int r = e / kT, t = e % kT;
-      const int64_t row = (b * p.dim + d0 + min(r, nvalid - 1)) * L;
-      const bool in = t0 + t < L;
-      sDl[r * TP + t] = in ? ld(gdl, row + t0 + t) : 0.0f;
-      sU[r * TP + t] = in ? ld(gu, row + t0 + t) : 0.0f;
-      sDy[r * TP + t] = (in && r < nvalid) ? ld(gdy, row + t0 + t) : 0.0f;
-      if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(gz, row + t0 + t) : 0.0f;
+    float h_start;
+    if constexpr (kPrefetch) {
+      stage_tile(ti, R);
+      h_start = mine ? R.h0 : 0.0f;
+    } else {
+      for (int e = tid; e < CH * kT; e += 256) {
+        const int r = e / kT, t = e % kT;
+        const int64_t row = (b * p.dim + d0 + min(r, nvalid - 1)) * L;
+        const bool in = t0 + t < L;
+        sDl[r * TP + t] = in ? ld(gdl, row + t0 + t) : 0.0f;
+        sU[r * TP + t] = in ? ld(gu, row + t0 + t) : 0.0f;
+        sDy[r * TP + t] = (in && r < nvalid) ? ld(gdy, row + t0 + t) : 0.0f;
+        if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(gz, row + t0 + t) : 0.0f;
+      }
+      for (int e = tid; e < N * kT; e += 256) {
+        const int r = e / kT, t = e % kT;
+        const int64_t row = ((b * p.ngroups + g) * N + r) * L;
+        const bool in = t0 + t < L;
+        sB[r * TP + t] = in ? ld(gB, row + t0 + t) : 0.0f;
+        sC[r * TP + t] = in ? ld(gC, row + t0 + t) : 0.0f;
+      }
+      h_start = mine ? p.ckpt[((b * p.dim + d) * ntiles + ti) * N + n] : 0.0f;
     }
-    for (int e = tid; e < N * kT; e += 256) {
-      const int r = e / kT, t = e % kT;
-      const int64_t row = ((b * p.ngroups + g) * N + r) * L;
-      const bool in = t0 + t < L;
-      sB[r * TP + t] = in ? ld(gB, row + t0 + t) : 0.0f;
-      sC[r * TP + t] = in ? ld(gC, row + t0 + t) : 0.0f;
-    }
-    const float h_start = mine ? p.ckpt[((b * p.dim + d) * ntiles + ti) * N + n] : 0.0f;
     __syncthreads();
+    if constexpr (kPrefetch) {
+      if (ti > 0) load_tile(ti - 1, R);
+    }
 
     // ---- recompute the tile's states; readout partials for the gate --------
     float hist[kT];
+    float dec[kT];  // exp(dt A) of each step, reused by the adjoint
     {
       float h = h_start;
 #pragma unroll
@@ -162,8 +237,10 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float dl = dl4.v[i];
-          h = fmaf(__builtin_amdgcn_exp2f(dl * a2), h, dl * u4.v[i] * b4.v[i]);
+          const float a = __builtin_amdgcn_exp2f(dl * a2);
+          h = fmaf(a, h, dl * u4.v[i] * b4.v[i]);
           hist[t4 + i] = h;
+          dec[t4 + i] = a;
           if constexpr (HAS_Z) sQ[chl * RS + (t4 + i) * JS + n] = c4.v[i] * h;
         }
       }
@@ -197,7 +274,10 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     __syncthreads();
 
     // ---- adjoint, backwards through the tile --------------------------------
-    float pdu[kT], pddl[kT], pdB[kT], pdC[kT];
+    // The du and dB terms go straight to LDS (both buffers are free since the
+    // barrier above); the ddt and dC terms wait in registers for the second
+    // reduction phase.
+    float pddl[kT], pdC[kT];
 #pragma unroll
     for (int t4 = kT - 4; t4 >= 0; t4 -= 4) {
       const F4 dl4 = sDl4[(chl * TP + t4) / 4], u4 = sU4[(chl * TP + t4) / 4], dy4 = sDy4[(chl * TP + t4) / 4];
@@ -206,12 +286,12 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
       for (int i = 3; i >= 0; --i) {
         const int t = t4 + i;
         const float dl = dl4.v[i], uu = u4.v[i], dyh = dy4.v[i], bv = b4.v[i], cv = c4.v[i];
-        const float a = __builtin_amdgcn_exp2f(dl * a2);
+        const float a = dec[t];
         const float hprev = t > 0 ? hist[t - 1] : h_start;
         const float l = fmaf(dyh, cv, lam);
         pdC[t] = mine ? dyh * hist[t] : 0.0f;
-        pdB[t] = mine ? l * dl * uu : 0.0f;
-        pdu[t] = l * dl * bv;
+        sR[(t * N + n) * CS + chl] = mine ? l * dl * uu : 0.0f;
+        sQ[chl * RS + t * JS + n] = l * dl * bv;
         pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
         dA_acc = fmaf(l * dl * a, hprev, dA_acc);
         lam = a * l;
@@ -221,10 +301,12 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     // ---- reductions: (du over states, dB over channels), then (ddt, dC) ---
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
+      if (phase == 1) {
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        sQ[chl * RS + t * JS + n] = phase == 0 ? pdu[t] : pddl[t];
-        sR[(t * N + n) * CS + chl] = phase == 0 ? pdB[t] : pdC[t];
+        for (int t = 0; t < kT; ++t) {
+          sQ[chl * RS + t * JS + n] = pddl[t];
+          sR[(t * N + n) * CS + chl] = pdC[t];
+        }
       }
       __syncthreads();
 #pragma unroll
