@@ -81,8 +81,12 @@ int check_scan_dims(const ssm_scan_dims_t *d) {
 }
 
 // Chunk count the call uses.  0 asks the library: split the sequence only when
-// the channels alone give fewer than ~1024 wavefronts (one per SIMD of the
-// 256-CU part), and keep every chunk at least 64 steps long.
+// the channels alone give fewer than 1024 wavefronts (one per SIMD of the
+// 256-CU part) and the sequence has at least 384 steps; then aim at ~4096
+// wavefronts with chunks of at least 128 steps (at most 64 chunks).  Measured
+// on 1536 channels: 384 steps and fewer run fastest in one pass (the summary
+// pass and a second launch cost more than they save), 4096 steps take 65 us
+// in 8-16 chunks against 149 us in one.
 int32_t resolve_chunks(const ssm_scan_dims_t *d, int64_t *chunk_len) {
   const int64_t L = d->seqlen;
   if (L <= 1 || d->batch == 0 || d->dim == 0) {
@@ -92,10 +96,14 @@ int32_t resolve_chunks(const ssm_scan_dims_t *d, int64_t *chunk_len) {
   int64_t want = d->n_chunks;
   if (want == 0) {
     const int64_t waves = d->batch * d->dim * d->dstate / 64;
-    want = waves >= 1024 ? 1 : ceil_div(1024, waves > 0 ? waves : 1);
-    const int64_t cap = L / 64 > 1 ? L / 64 : 1;
-    if (want > cap) want = cap;
-    if (want > 64) want = 64;
+    if (waves >= 1024 || L < 384) {
+      want = 1;
+    } else {
+      want = ceil_div(4096, waves > 0 ? waves : 1);
+      const int64_t cap = L / 128;
+      if (want > cap) want = cap;
+      if (want > 64) want = 64;
+    }
   }
   if (want > L) want = L;
   int64_t len = ceil_div(L, want);

@@ -143,10 +143,16 @@ def test_scan_auto_chunks_keep_big_work_in_one_pass():
     # enough channels for >= 1024 wavefronts: a single pass
     assert ssm.scan_resolved_chunks(_dims(batch=8, dim=1536, seqlen=2048)) == 1
     assert ssm.scan_resolved_chunks(_dims(batch=4, dim=5120, seqlen=4096)) == 1
-    # few channels: split, with chunks of at least 64 steps
+    # few channels: split, aiming at ~4096 wavefronts with chunks of >= 128 steps
     k = ssm.scan_resolved_chunks(_dims(batch=1, dim=64, seqlen=4096))
-    assert 1 < k <= 64
+    assert k == 32                               # capped by 4096 / 128
+    assert ssm.scan_resolved_chunks(_dims(batch=1, dim=1536, seqlen=4096)) == 11   # 384 wavefronts
+    assert ssm.scan_resolved_chunks(_dims(batch=1, dim=1536, seqlen=1024)) == 8
+    assert ssm.scan_resolved_chunks(_dims(batch=2, dim=768, seqlen=2048)) == 11
+    # short sequences stay in one pass
     assert ssm.scan_resolved_chunks(_dims(batch=1, dim=64, seqlen=100)) == 1
+    assert ssm.scan_resolved_chunks(_dims(batch=1, dim=1536, seqlen=128)) == 1
+    assert ssm.scan_resolved_chunks(_dims(batch=1, dim=64, seqlen=383)) == 1
 
 
 def _sdims(**kw):
