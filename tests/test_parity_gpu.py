@@ -536,6 +536,47 @@ def test_scan_backward_medium_bf16():
         assert err <= TOL_BF16, (k, err)
 
 
+def test_scan_backward_long_prefill_full_size():
+    """The long-prefill workload (8 x 1536 channels x 2048 steps, float32,
+    gate and D skip) at full size, every gradient against the oracle's
+    (about 15 s of oracle time)."""
+    s = WORKLOADS["long_prefill_8x1536x2048_f32"]
+    inp = make_scan_inputs(s)
+    dy = make_state((s.batch, s.dim, s.seqlen), seed=5800)
+    dhl = make_state((s.batch, s.dim, s.dstate), seed=5801)
+    g = ssm.scan_bwd(_dev(inp["u"]), _dev(inp["delta"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                     _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy), dh_last=_dev(dhl))
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else v.cpu()) for k, v in g.items()}
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], None, dy, dhl)
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        err = rel_err(g[k], ref[k])
+        assert err <= TOL_BWD_F32, (k, err)
+
+
+def test_scan_backward_large_channel_sampled():
+    """The large-channel workload (4 x 5120 channels x 4096 steps, bf16) at
+    full size.  Per-channel gradients (du, ddt, dz, dh0, and dA, dD, which sum
+    over batch rows only) of 32 sampled channels against the oracle on those
+    channels' slice; dB and dC sum over all 5120 channels and are covered at
+    full size by the long-prefill test."""
+    s = WORKLOADS["large_channel_4x5120x4096_bf16"]
+    inp = make_scan_inputs(s)
+    dy = make_state((s.batch, s.dim, s.seqlen), seed=5900).to(torch.bfloat16)
+    g = ssm.scan_bwd(_dev(inp["u"]), _dev(inp["delta"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                     _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy))
+    torch.cuda.synchronize()
+    ch = torch.from_numpy(np.sort(np.random.default_rng(5901).choice(s.dim, size=32, replace=False)))
+    sl = lambda t: t[:, ch].contiguous()
+    ref = oracle.scan_bwd(sl(inp["u"]), sl(inp["delta"]), inp["A"][ch].contiguous(), inp["B"], inp["C"],
+                          inp["D"][ch].contiguous(), sl(inp["z"]), None, sl(dy), None)
+    got = {"du": g["du"].cpu()[:, ch], "ddelta": g["ddelta"].cpu()[:, ch], "dz": g["dz"].cpu()[:, ch],
+           "dh0": g["dh0"].cpu()[:, ch], "dA": g["dA"].cpu()[ch], "dD": g["dD"].cpu()[ch]}
+    for k, v in got.items():
+        err = rel_err(v.float(), ref[k])
+        assert err <= TOL_BF16, (k, err)
+
+
 def test_scan_backward_deterministic():
     """Two calls give bitwise equal gradients: the sums over channel tiles and
     batch rows run in a fixed order."""
