@@ -450,6 +450,37 @@ def test_ssd_decode_steps(P, N, G, has_z):
     assert rel_err(state.cpu(), hr) <= TOL_BF16
 
 
+def test_decode_steps_at_bench_state_sizes():
+    """One step of each decode call on the state sizes the bench times: the
+    scan step on (4, 5120, 16) bf16 with a gate, the SSD step on
+    (32, 32 heads, 64, 128) bf16; whole outputs and states against the oracle."""
+    g = torch.Generator().manual_seed(5990)
+    rnd = lambda *sh: torch.randn(*sh, generator=g).to(torch.bfloat16)
+    pos = lambda *sh: (torch.rand(*sh, generator=g) * 0.1 + 1e-3).to(torch.bfloat16)
+    b, d, n = 4, 5120, 16
+    u, dl, z, Bm, Cm = rnd(b, d), pos(b, d), rnd(b, d), rnd(b, 1, n), rnd(b, 1, n)
+    A = -torch.rand(d, n, generator=g) - 0.5
+    D = torch.randn(d, generator=g)
+    S = make_state((b, d, n), seed=5991)
+    state = S.cuda().clone()
+    y = ssm.scan_step(_dev(u), _dev(dl), _dev(A), _dev(Bm), _dev(Cm), _dev(D), _dev(z), state=state)
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_step(u, dl, A, Bm, Cm, D, z, state=S)
+    assert rel_err(y.float().cpu(), yr) <= TOL_BF16
+    assert rel_err(state.cpu(), hr) <= TOL_BF16
+    b, H, P, n = 32, 32, 64, 128
+    x, dt, Bm, Cm = rnd(b, H, P), pos(b, H), rnd(b, 1, n), rnd(b, 1, n)
+    Ah = -torch.rand(H, generator=g) - 0.5
+    Dh = torch.ones(H)
+    S = make_state((b, H, P, n), seed=5992, scale=0.1)
+    state = S.cuda().clone()
+    y = ssm.ssd_step(_dev(x), _dev(dt), _dev(Ah), _dev(Bm), _dev(Cm), _dev(Dh), None, state=state)
+    torch.cuda.synchronize()
+    yr, hr = oracle.ssd_step(x, dt, Ah, Bm, Cm, Dh, None, state=S)
+    assert rel_err(y.float().cpu(), yr) <= TOL_BF16
+    assert rel_err(state.cpu(), hr) <= TOL_BF16
+
+
 def test_ssd_prefill_then_128_decode_steps():
     """A 64-token chunked prefill leaves its state in a cache; 128 decode steps
     continue from it in place.  Every step's y and the final state match one
