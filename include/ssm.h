@@ -51,6 +51,20 @@ typedef enum {
   SSM_ERR_HIP = -7          /* a HIP launch failed                           */
 } ssm_status_t;
 
+/*
+ * dims.flags bits; every other bit must be 0.
+ *   SSM_DT_SOFTPLUS: the delta (dt) argument holds raw values and every kernel
+ *     steps with softplus(delta + dt_bias), softplus(v) = log(1 + exp(v)),
+ *     dt_bias being the per-channel (per-head) float32 vector named in the
+ *     dims (zero when NULL; it must be NULL without this flag).  Steps past
+ *     the end of a sequence still count as zero steps.
+ *     [Mamba-3 NKI], "How it works", Phase 0: dt_softplus = softplus(dt + dt_bias).
+ *   SSM_LAM_SIGMOID (ssd_trap_chunked_fwd only): lam holds raw values and the
+ *     recurrence uses sigmoid(lam) = 1 / (1 + exp(-lam)).
+ *     [Mamba-3 NKI], "How it works", Phase 0: lam_sigmoid = sigmoid(lam).
+ */
+enum { SSM_DT_SOFTPLUS = 1, SSM_LAM_SIGMOID = 2 };
+
 /* ------------------------------------------------------------------------ */
 /* Selective scan                                                            */
 /* ------------------------------------------------------------------------ */
@@ -65,9 +79,10 @@ typedef enum {
  *              k > 1 = split L into chunks of len = 32 * ceil(ceil(L / k) / 32)
  *              steps (ceil(L / len) <= k chunks) that run in parallel, joined
  *              by the (decay product, state) carry.
- *   flags    : reserved, must be 0.
+ *   flags    : 0 or SSM_DT_SOFTPLUS.
  *   workspace, workspace_bytes: caller-owned device scratch of at least
  *              ssm_scan_workspace_size() bytes (may be NULL when that is 0).
+ *   dt_bias  : (dim) float32, nullable; read only with SSM_DT_SOFTPLUS.
  * Supported: dstate in {1, 2, 4, 8, 16, 32, 64}; any batch, dim, seqlen >= 0.
  */
 typedef struct {
@@ -77,6 +92,7 @@ typedef struct {
   int32_t flags;
   void *workspace;
   size_t workspace_bytes;
+  const float *dt_bias;
 } ssm_scan_dims_t;
 
 /*
@@ -171,6 +187,10 @@ SSM_API int ssm_scan_bwd_workspace_size(const ssm_scan_dims_t *dims, size_t *byt
  * over channels (dB, dC) and over batch rows (dA, dD) are formed per channel
  * tile or batch row in the workspace and then added in a fixed order, so every
  * output is deterministic.  Supported sizes are those of ssm_scan_fwd.
+ * With SSM_DT_SOFTPLUS the recurrence runs on softplus(delta + dt_bias) and
+ * ddelta is the gradient with respect to the raw delta (the softplus chain
+ * applied, i.e. times sigmoid(delta + dt_bias)); the gradient of dt_bias is
+ * the sum of ddelta over batch and steps.
  */
 SSM_API int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
                  const void *C, const float *D, const void *z, const float *h0, const void *dy,
@@ -187,7 +207,8 @@ SSM_API int ssm_scan_bwd(const void *u, const void *delta, const float *A, const
  *   divides H, head h reads group h / (H / G)), chunk (Q).
  *   in_dtype must be SSM_BF16 (the intra-chunk contractions run on bf16
  *   matrix cores with float32 accumulation); out_dtype is SSM_BF16 or SSM_F32.
- *   flags: reserved, must be 0.
+ *   flags: 0, SSM_DT_SOFTPLUS, and (ssd_trap_chunked_fwd) SSM_LAM_SIGMOID.
+ *   dt_bias: (nheads) float32, nullable; read only with SSM_DT_SOFTPLUS.
  * Supported: headdim = 64, dstate in {64, 128}, chunk = 64, any seqlen >= 0
  * (a ragged last chunk is masked).
  * Alignment: x, z, B, C, h0 and h_last must be 16-byte aligned (they are read
@@ -200,6 +221,7 @@ typedef struct {
   int32_t reserved;
   void *workspace;
   size_t workspace_bytes;
+  const float *dt_bias;
 } ssd_dims_t;
 
 /* Workspace the SSD needs for `dims` (currently always 0). */
@@ -272,13 +294,15 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
 /*
  * Sizes of one selective-scan decode step.
  *   batch, dim (channels), dstate (N), ngroups (G divides dim);
- *   in_dtype: u, delta, B, C, z; out_dtype: y.  flags, reserved: must be 0.
+ *   in_dtype: u, delta, B, C, z; out_dtype: y.  flags: 0 or SSM_DT_SOFTPLUS
+ *   (dt_bias: (dim) float32, nullable); reserved: must be 0.
  * Supported: dstate a power of two up to 256; any batch, dim >= 0.
  */
 typedef struct {
   int64_t batch, dim, dstate, ngroups;
   int32_t in_dtype, out_dtype;
   int32_t flags, reserved;
+  const float *dt_bias;
 } ssm_step_dims_t;
 
 /*
@@ -303,13 +327,15 @@ SSM_API int ssm_scan_step(const void *u, const void *delta, const float *A, cons
 
 /*
  * Sizes of one SSD decode step: batch, nheads (H), headdim (P), dstate (N),
- * ngroups (G divides H); in_dtype: x, dt, B, C, z; out_dtype: y.
+ * ngroups (G divides H); in_dtype: x, dt, B, C, z; out_dtype: y; flags: 0 or
+ * SSM_DT_SOFTPLUS (dt_bias: (nheads) float32, nullable); reserved: must be 0.
  * Supported: any headdim >= 1, dstate a power of two up to 256.
  */
 typedef struct {
   int64_t batch, nheads, headdim, dstate, ngroups;
   int32_t in_dtype, out_dtype;
   int32_t flags, reserved;
+  const float *dt_bias;
 } ssd_step_dims_t;
 
 /*

@@ -44,7 +44,37 @@ class Oracle:
         lib.oracle_scan_bwd_f64.argtypes = [i64] * 5 + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.restype = ctypes.c_int
+        lib.oracle_softplus_f64.argtypes = [i64] * 3 + [dp] * 3
+        lib.oracle_softplus_f64.restype = None
+        lib.oracle_softplus_grad_f64.argtypes = [i64] * 3 + [dp] * 4
+        lib.oracle_softplus_grad_f64.restype = None
+        lib.oracle_sigmoid_f64.argtypes = [i64] + [dp] * 2
+        lib.oracle_sigmoid_f64.restype = None
         self.lib = lib
+
+    def softplus(self, raw, bias, inner):
+        """Phase-0 step: softplus(raw + bias[(i / inner) % len(bias)]) elementwise
+        over the flattened raw array (bias None: 0)."""
+        raw, bias = f64(raw), f64(bias)
+        out = np.empty_like(raw)
+        nb = 1 if bias is None else bias.size
+        self.lib.oracle_softplus_f64(raw.size, inner, nb, _ptr(raw), _ptr(bias), _ptr(out))
+        return out
+
+    def softplus_grad(self, raw, bias, inner, grad):
+        """grad * sigmoid(raw + bias), the chain rule through ``softplus``."""
+        raw, bias, grad = f64(raw), f64(bias), f64(grad)
+        out = np.empty_like(raw)
+        nb = 1 if bias is None else bias.size
+        self.lib.oracle_softplus_grad_f64(raw.size, inner, nb, _ptr(raw), _ptr(bias), _ptr(grad), _ptr(out))
+        return out
+
+    def sigmoid(self, raw):
+        """Phase-0 trapezoid weight: 1 / (1 + exp(-raw)) elementwise."""
+        raw = f64(raw)
+        out = np.empty_like(raw)
+        self.lib.oracle_sigmoid_f64(raw.size, _ptr(raw), _ptr(out))
+        return out
 
     def scan(self, u, delta, A, B, C, D=None, z=None, h0=None):
         """Selective scan in float64. Returns (y, h_last) as float64 arrays.
@@ -156,40 +186,66 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def scan(u, delta, A, B, C, D=None, z=None, h0=None):
-    """Selective scan in float64 with the default build; see ``Oracle.scan``."""
-    return _load().scan(u, delta, A, B, C, D, z, h0)
+def scan(u, delta, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None):
+    """Selective scan in float64 with the default build; see ``Oracle.scan``.
+    dt_softplus: delta holds raw values and the step is softplus(delta +
+    dt_bias[d]) (the Phase-0 map; dt_bias (dim,) or None)."""
+    o = _load()
+    if dt_softplus:
+        delta = o.softplus(delta, dt_bias, f64(u).shape[2]).reshape(f64(u).shape)
+    return o.scan(u, delta, A, B, C, D, z, h0)
 
 
-def scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
-    """Selective-scan gradients in float64 with the default build; see ``Oracle.scan_bwd``."""
-    return _load().scan_bwd(u, delta, A, B, C, D, z, h0, dy, dh_last)
+def scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, dt_softplus=False,
+             dt_bias=None):
+    """Selective-scan gradients in float64 with the default build; see
+    ``Oracle.scan_bwd``.  With dt_softplus the forward steps with
+    softplus(delta + dt_bias) and ddelta is the gradient of the raw delta."""
+    o = _load()
+    if not dt_softplus:
+        return o.scan_bwd(u, delta, A, B, C, D, z, h0, dy, dh_last)
+    L = f64(u).shape[2]
+    step = o.softplus(delta, dt_bias, L).reshape(f64(u).shape)
+    g = o.scan_bwd(u, step, A, B, C, D, z, h0, dy, dh_last)
+    g["ddelta"] = o.softplus_grad(delta, dt_bias, L, g["ddelta"]).reshape(step.shape)
+    return g
 
 
-def ssd_trap(x, dt, lam, A, B, C, D=None, z=None, h0=None):
-    """Trapezoidal SSD in float64 with the default build; see ``Oracle.ssd_trap``."""
-    return _load().ssd_trap(x, dt, lam, A, B, C, D, z, h0)
+def ssd_trap(x, dt, lam, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None,
+             lam_sigmoid=False):
+    """Trapezoidal SSD in float64 with the default build; see ``Oracle.ssd_trap``.
+    dt_softplus / lam_sigmoid: dt and lam hold raw values (Phase-0 maps)."""
+    o = _load()
+    if dt_softplus:
+        dt = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
+    if lam_sigmoid:
+        lam = o.sigmoid(lam).reshape(f64(lam).shape)
+    return o.ssd_trap(x, dt, lam, A, B, C, D, z, h0)
 
 
-def ssd(x, dt, A, B, C, D=None, z=None, h0=None):
-    """Scalar-decay SSD in float64 with the default build; see ``Oracle.ssd``."""
-    return _load().ssd(x, dt, A, B, C, D, z, h0)
+def ssd(x, dt, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None):
+    """Scalar-decay SSD in float64 with the default build; see ``Oracle.ssd``.
+    dt_softplus: dt holds raw values and the step is softplus(dt + dt_bias[h])."""
+    o = _load()
+    if dt_softplus:
+        dt = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
+    return o.ssd(x, dt, A, B, C, D, z, h0)
 
 
-def scan_step(u, delta, A, B, C, D=None, z=None, state=None):
+def scan_step(u, delta, A, B, C, D=None, z=None, state=None, dt_softplus=False, dt_bias=None):
     """One decode step of the selective scan: the recurrence at a single token
     from the cached ``state`` (zero when None), i.e. ``scan`` with seqlen 1 and
     h0 = state.  u, delta, z: (batch, dim); B, C: (batch, G, N);
     state: (batch, dim, N).  Returns (y (batch, dim), new state)."""
     col = lambda a: None if a is None else f64(a)[..., None]
-    y, h = scan(col(u), col(delta), A, col(B), col(C), D, col(z), state)
+    y, h = scan(col(u), col(delta), A, col(B), col(C), D, col(z), state, dt_softplus, dt_bias)
     return y[..., 0], h
 
 
-def ssd_step(x, dt, A, B, C, D=None, z=None, state=None):
+def ssd_step(x, dt, A, B, C, D=None, z=None, state=None, dt_softplus=False, dt_bias=None):
     """One decode step of the scalar-decay SSD: ``ssd`` with seqlen 1 and
     h0 = state.  x, z: (batch, H, P); dt: (batch, H); B, C: (batch, G, N);
     state: (batch, H, P, N).  Returns (y (batch, H, P), new state)."""
     row = lambda a: None if a is None else f64(a)[:, None]
-    y, h = ssd(row(x), row(dt), A, row(B), row(C), D, row(z), state)
+    y, h = ssd(row(x), row(dt), A, row(B), row(C), D, row(z), state, dt_softplus, dt_bias)
     return y[:, 0], h

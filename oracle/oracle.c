@@ -314,3 +314,39 @@ int oracle_ssd_trap_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
     }
     return 0;
 }
+
+/*
+ * Phase-0 maps of the raw step and trapezoid inputs ("Mamba-3 NKI Kernels for
+ * AWS Neuron", section "How it works", Phase 0: dt_softplus = softplus(dt +
+ * dt_bias), lam_sigmoid = sigmoid(lam)).
+ *
+ * For n raw values laid out with the biased index the slowest of `inner`
+ * consecutive elements and `nb` biases repeating: element i uses bias
+ * bias[(i / inner) % nb] (bias NULL: 0).
+ *   softplus(v) = log(1 + exp(v)), written as v + log1p(exp(-v)) for v > 0.
+ *   sigmoid(v)  = 1 / (1 + exp(-v)), the derivative of softplus.
+ */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+void oracle_softplus_f64(int64_t n, int64_t inner, int64_t nb, const double *raw, const double *bias,
+                         double *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double bv = bias ? bias[(i / inner) % nb] : 0.0;
+    out[i] = softplus(raw[i] + bv);
+  }
+}
+
+/* grad_out[i] = grad_in[i] * sigmoid(raw[i] + bias): the chain rule through
+ * softplus, from the gradient of the step to that of the raw value. */
+void oracle_softplus_grad_f64(int64_t n, int64_t inner, int64_t nb, const double *raw, const double *bias,
+                              const double *grad_in, double *grad_out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double bv = bias ? bias[(i / inner) % nb] : 0.0;
+    grad_out[i] = grad_in[i] * sigmoid(raw[i] + bv);
+  }
+}
+
+void oracle_sigmoid_f64(int64_t n, const double *raw, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = sigmoid(raw[i]);
+}

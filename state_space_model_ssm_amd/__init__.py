@@ -16,13 +16,14 @@ import os
 from typing import Optional
 
 __all__ = [
-    "SSM_F32", "SSM_BF16", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
+    "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
     "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
 
 SSM_F32, SSM_BF16 = 0, 1
+SSM_DT_SOFTPLUS, SSM_LAM_SIGMOID = 1, 2   # dims.flags bits (Phase-0 maps of dt and lam)
 STATUS = {0: "SSM_OK", -1: "SSM_ERR_NULL", -2: "SSM_ERR_SHAPE", -3: "SSM_ERR_DTYPE",
           -4: "SSM_ERR_ALIGN", -5: "SSM_ERR_UNSUPPORTED", -6: "SSM_ERR_WORKSPACE",
           -7: "SSM_ERR_HIP"}
@@ -43,7 +44,8 @@ class ScanDims(ctypes.Structure):
                 ("seqlen", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("n_chunks", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("dt_bias", ctypes.c_void_p)]
 
 
 class SsdDims(ctypes.Structure):
@@ -51,19 +53,21 @@ class SsdDims(ctypes.Structure):
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("dt_bias", ctypes.c_void_p)]
 
 
 class StepDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
                 ("ngroups", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32), ("dt_bias", ctypes.c_void_p)]
 
 
 class SsdStepDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("dt_bias", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -161,6 +165,18 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream or None
 
 
+def _phase0(dims, n: int, dt_softplus: bool, dt_bias, lam_sigmoid: bool = False):
+    """Set the Phase-0 flags of ``dims``: softplus(dt + dt_bias) as the step
+    (dt_bias: (n,) float32 or None) and sigmoid(lam) for the trapezoid."""
+    if dt_bias is not None:
+        if not dt_softplus:
+            raise ValueError("dt_bias is used only with dt_softplus=True")
+        if dt_bias.dtype != _torch().float32 or tuple(dt_bias.shape) != (n,):
+            raise ValueError(f"dt_bias must be float32 of shape ({n},)")
+    dims.flags = (SSM_DT_SOFTPLUS if dt_softplus else 0) | (SSM_LAM_SIGMOID if lam_sigmoid else 0)
+    dims.dt_bias = _ptr(dt_bias)
+
+
 def _scan_dims(u, B, in_dtype, out_dtype, n_chunks) -> ScanDims:
     batch, dim, L = u.shape
     G, N = B.shape[1], B.shape[2]
@@ -182,13 +198,16 @@ def scan_resolved_chunks(dims: ScanDims) -> int:
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_chunks: int = 0,
-             return_h_last: bool = True, y=None, h_last=None, workspace=None, stream=None):
+             return_h_last: bool = True, y=None, h_last=None, workspace=None, stream=None,
+             dt_softplus: bool = False, dt_bias=None):
     """Selective-scan forward (``ssm_scan_fwd``). Returns ``(y, h_last)``.
 
     u, delta, z: (batch, dim, L); A: (dim, N) float32; B, C: (batch, G, N, L);
     D: (dim,) float32; h0: (batch, dim, N) float32 initial state (zero when
     None).  u/delta/B/C/z share one dtype (float32 or bfloat16); y defaults to
     that dtype, h_last is float32 (batch, dim, N) and may be h0 itself.
+    dt_softplus: delta is raw and the step is softplus(delta + dt_bias)
+    (dt_bias: (dim,) float32 or None).
     """
     torch = _torch()
     in_code = _dtype_code(u.dtype)
@@ -211,6 +230,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_ch
     if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, dim, N)):
         raise ValueError("h0 must be float32 (batch, dim, dstate)")
     dims = _scan_dims(u, B, in_code, out_code, n_chunks)
+    _phase0(dims, dim, dt_softplus, dt_bias)
     need = scan_workspace_size(dims)
     if y is None:
         y = torch.empty((batch, dim, L), dtype=out_dt, device=u.device)
@@ -233,12 +253,14 @@ def scan_bwd_workspace_size(dims: ScanDims) -> int:
     return n.value
 
 
-def scan_bwd(u, delta, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, workspace=None, stream=None):
+def scan_bwd(u, delta, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, workspace=None, stream=None,
+             dt_softplus: bool = False, dt_bias=None):
     """Selective-scan backward (``ssm_scan_bwd``): gradients of a loss with
     upstream gradients dy (shaped like y, in y's dtype) and dh_last (float32,
     optional).  Returns a dict du, ddelta (u's dtype), dA, dB, dC (float32),
     dD (float32, when D is given), dz (u's dtype, when z is given) and dh0
-    (float32)."""
+    (float32).  With dt_softplus, ddelta is the gradient of the raw delta
+    (that of dt_bias is its sum over batch and steps)."""
     torch = _torch()
     in_code = _dtype_code(u.dtype)
     out_code = _dtype_code(dy.dtype)
@@ -249,6 +271,7 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, wo
     if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, dim, N)):
         raise ValueError("h0 must be float32 (batch, dim, dstate)")
     dims = _scan_dims(u, B, in_code, out_code, 0)
+    _phase0(dims, dim, dt_softplus, dt_bias)
     need = scan_bwd_workspace_size(dims)
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -285,7 +308,8 @@ def ssd_workspace_size(dims: SsdDims) -> int:
 
 
 def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
-                    return_h_last: bool = True, y=None, h_last=None, stream=None):
+                    return_h_last: bool = True, y=None, h_last=None, stream=None,
+                    dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False):
     """Scalar-decay chunked SSD forward, plain (lam None: ``ssd_chunked_fwd``)
     or trapezoidal (``ssd_trap_chunked_fwd``). Returns ``(y, h_last)``.
 
@@ -316,6 +340,7 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
     if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, H, P, N)):
         raise ValueError("h0 must be float32 (batch, nheads, headdim, dstate)")
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
+    _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
     if y is None:
         y = torch.empty((batch, L, H, P), dtype=out_dt, device=x.device)
     if h_last is None and return_h_last:
@@ -337,19 +362,22 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, **kw):
     x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
     B, C: (batch, L, G, N) bf16; h0: (batch, H, P, N) float32 initial state
     (zero when None).  h_last is float32 (batch, H, P, N) and may be h0 itself.
-    Keywords: h0, chunk, out_dtype, return_h_last, y, h_last, stream.
+    Keywords: h0, chunk, out_dtype, return_h_last, y, h_last, stream,
+    dt_softplus (dt is raw, the step is softplus(dt + dt_bias)), dt_bias
+    ((H,) float32).
     """
     return _ssd_call(x, dt, None, A, B, C, D, z, **kw)
 
 
 def ssd_trap_chunked_fwd(x, dt, lam, A, B, C, D=None, z=None, **kw):
     """Trapezoidal (Mamba-3 SISO) chunked SSD (``ssd_trap_chunked_fwd``):
-    lam (batch, L, H) bf16 in [0, 1] (after its sigmoid).  Otherwise as
-    ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
+    lam (batch, L, H) bf16 in [0, 1] (after its sigmoid; raw with
+    lam_sigmoid=True).  Otherwise as ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
     return _ssd_call(x, dt, lam, A, B, C, D, z, **kw)
 
 
-def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None):
+def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None,
+              dt_softplus: bool = False, dt_bias=None):
     """One selective-scan decode step (``ssm_scan_step``); ``state`` is updated
     in place.  Returns y.
 
@@ -375,12 +403,14 @@ def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=Non
         y = torch.empty((batch, dim), dtype=out_dt, device=u.device)
     dims = StepDims(batch=batch, dim=dim, dstate=N, ngroups=G, in_dtype=in_code, out_dtype=out_code,
                     flags=0, reserved=0)
+    _phase0(dims, dim, dt_softplus, dt_bias)
     _check(lib().ssm_scan_step(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
     return y
 
 
-def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None):
+def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None,
+             dt_softplus: bool = False, dt_bias=None):
     """One scalar-decay SSD decode step (``ssd_step``); ``state`` is updated in
     place.  Returns y.
 
@@ -406,6 +436,7 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, s
         y = torch.empty((batch, H, P), dtype=out_dt, device=x.device)
     dims = SsdStepDims(batch=batch, nheads=H, headdim=P, dstate=N, ngroups=G, in_dtype=in_code,
                        out_dtype=out_code, flags=0, reserved=0)
+    _phase0(dims, H, dt_softplus, dt_bias)
     _check(lib().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                           _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
     return y

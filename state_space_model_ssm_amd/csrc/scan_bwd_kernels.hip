@@ -122,6 +122,13 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
   const float a_n = mine ? p.A[d * N + n] : 0.0f;
   const float a2 = a_n * kLog2e;
 
+  // Step size of a staged raw delta of channel row r (softplus(delta + bias)
+  // with SSM_DT_SOFTPLUS).
+  auto step_of = [&](float raw, int r) __attribute__((always_inline)) {
+    if (!p.dt_softplus) return raw;
+    const float bias = p.dt_bias != nullptr ? p.dt_bias[d0 + min(r, nvalid - 1)] : 0.0f;
+    return dt_softplus(raw + bias);
+  };
   float lam = (mine && p.dh_last != nullptr) ? p.dh_last[(b * p.dim + d) * N + n] : 0.0f;
   float dA_acc = 0.0f;
   float dD_acc[(Cfg::PAIRS_CT + 255) / 256];
@@ -172,7 +179,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
       if (Cfg::PAIRS_CT % 256 != 0 && e >= Cfg::PAIRS_CT) continue;
       const int r = e / kT, t = e % kT;
       const bool in = t0 + t < L;
-      sDl[r * TP + t] = in ? ld(R.dl + k, 0) : 0.0f;
+      sDl[r * TP + t] = in ? step_of(ld(R.dl + k, 0), r) : 0.0f;
       sU[r * TP + t] = in ? ld(R.u + k, 0) : 0.0f;
       sDy[r * TP + t] = (in && r < nvalid) ? ld(R.dy + k, 0) : 0.0f;
       if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(R.z + k, 0) : 0.0f;
@@ -205,7 +212,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
         const int r = e / kT, t = e % kT;
         const int64_t row = (b * p.dim + d0 + min(r, nvalid - 1)) * L;
         const bool in = t0 + t < L;
-        sDl[r * TP + t] = in ? ld(gdl, row + t0 + t) : 0.0f;
+        sDl[r * TP + t] = in ? step_of(ld(gdl, row + t0 + t), r) : 0.0f;
         sU[r * TP + t] = in ? ld(gu, row + t0 + t) : 0.0f;
         sDy[r * TP + t] = (in && r < nvalid) ? ld(gdy, row + t0 + t) : 0.0f;
         if constexpr (HAS_Z) sZ[r * TP + t] = in ? ld(gz, row + t0 + t) : 0.0f;
@@ -321,7 +328,10 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
               const float dskip = p.D != nullptr ? p.D[d0 + r] : 0.0f;
               st(static_cast<Tin *>(p.du), o, fmaf(sDy[r * TP + t], dskip, s));
             } else {
-              st(static_cast<Tin *>(p.ddelta), o, s);
+              // With the softplus step map, d(step)/d(raw delta) =
+              // sigmoid(raw + bias) = 1 - exp(-step).
+              const float g = p.dt_softplus ? -expm1f(-sDl[r * TP + t]) : 1.0f;
+              st(static_cast<Tin *>(p.ddelta), o, s * g);
             }
           }
         }

@@ -310,7 +310,7 @@ scan_chunk_kernel(const ScanParams p) {
   int jkind[JPT], jrow[JPT], jcol[JPT];
   bool jon[JPT];
   int64_t jbase[JPT];
-  float jdsk[JPT];
+  float jdsk[JPT], jbias[JPT];
 #pragma unroll
   for (int k = 0; k < JPT; ++k) {
     int job = tid + 256 * k;
@@ -329,11 +329,13 @@ scan_chunk_kernel(const ScanParams p) {
       const int r = min(jrow[k], nvalid - 1);
       jbase[k] = (b * p.dim + d0 + r) * L;
       jdsk[k] = (jrow[k] < nvalid && p.D != nullptr) ? p.D[d0 + jrow[k]] : 0.0f;
+      jbias[k] = p.dt_bias != nullptr ? p.dt_bias[d0 + r] : 0.0f;
       jsrc1[k] = gdl;
       jsrc2[k] = gu;
     } else {
       jbase[k] = ((b * p.ngroups + g) * N + jrow[k]) * L;
       jdsk[k] = 0.0f;
+      jbias[k] = 0.0f;
       jsrc1[k] = gB;
       jsrc2[k] = gC;
     }
@@ -401,7 +403,7 @@ scan_chunk_kernel(const ScanParams p) {
     }
   };
 
-  auto stage = [&](const Regs &R, int par) __attribute__((always_inline)) {
+  auto stage = [&](const Regs &R, int par, int64_t t0) __attribute__((always_inline)) {
     static_assert(VEC % 4 == 0 || VEC == 2, "staging store width");
 #pragma unroll
     for (int k = 0; k < JPT; ++k) {
@@ -411,6 +413,13 @@ scan_chunk_kernel(const ScanParams p) {
       unpack(R.b[k].v, WORDS, vb, gu);
       const int o = jrow[k] * TP + jcol[k];
       if (jkind[k] == 0) {
+        if (p.dt_softplus) {
+          // The raw step: softplus(delta + bias) inside the sequence; padded
+          // steps past its end stay zero steps.
+#pragma unroll
+          for (int i = 0; i < VEC; ++i)
+            va[i] = t0 + jcol[k] + i < t_end ? dt_softplus(va[i] + jbias[k]) : 0.0f;
+        }
         const int ob = par * CH * TP + o;
         float vw[VEC], vd[VEC];
 #pragma unroll
@@ -553,7 +562,7 @@ scan_chunk_kernel(const ScanParams p) {
 #pragma unroll
     for (int e = 0; e < NB * OPL; ++e) zz[e] = R.z[e];
     const int par = ti & 1;
-    stage(R, par);
+    stage(R, par, t0);
     __syncthreads();
     if (pf && ti + DEPTH < nfast) prefetch_fast(R, ti + DEPTH);
     if constexpr (SUMMARY) {

@@ -151,6 +151,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   const int64_t L = p.seqlen, H = p.nheads, G = p.ngroups;
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.0f;
+  // Phase-0 maps of the raw inputs when asked for: the step softplus(dt +
+  // dt_bias[h]) and the trapezoid weight sigmoid(lam).
+  const float dt_bias = (p.dt_softplus && p.dt_bias != nullptr) ? p.dt_bias[h] : 0.0f;
+  auto step_of = [&](float raw) __attribute__((always_inline)) {
+    return p.dt_softplus ? dt_softplus(raw + dt_bias) : raw;
+  };
+  auto lam_of = [&](float raw) __attribute__((always_inline)) {
+    return p.lam_sigmoid ? 1.0f / (1.0f + expf(-raw)) : raw;
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
@@ -260,7 +269,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
     put_t(sXt32, (tid % (P / 8)) * 8, tid / (P / 8), R.xv[0], R.xv[1], std::integral_constant<int, P>{});
     // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
     if (wave == 0) {
-      const float dtv = (c0 + lane < L) ? bf2f(static_cast<uint16_t>(R.dt)) : 0.0f;
+      const float dtv = (c0 + lane < L) ? step_of(bf2f(static_cast<uint16_t>(R.dt))) : 0.0f;
       // Inclusive prefix sum over the 64 lanes: within each 16-lane row by
       // DPP row shifts (lanes shifted in from outside the row read 0), then
       // the totals of the rows below, read from lanes 15, 31 and 47.
@@ -276,10 +285,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       if constexpr (TRAP) {
         // Weight of this step's input wherever it reaches a later step; the
         // step after the sequence has dt = 0, so the last step keeps gamma.
-        const float gam = (c0 + lane < L) ? bf2f(static_cast<uint16_t>(R.lam)) * dtv : 0.0f;
+        const float gam = (c0 + lane < L) ? lam_of(bf2f(static_cast<uint16_t>(R.lam))) * dtv : 0.0f;
         const bool nx = c0 + lane + 1 < L;
-        const float dtn = nx ? bf2f(static_cast<uint16_t>(R.dtn)) : 0.0f;
-        const float lamn = nx ? bf2f(static_cast<uint16_t>(R.lamn)) : 0.0f;
+        const float dtn = nx ? step_of(bf2f(static_cast<uint16_t>(R.dtn))) : 0.0f;
+        const float lamn = nx ? lam_of(bf2f(static_cast<uint16_t>(R.lamn))) : 0.0f;
         w = gam + dtn * (1.0f - lamn);
         sGam[lane] = gam;
       }

@@ -55,8 +55,18 @@ bool overlap(Span a, Span b) {
 // Selective scan
 // ---------------------------------------------------------------------------
 
+// dims.flags may hold only `allowed` bits; dt_bias needs SSM_DT_SOFTPLUS.
+int check_dt_flags(int32_t flags, int32_t allowed, const float *dt_bias) {
+  if ((flags & ~allowed) != 0) return fail(SSM_ERR_SHAPE, "flags 0x%x: unknown or unsupported bits", flags);
+  if (dt_bias != nullptr && !(flags & SSM_DT_SOFTPLUS))
+    return fail(SSM_ERR_SHAPE, "dt_bias is read only with SSM_DT_SOFTPLUS");
+  if (!aligned(dt_bias, 4)) return fail(SSM_ERR_ALIGN, "dt_bias must be 4-byte aligned");
+  return SSM_OK;
+}
+
 int check_scan_dims(const ssm_scan_dims_t *d) {
   if (!d) return fail(SSM_ERR_NULL, "dims is NULL");
+  int rc0 = SSM_OK;
   if (d->batch < 0 || d->dim < 0 || d->seqlen < 0)
     return fail(SSM_ERR_SHAPE, "negative size (batch=%lld dim=%lld seqlen=%lld)",
                 (long long)d->batch, (long long)d->dim, (long long)d->seqlen);
@@ -67,7 +77,8 @@ int check_scan_dims(const ssm_scan_dims_t *d) {
                 (long long)d->dim);
   if (!valid_dtype(d->in_dtype)) return fail(SSM_ERR_DTYPE, "in_dtype %d is not an ssm_dtype_t", d->in_dtype);
   if (!valid_dtype(d->out_dtype)) return fail(SSM_ERR_DTYPE, "out_dtype %d is not an ssm_dtype_t", d->out_dtype);
-  if (d->flags != 0) return fail(SSM_ERR_SHAPE, "flags must be 0 (got %d)", d->flags);
+  rc0 = check_dt_flags(d->flags, SSM_DT_SOFTPLUS, d->dt_bias);
+  if (rc0 != SSM_OK) return rc0;
   if (d->n_chunks < 0 || d->n_chunks > kMaxChunks)
     return fail(SSM_ERR_SHAPE, "n_chunks must be in [0, %d] (got %d)", kMaxChunks, d->n_chunks);
   const int64_t N = d->dstate;
@@ -161,7 +172,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   int64_t chunk_len = 1;
   const int32_t chunks = resolve_chunks(&d, &chunk_len);
   const Span ins[] = {{u, n_bdl * ei}, {delta, n_bdl * ei}, {z, n_bdl * ei}, {B, n_bc * ei},
-                      {C, n_bc * ei},  {A, n_a * 4ull},    {D, d.dim * 4ull}};
+                      {C, n_bc * ei},  {A, n_a * 4ull},    {D, d.dim * 4ull}, {d.dt_bias, d.dim * 4ull}};
   const Span sy{y, n_bdl * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
@@ -196,6 +207,8 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   p.h0 = h0;
   p.y = y;
   p.h_last = h_last;
+  p.dt_bias = d.dt_bias;
+  p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
   p.carry = static_cast<float *>(need > 0 ? d.workspace : nullptr);
   p.batch = d.batch;
   p.dim = d.dim;
@@ -276,7 +289,7 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
     return fail(SSM_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
   const Span ins[] = {{u, n_bdl * ei},  {delta, n_bdl * ei}, {z, n_bdl * ei},   {B, n_bc * ei},
                       {C, n_bc * ei},   {A, n_a * 4ull},     {D, d.dim * 4ull}, {h0, n_h * 4ull},
-                      {dy, n_bdl * eo}, {dh_last, n_h * 4ull}};
+                      {dy, n_bdl * eo}, {dh_last, n_h * 4ull}, {d.dt_bias, d.dim * 4ull}};
   const Span outs[] = {{du, n_bdl * ei}, {ddelta, n_bdl * ei}, {dz, n_bdl * ei},  {dA, n_a * 4ull},
                        {dB, n_bc * 4ull}, {dC, n_bc * 4ull},    {dD, d.dim * 4ull}, {dh0, n_h * 4ull}};
   for (const Span &o : outs) {
@@ -308,6 +321,8 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
   f.C = C;
   f.A = A;
   f.h0 = h0;
+  f.dt_bias = d.dt_bias;
+  f.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
   f.carry = static_cast<float *>(d.workspace);
   f.batch = d.batch;
   f.dim = d.dim;
@@ -341,6 +356,8 @@ int ssm_scan_bwd(const void *u, const void *delta, const float *A, const void *B
   p.dC = dC;
   p.dD = dD;
   p.dh0 = dh0;
+  p.dt_bias = d.dt_bias;
+  p.dt_softplus = f.dt_softplus;
   p.ckpt = static_cast<const float *>(d.workspace);
   const BwdWorkspace wl = scan_bwd_layout(&d);
   float *ws = static_cast<float *>(d.workspace);
@@ -377,7 +394,9 @@ static int check_ssd_dims(const ssd_dims_t *d) {
                 (long long)d->nheads);
   if (!valid_dtype(d->in_dtype)) return fail(SSM_ERR_DTYPE, "in_dtype %d is not an ssm_dtype_t", d->in_dtype);
   if (!valid_dtype(d->out_dtype)) return fail(SSM_ERR_DTYPE, "out_dtype %d is not an ssm_dtype_t", d->out_dtype);
-  if (d->flags != 0 || d->reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (d->reserved != 0) return fail(SSM_ERR_SHAPE, "reserved must be 0");
+  const int rc0 = check_dt_flags(d->flags, SSM_DT_SOFTPLUS | SSM_LAM_SIGMOID, d->dt_bias);
+  if (rc0 != SSM_OK) return rc0;
   if (d->in_dtype != SSM_BF16)
     return fail(SSM_ERR_UNSUPPORTED, "ssd_chunked_fwd takes bf16 inputs only (matrix-core operands)");
   if (d->headdim != 64) return fail(SSM_ERR_UNSUPPORTED, "headdim %lld not supported (64)", (long long)d->headdim);
@@ -414,13 +433,16 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
   if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16))
     return fail(SSM_ERR_ALIGN, "x, z, B and C must be 16-byte aligned");
   if (trap && n_dt > 0 && !lam) return fail(SSM_ERR_NULL, "lam is required");
+  if (!trap && (d.flags & SSM_LAM_SIGMOID))
+    return fail(SSM_ERR_SHAPE, "SSM_LAM_SIGMOID applies to ssd_trap_chunked_fwd only");
   if (!aligned(dt, 2) || !aligned(lam, 2)) return fail(SSM_ERR_ALIGN, "dt and lam must be 2-byte aligned");
   if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
   if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
   if (!aligned(h0, 16) || !aligned(h_last, 16))
     return fail(SSM_ERR_ALIGN, "h0 and h_last must be 16-byte aligned");
-  const Span ins[] = {{x, n_x * 2ull}, {dt, n_dt * 2ull}, {z, n_x * 2ull}, {B, n_bc * 2ull},
-                      {C, n_bc * 2ull}, {A, d.nheads * 4ull}, {D, d.nheads * 4ull}, {lam, n_dt * 2ull}};
+  const Span ins[] = {{x, n_x * 2ull},  {dt, n_dt * 2ull},     {z, n_x * 2ull},
+                      {B, n_bc * 2ull}, {C, n_bc * 2ull},     {A, d.nheads * 4ull},
+                      {D, d.nheads * 4ull}, {lam, n_dt * 2ull}, {d.dt_bias, d.nheads * 4ull}};
   const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
@@ -443,6 +465,9 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
   p.h0 = h0;
   p.y = y;
   p.h_last = h_last;
+  p.dt_bias = d.dt_bias;
+  p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.lam_sigmoid = (d.flags & SSM_LAM_SIGMOID) ? 1 : 0;
   p.batch = d.batch;
   p.seqlen = d.seqlen;
   p.nheads = d.nheads;
@@ -480,7 +505,8 @@ static bool step_dstate_ok(int64_t n) {
 static int step_common(const void *u, const void *delta, const float *A, const void *B, const void *C,
                        const float *D, const void *z, float *state, void *y, int64_t batch, int64_t chan,
                        int64_t dstate, int64_t ngroups, int64_t headdim, int64_t n_a, int64_t n_dt,
-                       int64_t n_d, int32_t in_dtype, int32_t out_dtype, int per_head, void *stream) {
+                       int64_t n_d, int32_t in_dtype, int32_t out_dtype, int per_head, int32_t flags,
+                       const float *dt_bias, void *stream) {
   const int64_t n_x = batch * chan;
   const int64_t n_bc = batch * ngroups * dstate;
   const int64_t n_h = n_x * dstate;
@@ -495,7 +521,7 @@ static int step_common(const void *u, const void *delta, const float *A, const v
   if (!aligned(state, dstate >= 4 ? 16 : 4))
     return fail(SSM_ERR_ALIGN, "state must be %d-byte aligned", dstate >= 4 ? 16 : 4);
   const Span ins[] = {{u, n_x * ei}, {delta, n_dt * ei}, {z, n_x * ei}, {B, n_bc * ei},
-                      {C, n_bc * ei}, {A, n_a * 4ull},  {D, n_d * 4ull}};
+                      {C, n_bc * ei}, {A, n_a * 4ull},  {D, n_d * 4ull}, {dt_bias, n_d * 4ull}};
   const Span sy{y, n_x * eo}, ss{state, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, ss)) return fail(SSM_ERR_SHAPE, "y or the state overlaps an input");
@@ -515,6 +541,8 @@ static int step_common(const void *u, const void *delta, const float *A, const v
   p.D = D;
   p.state = state;
   p.y = y;
+  p.dt_bias = dt_bias;
+  p.dt_softplus = (flags & SSM_DT_SOFTPLUS) ? 1 : 0;
   p.batch = batch;
   p.dim = chan;
   p.ngroups = ngroups;
@@ -535,11 +563,14 @@ int ssm_scan_step(const void *u, const void *delta, const float *A, const void *
   if (d.dstate < 1 || d.ngroups < 1) return fail(SSM_ERR_SHAPE, "dstate and ngroups must be >= 1");
   if (d.dim % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide dim");
   if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
-  if (d.flags != 0 || d.reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (d.reserved != 0) return fail(SSM_ERR_SHAPE, "reserved must be 0");
+  const int rc = check_dt_flags(d.flags, SSM_DT_SOFTPLUS, d.dt_bias);
+  if (rc != SSM_OK) return rc;
   if (!step_dstate_ok(d.dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two up to 256)", (long long)d.dstate);
   return step_common(u, delta, A, B, C, D, z, state, y, d.batch, d.dim, d.dstate, d.ngroups, 1,
-                     d.dim * d.dstate, d.batch * d.dim, d.dim, d.in_dtype, d.out_dtype, 0, stream);
+                     d.dim * d.dstate, d.batch * d.dim, d.dim, d.in_dtype, d.out_dtype, 0, d.flags, d.dt_bias,
+                     stream);
 }
 
 int ssd_step(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
@@ -551,12 +582,15 @@ int ssd_step(const void *x, const void *dt, const float *A, const void *B, const
     return fail(SSM_ERR_SHAPE, "headdim, dstate and ngroups must be >= 1");
   if (d.nheads % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide nheads");
   if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
-  if (d.flags != 0 || d.reserved != 0) return fail(SSM_ERR_SHAPE, "flags and reserved must be 0");
+  if (d.reserved != 0) return fail(SSM_ERR_SHAPE, "reserved must be 0");
+  const int rc = check_dt_flags(d.flags, SSM_DT_SOFTPLUS, d.dt_bias);
+  if (rc != SSM_OK) return rc;
   if (!step_dstate_ok(d.dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two up to 256)", (long long)d.dstate);
   if (d.nheads > 0 && d.headdim > kMaxGridX / d.nheads) return fail(SSM_ERR_UNSUPPORTED, "too many channels");
   return step_common(x, dt, A, B, C, D, z, state, y, d.batch, d.nheads * d.headdim, d.dstate, d.ngroups,
-                     d.headdim, d.nheads, d.batch * d.nheads, d.nheads, d.in_dtype, d.out_dtype, 1, stream);
+                     d.headdim, d.nheads, d.batch * d.nheads, d.nheads, d.in_dtype, d.out_dtype, 1, d.flags,
+                     d.dt_bias, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,6 +613,6 @@ const char *ssm_status_string(int status) {
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
 
-int ssm_version(void) { return 200; }
+int ssm_version(void) { return 300; }
 
 }  // extern "C"

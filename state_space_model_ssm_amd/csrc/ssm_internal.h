@@ -8,6 +8,10 @@
 
 namespace ssm {
 
+// softplus(v) = log(1 + exp(v)), the step-size map of SSM_DT_SOFTPLUS: v itself
+// above 20 (where log(1 + exp(v)) rounds to v in float32), else log1p(exp(v)).
+__device__ __forceinline__ float dt_softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+
 // One selective-scan launch (see ssm_scan_fwd in include/ssm.h for the math).
 struct ScanParams {
   const void *u, *delta, *B, *C, *z;  // in_dtype
@@ -16,6 +20,8 @@ struct ScanParams {
   void *y;                            // out_dtype
   float *h_last;                      // nullable
   float *carry;                       // chunked path: [batch][dim][n_chunks-1][2][dstate]
+  const float *dt_bias;               // nullable (dim); read when dt_softplus
+  int32_t dt_softplus;                // step with softplus(delta + dt_bias)
   int64_t batch, dim, seqlen, ngroups, dim_per_group;
   int64_t chunk_len;                  // time steps per chunk
   int64_t tiles_per_group;            // channel tiles per (batch, group)
@@ -57,6 +63,8 @@ struct ScanBwdParams {
   void *du, *ddelta, *dz;             // in_dtype; dz only with z
   float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
   const float *ckpt;                  // [batch][dim][ceil(L / kScanCkptStep)][dstate]
+  const float *dt_bias;               // nullable (dim); read when dt_softplus
+  int32_t dt_softplus;                // step with softplus(delta + dt_bias); ddelta is then d/d(raw delta)
   // Workspace for the sums: per channel tile, dB and dC terms
   // [batch][ngroups][tiles_per_group][dstate][L]; per batch row, dA terms
   // [batch][dim][dstate] and dD terms [batch][dim].
@@ -77,6 +85,8 @@ struct SsdParams {
   const float *h0;                    // nullable initial state [batch][nheads][headdim][dstate]
   void *y;                            // out dtype
   float *h_last;                      // nullable
+  const float *dt_bias;               // nullable (nheads); read when dt_softplus
+  int32_t dt_softplus, lam_sigmoid;   // dt = softplus(dt + dt_bias); lam = sigmoid(lam)
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
 };
 
@@ -90,6 +100,8 @@ struct StepParams {
   const float *A, *D;                 // float32; D nullable
   float *state;                       // [batch][dim][dstate], updated in place
   void *y;                            // out_dtype
+  const float *dt_bias;               // nullable (per dt element's channel or head); read when dt_softplus
+  int32_t dt_softplus;
   int64_t batch, dim, ngroups, headdim;
   int32_t dstate;
 };

@@ -57,7 +57,8 @@ __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
   const int64_t hd = HEAD ? d / p.headdim : d;    // per-head quantities live here
 
   const float u = ld(gu, cc);
-  const float dt = HEAD ? ld(gdt, b * (p.dim / p.headdim) + hd) : ld(gdt, cc);
+  float dt = HEAD ? ld(gdt, b * (p.dim / p.headdim) + hd) : ld(gdt, cc);
+  if (p.dt_softplus) dt = dt_softplus(dt + (p.dt_bias != nullptr ? p.dt_bias[hd] : 0.0f));
   float *st_row = p.state + cc * N + j * K;
   const int64_t bc = (b * p.ngroups + g) * N + j * K;
 

@@ -30,7 +30,7 @@ import torch
 
 __all__ = [
     "ScanShape", "SsdShape", "WORKLOADS", "make_scan_inputs", "make_ssd_inputs",
-    "inv_softplus",
+    "inv_softplus", "make_raw_step",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -133,6 +133,18 @@ def make_lam(shape, seed: int) -> torch.Tensor:
     rng = np.random.default_rng(seed)
     v = 1.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
     return _store(v, "bf16")
+
+
+def make_raw_step(shape, nbias: int, seed: int, dtype: str = "f32", scale: float = 0.5):
+    """Seeded raw step values and their bias for the fused Phase-0 step map
+    softplus(raw + bias): raw ~ N(0, scale^2) of ``shape`` stored in ``dtype``,
+    and a float32 bias of ``nbias`` values, bias = inv_softplus(dt0) with dt0
+    log-uniform on [1e-3, 1e-1] (so that softplus(bias) is a typical step)."""
+    rng = np.random.default_rng(seed)
+    raw = scale * rng.standard_normal(shape)
+    dt0 = np.exp(rng.uniform(math.log(1e-3), math.log(1e-1), nbias))
+    bias = np.log(np.expm1(dt0))
+    return _store(raw, dtype), torch.from_numpy(bias.astype(np.float32))
 
 
 def make_scan_inputs(s: ScanShape, a_override: Optional[np.ndarray] = None) -> dict:

@@ -17,6 +17,9 @@ Definitions followed (page titles and sections):
     the Mamba-2 structure; section "Repository layout": segsum and causal masks.
   * "We brought Mamba to Trainium", section "We built the parallel scan": the
     recurrence is associative, so it can be split and recombined.
+  * "Mamba-3 NKI Kernels for AWS Neuron", section "How it works", Phase 0: the
+    raw step goes through softplus(dt + dt_bias), the raw trapezoid weight
+    through a sigmoid.
 """
 from __future__ import annotations
 
@@ -441,6 +444,53 @@ def check_ssd_trap_single_ssd_form(orc):
                     _close(h[bb, hd], state, what=f"single-SSD form h_last (b{bb} h{hd})")
 
 
+def _rel_close(got, want, rtol, what):
+    got, want = np.asarray(got, dtype=np.float64), np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
+    err = np.abs(got - want) / np.maximum(np.abs(want), 1e-300)
+    assert float(np.max(err)) <= rtol, f"{what}: max rel err {float(np.max(err)):.3e}"
+
+
+def check_phase0_softplus(orc):
+    """The Phase-0 step map ("Mamba-3 NKI Kernels for AWS Neuron", section "How
+    it works", Phase 0) against numpy's log(exp(0) + exp(v)) on [-700, 750]
+    (no overflow at the ends), softplus(v) - softplus(-v) = v, softplus(0) =
+    log 2, and the bias index of both layouts: element (b, d, t) of a
+    (batch, dim, L) array adds bias[d], element (b, t, h) of a (batch, L, H)
+    array adds bias[h]."""
+    rng = np.random.default_rng(71)
+    v = np.concatenate([rng.uniform(-40, 40, 300), [-700.0, -30.0, 0.0, 30.0, 750.0]])
+    _rel_close(orc.softplus(v, None, 1), np.logaddexp(0.0, v), 1e-14, "softplus vs logaddexp")
+    w = rng.uniform(-30, 30, 200)
+    _close(orc.softplus(w, None, 1) - orc.softplus(-w, None, 1), w, rtol=1e-14, what="softplus odd part")
+    _close(orc.softplus(np.zeros(1), None, 1), [math.log(2.0)], rtol=1e-15, what="softplus(0)")
+    raw, bias = rng.uniform(-6, 6, (2, 3, 5)), rng.uniform(-3, 3, 3)
+    _rel_close(orc.softplus(raw, bias, 5).reshape(raw.shape), np.logaddexp(0.0, raw + bias[None, :, None]),
+               1e-14, "softplus bias per channel (batch, dim, L)")
+    raw2 = rng.uniform(-6, 6, (2, 5, 3))
+    _rel_close(orc.softplus(raw2, bias, 1).reshape(raw2.shape), np.logaddexp(0.0, raw2 + bias[None, None, :]),
+               1e-14, "softplus bias per head (batch, L, H)")
+
+
+def check_phase0_sigmoid_and_softplus_grad(orc):
+    """sigmoid against scipy's expit, sigmoid(v) + sigmoid(-v) = 1 and
+    sigmoid(0) = 1/2; the chain rule through the biased softplus against
+    central finite differences of the softplus itself (its derivative is the
+    sigmoid), in the (batch, dim, L) layout."""
+    from scipy.special import expit
+    rng = np.random.default_rng(72)
+    v = np.concatenate([rng.uniform(-40, 40, 300), [-700.0, 0.0, 700.0]])
+    _rel_close(orc.sigmoid(v), expit(v), 1e-14, "sigmoid vs expit")
+    _close(orc.sigmoid(v) + orc.sigmoid(-v), np.ones_like(v), rtol=1e-15, what="sigmoid symmetry")
+    _close(orc.sigmoid(np.zeros(1)), [0.5], rtol=0.0, what="sigmoid(0)")
+    raw, bias = rng.uniform(-6, 6, (2, 3, 4)), rng.uniform(-2, 2, 3)
+    g = rng.standard_normal(raw.shape)
+    got = orc.softplus_grad(raw, bias, 4, g).reshape(raw.shape)
+    e = 1e-6
+    fd = (orc.softplus(raw + e, bias, 4) - orc.softplus(raw - e, bias, 4)).reshape(raw.shape) / (2 * e)
+    _close(got, g * fd, rtol=1e-8, what="softplus chain rule vs finite differences")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -456,4 +506,6 @@ ALL_CHECKS = [
     check_scan_bwd_finite_differences,
     check_ssd_trap_lam_one_is_ssd,
     check_ssd_trap_single_ssd_form,
+    check_phase0_softplus,
+    check_phase0_sigmoid_and_softplus_grad,
 ]

@@ -52,7 +52,7 @@ def test_library_loads_and_exports_exactly_the_header():
 
 
 def test_version_and_status_strings():
-    assert ssm.version() == 200
+    assert ssm.version() == 300
     for code, name in ssm.STATUS.items():
         assert ssm.status_string(code) == name
     assert ssm.status_string(-99) == "SSM_ERR_UNKNOWN"
@@ -73,7 +73,7 @@ def _scan(dims, u=FAKE, delta=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), -2), (dict(dim=-3), -2), (dict(seqlen=-1), -2), (dict(dstate=0), -2),
     (dict(ngroups=0), -2), (dict(dim=64, ngroups=3), -2), (dict(in_dtype=2), -3),
-    (dict(out_dtype=-1), -3), (dict(flags=1), -2), (dict(n_chunks=-1), -2),
+    (dict(out_dtype=-1), -3), (dict(flags=4), -2), (dict(flags=2), -2), (dict(n_chunks=-1), -2),
     (dict(n_chunks=5000), -2), (dict(dstate=12), -5), (dict(dstate=128), -5),
 ])
 def test_scan_rejects_bad_dims(kw, code):
@@ -92,6 +92,48 @@ def test_scan_rejects_null_and_misaligned():
     assert _scan(d, u=FAKE + 2) == -4                       # f32 input needs 4-byte alignment
     assert _scan(d, h=FAKE + 0x20000002) == -4
     assert _scan(_dims(out_dtype=1), y=FAKE + 0x10000001) == -4
+
+
+def test_dt_bias_rules():
+    """dt_bias is read only with SSM_DT_SOFTPLUS, must be 4-byte aligned and
+    must not overlap an output (scan, SSD and step calls)."""
+    bias = FAKE + 0x700000
+    assert _scan(_dims(dt_bias=bias)) == -2                                   # bias without the flag
+    assert _scan(_dims(flags=ssm.SSM_DT_SOFTPLUS, dt_bias=bias + 2)) == -4     # misaligned
+    assert _scan(_dims(flags=ssm.SSM_DT_SOFTPLUS, dt_bias=FAKE + 0x10000000 + 8)) == -2   # inside y
+    assert _ssd(_sdims(dt_bias=bias)) == -2
+    assert _ssd(_sdims(flags=ssm.SSM_DT_SOFTPLUS, dt_bias=bias + 1)) == -4
+    assert _ssd(_sdims(flags=ssm.SSM_DT_SOFTPLUS, dt_bias=FAKE + 0x10000000 + 8)) == -2
+    assert _step(_stepdims(dt_bias=bias)) == -2
+    assert _step(_stepdims(flags=ssm.SSM_DT_SOFTPLUS, dt_bias=FAKE + 0x10000000 + 8)) == -2
+    assert _step(_ssdstepdims(flags=ssm.SSM_LAM_SIGMOID), ssd=True) == -2    # lam map: trapezoid only
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """ctypes mirrors of the dims structs have the C sizes and field offsets."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "ssm.h"\n'
+        '#define P(T, F) printf("%s %s %zu %zu\\n", #T, #F, sizeof(T), offsetof(T, F))\n'
+        "int main(void) { P(ssm_scan_dims_t, dt_bias); P(ssm_scan_dims_t, workspace_bytes);"
+        " P(ssd_dims_t, dt_bias); P(ssd_dims_t, workspace); P(ssm_step_dims_t, dt_bias);"
+        " P(ssd_step_dims_t, dt_bias); return 0; }\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    mirrors = {"ssm_scan_dims_t": ssm.ScanDims, "ssd_dims_t": ssm.SsdDims,
+               "ssm_step_dims_t": ssm.StepDims, "ssd_step_dims_t": ssm.SsdStepDims}
+    for line in filter(None, out):
+        name, field, size, off = line.split()
+        cls = mirrors[name]
+        assert ctypes.sizeof(cls) == int(size), (name, ctypes.sizeof(cls), size)
+        assert getattr(cls, field).offset == int(off), (name, field)
 
 
 def test_scan_rejects_overlap():
@@ -170,7 +212,7 @@ def _ssd(dims, x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), -2), (dict(seqlen=-1), -2), (dict(headdim=0), -2), (dict(ngroups=3), -2),
     (dict(in_dtype=7), -3), (dict(in_dtype=0), -5), (dict(headdim=32), -5), (dict(dstate=96), -5),
-    (dict(chunk=32), -5), (dict(flags=2), -2), (dict(reserved=1), -2),
+    (dict(chunk=32), -5), (dict(flags=2), -2), (dict(flags=8), -2), (dict(reserved=1), -2),
 ])
 def test_ssd_rejects_bad_dims(kw, code):
     assert _ssd(_sdims(**kw)) == code, ssm.last_error()
@@ -231,7 +273,7 @@ def _ssdstepdims(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), -2), (dict(dim=65, ngroups=2), -2), (dict(dstate=12), -5), (dict(dstate=512), -5),
-    (dict(in_dtype=5), -3), (dict(flags=1), -2), (dict(reserved=3), -2), (dict(dstate=0), -2),
+    (dict(in_dtype=5), -3), (dict(flags=2), -2), (dict(reserved=3), -2), (dict(dstate=0), -2),
 ])
 def test_scan_step_rejects_bad_dims(kw, code):
     assert _step(_stepdims(**kw)) == code, ssm.last_error()

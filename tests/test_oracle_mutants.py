@@ -56,6 +56,11 @@ MUTANTS = [
     ("bwd_readout_ungated", [("const double l = lam[n] + dyh * C[j];", "const double l = lam[n] + dy[i] * C[j];")]),
     ("bwd_dh_last_ignored", [("lam[n] = dh_last ? dh_last[(b * dim + d) * dstate + n] : 0.0;", "lam[n] = 0.0;")]),
     ("bwd_dD_ungated", [("dD[d] += dyh * x;", "dD[d] += dy[i] * x;")]),
+    ("softplus_overflows", [("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));", "return log1p(exp(v));")]),
+    ("softplus_bias_dropped", [("out[i] = softplus(raw[i] + bv);", "out[i] = softplus(raw[i]);")]),
+    ("softplus_bias_index", [("bias[(i / inner) % nb]", "bias[i % nb]")]),
+    ("softplus_grad_sign", [("grad_in[i] * sigmoid(raw[i] + bv)", "grad_in[i] * sigmoid(-(raw[i] + bv))")]),
+    ("sigmoid_sign", [("return 1.0 / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(v));")]),
 ]
 
 

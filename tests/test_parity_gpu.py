@@ -20,8 +20,8 @@ import torch
 
 import oracle
 import state_space_model_ssm_amd as ssm
-from state_space_model_ssm_amd.synth import (WORKLOADS, ScanShape, SsdShape, make_lam, make_scan_inputs,
-                                             make_ssd_inputs, make_state)
+from state_space_model_ssm_amd.synth import (WORKLOADS, ScanShape, SsdShape, make_lam, make_raw_step,
+                                             make_scan_inputs, make_ssd_inputs, make_state)
 
 pytestmark = pytest.mark.gpu
 
@@ -709,3 +709,128 @@ def test_ssd_trap_named_workload_full_size():
         hs.append(h[b, hd].numpy()); hrs.append(hr[0, 0])
     assert rel_err(np.stack(ys), np.stack(yrs)) <= TOL_BF16
     assert rel_err(np.stack(hs), np.stack(hrs)) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# Fused Phase-0 maps: step = softplus(raw + dt_bias), trapezoid lam = sigmoid(raw)
+# ---------------------------------------------------------------------------
+
+PHASE0_SCAN_CASES = [
+    # (batch, dim, N, L, G, dtype, n_chunks, with_bias)
+    (2, 50, 16, 257, 1, "f32", 1, True),       # sweep, ragged channel and time tiles
+    (2, 50, 16, 257, 1, "f32", 3, False),      # chunked carry, no bias
+    (2, 48, 16, 100, 2, "bf16", 1, True),
+    (2, 50, 16, 264, 1, "bf16", 4, True),      # vector tiles, element tail, chunks
+    (2, 70, 4, 65, 2, "f32", 2, True),
+    (2, 6, 64, 97, 1, "bf16", 1, True),
+]
+
+
+@pytest.mark.parametrize("case", PHASE0_SCAN_CASES, ids=lambda c: "b{}d{}n{}l{}g{}_{}_k{}_bias{}".format(*c))
+def test_scan_dt_softplus(case):
+    batch, dim, N, L, G, dtype, k, with_bias = case
+    seed = 7000 + zlib.crc32(repr(case).encode()) % 1000
+    s = ScanShape(batch, dim, N, L, G, dtype, has_z=True, dskip="normal", a_kind="loguniform", seed=seed)
+    inp = make_scan_inputs(s)
+    raw, bias = make_raw_step((batch, dim, L), dim, seed + 1, dtype)
+    bias = bias if with_bias else None
+    h0 = make_state((batch, dim, N), seed=seed + 2)
+    inp["delta"] = raw
+    y = torch.full((batch, dim, L), float("nan"), dtype=DT[dtype], device="cuda")
+    h = torch.full((batch, dim, N), float("nan"), dtype=torch.float32, device="cuda")
+    ssm.scan_fwd(*(_dev(inp[k_]) for k_ in ("u", "delta", "A", "B", "C", "D", "z")), h0=_dev(h0), n_chunks=k,
+                 y=y, h_last=h, dt_softplus=True, dt_bias=_dev(bias))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan(inp["u"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0,
+                         dt_softplus=True, dt_bias=bias)
+    tol = tol_for(dtype)
+    assert rel_err(y.float().cpu(), yr) <= tol, rel_err(y.float().cpu(), yr)
+    assert rel_err(h.cpu(), hr) <= tol, rel_err(h.cpu(), hr)
+
+
+@pytest.mark.parametrize("trap", [False, True])
+def test_ssd_dt_softplus(trap):
+    """The SSD (and the trapezoidal SSD with lam = sigmoid(raw lam)) on raw dt
+    with a per-head bias, ragged last chunk, groups, gate and h0."""
+    batch, L, H, N, G = 2, 200, 4, 128, 2
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=True, dskip="normal", seed=7100 + trap)
+    inp = make_ssd_inputs(s)
+    raw, bias = make_raw_step((batch, L, H), H, 7110 + trap, "bf16")
+    h0 = make_state((batch, H, 64, N), seed=7120, scale=0.5)
+    args = [_dev(inp[k]) for k in ("A", "B", "C", "D", "z")]
+    if trap:
+        lraw = make_state((batch, L, H), seed=7130).to(torch.bfloat16)
+        y, h = ssm.ssd_trap_chunked_fwd(_dev(inp["x"]), _dev(raw), _dev(lraw), *args, h0=_dev(h0),
+                                        dt_softplus=True, dt_bias=_dev(bias), lam_sigmoid=True)
+        yr, hr = oracle.ssd_trap(inp["x"], raw, lraw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0,
+                                 dt_softplus=True, dt_bias=bias, lam_sigmoid=True)
+    else:
+        y, h = ssm.ssd_chunked_fwd(_dev(inp["x"]), _dev(raw), *args, h0=_dev(h0), dt_softplus=True,
+                                   dt_bias=_dev(bias))
+        yr, hr = oracle.ssd(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0,
+                            dt_softplus=True, dt_bias=bias)
+    torch.cuda.synchronize()
+    assert rel_err(y.float().cpu(), yr) <= TOL_BF16, rel_err(y.float().cpu(), yr)
+    assert rel_err(h.cpu(), hr) <= TOL_BF16, rel_err(h.cpu(), hr)
+
+
+def test_decode_steps_dt_softplus():
+    """Scan and SSD decode steps on raw dt with a bias per channel / per head,
+    chained over 8 tokens, against the oracle over the same tokens."""
+    L = 8
+    s = ScanShape(2, 40, 16, L, 1, "f32", has_z=True, dskip="normal", a_kind="loguniform", seed=7200)
+    inp = make_scan_inputs(s)
+    raw, bias = make_raw_step((2, 40, L), 40, 7201, "f32")
+    S0 = make_state((2, 40, 16), seed=7202)
+    yr, hr = oracle.scan(inp["u"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], S0,
+                         dt_softplus=True, dt_bias=bias)
+    state, ys = S0.cuda().clone(), []
+    for t in range(L):
+        tok = {k: inp[k][..., t].contiguous().cuda() for k in ("u", "z", "B", "C")}
+        ys.append(ssm.scan_step(tok["u"], raw[..., t].contiguous().cuda(), _dev(inp["A"]), tok["B"], tok["C"],
+                                _dev(inp["D"]), tok["z"], state=state, dt_softplus=True,
+                                dt_bias=_dev(bias)).cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(ys, dim=-1), yr) <= TOL_F32
+    assert rel_err(state.cpu(), hr) <= TOL_F32
+    s = SsdShape(2, L, 4, 64, 128, 1, 64, "bf16", has_z=False, dskip="ones", seed=7210)
+    inp = make_ssd_inputs(s)
+    raw, bias = make_raw_step((2, L, 4), 4, 7211, "bf16")
+    S0 = make_state((2, 4, 64, 128), seed=7212, scale=0.5)
+    yr, hr = oracle.ssd(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], None, S0,
+                        dt_softplus=True, dt_bias=bias)
+    state, ys = S0.cuda().clone(), []
+    for t in range(L):
+        tok = {k: inp[k][:, t].contiguous().cuda() for k in ("x", "B", "C")}
+        ys.append(ssm.ssd_step(tok["x"], raw[:, t].contiguous().cuda(), _dev(inp["A"]), tok["B"], tok["C"],
+                               _dev(inp["D"]), None, state=state, dt_softplus=True,
+                               dt_bias=_dev(bias)).float().cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(ys, dim=1), yr) <= TOL_BF16
+    assert rel_err(state.cpu(), hr) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype,N,with_bias", [("f32", 16, True), ("f32", 4, False), ("bf16", 16, True),
+                                               ("f32", 64, True)])
+def test_scan_backward_dt_softplus(dtype, N, with_bias):
+    """Backward on raw delta: ddelta is the gradient of the raw value (and its
+    sum over batch and steps that of dt_bias), every gradient against the
+    oracle's chain rule through softplus."""
+    batch, dim, L = 2, 40, 100
+    seed = 7300 + N + 7 * with_bias + (dtype == "bf16")
+    s = ScanShape(batch, dim, N, L, 1, dtype, has_z=True, dskip="normal", a_kind="loguniform", seed=seed)
+    inp = make_scan_inputs(s)
+    raw, bias = make_raw_step((batch, dim, L), dim, seed + 1, dtype)
+    bias = bias if with_bias else None
+    h0, dhl = make_state((batch, dim, N), seed=seed + 2), make_state((batch, dim, N), seed=seed + 3)
+    dy = make_state((batch, dim, L), seed=seed + 4).to(DT[dtype])
+    ref = oracle.scan_bwd(inp["u"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0, dy, dhl,
+                          dt_softplus=True, dt_bias=bias)
+    g = ssm.scan_bwd(_dev(inp["u"]), _dev(raw), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                     _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy), h0=_dev(h0), dh_last=_dev(dhl),
+                     dt_softplus=True, dt_bias=_dev(bias))
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_BWD_F32
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        err = rel_err(g[k].float().cpu(), ref[k])
+        assert err <= tol, (k, err)
