@@ -15,9 +15,10 @@
 // associative (decay, state) combine of "We brought Mamba to Trainium",
 // section "We built the parallel scan", with a scalar decay per head.
 //
-// One workgroup (4 wavefronts) per (b, h) walks the chunks in order and keeps
-// S^T in float32 MFMA accumulators: wavefront w owns the 16 headdim columns
-// p in [16w, 16w+16) for all dstate rows.  Chunk operands are staged in LDS as
+// Four wavefronts per (b, h) walk the chunks in order and keep S^T in float32
+// MFMA accumulators: wavefront w of a head owns the 16 headdim columns p in
+// [16w, 16w+16) for all dstate rows.  A workgroup takes one, two or four heads
+// of one group (which share B and C).  Chunk operands are staged in LDS as
 // bf16 (x transposed to [p][s], B also transposed to [n][s]) so that every
 // MFMA operand fragment is one 16-byte (or two 8-byte) LDS read.
 //
@@ -107,29 +108,41 @@ __device__ __forceinline__ int tidx(int col, int t) {
 // this SSD with the input of step s weighted by scale_s = gamma_s +
 // dt_{s+1} (1 - lam_{s+1}) wherever it reaches a later step, and by
 // gamma_s = lam_s dt_s at its own step (the diagonal of M).
-template <typename Tout, int N, bool HAS_Z, bool TRAP = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WPE, SSD_WPE))) ssd_chunk_kernel(const SsdParams p) {
+//
+// HPB heads per workgroup (4 HPB wavefronts): the heads of one group share B
+// and C, so the workgroup stages B and C once per chunk and computes each
+// G^T tile once, masking it with every head's decays; each head keeps its own
+// four wavefronts, x, M and state.  Four heads per workgroup put four
+// wavefronts on every SIMD, which hides the latency of each head's chain of
+// dependent LDS reads, MFMAs and barriers.
+template <typename Tout, int N, bool HAS_Z, bool TRAP, int HPB>
+__global__ void __launch_bounds__(256 * HPB)
+__attribute__((amdgpu_waves_per_eu(HPB == 4 ? 4 : SSD_WPE, HPB == 4 ? 4 : SSD_WPE)))
+ssd_chunk_kernel(const SsdParams p) {
+  constexpr int NTH = 256 * HPB;  // threads per workgroup
   constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
   constexpr int NK = N / 32;      // K steps over dstate
+  // bf16 y leaves through LDS as 16-byte row vectors (in each head's M
+  // buffer); float32 y is stored from the MFMA layout directly.
+  constexpr bool kStageY = sizeof(Tout) == 2;
+  constexpr int YV = 8;                        // bf16 y elements per 16-byte vector
+  constexpr int YP = P + YV;                   // padded y row
+  constexpr int YJ = Q * (P / YV) / 256;       // y vectors per thread of a head per chunk
+  constexpr int SM = (kStageY && Q * YP > Q * QP) ? Q * YP : Q * QP;  // one head's M (or y) buffer
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * NP];   // C[t][n]
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];   // B[s][n]
   __shared__ __attribute__((aligned(16))) uint16_t sBt[N * QP];  // B[n][s]
-  __shared__ __attribute__((aligned(16))) uint16_t sXt[P * QP];  // x[p][s]
-  // M[t][s] (bf16, rows of QP), then the chunk's y[t][p] (Tout, rows of YP).
-  constexpr int YV = 16 / static_cast<int>(sizeof(Tout));   // y elements per 16-byte vector
-  constexpr int YP = P + YV;                                 // padded y row
-  constexpr int YJ = Q * (P / YV) / 256;                     // y vectors per thread per chunk
-  constexpr int SM_BYTES = Q * QP * 2 > Q * YP * static_cast<int>(sizeof(Tout))
-                               ? Q * QP * 2 : Q * YP * static_cast<int>(sizeof(Tout));
-  __shared__ __attribute__((aligned(16))) uint16_t sM[SM_BYTES / 2];
-  Tout *sY = reinterpret_cast<Tout *>(sM);
-  __shared__ __attribute__((aligned(16))) float sA[Q];           // a_t
-  __shared__ __attribute__((aligned(16))) float sEa[Q];          // exp(a_t)
-  __shared__ __attribute__((aligned(16))) float sW[Q];           // exp(a_last - a_s) w_s
-  __shared__ __attribute__((aligned(16))) float sDt[Q];          // w_s: dt_s (scale_s when TRAP)
-  __shared__ __attribute__((aligned(16))) float sGam[TRAP ? Q : 1];  // gamma_s (TRAP)
-  __shared__ float sDecay;                                       // exp(a_last)
+  __shared__ __attribute__((aligned(16))) uint16_t sXtH[HPB * P * QP];  // per head: x[p][s]
+  __shared__ __attribute__((aligned(16))) uint16_t sMH[HPB * SM];       // per head: M[t][s], then y[t][p]
+  // Per head: a_t, exp(a_t), exp(a_last - a_s) w_s, w_s (dt_s, or scale_s
+  // when TRAP), gamma_s (TRAP) and exp(a_last).
+  __shared__ __attribute__((aligned(16))) float sAH[HPB * Q];
+  __shared__ __attribute__((aligned(16))) float sEaH[HPB * Q];
+  __shared__ __attribute__((aligned(16))) float sWH[HPB * Q];
+  __shared__ __attribute__((aligned(16))) float sDtH[HPB * Q];
+  __shared__ __attribute__((aligned(16))) float sGamH[TRAP ? HPB * Q : 1];
+  __shared__ float sDecayH[HPB];
 
   const uint16_t *__restrict__ gx = static_cast<const uint16_t *>(p.x);
   const uint16_t *__restrict__ gdt = static_cast<const uint16_t *>(p.dt);
@@ -139,16 +152,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   const uint16_t *__restrict__ glam = static_cast<const uint16_t *>(p.lam);
   Tout *__restrict__ gy = static_cast<Tout *>(p.y);
 
-  // Blocks of one batch row share B and C.  Consecutive block ids are dealt
-  // round-robin to the 8 XCDs, so remap ids to give each XCD a contiguous run
-  // of (b, h) pairs and keep a batch row's B/C in one L2.
-  const int64_t nblk = p.batch * p.nheads;
+  const int64_t L = p.seqlen, H = p.nheads, G = p.ngroups;
+  const int64_t hblocks = H / HPB;  // workgroups per batch row
+  // Workgroups of one batch row share B and C.  Consecutive workgroup ids are
+  // dealt round-robin to the 8 XCDs, so remap ids to give each XCD a
+  // contiguous run of (b, head block) pairs and keep a batch row's B/C in one L2.
+  const int64_t nblk = p.batch * hblocks;
   int64_t id = blockIdx.x;
   if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;
-  const int64_t b = id / p.nheads;
-  const int64_t h = id % p.nheads;
-  const int64_t g = h / (p.nheads / p.ngroups);
-  const int64_t L = p.seqlen, H = p.nheads, G = p.ngroups;
+  const int64_t b = id / hblocks;
+  const int64_t h0i = (id % hblocks) * HPB;  // first head of the workgroup
+  const int64_t g = h0i / (H / G);
+
+  const int tid = threadIdx.x;
+  // The wavefront index is uniform over a wavefront; taking it from the first
+  // lane lets everything derived from it (head, LDS bases, per-head scalars)
+  // live in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int q = lane / 16;
+  const int r16 = lane % 16;
+  const int hs = wave / 4;                  // this wavefront's head slot
+  const int htid = tid % 256;               // thread index within the head's wavefronts
+  const int pcol = (wave % 4) * 16 + r16;   // this lane's headdim column in S^T and Y
+  const int64_t h = h0i + hs;
+  uint16_t *const sXt = sXtH + hs * (P * QP);
+  uint16_t *const sM = sMH + hs * SM;
+  const float *const sA = sAH + hs * Q;
+  const float *const sEa = sEaH + hs * Q;
+  const float *const sW = sWH + hs * Q;
+
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.0f;
   // Phase-0 maps of the raw inputs when asked for: the step softplus(dt +
@@ -160,13 +193,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   auto lam_of = [&](float raw) __attribute__((always_inline)) {
     return p.lam_sigmoid ? 1.0f / (1.0f + expf(-raw)) : raw;
   };
-
-  const int tid = threadIdx.x;
-  const int wave = tid / 64;
-  const int lane = tid % 64;
-  const int q = lane / 16;
-  const int r16 = lane % 16;
-  const int pcol = wave * 16 + r16;  // this lane's headdim column in S^T and Y
 
   floatx4 S[NT];  // S^T tiles: rows n = 16 ni + 4q + r, column p = pcol
 #pragma unroll
@@ -189,8 +215,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   // step pairs) XOR the pair index with a multiple of the wavefront's tp span
   // chosen by the row, which spreads one store instruction over all 64 banks;
   // fragment reads apply the same XOR, and keep 16-byte groups contiguous.
-  constexpr int BJ = (Q / 2) * (N / 8) / 256;  // B/C jobs per thread per chunk
-  static_assert(BJ >= 1 && (Q / 2) * (P / 8) == 256 && QP % 2 == 0, "staging map");
+  // B and C jobs (one tensor each: jobs below BC_JOBS / 2 are B's) are spread
+  // over the whole workgroup, so whole wavefronts take one or none; x jobs
+  // over each head's 256 threads.
+  constexpr int BC_JOBS = 2 * (Q / 2) * (N / 8);
+  constexpr int BJ = (BC_JOBS + NTH - 1) / NTH;  // B/C jobs per thread per chunk
+  static_assert(BC_JOBS % 128 == 0 && (Q / 2) * (P / 8) == 256 && QP % 2 == 0, "staging map");
   uint32_t *sBt32 = reinterpret_cast<uint32_t *>(sBt);
   uint32_t *sXt32 = reinterpret_cast<uint32_t *>(sXt);
   auto pair_lo = [](uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); };
@@ -214,61 +244,68 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   // reach no output row that is stored and add nothing to the state (their
   // weights in M and in the state update are 0).  The loads are branch-free.
   struct ChunkRegs {
-    uint4 bv[BJ][2], cv[BJ][2];
+    uint4 bc[BJ][2];  // steps 2 tp and 2 tp + 1 of a B or C job
     uint4 xv[2];
-    uint32_t dt;  // raw bf16 bits of dt at step `lane` (wavefront 0 uses it)
+    uint32_t dt;  // raw bf16 bits of this head's dt at step `lane` (its first wavefront uses it)
     uint32_t lam, dtn, lamn;  // TRAP: lam at step `lane`, dt and lam at step `lane` + 1
   };
+  // Global addresses: a uniform base at the chunk's first step plus a 32-bit
+  // lane offset (the host keeps 64 rows of x and of B/C below 2^31 elements).
+  const int rx = static_cast<int>(H * P), rbc = static_cast<int>(G * N), rdt = static_cast<int>(H);
   auto load_chunk = [&](int64_t c0, ChunkRegs &R) __attribute__((always_inline)) {
+    const int last = static_cast<int>(min(static_cast<int64_t>(Q), L - c0) - 1);  // last valid step offset
 #pragma unroll
     for (int k = 0; k < BJ; ++k) {
-      const int v = tid + 256 * k;
-      const int tp = v / (N / 8);
-      const int nv = (v % (N / 8)) * 8;
+      const int v = tid + NTH * k;
+      if (BC_JOBS % NTH == 0 || v < BC_JOBS) {
+        const int vv = v % (BC_JOBS / 2);
+        const int tp = vv / (N / 8);
+        const int nv = (vv % (N / 8)) * 8;
+        const uint16_t *src = (v < BC_JOBS / 2 ? gB : gC) + ((b * L + c0) * G + g) * N;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t tc = min(c0 + 2 * tp + e, L - 1);
-        const int64_t off = ((b * L + tc) * G + g) * N + nv;
-        R.bv[k][e] = *reinterpret_cast<const uint4 *>(gB + off);
-        R.cv[k][e] = *reinterpret_cast<const uint4 *>(gC + off);
+        for (int e = 0; e < 2; ++e)
+          R.bc[k][e] = *reinterpret_cast<const uint4 *>(src + min(2 * tp + e, last) * rbc + nv);
       }
     }
     {
-      const int tp = tid / (P / 8);
-      const int pv = (tid % (P / 8)) * 8;
+      const int tp = htid / (P / 8);
+      const int pv = (htid % (P / 8)) * 8;
+      const uint16_t *src = gx + ((b * L + c0) * H + h) * P;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t tc = min(c0 + 2 * tp + e, L - 1);
-        R.xv[e] = *reinterpret_cast<const uint4 *>(gx + ((b * L + tc) * H + h) * P + pv);
-      }
+      for (int e = 0; e < 2; ++e) R.xv[e] = *reinterpret_cast<const uint4 *>(src + min(2 * tp + e, last) * rx + pv);
     }
     // Unconditional load from a clamped step: no branch, so nothing waits
     // on it (or on the loads before it) until the chunk is staged.
-    R.dt = gdt[(b * L + min(c0 + lane, L - 1)) * H + h];
+    const int64_t dbase = (b * L + c0) * H + h;
+    const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0) - 1);  // the next chunk's first step too
+    R.dt = gdt[dbase + min(lane, last) * rdt];
     if constexpr (TRAP) {
-      R.lam = glam[(b * L + min(c0 + lane, L - 1)) * H + h];
-      R.dtn = gdt[(b * L + min(c0 + lane + 1, L - 1)) * H + h];
-      R.lamn = glam[(b * L + min(c0 + lane + 1, L - 1)) * H + h];
+      R.lam = glam[dbase + min(lane, last) * rdt];
+      R.dtn = gdt[dbase + min(lane + 1, lastn) * rdt];
+      R.lamn = glam[dbase + min(lane + 1, lastn) * rdt];
     }
   };
   auto stage_chunk = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
     // B and C: natural layout [t][n] for both, B also transposed to [n][t].
 #pragma unroll
     for (int k = 0; k < BJ; ++k) {
-      const int v = tid + 256 * k;
-      const int tp = v / (N / 8);
-      const int nv = (v % (N / 8)) * 8;
+      const int v = tid + NTH * k;
+      if (BC_JOBS % NTH == 0 || v < BC_JOBS) {
+        const int vv = v % (BC_JOBS / 2);
+        const int tp = vv / (N / 8);
+        const int nv = (vv % (N / 8)) * 8;
+        const bool is_b = v < BC_JOBS / 2;  // uniform over a wavefront
+        uint16_t *dst = is_b ? sB : sC;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<uint4 *>(&sB[(2 * tp + e) * NP + nv]) = R.bv[k][e];
-        *reinterpret_cast<uint4 *>(&sC[(2 * tp + e) * NP + nv]) = R.cv[k][e];
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4 *>(&dst[(2 * tp + e) * NP + nv]) = R.bc[k][e];
+        if (is_b) put_t(sBt32, nv, tp, R.bc[k][0], R.bc[k][1], std::integral_constant<int, N>{});
       }
-      put_t(sBt32, nv, tp, R.bv[k][0], R.bv[k][1], std::integral_constant<int, N>{});
     }
     // x transposed to [p][t].
-    put_t(sXt32, (tid % (P / 8)) * 8, tid / (P / 8), R.xv[0], R.xv[1], std::integral_constant<int, P>{});
-    // dt and the in-chunk cumulative decay (wavefront 0: one lane per step).
-    if (wave == 0) {
+    put_t(sXt32, (htid % (P / 8)) * 8, htid / (P / 8), R.xv[0], R.xv[1], std::integral_constant<int, P>{});
+    // dt and the in-chunk cumulative decay (the head's first wavefront: one
+    // lane per step).
+    if (wave % 4 == 0) {
       const float dtv = (c0 + lane < L) ? step_of(bf2f(static_cast<uint16_t>(R.dt))) : 0.0f;
       // Inclusive prefix sum over the 64 lanes: within each 16-lane row by
       // DPP row shifts (lanes shifted in from outside the row read 0), then
@@ -290,13 +327,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         const float dtn = nx ? step_of(bf2f(static_cast<uint16_t>(R.dtn))) : 0.0f;
         const float lamn = nx ? lam_of(bf2f(static_cast<uint16_t>(R.lamn))) : 0.0f;
         w = gam + dtn * (1.0f - lamn);
-        sGam[lane] = gam;
+        sGamH[hs * Q + lane] = gam;
       }
-      sA[lane] = a;
-      sEa[lane] = fast_exp(a);
-      sW[lane] = fast_exp(alast - a) * w;
-      sDt[lane] = w;
-      if (lane == 0) sDecay = fast_exp(alast);
+      sAH[hs * Q + lane] = a;
+      sEaH[hs * Q + lane] = fast_exp(a);
+      sWH[hs * Q + lane] = fast_exp(alast - a) * w;
+      sDtH[hs * Q + lane] = w;
+      if (lane == 0) sDecayH[hs] = fast_exp(alast);
     }
   };
 
@@ -308,6 +345,59 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 #if SSD_PREFETCH
     if (c0 + Q < L) load_chunk(c0 + Q, R);
 #endif
+
+    // ---- M = mask(G^T) into LDS, for every head of the workgroup -----------
+    // 12 tiles (si, ti): the lower-triangular tiles plus the two upper tiles
+    // (1,0) and (3,2) that the K = 32 steps of Y_diag read; those are written
+    // as zeros.  Tile k goes to wavefront k mod (4 HPB).
+    {
+      // (si, ti) pairs, four bits each: si | ti << 2, in the order listed above.
+      constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 |
+                                  0xAull << 20 | 0xCull << 24 | 0xDull << 28 | 0xEull << 32 |
+                                  0xFull << 36 | 0x1ull << 40 | 0xBull << 44;
+      constexpr int kRounds = (12 + 4 * HPB - 1) / (4 * HPB);
+#pragma unroll
+      for (int u = 0; u < kRounds; ++u) {
+        const int k = wave + 4 * HPB * u;
+        if (12 % (4 * HPB) == 0 || k < 12) {
+          const int code = static_cast<int>((kTiles >> (4 * k)) & 0xF);
+          const int si = code & 3;
+          const int ti = code >> 2;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (si <= ti) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+              const bf16x8 afrag = lds8(&sB[(si * 16 + r16) * NP + 32 * kk + 8 * q]);
+              const bf16x8 bfrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
+              acc = mfma(afrag, bfrag, acc);
+            }
+          }
+          const int t = ti * 16 + r16;
+          const int sb = si * 16 + 4 * q;
+#pragma unroll
+          for (int j = 0; j < HPB; ++j) {
+            const float at = sAH[j * Q + t];
+            const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sAH[j * Q + sb]);
+            const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDtH[j * Q + sb]);
+            floatx4 gm4 = dt4;
+            if constexpr (TRAP) gm4 = *reinterpret_cast<const floatx4 *>(&sGamH[j * Q + sb]);
+            uint16_t m[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              // Branch-free: above the diagonal the exponent is clamped to 0
+              // (a_t - a_s > 0 there) and the product is multiplied by 0.
+              const int s = sb + r;
+              const float ws = s < t ? dt4[r] : gm4[r];
+              const float keep = s <= t ? 1.0f : 0.0f;
+              m[r] = f2bf(acc[r] * fast_exp(fminf(at - as4[r], 0.0f)) * ws * keep);
+            }
+            *reinterpret_cast<uint2 *>(&sMH[j * SM + t * QP + si * 16 + 4 * q]) =
+                *reinterpret_cast<const uint2 *>(m);
+          }
+        }
+      }
+    }
+    __syncthreads();
 
     // ---- Y_off = diag(exp(a_t)) C S_prev^T ---------------------------------
     floatx4 Y[4];
@@ -336,7 +426,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
 
     // ---- S_new = exp(a_last) S_prev + B^T (w x) ----------------------------
     {
-      const float decay = sDecay;
+      const float decay = sDecayH[hs];
 #pragma unroll
       for (int i = 0; i < NT; ++i) S[i] *= decay;
 #pragma unroll
@@ -360,48 +450,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       }
     }
 
-    // ---- M = mask(G^T) into LDS: 12 tiles (si, ti), three per wavefront ----
-    // The lower-triangular tiles plus the two upper tiles (1,0) and (3,2) that
-    // the K = 32 steps of Y_diag read; those are written as zeros.
-    {
-      // (si, ti) pairs, four bits each: si | ti << 2, in the order listed above.
-      constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 |
-                                  0xAull << 20 | 0xCull << 24 | 0xDull << 28 | 0xEull << 32 |
-                                  0xFull << 36 | 0x1ull << 40 | 0xBull << 44;
-#pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int code = static_cast<int>((kTiles >> (4 * (wave + 4 * u))) & 0xF);
-        const int si = code & 3;
-        const int ti = code >> 2;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (si <= ti) {
-#pragma unroll
-          for (int kk = 0; kk < NK; ++kk) {
-            const bf16x8 afrag = lds8(&sB[(si * 16 + r16) * NP + 32 * kk + 8 * q]);
-            const bf16x8 bfrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
-            acc = mfma(afrag, bfrag, acc);
-          }
-        }
-        const int t = ti * 16 + r16;
-        const float at = sA[t];
-        const int sb = si * 16 + 4 * q;
-        const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sA[sb]);
-        const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
-        floatx4 gm4 = dt4;
-        if constexpr (TRAP) gm4 = *reinterpret_cast<const floatx4 *>(&sGam[sb]);
-        uint16_t m[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = sb + r;
-          const float ws = s < t ? dt4[r] : gm4[r];
-          const float v = (s <= t) ? acc[r] * fast_exp(at - as4[r]) * ws : 0.0f;
-          m[r] = f2bf(v);
-        }
-        *reinterpret_cast<uint2 *>(&sM[t * QP + si * 16 + 4 * q]) = *reinterpret_cast<const uint2 *>(m);
-      }
-    }
-    __syncthreads();
-
     // ---- Y += M X (causal: K steps at or below the diagonal) ---------------
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
@@ -415,16 +463,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
       }
     }
 
-    // ---- epilogue: D skip and gate in the MFMA layout, then y through LDS ----
+    // ---- epilogue: D skip and gate in the MFMA layout ------------------------
     // The gate's z values are loaded first, all together, from clamped steps,
     // so the loads are waited for once.
     uint32_t zr[16];
+    const int64_t ybase = ((b * L + c0) * H + h) * P;  // (c0, h, 0) of x, z and y
     if constexpr (HAS_Z) {
+      const int last = static_cast<int>(min(static_cast<int64_t>(Q), L - c0) - 1);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t tc = min(c0 + (e / 4) * 16 + 4 * q + (e % 4), L - 1);
-        zr[e] = gz[((b * L + tc) * H + h) * P + pcol];
-      }
+      for (int e = 0; e < 16; ++e) zr[e] = gz[ybase + min((e / 4) * 16 + 4 * q + (e % 4), last) * rx + pcol];
     }
     float yv[16];
 #pragma unroll
@@ -437,23 +484,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
         yv[ti * 4 + r] = v;
       }
     }
-    __syncthreads();  // every wavefront is done reading M; its buffer takes y
-#pragma unroll
-    for (int e = 0; e < 16; ++e) st(sY, ((e / 4) * 16 + 4 * q + (e % 4)) * YP + pcol, yv[e]);
+    // Every wavefront is done reading M and x: the M buffers take y, and the
+    // next chunk may be staged.
     __syncthreads();
-    // y rows of the chunk as 16-byte vectors: P / YV vectors per step.
+    if constexpr (kStageY) {
+      Tout *sY = reinterpret_cast<Tout *>(sM);
 #pragma unroll
-    for (int k = 0; k < YJ; ++k) {
-      const int v = tid + 256 * k;
-      const int t = v / (P / YV);
-      const int pv = (v % (P / YV)) * YV;
-      if (c0 + t < L)
-        *reinterpret_cast<uint4 *>(gy + ((b * L + c0 + t) * H + h) * P + pv) =
-            *reinterpret_cast<const uint4 *>(&sY[t * YP + pv]);
+      for (int e = 0; e < 16; ++e) st(sY, ((e / 4) * 16 + 4 * q + (e % 4)) * YP + pcol, yv[e]);
+      __syncthreads();
+      // y rows of the chunk as 16-byte vectors: P / YV vectors per step.
+#pragma unroll
+      for (int k = 0; k < YJ; ++k) {
+        const int v = htid + 256 * k;
+        const int t = v / (P / YV);
+        const int pv = (v % (P / YV)) * YV;
+        if (c0 + t < L)
+          *reinterpret_cast<uint4 *>(gy + ybase + t * rx + pv) =
+              *reinterpret_cast<const uint4 *>(&sY[t * YP + pv]);
+      }
+      // No barrier here: the next chunk's staging writes none of the y
+      // buffers, and they are rewritten (as M) only after the next barrier.
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = (e / 4) * 16 + 4 * q + (e % 4);
+        if (c0 + t < L) st(gy + ybase, t * rx + pcol, yv[e]);
+      }
     }
-    // No barrier here: the next chunk's staging writes none of the y buffer,
-    // and every wavefront read its last staged operands before the barrier
-    // above; the y buffer is rewritten (as M) only after the next barrier.
 #if !SSD_PREFETCH
     if (c0 + Q < L) load_chunk(c0 + Q, R);
 #endif
@@ -467,14 +524,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SSD_WP
   }
 }
 
+template <typename Tout, int N, bool TRAP, int HPB>
+hipError_t launch_hpb(const SsdParams &p, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(p.batch * (p.nheads / HPB)));
+  if (p.z != nullptr)
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, true, TRAP, HPB>), grid, dim3(256 * HPB), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, false, TRAP, HPB>), grid, dim3(256 * HPB), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename Tout, int N, bool TRAP>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
-  if (p.z != nullptr)
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, true, TRAP>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((ssd_chunk_kernel<Tout, N, false, TRAP>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  // Four heads per workgroup (four wavefronts per SIMD, 128 registers) only
+  // where the kernel fits those registers without spilling: bf16 y, no gate,
+  // scalar decay.  The gate's prefetched z, float32 y held for direct stores
+  // and the trapezoid's extra weights spill there, and run faster with two.
+  const int max_hpb = (sizeof(Tout) == 2 && !TRAP && p.z == nullptr) ? 4 : 2;
+  switch (ssd_heads_per_block(p.batch, p.nheads, p.ngroups, max_hpb)) {
+    case 4: return launch_hpb<Tout, N, TRAP, 4>(p, stream);
+    case 2: return launch_hpb<Tout, N, TRAP, 2>(p, stream);
+    default: return launch_hpb<Tout, N, TRAP, 1>(p, stream);
+  }
 }
 
 template <typename Tout>
@@ -490,6 +561,15 @@ hipError_t launch_typed(const SsdParams &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+int ssd_heads_per_block(int64_t batch, int64_t nheads, int64_t ngroups, int max_hpb) {
+  // The most heads (up to max_hpb) that divide a group's heads while the grid
+  // still gives every CU a workgroup.
+  const int64_t hpg = nheads / ngroups;
+  for (int hpb = max_hpb; hpb >= 2; hpb /= 2)
+    if (hpg % hpb == 0 && batch * nheads / hpb >= kSsdMinBlocks) return hpb;
+  return 1;
+}
 
 hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream) {
   if (p.headdim != P || p.chunk != Q) return hipErrorInvalidValue;

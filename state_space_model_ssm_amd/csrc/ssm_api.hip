@@ -405,6 +405,9 @@ static int check_ssd_dims(const ssd_dims_t *d) {
   if (d->chunk != 64) return fail(SSM_ERR_UNSUPPORTED, "chunk %lld not supported (64)", (long long)d->chunk);
   if (d->batch > 0 && d->nheads > kMaxGridX / d->batch)
     return fail(SSM_ERR_UNSUPPORTED, "batch * nheads exceeds the grid limit");
+  // A chunk's rows of x, z, y and of B, C are addressed with 32-bit offsets.
+  if (d->nheads * d->headdim >= (1ll << 25) || d->ngroups * d->dstate >= (1ll << 25))
+    return fail(SSM_ERR_UNSUPPORTED, "nheads * headdim and ngroups * dstate must be below 2^25");
   return SSM_OK;
 }
 

@@ -91,6 +91,11 @@ struct SsdParams {
 };
 
 hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
+// Heads one SSD workgroup takes (1, 2 or 4, at most max_hpb; they share a
+// group), and the grid size below which fewer heads per workgroup are taken
+// (the CU count).
+constexpr int64_t kSsdMinBlocks = 256;
+int ssd_heads_per_block(int64_t batch, int64_t nheads, int64_t ngroups, int max_hpb);
 
 // One decode step (see ssm_scan_step and ssd_step in include/ssm.h).  The
 // SSD step is the scan step over channels d = (head, p) with A, dt and D

@@ -327,6 +327,40 @@ def test_ssd_small(case):
     assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
 
 
+# Workgroups take 4 heads of a group (bf16 y, no gate, scalar decay) or 2
+# heads (gate, float32 y, trapezoid) when the grid still has a workgroup per
+# CU: batch * nheads >= 1024 (4 heads) or >= 512 (2 heads).  These cases run
+# those paths with ragged chunks, groups and h0, whole tensors against the oracle.
+WIDE_SSD_CASES = [
+    # (batch, L, H, N, G, has_z, out, trap, h0)           heads per workgroup
+    (16, 100, 64, 128, 2, False, "bf16", False, True),   # 4
+    (16, 70, 64, 64, 4, False, "bf16", False, False),    # 4, dstate 64
+    (8, 130, 64, 128, 1, True, "bf16", False, True),     # 2 (gate)
+    (8, 65, 64, 128, 2, False, "f32", False, False),     # 2 (float32 y)
+    (8, 100, 64, 128, 1, True, "bf16", True, True),      # 2 (trapezoid)
+    (86, 64, 6, 128, 1, False, "bf16", False, False),    # 2 (6 heads per group)
+]
+
+
+@pytest.mark.parametrize("case", WIDE_SSD_CASES, ids=lambda c: "b{}l{}h{}n{}g{}_z{}_{}_trap{}_h0{}".format(*c))
+def test_ssd_multi_head_workgroups(case):
+    batch, L, H, N, G, has_z, out, trap, with_h0 = case
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip="normal",
+                 seed=7400 + zlib.crc32(repr(case).encode()) % 1000)
+    inp = make_ssd_inputs(s)
+    h0 = make_state((batch, H, 64, N), seed=7500 + L, scale=0.5) if with_h0 else None
+    out_dt = DT[out]
+    if trap:
+        lam = make_lam((batch, L, H), seed=7600 + L)
+        y, h = run_trap(inp, lam, h0, out_dtype=out_dt)
+        yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
+    else:
+        y, h = run_ssd(inp, out_dtype=out_dt, h0=h0)
+        yr, hr = ref_ssd(inp, h0=h0)
+    assert rel_err(y, yr) <= TOL_BF16, rel_err(y, yr)
+    assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
+
+
 def test_ssd_f32_output_and_empty():
     s = SsdShape(2, 128, 2, 64, 128, 1, 64, "bf16", seed=31)
     inp = make_ssd_inputs(s)
