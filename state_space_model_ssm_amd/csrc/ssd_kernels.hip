@@ -130,19 +130,34 @@ ssd_chunk_kernel(const SsdParams p) {
   constexpr int YP = P + YV;                   // padded y row
   constexpr int YJ = Q * (P / YV) / 256;       // y vectors per thread of a head per chunk
   constexpr int SM = (kStageY && Q * YP > Q * QP) ? Q * YP : Q * QP;  // one head's M (or y) buffer
-  __shared__ __attribute__((aligned(16))) uint16_t sC[Q * NP];   // C[t][n]
-  __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NP];   // B[s][n]
-  __shared__ __attribute__((aligned(16))) uint16_t sBt[N * QP];  // B[n][s]
-  __shared__ __attribute__((aligned(16))) uint16_t sXtH[HPB * P * QP];  // per head: x[p][s]
-  __shared__ __attribute__((aligned(16))) uint16_t sMH[HPB * SM];       // per head: M[t][s], then y[t][p]
+  // One LDS block, laid out by hand: the small per-head arrays first, at
+  // addresses that fit the immediate offset of an LDS instruction (so their
+  // per-lane addresses need no registers of their own), then the tiles.
   // Per head: a_t, exp(a_t), exp(a_last - a_s) w_s, w_s (dt_s, or scale_s
   // when TRAP), gamma_s (TRAP) and exp(a_last).
-  __shared__ __attribute__((aligned(16))) float sAH[HPB * Q];
-  __shared__ __attribute__((aligned(16))) float sEaH[HPB * Q];
-  __shared__ __attribute__((aligned(16))) float sWH[HPB * Q];
-  __shared__ __attribute__((aligned(16))) float sDtH[HPB * Q];
-  __shared__ __attribute__((aligned(16))) float sGamH[TRAP ? HPB * Q : 1];
-  __shared__ float sDecayH[HPB];
+  constexpr int kHeadF = HPB * Q * 4;                       // bytes of one per-head float array
+  constexpr int kOffA = 0, kOffEa = kOffA + kHeadF, kOffW = kOffEa + kHeadF, kOffDt = kOffW + kHeadF;
+  constexpr int kOffGam = kOffDt + kHeadF;
+  constexpr int kOffDecay = kOffGam + (TRAP ? kHeadF : 16);
+  constexpr int kOffC = kOffDecay + 16 * ((HPB * 4 + 15) / 16);
+  constexpr int kOffB = kOffC + Q * NP * 2;                 // C[t][n], then B[s][n]
+  constexpr int kOffBt = kOffB + Q * NP * 2;                // B[n][s]
+  constexpr int kOffXt = kOffBt + N * QP * 2;               // per head: x[p][s]
+  constexpr int kOffM = kOffXt + HPB * P * QP * 2;          // per head: M[t][s], then y[t][p]
+  constexpr int kLds = kOffM + HPB * SM * 2;
+  static_assert(kOffC % 16 == 0 && kOffBt % 16 == 0 && kOffXt % 16 == 0 && kOffM % 16 == 0, "LDS layout");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  float *const sAH = reinterpret_cast<float *>(smem + kOffA);
+  float *const sEaH = reinterpret_cast<float *>(smem + kOffEa);
+  float *const sWH = reinterpret_cast<float *>(smem + kOffW);
+  float *const sDtH = reinterpret_cast<float *>(smem + kOffDt);
+  float *const sGamH = reinterpret_cast<float *>(smem + kOffGam);
+  float *const sDecayH = reinterpret_cast<float *>(smem + kOffDecay);
+  uint16_t *const sC = reinterpret_cast<uint16_t *>(smem + kOffC);
+  uint16_t *const sB = reinterpret_cast<uint16_t *>(smem + kOffB);
+  uint16_t *const sBt = reinterpret_cast<uint16_t *>(smem + kOffBt);
+  uint16_t *const sXtH = reinterpret_cast<uint16_t *>(smem + kOffXt);
+  uint16_t *const sMH = reinterpret_cast<uint16_t *>(smem + kOffM);
 
   const uint16_t *__restrict__ gx = static_cast<const uint16_t *>(p.x);
   const uint16_t *__restrict__ gdt = static_cast<const uint16_t *>(p.dt);
@@ -164,17 +179,17 @@ ssd_chunk_kernel(const SsdParams p) {
   const int64_t h0i = (id % hblocks) * HPB;  // first head of the workgroup
   const int64_t g = h0i / (H / G);
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
   // The wavefront index is uniform over a wavefront; taking it from the first
   // lane lets everything derived from it (head, LDS bases, per-head scalars)
   // live in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int lane = tid % 64;
-  const int q = lane / 16;
-  const int r16 = lane % 16;
+  int lane = tid % 64;
+  int q = lane / 16;
+  int r16 = lane % 16;
   const int hs = wave / 4;                  // this wavefront's head slot
-  const int htid = tid % 256;               // thread index within the head's wavefronts
-  const int pcol = (wave % 4) * 16 + r16;   // this lane's headdim column in S^T and Y
+  int htid = tid % 256;               // thread index within the head's wavefronts
+  int pcol = (wave % 4) * 16 + r16;   // this lane's headdim column in S^T and Y
   const int64_t h = h0i + hs;
   uint16_t *const sXt = sXtH + hs * (P * QP);
   uint16_t *const sM = sMH + hs * SM;
@@ -340,6 +355,13 @@ ssd_chunk_kernel(const SsdParams p) {
   ChunkRegs R;
   if (L > 0) load_chunk(0, R);  // an empty sequence reads nothing (its step indexes would be -1)
   for (int64_t c0 = 0; c0 < L; c0 += Q) {
+    if constexpr (HPB == 4) {
+      // At four wavefronts per SIMD (128 registers) the lane indices pass
+      // through an empty asm each chunk, so the LDS and global addresses
+      // derived from them are recomputed (a few VALU operations) instead of
+      // being held, or spilled, across the loop.
+      asm volatile("" : "+v"(tid), "+v"(lane), "+v"(q), "+v"(r16), "+v"(htid), "+v"(pcol));
+    }
     stage_chunk(R, c0);
     __syncthreads();
 #if SSD_PREFETCH
@@ -536,12 +558,7 @@ hipError_t launch_hpb(const SsdParams &p, hipStream_t stream) {
 
 template <typename Tout, int N, bool TRAP>
 hipError_t launch_n(const SsdParams &p, hipStream_t stream) {
-  // Four heads per workgroup (four wavefronts per SIMD, 128 registers) only
-  // where the kernel fits those registers without spilling: bf16 y, no gate,
-  // scalar decay.  The gate's prefetched z, float32 y held for direct stores
-  // and the trapezoid's extra weights spill there, and run faster with two.
-  const int max_hpb = (sizeof(Tout) == 2 && !TRAP && p.z == nullptr) ? 4 : 2;
-  switch (ssd_heads_per_block(p.batch, p.nheads, p.ngroups, max_hpb)) {
+  switch (ssd_heads_per_block(p.batch, p.nheads, p.ngroups, 4)) {
     case 4: return launch_hpb<Tout, N, TRAP, 4>(p, stream);
     case 2: return launch_hpb<Tout, N, TRAP, 2>(p, stream);
     default: return launch_hpb<Tout, N, TRAP, 1>(p, stream);

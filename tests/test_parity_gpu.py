@@ -327,14 +327,17 @@ def test_ssd_small(case):
     assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
 
 
-# Workgroups take 4 heads of a group (bf16 y, no gate, scalar decay) or 2
-# heads (gate, float32 y, trapezoid) when the grid still has a workgroup per
-# CU: batch * nheads >= 1024 (4 heads) or >= 512 (2 heads).  These cases run
-# those paths with ragged chunks, groups and h0, whole tensors against the oracle.
+# Workgroups take 4 heads of a group when batch * nheads >= 1024, 2 heads when
+# it is >= 512 (or a group's head count is even but not a multiple of 4), so
+# that the grid still has a workgroup per CU.  These cases run those paths
+# with ragged chunks, groups, h0, gate, float32 y and the trapezoid, whole
+# tensors against the oracle.
 WIDE_SSD_CASES = [
     # (batch, L, H, N, G, has_z, out, trap, h0)           heads per workgroup
     (16, 100, 64, 128, 2, False, "bf16", False, True),   # 4
     (16, 70, 64, 64, 4, False, "bf16", False, False),    # 4, dstate 64
+    (16, 100, 64, 128, 1, True, "bf16", True, True),     # 4, trapezoid and gate
+    (16, 65, 64, 128, 2, True, "f32", False, False),     # 4, float32 y and gate
     (8, 130, 64, 128, 1, True, "bf16", False, True),     # 2 (gate)
     (8, 65, 64, 128, 2, False, "f32", False, False),     # 2 (float32 y)
     (8, 100, 64, 128, 1, True, "bf16", True, True),      # 2 (trapezoid)
