@@ -239,7 +239,8 @@ def main():
                                  "hbm_GB/s_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6, 1),
                                  "hbm_frac_with_h_last": round((w.metric_bytes() + w.hlast_bytes()) / wms / 1e6 /
                                                                HBM_PEAK_GBS, 4),
-                                 "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2)}
+                                 "mfma_TFLOP/s": round(ssd_flops(w) / wms / 1e9, 2),
+                                 "traffic": measured_traffic(name)}
                 if args.cold_reps > 0:
                     context[name]["cold"] = time_cold(f, args.cold_reps)
         context.update(decode_context(ssm, dev, stream, time_calls))
