@@ -27,6 +27,8 @@
 // step to the workspace, as it writes its per-batch dA and dD terms, and a
 // reduction kernel then adds those over channel tiles (dB, dC) or batch rows
 // (dA, dD) in a fixed order.  No atomics: every output is deterministic.
+#include <type_traits>
+
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -86,16 +88,69 @@ __device__ __forceinline__ float sum_row(const float *row) {
   return v[0];
 }
 
+// Value of lane J of this lane's 16-lane DPP row (row_newbcast), folded by
+// the compiler into the consuming VOP2 instruction where it can be.
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, true));
+}
+
+struct alignas(8) F2 {
+  float v[2];
+};
+
+// Sums of the even and of the odd floats of 2M consecutive LDS floats (M
+// pairs, 16-byte aligned), each pairwise in the order of sum_row<M>.
+template <int M>
+__device__ __forceinline__ F2 sum_row2(const float *row) {
+  float x[M], y[M];
+#pragma unroll
+  for (int i = 0; i < 2 * M; i += 4) {
+    const F4 q = *reinterpret_cast<const F4 *>(row + i);
+    x[i / 2] = q.v[0]; y[i / 2] = q.v[1]; x[i / 2 + 1] = q.v[2]; y[i / 2 + 1] = q.v[3];
+  }
+#pragma unroll
+  for (int w = 1; w < M; w *= 2) {
+#pragma unroll
+    for (int i = 0; i + w < M; i += 2 * w) {
+      x[i] += x[i + w];
+      y[i] += y[i + w];
+    }
+  }
+  return F2{{x[0], y[0]}};
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <typename Tin, typename Tout, int N, bool HAS_Z>
 __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
   using Cfg = BwdCfg<N>;
   constexpr int CH = Cfg::CH, TP = Cfg::TP, JS = Cfg::JS, RS = Cfg::RS, CS = Cfg::CS;
+  // N = 16: the 16 lanes of a DPP row are the states of one channel, and the
+  // thread that loads step j of a channel's (dt, u, dy, z) row segment is lane
+  // j of that channel's row.  Those values stay in registers and reach the
+  // row's lanes by DPP row broadcasts; only B and C go through LDS.
+  constexpr bool kRegs = N == 16;
+  constexpr int CT = kRegs ? 1 : CH * TP / 4;
 
-  __shared__ F4 sDl4[CH * TP / 4], sU4[CH * TP / 4], sDy4[CH * TP / 4], sZ4[HAS_Z ? CH * TP / 4 : 1];
+  __shared__ F4 sDl4[CT], sU4[CT], sDy4[CT], sZ4[HAS_Z ? CT : 1];
   __shared__ F4 sB4[N * TP / 4], sC4[N * TP / 4];
   float *sDl = sDl4[0].v, *sU = sU4[0].v, *sDy = sDy4[0].v, *sZ = sZ4[0].v, *sB = sB4[0].v, *sC = sC4[0].v;
-  __shared__ __attribute__((aligned(16))) float sQ[CH * RS];          // [channel][step][state]
-  __shared__ __attribute__((aligned(16))) float sR[kT * N * CS];      // [step][state][channel]
+  // kRegs: one reduction round per tile over pairs, (du, ddt) terms as
+  // [channel][step][state][2] and (dB, dC) terms as [step][state][channel][2];
+  // a reader's 16-byte groups fall on distinct banks (rows of JS2 and CS2
+  // floats), and a writing half-wavefront covers all 64 banks (RS2 = 32 mod 64).
+  constexpr int JS2 = 2 * N + 4, CS2 = 2 * CH + 4;
+  constexpr int RS2 = kT * JS2 + ((32 - (kT * JS2) % 64) % 64 + 64) % 64;
+  __shared__ __attribute__((aligned(16))) float sQ[kRegs ? CH * RS2 : CH * RS];      // [channel][step][state]
+  __shared__ __attribute__((aligned(16))) float sR[kRegs ? kT * N * CS2 : kT * N * CS];  // [step][state][channel]
 
   const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
   const Tin *__restrict__ gdl = static_cast<const Tin *>(p.delta);
@@ -174,7 +229,7 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
   auto stage_tile = [&](int64_t ti, const TileIn &R) __attribute__((always_inline)) {
     const int64_t t0 = ti * kT;
 #pragma unroll
-    for (int k = 0; k < PE; ++k) {
+    for (int k = 0; k < (kRegs ? 0 : PE); ++k) {
       const int e = tid + 256 * k;
       if (Cfg::PAIRS_CT % 256 != 0 && e >= Cfg::PAIRS_CT) continue;
       const int r = e / kT, t = e % kT;
@@ -201,12 +256,26 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
 
   for (int64_t ti = ntiles - 1; ti >= 0; --ti) {
     const int64_t t0 = ti * kT;
-    __syncthreads();  // the previous tile is done with every LDS buffer
+    // The previous tile must be done with every buffer this staging writes.
+    // With kRegs that is only B and C, last read before the previous tile's
+    // reduction barriers; otherwise the previous tile's last phase still reads
+    // the staged dt.
+    if constexpr (!kRegs) __syncthreads();
     // ---- stage the tile: rows of 16 steps, zero past the end ---------------
     float h_start;
+    // kRegs: this lane's step n of its channel (chl): the step size, u, dy
+    // and z; zero past the end (and dy zero on rows past the tile's channels).
+    float vdl = 0.0f, vu = 0.0f, vdy = 0.0f, vz = 0.0f;
     if constexpr (kPrefetch) {
       stage_tile(ti, R);
       h_start = mine ? R.h0 : 0.0f;
+      if constexpr (kRegs) {
+        const bool in = t0 + n < L;
+        vdl = in ? step_of(ld(R.dl, 0), chl) : 0.0f;
+        vu = in ? ld(R.u, 0) : 0.0f;
+        vdy = (in && chl < nvalid) ? ld(R.dy, 0) : 0.0f;
+        if constexpr (HAS_Z) vz = in ? ld(R.z, 0) : 0.0f;
+      }
     } else {
       for (int e = tid; e < CH * kT; e += 256) {
         const int r = e / kT, t = e % kT;
@@ -234,7 +303,28 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     // ---- recompute the tile's states; readout partials for the gate --------
     float hist[kT];
     float dec[kT];  // exp(dt A) of each step, reused by the adjoint
-    {
+    float bvr[kT], cvr[kT];  // kRegs: B and C of this lane's state, reused by the adjoint
+    const float vw = vdl * vu;  // kRegs: dt u of this lane's (channel, step)
+    if constexpr (kRegs) {
+#pragma unroll
+      for (int q4 = 0; q4 < kT / 4; ++q4) {
+        const F4 b4 = sB4[(n * TP) / 4 + q4], c4 = sC4[(n * TP) / 4 + q4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bvr[4 * q4 + i] = b4.v[i];
+          cvr[4 * q4 + i] = c4.v[i];
+        }
+      }
+      float h = h_start;
+      static_for<0, kT>([&](auto T) {
+        constexpr int t = decltype(T)::value;
+        const float a = __builtin_amdgcn_exp2f(row_bcast<t>(vdl) * a2);
+        h = fmaf(a, h, row_bcast<t>(vw) * bvr[t]);
+        hist[t] = h;
+        dec[t] = a;
+        if constexpr (HAS_Z) sQ[chl * RS + t * JS + n] = cvr[t] * h;
+      });
+    } else {
       float h = h_start;
 #pragma unroll
       for (int t4 = 0; t4 < kT; t4 += 4) {
@@ -254,60 +344,113 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
     }
     // ---- per (channel, step): dyhat (and dz, from yhat) --------------------
     if constexpr (HAS_Z) __syncthreads();
+    float vdyh = vdy;  // kRegs: dyhat of this lane's (channel, step)
+    if constexpr (kRegs) {
+      const float dskip = (p.D != nullptr && chl < nvalid) ? p.D[d0 + chl] : 0.0f;
+      if constexpr (HAS_Z) {
+        const float yhat = fmaf(dskip, vu, sum_row<N>(sQ + chl * RS + n * JS));
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-vz * kLog2e));
+        vdyh = vdy * vz * sg;
+        if (chl < nvalid && t0 + n < L)
+          st(static_cast<Tin *>(p.dz), (b * p.dim + d0 + chl) * L + t0 + n,
+             vdy * yhat * sg * (1.0f + vz * (1.0f - sg)));
+      }
+      dD_acc[0] = fmaf(vdyh, vu, dD_acc[0]);
+    } else {
 #pragma unroll
-    for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
-      const int e = tid + 256 * k;
-      if (e < Cfg::PAIRS_CT) {
-        const int r = e / kT, t = e % kT;
-        const float uu = sU[r * TP + t];
-        const float dy = sDy[r * TP + t];
-        const float dskip = (p.D != nullptr && r < nvalid) ? p.D[d0 + r] : 0.0f;
-        float dyh = dy;
-        if constexpr (HAS_Z) {
-          const float yhat = fmaf(dskip, uu, sum_row<N>(sQ + r * RS + t * JS));
-          const float zz = sZ[r * TP + t];
-          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-          dyh = dy * zz * sg;
-          if (r < nvalid && t0 + t < L)
-            st(static_cast<Tin *>(p.dz), (b * p.dim + d0 + r) * L + t0 + t,
-               dy * yhat * sg * (1.0f + zz * (1.0f - sg)));
+      for (int k = 0; k < (Cfg::PAIRS_CT + 255) / 256; ++k) {
+        const int e = tid + 256 * k;
+        if (e < Cfg::PAIRS_CT) {
+          const int r = e / kT, t = e % kT;
+          const float uu = sU[r * TP + t];
+          const float dy = sDy[r * TP + t];
+          const float dskip = (p.D != nullptr && r < nvalid) ? p.D[d0 + r] : 0.0f;
+          float dyh = dy;
+          if constexpr (HAS_Z) {
+            const float yhat = fmaf(dskip, uu, sum_row<N>(sQ + r * RS + t * JS));
+            const float zz = sZ[r * TP + t];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+            dyh = dy * zz * sg;
+            if (r < nvalid && t0 + t < L)
+              st(static_cast<Tin *>(p.dz), (b * p.dim + d0 + r) * L + t0 + t,
+                 dy * yhat * sg * (1.0f + zz * (1.0f - sg)));
+          }
+          dD_acc[k] = fmaf(dyh, uu, dD_acc[k]);
+          // sDy now holds dyhat; the reader of (r, t) wrote it and no one else
+          // reads sDy[r][t] before the barrier below.
+          sDy[r * TP + t] = dyh;
         }
-        dD_acc[k] = fmaf(dyh, uu, dD_acc[k]);
-        // sDy now holds dyhat; the reader of (r, t) wrote it and no one else
-        // reads sDy[r][t] before the barrier below.
-        sDy[r * TP + t] = dyh;
       }
     }
-    __syncthreads();
+    // sQ (the gate's partials) and sDy are read above; the adjoint rewrites sQ.
+    if constexpr (!kRegs || HAS_Z) __syncthreads();
 
     // ---- adjoint, backwards through the tile --------------------------------
     // The du and dB terms go straight to LDS (both buffers are free since the
     // barrier above); the ddt and dC terms wait in registers for the second
     // reduction phase.
-    float pddl[kT], pdC[kT];
-#pragma unroll
-    for (int t4 = kT - 4; t4 >= 0; t4 -= 4) {
-      const F4 dl4 = sDl4[(chl * TP + t4) / 4], u4 = sU4[(chl * TP + t4) / 4], dy4 = sDy4[(chl * TP + t4) / 4];
-      const F4 b4 = sB4[(n * TP + t4) / 4], c4 = sC4[(n * TP + t4) / 4];
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        const int t = t4 + i;
-        const float dl = dl4.v[i], uu = u4.v[i], dyh = dy4.v[i], bv = b4.v[i], cv = c4.v[i];
+    float pddl[kRegs ? 1 : kT], pdC[kRegs ? 1 : kT];
+    if constexpr (kRegs) {
+      static_for<0, kT>([&](auto I) {
+        constexpr int t = kT - 1 - decltype(I)::value;
         const float a = dec[t];
-        const float hprev = t > 0 ? hist[t - 1] : h_start;
-        const float l = fmaf(dyh, cv, lam);
-        pdC[t] = mine ? dyh * hist[t] : 0.0f;
-        sR[(t * N + n) * CS + chl] = mine ? l * dl * uu : 0.0f;
-        sQ[chl * RS + t * JS + n] = l * dl * bv;
-        pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
-        dA_acc = fmaf(l * dl * a, hprev, dA_acc);
+        const float hprev = t > 0 ? hist[t > 0 ? t - 1 : 0] : h_start;
+        const float l = fmaf(row_bcast<t>(vdyh), cvr[t], lam);
+        const float lb = l * bvr[t];
+        const float qa = l * (a * hprev);
+        *reinterpret_cast<F2 *>(&sQ[chl * RS2 + t * JS2 + 2 * n]) =
+            F2{{lb * row_bcast<t>(vdl), fmaf(qa, a_n, lb * row_bcast<t>(vu))}};
+        *reinterpret_cast<F2 *>(&sR[(t * N + n) * CS2 + 2 * chl]) =
+            F2{{mine ? l * row_bcast<t>(vw) : 0.0f, mine ? row_bcast<t>(vdyh) * hist[t] : 0.0f}};
+        dA_acc = fmaf(qa, row_bcast<t>(vdl), dA_acc);
         lam = a * l;
+      });
+    } else {
+#pragma unroll
+      for (int t4 = kT - 4; t4 >= 0; t4 -= 4) {
+        const F4 dl4 = sDl4[(chl * TP + t4) / 4], u4 = sU4[(chl * TP + t4) / 4], dy4 = sDy4[(chl * TP + t4) / 4];
+        const F4 b4 = sB4[(n * TP + t4) / 4], c4 = sC4[(n * TP + t4) / 4];
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          const int t = t4 + i;
+          const float dl = dl4.v[i], uu = u4.v[i], dyh = dy4.v[i], bv = b4.v[i], cv = c4.v[i];
+          const float a = dec[t];
+          const float hprev = t > 0 ? hist[t - 1] : h_start;
+          const float l = fmaf(dyh, cv, lam);
+          pdC[t] = mine ? dyh * hist[t] : 0.0f;
+          sR[(t * N + n) * CS + chl] = mine ? l * dl * uu : 0.0f;
+          sQ[chl * RS + t * JS + n] = l * dl * bv;
+          pddl[t] = l * fmaf(bv, uu, a_n * a * hprev);
+          dA_acc = fmaf(l * dl * a, hprev, dA_acc);
+          lam = a * l;
+        }
       }
     }
 
     // ---- reductions: (du over states, dB over channels), then (ddt, dC) ---
+    if constexpr (kRegs) {
+      // One round: this lane sums (du, ddt) of its (channel, step) = (chl, n)
+      // over states, and (dB, dC) of (step, state) = (chl, n) over channels.
+      __syncthreads();
+      const F2 sq = sum_row2<N>(sQ + chl * RS2 + n * JS2);
+      if (chl < nvalid && t0 + n < L) {
+        const int64_t o = (b * p.dim + d0 + chl) * L + t0 + n;
+        const float dskip = p.D != nullptr ? p.D[d0 + chl] : 0.0f;
+        st(static_cast<Tin *>(p.du), o, fmaf(vdyh, dskip, sq.v[0]));
+        // With the softplus step map, d(step)/d(raw delta) =
+        // sigmoid(raw + bias) = 1 - exp(-step).
+        const float gsp = p.dt_softplus ? -expm1f(-vdl) : 1.0f;
+        st(static_cast<Tin *>(p.ddelta), o, sq.v[1] * gsp);
+      }
+      const F2 sr = sum_row2<CH>(sR + (chl * N + n) * CS2);
+      if (t0 + chl < L) {
+        const int64_t at = (((b * p.ngroups + g) * p.tiles_per_group + tile) * N + n) * L + t0 + chl;
+        p.part_dB[at] = sr.v[0];
+        p.part_dC[at] = sr.v[1];
+      }
+    }
 #pragma unroll
-    for (int phase = 0; phase < 2; ++phase) {
+    for (int phase = 0; phase < (kRegs ? 0 : 2); ++phase) {
       if (phase == 1) {
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
@@ -326,11 +469,12 @@ __global__ void __launch_bounds__(256) scan_bwd_kernel(const ScanBwdParams p) {
             const int64_t o = (b * p.dim + d0 + r) * L + t0 + t;
             if (phase == 0) {
               const float dskip = p.D != nullptr ? p.D[d0 + r] : 0.0f;
-              st(static_cast<Tin *>(p.du), o, fmaf(sDy[r * TP + t], dskip, s));
+              // kRegs: this lane is (r, t) = (chl, n), whose dyhat it holds.
+              st(static_cast<Tin *>(p.du), o, fmaf(kRegs ? vdyh : sDy[r * TP + t], dskip, s));
             } else {
               // With the softplus step map, d(step)/d(raw delta) =
               // sigmoid(raw + bias) = 1 - exp(-step).
-              const float g = p.dt_softplus ? -expm1f(-sDl[r * TP + t]) : 1.0f;
+              const float g = p.dt_softplus ? -expm1f(-(kRegs ? vdl : sDl[r * TP + t])) : 1.0f;
               st(static_cast<Tin *>(p.ddelta), o, s * g);
             }
           }
