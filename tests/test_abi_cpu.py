@@ -213,6 +213,8 @@ def _ssd(dims, x=FAKE, dt=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
     (dict(batch=-1), -2), (dict(seqlen=-1), -2), (dict(headdim=0), -2), (dict(ngroups=3), -2),
     (dict(in_dtype=7), -3), (dict(in_dtype=0), -5), (dict(headdim=32), -5), (dict(dstate=96), -5),
     (dict(chunk=32), -5), (dict(flags=2), -2), (dict(flags=8), -2), (dict(reserved=1), -2),
+    # 32-bit in-chunk offsets: nheads * headdim and ngroups * dstate below 2^25
+    (dict(nheads=1 << 19), -5), (dict(nheads=1 << 18, ngroups=1 << 18), -5),
 ])
 def test_ssd_rejects_bad_dims(kw, code):
     assert _ssd(_sdims(**kw)) == code, ssm.last_error()
