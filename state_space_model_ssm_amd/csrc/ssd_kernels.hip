@@ -54,7 +54,10 @@ typedef float floatx8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int Q = 64;   // chunk length
 constexpr int P = 64;   // headdim
-constexpr int QP = Q + 8;  // padded LDS row (bf16 elements) of [.][s] arrays
+// Padded LDS rows (bf16 elements) of the [.][s] arrays; with the [.][n] rows
+// N + 24, measured ~4% faster than 8-element pads (fewer bank conflicts in
+// the fragment reads and the transposed stores).
+constexpr int QP = Q + 16;
 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
@@ -120,7 +123,7 @@ __global__ void __launch_bounds__(256 * HPB)
 __attribute__((amdgpu_waves_per_eu(HPB == 4 ? 4 : SSD_WPE, HPB == 4 ? 4 : SSD_WPE)))
 ssd_chunk_kernel(const SsdParams p) {
   constexpr int NTH = 256 * HPB;  // threads per workgroup
-  constexpr int NP = N + 8;       // padded LDS row of [.][n] arrays
+  constexpr int NP = N + 24;      // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
   constexpr int NK = N / 32;      // K steps over dstate
   // bf16 y leaves through LDS as 16-byte row vectors (in each head's M
