@@ -82,7 +82,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-context", action="store_true", help="skip the other named workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -114,10 +114,19 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
-    def time_calls(fn, steps, warmup):
+    def time_calls(fn, steps, warmup, min_warm_s=0.02):
+        """W untimed calls, then more until at least min_warm_s of back-to-back
+        calls have run (the GPU clocks settle after a few ms of load, and the
+        workloads timed after microsecond-scale ones would otherwise be timed
+        partly at lower clocks); then `steps` calls timed with HIP events."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < min_warm_s:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -187,7 +196,7 @@ def main():
         raise SystemExit("the headline workload must be a selective scan")
     host = make_scan_inputs(s)
     fn, chunks = scan_runner(s, host)
-    ms, wall = time_calls(fn, args.steps, args.warmup)
+    ms, wall = time_calls(fn, args.steps, args.warmup, min_warm_s=0.0)  # exactly W untimed steps
     sec = ms / 1e3
     gelem = s.elements / sec / 1e9
     mbytes = s.metric_bytes()
