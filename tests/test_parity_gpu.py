@@ -811,6 +811,30 @@ def test_ssd_dt_softplus(trap):
     assert rel_err(h.cpu(), hr) <= TOL_BF16, rel_err(h.cpu(), hr)
 
 
+@pytest.mark.parametrize("trap", [False, True])
+def test_ssd_dt_softplus_four_heads_per_workgroup(trap):
+    """The Phase-0 maps on the four-heads-per-workgroup path (batch 16 x 64
+    heads): each head's bias and, for the trapezoid, sigmoid(raw lam)."""
+    batch, L, H, N, G = 16, 100, 64, 128, 2
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=False, dskip="normal", seed=7150 + trap)
+    inp = make_ssd_inputs(s)
+    raw, bias = make_raw_step((batch, L, H), H, 7160 + trap, "bf16")
+    args = [_dev(inp[k]) for k in ("A", "B", "C", "D", "z")]
+    if trap:
+        lraw = make_state((batch, L, H), seed=7170).to(torch.bfloat16)
+        y, h = ssm.ssd_trap_chunked_fwd(_dev(inp["x"]), _dev(raw), _dev(lraw), *args, dt_softplus=True,
+                                        dt_bias=_dev(bias), lam_sigmoid=True)
+        yr, hr = oracle.ssd_trap(inp["x"], raw, lraw, inp["A"], inp["B"], inp["C"], inp["D"], None, None,
+                                 dt_softplus=True, dt_bias=bias, lam_sigmoid=True)
+    else:
+        y, h = ssm.ssd_chunked_fwd(_dev(inp["x"]), _dev(raw), *args, dt_softplus=True, dt_bias=_dev(bias))
+        yr, hr = oracle.ssd(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], None, None,
+                            dt_softplus=True, dt_bias=bias)
+    torch.cuda.synchronize()
+    assert rel_err(y.float().cpu(), yr) <= TOL_BF16, rel_err(y.float().cpu(), yr)
+    assert rel_err(h.cpu(), hr) <= TOL_BF16, rel_err(h.cpu(), hr)
+
+
 def test_decode_steps_dt_softplus():
     """Scan and SSD decode steps on raw dt with a bias per channel / per head,
     chained over 8 tokens, against the oracle over the same tokens."""
