@@ -120,15 +120,12 @@ __device__ __forceinline__ Words<W> load_seg_tail(const uint16_t *row, int64_t t
   return r;
 }
 
-#ifndef SCAN_DPP_T
-#define SCAN_DPP_T 32
-#endif
-#ifndef SCAN_DPP_VEC
-#define SCAN_DPP_VEC 4
-#endif
-#ifndef SCAN_WAVES16
-#define SCAN_WAVES16 4
-#endif
+// DPP path (N >= 16): 32-step time tiles, staging loads of 4 elements, and
+// (N = 16) registers held to four wavefronts per SIMD.  Measured against 16-
+// and 64-step tiles, 2- and 8-element loads, and three wavefronts.
+constexpr int kDppTile = 32;
+constexpr int kDppVec = 4;
+constexpr int kWaves16 = 4;
 
 template <int N>
 struct TileCfg {
@@ -136,7 +133,7 @@ struct TileCfg {
   static constexpr int CH = 256 / N;                             // channels per block
   static constexpr int CPW = 64 / N;                             // channels per wavefront
   // Time steps per tile.
-  static constexpr int T = kDpp ? SCAN_DPP_T : (N >= 4 ? 32 : (N == 2 ? 16 : 8));
+  static constexpr int T = kDpp ? kDppTile : (N >= 4 ? 32 : (N == 2 ? 16 : 8));
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
   static constexpr int BS = T < 16 ? T : 16;                     // steps per readout block
   static constexpr int NB = T / BS;                              // readout blocks per tile
@@ -159,7 +156,7 @@ struct TileCfg {
   // Wavefronts per SIMD the register allocation aims at: for N = 16 the
   // block's LDS (39.5 KiB) allows four blocks per CU, so registers are held
   // to 128 per lane to match.
-  static constexpr int kWaves = N == 16 ? SCAN_WAVES16 : 1;
+  static constexpr int kWaves = N == 16 ? kWaves16 : 1;
 };
 
 // One block's view of the tensors and its fixed index math.
@@ -169,7 +166,7 @@ struct Block {
   static constexpr int CH = Cfg::CH, T = Cfg::T;
   // Storage elements per staging load: two on the DPP path (one load per
   // thread and tile), else one 16-byte vector.
-  static constexpr int VEC = Cfg::kDpp ? SCAN_DPP_VEC : 16 / static_cast<int>(sizeof(Tin));
+  static constexpr int VEC = Cfg::kDpp ? kDppVec : 16 / static_cast<int>(sizeof(Tin));
   static constexpr int WORDS = VEC * static_cast<int>(sizeof(Tin)) / 4;  // 32-bit words per load
   static constexpr int SEG = (T + VEC - 1) / VEC;   // loads per tile row
   static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
@@ -188,25 +185,15 @@ struct TileRegs {
   uint32_t z[Cfg::NB * Cfg::OPL];    // raw storage bits of z; converted in the readout
 };
 
-#ifndef SCAN_WSYNC
-#define SCAN_WSYNC 1
-#endif
-#ifndef SCAN_PIPE
-#define SCAN_PIPE 1
-#endif
 
 // Orders this wavefront's LDS accesses across lanes.  LDS instructions of one
 // wavefront execute in issue order, so a later load sees an earlier store of
 // any lane of the same wavefront; the fences keep the compiler from moving
 // LDS accesses across.
 __device__ __forceinline__ void wave_lds_sync() {
-#if SCAN_WSYNC
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#else
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#endif
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
@@ -568,7 +555,7 @@ scan_chunk_kernel(const ScanParams p) {
     if constexpr (SUMMARY) {
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) recur_block(par, bb, t0);
-    } else if constexpr (kDpp && SCAN_PIPE) {
+    } else if constexpr (kDpp) {
       // The next block's operands load between this block's partial reads
       // and the sums that consume them.
       DppOps o;

@@ -33,15 +33,6 @@
 
 #include "ssm_internal.h"
 
-#ifndef SSD_WPE
-#define SSD_WPE 2
-#endif
-#ifndef SSD_PREFETCH
-#define SSD_PREFETCH 1
-#endif
-#ifndef SSD_H0_WAIT
-#define SSD_H0_WAIT 1
-#endif
 
 namespace ssm {
 namespace {
@@ -120,7 +111,7 @@ __device__ __forceinline__ int tidx(int col, int t) {
 // dependent LDS reads, MFMAs and barriers.
 template <typename Tout, int N, bool HAS_Z, bool TRAP, int HPB>
 __global__ void __launch_bounds__(256 * HPB)
-__attribute__((amdgpu_waves_per_eu(HPB == 4 ? 4 : SSD_WPE, HPB == 4 ? 4 : SSD_WPE)))
+__attribute__((amdgpu_waves_per_eu(HPB == 4 ? 4 : 2, HPB == 4 ? 4 : 2)))
 ssd_chunk_kernel(const SsdParams p) {
   constexpr int NTH = 256 * HPB;  // threads per workgroup
   constexpr int NP = N + 24;      // padded LDS row of [.][n] arrays
@@ -220,12 +211,10 @@ ssd_chunk_kernel(const SsdParams p) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
   }
-#if SSD_H0_WAIT
   // Retire the initial-state loads here (s_waitcnt vmcnt(0)).  Otherwise they
   // may count as outstanding at the top of the chunk loop, and the first use
   // of S in every chunk would wait for all loads in flight, prefetches included.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-#endif
 
   // Staging jobs: a job covers steps (2 tp, 2 tp + 1) of one 8-column group;
   // the 8-column groups of a row go to consecutive lanes, so a wavefront's
@@ -367,9 +356,7 @@ ssd_chunk_kernel(const SsdParams p) {
     }
     stage_chunk(R, c0);
     __syncthreads();
-#if SSD_PREFETCH
     if (c0 + Q < L) load_chunk(c0 + Q, R);
-#endif
 
     // ---- M = mask(G^T) into LDS, for every head of the workgroup -----------
     // 12 tiles (si, ti): the lower-triangular tiles plus the two upper tiles
@@ -536,9 +523,6 @@ ssd_chunk_kernel(const SsdParams p) {
         if (c0 + t < L) st(gy + ybase, t * rx + pcol, yv[e]);
       }
     }
-#if !SSD_PREFETCH
-    if (c0 + Q < L) load_chunk(c0 + Q, R);
-#endif
   }
 
   if (p.h_last) {
