@@ -210,7 +210,9 @@ SSM_API int ssm_scan_bwd(const void *u, const void *delta, const float *A, const
  *   flags: 0, SSM_DT_SOFTPLUS, and (ssd_trap_chunked_fwd) SSM_LAM_SIGMOID.
  *   dt_bias: (nheads) float32, nullable; read only with SSM_DT_SOFTPLUS.
  * Supported: headdim = 64, dstate in {64, 128}, chunk = 64, any seqlen >= 0
- * (a ragged last chunk is masked).
+ * (a ragged last chunk is masked); nheads * headdim and ngroups * dstate below
+ * 2^25 (a chunk's rows are addressed with 32-bit offsets), else
+ * SSM_ERR_UNSUPPORTED.
  * Alignment: x, z, B, C, h0 and h_last must be 16-byte aligned (they are read
  * and written as 16-byte vectors); dt and y need their element alignment.
  */
@@ -247,8 +249,8 @@ SSM_API int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
  *
  * Layouts:
  *   x, z    : (batch, seqlen, nheads, headdim) bf16    z nullable
- *   dt      : (batch, seqlen, nheads) bf16  (already positive: any softplus
- *             and bias are applied by the caller)
+ *   dt      : (batch, seqlen, nheads) bf16  (the step; with SSM_DT_SOFTPLUS
+ *             the raw value, and the step is softplus(dt + dt_bias[h]))
  *   A, D    : (nheads) float32                          D nullable
  *   B, C    : (batch, seqlen, ngroups, dstate) bf16
  *   h0      : (batch, nheads, headdim, dstate) float32  nullable (initial state)
@@ -269,7 +271,8 @@ SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const
  * with the previous-token term zero before the first token.
  *   [Mamba-3 NKI], "How it works", Phase 0: alpha, gamma = lam dt and
  *     beta = (dt - gamma) alpha (lam after its sigmoid, dt after its
- *     softplus: both are applied by the caller); the step form is its Eq. 9;
+ *     softplus: applied by the caller, or by the kernel with the flags
+ *     SSM_LAM_SIGMOID and SSM_DT_SOFTPLUS); the step form is its Eq. 9;
  *   [Mamba-3 NKI], "Kernel details", mamba3_siso_ssd_kernel: chunked in the
  *     single-SSD form, the input of step s weighted by scale_s = gamma_s +
  *     dt_{s+1} (1 - lam_{s+1}) at later steps, plus a diagonal correction
