@@ -50,7 +50,32 @@ class Oracle:
         lib.oracle_softplus_grad_f64.restype = None
         lib.oracle_sigmoid_f64.argtypes = [i64] + [dp] * 2
         lib.oracle_sigmoid_f64.restype = None
+        lib.oracle_rope_bc_f64.argtypes = [i64] * 6 + [dp] * 8
+        lib.oracle_rope_bc_f64.restype = ctypes.c_int
         self.lib = lib
+
+    def rope_bc(self, dt, theta, B, C, angle0=None):
+        """Rotary step on B and C in float64. Returns (B_rot, C_rot, angle_last).
+
+        dt: (batch, L, H) (the step); theta: (batch, L, TH, N / 2) with TH 1 or H;
+        B, C: (batch, L, G, N); angle0, angle_last: (batch, H, N / 2);
+        B_rot, C_rot: (batch, L, H, N).
+        """
+        dt, theta, B, C, angle0 = map(f64, (dt, theta, B, C, angle0))
+        batch, L, H = dt.shape
+        G, N = B.shape[2], B.shape[3]
+        TH = theta.shape[2]
+        assert B.shape == (batch, L, G, N) and C.shape == B.shape
+        assert theta.shape == (batch, L, TH, N // 2)
+        assert angle0 is None or angle0.shape == (batch, H, N // 2)
+        b_rot = np.zeros((batch, L, H, N))
+        c_rot = np.zeros((batch, L, H, N))
+        last = np.zeros((batch, H, N // 2))
+        rc = self.lib.oracle_rope_bc_f64(batch, L, H, G, N, TH, _ptr(dt), _ptr(theta), _ptr(B), _ptr(C),
+                                         _ptr(angle0), _ptr(b_rot), _ptr(c_rot), _ptr(last))
+        if rc != 0:
+            raise ValueError("oracle_rope_bc_f64 rejected the shapes")
+        return b_rot, c_rot, last
 
     def softplus(self, raw, bias, inner):
         """Phase-0 step: softplus(raw + bias[(i / inner) % len(bias)]) elementwise
@@ -249,3 +274,13 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, state=None, dt_softplus=False, dt_b
     row = lambda a: None if a is None else f64(a)[:, None]
     y, h = ssd(row(x), row(dt), A, row(B), row(C), D, row(z), state, dt_softplus, dt_bias)
     return y[:, 0], h
+
+
+def rope_bc(dt, theta, B, C, angle0=None, dt_softplus=False, dt_bias=None):
+    """Rotary step on B and C in float64 with the default build; see
+    ``Oracle.rope_bc``.  dt_softplus: dt holds raw values and the step is
+    softplus(dt + dt_bias[h])."""
+    o = _load()
+    if dt_softplus:
+        dt = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
+    return o.rope_bc(dt, theta, B, C, angle0)

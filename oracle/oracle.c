@@ -350,3 +350,60 @@ void oracle_softplus_grad_f64(int64_t n, int64_t inner, int64_t nb, const double
 void oracle_sigmoid_f64(int64_t n, const double *raw, double *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = sigmoid(raw[i]);
 }
+
+/*
+ * Rotary step on B and C: the complex-valued state of Mamba-3.
+ *   "Mamba-3 NKI Kernels for AWS Neuron", section "How it works", Phase 1:
+ *   the angles are the negated running sum of dt * theta over the sequence,
+ *   and B and C are rotated by them; the same page lists a complex-valued
+ *   state via data-dependent RoPE among the Mamba-3 features.
+ * The page gives no formula for the rotation itself; read plainly:
+ *   phi_t[k] = angle0[k] - sum_{s <= t} dt_s * theta_s[k]   (k < dstate / 2,
+ *     per batch row and head; dt is the step, after any softplus),
+ *   and each state pair (k, k + dstate / 2), taken as the complex number
+ *   v1 + i v2, is multiplied by exp(i phi_t):
+ *     (v1, v2) -> (v1 cos phi - v2 sin phi, v1 sin phi + v2 cos phi),
+ *   B and C of step t with the same angle.  The rotated B and C differ from
+ *   head to head, so they are stored per head.
+ *   dt           : (batch, seqlen, nheads)
+ *   theta        : (batch, seqlen, theta_heads, dstate / 2), theta_heads 1
+ *                  (one set of angles for every head) or nheads
+ *   B, C         : (batch, seqlen, ngroups, dstate); head h reads group
+ *                  h / (nheads / ngroups)
+ *   angle0       : (batch, nheads, dstate / 2) angle before the first step
+ *                  (nullable: 0)
+ *   B_rot, C_rot : (batch, seqlen, nheads, dstate)
+ *   angle_last   : (batch, nheads, dstate / 2) angle after the last step
+ */
+int oracle_rope_bc_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ngroups, int64_t dstate,
+                       int64_t theta_heads, const double *dt, const double *theta, const double *B,
+                       const double *C, const double *angle0, double *B_rot, double *C_rot,
+                       double *angle_last) {
+  if (batch < 0 || seqlen < 0 || nheads < 1 || ngroups < 1 || nheads % ngroups != 0 || dstate < 2 ||
+      dstate % 2 != 0 || (theta_heads != 1 && theta_heads != nheads))
+    return -1;
+  const int64_t half = dstate / 2, hpg = nheads / ngroups;
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t h = 0; h < nheads; ++h) {
+      const int64_t g = h / hpg;
+      const int64_t th = theta_heads == 1 ? 0 : h;
+      for (int64_t k = 0; k < half; ++k) {
+        double phi = angle0 ? angle0[(b * nheads + h) * half + k] : 0.0;
+        for (int64_t t = 0; t < seqlen; ++t) {
+          phi -= dt[(b * seqlen + t) * nheads + h] * theta[((b * seqlen + t) * theta_heads + th) * half + k];
+          const double c = cos(phi), s = sin(phi);
+          const int64_t src = ((b * seqlen + t) * ngroups + g) * dstate;
+          const int64_t dst = ((b * seqlen + t) * nheads + h) * dstate;
+          const double b1 = B[src + k], b2 = B[src + k + half];
+          const double c1 = C[src + k], c2 = C[src + k + half];
+          B_rot[dst + k] = b1 * c - b2 * s;
+          B_rot[dst + k + half] = b1 * s + b2 * c;
+          C_rot[dst + k] = c1 * c - c2 * s;
+          C_rot[dst + k + half] = c1 * s + c2 * c;
+        }
+        angle_last[(b * nheads + h) * half + k] = phi;
+      }
+    }
+  }
+  return 0;
+}

@@ -20,6 +20,9 @@ Definitions followed (page titles and sections):
   * "Mamba-3 NKI Kernels for AWS Neuron", section "How it works", Phase 0: the
     raw step goes through softplus(dt + dt_bias), the raw trapezoid weight
     through a sigmoid.
+  * same page and section, Phase 1: the angles are the negated running sum of
+    dt * theta and rotate B and C (the complex-valued state of its Mamba-3
+    feature list).
 """
 from __future__ import annotations
 
@@ -491,6 +494,101 @@ def check_phase0_sigmoid_and_softplus_grad(orc):
     _close(got, g * fd, rtol=1e-8, what="softplus chain rule vs finite differences")
 
 
+# --------------------------------------------------------------------------
+# Rotary step on B and C (Mamba-3 complex-valued state)
+# --------------------------------------------------------------------------
+
+def check_rope_closed_form(orc):
+    """Constant step c and a constant theta w per (head, pair): after step t
+    the angle is a0 - (t + 1) c w, so a unit vector on the first member of
+    pair k (k and k + N/2) turns into (cos phi, sin phi) on the pair and one
+    on the second member into (-sin phi, cos phi); C (here 3 B) the same, and
+    angle_last = a0 - L c w.  Per-head thetas, two groups with distinct
+    amplitudes (head h reads group h / (H / G))."""
+    batch, L, H, G, N = 1, 7, 4, 2, 6
+    half = N // 2
+    c = 0.3
+    rng = np.random.default_rng(81)
+    w = rng.uniform(-2.0, 2.0, (H, half))
+    a0 = rng.uniform(-1.0, 1.0, (batch, H, half))
+    dt = np.full((batch, L, H), c)
+    theta = np.broadcast_to(w[None, None], (batch, L, H, half)).copy()
+    for k in range(half):
+        for second in (False, True):
+            B = np.zeros((batch, L, G, N))
+            for g in range(G):
+                B[:, :, g, k + (half if second else 0)] = g + 1.0
+            br, cr, last = orc.rope_bc(dt, theta, B, 3.0 * B, a0)
+            for h in range(H):
+                amp = h // (H // G) + 1.0
+                for t in range(L):
+                    phi = a0[0, h, k] - (t + 1) * c * w[h, k]
+                    want = np.zeros(N)
+                    if second:
+                        want[k], want[k + half] = -math.sin(phi), math.cos(phi)
+                    else:
+                        want[k], want[k + half] = math.cos(phi), math.sin(phi)
+                    _close(br[0, t, h], amp * want, what=f"rope B (k{k} second={second} h{h} t{t})")
+                    _close(cr[0, t, h], 3.0 * amp * want, what=f"rope C (k{k} second={second} h{h} t{t})")
+            _close(last, a0 - L * c * w[None], what="rope angle_last")
+
+
+def check_rope_complex_state(orc):
+    """Rotating B and C turns the real SSD into the complex-state recurrence of
+    Mamba-3.  With each pair (k, k + N/2) of B and C read as a complex number
+    b, c:  h_t = exp(dt_t A) exp(i dt_t theta_t) h_{t-1} + dt_t x_t b_t and
+    y_t = Re(sum_k conj(c_t,k) h_t,k).  That loop, on the unrotated B and C,
+    must equal the oracle's SSD (one group per head) on the oracle's rotated
+    B and C."""
+    rng = np.random.default_rng(82)
+    batch, L, H, P, N = 2, 9, 3, 2, 4
+    half = N // 2
+    x, dt, A, B, C, _, _ = _rand_ssd(rng, batch, L, H, P, N, 1)
+    theta = rng.uniform(-3.0, 3.0, (batch, L, H, half))
+    br, cr, _ = orc.rope_bc(dt, theta, B, C)
+    y, _ = orc.ssd(x, dt, A, br, cr)
+    for b in range(batch):
+        for h in range(H):
+            hc = np.zeros((P, half), dtype=complex)
+            for t in range(L):
+                bz = B[b, t, 0, :half] + 1j * B[b, t, 0, half:]
+                cz = C[b, t, 0, :half] + 1j * C[b, t, 0, half:]
+                rot = np.exp(dt[b, t, h] * A[h]) * np.exp(1j * dt[b, t, h] * theta[b, t, h])
+                hc = rot[None, :] * hc + dt[b, t, h] * x[b, t, h][:, None] * bz[None, :]
+                _close(y[b, t, h], np.real(hc @ np.conj(cz)), rtol=1e-11, what=f"complex state (b{b} h{h} t{t})")
+
+
+def check_rope_chaining_and_identities(orc):
+    """Two calls, the second starting from the first's angle_last, equal one
+    call over the whole sequence; one set of angles for all heads
+    (theta_heads = 1) equals the same angles given to every head; theta = 0
+    copies B and C to every head of their group unchanged."""
+    rng = np.random.default_rng(83)
+    batch, L, H, G, N = 2, 11, 4, 2, 8
+    half = N // 2
+    dt = np.exp(rng.uniform(math.log(1e-2), math.log(0.5), (batch, L, H)))
+    theta = rng.uniform(-3.0, 3.0, (batch, L, H, half))
+    B = rng.standard_normal((batch, L, G, N))
+    C = rng.standard_normal((batch, L, G, N))
+    a0 = rng.uniform(-2.0, 2.0, (batch, H, half))
+    full = orc.rope_bc(dt, theta, B, C, a0)
+    m = 5
+    first = orc.rope_bc(dt[:, :m], theta[:, :m], B[:, :m], C[:, :m], a0)
+    second = orc.rope_bc(dt[:, m:], theta[:, m:], B[:, m:], C[:, m:], first[2])
+    _close(np.concatenate([first[0], second[0]], axis=1), full[0], what="rope chained B")
+    _close(np.concatenate([first[1], second[1]], axis=1), full[1], what="rope chained C")
+    _close(second[2], full[2], what="rope chained angle_last")
+    shared = theta[:, :, :1]
+    one = orc.rope_bc(dt, shared, B, C, a0)
+    every = orc.rope_bc(dt, np.repeat(shared, H, axis=2), B, C, a0)
+    for a, b_, what in zip(one, every, ("B", "C", "angle_last")):
+        _close(a, b_, rtol=0.0, what=f"rope shared theta {what}")
+    br, cr, last = orc.rope_bc(dt, np.zeros_like(theta), B, C, a0 * 0.0)
+    _close(br, np.repeat(B, H // G, axis=2), rtol=0.0, what="rope theta = 0, B")
+    _close(cr, np.repeat(C, H // G, axis=2), rtol=0.0, what="rope theta = 0, C")
+    _close(last, np.zeros_like(last), rtol=0.0, what="rope theta = 0, angle_last")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -508,4 +606,7 @@ ALL_CHECKS = [
     check_ssd_trap_single_ssd_form,
     check_phase0_softplus,
     check_phase0_sigmoid_and_softplus_grad,
+    check_rope_closed_form,
+    check_rope_complex_state,
+    check_rope_chaining_and_identities,
 ]

@@ -4,7 +4,9 @@ the definition: the decay and its sign, the dt on the input, the readout order,
 B versus C, the D skip, the gate and its order, the group index, the B/C
 layout, the initial state and the final state; and each term of the backward
 (the adjoint's decay, the state each gradient uses, the gate derivative, the
-upstream state gradient)."""
+upstream state gradient); and the rotary step on B and C (the angle's sign
+and running sum, the rotation, the pairing of states, the group, the per-head
+angles, the starting angle, C's rotation)."""
 import os
 import subprocess
 
@@ -61,6 +63,26 @@ MUTANTS = [
     ("softplus_bias_index", [("bias[(i / inner) % nb]", "bias[i % nb]")]),
     ("softplus_grad_sign", [("grad_in[i] * sigmoid(raw[i] + bv)", "grad_in[i] * sigmoid(-(raw[i] + bv))")]),
     ("sigmoid_sign", [("return 1.0 / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(v));")]),
+    ("rope_angle_sign", [("phi -= dt[(b * seqlen + t) * nheads + h]", "phi += dt[(b * seqlen + t) * nheads + h]")]),
+    ("rope_exclusive_sum", [(
+        "phi -= dt[(b * seqlen + t) * nheads + h] * theta[((b * seqlen + t) * theta_heads + th) * half + k];\n"
+        "          const double c = cos(phi), s = sin(phi);",
+        "const double c = cos(phi), s = sin(phi);\n"
+        "          phi -= dt[(b * seqlen + t) * nheads + h] * theta[((b * seqlen + t) * theta_heads + th) * half + k];")]),
+    ("rope_rotation_sign", [("B_rot[dst + k + half] = b1 * s + b2 * c;", "B_rot[dst + k + half] = -b1 * s + b2 * c;")]),
+    ("rope_pairs_adjacent", [("const double b1 = B[src + k], b2 = B[src + k + half];",
+                              "const double b1 = B[src + 2 * k], b2 = B[src + 2 * k + 1];"),
+                             ("const double c1 = C[src + k], c2 = C[src + k + half];",
+                              "const double c1 = C[src + 2 * k], c2 = C[src + 2 * k + 1];"),
+                             ("B_rot[dst + k] = b1", "B_rot[dst + 2 * k] = b1"),
+                             ("B_rot[dst + k + half] = b1", "B_rot[dst + 2 * k + 1] = b1"),
+                             ("C_rot[dst + k] = c1", "C_rot[dst + 2 * k] = c1"),
+                             ("C_rot[dst + k + half] = c1", "C_rot[dst + 2 * k + 1] = c1")]),
+    ("rope_group_index", [("const int64_t g = h / hpg;", "const int64_t g = h % ngroups;")]),
+    ("rope_theta_head", [("const int64_t th = theta_heads == 1 ? 0 : h;", "const int64_t th = 0;")]),
+    ("rope_angle0_ignored", [("double phi = angle0 ? angle0[(b * nheads + h) * half + k] : 0.0;", "double phi = 0.0;")]),
+    ("rope_c_unrotated", [("C_rot[dst + k] = c1 * c - c2 * s;", "C_rot[dst + k] = c1;"),
+                          ("C_rot[dst + k + half] = c1 * s + c2 * c;", "C_rot[dst + k + half] = c2;")]),
 ]
 
 
