@@ -303,8 +303,9 @@ def main():
 
 
 def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs):
-    """The scan backward on the long-prefill and large-channel workloads, and
-    the trapezoidal SSD on the SSD workload's shapes."""
+    """The scan backward on the long-prefill and large-channel workloads; the
+    trapezoidal SSD, the rotary step on B and C and the SSD on the rotated
+    (per-head) B and C, on the SSD workload's shapes."""
     import torch
     from state_space_model_ssm_amd.synth import make_lam
     out = {}
@@ -330,6 +331,26 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
     nbytes = w.metric_bytes() + w.hlast_bytes() + lam.numel() * 2
     out["ssd_trap_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
                                               "hbm_GB/s_with_h_last": round(nbytes / ms / 1e6, 1)}
+    # The rotary step on the same shapes (one set of angles for all heads),
+    # then the SSD on the rotated, per-head B and C.
+    from state_space_model_ssm_amd.synth import make_theta
+    theta = make_theta((w.batch, w.seqlen, 1, w.dstate // 2), seed=11, dtype="bf16").to(dev)
+    rows = w.batch * w.seqlen
+    br = torch.empty((w.batch, w.seqlen, w.nheads, w.dstate), dtype=torch.bfloat16, device=dev)
+    cr = torch.empty_like(br)
+    ang = torch.empty((w.batch, w.nheads, w.dstate // 2), dtype=torch.float32, device=dev)
+    ms, _ = time_calls(lambda: ssm.rope_bc(d["dt"], theta, d["B"], d["C"], B_rot=br, C_rot=cr, angle_last=ang,
+                                           stream=stream), 50, 5)
+    # Bytes: dt, theta, B and C read once; B_rot, C_rot and the angles written.
+    nbytes = (d["dt"].numel() + theta.numel() + d["B"].numel() + d["C"].numel()) * 2 + \
+        (br.numel() + cr.numel()) * 2 + ang.numel() * 4
+    out["rope_bc_32x256_h32n128_bf16"] = {"ms": round(ms, 5), "hbm_GB/s": round(nbytes / ms / 1e6, 1),
+                                          "hbm_frac": round(nbytes / ms / 1e6 / 8000.0, 4),
+                                          "rows": rows}
+    ms, _ = time_calls(lambda: ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], y=y,
+                                                   h_last=h, stream=stream), 50, 5)
+    out["ssd_rotated_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                                 "ngroups": w.nheads}
     return out
 
 

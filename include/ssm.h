@@ -291,6 +291,62 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
                          void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Rotary step on B and C (Mamba-3 complex-valued state)                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sizes of one rotary step.
+ *   batch, seqlen (L), nheads (H), ngroups (G divides H; head h reads group
+ *   h / (H / G)), dstate (N: a power of two from 2 to 256),
+ *   theta_heads: 1 (one set of angles for every head) or nheads;
+ *   in_dtype: dt, theta, B, C; out_dtype: B_rot, C_rot;
+ *   flags: 0 or SSM_DT_SOFTPLUS (dt_bias: (nheads) float32, nullable);
+ *   reserved: must be 0.
+ */
+typedef struct {
+  int64_t batch, seqlen, nheads, ngroups, dstate, theta_heads;
+  int32_t in_dtype, out_dtype;
+  int32_t flags;
+  int32_t reserved;
+  const float *dt_bias;
+} ssm_rope_dims_t;
+
+/*
+ * Rotary step on B and C: for every batch row b, head h and state pair
+ * k < N/2 (states k and k + N/2, read as the complex number B[k] + i B[k+N/2])
+ *   phi_t[k]   = angle0[b,h,k] - sum_{s <= t} dt_s[b,h] * theta_s[b,h',k]
+ *   B_rot_t[k] = B_t[k] cos phi_t[k] - B_t[k + N/2] sin phi_t[k]
+ *   B_rot_t[k + N/2] = B_t[k] sin phi_t[k] + B_t[k + N/2] cos phi_t[k]
+ * and C alike with the same angle (h' = h, or 0 when theta_heads = 1).
+ *   [Mamba-3 NKI], "How it works", Phase 1: the angles are the negated
+ *     running sum of dt * theta, and B and C are rotated by them; the page's
+ *     list of Mamba-3 features names this a complex-valued state driven by
+ *     data-dependent RoPE.  The page gives no formula for the rotation; the
+ *     pairing (k, k + N/2) and the direction are this library's reading.
+ * The rotated B and C feed ssd_chunked_fwd / ssd_trap_chunked_fwd with
+ * ngroups = nheads; chained over a sequence split in pieces (prefill then
+ * decode), angle_last of one call is angle0 of the next.
+ *
+ * Layouts:
+ *   dt         : (batch, seqlen, nheads) in_dtype (the step; with
+ *                SSM_DT_SOFTPLUS the raw value, the step being
+ *                softplus(dt + dt_bias[h]))
+ *   theta      : (batch, seqlen, theta_heads, dstate / 2) in_dtype
+ *   B, C       : (batch, seqlen, ngroups, dstate) in_dtype
+ *   angle0     : (batch, nheads, dstate / 2) float32, nullable (zero)
+ *   B_rot, C_rot: (batch, seqlen, nheads, dstate) out_dtype
+ *   angle_last : (batch, nheads, dstate / 2) float32, nullable; may be
+ *                exactly angle0 (updated in place)
+ * The running angle is summed in float64 inside the call; angle0 and
+ * angle_last are float32.  Pointers need their element alignment; outputs
+ * must not overlap inputs or each other (angle_last == angle0 excepted).
+ * Supported: any batch, seqlen >= 0 with batch * nheads < 2^31.
+ */
+SSM_API int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,
+                        const float *angle0, void *B_rot, void *C_rot, float *angle_last,
+                        const ssm_rope_dims_t *dims, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Single-token decode steps (state cache updated in place)                  */
 /* ------------------------------------------------------------------------ */
 

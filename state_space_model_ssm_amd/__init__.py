@@ -18,6 +18,7 @@ from typing import Optional
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
     "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
+    "rope_bc", "RopeDims",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
@@ -70,6 +71,13 @@ class SsdStepDims(ctypes.Structure):
                 ("dt_bias", ctypes.c_void_p)]
 
 
+class RopeDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("dstate", ctypes.c_int64), ("theta_heads", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("dt_bias", ctypes.c_void_p)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -104,6 +112,8 @@ def lib():
         L.ssm_scan_step.restype = i32
         L.ssd_step.argtypes = [vp] * 9 + [ctypes.POINTER(SsdStepDims), vp]
         L.ssd_step.restype = i32
+        L.ssm_rope_bc.argtypes = [vp] * 8 + [ctypes.POINTER(RopeDims), vp]
+        L.ssm_rope_bc.restype = i32
         L.ssm_status_string.argtypes = [i32]
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -440,3 +450,45 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, s
     _check(lib().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                           _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
     return y
+
+
+def rope_bc(dt, theta, B, C, *, angle0=None, out_dtype=None, B_rot=None, C_rot=None, angle_last=None,
+            return_angle_last: bool = True, stream=None, dt_softplus: bool = False, dt_bias=None):
+    """Rotary step on B and C (``ssm_rope_bc``). Returns ``(B_rot, C_rot,
+    angle_last)`` (angle_last None when not asked for).
+
+    dt: (batch, L, H); theta: (batch, L, TH, N / 2) with TH 1 or H;
+    B, C: (batch, L, G, N), all of one dtype; angle0, angle_last:
+    (batch, H, N / 2) float32 (angle_last may be angle0, updated in place);
+    B_rot, C_rot: (batch, L, H, N) in out_dtype (default: the input dtype),
+    ready for the SSD with ngroups = H.
+    """
+    torch = _torch()
+    in_code = _dtype_code(B.dtype)
+    out_dt = B.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("dt", dt), ("theta", theta), ("C", C)):
+        if t.dtype != B.dtype:
+            raise TypeError(f"{name} must have dtype {B.dtype}")
+    batch, L, G, N = B.shape
+    H = dt.shape[2]
+    TH = theta.shape[2]
+    if dt.shape != (batch, L, H) or C.shape != B.shape or N % 2 != 0:
+        raise ValueError("dt must be (batch, L, H), C shaped like B, dstate even")
+    if theta.shape != (batch, L, TH, N // 2):
+        raise ValueError("theta must be (batch, L, 1 or H, dstate / 2)")
+    for name, t in (("angle0", angle0), ("angle_last", angle_last)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (batch, H, N // 2)):
+            raise ValueError(f"{name} must be float32 (batch, nheads, dstate / 2)")
+    if B_rot is None:
+        B_rot = torch.empty((batch, L, H, N), dtype=out_dt, device=B.device)
+    if C_rot is None:
+        C_rot = torch.empty((batch, L, H, N), dtype=out_dt, device=B.device)
+    if angle_last is None and return_angle_last:
+        angle_last = torch.empty((batch, H, N // 2), dtype=torch.float32, device=B.device)
+    dims = RopeDims(batch=batch, seqlen=L, nheads=H, ngroups=G, dstate=N, theta_heads=TH, in_dtype=in_code,
+                    out_dtype=out_code, flags=0, reserved=0)
+    _phase0(dims, H, dt_softplus, dt_bias)
+    _check(lib().ssm_rope_bc(_ptr(dt), _ptr(theta), _ptr(B), _ptr(C), _ptr(angle0), _ptr(B_rot), _ptr(C_rot),
+                             _ptr(angle_last), ctypes.byref(dims), _stream(stream)))
+    return B_rot, C_rot, angle_last

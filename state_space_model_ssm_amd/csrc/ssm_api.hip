@@ -597,6 +597,75 @@ int ssd_step(const void *x, const void *dt, const float *A, const void *B, const
 }
 
 // ---------------------------------------------------------------------------
+// Rotary step on B and C
+// ---------------------------------------------------------------------------
+
+int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C, const float *angle0,
+                void *B_rot, void *C_rot, float *angle_last, const ssm_rope_dims_t *dims, void *stream) {
+  if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+  const ssm_rope_dims_t &d = *dims;
+  if (d.batch < 0 || d.seqlen < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (d.nheads < 1 || d.ngroups < 1) return fail(SSM_ERR_SHAPE, "nheads and ngroups must be >= 1");
+  if (d.nheads % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide nheads");
+  if (d.theta_heads != 1 && d.theta_heads != d.nheads) return fail(SSM_ERR_SHAPE, "theta_heads must be 1 or nheads");
+  if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
+  if (d.reserved != 0) return fail(SSM_ERR_SHAPE, "reserved must be 0");
+  const int rc = check_dt_flags(d.flags, SSM_DT_SOFTPLUS, d.dt_bias);
+  if (rc != SSM_OK) return rc;
+  if (d.dstate < 2 || !step_dstate_ok(d.dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two from 2 to 256)", (long long)d.dstate);
+  if (d.batch > 0 && d.nheads > kMaxGridX / d.batch) return fail(SSM_ERR_UNSUPPORTED, "batch * nheads exceeds the grid limit");
+  const int64_t rows = d.batch * d.seqlen;
+  const int64_t half = d.dstate / 2;
+  if (rows > 0 && (!dt || !theta || !B || !C || !B_rot || !C_rot))
+    return fail(SSM_ERR_NULL, "dt, theta, B, C, B_rot and C_rot are required");
+  const size_t ei = dtype_size(d.in_dtype), eo = dtype_size(d.out_dtype);
+  if (!aligned(dt, ei) || !aligned(theta, ei) || !aligned(B, ei) || !aligned(C, ei))
+    return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
+  if (!aligned(B_rot, eo) || !aligned(C_rot, eo)) return fail(SSM_ERR_ALIGN, "B_rot and C_rot must be aligned to %zu bytes", eo);
+  if (!aligned(angle0, 4) || !aligned(angle_last, 4)) return fail(SSM_ERR_ALIGN, "angles must be 4-byte aligned");
+  const int64_t n_ang = d.batch * d.nheads * half;
+  const Span ins[] = {{dt, rows * d.nheads * ei},
+                      {theta, rows * d.theta_heads * half * ei},
+                      {B, rows * d.ngroups * d.dstate * ei},
+                      {C, rows * d.ngroups * d.dstate * ei},
+                      {d.dt_bias, d.nheads * 4ull},
+                      {angle0, n_ang * 4ull}};
+  const Span sb{B_rot, rows * d.nheads * d.dstate * eo}, sc{C_rot, rows * d.nheads * d.dstate * eo};
+  const Span sa{angle_last, n_ang * 4ull};
+  for (const Span &s : ins) {
+    if (overlap(s, sb) || overlap(s, sc)) return fail(SSM_ERR_SHAPE, "B_rot or C_rot overlaps an input");
+    if (s.p != angle0 && overlap(s, sa)) return fail(SSM_ERR_SHAPE, "angle_last overlaps an input");
+  }
+  if (angle_last != nullptr && angle0 != nullptr && angle_last != angle0 && overlap(sa, Span{angle0, n_ang * 4ull}))
+    return fail(SSM_ERR_SHAPE, "angle_last overlaps angle0 without being it");
+  if (overlap(sb, sc) || overlap(sb, sa) || overlap(sc, sa)) return fail(SSM_ERR_SHAPE, "outputs overlap each other");
+  if (d.batch * d.nheads == 0 || (rows == 0 && angle_last == nullptr)) return ok();
+
+  ssm::RopeParams p{};
+  p.dt = dt;
+  p.theta = theta;
+  p.B = B;
+  p.C = C;
+  p.angle0 = angle0;
+  p.dt_bias = d.dt_bias;
+  p.B_rot = B_rot;
+  p.C_rot = C_rot;
+  p.angle_last = angle_last;
+  p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.dstate = static_cast<int32_t>(d.dstate);
+  p.batch = d.batch;
+  p.seqlen = d.seqlen;
+  p.nheads = d.nheads;
+  p.ngroups = d.ngroups;
+  p.theta_heads = d.theta_heads;
+  const hipError_t e = ssm::launch_rope(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "rope launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Diagnostics
 // ---------------------------------------------------------------------------
 
@@ -616,6 +685,6 @@ const char *ssm_status_string(int status) {
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
 
-int ssm_version(void) { return 300; }
+int ssm_version(void) { return 400; }
 
 }  // extern "C"

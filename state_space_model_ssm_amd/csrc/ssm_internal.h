@@ -113,4 +113,17 @@ struct StepParams {
 
 hipError_t launch_step(const StepParams &p, int per_head, int in_bf16, int out_bf16, hipStream_t stream);
 
+// Rotary step on B and C (Mamba-3 Phase 1).
+struct RopeParams {
+  const void *dt, *theta, *B, *C;     // in_dtype
+  const float *angle0, *dt_bias;      // nullable
+  void *B_rot, *C_rot;                // out_dtype
+  float *angle_last;                  // nullable; may be angle0 itself
+  int32_t dt_softplus;
+  int32_t dstate;
+  int64_t batch, seqlen, nheads, ngroups, theta_heads;
+};
+
+hipError_t launch_rope(const RopeParams &p, int in_bf16, int out_bf16, hipStream_t stream);
+
 }  // namespace ssm

@@ -135,6 +135,15 @@ def make_lam(shape, seed: int) -> torch.Tensor:
     return _store(v, "bf16")
 
 
+def make_theta(shape, seed: int, dtype: str = "bf16", scale: float = 1.0) -> torch.Tensor:
+    """Seeded rotary angle rates theta ~ N(0, scale^2) of ``shape`` (batch, time,
+    1 or heads, dstate / 2), stored in ``dtype``: the Phase-1 input of "Mamba-3
+    NKI Kernels for AWS Neuron", section "How it works" (the pages give no
+    distribution for it)."""
+    rng = np.random.default_rng(seed)
+    return _store(scale * rng.standard_normal(shape), dtype)
+
+
 def make_raw_step(shape, nbias: int, seed: int, dtype: str = "f32", scale: float = 0.5):
     """Seeded raw step values and their bias for the fused Phase-0 step map
     softplus(raw + bias): raw ~ N(0, scale^2) of ``shape`` stored in ``dtype``,

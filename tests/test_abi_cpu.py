@@ -45,14 +45,14 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 13, declared
+    assert len(declared) == 14, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
 
 
 def test_version_and_status_strings():
-    assert ssm.version() == 300
+    assert ssm.version() == 400
     for code, name in ssm.STATUS.items():
         assert ssm.status_string(code) == name
     assert ssm.status_string(-99) == "SSM_ERR_UNKNOWN"
@@ -336,3 +336,45 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ssm, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         ssm.lib()
+
+
+def _ropedims(**kw):
+    base = dict(batch=2, seqlen=64, nheads=4, ngroups=1, dstate=16, theta_heads=1, in_dtype=1, out_dtype=1,
+                flags=0, reserved=0)
+    base.update(kw)
+    return ssm.RopeDims(**base)
+
+
+def _rope(dims, dt=FAKE, theta=FAKE + 0x100000, B=FAKE + 0x200000, C=FAKE + 0x300000, angle0=None,
+          B_rot=FAKE + 0x10000000, C_rot=FAKE + 0x18000000, angle_last=None):
+    return ssm.lib().ssm_rope_bc(dt, theta, B, C, angle0, B_rot, C_rot, angle_last, ctypes.byref(dims), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(seqlen=-1), -2), (dict(nheads=0), -2), (dict(nheads=6, ngroups=4), -2),
+    (dict(theta_heads=3), -2), (dict(theta_heads=0), -2), (dict(dstate=12), -5), (dict(dstate=1), -5),
+    (dict(dstate=512), -5), (dict(dstate=0), -5), (dict(in_dtype=5), -3), (dict(out_dtype=-1), -3),
+    (dict(flags=2), -2), (dict(reserved=1), -2), (dict(dt_bias=FAKE + 0x800000), -2),
+])
+def test_rope_rejects_bad_dims(kw, code):
+    assert _rope(_ropedims(**kw)) == code, ssm.last_error()
+
+
+def test_rope_rejects_null_misaligned_overlap():
+    d = _ropedims()
+    assert _rope(d, dt=None) == -1
+    assert _rope(d, theta=None) == -1
+    assert _rope(d, C_rot=None) == -1
+    assert _rope(d, dt=FAKE + 1) == -4                          # bf16 needs 2-byte alignment
+    assert _rope(_ropedims(in_dtype=0), B=FAKE + 0x200002) == -4  # float32 needs 4
+    assert _rope(d, angle0=FAKE + 0x400002) == -4
+    assert _rope(d, B_rot=FAKE + 0x200000) == -2                # B_rot is B
+    assert _rope(d, C_rot=FAKE + 0x10000000 + 64) == -2         # C_rot inside B_rot
+    assert _rope(d, angle_last=FAKE + 0x10000000) == -2         # angle_last inside B_rot
+    assert _rope(d, angle_last=FAKE + 0x100000 + 16) == -2      # angle_last inside theta
+    assert _rope(d, angle0=FAKE + 0x400000, angle_last=FAKE + 0x400000 + 8) == -2  # overlaps angle0, not it
+
+
+def test_rope_empty_inputs_launch_nothing():
+    assert _rope(_ropedims(batch=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
+    assert _rope(_ropedims(seqlen=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0

@@ -1,0 +1,158 @@
+"""Parity of the rotary step on B and C (``ssm_rope_bc``) with the float64
+CPU oracle, alone and feeding the chunked SSD.
+
+Bar: max|out - ref| / max|ref| <= 1e-5 when every stored tensor is float32,
+<= 2e-2 when any is bfloat16, for B_rot, C_rot, angle_last and the SSD's y
+and h_last.  Outputs are NaN-poisoned before each call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import state_space_model_ssm_amd as ssm
+from state_space_model_ssm_amd.synth import (WORKLOADS, SsdShape, make_lam, make_raw_step, make_ssd_inputs,
+                                             make_state, make_theta)
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-5, 2e-2
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+def rel_err(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if want.size == 0:
+        return 0.0
+    diff = np.abs(got - want)
+    if np.isnan(diff).any():
+        return float("inf")
+    scale = float(np.max(np.abs(want)))
+    return float(np.max(diff)) / (scale if scale > 0 else 1.0)
+
+
+def _inputs(batch, L, H, G, N, TH, dtype, seed, theta_scale):
+    rng = np.random.default_rng(seed)
+    dt = np.logaddexp(0.0, rng.standard_normal((batch, L, H)) - 4.6)  # softplus: steps around 0.01
+    B = rng.standard_normal((batch, L, G, N)) / np.sqrt(N)
+    C = rng.standard_normal((batch, L, G, N)) / np.sqrt(N)
+    cast = lambda a: torch.from_numpy(a).to(DT[dtype])
+    theta = make_theta((batch, L, TH, N // 2), seed + 1, dtype, theta_scale)
+    angle0 = torch.from_numpy(rng.uniform(-4.0, 4.0, (batch, H, N // 2)).astype(np.float32))
+    return cast(dt), theta, cast(B), cast(C), angle0
+
+
+def _run(dt, theta, B, C, angle0, out_dtype, **kw):
+    batch, L, G, N = B.shape
+    H = dt.shape[2]
+    br = torch.full((batch, L, H, N), float("nan"), dtype=out_dtype, device="cuda")
+    cr = torch.full_like(br, float("nan"))
+    al = torch.full((batch, H, N // 2), float("nan"), dtype=torch.float32, device="cuda")
+    a0 = None if angle0 is None else angle0.cuda()
+    ssm.rope_bc(dt.cuda(), theta.cuda(), B.cuda(), C.cuda(), angle0=a0, out_dtype=out_dtype, B_rot=br,
+                C_rot=cr, angle_last=al, **kw)
+    torch.cuda.synchronize()
+    return br.float().cpu(), cr.float().cpu(), al.cpu()
+
+
+# (batch, L, H, G, N, theta_heads, in dtype, out dtype, angle0, theta scale, seed)
+CASES = [
+    (2, 100, 4, 2, 16, 4, "f32", "f32", True, 20.0, 1),     # 64 time segments of 2 steps, ragged
+    (1, 1000, 2, 1, 128, 1, "f32", "f32", False, 20.0, 2),  # 8 segments of 125 steps
+    (2, 37, 3, 3, 2, 3, "f32", "f32", True, 5.0, 3),        # one pair, most segments empty
+    (1, 5, 2, 1, 256, 2, "f32", "bf16", True, 5.0, 4),      # 128 pairs, 4 segments
+    (2, 256, 8, 1, 64, 1, "bf16", "bf16", False, 1.0, 5),
+    (1, 300, 4, 2, 32, 4, "bf16", "f32", True, 10.0, 6),
+    (1, 0, 2, 1, 16, 1, "f32", "f32", True, 1.0, 7),        # empty sequence: angle_last = angle0
+    (1, 4096, 2, 1, 16, 2, "f32", "f32", True, 30.0, 8),    # angles reach ~10^3 rad
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}l{}h{}g{}n{}th{}_{}_{}_a0{}".format(*c[:9]))
+def test_rope_matches_oracle(case):
+    batch, L, H, G, N, TH, din, dout, with_a0, scale, seed = case
+    dt, theta, B, C, angle0 = _inputs(batch, L, H, G, N, TH, din, seed, scale)
+    a0 = angle0 if with_a0 else None
+    br, cr, al = _run(dt, theta, B, C, a0, DT[dout])
+    rb, rc, ra = oracle.rope_bc(dt, theta, B, C, a0)
+    tol = TOL_F32 if din == dout == "f32" else TOL_BF16
+    assert rel_err(br, rb) <= tol and rel_err(cr, rc) <= tol, (rel_err(br, rb), rel_err(cr, rc))
+    assert rel_err(al, ra) <= TOL_F32, rel_err(al, ra)
+
+
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_rope_dt_softplus(with_bias):
+    batch, L, H, N = 2, 130, 4, 32
+    raw, bias = make_raw_step((batch, L, H), H, seed=41, dtype="f32")
+    _, theta, B, C, angle0 = _inputs(batch, L, H, 1, N, H, "f32", 42, 10.0)
+    bias = bias if with_bias else None
+    br, cr, al = _run(raw, theta, B, C, angle0, torch.float32, dt_softplus=True,
+                      dt_bias=None if bias is None else bias.cuda())
+    rb, rc, ra = oracle.rope_bc(raw, theta, B, C, angle0, dt_softplus=True, dt_bias=bias)
+    assert max(rel_err(br, rb), rel_err(cr, rc), rel_err(al, ra)) <= TOL_F32
+
+
+def test_rope_chained_in_place():
+    """A sequence rotated in three pieces, each call taking the angle its
+    predecessor left in the same buffer, equals one call over the whole."""
+    batch, L, H, G, N = 2, 200, 4, 1, 64
+    dt, theta, B, C, angle0 = _inputs(batch, L, H, G, N, 1, "f32", 51, 20.0)
+    rb, rc, ra = oracle.rope_bc(dt, theta, B, C, angle0)
+    ang = angle0.cuda().clone()
+    outs = []
+    for lo, hi in ((0, 70), (70, 71), (71, 200)):
+        sl = lambda t: t[:, lo:hi].contiguous().cuda()
+        b_rot, c_rot, _ = ssm.rope_bc(sl(dt), sl(theta), sl(B), sl(C), angle0=ang, angle_last=ang)
+        outs.append((b_rot, c_rot))
+    torch.cuda.synchronize()
+    got_b = torch.cat([o[0] for o in outs], dim=1).float().cpu()
+    got_c = torch.cat([o[1] for o in outs], dim=1).float().cpu()
+    assert max(rel_err(got_b, rb), rel_err(got_c, rc), rel_err(ang.cpu(), ra)) <= TOL_F32
+
+
+@pytest.mark.parametrize("trap", [False, True])
+def test_rope_feeds_ssd(trap):
+    """Rotary step, then the chunked SSD with one group per head (bf16, so one
+    head per workgroup), against the oracle's rotary step and SSD."""
+    s = SsdShape(8, 192, 32, 64, 128, 1, 64, "bf16", has_z=True, dskip="normal", seed=61)
+    inp = make_ssd_inputs(s)
+    theta = make_theta((s.batch, s.seqlen, 1, s.dstate // 2), 62, "bf16", 20.0)
+    lam = make_lam((s.batch, s.seqlen, s.nheads), 63)
+    h0 = make_state((s.batch, s.nheads, s.headdim, s.dstate), 64, 0.5)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    br, cr, _ = ssm.rope_bc(d["dt"], theta.cuda(), d["B"], d["C"])
+    if trap:
+        y, hl = ssm.ssd_trap_chunked_fwd(d["x"], d["dt"], lam.cuda(), d["A"], br, cr, d["D"], d["z"], h0=h0.cuda())
+    else:
+        y, hl = ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], h0=h0.cuda())
+    torch.cuda.synchronize()
+    rb, rc, _ = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
+    # The SSD reads B and C as bf16: the oracle SSD takes the oracle's rotated
+    # B and C rounded the same way.
+    rb16 = torch.from_numpy(rb).to(torch.bfloat16)
+    rc16 = torch.from_numpy(rc).to(torch.bfloat16)
+    if trap:
+        ry, rh = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], rb16, rc16, inp["D"], inp["z"], h0)
+    else:
+        ry, rh = oracle.ssd(inp["x"], inp["dt"], inp["A"], rb16, rc16, inp["D"], inp["z"], h0)
+    assert rel_err(y.float().cpu(), ry) <= TOL_BF16 and rel_err(hl.cpu(), rh) <= TOL_BF16
+
+
+def test_rope_named_workload_full_size():
+    """The rotary step at the SSD workload's full size (32 x 256, 32 heads,
+    dstate 128, bf16, one set of angles for all heads), every output."""
+    s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(s)
+    theta = make_theta((s.batch, s.seqlen, 1, s.dstate // 2), 71, "bf16", 1.0)
+    br, cr, al = _run(inp["dt"], theta, inp["B"], inp["C"], None, torch.bfloat16)
+    rb, rc, ra = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
+    assert max(rel_err(br, rb), rel_err(cr, rc)) <= TOL_BF16
+    assert rel_err(al, ra) <= TOL_F32
