@@ -338,8 +338,10 @@ typedef struct {
  *   angle_last : (batch, nheads, dstate / 2) float32, nullable; may be
  *                exactly angle0 (updated in place)
  * The running angle is summed in float64 inside the call; angle0 and
- * angle_last are float32.  Pointers need their element alignment; outputs
- * must not overlap inputs or each other (angle_last == angle0 excepted).
+ * angle_last are float32.  theta, B, C, B_rot and C_rot must be 16-byte
+ * aligned (they are accessed as vectors of up to four pairs' halves); dt,
+ * angle0 and angle_last need their element alignment.  Outputs must not
+ * overlap inputs or each other (angle_last == angle0 excepted).
  * Supported: any batch, seqlen >= 0 with batch * nheads < 2^31.
  */
 SSM_API int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,

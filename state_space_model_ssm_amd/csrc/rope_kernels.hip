@@ -11,13 +11,15 @@
 //
 // The work is a prefix sum over time followed by an elementwise rotation: it
 // is bound by HBM (the rotated B and C are written per head).  One workgroup
-// per (b, h): lane k of a KP = N/2 lane group owns pair k, and the NSEG groups
-// of the workgroup own consecutive time segments.  Each segment first sums its
+// per (b, h): each thread of a group of KP / 4 threads owns four consecutive
+// pairs, and the NSEG groups of the workgroup own consecutive time segments.  Each segment first sums its
 // dt * theta, the segment totals are combined through LDS, and then every
 // segment walks its steps from its own starting angle.  The running angle is
-// kept in float64 (a float32 sum over thousands of steps would drift by more
-// than the result's tolerance); it is reduced to [-pi, pi] in float64 and the
-// rotation itself is float32.
+// summed in float64 (a float32 sum over thousands of steps would drift by more
+// than the result's tolerance), in revolutions, reduced to
+// [-1/2, 1/2] in float64, and the sine, cosine and rotation are float32 (the
+// hardware v_sin_f32 / v_cos_f32, which take revolutions; the outputs then
+// differ from the float64 oracle by ~1.4e-7 of their largest magnitude).
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -27,78 +29,184 @@ __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
-__device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
-  p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));  // round to nearest even
+
+constexpr double kInvTwoPi = 0.15915494309189533576888;
+// Steps whose loads are issued together: 2 per rotation batch and 4 per
+// batch of the angle sums (1 rotation step per batch measured 7% slower; 4 or
+// 8 no faster).
+constexpr int kBatch = 2;
+constexpr int kSumBatch = 4;
+
+// Vector loads and stores of V consecutive elements (V * element size bytes,
+// aligned to that size).
+template <int BYTES> struct RawT;
+template <> struct RawT<2> { typedef uint16_t T; };
+template <> struct RawT<4> { typedef uint32_t T; };
+template <> struct RawT<8> { typedef uint2 T; };
+template <> struct RawT<16> { typedef uint4 T; };
+
+template <int V>
+__device__ __forceinline__ void vload(const float *p, float (&v)[V]) {
+  const auto r = *reinterpret_cast<const typename RawT<4 * V>::T *>(p);
+  static_assert(sizeof(r) == sizeof(v), "vector width");
+  __builtin_memcpy(v, &r, sizeof(v));
+}
+template <int V>
+__device__ __forceinline__ void vload(const uint16_t *p, float (&v)[V]) {
+  const auto r = *reinterpret_cast<const typename RawT<2 * V>::T *>(p);
+  uint16_t e[V];
+  static_assert(sizeof(r) == sizeof(e), "vector width");
+  __builtin_memcpy(e, &r, sizeof(e));
+#pragma unroll
+  for (int j = 0; j < V; ++j) v[j] = __uint_as_float(static_cast<uint32_t>(e[j]) << 16);
+}
+template <int V>
+__device__ __forceinline__ void vstore(float *p, const float (&v)[V]) {
+  typename RawT<4 * V>::T r;
+  __builtin_memcpy(&r, v, sizeof(v));
+  *reinterpret_cast<typename RawT<4 * V>::T *>(p) = r;
+}
+template <int V>
+__device__ __forceinline__ void vstore(uint16_t *p, const float (&v)[V]) {
+  uint16_t e[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) e[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[j]));  // round to nearest even
+  typename RawT<2 * V>::T r;
+  __builtin_memcpy(&r, e, sizeof(e));
+  *reinterpret_cast<typename RawT<2 * V>::T *>(p) = r;
 }
 
-constexpr double kTwoPi = 6.283185307179586476925;
-constexpr double kInvTwoPi = 0.15915494309189533576888;
-
-// Time segments per workgroup for KP pair lanes (at most 512 threads, at
-// least one wavefront).
+// Pairs per thread (consecutive k), threads per (batch, time, head) row, and
+// time segments per workgroup (at most 512 threads, at least one wavefront).
+// Four pairs per thread (8-byte bf16 or 16-byte float32 accesses per row
+// half) measured 36 us on 32 x 256 x 32 heads x 128 states against 49 us
+// with one pair per thread and 42 us with eight (more registers, fewer
+// wavefronts).
 template <int KP>
-constexpr int rope_segments() { return KP >= 8 ? 512 / KP : 64; }
+struct RopeCfg {
+  static constexpr int VEC = KP < 4 ? KP : 4;
+  static constexpr int TPR = KP / VEC;
+  static constexpr int NSEG = 512 / TPR < 64 ? 512 / TPR : 64;
+  static constexpr int THREADS = TPR * NSEG;
+};
 
 template <typename Tin, typename Tout, int KP>
 __global__ void __launch_bounds__(512) rope_bc_kernel(const RopeParams p) {
-  constexpr int NSEG = rope_segments<KP>();
+  using Cfg = RopeCfg<KP>;
+  constexpr int VEC = Cfg::VEC, TPR = Cfg::TPR, NSEG = Cfg::NSEG;
   constexpr int N = 2 * KP;
   __shared__ double sPart[NSEG * KP];
-  const Tin *__restrict__ gdt = static_cast<const Tin *>(p.dt);
-  const Tin *__restrict__ gth = static_cast<const Tin *>(p.theta);
-  const Tin *__restrict__ gB = static_cast<const Tin *>(p.B);
-  const Tin *__restrict__ gC = static_cast<const Tin *>(p.C);
-  Tout *__restrict__ gBr = static_cast<Tout *>(p.B_rot);
-  Tout *__restrict__ gCr = static_cast<Tout *>(p.C_rot);
 
-  const int seg = threadIdx.x / KP;
-  const int k = threadIdx.x % KP;
+  const int seg = threadIdx.x / TPR;
+  const int k0 = (threadIdx.x % TPR) * VEC;
   const int64_t H = p.nheads, L = p.seqlen;
   const int64_t b = blockIdx.x / H, h = blockIdx.x % H;
   const int64_t g = h / (H / p.ngroups);
   const int64_t th = p.theta_heads == 1 ? 0 : h;
   const int64_t seglen = (L + NSEG - 1) / NSEG;
   const int64_t t0 = min(L, seg * seglen), t1 = min(L, t0 + seglen);
+  const int n = static_cast<int>(t1 - t0);  // steps of this segment
   const float bias = (p.dt_softplus && p.dt_bias != nullptr) ? p.dt_bias[h] : 0.0f;
-  auto turn = [&](int64_t t) __attribute__((always_inline)) {  // dt_t * theta_t[k]
-    float dt = ld(gdt, (b * L + t) * H + h);
-    if (p.dt_softplus) dt = dt_softplus(dt + bias);
-    return static_cast<double>(dt) * static_cast<double>(ld(gth, ((b * L + t) * p.theta_heads + th) * KP + k));
+
+  // Pointers at step t0 of this thread's rows, and their per-step strides.
+  const int64_t row0 = b * L + t0;
+  const Tin *dtp = static_cast<const Tin *>(p.dt) + row0 * H + h;
+  const Tin *thp = static_cast<const Tin *>(p.theta) + (row0 * p.theta_heads + th) * KP + k0;
+  const Tin *bp = static_cast<const Tin *>(p.B) + (row0 * p.ngroups + g) * N + k0;
+  const Tin *cp = static_cast<const Tin *>(p.C) + (row0 * p.ngroups + g) * N + k0;
+  Tout *brp = static_cast<Tout *>(p.B_rot) + (row0 * H + h) * N + k0;
+  Tout *crp = static_cast<Tout *>(p.C_rot) + (row0 * H + h) * N + k0;
+  const int64_t s_dt = H, s_th = p.theta_heads * KP, s_bc = p.ngroups * N, s_out = H * N;
+  auto step = [&](int i) __attribute__((always_inline)) {
+    const float dt = ld(dtp, i * s_dt);
+    return p.dt_softplus ? dt_softplus(dt + bias) : dt;
   };
 
-  // The starting angle is read before the barrier, so angle_last may be
+  // The starting angles are read before the barrier, so angle_last may be
   // angle0 itself (it is written after the barrier).
-  const int64_t ai = (b * H + h) * KP + k;
-  double phi = p.angle0 != nullptr ? static_cast<double>(p.angle0[ai]) : 0.0;
-  double part = 0.0;
-  for (int64_t t = t0; t < t1; ++t) part += turn(t);
-  sPart[seg * KP + k] = part;
-  __syncthreads();
-  for (int j = 0; j < seg; ++j) phi -= sPart[j * KP + k];
-  if (seg == NSEG - 1 && p.angle_last != nullptr) p.angle_last[ai] = static_cast<float>(phi - part);
+  const int64_t ai = (b * H + h) * KP + k0;
+  double phi[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) phi[j] = p.angle0 != nullptr ? static_cast<double>(p.angle0[ai + j]) : 0.0;
 
-#pragma unroll 4
-  for (int64_t t = t0; t < t1; ++t) {
-    phi -= turn(t);
-    const float r = static_cast<float>(phi - kTwoPi * rint(phi * kInvTwoPi));
-    float sn, cs;
-    sincosf(r, &sn, &cs);
-    const int64_t src = ((b * L + t) * p.ngroups + g) * N + k;
-    const int64_t dst = ((b * L + t) * H + h) * N + k;
-    const float b1 = ld(gB, src), b2 = ld(gB, src + KP);
-    const float c1 = ld(gC, src), c2 = ld(gC, src + KP);
-    st(gBr, dst, b1 * cs - b2 * sn);
-    st(gBr, dst + KP, b1 * sn + b2 * cs);
-    st(gCr, dst, c1 * cs - c2 * sn);
-    st(gCr, dst + KP, c1 * sn + c2 * cs);
+  // Steps go in batches whose loads are all issued before any of them is
+  // used; steps past the segment's end load the segment's last step
+  // (branch-free) and are not used.
+  double part[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) part[j] = 0.0;
+  for (int i0 = 0; i0 < n; i0 += kSumBatch) {
+    float dv[kSumBatch], tv[kSumBatch][VEC];
+#pragma unroll
+    for (int q = 0; q < kSumBatch; ++q) {
+      const int i = min(i0 + q, n - 1);
+      dv[q] = step(i);
+      vload<VEC>(thp + i * s_th, tv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kSumBatch; ++q)
+      if (i0 + q < n) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) part[j] += static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) sPart[seg * KP + k0 + j] = part[j];
+  __syncthreads();
+  for (int s = 0; s < seg; ++s) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) phi[j] -= sPart[s * KP + k0 + j];
+  }
+  if (seg == NSEG - 1 && p.angle_last != nullptr) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) p.angle_last[ai + j] = static_cast<float>(phi[j] - part[j]);
+  }
+
+  // The running angles in revolutions, reduced to [-1/2, 1/2] for the
+  // hardware sine and cosine (which take revolutions).
+  double rev[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) rev[j] = phi[j] * kInvTwoPi;
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float dv[kBatch], tv[kBatch][VEC], b1[kBatch][VEC], b2[kBatch][VEC], c1[kBatch][VEC], c2[kBatch][VEC];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = min(i0 + q, n - 1);
+      dv[q] = step(i);
+      vload<VEC>(thp + i * s_th, tv[q]);
+      vload<VEC>(bp + i * s_bc, b1[q]);
+      vload<VEC>(bp + i * s_bc + KP, b2[q]);
+      vload<VEC>(cp + i * s_bc, c1[q]);
+      vload<VEC>(cp + i * s_bc + KP, c2[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (i0 + q < n) {
+        float ob1[VEC], ob2[VEC], oc1[VEC], oc2[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+          rev[j] -= static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]) * kInvTwoPi;
+          const float fr = static_cast<float>(rev[j] - rint(rev[j]));
+          const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+          ob1[j] = b1[q][j] * cs - b2[q][j] * sn;
+          ob2[j] = b1[q][j] * sn + b2[q][j] * cs;
+          oc1[j] = c1[q][j] * cs - c2[q][j] * sn;
+          oc2[j] = c1[q][j] * sn + c2[q][j] * cs;
+        }
+        const int64_t o = (i0 + q) * s_out;
+        vstore<VEC>(brp + o, ob1);
+        vstore<VEC>(brp + o + KP, ob2);
+        vstore<VEC>(crp + o, oc1);
+        vstore<VEC>(crp + o + KP, oc2);
+      }
+    }
   }
 }
 
 template <typename Tin, typename Tout, int KP>
 hipError_t launch_kp(const RopeParams &p, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
-  hipLaunchKernelGGL((rope_bc_kernel<Tin, Tout, KP>), grid, dim3(KP * rope_segments<KP>()), 0, stream, p);
+  hipLaunchKernelGGL((rope_bc_kernel<Tin, Tout, KP>), grid, dim3(RopeCfg<KP>::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 

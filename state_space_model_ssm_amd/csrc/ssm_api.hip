@@ -620,9 +620,9 @@ int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,
   if (rows > 0 && (!dt || !theta || !B || !C || !B_rot || !C_rot))
     return fail(SSM_ERR_NULL, "dt, theta, B, C, B_rot and C_rot are required");
   const size_t ei = dtype_size(d.in_dtype), eo = dtype_size(d.out_dtype);
-  if (!aligned(dt, ei) || !aligned(theta, ei) || !aligned(B, ei) || !aligned(C, ei))
-    return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
-  if (!aligned(B_rot, eo) || !aligned(C_rot, eo)) return fail(SSM_ERR_ALIGN, "B_rot and C_rot must be aligned to %zu bytes", eo);
+  if (!aligned(dt, ei)) return fail(SSM_ERR_ALIGN, "dt must be aligned to %zu bytes", ei);
+  if (!aligned(theta, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(B_rot, 16) || !aligned(C_rot, 16))
+    return fail(SSM_ERR_ALIGN, "theta, B, C, B_rot and C_rot must be 16-byte aligned");
   if (!aligned(angle0, 4) || !aligned(angle_last, 4)) return fail(SSM_ERR_ALIGN, "angles must be 4-byte aligned");
   const int64_t n_ang = d.batch * d.nheads * half;
   const Span ins[] = {{dt, rows * d.nheads * ei},

@@ -366,7 +366,9 @@ def test_rope_rejects_null_misaligned_overlap():
     assert _rope(d, theta=None) == -1
     assert _rope(d, C_rot=None) == -1
     assert _rope(d, dt=FAKE + 1) == -4                          # bf16 needs 2-byte alignment
-    assert _rope(_ropedims(in_dtype=0), B=FAKE + 0x200002) == -4  # float32 needs 4
+    assert _rope(d, B=FAKE + 0x200008) == -4                    # B, C, theta and outputs need 16
+    assert _rope(d, theta=FAKE + 0x100004) == -4
+    assert _rope(d, C_rot=FAKE + 0x18000002) == -4
     assert _rope(d, angle0=FAKE + 0x400002) == -4
     assert _rope(d, B_rot=FAKE + 0x200000) == -2                # B_rot is B
     assert _rope(d, C_rot=FAKE + 0x10000000 + 64) == -2         # C_rot inside B_rot
