@@ -100,7 +100,14 @@ __global__ void __launch_bounds__(512) rope_bc_kernel(const RopeParams p) {
   const int seg = threadIdx.x / TPR;
   const int k0 = (threadIdx.x % TPR) * VEC;
   const int64_t H = p.nheads, L = p.seqlen;
-  const int64_t b = blockIdx.x / H, h = blockIdx.x % H;
+  // The heads of a batch row read the same theta (when shared), B and C.
+  // Consecutive workgroup ids are dealt round-robin to the 8 XCDs, so remap
+  // ids to give each XCD a contiguous run of (b, h) and keep a batch row's
+  // shared rows in one L2 (without it every XCD fetches them: 8x the reads).
+  const int64_t nblk = p.batch * H;
+  int64_t id = blockIdx.x;
+  if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;
+  const int64_t b = id / H, h = id % H;
   const int64_t g = h / (H / p.ngroups);
   const int64_t th = p.theta_heads == 1 ? 0 : h;
   const int64_t seglen = (L + NSEG - 1) / NSEG;
