@@ -346,7 +346,7 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
         (br.numel() + cr.numel()) * 2 + ang.numel() * 4
     out["rope_bc_32x256_h32n128_bf16"] = {"ms": round(ms, 5), "hbm_GB/s": round(nbytes / ms / 1e6, 1),
                                           "hbm_frac": round(nbytes / ms / 1e6 / 8000.0, 4),
-                                          "rows": rows}
+                                          "rows": rows, "traffic": measured_traffic("rope_bc_32x256_h32n128_bf16")}
     ms, _ = time_calls(lambda: ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], y=y,
                                                    h_last=h, stream=stream), 50, 5)
     out["ssd_rotated_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
