@@ -175,6 +175,17 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream or None
 
 
+def _out(t, shape, dtype, like, name):
+    """A caller-given output tensor, checked against the shape and dtype the
+    call writes (the library trusts the sizes in the dims), or a new one."""
+    if t is None:
+        return _torch().empty(shape, dtype=dtype, device=like.device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)} on {like.device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
 def _phase0(dims, n: int, dt_softplus: bool, dt_bias, lam_sigmoid: bool = False):
     """Set the Phase-0 flags of ``dims``: softplus(dt + dt_bias) as the step
     (dt_bias: (n,) float32 or None) and sigmoid(lam) for the trapezoid."""
@@ -242,10 +253,9 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_ch
     dims = _scan_dims(u, B, in_code, out_code, n_chunks)
     _phase0(dims, dim, dt_softplus, dt_bias)
     need = scan_workspace_size(dims)
-    if y is None:
-        y = torch.empty((batch, dim, L), dtype=out_dt, device=u.device)
-    if h_last is None and return_h_last:
-        h_last = torch.empty((batch, dim, N), dtype=torch.float32, device=u.device)
+    y = _out(y, (batch, dim, L), out_dt, u, "y")
+    if h_last is not None or return_h_last:
+        h_last = _out(h_last, (batch, dim, N), torch.float32, u, "h_last")
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
@@ -351,10 +361,9 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
         raise ValueError("h0 must be float32 (batch, nheads, headdim, dstate)")
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
     _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
-    if y is None:
-        y = torch.empty((batch, L, H, P), dtype=out_dt, device=x.device)
-    if h_last is None and return_h_last:
-        h_last = torch.empty((batch, H, P, N), dtype=torch.float32, device=x.device)
+    y = _out(y, (batch, L, H, P), out_dt, x, "y")
+    if h_last is not None or return_h_last:
+        h_last = _out(h_last, (batch, H, P, N), torch.float32, x, "h_last")
     if lam is None:
         rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                    _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
@@ -409,8 +418,7 @@ def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=Non
         raise ValueError("B, C must be (batch, ngroups, dstate) and A (dim, dstate)")
     if state.dtype != torch.float32 or state.shape != (batch, dim, N):
         raise ValueError("state must be float32 (batch, dim, dstate)")
-    if y is None:
-        y = torch.empty((batch, dim), dtype=out_dt, device=u.device)
+    y = _out(y, (batch, dim), out_dt, u, "y")
     dims = StepDims(batch=batch, dim=dim, dstate=N, ngroups=G, in_dtype=in_code, out_dtype=out_code,
                     flags=0, reserved=0)
     _phase0(dims, dim, dt_softplus, dt_bias)
@@ -442,8 +450,7 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, s
         raise ValueError("B, C must be (batch, ngroups, dstate) and A (nheads,)")
     if state.dtype != torch.float32 or state.shape != (batch, H, P, N):
         raise ValueError("state must be float32 (batch, nheads, headdim, dstate)")
-    if y is None:
-        y = torch.empty((batch, H, P), dtype=out_dt, device=x.device)
+    y = _out(y, (batch, H, P), out_dt, x, "y")
     dims = SsdStepDims(batch=batch, nheads=H, headdim=P, dstate=N, ngroups=G, in_dtype=in_code,
                        out_dtype=out_code, flags=0, reserved=0)
     _phase0(dims, H, dt_softplus, dt_bias)
@@ -477,15 +484,12 @@ def rope_bc(dt, theta, B, C, *, angle0=None, out_dtype=None, B_rot=None, C_rot=N
         raise ValueError("dt must be (batch, L, H), C shaped like B, dstate even")
     if theta.shape != (batch, L, TH, N // 2):
         raise ValueError("theta must be (batch, L, 1 or H, dstate / 2)")
-    for name, t in (("angle0", angle0), ("angle_last", angle_last)):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (batch, H, N // 2)):
-            raise ValueError(f"{name} must be float32 (batch, nheads, dstate / 2)")
-    if B_rot is None:
-        B_rot = torch.empty((batch, L, H, N), dtype=out_dt, device=B.device)
-    if C_rot is None:
-        C_rot = torch.empty((batch, L, H, N), dtype=out_dt, device=B.device)
-    if angle_last is None and return_angle_last:
-        angle_last = torch.empty((batch, H, N // 2), dtype=torch.float32, device=B.device)
+    if angle0 is not None and (angle0.dtype != torch.float32 or angle0.shape != (batch, H, N // 2)):
+        raise ValueError("angle0 must be float32 (batch, nheads, dstate / 2)")
+    B_rot = _out(B_rot, (batch, L, H, N), out_dt, B, "B_rot")
+    C_rot = _out(C_rot, (batch, L, H, N), out_dt, B, "C_rot")
+    if angle_last is not None or return_angle_last:
+        angle_last = _out(angle_last, (batch, H, N // 2), torch.float32, B, "angle_last")
     dims = RopeDims(batch=batch, seqlen=L, nheads=H, ngroups=G, dstate=N, theta_heads=TH, in_dtype=in_code,
                     out_dtype=out_code, flags=0, reserved=0)
     _phase0(dims, H, dt_softplus, dt_bias)
