@@ -156,3 +156,34 @@ def test_rope_named_workload_full_size():
     rb, rc, ra = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
     assert max(rel_err(br, rb), rel_err(cr, rc)) <= TOL_BF16
     assert rel_err(al, ra) <= TOL_F32
+
+
+def test_rope_prefill_then_decode_steps():
+    """Mamba-3 serving order: a 64-token prefill (rotary step, then the SSD on
+    the per-head B and C), then 16 decode tokens, each a one-token rotary step
+    from the cached angle (updated in place) and an SSD decode step on the
+    cached state; every output against the oracle over all 80 tokens."""
+    s = SsdShape(2, 80, 8, 64, 64, 1, 64, "bf16", has_z=True, dskip="normal", seed=91)
+    inp = make_ssd_inputs(s)
+    theta = make_theta((s.batch, s.seqlen, s.nheads, s.dstate // 2), 92, "bf16", 10.0)
+    rb, rc, _ = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
+    rb16 = torch.from_numpy(rb).to(torch.bfloat16)
+    rc16 = torch.from_numpy(rc).to(torch.bfloat16)
+    ry, rh = oracle.ssd(inp["x"], inp["dt"], inp["A"], rb16, rc16, inp["D"], inp["z"])
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    th = theta.cuda()
+    T = 64
+    pre = lambda t: t[:, :T].contiguous()
+    br, cr, ang = ssm.rope_bc(pre(d["dt"]), pre(th), pre(d["B"]), pre(d["C"]))
+    y0, state = ssm.ssd_chunked_fwd(pre(d["x"]), pre(d["dt"]), d["A"], br, cr, d["D"], pre(d["z"]))
+    ys = [y0.float()]
+    for t in range(T, s.seqlen):
+        one = lambda a: a[:, t:t + 1].contiguous()
+        b1, c1, _ = ssm.rope_bc(one(d["dt"]), one(th), one(d["B"]), one(d["C"]), angle0=ang, angle_last=ang)
+        y = ssm.ssd_step(d["x"][:, t].contiguous(), d["dt"][:, t].contiguous(), d["A"], b1[:, 0].contiguous(),
+                         c1[:, 0].contiguous(), d["D"], d["z"][:, t].contiguous(), state=state)
+        ys.append(y.float()[:, None])
+    torch.cuda.synchronize()
+    got = torch.cat(ys, dim=1).cpu()
+    assert rel_err(got, ry) <= TOL_BF16, rel_err(got, ry)
+    assert rel_err(state.cpu(), rh) <= TOL_BF16, rel_err(state.cpu(), rh)
