@@ -11,8 +11,9 @@
 //
 // The work is a prefix sum over time followed by an elementwise rotation: it
 // is bound by HBM (the rotated B and C are written per head).  One workgroup
-// per (b, h): each thread of a group of KP / 4 threads owns four consecutive
-// pairs, and the NSEG groups of the workgroup own consecutive time segments.  Each segment first sums its
+// per (b, h): each thread owns four consecutive pairs (all of them when
+// N / 2 < 4), a group of threads covers a row's N / 2 pairs, and the NSEG
+// groups of the workgroup own consecutive time segments.  Each segment first sums its
 // dt * theta, the segment totals are combined through LDS, and then every
 // segment walks its steps from its own starting angle.  The running angle is
 // summed in float64 (a float32 sum over thousands of steps would drift by more
