@@ -14,7 +14,9 @@ Besides the headline, the line carries:
     limits it, from HIP events recorded on the launch stream around the timed
     region;
   * ``cpu_baseline``: the float64 CPU oracle timed on a bounded sample of the
-    same workload (single thread);
+    same workload on every host core the process may use (independent batch
+    rows and channel ranges on parallel threads, each running the unchanged
+    oracle), with the single-threaded figure beside it;
   * ``workloads``: the other named workloads (the tiny, page-1 and long-prefill
     scans and the chunked SSD), timed the same way, for context.
 """
@@ -86,8 +88,11 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-context", action="store_true", help="skip the other named workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target wall time of each oracle baseline leg (single thread, all cores)")
+    ap.add_argument("--warm-floor-s", type=float, default=0.05,
+                    help="least time of back-to-back untimed headline calls before timing "
+                         "(the GPU clocks settle after a few ms of load)")
     ap.add_argument("--cold-reps", type=int, default=30,
                     help="calls timed one at a time after a 512 MiB cache flush (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -196,7 +201,7 @@ def main():
         raise SystemExit("the headline workload must be a selective scan")
     host = make_scan_inputs(s)
     fn, chunks = scan_runner(s, host)
-    ms, wall = time_calls(fn, args.steps, args.warmup, min_warm_s=0.0)  # exactly W untimed steps
+    ms, wall = time_calls(fn, args.steps, args.warmup, min_warm_s=args.warm_floor_s)
     sec = ms / 1e3
     gelem = s.elements / sec / 1e9
     mbytes = s.metric_bytes()
@@ -208,7 +213,10 @@ def main():
     t_alu = slots / VALU_SLOTS_PER_S
     if t_alu >= t_hbm:
         roof = {"bound": "alu", "achieved": round(alu_tflops, 3), "peak": round(FP32_VECTOR_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_VECTOR_TFLOPS, 4)}
+                "unit": "TFLOP/s", "frac": round(alu_tflops / FP32_VECTOR_TFLOPS, 4),
+                "unit_note": "fp32 VALU issue-slot equivalents: the method's slots per element x 2 "
+                             "(an FMA is 2 flops in one slot; a transcendental takes 4 slots, "
+                             "counted as 8)"}
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
@@ -259,20 +267,7 @@ def main():
     # ---- CPU baseline: the float64 oracle on a bounded sample ------------------
     cpu = None
     if not args.no_cpu:
-        import oracle
-        oracle.build(force=False)
-        probe = 16
-        t0 = time.perf_counter()
-        _cpu_slice(oracle, host, s, probe)
-        per_ch = (time.perf_counter() - t0) / probe
-        nch = int(max(probe, min(s.batch * s.dim, args.cpu_seconds / max(per_ch, 1e-9))))
-        t0 = time.perf_counter()
-        _cpu_slice(oracle, host, s, nch)
-        dt_cpu = time.perf_counter() - t0
-        cpu = {"value": round(nch * s.seqlen / dt_cpu / 1e9, 6), "unit": "Gelem/s", "cores": 1,
-               "kind": "oracle", "seconds": round(dt_cpu, 2),
-               "sample": f"first {nch} of {s.batch * s.dim} channels (batch-major), all {s.seqlen} steps, "
-                         f"single-threaded float64 recurrence"}
+        cpu = cpu_baseline(host, s, args.cpu_seconds)
 
     out = {
         "metric": "selective-scan Gelem/s (B*D*L) + achieved HBM GB/s as % of MI355X peak",
@@ -401,22 +396,71 @@ def ssd_flops(w) -> float:
     return w.batch * chunks * (per_bc * w.ngroups + per_bch * w.nheads)
 
 
-def _cpu_slice(oracle, host, s, nch):
-    """Run the oracle on the first nch (batch, channel) rows of the workload."""
-    import numpy as np
-    done = 0
-    b = 0
+def _channel_units(s, nch, per_unit):
+    """The first nch (batch, channel) rows of the workload, batch-major, as
+    (batch row, first channel, channel count) units of at most per_unit
+    channels (one group)."""
+    units, done, b = [], 0, 0
     while done < nch:
         take = min(nch - done, s.dim)
-        sl = {"u": host["u"][b:b + 1, :take], "delta": host["delta"][b:b + 1, :take],
-              "A": host["A"][:take], "B": host["B"][b:b + 1], "C": host["C"][b:b + 1],
-              "D": None if host["D"] is None else host["D"][:take],
-              "z": None if host["z"] is None else host["z"][b:b + 1, :take]}
-        if s.ngroups != 1:
-            raise SystemExit("cpu baseline sample assumes one group")
-        oracle.scan(sl["u"], sl["delta"], sl["A"], sl["B"], sl["C"], sl["D"], sl["z"])
+        for d0 in range(0, take, per_unit):
+            units.append((b, d0, min(per_unit, take - d0)))
         done += take
         b += 1
+    return units
+
+
+def _run_units(oracle, h64, units, threads):
+    """The unchanged oracle on each unit's contiguous slice of the float64
+    inputs; `threads` host threads (the oracle's C call releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(unit):
+        b, d0, n = unit
+        sl = lambda k: None if h64[k] is None else h64[k][b:b + 1, d0:d0 + n]
+        oracle.scan(sl("u"), sl("delta"), h64["A"][d0:d0 + n], h64["B"][b:b + 1], h64["C"][b:b + 1],
+                    None if h64["D"] is None else h64["D"][d0:d0 + n], sl("z"))
+
+    if threads == 1:
+        for unit in units:
+            one(unit)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, units))
+
+
+def cpu_baseline(host, s, seconds):
+    """The float64 oracle on the host: a bounded sample of the workload (the
+    first channels, batch-major, every step) timed single-threaded and on
+    every core in the process's affinity set, each leg aiming at `seconds` of
+    wall time.  The inputs are widened to float64 before the clock starts."""
+    import oracle
+    oracle.build(force=False)
+    if s.ngroups != 1:
+        raise SystemExit("cpu baseline sample assumes one group")
+    h64 = {k: (None if v is None else oracle.f64(v)) for k, v in host.items()}
+    total = s.batch * s.dim
+    probe = 16
+    t0 = time.perf_counter()
+    _run_units(oracle, h64, _channel_units(s, probe, probe), 1)
+    per_ch = (time.perf_counter() - t0) / probe
+    legs = {}
+    cores = len(os.sched_getaffinity(0))
+    for threads in (1, cores):
+        nch = int(max(probe, min(total, threads * seconds / max(per_ch, 1e-9))))
+        per_unit = nch if threads == 1 else max(1, -(-min(nch, s.dim) // (4 * threads)))
+        units = _channel_units(s, nch, per_unit)
+        t0 = time.perf_counter()
+        _run_units(oracle, h64, units, threads)
+        dt = time.perf_counter() - t0
+        legs[threads] = {"value": round(nch * s.seqlen / dt / 1e9, 6), "unit": "Gelem/s", "cores": threads,
+                         "kind": "oracle", "seconds": round(dt, 3),
+                         "sample": f"first {nch} of {total} channels (batch-major), all {s.seqlen} steps; "
+                                   f"float64 recurrence on {threads} host thread(s)"
+                                   + ("" if threads == 1 else f" over {len(units)} channel ranges")}
+    out = dict(legs[cores])
+    out["single_thread"] = legs[1]
+    return out
 
 
 if __name__ == "__main__":

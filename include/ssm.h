@@ -108,6 +108,13 @@ SSM_API int ssm_scan_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes);
 SSM_API int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks);
 
 /*
+ * The same workspace size as the return value: the bytes ssm_scan_fwd needs
+ * for `dims`, or SIZE_MAX when `dims` fails a check (ssm_last_error_message()
+ * then says why).
+ */
+SSM_API size_t ssm_scan_workspace_bytes(const ssm_scan_dims_t *dims);
+
+/*
  * Selective-scan forward.
  *
  * For every batch b and channel d (state h in R^N; before t = 0 it is
@@ -229,6 +236,9 @@ typedef struct {
 /* Workspace the SSD needs for `dims` (currently always 0). */
 SSM_API int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
 
+/* The same as the return value, or SIZE_MAX when `dims` fails a check. */
+SSM_API size_t ssd_workspace_bytes(const ssd_dims_t *dims);
+
 /*
  * Scalar-decay SSD forward: the selective scan with one decay per (batch,
  * time, head), shared by the head's headdim x dstate states, computed chunk by
@@ -338,7 +348,10 @@ typedef struct {
  *   angle_last : (batch, nheads, dstate / 2) float32, nullable; may be
  *                exactly angle0 (updated in place)
  * The running angle is summed in float64 inside the call; angle0 and
- * angle_last are float32.  theta, B, C, B_rot and C_rot must be 16-byte
+ * angle_last are float32.  angle_last is the final angle reduced modulo 2 pi
+ * to [-pi, pi] (in float64, before the float32 rounding), which is all a
+ * later call starting from it needs; it equals angle0 - sum dt theta up to a
+ * multiple of 2 pi.  theta, B, C, B_rot and C_rot must be 16-byte
  * aligned (they are accessed as vectors of up to four pairs' halves); dt,
  * angle0 and angle_last need their element alignment.  Outputs must not
  * overlap inputs or each other (angle_last == angle0 excepted).
@@ -426,6 +439,9 @@ SSM_API const char *ssm_status_string(int status);
 /* Reason for the last failure on the calling host thread ("" if none).
  * The pointer stays valid until the next libssm call on that thread. */
 SSM_API const char *ssm_last_error(void);
+
+/* The same string as ssm_last_error(). */
+SSM_API const char *ssm_last_error_message(void);
 
 /* Library ABI version: major * 10000 + minor * 100 + patch. */
 SSM_API int ssm_version(void);

@@ -120,6 +120,12 @@ def lib():
         L.ssm_last_error.restype = ctypes.c_char_p
         L.ssm_version.argtypes = []
         L.ssm_version.restype = i32
+        L.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDims)]
+        L.ssm_scan_workspace_bytes.restype = ctypes.c_size_t
+        L.ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims)]
+        L.ssd_workspace_bytes.restype = ctypes.c_size_t
+        L.ssm_last_error_message.argtypes = []
+        L.ssm_last_error_message.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -173,6 +179,18 @@ def _stream(stream) -> Optional[int]:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream or None
+
+
+def _alloc_on(stream):
+    """Context in which the binding allocates outputs and workspace: on the
+    stream the kernels will run on.  PyTorch's caching allocator ties a block
+    to the stream current at its allocation, so a workspace freed when the
+    call returns is reused only by later work on that same stream, which runs
+    after the kernels that still read it."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
 
 
 def _out(t, shape, dtype, like, name):
@@ -253,14 +271,15 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_ch
     dims = _scan_dims(u, B, in_code, out_code, n_chunks)
     _phase0(dims, dim, dt_softplus, dt_bias)
     need = scan_workspace_size(dims)
-    y = _out(y, (batch, dim, L), out_dt, u, "y")
-    if h_last is not None or return_h_last:
-        h_last = _out(h_last, (batch, dim, N), torch.float32, u, "h_last")
-    if need > 0:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
-        dims.workspace = _ptr(workspace)
-        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    with _alloc_on(stream):
+        y = _out(y, (batch, dim, L), out_dt, u, "y")
+        if h_last is not None or return_h_last:
+            h_last = _out(h_last, (batch, dim, N), torch.float32, u, "h_last")
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+            dims.workspace = _ptr(workspace)
+            dims.workspace_bytes = workspace.numel() * workspace.element_size()
     rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
@@ -293,19 +312,20 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, wo
     dims = _scan_dims(u, B, in_code, out_code, 0)
     _phase0(dims, dim, dt_softplus, dt_bias)
     need = scan_bwd_workspace_size(dims)
-    if need > 0:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
-        dims.workspace = _ptr(workspace)
-        dims.workspace_bytes = workspace.numel() * workspace.element_size()
     f32 = torch.float32
-    g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
-         "dA": torch.empty((dim, N), dtype=f32, device=u.device),
-         "dB": torch.empty(B.shape, dtype=f32, device=u.device),
-         "dC": torch.empty(C.shape, dtype=f32, device=u.device),
-         "dD": None if D is None else torch.empty((dim,), dtype=f32, device=u.device),
-         "dz": None if z is None else torch.empty_like(u),
-         "dh0": torch.empty((batch, dim, N), dtype=f32, device=u.device)}
+    with _alloc_on(stream):
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=u.device)
+            dims.workspace = _ptr(workspace)
+            dims.workspace_bytes = workspace.numel() * workspace.element_size()
+        g = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+             "dA": torch.empty((dim, N), dtype=f32, device=u.device),
+             "dB": torch.empty(B.shape, dtype=f32, device=u.device),
+             "dC": torch.empty(C.shape, dtype=f32, device=u.device),
+             "dD": None if D is None else torch.empty((dim,), dtype=f32, device=u.device),
+             "dz": None if z is None else torch.empty_like(u),
+             "dh0": torch.empty((batch, dim, N), dtype=f32, device=u.device)}
     _check(lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0),
                               _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]),
                               _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]),
@@ -361,9 +381,10 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
         raise ValueError("h0 must be float32 (batch, nheads, headdim, dstate)")
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
     _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
-    y = _out(y, (batch, L, H, P), out_dt, x, "y")
-    if h_last is not None or return_h_last:
-        h_last = _out(h_last, (batch, H, P, N), torch.float32, x, "h_last")
+    with _alloc_on(stream):
+        y = _out(y, (batch, L, H, P), out_dt, x, "y")
+        if h_last is not None or return_h_last:
+            h_last = _out(h_last, (batch, H, P, N), torch.float32, x, "h_last")
     if lam is None:
         rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                    _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
@@ -418,7 +439,8 @@ def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=Non
         raise ValueError("B, C must be (batch, ngroups, dstate) and A (dim, dstate)")
     if state.dtype != torch.float32 or state.shape != (batch, dim, N):
         raise ValueError("state must be float32 (batch, dim, dstate)")
-    y = _out(y, (batch, dim), out_dt, u, "y")
+    with _alloc_on(stream):
+        y = _out(y, (batch, dim), out_dt, u, "y")
     dims = StepDims(batch=batch, dim=dim, dstate=N, ngroups=G, in_dtype=in_code, out_dtype=out_code,
                     flags=0, reserved=0)
     _phase0(dims, dim, dt_softplus, dt_bias)
@@ -450,7 +472,8 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, s
         raise ValueError("B, C must be (batch, ngroups, dstate) and A (nheads,)")
     if state.dtype != torch.float32 or state.shape != (batch, H, P, N):
         raise ValueError("state must be float32 (batch, nheads, headdim, dstate)")
-    y = _out(y, (batch, H, P), out_dt, x, "y")
+    with _alloc_on(stream):
+        y = _out(y, (batch, H, P), out_dt, x, "y")
     dims = SsdStepDims(batch=batch, nheads=H, headdim=P, dstate=N, ngroups=G, in_dtype=in_code,
                        out_dtype=out_code, flags=0, reserved=0)
     _phase0(dims, H, dt_softplus, dt_bias)
@@ -486,10 +509,11 @@ def rope_bc(dt, theta, B, C, *, angle0=None, out_dtype=None, B_rot=None, C_rot=N
         raise ValueError("theta must be (batch, L, 1 or H, dstate / 2)")
     if angle0 is not None and (angle0.dtype != torch.float32 or angle0.shape != (batch, H, N // 2)):
         raise ValueError("angle0 must be float32 (batch, nheads, dstate / 2)")
-    B_rot = _out(B_rot, (batch, L, H, N), out_dt, B, "B_rot")
-    C_rot = _out(C_rot, (batch, L, H, N), out_dt, B, "C_rot")
-    if angle_last is not None or return_angle_last:
-        angle_last = _out(angle_last, (batch, H, N // 2), torch.float32, B, "angle_last")
+    with _alloc_on(stream):
+        B_rot = _out(B_rot, (batch, L, H, N), out_dt, B, "B_rot")
+        C_rot = _out(C_rot, (batch, L, H, N), out_dt, B, "C_rot")
+        if angle_last is not None or return_angle_last:
+            angle_last = _out(angle_last, (batch, H, N // 2), torch.float32, B, "angle_last")
     dims = RopeDims(batch=batch, seqlen=L, nheads=H, ngroups=G, dstate=N, theta_heads=TH, in_dtype=in_code,
                     out_dtype=out_code, flags=0, reserved=0)
     _phase0(dims, H, dt_softplus, dt_bias)

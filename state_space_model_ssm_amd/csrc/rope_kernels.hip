@@ -32,6 +32,7 @@ __device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
 }
 
 constexpr double kInvTwoPi = 0.15915494309189533576888;
+constexpr double kTwoPi = 6.28318530717958647692529;
 // Steps whose loads are issued together: 2 per rotation batch and 4 per
 // batch of the angle sums (1 rotation step per batch measured 7% slower; 4 or
 // 8 no faster).
@@ -168,9 +169,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6))) r
 #pragma unroll
     for (int j = 0; j < VEC; ++j) phi[j] -= sPart[s * KP + k0 + j];
   }
+  // angle_last is the final angle reduced to [-pi, pi] in float64 before it
+  // is rounded to float32: only the angle modulo 2 pi matters to a later call
+  // that starts from it, and a float32 of the unreduced running angle would
+  // lose its low bits once the angle has grown (at 1e4 rad one float32 ulp is
+  // 1e-3 rad).
   if (seg == NSEG - 1 && p.angle_last != nullptr) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) p.angle_last[ai + j] = static_cast<float>(phi[j] - part[j]);
+    for (int j = 0; j < VEC; ++j) {
+      const double r = (phi[j] - part[j]) * kInvTwoPi;
+      p.angle_last[ai + j] = static_cast<float>((r - rint(r)) * kTwoPi);
+    }
   }
 
   // The running angles in revolutions, reduced to [-1/2, 1/2] for the

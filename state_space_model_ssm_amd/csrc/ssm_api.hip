@@ -141,6 +141,11 @@ int ssm_scan_workspace_size(const ssm_scan_dims_t *dims, size_t *bytes) {
   return ok();
 }
 
+size_t ssm_scan_workspace_bytes(const ssm_scan_dims_t *dims) {
+  size_t bytes = 0;
+  return ssm_scan_workspace_size(dims, &bytes) == SSM_OK ? bytes : SIZE_MAX;
+}
+
 int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks) {
   if (!n_chunks) return fail(SSM_ERR_NULL, "n_chunks is NULL");
   const int rc = check_scan_dims(dims);
@@ -419,6 +424,11 @@ int ssd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
   return ok();
 }
 
+size_t ssd_workspace_bytes(const ssd_dims_t *dims) {
+  size_t bytes = 0;
+  return ssd_workspace_size(dims, &bytes) == SSM_OK ? bytes : SIZE_MAX;
+}
+
 static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, const float *A, const void *B,
                    const void *C, const float *D, const void *z, const float *h0, void *y, float *h_last,
                    const ssd_dims_t *dims, void *stream) {
@@ -684,6 +694,8 @@ const char *ssm_status_string(int status) {
 }
 
 const char *ssm_last_error(void) { return g_last_error.c_str(); }
+
+const char *ssm_last_error_message(void) { return g_last_error.c_str(); }
 
 int ssm_version(void) { return 400; }
 

@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 14, declared
+    assert len(declared) == 17, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -380,3 +380,23 @@ def test_rope_rejects_null_misaligned_overlap():
 def test_rope_empty_inputs_launch_nothing():
     assert _rope(_ropedims(batch=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
     assert _rope(_ropedims(seqlen=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
+
+
+def test_size_returning_workspace_queries_and_error_message():
+    """ssm_scan_workspace_bytes / ssd_workspace_bytes return what the
+    status-returning queries write, SIZE_MAX on a failed check, and
+    ssm_last_error_message() is the same text as ssm_last_error()."""
+    lib = ssm.lib()
+    size_max = ctypes.c_size_t(-1).value
+    for k in (0, 1, 3, 16):
+        d = _dims(n_chunks=k, seqlen=1000)
+        assert lib.ssm_scan_workspace_bytes(ctypes.byref(d)) == ssm.scan_workspace_size(d)
+    assert lib.ssm_scan_workspace_bytes(ctypes.byref(_dims(dstate=12))) == size_max
+    assert lib.ssm_last_error_message() == lib.ssm_last_error()
+    assert b"dstate" in lib.ssm_last_error_message()
+    sd = ssm.SsdDims(batch=2, seqlen=128, nheads=4, headdim=64, dstate=128, ngroups=1, chunk=64,
+                     in_dtype=1, out_dtype=1, flags=0, reserved=0, workspace=None, workspace_bytes=0)
+    assert lib.ssd_workspace_bytes(ctypes.byref(sd)) == ssm.ssd_workspace_size(sd) == 0
+    sd.headdim = 32
+    assert lib.ssd_workspace_bytes(ctypes.byref(sd)) == size_max
+    assert b"headdim" in lib.ssm_last_error_message()

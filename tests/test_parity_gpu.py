@@ -8,11 +8,15 @@ element the kernels fail to write shows up as NaN.
 
 Small cases run the oracle on the whole tensor; they span several channel
 tiles and time tiles with ragged tails.  The five named workloads run at full
-size in the launch configuration the benchmark uses; for the two large ones the
-oracle checks a seeded sample of whole channels (every time step).
+size in the launch configuration the benchmark uses, and the oracle checks the
+whole output tensors (y and h_last; every gradient for the backward).  The
+scan oracle is independent per batch row, so the large workloads run it on
+the batch rows in parallel host threads (the float64 sums over batch rows of
+dA and dD are then added here); the measured errors are printed.
 """
 import math
 import zlib
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -203,6 +207,39 @@ def test_scan_deterministic():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_side_stream_without_caller_workspace():
+    """Calls on a side stream with the workspace left to the binding: the
+    binding's workspace and outputs belong to that stream, so memory the
+    current stream allocates and overwrites right after the call (while the
+    side stream may still be running) cannot be the workspace.  Chunked scan
+    forward and scan backward against the oracle."""
+    s = ScanShape(4, 256, 16, 2048, 1, "f32", has_z=True, dskip="normal", a_kind="loguniform", seed=4050)
+    inp = make_scan_inputs(s)
+    dy = make_state((4, 256, 2048), seed=4051)
+    side = torch.cuda.Stream()
+    d = {k: _dev(v) for k, v in inp.items()}
+    dyd = dy.cuda()
+    torch.cuda.synchronize()
+    need_f = 8 * 4 * 256 * 15 * 16
+    with torch.cuda.stream(side):
+        # Queue work ahead so the calls below are still pending when they return.
+        for _ in range(3):
+            ssm.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], n_chunks=1)
+    y, h = ssm.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], n_chunks=16,
+                        stream=side)
+    g = ssm.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dyd, stream=side)
+    junk = [torch.full((need_f // 4,), float("nan"), device="cuda") for _ in range(4)]
+    big = torch.full((ssm.scan_bwd_workspace_size(ssm._scan_dims(d["u"], d["B"], 0, 0, 0)) // 4,),
+                     float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    del junk, big
+    yr, hr = ref_scan(inp)
+    assert rel_err(y.cpu(), yr) <= TOL_F32 and rel_err(h.cpu(), hr) <= TOL_F32
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], None, dy, None)
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        assert rel_err(g[k].cpu(), ref[k]) <= TOL_BWD_F32, k
+
+
 # ---------------------------------------------------------------------------
 # Selective scan: initial state h0 and continuation of a split sequence
 # ---------------------------------------------------------------------------
@@ -246,40 +283,38 @@ def test_scan_split_continuation_in_place(L1):
 # Selective scan: the named workloads at full size
 # ---------------------------------------------------------------------------
 
-def _sample_channels(s: ScanShape, count: int, seed: int):
-    rng = np.random.default_rng(seed)
-    idx = rng.choice(s.batch * s.dim, size=min(count, s.batch * s.dim), replace=False)
-    return sorted((int(i) // s.dim, int(i) % s.dim) for i in idx)
+def _batch_rows(inp, b, keys=("u", "delta", "z", "B", "C")):
+    """Batch row b of the scan inputs (a view per row; A and D are shared)."""
+    return {k: (v[b:b + 1] if (k in keys and v is not None) else v) for k, v in inp.items()}
+
+
+def ref_scan_rows(inp, h0=None):
+    """The scan oracle over the whole tensor, one host thread per batch row
+    (the rows are independent; each thread runs the unchanged oracle)."""
+    batch = inp["u"].shape[0]
+
+    def one(b):
+        return ref_scan(_batch_rows(inp, b), None if h0 is None else h0[b:b + 1])
+
+    with ThreadPoolExecutor(max_workers=min(batch, 16)) as ex:
+        parts = list(ex.map(one, range(batch)))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "page1_1536x128_f32", "long_prefill_8x1536x2048_f32",
                                   "large_channel_4x5120x4096_bf16"])
 def test_scan_named_workload_full_size(name):
+    """Each named scan workload at full size, in the launch configuration the
+    benchmark times, against the oracle over the whole y and h_last."""
     s = WORKLOADS[name]
     inp = make_scan_inputs(s)
     y, h = run_scan(inp)
     tol = tol_for(s.dtype)
-    assert not torch.isnan(y).any() and not torch.isnan(h).any()
-    if s.elements <= 1 << 20:
-        yr, hr = ref_scan(inp)
-        assert rel_err(y, yr) <= tol, rel_err(y, yr)
-        assert rel_err(h, hr) <= tol, rel_err(h, hr)
-        return
-    # Sampled whole channels: the oracle on (1, 1, L) slices of the same inputs.
-    ys, yrs, hs, hrs = [], [], [], []
-    for (b, d) in _sample_channels(s, 96, seed=s.seed):
-        g = d // (s.dim // s.ngroups)
-        sl = {"u": inp["u"][b:b + 1, d:d + 1], "delta": inp["delta"][b:b + 1, d:d + 1],
-              "A": inp["A"][d:d + 1], "B": inp["B"][b:b + 1, g:g + 1], "C": inp["C"][b:b + 1, g:g + 1],
-              "D": None if inp["D"] is None else inp["D"][d:d + 1],
-              "z": None if inp["z"] is None else inp["z"][b:b + 1, d:d + 1]}
-        yr, hr = ref_scan(sl)
-        ys.append(y[b, d].numpy())
-        yrs.append(yr[0, 0])
-        hs.append(h[b, d].numpy())
-        hrs.append(hr[0, 0])
-    assert rel_err(np.stack(ys), np.stack(yrs)) <= tol, rel_err(np.stack(ys), np.stack(yrs))
-    assert rel_err(np.stack(hs), np.stack(hrs)) <= tol, rel_err(np.stack(hs), np.stack(hrs))
+    yr, hr = ref_scan_rows(inp)
+    ey, eh = rel_err(y, yr), rel_err(h, hr)
+    print(f"{name}: whole-tensor rel err y {ey:.3e}, h_last {eh:.3e} (bar {tol:g})")
+    assert ey <= tol, ey
+    assert eh <= tol, eh
 
 
 # ---------------------------------------------------------------------------
@@ -406,27 +441,16 @@ def test_ssd_split_continuation_in_place(L1):
 
 
 def test_ssd_named_workload_full_size():
+    """The SSD workload (batch 32, 256 steps, 32 heads x 64, dstate 128) at
+    full size against the oracle over the whole y and h_last."""
     s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
     inp = make_ssd_inputs(s)
     y, h = run_ssd(inp)
-    assert not torch.isnan(y).any() and not torch.isnan(h).any()
-    rng = np.random.default_rng(s.seed)
-    pairs = rng.choice(s.batch * s.nheads, size=48, replace=False)
-    ys, yrs, hs, hrs = [], [], [], []
-    for i in sorted(int(v) for v in pairs):
-        b, hd = divmod(i, s.nheads)
-        g = hd // (s.nheads // s.ngroups)
-        sl = {"x": inp["x"][b:b + 1, :, hd:hd + 1], "dt": inp["dt"][b:b + 1, :, hd:hd + 1],
-              "A": inp["A"][hd:hd + 1], "B": inp["B"][b:b + 1, :, g:g + 1],
-              "C": inp["C"][b:b + 1, :, g:g + 1],
-              "D": None if inp["D"] is None else inp["D"][hd:hd + 1], "z": None}
-        yr, hr = ref_ssd(sl)
-        ys.append(y[b, :, hd].numpy())
-        yrs.append(yr[0, :, 0])
-        hs.append(h[b, hd].numpy())
-        hrs.append(hr[0, 0])
-    assert rel_err(np.stack(ys), np.stack(yrs)) <= TOL_BF16, rel_err(np.stack(ys), np.stack(yrs))
-    assert rel_err(np.stack(hs), np.stack(hrs)) <= TOL_BF16, rel_err(np.stack(hs), np.stack(hrs))
+    yr, hr = ref_ssd(inp)
+    ey, eh = rel_err(y, yr), rel_err(h, hr)
+    print(f"ssd_32x256_h32p64n128_bf16: whole-tensor rel err y {ey:.3e}, h_last {eh:.3e} (bar {TOL_BF16:g})")
+    assert ey <= TOL_BF16, ey
+    assert eh <= TOL_BF16, eh
 
 
 def test_ssd_deterministic():
@@ -622,26 +646,45 @@ def test_scan_backward_long_prefill_full_size():
         assert err <= TOL_BWD_F32, (k, err)
 
 
-def test_scan_backward_large_channel_sampled():
+def ref_scan_bwd_rows(inp, dy, dh_last=None):
+    """The oracle backward over the whole tensor, one host thread per batch row
+    (every gradient but dA and dD is per batch row; those two sum over batch
+    rows, and the rows' float64 sums are added here)."""
+    batch = inp["u"].shape[0]
+
+    def one(b):
+        r = _batch_rows(inp, b)
+        return oracle.scan_bwd(r["u"], r["delta"], r["A"], r["B"], r["C"], r["D"], r["z"], None,
+                               dy[b:b + 1], None if dh_last is None else dh_last[b:b + 1])
+
+    with ThreadPoolExecutor(max_workers=min(batch, 16)) as ex:
+        parts = list(ex.map(one, range(batch)))
+    out = {}
+    for k in ("du", "ddelta", "dB", "dC", "dz", "dh0"):
+        out[k] = None if parts[0][k] is None else np.concatenate([p[k] for p in parts])
+    for k in ("dA", "dD"):
+        out[k] = None if parts[0][k] is None else np.sum([p[k] for p in parts], axis=0)
+    return out
+
+
+def test_scan_backward_large_channel_full_size():
     """The large-channel workload (4 x 5120 channels x 4096 steps, bf16) at
-    full size.  Per-channel gradients (du, ddt, dz, dh0, and dA, dD, which sum
-    over batch rows only) of 32 sampled channels against the oracle on those
-    channels' slice; dB and dC sum over all 5120 channels and are covered at
-    full size by the long-prefill test."""
+    full size: every gradient (du, ddelta, dz, dA, dB, dC, dD, dh0) over the
+    whole tensor against the oracle backward."""
     s = WORKLOADS["large_channel_4x5120x4096_bf16"]
     inp = make_scan_inputs(s)
     dy = make_state((s.batch, s.dim, s.seqlen), seed=5900).to(torch.bfloat16)
     g = ssm.scan_bwd(_dev(inp["u"]), _dev(inp["delta"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
                      _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy))
     torch.cuda.synchronize()
-    ch = torch.from_numpy(np.sort(np.random.default_rng(5901).choice(s.dim, size=32, replace=False)))
-    sl = lambda t: t[:, ch].contiguous()
-    ref = oracle.scan_bwd(sl(inp["u"]), sl(inp["delta"]), inp["A"][ch].contiguous(), inp["B"], inp["C"],
-                          inp["D"][ch].contiguous(), sl(inp["z"]), None, sl(dy), None)
-    got = {"du": g["du"].cpu()[:, ch], "ddelta": g["ddelta"].cpu()[:, ch], "dz": g["dz"].cpu()[:, ch],
-           "dh0": g["dh0"].cpu()[:, ch], "dA": g["dA"].cpu()[ch], "dD": g["dD"].cpu()[ch]}
-    for k, v in got.items():
-        err = rel_err(v.float(), ref[k])
+    g = {k: (None if v is None else v.cpu()) for k, v in g.items()}
+    ref = ref_scan_bwd_rows(inp, dy)
+    errs = {}
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        errs[k] = rel_err(g[k].float(), ref[k])
+    print("large_channel_4x5120x4096_bf16 backward: whole-tensor rel err " +
+          ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    for k, err in errs.items():
         assert err <= TOL_BF16, (k, err)
 
 
@@ -727,25 +770,17 @@ def test_ssd_trap_lam_one_equals_ssd_bitwise():
 
 def test_ssd_trap_named_workload_full_size():
     """The SSD workload's shapes (batch 32, 256 steps, 32 heads x 64, dstate
-    128) with trapezoid weights; 48 sampled (batch, head) pairs checked."""
+    128) with trapezoid weights, against the oracle over the whole y and
+    h_last."""
     s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
     inp = make_ssd_inputs(s)
     lam = make_lam((s.batch, s.seqlen, s.nheads), seed=6400)
     y, h = run_trap(inp, lam)
-    assert not torch.isnan(y).any() and not torch.isnan(h).any()
-    rng = np.random.default_rng(6401)
-    pairs = rng.choice(s.batch * s.nheads, size=48, replace=False)
-    ys, yrs, hs, hrs = [], [], [], []
-    for i in sorted(int(v) for v in pairs):
-        b, hd = divmod(i, s.nheads)
-        sl = dict(x=inp["x"][b:b + 1, :, hd:hd + 1], dt=inp["dt"][b:b + 1, :, hd:hd + 1],
-                  lam=lam[b:b + 1, :, hd:hd + 1], A=inp["A"][hd:hd + 1], B=inp["B"][b:b + 1],
-                  C=inp["C"][b:b + 1], D=None if inp["D"] is None else inp["D"][hd:hd + 1])
-        yr, hr = oracle.ssd_trap(sl["x"], sl["dt"], sl["lam"], sl["A"], sl["B"], sl["C"], sl["D"])
-        ys.append(y[b, :, hd].numpy()); yrs.append(yr[0, :, 0])
-        hs.append(h[b, hd].numpy()); hrs.append(hr[0, 0])
-    assert rel_err(np.stack(ys), np.stack(yrs)) <= TOL_BF16
-    assert rel_err(np.stack(hs), np.stack(hrs)) <= TOL_BF16
+    yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"])
+    ey, eh = rel_err(y, yr), rel_err(h, hr)
+    print(f"ssd_trap on the SSD workload's shapes: whole-tensor rel err y {ey:.3e}, h_last {eh:.3e}")
+    assert ey <= TOL_BF16, ey
+    assert eh <= TOL_BF16, eh
 
 
 # ---------------------------------------------------------------------------

@@ -39,6 +39,20 @@ def rel_err(got, want) -> float:
     return float(np.max(diff)) / (scale if scale > 0 else 1.0)
 
 
+def angle_err(got, want) -> float:
+    """Largest difference of two angle arrays modulo 2 pi, over pi (the
+    library returns the angle reduced to [-pi, pi]; only its value modulo
+    2 pi matters), and inf if any returned angle is outside [-pi, pi]."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if got.size == 0:
+        return 0.0
+    if np.isnan(got).any() or np.abs(got).max() > np.pi * (1 + 1e-6):
+        return float("inf")
+    d = np.remainder(got - want + np.pi, 2 * np.pi) - np.pi
+    return float(np.abs(d).max()) / np.pi
+
+
 def _inputs(batch, L, H, G, N, TH, dtype, seed, theta_scale):
     rng = np.random.default_rng(seed)
     dt = np.logaddexp(0.0, rng.standard_normal((batch, L, H)) - 4.6)  # softplus: steps around 0.01
@@ -85,7 +99,7 @@ def test_rope_matches_oracle(case):
     rb, rc, ra = oracle.rope_bc(dt, theta, B, C, a0)
     tol = TOL_F32 if din == dout == "f32" else TOL_BF16
     assert rel_err(br, rb) <= tol and rel_err(cr, rc) <= tol, (rel_err(br, rb), rel_err(cr, rc))
-    assert rel_err(al, ra) <= TOL_F32, rel_err(al, ra)
+    assert angle_err(al, ra) <= TOL_F32, angle_err(al, ra)
 
 
 @pytest.mark.parametrize("with_bias", [True, False])
@@ -97,7 +111,7 @@ def test_rope_dt_softplus(with_bias):
     br, cr, al = _run(raw, theta, B, C, angle0, torch.float32, dt_softplus=True,
                       dt_bias=None if bias is None else bias.cuda())
     rb, rc, ra = oracle.rope_bc(raw, theta, B, C, angle0, dt_softplus=True, dt_bias=bias)
-    assert max(rel_err(br, rb), rel_err(cr, rc), rel_err(al, ra)) <= TOL_F32
+    assert max(rel_err(br, rb), rel_err(cr, rc), angle_err(al, ra)) <= TOL_F32
 
 
 def test_rope_chained_in_place():
@@ -115,7 +129,35 @@ def test_rope_chained_in_place():
     torch.cuda.synchronize()
     got_b = torch.cat([o[0] for o in outs], dim=1).float().cpu()
     got_c = torch.cat([o[1] for o in outs], dim=1).float().cpu()
-    assert max(rel_err(got_b, rb), rel_err(got_c, rc), rel_err(ang.cpu(), ra)) <= TOL_F32
+    assert max(rel_err(got_b, rb), rel_err(got_c, rc), angle_err(ang.cpu(), ra)) <= TOL_F32
+
+
+def test_rope_chained_large_angles():
+    """Four chained calls whose running angle grows past 10^4 rad (theta with
+    a mean of 400, steps around 0.01: ~4 rad per step over 3000 steps).  The
+    angle handed from call to call is reduced modulo 2 pi before its float32
+    store, so every piece rotates as one float64 call over the whole sequence
+    would (float32 bar)."""
+    batch, L, H, G, N = 1, 3000, 2, 1, 32
+    rng = np.random.default_rng(71)
+    dt = torch.from_numpy(np.logaddexp(0.0, rng.standard_normal((batch, L, H)) - 4.6)).float()
+    theta = torch.from_numpy(400.0 + 5.0 * rng.standard_normal((batch, L, H, N // 2))).float()
+    B = torch.from_numpy(rng.standard_normal((batch, L, G, N)) / np.sqrt(N)).float()
+    C = torch.from_numpy(rng.standard_normal((batch, L, G, N)) / np.sqrt(N)).float()
+    angle0 = torch.from_numpy(rng.uniform(-3.0, 3.0, (batch, H, N // 2))).float()
+    rb, rc, ra = oracle.rope_bc(dt, theta, B, C, angle0)
+    assert np.abs(ra).max() > 1e4
+    ang = angle0.cuda().clone()
+    outs = []
+    for lo, hi in ((0, 700), (700, 1500), (1500, 1501), (1501, 3000)):
+        sl = lambda t: t[:, lo:hi].contiguous().cuda()
+        b_rot, c_rot, _ = ssm.rope_bc(sl(dt), sl(theta), sl(B), sl(C), angle0=ang, angle_last=ang)
+        outs.append((b_rot, c_rot))
+    torch.cuda.synchronize()
+    got_b = torch.cat([o[0] for o in outs], dim=1).cpu()
+    got_c = torch.cat([o[1] for o in outs], dim=1).cpu()
+    errs = (rel_err(got_b, rb), rel_err(got_c, rc), angle_err(ang.cpu(), ra))
+    assert max(errs) <= TOL_F32, errs
 
 
 @pytest.mark.parametrize("trap", [False, True])
@@ -155,7 +197,7 @@ def test_rope_named_workload_full_size():
     br, cr, al = _run(inp["dt"], theta, inp["B"], inp["C"], None, torch.bfloat16)
     rb, rc, ra = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
     assert max(rel_err(br, rb), rel_err(cr, rc)) <= TOL_BF16
-    assert rel_err(al, ra) <= TOL_F32
+    assert angle_err(al, ra) <= TOL_F32
 
 
 def test_rope_prefill_then_decode_steps():
