@@ -152,6 +152,27 @@ SSM_API int ssm_scan_fwd(const void *u, const void *delta, const float *A, const
                  float *h_last, const ssm_scan_dims_t *dims, void *stream);
 
 /*
+ * Allocation-free selective-scan forward, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, math,
+ * supported sizes and checks as ssm_scan_fwd; dims->workspace and
+ * dims->workspace_bytes are ignored.  The chunked carry (needed only when
+ * ssm_scan_resolved_chunks() > 1: 8 * batch * dim * (chunks - 1) * dstate
+ * bytes) lives instead in a static device array of 16 MiB that the library
+ * holds on each GPU it runs on until the process ends; a call whose carry
+ * would exceed it returns SSM_ERR_WORKSPACE and launches nothing.  The call
+ * allocates and frees nothing (its first call on a device looks up that
+ * device's copy of the array).  Every chunk's carry is written before it is
+ * read within one call, so nothing in the array needs clearing; but all calls
+ * on one GPU share the array, so calls that may overlap in time on one GPU
+ * (on different streams, or from several host threads) race and must be
+ * serialised by the caller.
+ */
+SSM_API int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B,
+                         const void *C, const float *D, const void *z, const float *h0, void *y,
+                         float *h_last, const ssm_scan_dims_t *dims, void *stream);
+
+/*
  * Workspace ssm_scan_bwd needs for `dims` (n_chunks is ignored), 4 bytes per
  * float: the forward state every 16 steps, batch * dim * dstate *
  * ceil(seqlen / 16) floats; the dB and dC terms of every tile of

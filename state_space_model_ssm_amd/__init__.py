@@ -17,7 +17,7 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
-    "scan_fwd", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
+    "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
     "rope_bc", "RopeDims",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
@@ -94,6 +94,8 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int
         L.ssm_scan_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(ScanDims), vp]
         L.ssm_scan_fwd.restype = i32
+        L.ssm_scan_fwd_noalloc.argtypes = [vp] * 10 + [ctypes.POINTER(ScanDims), vp]
+        L.ssm_scan_fwd_noalloc.restype = i32
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssm_scan_workspace_size.restype = i32
         L.ssm_scan_resolved_chunks.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_int32)]
@@ -283,6 +285,39 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, *, h0=None, out_dtype=None, n_ch
     rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     _check(rc)
+    return y, h_last
+
+
+def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, *, y, h_last=None, h0=None, n_chunks: int = 0,
+                     stream=None, dt_softplus: bool = False, dt_bias=None):
+    """Selective-scan forward through ``ssm_scan_fwd_noalloc``: the library's
+    static scratch holds the chunked carry, so the call allocates nothing.
+    The caller passes y (and h_last, if wanted) preallocated; arguments are
+    otherwise those of ``scan_fwd``.  Returns ``(y, h_last)``."""
+    torch = _torch()
+    in_code = _dtype_code(u.dtype)
+    out_code = _dtype_code(y.dtype)
+    batch, dim, L = u.shape
+    N = B.shape[2]
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z)):
+        if t is not None and t.dtype != u.dtype:
+            raise TypeError(f"{name} must have dtype {u.dtype}")
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("delta and z must have the shape of u")
+    if B.dim() != 4 or B.shape[0] != batch or B.shape[3] != L or C.shape != B.shape:
+        raise ValueError("B and C must be (batch, ngroups, dstate, seqlen)")
+    if A.shape != (dim, N) or A.dtype != torch.float32 or (D is not None and (D.shape != (dim,) or
+                                                                             D.dtype != torch.float32)):
+        raise ValueError("A must be float32 (dim, dstate) and D float32 (dim,)")
+    if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, dim, N)):
+        raise ValueError("h0 must be float32 (batch, dim, dstate)")
+    _out(y, (batch, dim, L), y.dtype, u, "y")
+    if h_last is not None:
+        _out(h_last, (batch, dim, N), torch.float32, u, "h_last")
+    dims = _scan_dims(u, B, in_code, out_code, n_chunks)
+    _phase0(dims, dim, dt_softplus, dt_bias)
+    _check(lib().ssm_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                      _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream)))
     return y, h_last
 
 

@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ssm_internal.h"
@@ -155,9 +156,49 @@ int ssm_scan_resolved_chunks(const ssm_scan_dims_t *dims, int32_t *n_chunks) {
   return ok();
 }
 
-int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+}  // extern "C"
+
+namespace {
+
+// Scratch of ssm_scan_fwd_noalloc: the chunked carry of every call on a
+// device lives in this file-scope array (one copy per device, held until the
+// process ends).  Host code never uses the array's name as an address: the
+// device address is looked up once per device with hipGetSymbolAddress and
+// kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call there).
+int scratch_on_current_device(float **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSM_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(SSM_ERR_HIP, "hipGetSymbolAddress of the static scratch failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float *>(g_scratch_ptr[dev]);
+  return SSM_OK;
+}
+
+// ssm_scan_fwd and ssm_scan_fwd_noalloc: the same checks and kernels; the
+// chunked carry lives in the caller's workspace, or (noalloc) in `scratch`.
+int scan_fwd_run(const void *u, const void *delta, const float *A, const void *B, const void *C,
                  const float *D, const void *z, const float *h0, void *y, float *h_last,
-                 const ssm_scan_dims_t *dims, void *stream) {
+                 const ssm_scan_dims_t *dims, void *stream, bool noalloc) {
   int rc = check_scan_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssm_scan_dims_t &d = *dims;
@@ -188,7 +229,13 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   if (overlap(s0, sh) && !(h0 == h_last && chunks == 1))
     return fail(SSM_ERR_SHAPE, "h_last overlaps h0 (only h_last == h0 with one pass is allowed)");
   const size_t need = scan_workspace(&d, chunks);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > kScratchBytes)
+      return fail(SSM_ERR_WORKSPACE,
+                  "the chunked carry of %d chunks needs %zu bytes, more than the %zu-byte static scratch of "
+                  "ssm_scan_fwd_noalloc (ask for fewer chunks)",
+                  chunks, need, kScratchBytes);
+  } else if (need > 0) {
     if (!d.workspace || d.workspace_bytes < need)
       return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required for %d chunks (got %zu)", need,
                   chunks, d.workspace ? d.workspace_bytes : (size_t)0);
@@ -200,6 +247,15 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
     if (overlap(sw, sy) || overlap(sw, sh)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
   }
   if (d.batch == 0 || d.dim == 0) return ok();
+  float *carry = nullptr;
+  if (need > 0) {
+    if (noalloc) {
+      rc = scratch_on_current_device(&carry);
+      if (rc != SSM_OK) return rc;
+    } else {
+      carry = static_cast<float *>(d.workspace);
+    }
+  }
 
   ssm::ScanParams p{};
   p.u = u;
@@ -214,7 +270,7 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
   p.h_last = h_last;
   p.dt_bias = d.dt_bias;
   p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
-  p.carry = static_cast<float *>(need > 0 ? d.workspace : nullptr);
+  p.carry = carry;
   p.batch = d.batch;
   p.dim = d.dim;
   p.seqlen = d.seqlen;
@@ -231,6 +287,22 @@ int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "scan launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_scan_fwd(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *h0, void *y, float *h_last,
+                 const ssm_scan_dims_t *dims, void *stream) {
+  return scan_fwd_run(u, delta, A, B, C, D, z, h0, y, h_last, dims, stream, false);
+}
+
+int ssm_scan_fwd_noalloc(const void *u, const void *delta, const float *A, const void *B, const void *C,
+                         const float *D, const void *z, const float *h0, void *y, float *h_last,
+                         const ssm_scan_dims_t *dims, void *stream) {
+  return scan_fwd_run(u, delta, A, B, C, D, z, h0, y, h_last, dims, stream, true);
 }
 
 // ---------------------------------------------------------------------------

@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -400,3 +400,19 @@ def test_size_returning_workspace_queries_and_error_message():
     sd.headdim = 32
     assert lib.ssd_workspace_bytes(ctypes.byref(sd)) == size_max
     assert b"headdim" in lib.ssm_last_error_message()
+
+
+def test_noalloc_scan_rejects_a_carry_beyond_its_scratch():
+    """ssm_scan_fwd_noalloc runs the same host checks as ssm_scan_fwd, and a
+    chunked carry larger than its 16 MiB static scratch is SSM_ERR_WORKSPACE
+    before any HIP call (8 * 4 * 4096 * 63 * 16 bytes = 132 MB here)."""
+    lib = ssm.lib()
+    d = _dims(batch=4, dim=4096, dstate=16, seqlen=8192, n_chunks=64)
+    G = 1 << 30  # the fake tensors (512 MiB each) must not overlap
+    rc = lib.ssm_scan_fwd_noalloc(FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G, FAKE + 4 * G,
+                                  None, None, None, FAKE + 5 * G, None, ctypes.byref(d), None)
+    assert rc == -6 and b"static scratch" in lib.ssm_last_error()
+    d = _dims(dstate=12)
+    rc = lib.ssm_scan_fwd_noalloc(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                  None, None, None, FAKE + 0x10000000, None, ctypes.byref(d), None)
+    assert rc == -5
