@@ -39,7 +39,7 @@ class Oracle:
         lib.oracle_scan_f64.argtypes = [i64] * 5 + [dp] * 10
         lib.oracle_scan_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.argtypes = [i64] * 6 + [dp] * 10
-        lib.oracle_ssd_trap_f64.argtypes = [i64] * 6 + [dp] * 11
+        lib.oracle_ssd_trap_f64.argtypes = [i64] * 6 + [dp] * 13
         lib.oracle_ssd_trap_f64.restype = ctypes.c_int
         lib.oracle_scan_bwd_f64.argtypes = [i64] * 5 + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
@@ -123,22 +123,27 @@ class Oracle:
             raise ValueError("oracle_scan_f64 rejected the shapes")
         return y, h
 
-    def ssd_trap(self, x, dt, lam, A, B, C, D=None, z=None, h0=None):
+    def ssd_trap(self, x, dt, lam, A, B, C, D=None, z=None, h0=None, x_prev=None, B_prev=None):
         """Trapezoidal (three-term) SSD in float64. Returns (y, h_last).
 
         x, z: (batch, L, H, P); dt, lam: (batch, L, H); B, C: (batch, L, G, N);
-        A, D: (H,); h0, h_last: (batch, H, P, N).
+        A, D: (H,); h0, h_last: (batch, H, P, N); x_prev (batch, H, P) and
+        B_prev (batch, G, N): the token before the sequence (both or neither).
         """
         x, dt, lam, A, B, C, D, z, h0 = map(f64, (x, dt, lam, A, B, C, D, z, h0))
+        x_prev, B_prev = f64(x_prev), f64(B_prev)
         batch, L, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         assert dt.shape == (batch, L, H) and lam.shape == dt.shape and A.shape == (H,)
         assert B.shape == (batch, L, G, N) and C.shape == B.shape
         assert h0 is None or h0.shape == (batch, H, P, N)
+        assert (x_prev is None) == (B_prev is None)
+        assert x_prev is None or (x_prev.shape == (batch, H, P) and B_prev.shape == (batch, G, N))
         y = np.zeros_like(x)
         h = np.zeros((batch, H, P, N))
         rc = self.lib.oracle_ssd_trap_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(lam), _ptr(A),
-                                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h))
+                                          _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev),
+                                          _ptr(B_prev), _ptr(y), _ptr(h))
         if rc != 0:
             raise ValueError("oracle_ssd_trap_f64 rejected the shapes")
         return y, h
@@ -237,15 +242,28 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, 
 
 
 def ssd_trap(x, dt, lam, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None,
-             lam_sigmoid=False):
+             lam_sigmoid=False, x_prev=None, B_prev=None):
     """Trapezoidal SSD in float64 with the default build; see ``Oracle.ssd_trap``.
-    dt_softplus / lam_sigmoid: dt and lam hold raw values (Phase-0 maps)."""
+    dt_softplus / lam_sigmoid: dt and lam hold raw values (Phase-0 maps).
+    x_prev, B_prev: the token before the sequence (its previous-token term)."""
     o = _load()
     if dt_softplus:
         dt = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
     if lam_sigmoid:
         lam = o.sigmoid(lam).reshape(f64(lam).shape)
-    return o.ssd_trap(x, dt, lam, A, B, C, D, z, h0)
+    return o.ssd_trap(x, dt, lam, A, B, C, D, z, h0, x_prev, B_prev)
+
+
+def ssd_trap_step(x, dt, lam, A, B, C, D=None, z=None, state=None, x_prev=None, B_prev=None,
+                  dt_softplus=False, dt_bias=None, lam_sigmoid=False):
+    """One decode step of the trapezoidal SSD: ``ssd_trap`` with seqlen 1,
+    h0 = state and the previous token's x_prev (batch, H, P) and B_prev
+    (batch, G, N).  x, z: (batch, H, P); dt, lam: (batch, H); B, C:
+    (batch, G, N); state: (batch, H, P, N).  Returns (y (batch, H, P), new state)."""
+    row = lambda a: None if a is None else f64(a)[:, None]
+    y, h = ssd_trap(row(x), row(dt), row(lam), A, row(B), row(C), D, row(z), state, dt_softplus, dt_bias,
+                    lam_sigmoid, x_prev, B_prev)
+    return y[:, 0], h
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None):

@@ -261,28 +261,36 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
  *   H_t = alpha_t H_{t-1} + beta_t (B_{t-1} x_{t-1}) + gamma_t (B_t x_t),
  * read out as y_t = C_t . H_t; Phase 5 adds the D skip and the silu gate.
  * Before the first token H is h0 (zero when NULL) and the previous input
- * B_{-1} x_{-1} is zero.  h_last is H after the last token.
+ * B_{-1} x_{-1} is the outer product of the token before the sequence,
+ * x_prev (batch, nheads, headdim) and B_prev (batch, ngroups, dstate), or zero
+ * when both are NULL (the step() decode path of the same section carries this
+ * previous-token term from call to call).  h_last is H after the last token.
  *   lam : (batch, seqlen, nheads); other layouts as oracle_ssd_f64.
- * Returns 0, or -1 on a bad shape.
+ * Returns 0, or -1 on a bad shape (or only one of x_prev, B_prev given).
  */
 int oracle_ssd_trap_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                         int64_t dstate, int64_t ngroups, const double *x, const double *dt,
                         const double *lam, const double *A, const double *B, const double *C,
                         const double *Dskip, const double *z, const double *h0,
+                        const double *x_prev, const double *B_prev,
                         double *y, double *h_last)
 {
     if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1 ||
-        ngroups < 1 || nheads % ngroups != 0 || headdim * dstate > 65536)
+        ngroups < 1 || nheads % ngroups != 0 || headdim * dstate > 65536 ||
+        (x_prev == NULL) != (B_prev == NULL))
         return -1;
     static double H[65536], prev[65536];
     const int64_t hpg = nheads / ngroups;
     for (int64_t b = 0; b < batch; ++b) {
         for (int64_t hd = 0; hd < nheads; ++hd) {
             const int64_t g = hd / hpg;
-            for (int64_t k = 0; k < headdim * dstate; ++k) {
+            for (int64_t k = 0; k < headdim * dstate; ++k)
                 H[k] = h0 ? h0[(b * nheads + hd) * headdim * dstate + k] : 0.0;
-                prev[k] = 0.0;
-            }
+            for (int64_t p = 0; p < headdim; ++p)
+                for (int64_t n = 0; n < dstate; ++n)
+                    prev[p * dstate + n] = x_prev ? B_prev[(b * ngroups + g) * dstate + n] *
+                                                        x_prev[(b * nheads + hd) * headdim + p]
+                                                  : 0.0;
             for (int64_t t = 0; t < seqlen; ++t) {
                 const double d = dt[(b * seqlen + t) * nheads + hd];
                 const double lm = lam[(b * seqlen + t) * nheads + hd];

@@ -447,6 +447,51 @@ def check_ssd_trap_single_ssd_form(orc):
                     _close(h[bb, hd], state, what=f"single-SSD form h_last (b{bb} h{hd})")
 
 
+def check_ssd_trap_previous_token(orc):
+    """The previous-token term carried across a split.  (1) A sequence run in
+    two pieces, the second starting from the first's h_last and its last
+    token's x and B (x_prev, B_prev), equals one run over the whole, at every
+    split point, and token-by-token calls chained the same way equal it too
+    ("Mamba-3 NKI Kernels for AWS Neuron", section "How it works": the step()
+    recurrence carries beta * prev_Bx from token to token).  (2) One token
+    with h0 and a previous token, written out:
+    S = alpha h0 + beta x_prev B_prev^T + gamma x_0 B_0^T, y = (S C_0 + D x_0) silu(z_0),
+    with alpha = exp(dt A), gamma = lam dt, beta = (dt - gamma) alpha."""
+    rng = np.random.default_rng(63)
+    b, L, H, P, N, G = 2, 10, 4, 3, 5, 2
+    v = _trap_inputs(rng, b, L, H, P, N, G)
+    args = lambda t0, t1: [v[k][:, t0:t1] for k in ("x", "dt", "lam")] + [v["A"]] + \
+        [v[k][:, t0:t1] for k in ("B", "C")] + [v["D"], v["z"][:, t0:t1]]
+    y, h = orc.ssd_trap(*args(0, L), v["h0"])
+    for L1 in (1, 4, 9):
+        y1, h1 = orc.ssd_trap(*args(0, L1), v["h0"])
+        y2, h2 = orc.ssd_trap(*args(L1, L), h1, v["x"][:, L1 - 1], v["B"][:, L1 - 1])
+        _close(np.concatenate([y1, y2], axis=1), y, rtol=1e-12, what=f"split at {L1}: y")
+        _close(h2, h, rtol=1e-12, what=f"split at {L1}: h_last")
+    st, ys, xp, bp = v["h0"], [], None, None
+    for t in range(L):
+        yt, st = orc.ssd_trap(*args(t, t + 1), st, xp, bp)
+        ys.append(yt)
+        xp, bp = v["x"][:, t], v["B"][:, t]
+    _close(np.concatenate(ys, axis=1), y, rtol=1e-12, what="token-by-token chain: y")
+    _close(st, h, rtol=1e-12, what="token-by-token chain: h_last")
+    xp, bp = rng.standard_normal((b, H, P)), rng.standard_normal((b, G, N))
+    y1, h1 = orc.ssd_trap(*args(0, 1), v["h0"], xp, bp)
+    for bb in range(b):
+        for hd in range(H):
+            g = hd // (H // G)
+            dt, lam = v["dt"][bb, 0, hd], v["lam"][bb, 0, hd]
+            alpha = np.exp(dt * v["A"][hd])
+            gamma = lam * dt
+            beta = (dt - gamma) * alpha
+            S = alpha * v["h0"][bb, hd] + beta * np.outer(xp[bb, hd], bp[bb, g]) + \
+                gamma * np.outer(v["x"][bb, 0, hd], v["B"][bb, 0, g])
+            zt = v["z"][bb, 0, hd]
+            yt = (S @ v["C"][bb, 0, g] + v["D"][hd] * v["x"][bb, 0, hd]) * zt / (1 + np.exp(-zt))
+            _close(y1[bb, 0, hd], yt, what=f"one token with a previous token: y (b{bb} h{hd})")
+            _close(h1[bb, hd], S, what=f"one token with a previous token: h_last (b{bb} h{hd})")
+
+
 def _rel_close(got, want, rtol, what):
     got, want = np.asarray(got, dtype=np.float64), np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, f"{what}: shape {got.shape} != {want.shape}"
@@ -604,6 +649,7 @@ ALL_CHECKS = [
     check_scan_bwd_finite_differences,
     check_ssd_trap_lam_one_is_ssd,
     check_ssd_trap_single_ssd_form,
+    check_ssd_trap_previous_token,
     check_phase0_softplus,
     check_phase0_sigmoid_and_softplus_grad,
     check_rope_closed_form,

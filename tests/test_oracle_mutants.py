@@ -4,7 +4,7 @@ the definition: the decay and its sign, the dt on the input, the readout order,
 B versus C, the D skip, the gate and its order, the group index, the B/C
 layout, the initial state and the final state; and each term of the backward
 (the adjoint's decay, the state each gradient uses, the gate derivative, the
-upstream state gradient); and the rotary step on B and C (the angle's sign
+upstream state gradient); the trapezoid's previous-token term; and the rotary step on B and C (the angle's sign
 and running sum, the rotation, the pairing of states, the group, the per-head
 angles, the starting angle, C's rotation)."""
 import os
@@ -48,6 +48,11 @@ MUTANTS = [
     ("trap_gamma_ignores_lam", [("const double gamma = lm * d;", "const double gamma = d;")]),
     ("trap_prev_updated_first", [("H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;\n                        prev[k] = bx;",
                                   "prev[k] = bx;\n                        H[k] = alpha * H[k] + beta * prev[k] + gamma * bx;")]),
+    ("trap_prev_ignored", [("prev[p * dstate + n] = x_prev ?", "prev[p * dstate + n] = 0 ?")]),
+    ("trap_prev_group_index", [("B_prev[(b * ngroups + g) * dstate + n]",
+                                "B_prev[(b * ngroups + hd % ngroups) * dstate + n]")]),
+    ("trap_prev_head_index", [("x_prev[(b * nheads + hd) * headdim + p]",
+                               "x_prev[(b * nheads + g) * headdim + p]")]),
     ("bwd_no_decay_in_adjoint", [("lam[n] = abar * l;", "lam[n] = l;")]),
     ("bwd_dA_uses_new_state", [("dA[d * dstate + n] += l * dl * abar * hprev;",
                                 "dA[d * dstate + n] += l * dl * abar * hs[(t + 1) * dstate + n];")]),
