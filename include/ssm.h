@@ -309,17 +309,23 @@ SSM_API int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const
  *     dt_{s+1} (1 - lam_{s+1}) at later steps, plus a diagonal correction
  *     (weight gamma_s at its own step), chunk 64.
  * Arguments, layouts and supported sizes are those of ssd_chunked_fwd, plus
- *   lam : (batch, seqlen, nheads) bf16, 2-byte aligned.
- * h0 is the state S before the first token; the previous-token term of the
- * first token is zero, so a call continues an earlier one exactly only when
- * that one's last token has lam = 1.  h_last is S after the last token.
+ *   lam    : (batch, seqlen, nheads) bf16, 2-byte aligned;
+ *   x_prev : (batch, nheads, headdim) bf16, 16-byte aligned, nullable;
+ *   B_prev : (batch, ngroups, dstate) bf16, 16-byte aligned, nullable;
+ * x_prev and B_prev are the token before the sequence (given together or not
+ * at all): the first token's previous-token term is beta_0 x_prev B_prev^T,
+ * or zero when they are NULL.  h0 is the state S before the first token and
+ * h_last is S after the last token, so a call on steps [L1, L) with h0 = the
+ * h_last of a call on [0, L1) and x_prev, B_prev = x and B of step L1 - 1
+ * continues that sequence exactly (and ssd_trap_step continues it token by
+ * token the same way).
  * The rotary and normalisation steps that precede the SSD core in Mamba-3
  * are not part of this call.
  */
 SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A,
                          const void *B, const void *C, const float *D, const void *z,
-                         const float *h0, void *y, float *h_last, const ssd_dims_t *dims,
-                         void *stream);
+                         const float *h0, const void *x_prev, const void *B_prev, void *y,
+                         float *h_last, const ssd_dims_t *dims, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Rotary step on B and C (Mamba-3 complex-valued state)                     */
@@ -449,6 +455,34 @@ typedef struct {
 SSM_API int ssd_step(const void *x, const void *dt, const float *A, const void *B, const void *C,
              const float *D, const void *z, float *state, void *y, const ssd_step_dims_t *dims,
              void *stream);
+
+/*
+ * One decode step of the trapezoidal (Mamba-3 SISO) SSD: for every (b, h, p),
+ * with alpha = exp(dt[b,h] A[h]), gamma = lam[b,h] dt[b,h] and
+ * beta = (dt[b,h] - gamma) alpha,
+ *   state[p][n] <- alpha state[p][n] + beta x_prev[p] B_prev[n] + gamma x[p] B[n]
+ *   y[p]        = (sum_n C[n] state[p][n] + D[h] x[p]) * silu(z[p])
+ *   [Mamba-3 NKI], "How it works": decode through step() is this direct
+ *     recurrence (its Eq. 9), h_t = alpha h_{t-1} + beta prev_Bx +
+ *     gamma B_t x_t with output C_t^T h_t; Phase 0 gives alpha, beta, gamma
+ *     (lam after its sigmoid: applied by the caller, or by the kernel with
+ *     SSM_LAM_SIGMOID; dt likewise with SSM_DT_SOFTPLUS);
+ *   [Mamba-3 NKI], "Kernel details", mamba3_siso_decode_state_kernel.
+ * x_prev, B_prev: the previous token's x (batch, nheads, headdim) and B
+ *   (batch, ngroups, dstate), in_dtype, given together or not at all (NULL:
+ *   the term is zero, as for the first token of a sequence).  After a
+ *   prefill by ssd_trap_chunked_fwd, pass its last token's x and B (or the
+ *   rotated B); each later step passes the previous step's x and B.  They are
+ *   read only; the caller keeps them.
+ * lam: (batch, nheads) in_dtype.  Other layouts, alignment, flags (plus
+ *   SSM_LAM_SIGMOID) and sizes as ssd_step; no input may overlap y or state.
+ * Equal to ssd_trap_chunked_fwd with seqlen 1, h0 = h_last = state and the
+ * same x_prev, B_prev.
+ */
+SSM_API int ssd_trap_step(const void *x, const void *dt, const void *lam, const float *A, const void *B,
+                  const void *C, const float *D, const void *z, const void *x_prev,
+                  const void *B_prev, float *state, void *y, const ssd_step_dims_t *dims,
+                  void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

@@ -18,6 +18,7 @@ from typing import Optional
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
     "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
+    "ssd_trap_step",
     "rope_bc", "RopeDims",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
@@ -101,7 +102,7 @@ def lib():
         L.ssm_scan_resolved_chunks.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_int32)]
         L.ssm_scan_resolved_chunks.restype = i32
         L.ssd_chunked_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(SsdDims), vp]
-        L.ssd_trap_chunked_fwd.argtypes = [vp] * 11 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_trap_chunked_fwd.argtypes = [vp] * 13 + [ctypes.POINTER(SsdDims), vp]
         L.ssd_trap_chunked_fwd.restype = ctypes.c_int
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
@@ -114,6 +115,8 @@ def lib():
         L.ssm_scan_step.restype = i32
         L.ssd_step.argtypes = [vp] * 9 + [ctypes.POINTER(SsdStepDims), vp]
         L.ssd_step.restype = i32
+        L.ssd_trap_step.argtypes = [vp] * 12 + [ctypes.POINTER(SsdStepDims), vp]
+        L.ssd_trap_step.restype = i32
         L.ssm_rope_bc.argtypes = [vp] * 8 + [ctypes.POINTER(RopeDims), vp]
         L.ssm_rope_bc.restype = i32
         L.ssm_status_string.argtypes = [i32]
@@ -384,7 +387,8 @@ def ssd_workspace_size(dims: SsdDims) -> int:
 
 def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
                     return_h_last: bool = True, y=None, h_last=None, stream=None,
-                    dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False):
+                    dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False,
+                    x_prev=None, B_prev=None):
     """Scalar-decay chunked SSD forward, plain (lam None: ``ssd_chunked_fwd``)
     or trapezoidal (``ssd_trap_chunked_fwd``). Returns ``(y, h_last)``.
 
@@ -414,6 +418,16 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
         raise ValueError("A and D must be (nheads,)")
     if h0 is not None and (h0.dtype != torch.float32 or h0.shape != (batch, H, P, N)):
         raise ValueError("h0 must be float32 (batch, nheads, headdim, dstate)")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev are given together or not at all")
+    if x_prev is not None:
+        if lam is None:
+            raise ValueError("x_prev and B_prev belong to the trapezoidal form")
+        G = B.shape[2]
+        if x_prev.shape != (batch, H, P) or B_prev.shape != (batch, G, N) or x_prev.dtype != x.dtype or \
+                B_prev.dtype != x.dtype:
+            raise ValueError("x_prev must be (batch, nheads, headdim) and B_prev (batch, ngroups, dstate), "
+                             "in the dtype of x")
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
     _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
     with _alloc_on(stream):
@@ -425,8 +439,8 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
                                    _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
     else:
         rc = lib().ssd_trap_chunked_fwd(_ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                        _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims),
-                                        _stream(stream))
+                                        _ptr(z), _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h_last),
+                                        ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last
 
@@ -447,7 +461,9 @@ def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, **kw):
 def ssd_trap_chunked_fwd(x, dt, lam, A, B, C, D=None, z=None, **kw):
     """Trapezoidal (Mamba-3 SISO) chunked SSD (``ssd_trap_chunked_fwd``):
     lam (batch, L, H) bf16 in [0, 1] (after its sigmoid; raw with
-    lam_sigmoid=True).  Otherwise as ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
+    lam_sigmoid=True).  Keywords x_prev (batch, H, P) and B_prev (batch, G, N):
+    the token before the sequence, when the call continues one.  Otherwise as
+    ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
     return _ssd_call(x, dt, lam, A, B, C, D, z, **kw)
 
 
@@ -514,6 +530,47 @@ def ssd_step(x, dt, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, s
     _phase0(dims, H, dt_softplus, dt_bias)
     _check(lib().ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                           _ptr(state), _ptr(y), ctypes.byref(dims), _stream(stream)))
+    return y
+
+
+def ssd_trap_step(x, dt, lam, A, B, C, D=None, z=None, *, state, x_prev=None, B_prev=None, out_dtype=None,
+                  y=None, stream=None, dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False):
+    """One trapezoidal SSD decode step (``ssd_trap_step``); ``state`` is
+    updated in place.  Returns y.
+
+    x, z: (batch, H, P); dt, lam: (batch, H); A, D: (H,) float32; B, C:
+    (batch, G, N); state: (batch, H, P, N) float32; x_prev (batch, H, P) and
+    B_prev (batch, G, N): the previous token's x and B (None for the first
+    token of a sequence).
+    """
+    torch = _torch()
+    in_code = _dtype_code(x.dtype)
+    out_dt = x.dtype if out_dtype is None else out_dtype
+    out_code = _dtype_code(out_dt)
+    for name, t in (("dt", dt), ("lam", lam), ("B", B), ("C", C), ("z", z), ("x_prev", x_prev),
+                    ("B_prev", B_prev)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} must have dtype {x.dtype}")
+    batch, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if dt.shape != (batch, H) or lam.shape != (batch, H) or (z is not None and z.shape != x.shape):
+        raise ValueError("dt and lam must be (batch, H) and z shaped like x")
+    if B.shape != (batch, G, N) or C.shape != B.shape or A.shape != (H,):
+        raise ValueError("B, C must be (batch, ngroups, dstate) and A (nheads,)")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev are given together or not at all")
+    if x_prev is not None and (x_prev.shape != x.shape or B_prev.shape != B.shape):
+        raise ValueError("x_prev must be shaped like x and B_prev like B")
+    if state.dtype != torch.float32 or state.shape != (batch, H, P, N):
+        raise ValueError("state must be float32 (batch, nheads, headdim, dstate)")
+    with _alloc_on(stream):
+        y = _out(y, (batch, H, P), out_dt, x, "y")
+    dims = SsdStepDims(batch=batch, nheads=H, headdim=P, dstate=N, ngroups=G, in_dtype=in_code,
+                       out_dtype=out_code, flags=0, reserved=0)
+    _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
+    _check(lib().ssd_trap_step(_ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(x_prev), _ptr(B_prev), _ptr(state), _ptr(y), ctypes.byref(dims),
+                               _stream(stream)))
     return y
 
 

@@ -212,6 +212,25 @@ ssd_chunk_kernel(const SsdParams p) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
   }
+  if constexpr (TRAP) {
+    // The token before the sequence: the first token's previous-token term
+    // beta_0 x_prev B_prev^T, with beta_0 = dt_0 (1 - lam_0) alpha_0, enters
+    // through the initial state, alpha_0 (S + dt_0 (1 - lam_0) x_prev B_prev^T).
+    if (p.x_prev != nullptr && L > 0) {
+      const int64_t i0 = b * L * H + h;  // dt and lam of this head's step 0
+      const float w0 = step_of(bf2f(gdt[i0])) * (1.0f - lam_of(bf2f(glam[i0])));
+      const float xw = w0 * bf2f(static_cast<const uint16_t *>(p.x_prev)[(b * H + h) * P + pcol]);
+      const uint16_t *bp = static_cast<const uint16_t *>(p.B_prev) + (b * G + g) * N + 4 * q;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(bp + 16 * i);
+        S[i][0] = fmaf(xw, bf2f(static_cast<uint16_t>(v.x)), S[i][0]);
+        S[i][1] = fmaf(xw, bf2f(static_cast<uint16_t>(v.x >> 16)), S[i][1]);
+        S[i][2] = fmaf(xw, bf2f(static_cast<uint16_t>(v.y)), S[i][2]);
+        S[i][3] = fmaf(xw, bf2f(static_cast<uint16_t>(v.y >> 16)), S[i][3]);
+      }
+    }
+  }
   // Retire the initial-state loads here (s_waitcnt vmcnt(0)).  Otherwise they
   // may count as outstanding at the top of the chunk loop, and the first use
   // of S in every chunk would wait for all loads in flight, prefetches included.

@@ -502,8 +502,8 @@ size_t ssd_workspace_bytes(const ssd_dims_t *dims) {
 }
 
 static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, const float *A, const void *B,
-                   const void *C, const float *D, const void *z, const float *h0, void *y, float *h_last,
-                   const ssd_dims_t *dims, void *stream) {
+                   const void *C, const float *D, const void *z, const float *h0, const void *x_prev,
+                   const void *B_prev, void *y, float *h_last, const ssd_dims_t *dims, void *stream) {
   const int rc = check_ssd_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssd_dims_t &d = *dims;
@@ -525,9 +525,15 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
   if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
   if (!aligned(h0, 16) || !aligned(h_last, 16))
     return fail(SSM_ERR_ALIGN, "h0 and h_last must be 16-byte aligned");
+  if ((x_prev == nullptr) != (B_prev == nullptr))
+    return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
+  if (!aligned(x_prev, 16) || !aligned(B_prev, 16))
+    return fail(SSM_ERR_ALIGN, "x_prev and B_prev must be 16-byte aligned");
+  const int64_t n_xp = d.batch * d.nheads * d.headdim, n_bp = d.batch * d.ngroups * d.dstate;
   const Span ins[] = {{x, n_x * 2ull},  {dt, n_dt * 2ull},     {z, n_x * 2ull},
                       {B, n_bc * 2ull}, {C, n_bc * 2ull},     {A, d.nheads * 4ull},
-                      {D, d.nheads * 4ull}, {lam, n_dt * 2ull}, {d.dt_bias, d.nheads * 4ull}};
+                      {D, d.nheads * 4ull}, {lam, n_dt * 2ull}, {d.dt_bias, d.nheads * 4ull},
+                      {x_prev, n_xp * 2ull}, {B_prev, n_bp * 2ull}};
   const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
@@ -542,6 +548,8 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
   p.x = x;
   p.dt = dt;
   p.lam = trap ? lam : nullptr;
+  p.x_prev = trap ? x_prev : nullptr;
+  p.B_prev = trap ? B_prev : nullptr;
   p.B = B;
   p.C = C;
   p.z = z;
@@ -568,13 +576,13 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
 int ssd_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
                     const float *D, const void *z, const float *h0, void *y, float *h_last,
                     const ssd_dims_t *dims, void *stream) {
-  return ssd_run(x, dt, nullptr, false, A, B, C, D, z, h0, y, h_last, dims, stream);
+  return ssd_run(x, dt, nullptr, false, A, B, C, D, z, h0, nullptr, nullptr, y, h_last, dims, stream);
 }
 
 int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A, const void *B,
-                         const void *C, const float *D, const void *z, const float *h0, void *y,
-                         float *h_last, const ssd_dims_t *dims, void *stream) {
-  return ssd_run(x, dt, lam, true, A, B, C, D, z, h0, y, h_last, dims, stream);
+                         const void *C, const float *D, const void *z, const float *h0, const void *x_prev,
+                         const void *B_prev, void *y, float *h_last, const ssd_dims_t *dims, void *stream) {
+  return ssd_run(x, dt, lam, true, A, B, C, D, z, h0, x_prev, B_prev, y, h_last, dims, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -591,22 +599,27 @@ static int step_common(const void *u, const void *delta, const float *A, const v
                        const float *D, const void *z, float *state, void *y, int64_t batch, int64_t chan,
                        int64_t dstate, int64_t ngroups, int64_t headdim, int64_t n_a, int64_t n_dt,
                        int64_t n_d, int32_t in_dtype, int32_t out_dtype, int per_head, int32_t flags,
-                       const float *dt_bias, void *stream) {
+                       const float *dt_bias, void *stream, const void *lam = nullptr,
+                       const void *x_prev = nullptr, const void *B_prev = nullptr) {
   const int64_t n_x = batch * chan;
   const int64_t n_bc = batch * ngroups * dstate;
   const int64_t n_h = n_x * dstate;
   if (n_x > 0 && (!u || !delta || !y || !state)) return fail(SSM_ERR_NULL, "input, dt, state and y are required");
   if (n_bc > 0 && (!B || !C)) return fail(SSM_ERR_NULL, "B and C are required");
   if (n_a > 0 && !A) return fail(SSM_ERR_NULL, "A is required");
+  if ((x_prev == nullptr) != (B_prev == nullptr))
+    return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
   const size_t ei = dtype_size(in_dtype), eo = dtype_size(out_dtype);
-  if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei))
+  if (!aligned(u, ei) || !aligned(delta, ei) || !aligned(B, ei) || !aligned(C, ei) || !aligned(z, ei) ||
+      !aligned(lam, ei) || !aligned(x_prev, ei) || !aligned(B_prev, ei))
     return fail(SSM_ERR_ALIGN, "input pointers must be aligned to %zu bytes", ei);
   if (!aligned(y, eo)) return fail(SSM_ERR_ALIGN, "y must be aligned to %zu bytes", eo);
   if (!aligned(A, 4) || !aligned(D, 4)) return fail(SSM_ERR_ALIGN, "A and D must be 4-byte aligned");
   if (!aligned(state, dstate >= 4 ? 16 : 4))
     return fail(SSM_ERR_ALIGN, "state must be %d-byte aligned", dstate >= 4 ? 16 : 4);
-  const Span ins[] = {{u, n_x * ei}, {delta, n_dt * ei}, {z, n_x * ei}, {B, n_bc * ei},
-                      {C, n_bc * ei}, {A, n_a * 4ull},  {D, n_d * 4ull}, {dt_bias, n_d * 4ull}};
+  const Span ins[] = {{u, n_x * ei},      {delta, n_dt * ei},    {z, n_x * ei},          {B, n_bc * ei},
+                      {C, n_bc * ei},      {A, n_a * 4ull},       {D, n_d * 4ull},        {dt_bias, n_d * 4ull},
+                      {lam, n_dt * ei},    {x_prev, n_x * ei},    {B_prev, n_bc * ei}};
   const Span sy{y, n_x * eo}, ss{state, n_h * 4ull};
   for (const Span &s : ins)
     if (overlap(s, sy) || overlap(s, ss)) return fail(SSM_ERR_SHAPE, "y or the state overlaps an input");
@@ -628,6 +641,10 @@ static int step_common(const void *u, const void *delta, const float *A, const v
   p.y = y;
   p.dt_bias = dt_bias;
   p.dt_softplus = (flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.lam = lam;
+  p.x_prev = x_prev;
+  p.B_prev = B_prev;
+  p.lam_sigmoid = (flags & SSM_LAM_SIGMOID) ? 1 : 0;
   p.batch = batch;
   p.dim = chan;
   p.ngroups = ngroups;
@@ -656,6 +673,37 @@ int ssm_scan_step(const void *u, const void *delta, const float *A, const void *
   return step_common(u, delta, A, B, C, D, z, state, y, d.batch, d.dim, d.dstate, d.ngroups, 1,
                      d.dim * d.dstate, d.batch * d.dim, d.dim, d.in_dtype, d.out_dtype, 0, d.flags, d.dt_bias,
                      stream);
+}
+
+// Checks shared by the SSD decode steps; `allowed` are the flag bits the
+// step takes.
+static int check_ssd_step_dims(const ssd_step_dims_t *dims, int32_t allowed) {
+  if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
+  const ssd_step_dims_t &d = *dims;
+  if (d.batch < 0 || d.nheads < 0) return fail(SSM_ERR_SHAPE, "negative size");
+  if (d.headdim < 1 || d.dstate < 1 || d.ngroups < 1)
+    return fail(SSM_ERR_SHAPE, "headdim, dstate and ngroups must be >= 1");
+  if (d.nheads % d.ngroups != 0) return fail(SSM_ERR_SHAPE, "ngroups must divide nheads");
+  if (!valid_dtype(d.in_dtype) || !valid_dtype(d.out_dtype)) return fail(SSM_ERR_DTYPE, "bad dtype code");
+  if (d.reserved != 0) return fail(SSM_ERR_SHAPE, "reserved must be 0");
+  const int rc = check_dt_flags(d.flags, allowed, d.dt_bias);
+  if (rc != SSM_OK) return rc;
+  if (!step_dstate_ok(d.dstate))
+    return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two up to 256)", (long long)d.dstate);
+  if (d.nheads > 0 && d.headdim > kMaxGridX / d.nheads) return fail(SSM_ERR_UNSUPPORTED, "too many channels");
+  return SSM_OK;
+}
+
+int ssd_trap_step(const void *x, const void *dt, const void *lam, const float *A, const void *B, const void *C,
+                  const float *D, const void *z, const void *x_prev, const void *B_prev, float *state, void *y,
+                  const ssd_step_dims_t *dims, void *stream) {
+  const int rc = check_ssd_step_dims(dims, SSM_DT_SOFTPLUS | SSM_LAM_SIGMOID);
+  if (rc != SSM_OK) return rc;
+  const ssd_step_dims_t &d = *dims;
+  if (d.batch * d.nheads > 0 && !lam) return fail(SSM_ERR_NULL, "lam is required");
+  return step_common(x, dt, A, B, C, D, z, state, y, d.batch, d.nheads * d.headdim, d.dstate, d.ngroups,
+                     d.headdim, d.nheads, d.batch * d.nheads, d.nheads, d.in_dtype, d.out_dtype, 1, d.flags,
+                     d.dt_bias, stream, lam, x_prev, B_prev);
 }
 
 int ssd_step(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
@@ -769,6 +817,6 @@ const char *ssm_last_error(void) { return g_last_error.c_str(); }
 
 const char *ssm_last_error_message(void) { return g_last_error.c_str(); }
 
-int ssm_version(void) { return 400; }
+int ssm_version(void) { return 500; }
 
 }  // extern "C"

@@ -81,6 +81,8 @@ hipError_t launch_scan_bwd(const ScanBwdParams &p, int in_bf16, int out_bf16, hi
 struct SsdParams {
   const void *x, *dt, *B, *C, *z;     // bf16
   const void *lam;                    // bf16 (batch, seqlen, nheads); non-null = trapezoidal form
+  const void *x_prev, *B_prev;        // trapezoid: the token before the sequence, bf16
+                                      // (batch, nheads, headdim) and (batch, ngroups, dstate); nullable
   const float *A, *D;                 // float32; D nullable
   const float *h0;                    // nullable initial state [batch][nheads][headdim][dstate]
   void *y;                            // out dtype
@@ -102,11 +104,14 @@ int ssd_heads_per_block(int64_t batch, int64_t nheads, int64_t ngroups, int max_
 // taken per head (headdim channels per head); the scan step has headdim 1.
 struct StepParams {
   const void *u, *delta, *B, *C, *z;  // in_dtype
+  const void *lam;                    // trapezoidal SSD step: (batch, nheads) in_dtype; else null
+  const void *x_prev, *B_prev;        // trapezoid: the previous token's x (batch, dim) and B
+                                      // (batch, ngroups, dstate), in_dtype; nullable (zero term)
   const float *A, *D;                 // float32; D nullable
   float *state;                       // [batch][dim][dstate], updated in place
   void *y;                            // out_dtype
   const float *dt_bias;               // nullable (per dt element's channel or head); read when dt_softplus
-  int32_t dt_softplus;
+  int32_t dt_softplus, lam_sigmoid;
   int64_t batch, dim, ngroups, headdim;
   int32_t dstate;
 };

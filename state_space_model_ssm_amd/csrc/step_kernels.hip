@@ -10,6 +10,11 @@
 // Per channel (scan step: A is (dim, N), dt is per channel) or per head (SSD
 // step: channel d = (head, p), A and dt are per head, D too).
 //
+// TRAP (SSD step only): the trapezoidal three-term step of the same section
+// (its Eq. 9), with alpha = exp(dt A), gamma = lam dt, beta = (dt - gamma) alpha:
+//   h[n] <- alpha h[n] + beta x_prev B_prev[n] + gamma x B[n]
+// where x_prev, B_prev are the previous token's inputs (zero when absent).
+//
 // The step reads and writes the whole state once, so it is bound by HBM:
 // every thread owns K = 8 consecutive states of one channel (two 16-byte
 // loads and stores in flight per thread: 5.9 TB/s on a 33.6 MB state, against
@@ -35,8 +40,9 @@ __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
 // measured slower.
 constexpr int kStepStates = 8;
 
-template <typename Tin, typename Tout, int N, bool HEAD, bool HAS_Z>
+template <typename Tin, typename Tout, int N, bool HEAD, bool HAS_Z, bool TRAP>
 __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
+  static_assert(!TRAP || HEAD, "the trapezoidal step is per head");
   constexpr int K = N < kStepStates ? N : kStepStates;  // states per thread
   constexpr int TPC = N / K;              // threads per channel (adjacent lanes)
   const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
@@ -73,13 +79,30 @@ __global__ void __launch_bounds__(256) step_kernel(const StepParams p) {
 #pragma unroll
     for (int k = 0; k < K; ++k) h[k] = st_row[k];
   }
-  const float dtu = dt * u;
+  if constexpr (TRAP) {
+    const Tin *__restrict__ glam = static_cast<const Tin *>(p.lam);
+    float lam = ld(glam, b * (p.dim / p.headdim) + hd);
+    if (p.lam_sigmoid) lam = 1.0f / (1.0f + expf(-lam));
+    const float gam = lam * dt;
+    const float decay = __builtin_amdgcn_exp2f(dt * p.A[hd] * kLog2e);
+    const float gu = gam * u;
+    // beta x_prev = (dt - gamma) alpha x_prev; zero without a previous token.
+    const float bxp = p.x_prev != nullptr ? (dt - gam) * decay * ld(static_cast<const Tin *>(p.x_prev), cc) : 0.0f;
+    const Tin *gBp = static_cast<const Tin *>(p.x_prev != nullptr ? p.B_prev : p.B);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const float a = HEAD ? p.A[hd] : p.A[d * N + j * K + k];
-    const float decay = __builtin_amdgcn_exp2f(dt * a * kLog2e);
-    h[k] = fmaf(decay, h[k], dtu * ld(gB, bc + k));
-    part = fmaf(ld(gC, bc + k), h[k], part);
+    for (int k = 0; k < K; ++k) {
+      h[k] = fmaf(decay, h[k], fmaf(bxp, ld(gBp, bc + k), gu * ld(gB, bc + k)));
+      part = fmaf(ld(gC, bc + k), h[k], part);
+    }
+  } else {
+    const float dtu = dt * u;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float a = HEAD ? p.A[hd] : p.A[d * N + j * K + k];
+      const float decay = __builtin_amdgcn_exp2f(dt * a * kLog2e);
+      h[k] = fmaf(decay, h[k], dtu * ld(gB, bc + k));
+      part = fmaf(ld(gC, bc + k), h[k], part);
+    }
   }
   if (live) {
     if constexpr (K % 4 == 0) {
@@ -112,10 +135,19 @@ hipError_t launch_n(const StepParams &p, hipStream_t stream) {
   const int64_t threads = p.batch * p.dim * TPC;
   if (threads == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
-  if (p.z != nullptr)
-    hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, true>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, false>), grid, dim3(256), 0, stream, p);
+  const bool trap = HEAD && p.lam != nullptr;
+  if (trap) {
+    if constexpr (HEAD) {
+      if (p.z != nullptr)
+        hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, true, true>), grid, dim3(256), 0, stream, p);
+      else
+        hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, false, true>), grid, dim3(256), 0, stream, p);
+    }
+  } else if (p.z != nullptr) {
+    hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, true, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((step_kernel<Tin, Tout, N, HEAD, false, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

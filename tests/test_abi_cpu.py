@@ -45,14 +45,14 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 18, declared
+    assert len(declared) == 19, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
 
 
 def test_version_and_status_strings():
-    assert ssm.version() == 400
+    assert ssm.version() == 500
     for code, name in ssm.STATUS.items():
         assert ssm.status_string(code) == name
     assert ssm.status_string(-99) == "SSM_ERR_UNKNOWN"
@@ -238,12 +238,36 @@ def test_ssd_rejects_null_misaligned_overlap():
 def test_ssd_trap_rules():
     d = _sdims()
     f = ssm.lib().ssd_trap_chunked_fwd
-    call = lambda lam, **kw: f(kw.get("x", FAKE), FAKE + 0x100000, lam, FAKE + 0x200000, FAKE + 0x300000,
-                               FAKE + 0x400000, None, None, None, kw.get("y", FAKE + 0x10000000), None,
-                               ctypes.byref(d), None)
+    call = lambda lam, xp=None, bp=None, **kw: f(kw.get("x", FAKE), FAKE + 0x100000, lam, FAKE + 0x200000,
+                                                 FAKE + 0x300000, FAKE + 0x400000, None, None, None, xp, bp,
+                                                 kw.get("y", FAKE + 0x10000000), None, ctypes.byref(d), None)
     assert call(None) == -1                         # lam is required
     assert call(FAKE + 0x500001) == -4              # 2-byte alignment
     assert call(FAKE + 0x10000000 + 64) == -2       # lam inside y
+    lam = FAKE + 0x600000
+    assert call(lam, xp=FAKE + 0x700000) == -1      # x_prev without B_prev
+    assert call(lam, bp=FAKE + 0x800000) == -1      # B_prev without x_prev
+    assert call(lam, xp=FAKE + 0x700008, bp=FAKE + 0x800000) == -4   # 16-byte alignment
+    assert call(lam, xp=FAKE + 0x700000, bp=FAKE + 0x10000000) == -2  # B_prev inside y
+
+
+def test_ssd_trap_step_rules():
+    f = ssm.lib().ssd_trap_step
+
+    def call(d, lam=FAKE + 0x500000, xp=None, bp=None, state=FAKE + 0x20000000, y=FAKE + 0x10000000):
+        return f(FAKE, FAKE + 0x100000, lam, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, None, None,
+                 xp, bp, state, y, ctypes.byref(d), None)
+
+    d = _ssdstepdims()
+    assert call(d, lam=None) == -1                                   # lam is required
+    assert call(d, xp=FAKE + 0x600000) == -1                         # x_prev without B_prev
+    assert call(d, lam=FAKE + 0x500001) == -4                        # element alignment
+    assert call(d, xp=FAKE + 0x600000, bp=FAKE + 0x20000000) == -2  # B_prev inside the state
+    assert call(_ssdstepdims(flags=4)) == -2                         # unknown flag bit
+    assert call(_ssdstepdims(dstate=96)) == -5
+    assert call(_ssdstepdims(batch=0), lam=None, state=None) == 0    # nothing to do
+    # SSM_LAM_SIGMOID is a trapezoid flag: ssd_step rejects it.
+    assert _step(_ssdstepdims(flags=2), ssd=True) == -2
 
 
 def test_empty_inputs_launch_nothing_and_succeed():

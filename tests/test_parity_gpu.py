@@ -783,6 +783,103 @@ def test_ssd_trap_named_workload_full_size():
     assert eh <= TOL_BF16, eh
 
 
+@pytest.mark.parametrize("P,N,G,has_z,flags", [(64, 128, 1, False, False), (64, 64, 2, True, False),
+                                               (5, 16, 1, True, False), (64, 128, 2, True, True)])
+def test_ssd_trap_decode_steps(P, N, G, has_z, flags):
+    """Chained ssd_trap_step calls (Eq. 9: alpha h + beta x_prev B_prev +
+    gamma x B), each passing the previous token's x and B, from a cached state
+    and a given token before the sequence, against one oracle run over the
+    same tokens.  flags: raw dt and lam through the fused softplus (with a
+    per-head bias) and sigmoid."""
+    L, b, H = 10, 2, 4
+    s = SsdShape(b, L, H, P, N, G, 64, "bf16", has_z=has_z, dskip="normal", seed=6500 + P + N + G)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((b, L, H), seed=6501 + N)
+    kw, okw = {}, {}
+    if flags:
+        raw, bias = make_raw_step((b, L, H), H, 6502, "bf16")
+        inp["dt"] = raw
+        lam = make_state((b, L, H), seed=6503).to(torch.bfloat16)
+        kw = dict(dt_softplus=True, dt_bias=bias.cuda(), lam_sigmoid=True)
+        okw = dict(dt_softplus=True, dt_bias=bias, lam_sigmoid=True)
+    S0 = make_state((b, H, P, N), seed=6504, scale=0.5)
+    g = torch.Generator().manual_seed(6505)
+    xp0 = torch.randn(b, H, P, generator=g).to(torch.bfloat16)
+    bp0 = (torch.randn(b, G, N, generator=g) / N ** 0.5).to(torch.bfloat16)
+    yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], S0,
+                             x_prev=xp0, B_prev=bp0, **okw)
+    state = S0.cuda().clone()
+    xp, bp = xp0.cuda(), bp0.cuda()
+    ys = []
+    for t in range(L):
+        tok = {k: (None if inp[k] is None else inp[k][:, t].contiguous().cuda()) for k in ("x", "dt", "z", "B", "C")}
+        y = ssm.ssd_trap_step(tok["x"], tok["dt"], lam[:, t].contiguous().cuda(), _dev(inp["A"]), tok["B"],
+                              tok["C"], _dev(inp["D"]), tok["z"], state=state, x_prev=xp, B_prev=bp, **kw)
+        ys.append(y.float().cpu())
+        xp, bp = tok["x"], tok["B"]
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(ys, dim=1), yr) <= TOL_BF16, rel_err(torch.stack(ys, dim=1), yr)
+    assert rel_err(state.cpu(), hr) <= TOL_BF16, rel_err(state.cpu(), hr)
+
+
+@pytest.mark.parametrize("batch,H,L1", [(2, 4, 1), (2, 4, 64), (2, 4, 100), (16, 64, 37), (8, 64, 65)])
+def test_ssd_trap_split_continuation(batch, H, L1):
+    """A trapezoidal sequence in two chunked calls: the second starts from the
+    first's h_last (updated in place) and its last token's x and B
+    (x_prev, B_prev), and equals one oracle run over the whole sequence (one,
+    four and two heads per workgroup)."""
+    L, N, G = 130, 128, 2
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=True, dskip="normal", seed=6600 + batch + L1)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((batch, L, H), seed=6601 + L1)
+    h0 = make_state((batch, H, 64, N), seed=6602, scale=0.5)
+    yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
+    d = {k: _dev(v) for k, v in inp.items()}
+    state = h0.cuda().clone()
+    part = lambda t, t0, t1: t[:, t0:t1].contiguous()
+    ys = []
+    for t0, t1 in ((0, L1), (L1, L)):
+        prev = {} if t0 == 0 else dict(x_prev=d["x"][:, t0 - 1].contiguous(), B_prev=d["B"][:, t0 - 1].contiguous())
+        y, _ = ssm.ssd_trap_chunked_fwd(part(d["x"], t0, t1), part(d["dt"], t0, t1), part(lam.cuda(), t0, t1),
+                                        d["A"], part(d["B"], t0, t1), part(d["C"], t0, t1), d["D"],
+                                        part(d["z"], t0, t1), h0=state, h_last=state, **prev)
+        ys.append(y.float().cpu())
+    torch.cuda.synchronize()
+    assert rel_err(torch.cat(ys, dim=1), yr) <= TOL_BF16, rel_err(torch.cat(ys, dim=1), yr)
+    assert rel_err(state.cpu(), hr) <= TOL_BF16, rel_err(state.cpu(), hr)
+
+
+def test_ssd_trap_prefill_then_128_decode_steps():
+    """A 64-token trapezoidal chunked prefill leaves its state in a cache; 128
+    ssd_trap_step calls continue from it in place, each passing the previous
+    token's x and B (the first one the prefill's last token).  Every step's y
+    and the final state match one oracle run over all 192 tokens (head dims
+    32 x 64, dstate 128)."""
+    Lp, Ld = 64, 128
+    s = SsdShape(1, Lp + Ld, 32, 64, 128, 1, 64, "bf16", has_z=True, dskip="ones", seed=6700)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((1, Lp + Ld, 32), seed=6701)
+    yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"])
+    d = {k: _dev(v) for k, v in inp.items()}
+    lamd = lam.cuda()
+    pre = lambda t: t[:, :Lp].contiguous()
+    cache = torch.full((1, 32, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
+    y0, _ = ssm.ssd_trap_chunked_fwd(pre(d["x"]), pre(d["dt"]), pre(lamd), d["A"], pre(d["B"]), pre(d["C"]),
+                                     d["D"], pre(d["z"]), h_last=cache)
+    ys = [y0.float().cpu()]
+    for t in range(Lp, Lp + Ld):
+        tok = lambda a, tt=t: a[:, tt].contiguous()
+        y = ssm.ssd_trap_step(tok(d["x"]), tok(d["dt"]), tok(lamd), d["A"], tok(d["B"]), tok(d["C"]), d["D"],
+                              tok(d["z"]), state=cache, x_prev=tok(d["x"], t - 1), B_prev=tok(d["B"], t - 1))
+        ys.append(y.float().cpu()[:, None])
+    torch.cuda.synchronize()
+    got = torch.cat(ys, dim=1)
+    print(f"trapezoidal prefill 64 + 128 decode steps: rel err y {rel_err(got, yr):.3e}, "
+          f"state {rel_err(cache.cpu(), hr):.3e}")
+    assert rel_err(got, yr) <= TOL_BF16
+    assert rel_err(cache.cpu(), hr) <= TOL_BF16
+
+
 # ---------------------------------------------------------------------------
 # Fused Phase-0 maps: step = softplus(raw + dt_bias), trapezoid lam = sigmoid(raw)
 # ---------------------------------------------------------------------------

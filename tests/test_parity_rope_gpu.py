@@ -229,3 +229,41 @@ def test_rope_prefill_then_decode_steps():
     got = torch.cat(ys, dim=1).cpu()
     assert rel_err(got, ry) <= TOL_BF16, rel_err(got, ry)
     assert rel_err(state.cpu(), rh) <= TOL_BF16, rel_err(state.cpu(), rh)
+
+
+def test_rope_trap_prefill_then_128_decode_steps():
+    """Mamba-3 SISO serving order with the trapezoid: a 64-token prefill
+    (rotary step, then the trapezoidal chunked SSD on the per-head B and C),
+    then 128 decode tokens, each a one-token rotary step from the cached angle
+    and an ssd_trap_step on the cached state that passes the previous token's
+    x and rotated B.  Every output against the oracle (rotary step, then the
+    trapezoidal SSD) over all 192 tokens."""
+    s = SsdShape(1, 192, 32, 64, 128, 1, 64, "bf16", has_z=True, dskip="ones", seed=95)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((1, 192, 32), seed=96)
+    theta = make_theta((1, 192, 1, 64), 97, "bf16", 5.0)
+    rb, rc, _ = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
+    rb16 = torch.from_numpy(rb).to(torch.bfloat16)
+    rc16 = torch.from_numpy(rc).to(torch.bfloat16)
+    ry, rh = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], rb16, rc16, inp["D"], inp["z"])
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    th, lamd = theta.cuda(), lam.cuda()
+    T = 64
+    pre = lambda t: t[:, :T].contiguous()
+    br, cr, ang = ssm.rope_bc(pre(d["dt"]), pre(th), pre(d["B"]), pre(d["C"]))
+    y0, state = ssm.ssd_trap_chunked_fwd(pre(d["x"]), pre(d["dt"]), pre(lamd), d["A"], br, cr, d["D"], pre(d["z"]))
+    ys = [y0.float()]
+    xp, bp = d["x"][:, T - 1].contiguous(), br[:, T - 1].contiguous()
+    for t in range(T, s.seqlen):
+        one = lambda a: a[:, t:t + 1].contiguous()
+        b1, c1, _ = ssm.rope_bc(one(d["dt"]), one(th), one(d["B"]), one(d["C"]), angle0=ang, angle_last=ang)
+        xt = d["x"][:, t].contiguous()
+        y = ssm.ssd_trap_step(xt, d["dt"][:, t].contiguous(), lamd[:, t].contiguous(), d["A"],
+                              b1[:, 0].contiguous(), c1[:, 0].contiguous(), d["D"], d["z"][:, t].contiguous(),
+                              state=state, x_prev=xp, B_prev=bp)
+        ys.append(y.float()[:, None])
+        xp, bp = xt, b1[:, 0].contiguous()
+    torch.cuda.synchronize()
+    got = torch.cat(ys, dim=1).cpu()
+    assert rel_err(got, ry) <= TOL_BF16, rel_err(got, ry)
+    assert rel_err(state.cpu(), rh) <= TOL_BF16, rel_err(state.cpu(), rh)
