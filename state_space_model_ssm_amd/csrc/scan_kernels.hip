@@ -10,18 +10,20 @@
 //   * One thread owns one (channel d, state n) pair and keeps h[n] in a float32
 //     register for its whole time range.  A 256-thread workgroup covers
 //     256 / N channels of one (batch, group), so the B_t/C_t tile it stages in
-//     LDS is shared by every channel of the block.  For N >= 16 the N states of
-//     a channel fill whole 16-lane DPP rows.
-//   * Time is walked in tiles of T steps.  Global loads are 16-byte vectors
-//     issued DEPTH tiles ahead into a static register ring.  Per tile the block
-//     writes dt, w = dt * u and D * u for its channels and B, C for its group
-//     into LDS; each thread then runs T steps of the recurrence and writes its
-//     readout partial C_t[n] h_t[n] to LDS; after a barrier the same 256
-//     threads, one per (channel, step) element, sum the N partials, add the D
+//     LDS is shared by every channel of the block.  Time is walked in tiles of
+//     T steps whose global loads are issued DEPTH tiles ahead into a static
+//     register ring; each thread runs T steps of the recurrence and writes its
+//     readout partial C_t[n] h_t[n] to LDS, and lanes of the same wavefront,
+//     one per (channel, step) element, then sum the N partials, add the D
 //     skip, apply the gate and store y.
-//   * N >= 16: the 16 lanes of a DPP row share one channel, so dt and w reach
-//     them by a row broadcast fused into the multiplies (v_mul_f32_dpp
-//     row_newbcast), from a single LDS word per lane per 16 steps.
+//   * N >= 16 (scan_row_kernel): a channel's states fill whole 16-lane DPP
+//     rows.  Lane j of a row loads its channel's dt, u and z at step j of each
+//     16-step block directly from global memory, so dt and w = dt * u reach
+//     the row by a broadcast fused into the multiplies (v_mul_f32_dpp
+//     row_newbcast) and the lane reading out (channel, step j) holds u and z;
+//     only B and C are staged in LDS.
+//   * N < 16 (scan_chunk_kernel): several channels share a 16-lane row, so
+//     the block also stages dt, w = dt * u and D * u in LDS.
 //   * The sequence may be split into chunks that run in parallel (grid.y).
 //     A first pass (SUMMARY) reduces every chunk but the last to the pair
 //     (prod_t exp(dt_t A), local end state); the sweep pass for chunk c folds
@@ -29,8 +31,8 @@
 //     (P1, h1) o (P2, h2) = (P1 P2, P2 h1 + h2)  ("We brought Mamba to
 //     Trainium", section "We built the parallel scan") to get its start state.
 //
-// Padding rule: time steps past the end of a chunk are staged with dt = 0 and
-// w = 0, so exp(0) = 1 and the state passes through them unchanged.
+// Padding rule: time steps past the end of a chunk take dt = 0 and w = 0, so
+// exp(0) = 1 and the state passes through them unchanged.
 #include <utility>
 
 #include "ssm_internal.h"
@@ -120,43 +122,29 @@ __device__ __forceinline__ Words<W> load_seg_tail(const uint16_t *row, int64_t t
   return r;
 }
 
-// DPP path (N >= 16): 32-step time tiles, staging loads of 4 elements, and
-// (N = 16) registers held to four wavefronts per SIMD.  Measured against 16-
-// and 64-step tiles, 2- and 8-element loads, and three wavefronts.
+// Row kernel (N >= 16): 32-step time tiles.  Measured against 16- and
+// 64-step tiles.
 constexpr int kDppTile = 32;
-constexpr int kDppVec = 4;
-constexpr int kWaves16 = 4;
 
+// Small-state kernel (N < 16): tile shapes.
 template <int N>
 struct TileCfg {
-  static constexpr bool kDpp = N >= 16;                          // dt, w by DPP row broadcast
+  static_assert(N < 16, "N >= 16 runs on the row kernel");
   static constexpr int CH = 256 / N;                             // channels per block
   static constexpr int CPW = 64 / N;                             // channels per wavefront
   // Time steps per tile.
-  static constexpr int T = kDpp ? kDppTile : (N >= 4 ? 32 : (N == 2 ? 16 : 8));
+  static constexpr int T = N >= 4 ? 32 : (N == 2 ? 16 : 8);
   static constexpr int TP = T + 4;                               // padded LDS row (floats)
   static constexpr int BS = T < 16 ? T : 16;                     // steps per readout block
   static constexpr int NB = T / BS;                              // readout blocks per tile
   static constexpr int OPL = (CPW * BS + 63) / 64;               // readout outputs per lane per block
   // Readout partials of a block live as [channel][step][state]: JS floats per
-  // step, RS per channel.  A recurrence store (one step, lanes over states)
-  // hits consecutive banks, and RS = min(N, 64) (mod 64) keeps the channel
-  // rows a wavefront stores at once on disjoint banks.  A reader lane sums one
-  // (channel, step) row in 16-byte groups; the 16 lanes of a 16-step block
-  // would hit the same banks, so on the DPP path each lane visits the groups
-  // of its row in the order q ^ swz(step) (kSwz, unpadded rows; the pairwise
-  // sum pairs the same groups in any such order, so the result is unchanged),
-  // and otherwise rows are padded by 4 floats.
-  static constexpr bool kSwz = kDpp;
-  static constexpr int G = N / 4;                                // 16-byte groups per row
-  static constexpr int JS = kSwz ? N : (N >= 4 ? N + 4 : N);
-  static constexpr int RS_ALIGN = N >= 4 ? (N < 64 ? N : 0) : 4;
+  // step (rows padded by 4 floats), RS per channel.  A recurrence store (one
+  // step, lanes over states) hits consecutive banks, and RS = N (mod 64)
+  // keeps the channel rows a wavefront stores at once on disjoint banks.
+  static constexpr int JS = N >= 4 ? N + 4 : N;
+  static constexpr int RS_ALIGN = N >= 4 ? N : 4;
   static constexpr int RS = BS * JS + ((RS_ALIGN - (BS * JS) % 64) % 64 + 64) % 64;
-  __device__ static int swz(int step) { return kSwz ? (step / (16 / G)) % G : 0; }
-  // Wavefronts per SIMD the register allocation aims at: for N = 16 the
-  // block's LDS (39.5 KiB) allows four blocks per CU, so registers are held
-  // to 128 per lane to match.
-  static constexpr int kWaves = N == 16 ? kWaves16 : 1;
 };
 
 // One block's view of the tensors and its fixed index math.
@@ -164,9 +152,8 @@ template <typename Tin, int N, bool SUMMARY>
 struct Block {
   using Cfg = TileCfg<N>;
   static constexpr int CH = Cfg::CH, T = Cfg::T;
-  // Storage elements per staging load: two on the DPP path (one load per
-  // thread and tile), else one 16-byte vector.
-  static constexpr int VEC = Cfg::kDpp ? kDppVec : 16 / static_cast<int>(sizeof(Tin));
+  // Storage elements per staging load: one 16-byte vector.
+  static constexpr int VEC = 16 / static_cast<int>(sizeof(Tin));
   static constexpr int WORDS = VEC * static_cast<int>(sizeof(Tin)) / 4;  // 32-bit words per load
   static constexpr int SEG = (T + VEC - 1) / VEC;   // loads per tile row
   static constexpr int PAIR_JOBS = CH * SEG;        // (dt, u) row segments
@@ -212,28 +199,18 @@ __device__ __forceinline__ void store_row(float *dst, const float *v) {
   }
 }
 
-// Operands of one 16-step block on the DPP path: dt and w of step j (lane j
-// of the row), and B, C of this lane's state for the 16 steps.
-struct DppOps {
-  float dl16, w16;
-  F4 b4[4], c4[4];
-};
-
 // SUMMARY: no readout; reduce the chunk to (decay product, end state).
 // CKPT (with SUMMARY, one chunk): instead store the state at every
 // kScanCkptStep-step boundary, from h0, for the backward pass.
 template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z, bool CKPT = false>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TileCfg<N>::kWaves)))
-scan_chunk_kernel(const ScanParams p) {
+__global__ void __launch_bounds__(256) scan_chunk_kernel(const ScanParams p) {
   using Cfg = TileCfg<N>;
   using Bk = Block<Tin, N, SUMMARY>;
   using Regs = TileRegs<Tin, N, SUMMARY>;
   constexpr int CH = Cfg::CH, CPW = Cfg::CPW, T = Cfg::T, TP = Cfg::TP, BS = Cfg::BS, NB = Cfg::NB;
   constexpr int OPL = Cfg::OPL, JS = Cfg::JS, RS = Cfg::RS;
   constexpr int VEC = Bk::VEC, SEG = Bk::SEG, JPT = Bk::JPT, WORDS = Bk::WORDS;
-  constexpr bool kDpp = Cfg::kDpp;
   static_assert(T % BS == 0 && BS % 4 == 0 && TP % 4 == 0 && RS % 4 == 0, "tile shape");
-  static_assert(!kDpp || BS == 16, "DPP readout blocks are 16 steps");
 
   // Staged inputs of a tile, double-buffered by tile parity: there is one
   // barrier per tile, so a wavefront may stage tile i+1 while others still
@@ -426,37 +403,7 @@ scan_chunk_kernel(const ScanParams p) {
   };
 
   // Steps blk*BS .. blk*BS+BS-1 of the tile staged in buffer `par` for this
-  // thread's (channel, state); the readout partials go to LDS.  On the DPP
-  // path the block's operands are loaded first (load_ops), so that they can be
-  // issued ahead of the previous block's readout.
-  auto load_ops = [&](int par, int blk, DppOps &o) __attribute__((always_inline)) {
-    const int tb = blk * BS;
-    const int dbase = par * CH * TP + chl * TP + tb;
-    const int bbase = par * N * TP + n * TP + tb;
-    const int j = tid % 16;
-    o.dl16 = sDl[dbase + j];
-    o.w16 = sW[dbase + j];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o.b4[q] = sB4[bbase / 4 + q];
-      o.c4[q] = SUMMARY ? F4{} : sC4[bbase / 4 + q];
-    }
-  };
-  auto recur_ops = [&](const DppOps &o) __attribute__((always_inline)) {
-    F4 pr[4];
-    float av[16], bx[16];
-    dpp_coeffs(o.dl16, o.w16, a2, o.b4, av, bx, std::make_integer_sequence<int, 16>{});
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      h = fmaf(av[i], h, bx[i]);
-      if constexpr (SUMMARY) prod *= av[i];
-      else pr[i / 4].v[i % 4] = o.c4[i / 4].v[i % 4] * h;
-    }
-    if constexpr (!SUMMARY) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sP[chl * RS + i * JS + n] = pr[i / 4].v[i % 4];
-    }
-  };
+  // thread's (channel, state); the readout partials go to LDS.
   auto recur_block = [&](int par, int blk, int64_t t0) __attribute__((always_inline)) {
     if constexpr (CKPT) {
       static_assert(kScanCkptStep % BS == 0 || BS % kScanCkptStep == 0, "checkpoint grid");
@@ -464,11 +411,7 @@ scan_chunk_kernel(const ScanParams p) {
       if (mine && ts < t_end && (ts - t_begin) % kScanCkptStep == 0)
         p.carry[((b * p.dim + d) * ((L + kScanCkptStep - 1) / kScanCkptStep) + ts / kScanCkptStep) * N + n] = h;
     }
-    if constexpr (kDpp) {
-      DppOps o;
-      load_ops(par, blk, o);
-      recur_ops(o);
-    } else {
+    {
       const int tb = blk * BS;
       const int dbase = par * CH * TP + chl * TP + tb;
       const int bbase = par * N * TP + n * TP + tb;
@@ -508,10 +451,9 @@ scan_chunk_kernel(const ScanParams p) {
     for (int k = 0; k < OPL; ++k) {
       const float *row = sP + erow[k] * RS + ej[k] * JS;
       if constexpr (N % 4 == 0) {
-        const int f = Cfg::swz(ej[k]);
 #pragma unroll
         for (int q = 0; q < N / 4; ++q) {
-          const F4 v4 = *reinterpret_cast<const F4 *>(row + 4 * (q ^ f));
+          const F4 v4 = *reinterpret_cast<const F4 *>(row + 4 * q);
           P.v[k][4 * q] = v4.v[0];
           P.v[k][4 * q + 1] = v4.v[1];
           P.v[k][4 * q + 2] = v4.v[2];
@@ -555,21 +497,6 @@ scan_chunk_kernel(const ScanParams p) {
     if constexpr (SUMMARY) {
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) recur_block(par, bb, t0);
-    } else if constexpr (kDpp) {
-      // The next block's operands load between this block's partial reads
-      // and the sums that consume them.
-      DppOps o;
-      load_ops(par, 0, o);
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        recur_ops(o);
-        wave_lds_sync();
-        Partials P;
-        readout_load(par, bb, P);
-        if (bb + 1 < NB) load_ops(par, bb + 1, o);
-        readout_finish(bb, t0, zz, P);
-        compiler_fence();
-      }
     } else {
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
@@ -616,6 +543,293 @@ scan_chunk_kernel(const ScanParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row kernel (N >= 16): one (channel, state) per thread, a channel's states
+// filling whole 16-lane DPP rows.
+//
+// Lane j of a row loads its own channel's dt, u (and z) at step j of every
+// 16-step block straight from global memory: a row reads 16 consecutive steps
+// of one channel row (32 or 64 contiguous bytes), so the loads coalesce by
+// rows.  dt and w = dt u then reach the row's lanes by DPP row broadcasts from
+// registers, and the lane that reads out (channel, step j) already holds u
+// and z.  Only B and C (shared by every channel of the block) are staged in
+// LDS, double-buffered by tile parity with one barrier per tile, and the
+// readout partials C_t[n] h_t[n] pass through LDS within each wavefront.  The
+// sweep is bound by LDS throughput, so dt, w and D u no longer occupy it.
+// ---------------------------------------------------------------------------
+// B/C staging loads of the row kernel: 2 steps per load, so that the 16 x 32
+// B/C tile of N = 16 is one job per thread.
+constexpr int kRowVec = 2;
+// Row kernel for N = 16: registers held to this many wavefronts per SIMD,
+// and tiles in flight per block by input dtype.
+constexpr int kRowWaves16 = 4;
+template <typename Tin>
+constexpr int kRowDepth = sizeof(Tin) == 2 ? 3 : 2;
+
+template <typename Tin, typename Tout, int N, bool SUMMARY, int DEPTH, bool HAS_Z, bool CKPT = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(N == 16 ? kRowWaves16 : 1)))
+scan_row_kernel(const ScanParams p) {
+  static_assert(N >= 16 && N <= 64 && N % 16 == 0, "row kernel state counts");
+  constexpr int CH = 256 / N;                 // channels per block
+  constexpr int RPC = N / 16;                 // DPP rows per channel
+  constexpr int T = kDppTile, BS = 16, NB = T / BS;
+  constexpr int TP = T + 4;                   // padded LDS row of B and C (floats)
+  constexpr int VEC = kRowVec;                // B/C staging: elements per load
+  constexpr int WORDS = VEC * static_cast<int>(sizeof(Tin)) / 4;
+  constexpr int SEG = T / VEC;                // loads per B/C row per tile
+  constexpr int BC_JOBS = N * SEG;
+  constexpr int JPT = (BC_JOBS + 255) / 256;  // B/C staging jobs per thread
+  constexpr int G4 = N / 4;                   // 16-byte groups per partial row
+  // Partials of one block: [channel][step][state], RS floats per channel with
+  // RS = N (mod 64) so the rows of one store instruction fall on disjoint banks.
+  constexpr int RS = BS * N + (((N < 64 ? N : 0) - (BS * N) % 64) % 64 + 64) % 64;
+  static_assert(T % BS == 0 && TP % 4 == 0 && RS % 4 == 0 && BC_JOBS % 64 == 0, "tile shape");
+  constexpr bool has_z = !SUMMARY && HAS_Z;
+
+  __shared__ F4 sB4[2 * N * TP / 4];
+  __shared__ F4 sC4[SUMMARY ? 1 : 2 * N * TP / 4];
+  __shared__ F4 sP4[SUMMARY ? 1 : CH * RS / 4];
+  float *sP = sP4[0].v;
+
+  const Tin *__restrict__ gu = static_cast<const Tin *>(p.u);
+  const Tin *__restrict__ gdl = static_cast<const Tin *>(p.delta);
+  const Tin *__restrict__ gB = static_cast<const Tin *>(p.B);
+  const Tin *__restrict__ gC = static_cast<const Tin *>(p.C);
+  const Tin *__restrict__ gz = static_cast<const Tin *>(p.z);
+  Tout *__restrict__ gy = static_cast<Tout *>(p.y);
+
+  const int tid = threadIdx.x;
+  const int n = tid % N;
+  const int chl = tid / N;
+  const int j = tid % 16;                            // step of a block this lane loads and reads out
+  const bool reader = ((tid / 16) % RPC) == 0;       // the channel's first row reads out
+
+  int64_t blk = blockIdx.x;
+  const int64_t tile = blk % p.tiles_per_group;
+  blk /= p.tiles_per_group;
+  const int64_t g = blk % p.ngroups;
+  const int64_t b = blk / p.ngroups;
+  const int c = static_cast<int>(blockIdx.y);
+  const int64_t L = p.seqlen;
+  const int64_t ch0 = tile * CH;
+  const int nvalid = static_cast<int>(min(static_cast<int64_t>(CH), p.dim_per_group - ch0));
+  const int64_t d0 = g * p.dim_per_group + ch0;
+  const int64_t t_begin = static_cast<int64_t>(c) * p.chunk_len;
+  const int64_t t_end = min(L, t_begin + p.chunk_len);
+  const int ntiles = static_cast<int>((t_end - t_begin + T - 1) / T);
+
+  // ---- this thread's state and its channel row ------------------------------
+  const bool mine = chl < nvalid;
+  const int64_t d = d0 + chl;
+  const int64_t crow = d0 + min(chl, nvalid - 1);    // rows past the group load a valid row
+  const int64_t ebase = (b * p.dim + crow) * L;
+  const float a2 = mine ? p.A[d * N + n] * kLog2e : 0.0f;
+  const float dskip = (!SUMMARY && p.D != nullptr) ? p.D[crow] : 0.0f;
+  const float bias = p.dt_bias != nullptr ? p.dt_bias[crow] : 0.0f;
+  float h = ((!SUMMARY || CKPT) && p.h0 != nullptr && mine) ? p.h0[(b * p.dim + d) * N + n] : 0.0f;
+  float prod = 1.0f;
+  if (!SUMMARY && c > 0 && mine) {
+    const float *cr = p.carry + (b * p.dim + d) * static_cast<int64_t>(p.n_chunks - 1) * (2 * N);
+    for (int k = 0; k < c; ++k) h = fmaf(cr[k * 2 * N + n], h, cr[k * 2 * N + N + n]);
+  }
+
+  // ---- B/C staging jobs: job k loads VEC steps of one B row and one C row ----
+  int jrow[JPT], jcol[JPT];
+  bool jon[JPT];
+  int64_t jbase[JPT];
+#pragma unroll
+  for (int k = 0; k < JPT; ++k) {
+    int job = tid + 256 * k;
+    jon[k] = __builtin_amdgcn_readfirstlane(static_cast<int>(job < BC_JOBS)) != 0;  // uniform: BC_JOBS % 64 == 0
+    if (!jon[k]) job = 0;
+    jrow[k] = job / SEG;
+    jcol[k] = (job % SEG) * VEC;
+    jbase[k] = ((b * p.ngroups + g) * N + jrow[k]) * L;
+  }
+
+  struct Regs {
+    uint32_t dl[NB], u[NB], z[NB];   // raw storage bits of this lane's step in each block
+    Words<WORDS> bw[JPT], cw[JPT];   // B and C row segments
+  };
+
+  // Tiles wholly inside [t_begin, t_end) with aligned B/C rows take vector
+  // loads; the last partial tile (or every tile when rows are misaligned)
+  // loads B/C element by element and zeroes steps past t_end.
+  const int nfast = p.vec_ok ? static_cast<int>((t_end - t_begin) / T) : 0;
+
+  auto prefetch = [&](Regs &R, int ti, bool fast) __attribute__((always_inline)) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int64_t t = t0 + bb * BS + j;
+      const bool in = fast || t < t_end;
+      const int64_t ti_ = in ? t : t_begin;  // a valid step for every lane
+      R.dl[bb] = in ? raw(gdl, ebase + ti_) : 0u;
+      R.u[bb] = in ? raw(gu, ebase + ti_) : 0u;
+      if constexpr (has_z) R.z[bb] = in ? raw(gz, ebase + ti_) : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      if (!jon[k]) continue;
+      if (fast) {
+        const int64_t o = jbase[k] + t0 + jcol[k];
+        R.bw[k] = *reinterpret_cast<const Words<WORDS> *>(gB + o);
+        if constexpr (!SUMMARY) R.cw[k] = *reinterpret_cast<const Words<WORDS> *>(gC + o);
+      } else {
+        R.bw[k] = load_seg_tail<WORDS>(gB + jbase[k], t0 + jcol[k], t_end);
+        if constexpr (!SUMMARY) R.cw[k] = load_seg_tail<WORDS>(gC + jbase[k], t0 + jcol[k], t_end);
+      }
+    }
+  };
+
+  auto stage = [&](const Regs &R, int par) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < JPT; ++k) {
+      if (!jon[k]) continue;
+      float vb[VEC], vc[VEC];
+      unpack(R.bw[k].v, WORDS, vb, gu);
+      const int o = par * N * TP + jrow[k] * TP + jcol[k];
+      store_row<VEC>(sB4[0].v + o, vb);
+      if constexpr (!SUMMARY) {
+        unpack(R.cw[k].v, WORDS, vc, gu);
+        store_row<VEC>(sC4[0].v + o, vc);
+      }
+    }
+  };
+
+  // B and C of this thread's state for the 16 steps of block bb.
+  struct Ops {
+    F4 b4[4], c4[4];
+  };
+  auto load_ops = [&](int par, int bb, Ops &o) __attribute__((always_inline)) {
+    const int q0 = (par * N * TP + n * TP + bb * BS) / 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o.b4[q] = sB4[q0 + q];
+      o.c4[q] = SUMMARY ? F4{} : sC4[q0 + q];
+    }
+  };
+
+  // The step (softplus(dt + bias) when asked; zero past the end) and w = dt u
+  // of this lane's step in block bb.
+  auto step_vals = [&](uint32_t rdl, uint32_t ru, int64_t t, float &dl, float &w, float &uv)
+                       __attribute__((always_inline)) {
+    dl = from_raw(rdl, gu);
+    uv = from_raw(ru, gu);
+    if (p.dt_softplus) dl = t < t_end ? dt_softplus(dl + bias) : 0.0f;
+    w = dl * uv;
+  };
+
+  // 16 recurrence steps of block bb; on the sweep the partials C_t[n] h_t[n]
+  // go to this wavefront's LDS rows.
+  auto recur = [&](float dl, float w, const Ops &o, int64_t ts) __attribute__((always_inline)) {
+    if constexpr (CKPT) {
+      static_assert(kScanCkptStep == BS, "checkpoint grid");
+      if (mine && ts < t_end)
+        p.carry[((b * p.dim + d) * ((L + kScanCkptStep - 1) / kScanCkptStep) + ts / kScanCkptStep) * N + n] = h;
+    }
+    float av[16], bx[16];
+    dpp_coeffs(dl, w, a2, o.b4, av, bx, std::make_integer_sequence<int, 16>{});
+    F4 pr[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h = fmaf(av[i], h, bx[i]);
+      if constexpr (SUMMARY) prod *= av[i];
+      else pr[i / 4].v[i % 4] = o.c4[i / 4].v[i % 4] * h;
+    }
+    if constexpr (!SUMMARY) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sP[chl * RS + i * N + n] = pr[i / 4].v[i % 4];
+    }
+  };
+
+  // Readout of (channel, step j) of a block: sum the N partials pairwise
+  // (16-byte groups visited in the order q ^ swz so the 16 lanes of a row hit
+  // distinct banks), add the D skip, gate, store.
+  auto readout_load = [&](float (&v)[N]) __attribute__((always_inline)) {
+    const float *row = sP + chl * RS + j * N;
+    const int f = (j / (16 / G4)) % G4;
+#pragma unroll
+    for (int q = 0; q < G4; ++q) {
+      const F4 v4 = *reinterpret_cast<const F4 *>(row + 4 * (q ^ f));
+      v[4 * q] = v4.v[0];
+      v[4 * q + 1] = v4.v[1];
+      v[4 * q + 2] = v4.v[2];
+      v[4 * q + 3] = v4.v[3];
+    }
+  };
+  auto readout_finish = [&](float (&v)[N], float uv, uint32_t zr, int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int wd = N / 2; wd >= 1; wd /= 2) {
+#pragma unroll
+      for (int i = 0; i < wd; ++i) v[i] += v[i + wd];
+    }
+    float y = fmaf(dskip, uv, v[0]);
+    if constexpr (has_z) y *= silu(from_raw(zr, gz));
+    if (reader && mine && t < t_end) st(gy, ebase + t, y);
+  };
+
+  auto do_tile = [&](Regs &R, int ti, bool pf) __attribute__((always_inline)) {
+    const int64_t t0 = t_begin + static_cast<int64_t>(ti) * T;
+    uint32_t rdl[NB], ru[NB], zr[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      rdl[bb] = R.dl[bb];
+      ru[bb] = R.u[bb];
+      zr[bb] = has_z ? R.z[bb] : 0u;
+    }
+    const int par = ti & 1;
+    stage(R, par);
+    __syncthreads();
+    if (pf && ti + DEPTH < nfast) prefetch(R, ti + DEPTH, true);
+    Ops o;
+    load_ops(par, 0, o);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      float dl, w, uv;
+      step_vals(rdl[bb], ru[bb], t0 + bb * BS + j, dl, w, uv);
+      recur(dl, w, o, t0 + bb * BS);
+      if constexpr (SUMMARY) {
+        if (bb + 1 < NB) load_ops(par, bb + 1, o);
+      } else {
+        wave_lds_sync();
+        float v[N];
+        readout_load(v);
+        if (bb + 1 < NB) load_ops(par, bb + 1, o);  // the next block's operands load before the sums
+        readout_finish(v, uv, zr[bb], t0 + bb * BS + j);
+        compiler_fence();
+      }
+    }
+  };
+
+  // Fast tiles: tile ti lives in ring slot ti % DEPTH; the slot loop is
+  // unrolled so every slot index is a compile-time constant.
+  static_assert(DEPTH >= 1 && DEPTH <= 6, "ring depth");
+  Regs ring[DEPTH];
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k)
+    if (k < nfast) prefetch(ring[k], k, true);
+  for (int ti0 = 0; ti0 < nfast; ti0 += DEPTH) {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)
+      if (ti0 + k < nfast) do_tile(ring[k], ti0 + k, true);
+  }
+  for (int ti = nfast; ti < ntiles; ++ti) {
+    prefetch(ring[0], ti, false);
+    do_tile(ring[0], ti, false);
+  }
+
+  if constexpr (SUMMARY && !CKPT) {
+    if (mine) {
+      float *cr = p.carry + ((b * p.dim + d) * static_cast<int64_t>(p.n_chunks - 1) + c) * (2 * N);
+      cr[n] = prod;
+      cr[N + n] = h;
+    }
+  } else {
+    if (c == p.n_chunks - 1 && p.h_last != nullptr && mine) p.h_last[(b * p.dim + d) * N + n] = h;
+  }
+}
+
 // Prefetch depth (tiles in flight per block) by input dtype: bf16 tiles are
 // half the bytes, so they keep one more tile in flight.
 template <typename Tin>
@@ -625,19 +839,29 @@ template <typename Tin, typename Tout, int N>
 hipError_t launch_typed(const ScanParams &p, hipStream_t stream) {
   const int64_t blocks = p.batch * p.ngroups * p.tiles_per_group;
   if (blocks == 0) return hipSuccess;
-  constexpr int kD = kDepth<Tin>;
+  constexpr bool kRow = N >= 16;
+  constexpr int kD = kRow ? kRowDepth<Tin> : kDepth<Tin>;
   if (p.n_chunks > 1) {
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, true, kD, false>),
-                       dim3(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks - 1)),
-                       dim3(256), 0, stream, p);
+    const dim3 sgrid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks - 1));
+    if constexpr (kRow)
+      hipLaunchKernelGGL((scan_row_kernel<Tin, Tout, N, true, kD, false>), sgrid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, true, kD, false>), sgrid, dim3(256), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid(static_cast<uint32_t>(blocks), static_cast<uint32_t>(p.n_chunks));
-  if (p.z != nullptr)
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, true>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, false>), grid, dim3(256), 0, stream, p);
+  if constexpr (kRow) {
+    if (p.z != nullptr)
+      hipLaunchKernelGGL((scan_row_kernel<Tin, Tout, N, false, kD, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((scan_row_kernel<Tin, Tout, N, false, kD, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.z != nullptr)
+      hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tout, N, false, kD, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -645,8 +869,12 @@ template <typename Tin, int N>
 hipError_t launch_ckpt_n(const ScanParams &p, hipStream_t stream) {
   const int64_t blocks = p.batch * p.ngroups * p.tiles_per_group;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tin, N, true, kDepth<Tin>, false, true>),
-                     dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p);
+  if constexpr (N >= 16)
+    hipLaunchKernelGGL((scan_row_kernel<Tin, Tin, N, true, kRowDepth<Tin>, false, true>),
+                       dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((scan_chunk_kernel<Tin, Tin, N, true, kDepth<Tin>, false, true>),
+                       dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
