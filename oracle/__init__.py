@@ -44,6 +44,8 @@ class Oracle:
         lib.oracle_scan_bwd_f64.argtypes = [i64] * 5 + [dp] * 18
         lib.oracle_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_ssd_f64.restype = ctypes.c_int
+        lib.oracle_ssd_bwd_f64.argtypes = [i64] * 6 + [dp] * 18
+        lib.oracle_ssd_bwd_f64.restype = ctypes.c_int
         lib.oracle_softplus_f64.argtypes = [i64] * 3 + [dp] * 3
         lib.oracle_softplus_f64.restype = None
         lib.oracle_softplus_grad_f64.argtypes = [i64] * 3 + [dp] * 4
@@ -171,6 +173,28 @@ class Oracle:
             raise ValueError("oracle_scan_bwd_f64 rejected the shapes")
         return g
 
+    def ssd_bwd(self, x, dt, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None):
+        """Gradients of the scalar-decay SSD in float64 for upstream gradients
+        dy (batch, L, H, P) and dh_last (batch, H, P, N; None = zero).  Returns a
+        dict: dx, ddt, dA, dB, dC, dh0, and dD / dz (None when D / z are None)."""
+        x, dt, A, B, C, D, z, h0, dy, dh_last = map(f64, (x, dt, A, B, C, D, z, h0, dy, dh_last))
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (batch, L, H) and B.shape == (batch, L, G, N) and C.shape == B.shape
+        assert A.shape == (H,) and dy.shape == x.shape
+        assert h0 is None or h0.shape == (batch, H, P, N)
+        assert dh_last is None or dh_last.shape == (batch, H, P, N)
+        g = {"dx": np.zeros_like(x), "ddt": np.zeros_like(dt), "dA": np.zeros(H), "dB": np.zeros_like(B),
+             "dC": np.zeros_like(C), "dD": None if D is None else np.zeros(H),
+             "dz": None if z is None else np.zeros_like(x), "dh0": np.zeros((batch, H, P, N))}
+        rc = self.lib.oracle_ssd_bwd_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                         _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
+                                         _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                         _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]))
+        if rc != 0:
+            raise ValueError("oracle_ssd_bwd_f64 rejected the shapes")
+        return g
+
     def ssd(self, x, dt, A, B, C, D=None, z=None, h0=None):
         """Scalar-decay SSD recurrence in float64. Returns (y, h_last).
 
@@ -264,6 +288,19 @@ def ssd_trap_step(x, dt, lam, A, B, C, D=None, z=None, state=None, x_prev=None, 
     y, h = ssd_trap(row(x), row(dt), row(lam), A, row(B), row(C), D, row(z), state, dt_softplus, dt_bias,
                     lam_sigmoid, x_prev, B_prev)
     return y[:, 0], h
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, dt_softplus=False, dt_bias=None):
+    """Scalar-decay SSD gradients in float64 with the default build; see
+    ``Oracle.ssd_bwd``.  With dt_softplus the forward steps with
+    softplus(dt + dt_bias[h]) and ddt is the gradient of the raw dt."""
+    o = _load()
+    if not dt_softplus:
+        return o.ssd_bwd(x, dt, A, B, C, D, z, h0, dy, dh_last)
+    step = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
+    g = o.ssd_bwd(x, step, A, B, C, D, z, h0, dy, dh_last)
+    g["ddt"] = o.softplus_grad(dt, dt_bias, 1, g["ddt"]).reshape(step.shape)
+    return g
 
 
 def ssd(x, dt, A, B, C, D=None, z=None, h0=None, dt_softplus=False, dt_bias=None):

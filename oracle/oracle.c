@@ -252,6 +252,125 @@ int oracle_scan_bwd_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
 }
 
 /*
+ * Gradients of the scalar-decay SSD above (reverse mode), float64.
+ *
+ * For a loss with upstream gradients dy (batch, seqlen, nheads, headdim) on y
+ * and dh_last (batch, nheads, headdim, dstate; nullable = zero) on h_last,
+ * returns the gradient with respect to every input: dx, dz (like x; dz only
+ * with z), ddt (batch, seqlen, nheads), dA, dD (nheads; dD only with Dskip),
+ * dB, dC (batch, seqlen, ngroups, dstate) and dh0 (batch, nheads, headdim,
+ * dstate).  "Mamba-3 NKI Kernels for AWS Neuron", section "Correctness",
+ * reports backward parity of the SSD against a reference but prints no
+ * formulas: this is the chain rule on the recurrence of oracle_ssd_f64,
+ * walked backwards with Lam_t = dL/dS_t (P x N):
+ *   yhat_t = S_t C_t + D x_t;  dyhat_t = dy_t silu(z_t);  dz_t = dy_t yhat_t silu'(z_t)
+ *   Lam_t  = dyhat_t C_t^T + alpha_{t+1} Lam_{t+1}   (Lam_{L-1} also receives dh_last)
+ *   dx_t   = dt_t Lam_t B_t + D dyhat_t;   dB_t += dt_t Lam_t^T x_t;   dC_t += S_t^T dyhat_t
+ *   ddt_t  = sum_{p,n} Lam_t (x_t B_t^T + A alpha_t S_{t-1});   dA += dt_t sum Lam_t alpha_t S_{t-1}
+ *   dD    += dyhat_t . x_t;   dh0 = alpha_0 Lam_0
+ * The forward states of one head are recomputed and kept (seqlen + 1 of them).
+ * Returns 0, -1 on a bad shape, -2 if memory runs out.
+ */
+int oracle_ssd_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t ngroups, const double *x, const double *dt,
+                       const double *A, const double *B, const double *C,
+                       const double *Dskip, const double *z, const double *h0,
+                       const double *dy, const double *dh_last,
+                       double *dx, double *ddt, double *dA, double *dB, double *dC,
+                       double *dD, double *dz, double *dh0)
+{
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1 ||
+        ngroups < 1 || nheads % ngroups != 0)
+        return -1;
+    const int64_t PN = headdim * dstate, hpg = nheads / ngroups;
+    double *S = malloc(sizeof(double) * (size_t)((seqlen + 1) * PN));
+    double *yhat = malloc(sizeof(double) * (size_t)((seqlen > 0 ? seqlen : 1) * headdim));
+    double *lam = malloc(sizeof(double) * (size_t)PN);
+    double *dyh = malloc(sizeof(double) * (size_t)headdim);
+    if (!S || !yhat || !lam || !dyh) {
+        free(S); free(yhat); free(lam); free(dyh);
+        return -2;
+    }
+    for (int64_t k = 0; k < nheads; ++k) dA[k] = 0.0;
+    if (Dskip)
+        for (int64_t k = 0; k < nheads; ++k) dD[k] = 0.0;
+    for (int64_t k = 0; k < batch * seqlen * ngroups * dstate; ++k) {
+        dB[k] = 0.0;
+        dC[k] = 0.0;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t hd = 0; hd < nheads; ++hd) {
+            const int64_t g = hd / hpg;
+            /* forward, keeping every state: S[t + 1] is the state after step t */
+            for (int64_t k = 0; k < PN; ++k)
+                S[k] = h0 ? h0[(b * nheads + hd) * PN + k] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const double d = dt[(b * seqlen + t) * nheads + hd];
+                const double alpha = exp(d * A[hd]);
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = ((b * seqlen + t) * nheads + hd) * headdim + p;
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const int64_t k = p * dstate + n;
+                        S[(t + 1) * PN + k] = alpha * S[t * PN + k] + d * Bt[n] * x[i];
+                        acc += Ct[n] * S[(t + 1) * PN + k];
+                    }
+                    if (Dskip) acc += Dskip[hd] * x[i];
+                    yhat[t * headdim + p] = acc;
+                }
+            }
+            /* backward */
+            for (int64_t k = 0; k < PN; ++k)
+                lam[k] = dh_last ? dh_last[(b * nheads + hd) * PN + k] : 0.0;
+            for (int64_t t = seqlen - 1; t >= 0; --t) {
+                const double d = dt[(b * seqlen + t) * nheads + hd];
+                const double alpha = exp(d * A[hd]);
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                double *dBt = dB + ((b * seqlen + t) * ngroups + g) * dstate;
+                double *dCt = dC + ((b * seqlen + t) * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = ((b * seqlen + t) * nheads + hd) * headdim + p;
+                    dyh[p] = dy[i];
+                    if (z) {
+                        const double sg = 1.0 / (1.0 + exp(-z[i]));
+                        dyh[p] = dy[i] * z[i] * sg;
+                        dz[i] = dy[i] * yhat[t * headdim + p] * sg * (1.0 + z[i] * (1.0 - sg));
+                    }
+                    if (Dskip) dD[hd] += dyh[p] * x[i];
+                }
+                double ddl = 0.0;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = ((b * seqlen + t) * nheads + hd) * headdim + p;
+                    double dxp = Dskip ? Dskip[hd] * dyh[p] : 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const int64_t k = p * dstate + n;
+                        const double l = lam[k] + dyh[p] * Ct[n];
+                        dCt[n] += S[(t + 1) * PN + k] * dyh[p];
+                        dBt[n] += l * d * x[i];
+                        dxp += l * d * Bt[n];
+                        ddl += l * (x[i] * Bt[n] + A[hd] * alpha * S[t * PN + k]);
+                        dA[hd] += l * d * alpha * S[t * PN + k];
+                        lam[k] = alpha * l;
+                    }
+                    dx[i] = dxp;
+                }
+                ddt[(b * seqlen + t) * nheads + hd] = ddl;
+            }
+            for (int64_t k = 0; k < PN; ++k)
+                dh0[(b * nheads + hd) * PN + k] = lam[k];
+        }
+    }
+    free(S);
+    free(yhat);
+    free(lam);
+    free(dyh);
+    return 0;
+}
+
+/*
  * Trapezoidal (Mamba-3 SISO) form of the scalar-decay SSD, float64.
  *
  * "Mamba-3 NKI Kernels for AWS Neuron": section "How it works", Phase 0 gives

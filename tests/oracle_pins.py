@@ -396,6 +396,66 @@ def check_scan_bwd_finite_differences(orc):
             _close(g[gk], fd, rtol=1e-7, what=f"d{k} against finite differences (seed {seed})")
 
 
+def check_ssd_bwd_finite_differences(orc):
+    """The SSD backward against central finite differences of the SSD forward,
+    with every optional input present (two group counts): the gradient of
+    L = sum(dy * y) + sum(dh_last * h_last) with respect to each element of
+    x, dt, A, B, C, D, z and h0."""
+    names = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz", "h0": "dh0"}
+    for seed, (b, L, H, P, N, G) in ((13, (2, 5, 2, 3, 4, 1)), (14, (1, 4, 4, 2, 3, 2))):
+        rng = np.random.default_rng(seed)
+        inp = {"x": rng.standard_normal((b, L, H, P)), "dt": np.exp(rng.uniform(-3, 0, (b, L, H))),
+               "A": -np.exp(rng.uniform(-1, 1, H)), "B": rng.standard_normal((b, L, G, N)),
+               "C": rng.standard_normal((b, L, G, N)), "D": rng.standard_normal(H),
+               "z": rng.standard_normal((b, L, H, P)), "h0": rng.standard_normal((b, H, P, N))}
+        dy, dhl = rng.standard_normal((b, L, H, P)), rng.standard_normal((b, H, P, N))
+
+        def loss(v):
+            y, h = orc.ssd(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"])
+            return float(np.sum(dy * y) + np.sum(dhl * h))
+
+        g = orc.ssd_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], inp["h0"],
+                        dy, dhl)
+        for k, gk in names.items():
+            fd = np.zeros_like(inp[k])
+            for idx in np.ndindex(inp[k].shape):
+                e = 1e-6 * max(1.0, abs(inp[k][idx]))
+                lo, hi = dict(inp), dict(inp)
+                lo[k], hi[k] = inp[k].copy(), inp[k].copy()
+                lo[k][idx] -= e
+                hi[k][idx] += e
+                fd[idx] = (loss(hi) - loss(lo)) / (2 * e)
+            _close(g[gk], fd, rtol=1e-7, what=f"ssd d{k} against finite differences (seed {seed})")
+
+
+def check_ssd_bwd_equals_scan_bwd_broadcast(orc):
+    """The SSD backward is the selective-scan backward with A[d=(h,p), n] = A_h
+    and dt broadcast over p: dx, dz, dB, dC, dh0 equal the scan's, and dA, dD,
+    ddt are the scan's summed over the head's p (and n for dA)."""
+    rng = np.random.default_rng(23)
+    batch, L, H, P, N, G = 2, 9, 4, 3, 5, 2
+    x, dt, A, B, C, D, z = _rand_ssd(rng, batch, L, H, P, N, G)
+    h0 = rng.standard_normal((batch, H, P, N))
+    dy, dhl = rng.standard_normal((batch, L, H, P)), rng.standard_normal((batch, H, P, N))
+    g = orc.ssd_bwd(x, dt, A, B, C, D, z, h0, dy, dhl)
+    dim = H * P
+    tr = lambda a: a.reshape(batch, L, dim).transpose(0, 2, 1).copy()
+    gs = orc.scan_bwd(tr(x), np.repeat(dt, P, axis=2).transpose(0, 2, 1).copy(),
+                      np.repeat(A, P)[:, None] * np.ones((1, N)), B.transpose(0, 2, 3, 1).copy(),
+                      C.transpose(0, 2, 3, 1).copy(), np.repeat(D, P), tr(z), h0.reshape(batch, dim, N),
+                      tr(dy), dhl.reshape(batch, dim, N))
+    back = lambda a: a.transpose(0, 2, 1).reshape(batch, L, H, P)
+    _close(g["dx"], back(gs["du"]), what="ssd dx vs scan du")
+    _close(g["dz"], back(gs["dz"]), what="ssd dz vs scan dz")
+    _close(g["dB"], gs["dB"].transpose(0, 3, 1, 2), what="ssd dB vs scan dB")
+    _close(g["dC"], gs["dC"].transpose(0, 3, 1, 2), what="ssd dC vs scan dC")
+    _close(g["dh0"], gs["dh0"].reshape(batch, H, P, N), what="ssd dh0 vs scan dh0")
+    _close(g["dA"], gs["dA"].reshape(H, P, N).sum(axis=(1, 2)), what="ssd dA vs scan dA summed")
+    _close(g["dD"], gs["dD"].reshape(H, P).sum(axis=1), what="ssd dD vs scan dD summed")
+    _close(g["ddt"], gs["ddelta"].reshape(batch, H, P, L).sum(axis=2).transpose(0, 2, 1),
+           what="ssd ddt vs scan ddelta summed")
+
+
 def _trap_inputs(rng, b, L, H, P, N, G):
     return {"x": rng.standard_normal((b, L, H, P)), "dt": np.exp(rng.uniform(-3, 0, (b, L, H))),
             "lam": rng.uniform(0, 1, (b, L, H)), "A": -np.exp(rng.uniform(-1, 1, H)),
@@ -647,6 +707,8 @@ ALL_CHECKS = [
     check_ssd_invariants,
     check_decode_steps_chain,
     check_scan_bwd_finite_differences,
+    check_ssd_bwd_finite_differences,
+    check_ssd_bwd_equals_scan_bwd_broadcast,
     check_ssd_trap_lam_one_is_ssd,
     check_ssd_trap_single_ssd_form,
     check_ssd_trap_previous_token,

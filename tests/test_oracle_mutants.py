@@ -63,6 +63,17 @@ MUTANTS = [
     ("bwd_readout_ungated", [("const double l = lam[n] + dyh * C[j];", "const double l = lam[n] + dy[i] * C[j];")]),
     ("bwd_dh_last_ignored", [("lam[n] = dh_last ? dh_last[(b * dim + d) * dstate + n] : 0.0;", "lam[n] = 0.0;")]),
     ("bwd_dD_ungated", [("dD[d] += dyh * x;", "dD[d] += dy[i] * x;")]),
+    ("ssd_bwd_no_decay_in_adjoint", [("                        lam[k] = alpha * l;", "                        lam[k] = l;")]),
+    ("ssd_bwd_dC_uses_old_state", [("dCt[n] += S[(t + 1) * PN + k] * dyh[p];", "dCt[n] += S[t * PN + k] * dyh[p];")]),
+    ("ssd_bwd_dA_without_decay", [("dA[hd] += l * d * alpha * S[t * PN + k];", "dA[hd] += l * d * S[t * PN + k];")]),
+    ("ssd_bwd_ddt_no_input_term", [("ddl += l * (x[i] * Bt[n] + A[hd] * alpha * S[t * PN + k]);",
+                                    "ddl += l * (A[hd] * alpha * S[t * PN + k]);")]),
+    ("ssd_bwd_dx_no_dt", [("dxp += l * d * Bt[n];", "dxp += l * Bt[n];")]),
+    ("ssd_bwd_gate_derivative", [("dz[i] = dy[i] * yhat[t * headdim + p] * sg * (1.0 + z[i] * (1.0 - sg));",
+                                  "dz[i] = dy[i] * yhat[t * headdim + p] * sg;")]),
+    ("ssd_bwd_dh_last_ignored", [("lam[k] = dh_last ? dh_last[(b * nheads + hd) * PN + k] : 0.0;", "lam[k] = 0.0;")]),
+    ("ssd_bwd_group_index", [("            const int64_t g = hd / hpg;\n            /* forward, keeping every state",
+                              "            const int64_t g = hd % ngroups;\n            /* forward, keeping every state")]),
     ("softplus_overflows", [("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));", "return log1p(exp(v));")]),
     ("softplus_bias_dropped", [("out[i] = softplus(raw[i] + bv);", "out[i] = softplus(raw[i]);")]),
     ("softplus_bias_index", [("bias[(i / inner) % nb]", "bias[i % nb]")]),
