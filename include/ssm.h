@@ -327,6 +327,53 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
                          const float *h0, const void *x_prev, const void *B_prev, void *y,
                          float *h_last, const ssd_dims_t *dims, void *stream);
 
+/*
+ * Workspace ssd_bwd needs for `dims`, 4 bytes per float: per-head dB and dC
+ * terms, 2 * batch * seqlen * nheads * dstate floats; one scalar per (batch,
+ * step, head), batch * seqlen * nheads floats; and three per (batch, head).
+ */
+SSM_API int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
+
+/*
+ * Backward of the scalar-decay SSD (ssd_chunked_fwd): gradients of a loss L
+ * with respect to every input, given dy = dL/dy and dh_last = dL/dh_last.
+ *
+ * The chain rule on the recurrence of ssd_chunked_fwd ([Mamba-3 NKI],
+ * "Correctness", reports backward parity of the SSD; no formulas are
+ * printed).  With yhat_t = S_t C_t + D x_t, dyhat_t = dy_t silu(z_t) and
+ * Lam_t = dL/dS_t walked from the last step to the first (Lam after the last
+ * step = dh_last):
+ *   Lam_t = dyhat_t C_t^T + exp(dt_{t+1} A) Lam_{t+1}
+ *   dx_t  = dt_t Lam_t B_t + D dyhat_t,        dz_t = dy_t yhat_t silu'(z_t)
+ *   ddt_t = sum_{p,n} Lam_t (x_t B_t^T + A exp(dt_t A) S_{t-1})
+ *   dB_t  = sum over the group's heads of dt_t Lam_t^T x_t
+ *   dC_t  = sum over the group's heads of S_t^T dyhat_t
+ *   dA    = sum over batch and steps of dt_t sum Lam_t exp(dt_t A) S_{t-1}
+ *   dD    = sum over batch and steps of dyhat_t . x_t;   dh0 = exp(dt_0 A) Lam_0
+ * Nothing from the forward call is needed: the states are rebuilt from h0.
+ *
+ * Inputs: as ssd_chunked_fwd (dims, x, dt, A, B, C, D, z, h0), plus
+ *   dy      : (batch, seqlen, nheads, headdim) out_dtype
+ *   dh_last : (batch, nheads, headdim, dstate) float32, nullable (zero)
+ * Outputs (overwritten):
+ *   dx, dz  : (batch, seqlen, nheads, headdim) bf16; dz required with z
+ *   ddt     : (batch, seqlen, nheads) bf16 (with SSM_DT_SOFTPLUS: the
+ *             gradient of the raw dt, i.e. times sigmoid(dt + dt_bias[h]))
+ *   dA, dD  : (nheads) float32; dD required with D
+ *   dB, dC  : (batch, seqlen, ngroups, dstate) float32
+ *   dh0     : (batch, nheads, headdim, dstate) float32, nullable
+ * The sums over heads (dB, dC) and over batch rows (dA, dD) run in a fixed
+ * order, so every output is deterministic.  No output may overlap an input,
+ * another output or the workspace (dims->workspace, at least
+ * ssd_bwd_workspace_size() bytes, 16-byte aligned).  Pointers need their
+ * element alignment.  Supported sizes are those of ssd_chunked_fwd; flags 0
+ * or SSM_DT_SOFTPLUS.
+ */
+SSM_API int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+            const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
+            void *dx, void *ddt, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
+            const ssd_dims_t *dims, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Rotary step on B and C (Mamba-3 complex-valued state)                     */
 /* ------------------------------------------------------------------------ */

@@ -18,7 +18,7 @@ from typing import Optional
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
     "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
-    "ssd_trap_step",
+    "ssd_trap_step", "ssd_bwd", "ssd_bwd_workspace_size",
     "rope_bc", "RopeDims",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
@@ -107,6 +107,10 @@ def lib():
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
+        L.ssd_bwd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssd_bwd_workspace_size.restype = i32
+        L.ssd_bwd.argtypes = [vp] * 18 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_bwd.restype = i32
         L.ssm_scan_bwd.argtypes = [vp] * 18 + [ctypes.POINTER(ScanDims), vp]
         L.ssm_scan_bwd.restype = i32
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
@@ -443,6 +447,54 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
                                         ctypes.byref(dims), _stream(stream))
     _check(rc)
     return y, h_last
+
+
+def ssd_bwd_workspace_size(dims: SsdDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssd_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def ssd_bwd(x, dt, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, workspace=None, stream=None,
+            dt_softplus: bool = False, dt_bias=None):
+    """Scalar-decay SSD backward (``ssd_bwd``): gradients of a loss with
+    upstream gradients dy (shaped like x, in the forward's output dtype) and
+    dh_last (float32, optional).  Returns a dict dx, ddt, dz (bf16; dz when z is
+    given), dA, dB, dC, dD (float32; dD when D is given) and dh0 (float32).
+    With dt_softplus, ddt is the gradient of the raw dt."""
+    torch = _torch()
+    in_code = _dtype_code(x.dtype)
+    out_code = _dtype_code(dy.dtype)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if dy.shape != x.shape or (z is not None and z.shape != x.shape) or dt.shape != (batch, L, H):
+        raise ValueError("dy and z must be shaped like x, dt (batch, L, H)")
+    if B.shape != (batch, L, G, N) or C.shape != B.shape or A.shape != (H,) or (D is not None and D.shape != (H,)):
+        raise ValueError("B, C must be (batch, L, ngroups, dstate) and A, D (nheads,)")
+    for name, t in (("h0", h0), ("dh_last", dh_last)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (batch, H, P, N)):
+            raise ValueError(f"{name} must be float32 (batch, nheads, headdim, dstate)")
+    dims = _ssd_dims(x, B, 64, in_code, out_code)
+    _phase0(dims, H, dt_softplus, dt_bias)
+    need = ssd_bwd_workspace_size(dims)
+    f32 = torch.float32
+    with _alloc_on(stream):
+        if need > 0:
+            if workspace is None or workspace.numel() * workspace.element_size() < need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            dims.workspace = _ptr(workspace)
+            dims.workspace_bytes = workspace.numel() * workspace.element_size()
+        g = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt),
+             "dA": torch.empty((H,), dtype=f32, device=x.device),
+             "dB": torch.empty(B.shape, dtype=f32, device=x.device),
+             "dC": torch.empty(C.shape, dtype=f32, device=x.device),
+             "dD": None if D is None else torch.empty((H,), dtype=f32, device=x.device),
+             "dz": None if z is None else torch.empty_like(x),
+             "dh0": torch.empty((batch, H, P, N), dtype=f32, device=x.device)}
+    _check(lib().ssd_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                         _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                         _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), ctypes.byref(dims), _stream(stream)))
+    return g
 
 
 def ssd_chunked_fwd(x, dt, A, B, C, D=None, z=None, **kw):

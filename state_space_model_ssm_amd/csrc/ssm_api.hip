@@ -586,6 +586,123 @@ int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const f
 }
 
 // ---------------------------------------------------------------------------
+// Scalar-decay SSD backward
+// ---------------------------------------------------------------------------
+
+// Backward workspace, in floats: per-head dB and dC terms, the scalars u_t,
+// and per (batch, head) phi0, dA and dD terms.
+struct SsdBwdWorkspace {
+  size_t bh_terms, u, per_bh;
+  size_t bytes() const { return 4 * (2 * bh_terms + u + 3 * per_bh); }
+};
+
+static SsdBwdWorkspace ssd_bwd_layout(const ssd_dims_t *d) {
+  SsdBwdWorkspace w;
+  w.bh_terms = static_cast<size_t>(d->batch * d->seqlen * d->nheads * d->dstate);
+  w.u = static_cast<size_t>(d->batch * d->seqlen * d->nheads);
+  w.per_bh = static_cast<size_t>(d->batch * d->nheads);
+  return w;
+}
+
+int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
+  const int rc = check_ssd_dims(dims);
+  if (rc != SSM_OK) return rc;
+  *bytes = ssd_bwd_layout(dims).bytes();
+  return ok();
+}
+
+int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
+            const void *z, const float *h0, const void *dy, const float *dh_last, void *dx, void *ddt, float *dA,
+            float *dB, float *dC, float *dD, void *dz, float *dh0, const ssd_dims_t *dims, void *stream) {
+  int rc = check_ssd_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssd_dims_t &d = *dims;
+  if (d.flags & SSM_LAM_SIGMOID) return fail(SSM_ERR_SHAPE, "SSM_LAM_SIGMOID applies to the trapezoidal form only");
+  const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
+  const int64_t n_dt = d.batch * d.seqlen * d.nheads;
+  const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
+  const int64_t n_h = d.batch * d.nheads * d.headdim * d.dstate;
+  if (n_x > 0 && (!x || !dt || !dy || !dx || !ddt)) return fail(SSM_ERR_NULL, "x, dt, dy, dx and ddt are required");
+  if (n_bc > 0 && (!B || !C || !dB || !dC)) return fail(SSM_ERR_NULL, "B, C, dB and dC are required");
+  if (d.nheads > 0 && (!A || !dA)) return fail(SSM_ERR_NULL, "A and dA are required");
+  if (n_x > 0 && z && !dz) return fail(SSM_ERR_NULL, "dz is required when z is given");
+  if (d.nheads > 0 && D && !dD) return fail(SSM_ERR_NULL, "dD is required when D is given");
+  if (!z) dz = nullptr;
+  if (!D) dD = nullptr;
+  const size_t eo = dtype_size(d.out_dtype);
+  if (!aligned(x, 2) || !aligned(dt, 2) || !aligned(B, 2) || !aligned(C, 2) || !aligned(z, 2) ||
+      !aligned(dx, 2) || !aligned(ddt, 2) || !aligned(dz, 2))
+    return fail(SSM_ERR_ALIGN, "bf16 pointers must be 2-byte aligned");
+  if (!aligned(dy, eo)) return fail(SSM_ERR_ALIGN, "dy must be aligned to %zu bytes", eo);
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(dh_last, 4) || !aligned(dA, 4) ||
+      !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4))
+    return fail(SSM_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+  const Span ins[] = {{x, n_x * 2ull},       {dt, n_dt * 2ull},   {z, n_x * 2ull},        {B, n_bc * 2ull},
+                      {C, n_bc * 2ull},      {A, d.nheads * 4ull}, {D, d.nheads * 4ull}, {h0, n_h * 4ull},
+                      {dy, n_x * eo},        {dh_last, n_h * 4ull}, {d.dt_bias, d.nheads * 4ull}};
+  const Span outs[] = {{dx, n_x * 2ull},     {ddt, n_dt * 2ull},  {dz, n_x * 2ull},       {dA, d.nheads * 4ull},
+                       {dB, n_bc * 4ull},    {dC, n_bc * 4ull},   {dD, d.nheads * 4ull},  {dh0, n_h * 4ull}};
+  for (const Span &o : outs) {
+    for (const Span &i : ins)
+      if (overlap(o, i)) return fail(SSM_ERR_SHAPE, "a gradient output overlaps an input");
+    for (const Span &o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return fail(SSM_ERR_SHAPE, "two gradient outputs overlap");
+  }
+  if (n_bc / 256 >= kMaxGridX) return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * ngroups * dstate exceeds the grid limit");
+  const SsdBwdWorkspace wl = ssd_bwd_layout(&d);
+  const size_t need = wl.bytes();
+  if (need > 0) {
+    if (!d.workspace || d.workspace_bytes < need)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                  d.workspace ? d.workspace_bytes : (size_t)0);
+    if (!aligned(d.workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Span sw{d.workspace, need};
+    for (const Span &s : ins)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an input");
+    for (const Span &s : outs)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
+  }
+  if (d.nheads == 0) return ok();
+  ssm::SsdBwdParams p{};
+  p.x = x;
+  p.dt = dt;
+  p.B = B;
+  p.C = C;
+  p.z = z;
+  p.dy = dy;
+  p.A = A;
+  p.D = D;
+  p.h0 = h0;
+  p.dh_last = dh_last;
+  p.dt_bias = d.dt_bias;
+  p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.dx = dx;
+  p.ddt = ddt;
+  p.dz = dz;
+  p.dA = dA;
+  p.dB = dB;
+  p.dC = dC;
+  p.dD = dD;
+  p.dh0 = dh0;
+  float *ws = static_cast<float *>(d.workspace);
+  p.ws_dBh = ws;
+  p.ws_dCh = ws + wl.bh_terms;
+  p.ws_u = p.ws_dCh + wl.bh_terms;
+  p.ws_phi0 = p.ws_u + wl.u;
+  p.ws_dApart = p.ws_phi0 + wl.per_bh;
+  p.ws_dDpart = p.ws_dApart + wl.per_bh;
+  p.batch = d.batch;
+  p.seqlen = d.seqlen;
+  p.nheads = d.nheads;
+  p.ngroups = d.ngroups;
+  p.dstate = d.dstate;
+  const hipError_t e = ssm::launch_ssd_bwd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssd backward launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Decode steps
 // ---------------------------------------------------------------------------
 

@@ -99,6 +99,25 @@ hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
 constexpr int64_t kSsdMinBlocks = 256;
 int ssd_heads_per_block(int64_t batch, int64_t nheads, int64_t ngroups, int max_hpb);
 
+// The SSD backward (see ssd_bwd in include/ssm.h): a forward walk and a
+// reverse walk per (batch, head), then sums over heads and batch rows.
+struct SsdBwdParams {
+  const void *x, *dt, *B, *C, *z;     // bf16
+  const void *dy;                     // bf16 or float32 (the forward's out dtype)
+  const float *A, *D, *h0, *dh_last;  // float32; D, h0, dh_last nullable
+  const float *dt_bias;               // nullable (nheads); read when dt_softplus
+  int32_t dt_softplus;
+  void *dx, *ddt, *dz;                // bf16; dz only with z
+  float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
+  // Workspace: per-head dB and dC terms [batch][seqlen][nheads][dstate], the
+  // scalars u_t = dyhat_t . Y_t [batch][seqlen][nheads], and per (batch,
+  // head) <dh_last, S_{L-1}>, dA and dD terms.
+  float *ws_dBh, *ws_dCh, *ws_u, *ws_phi0, *ws_dApart, *ws_dDpart;
+  int64_t batch, seqlen, nheads, ngroups, dstate;
+};
+
+hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream);
+
 // One decode step (see ssm_scan_step and ssd_step in include/ssm.h).  The
 // SSD step is the scan step over channels d = (head, p) with A, dt and D
 // taken per head (headdim channels per head); the scan step has headdim 1.

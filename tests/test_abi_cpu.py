@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 19, declared
+    assert len(declared) == 21, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -440,3 +440,38 @@ def test_noalloc_scan_rejects_a_carry_beyond_its_scratch():
     rc = lib.ssm_scan_fwd_noalloc(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
                                   None, None, None, FAKE + 0x10000000, None, ctypes.byref(d), None)
     assert rc == -5
+
+
+def test_ssd_bwd_rules():
+    """ssd_bwd runs the SSD's size checks plus its own before any HIP call."""
+    lib = ssm.lib()
+    G = 1 << 28  # spacing of the fake tensors (each well below it)
+    ptr = lambda k: FAKE + k * G
+
+    def call(d, **kw):
+        a = dict(x=ptr(0), dt=ptr(1), A=ptr(2), B=ptr(3), C=ptr(4), D=None, z=None, h0=None, dy=ptr(5),
+                 dhl=None, dx=ptr(6), ddt=ptr(7), dA=ptr(8), dB=ptr(9), dC=ptr(10), dD=None, dz=None, dh0=None)
+        a.update(kw)
+        return lib.ssd_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["dy"], a["dhl"],
+                           a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dh0"],
+                           ctypes.byref(d), None)
+
+    d = _sdims()
+    need = ctypes.c_size_t(0)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)) == 0
+    b, L, H, N = d.batch, d.seqlen, d.nheads, d.dstate
+    assert need.value == 4 * (2 * b * L * H * N + b * L * H + 3 * b * H)
+    assert call(d) == -6                                        # workspace missing
+    d.workspace, d.workspace_bytes = ptr(11), need.value
+    assert call(d, dx=None) == -1
+    assert call(d, z=ptr(12)) == -1                             # dz required with z
+    assert call(d, D=ptr(12)) == -1                             # dD required with D
+    assert call(d, dB=ptr(0)) == -2                             # output overlaps an input
+    assert call(d, dC=ptr(9)) == -2                             # two outputs overlap
+    assert call(d, dx=ptr(11)) == -2                            # output overlaps the workspace
+    assert call(d, dy=ptr(5) + 1) == -4                         # dy alignment (bf16: 2 bytes)
+    d2 = _sdims(flags=2)
+    d2.workspace, d2.workspace_bytes = ptr(11), need.value
+    assert call(d2) == -2                                       # no trapezoid flag here
+    d3 = _sdims(headdim=32)
+    assert call(d3) == -5

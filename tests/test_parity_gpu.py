@@ -1027,3 +1027,124 @@ def test_scan_backward_dt_softplus(dtype, N, with_bias):
     for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
         err = rel_err(g[k].float().cpu(), ref[k])
         assert err <= tol, (k, err)
+
+
+# ---------------------------------------------------------------------------
+# Scalar-decay SSD backward
+# ---------------------------------------------------------------------------
+
+SSD_BWD_KEYS = ("dx", "ddt", "dA", "dB", "dC", "dD", "dz", "dh0")
+
+SSD_BWD_CASES = [
+    # (batch, L, H, N, G, has_z, dskip, h0, dh_last, dy dtype)
+    (1, 64, 1, 128, 1, False, "ones", False, False, "bf16"),
+    (2, 203, 4, 128, 2, True, "normal", True, True, "bf16"),   # ragged step tile, groups, gate
+    (1, 1, 2, 128, 1, True, "normal", True, True, "bf16"),     # L = 1
+    (3, 130, 3, 64, 1, False, "normal", False, True, "f32"),   # dstate 64, float32 dy
+    (2, 67, 4, 64, 4, True, "none", True, False, "f32"),       # a group per head
+    (2, 97, 8, 128, 2, True, "normal", True, True, "f32"),
+    (4, 33, 6, 128, 3, True, "normal", False, True, "bf16"),
+]
+
+
+def _ssd_bwd_pair(inp, dy, h0=None, dhl=None, **kw):
+    g = ssm.ssd_bwd(_dev(inp["x"]), _dev(inp["dt"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                    _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy), h0=_dev(h0), dh_last=_dev(dhl),
+                    **{k: (_dev(v) if torch.is_tensor(v) else v) for k, v in kw.items()})
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.float().cpu()) for k, v in g.items()}
+
+
+def _check_ssd_bwd(g, ref, label=""):
+    errs = {}
+    for k in SSD_BWD_KEYS:
+        if ref[k] is None:
+            assert g[k] is None, k
+            continue
+        errs[k] = rel_err(g[k], ref[k])
+    if label:
+        print(f"{label}: whole-tensor rel err " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    for k, err in errs.items():
+        assert err <= TOL_BF16, (k, err)
+
+
+@pytest.mark.parametrize("case", SSD_BWD_CASES, ids=lambda c: "b{}l{}h{}n{}g{}_z{}_{}_h0{}_dh{}_{}".format(*c))
+def test_ssd_backward(case):
+    batch, L, H, N, G, has_z, dskip, with_h0, with_dhl, dyt = case
+    seed = 8000 + zlib.crc32(repr(case).encode()) % 1000
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip=dskip, seed=seed)
+    inp = make_ssd_inputs(s)
+    h0 = make_state((batch, H, 64, N), seed=seed + 1, scale=0.5) if with_h0 else None
+    dhl = make_state((batch, H, 64, N), seed=seed + 2, scale=0.5) if with_dhl else None
+    dy = make_state((batch, L, H, 64), seed=seed + 3).to(DT[dyt])
+    ref = oracle.ssd_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0, dy, dhl)
+    _check_ssd_bwd(_ssd_bwd_pair(inp, dy, h0, dhl), ref)
+
+
+def test_ssd_backward_dt_softplus():
+    """Raw dt with a per-head bias: ddt is the gradient of the raw value."""
+    batch, L, H, N, G = 2, 150, 4, 128, 2
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=True, dskip="normal", seed=8100)
+    inp = make_ssd_inputs(s)
+    raw, bias = make_raw_step((batch, L, H), H, 8101, "bf16")
+    h0 = make_state((batch, H, 64, N), seed=8102, scale=0.5)
+    dhl = make_state((batch, H, 64, N), seed=8103, scale=0.5)
+    dy = make_state((batch, L, H, 64), seed=8104).to(torch.bfloat16)
+    ref = oracle.ssd_bwd(inp["x"], raw, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0, dy, dhl,
+                         dt_softplus=True, dt_bias=bias)
+    inp = dict(inp, dt=raw)
+    _check_ssd_bwd(_ssd_bwd_pair(inp, dy, h0, dhl, dt_softplus=True, dt_bias=bias), ref)
+
+
+def test_ssd_backward_empty_sequence():
+    """L = 0: dh0 = dh_last and dA, dD are zero (written)."""
+    s = SsdShape(2, 0, 4, 64, 128, 1, 64, "bf16", has_z=True, dskip="normal", seed=8200)
+    inp = make_ssd_inputs(s)
+    dhl = make_state((2, 4, 64, 128), seed=8201)
+    dy = torch.zeros((2, 0, 4, 64), dtype=torch.bfloat16)
+    g = _ssd_bwd_pair(inp, dy, None, dhl)
+    assert torch.equal(g["dh0"], dhl)
+    assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0)
+
+
+def test_ssd_backward_deterministic():
+    s = SsdShape(3, 100, 4, 64, 128, 2, 64, "bf16", has_z=True, dskip="normal", seed=8300)
+    inp = make_ssd_inputs(s)
+    dy = make_state((3, 100, 4, 64), seed=8301).to(torch.bfloat16)
+    dhl = make_state((3, 4, 64, 128), seed=8302)
+    a = _ssd_bwd_pair(inp, dy, None, dhl)
+    b = _ssd_bwd_pair(inp, dy, None, dhl)
+    for k in SSD_BWD_KEYS:
+        assert (a[k] is None and b[k] is None) or torch.equal(a[k], b[k]), k
+
+
+def ref_ssd_bwd_rows(inp, dy, dh_last=None):
+    """The oracle SSD backward over the whole tensor, one host thread per batch
+    row (dA and dD sum over rows; every other gradient is per row)."""
+    batch = inp["x"].shape[0]
+
+    def one(b):
+        r = {k: (None if v is None else (v[b:b + 1] if k in ("x", "dt", "B", "C", "z") else v))
+             for k, v in inp.items()}
+        return oracle.ssd_bwd(r["x"], r["dt"], r["A"], r["B"], r["C"], r["D"], r["z"], None, dy[b:b + 1],
+                              None if dh_last is None else dh_last[b:b + 1])
+
+    with ThreadPoolExecutor(max_workers=min(batch, 16)) as ex:
+        parts = list(ex.map(one, range(batch)))
+    out = {}
+    for k in ("dx", "ddt", "dB", "dC", "dz", "dh0"):
+        out[k] = None if parts[0][k] is None else np.concatenate([p[k] for p in parts])
+    for k in ("dA", "dD"):
+        out[k] = None if parts[0][k] is None else np.sum([p[k] for p in parts], axis=0)
+    return out
+
+
+def test_ssd_backward_named_workload_full_size():
+    """The SSD workload (batch 32, 256 steps, 32 heads x 64, dstate 128) at
+    full size: every gradient over the whole tensor against the oracle."""
+    s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(s)
+    dy = make_state((s.batch, s.seqlen, s.nheads, s.headdim), seed=8400).to(torch.bfloat16)
+    dhl = make_state((s.batch, s.nheads, s.headdim, s.dstate), seed=8401, scale=0.5)
+    g = _ssd_bwd_pair(inp, dy, None, dhl)
+    _check_ssd_bwd(g, ref_ssd_bwd_rows(inp, dy, dhl), "ssd_32x256_h32p64n128_bf16 backward")
