@@ -221,7 +221,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(hbm_gbs / HBM_PEAK_GBS, 4)}
     roof["traffic"] = measured_traffic(args.workload) if chunks == 1 else None
-    roof["kernel"] = "scan_chunk_kernel<bf16,bf16,16,sweep>" if s.dtype == "bf16" else "scan_chunk_kernel<f32,f32,16,sweep>"
+    roof["kernel"] = "scan_row_kernel<bf16,bf16,16,sweep>" if s.dtype == "bf16" else "scan_row_kernel<f32,f32,16,sweep>"
     roof["hbm_gbs"] = round(hbm_gbs, 1)
     roof["hbm_frac"] = round(hbm_gbs / HBM_PEAK_GBS, 4)
     roof["alu_model_us"] = round(t_alu * 1e6, 2)
@@ -299,7 +299,7 @@ def main():
 
 def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs):
     """The scan backward on the long-prefill and large-channel workloads; the
-    trapezoidal SSD, the rotary step on B and C and the SSD on the rotated
+    trapezoidal SSD, the SSD backward, the rotary step on B and C and the SSD on the rotated
     (per-head) B and C, on the SSD workload's shapes."""
     import torch
     from state_space_model_ssm_amd.synth import make_lam
@@ -326,6 +326,20 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
     nbytes = w.metric_bytes() + w.hlast_bytes() + lam.numel() * 2
     out["ssd_trap_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
                                               "hbm_GB/s_with_h_last": round(nbytes / ms / 1e6, 1)}
+    # The SSD backward on the same shapes (bf16 dy, dh_last absent).  Bytes:
+    # x, dt, B, C, dy read and dx, ddt, dB, dC (float32) written once each, the
+    # least any backward moves.
+    g = torch.Generator(device="cpu").manual_seed(12)
+    dy = torch.randn(w.batch, w.seqlen, w.nheads, w.headdim, generator=g).to(torch.bfloat16).to(dev)
+    dims = ssm._ssd_dims(d["x"], d["B"], 64, ssm._dtype_code(d["x"].dtype), ssm._dtype_code(dy.dtype))
+    ws = torch.empty(max(ssm.ssd_bwd_workspace_size(dims), 1), dtype=torch.uint8, device=dev)
+    ms, _ = time_calls(lambda: ssm.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy,
+                                           workspace=ws, stream=stream), 20, 3)
+    nbytes = (2 * d["x"].numel() + 2 * d["dt"].numel()) * 2 + 2 * d["B"].numel() * (2 + 4) + dy.numel() * 2
+    out["ssd_backward_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                                  "hbm_GB/s_min_bytes": round(nbytes / ms / 1e6, 1),
+                                                  "workspace_MB": round(ws.numel() / 1e6, 1)}
+    del dy, ws
     # The rotary step on the same shapes (one set of angles for all heads),
     # then the SSD on the rotated, per-head B and C.
     from state_space_model_ssm_amd.synth import make_theta
