@@ -328,9 +328,12 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
                          float *h_last, const ssd_dims_t *dims, void *stream);
 
 /*
- * Workspace ssd_bwd needs for `dims`, 4 bytes per float: per-head dB and dC
- * terms, 2 * batch * seqlen * nheads * dstate floats; one scalar per (batch,
- * step, head), batch * seqlen * nheads floats; and three per (batch, head).
+ * Workspace ssd_bwd needs for `dims`.  With K = ceil(seqlen / 64) chunks and
+ * the chunk kernel's hpw heads per workgroup (a function of the sizes, up to
+ * 8): three bf16 state matrices per (batch, head, chunk) (3 * batch * nheads
+ * * K * headdim * dstate * 2 bytes), three floats per (batch, head, chunk),
+ * and two float32 (batch, seqlen, nheads / hpw, dstate) arrays of dB and dC
+ * terms; each region rounded up to 256 bytes.
  */
 SSM_API int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
 
@@ -338,19 +341,21 @@ SSM_API int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
  * Backward of the scalar-decay SSD (ssd_chunked_fwd): gradients of a loss L
  * with respect to every input, given dy = dL/dy and dh_last = dL/dh_last.
  *
- * The chain rule on the recurrence of ssd_chunked_fwd ([Mamba-3 NKI],
- * "Correctness", reports backward parity of the SSD; no formulas are
- * printed).  With yhat_t = S_t C_t + D x_t, dyhat_t = dy_t silu(z_t) and
- * Lam_t = dL/dS_t walked from the last step to the first (Lam after the last
- * step = dh_last):
- *   Lam_t = dyhat_t C_t^T + exp(dt_{t+1} A) Lam_{t+1}
+ * The chain rule on the chunked form of ssd_chunked_fwd ([Mamba-3 NKI],
+ * "Kernel details", the chunk-64 SSD; "Correctness" reports backward parity
+ * of the SSD and prints no formulas).  With yhat = S C + D x, dyhat = dy
+ * silu(z) and Lam_t = dL/dS_t (Lam after the last step = dh_last):
  *   dx_t  = dt_t Lam_t B_t + D dyhat_t,        dz_t = dy_t yhat_t silu'(z_t)
  *   ddt_t = sum_{p,n} Lam_t (x_t B_t^T + A exp(dt_t A) S_{t-1})
  *   dB_t  = sum over the group's heads of dt_t Lam_t^T x_t
  *   dC_t  = sum over the group's heads of S_t^T dyhat_t
  *   dA    = sum over batch and steps of dt_t sum Lam_t exp(dt_t A) S_{t-1}
  *   dD    = sum over batch and steps of dyhat_t . x_t;   dh0 = exp(dt_0 A) Lam_0
- * Nothing from the forward call is needed: the states are rebuilt from h0.
+ * computed chunk by chunk: a forward pass rebuilds the state entering every
+ * chunk from h0, a reverse pass the gradient leaving every chunk from
+ * dh_last, and every chunk's gradients then follow from matrix products over
+ * the chunk (bf16 operands, float32 accumulation, as the forward).  Nothing
+ * from the forward call is needed.
  *
  * Inputs: as ssd_chunked_fwd (dims, x, dt, A, B, C, D, z, h0), plus
  *   dy      : (batch, seqlen, nheads, headdim) out_dtype
@@ -365,9 +370,10 @@ SSM_API int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
  * The sums over heads (dB, dC) and over batch rows (dA, dD) run in a fixed
  * order, so every output is deterministic.  No output may overlap an input,
  * another output or the workspace (dims->workspace, at least
- * ssd_bwd_workspace_size() bytes, 16-byte aligned).  Pointers need their
- * element alignment.  Supported sizes are those of ssd_chunked_fwd; flags 0
- * or SSM_DT_SOFTPLUS.
+ * ssd_bwd_workspace_size() bytes, 16-byte aligned).  x, z, B, C, dy, h0,
+ * dh_last and dh0 must be 16-byte aligned, the other pointers element
+ * aligned.  Supported sizes are those of ssd_chunked_fwd; flags 0 or
+ * SSM_DT_SOFTPLUS.
  */
 SSM_API int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
             const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,

@@ -589,18 +589,24 @@ int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const f
 // Scalar-decay SSD backward
 // ---------------------------------------------------------------------------
 
-// Backward workspace, in floats: per-head dB and dC terms, the scalars u_t,
-// and per (batch, head) phi0, dA and dD terms.
+// Backward workspace: per (batch, head, chunk) three bf16 state matrices
+// (S_in twice, dS once) and three floats; per (batch, step, head block) the
+// float32 dB and dC terms.  Each region starts on a 256-byte boundary.
 struct SsdBwdWorkspace {
-  size_t bh_terms, u, per_bh;
-  size_t bytes() const { return 4 * (2 * bh_terms + u + 3 * per_bh); }
+  int64_t nchunks;
+  int32_t hpw;
+  size_t state, per_bhc, bp;  // elements of one region
+  static size_t up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+  size_t bytes() const { return 3 * up(2 * state) + 3 * up(4 * per_bhc) + 2 * up(4 * bp); }
 };
 
 static SsdBwdWorkspace ssd_bwd_layout(const ssd_dims_t *d) {
   SsdBwdWorkspace w;
-  w.bh_terms = static_cast<size_t>(d->batch * d->seqlen * d->nheads * d->dstate);
-  w.u = static_cast<size_t>(d->batch * d->seqlen * d->nheads);
-  w.per_bh = static_cast<size_t>(d->batch * d->nheads);
+  w.nchunks = (d->seqlen + 63) / 64;
+  w.hpw = d->nheads > 0 ? ssm::ssd_bwd_heads_per_block(d->batch, d->seqlen, d->nheads, d->ngroups) : 1;
+  w.per_bhc = static_cast<size_t>(d->batch * d->nheads * w.nchunks);
+  w.state = w.per_bhc * static_cast<size_t>(d->headdim * d->dstate);
+  w.bp = static_cast<size_t>(d->batch * d->seqlen * (d->nheads / w.hpw) * d->dstate);
   return w;
 }
 
@@ -631,13 +637,14 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   if (!z) dz = nullptr;
   if (!D) dD = nullptr;
   const size_t eo = dtype_size(d.out_dtype);
-  if (!aligned(x, 2) || !aligned(dt, 2) || !aligned(B, 2) || !aligned(C, 2) || !aligned(z, 2) ||
-      !aligned(dx, 2) || !aligned(ddt, 2) || !aligned(dz, 2))
-    return fail(SSM_ERR_ALIGN, "bf16 pointers must be 2-byte aligned");
-  if (!aligned(dy, eo)) return fail(SSM_ERR_ALIGN, "dy must be aligned to %zu bytes", eo);
-  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(h0, 4) || !aligned(dh_last, 4) || !aligned(dA, 4) ||
-      !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4) || !aligned(dh0, 4))
-    return fail(SSM_ERR_ALIGN, "float32 pointers must be 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16) || !aligned(dy, 16))
+    return fail(SSM_ERR_ALIGN, "x, z, B, C and dy must be 16-byte aligned");
+  if (!aligned(dt, 2) || !aligned(dx, 2) || !aligned(ddt, 2) || !aligned(dz, 2))
+    return fail(SSM_ERR_ALIGN, "dt, dx, ddt and dz must be 2-byte aligned");
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4))
+    return fail(SSM_ERR_ALIGN, "A, D, dA, dB, dC and dD must be 4-byte aligned");
+  if (!aligned(h0, 16) || !aligned(dh_last, 16) || !aligned(dh0, 16))
+    return fail(SSM_ERR_ALIGN, "h0, dh_last and dh0 must be 16-byte aligned");
   const Span ins[] = {{x, n_x * 2ull},       {dt, n_dt * 2ull},   {z, n_x * 2ull},        {B, n_bc * 2ull},
                       {C, n_bc * 2ull},      {A, d.nheads * 4ull}, {D, d.nheads * 4ull}, {h0, n_h * 4ull},
                       {dy, n_x * eo},        {dh_last, n_h * 4ull}, {d.dt_bias, d.nheads * 4ull}};
@@ -685,13 +692,18 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   p.dC = dC;
   p.dD = dD;
   p.dh0 = dh0;
-  float *ws = static_cast<float *>(d.workspace);
-  p.ws_dBh = ws;
-  p.ws_dCh = ws + wl.bh_terms;
-  p.ws_u = p.ws_dCh + wl.bh_terms;
-  p.ws_phi0 = p.ws_u + wl.u;
-  p.ws_dApart = p.ws_phi0 + wl.per_bh;
-  p.ws_dDpart = p.ws_dApart + wl.per_bh;
+  uint8_t *ws = static_cast<uint8_t *>(d.workspace);
+  const size_t st = SsdBwdWorkspace::up(2 * wl.state), sc = SsdBwdWorkspace::up(4 * wl.per_bhc);
+  p.ws_Sn = reinterpret_cast<uint16_t *>(ws);
+  p.ws_Sp = reinterpret_cast<uint16_t *>(ws + st);
+  p.ws_dSp = reinterpret_cast<uint16_t *>(ws + 2 * st);
+  p.ws_phi = reinterpret_cast<float *>(ws + 3 * st);
+  p.ws_dApart = reinterpret_cast<float *>(ws + 3 * st + sc);
+  p.ws_dDpart = reinterpret_cast<float *>(ws + 3 * st + 2 * sc);
+  p.ws_dBp = reinterpret_cast<float *>(ws + 3 * st + 3 * sc);
+  p.ws_dCp = reinterpret_cast<float *>(ws + 3 * st + 3 * sc + SsdBwdWorkspace::up(4 * wl.bp));
+  p.nchunks = wl.nchunks;
+  p.hpw = wl.hpw;
   p.batch = d.batch;
   p.seqlen = d.seqlen;
   p.nheads = d.nheads;

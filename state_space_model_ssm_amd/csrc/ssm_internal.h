@@ -99,8 +99,9 @@ hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
 constexpr int64_t kSsdMinBlocks = 256;
 int ssd_heads_per_block(int64_t batch, int64_t nheads, int64_t ngroups, int max_hpb);
 
-// The SSD backward (see ssd_bwd in include/ssm.h): a forward walk and a
-// reverse walk per (batch, head), then sums over heads and batch rows.
+// The SSD backward (see ssd_bwd in include/ssm.h): a forward and a reverse
+// state pass per (batch, head), then a kernel per (batch, chunk, block of hpw
+// heads) and the sums over head blocks, batch rows and chunks.
 struct SsdBwdParams {
   const void *x, *dt, *B, *C, *z;     // bf16
   const void *dy;                     // bf16 or float32 (the forward's out dtype)
@@ -109,12 +110,21 @@ struct SsdBwdParams {
   int32_t dt_softplus;
   void *dx, *ddt, *dz;                // bf16; dz only with z
   float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
-  // Workspace: per-head dB and dC terms [batch][seqlen][nheads][dstate], the
-  // scalars u_t = dyhat_t . Y_t [batch][seqlen][nheads], and per (batch,
-  // head) <dh_last, S_{L-1}>, dA and dD terms.
-  float *ws_dBh, *ws_dCh, *ws_u, *ws_phi0, *ws_dApart, *ws_dDpart;
-  int64_t batch, seqlen, nheads, ngroups, dstate;
+  // Workspace, per (batch, head, chunk): the chunk's entering state S_in as
+  // [dstate][headdim] (ws_Sn) and, with a gate, [headdim][dstate] (ws_Sp),
+  // the gradient of its leaving state as [headdim][dstate] (ws_dSp), all
+  // bf16; <dS, S_in>, the dA and dD terms (float32).  Per (batch, step, head
+  // block), the dB and dC terms [batch][seqlen][nheads / hpw][dstate].
+  uint16_t *ws_Sn, *ws_Sp, *ws_dSp;
+  float *ws_phi, *ws_dApart, *ws_dDpart, *ws_dBp, *ws_dCp;
+  int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
+  int32_t hpw;                        // heads per chunk-kernel workgroup
 };
+
+// The chunk kernel takes hpw heads of a group per workgroup: the most (up to
+// 8) that keep its grid at kSsdBwdMinBlocks workgroups or more.
+constexpr int64_t kSsdBwdMinBlocks = 1024;
+int ssd_bwd_heads_per_block(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ngroups);
 
 hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream);
 

@@ -459,8 +459,10 @@ def test_ssd_bwd_rules():
     d = _sdims()
     need = ctypes.c_size_t(0)
     assert lib.ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)) == 0
-    b, L, H, N = d.batch, d.seqlen, d.nheads, d.dstate
-    assert need.value == 4 * (2 * b * L * H * N + b * L * H + 3 * b * H)
+    b, L, H, N, P = d.batch, d.seqlen, d.nheads, d.dstate, d.headdim
+    up = lambda v: (v + 255) // 256 * 256
+    K, hpw = (L + 63) // 64, 1   # 2 x 2 x 4 heads: too few workgroups to share heads
+    assert need.value == 3 * up(2 * b * H * K * P * N) + 3 * up(4 * b * H * K) + 2 * up(4 * b * L * (H // hpw) * N)
     assert call(d) == -6                                        # workspace missing
     d.workspace, d.workspace_bytes = ptr(11), need.value
     assert call(d, dx=None) == -1
@@ -469,7 +471,8 @@ def test_ssd_bwd_rules():
     assert call(d, dB=ptr(0)) == -2                             # output overlaps an input
     assert call(d, dC=ptr(9)) == -2                             # two outputs overlap
     assert call(d, dx=ptr(11)) == -2                            # output overlaps the workspace
-    assert call(d, dy=ptr(5) + 1) == -4                         # dy alignment (bf16: 2 bytes)
+    assert call(d, dy=ptr(5) + 2) == -4                         # dy alignment (16 bytes)
+    assert call(d, h0=ptr(12) + 4) == -4                        # h0 alignment (16 bytes)
     d2 = _sdims(flags=2)
     d2.workspace, d2.workspace_bytes = ptr(11), need.value
     assert call(d2) == -2                                       # no trapezoid flag here
