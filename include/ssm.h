@@ -330,8 +330,8 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
 /*
  * Workspace ssd_bwd needs for `dims`.  With K = ceil(seqlen / 64) chunks and
  * the chunk kernel's hpw heads per workgroup (a function of the sizes, up to
- * 8): three bf16 state matrices per (batch, head, chunk) (3 * batch * nheads
- * * K * headdim * dstate * 2 bytes), three floats per (batch, head, chunk),
+ * 8): two bf16 state matrices per (batch, head, chunk) (2 * batch * nheads
+ * * K * headdim * dstate * 2 bytes), two floats per (batch, head, chunk),
  * and two float32 (batch, seqlen, nheads / hpw, dstate) arrays of dB and dC
  * terms; each region rounded up to 256 bytes.
  */

@@ -25,7 +25,7 @@
 //   * state pass, forward: per (batch, head), the chunk states S_in from h0
 //     (the forward's state update, MFMA over the chunk's steps), stored bf16;
 //   * state pass, reverse: per (batch, head), dS of every chunk from dh_last,
-//     stored bf16, with <dS, S_in> per chunk and dh0;
+//     stored bf16, and dh0;
 //   * chunk kernel: every (batch, chunk, block of heads) at once: the products
 //     above on matrix cores (v_mfma_f32_16x16x32_bf16), dx, ddt, dz directly,
 //     dB and dC summed over the block's heads in registers, dA and dD terms;
@@ -47,6 +47,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int Q = 64;        // chunk length
@@ -86,10 +87,11 @@ __device__ __forceinline__ bf16x8 frag_t(const uint16_t *T, int k0, int i0, int 
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Sum over the 16 lanes of this lane's DPP row, in every lane of the row.
+// Sum over the 16 lanes of this lane's DPP row, in every lane of the row
+// (rotations: every source lane is valid).
 template <int R>
 __device__ __forceinline__ float row_ror(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_sum(float v) {
   v += row_ror<8>(v);
@@ -119,10 +121,32 @@ __device__ __forceinline__ float wave_prefix(float a, int lane) {
   return a + (lane >= 16 ? r0 : 0.0f) + (lane >= 32 ? r1 : 0.0f) + (lane >= 48 ? r2 : 0.0f);
 }
 
+// Sum over the 64 lanes, the same in every lane: DPP row sums, then the
+// four row totals read with v_readlane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v = row_sum(v);
+  return (lane_value<0>(v) + lane_value<16>(v)) + (lane_value<32>(v) + lane_value<48>(v));
+}
+
+// Value of lane (l + N) of this lane's 16-lane row, 0 outside the row.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x100 + N, 0xF, 0xF, true));
+}
+
+// Inclusive suffix sum over the 64 lanes: sum of lanes l .. 63.
+__device__ __forceinline__ float wave_suffix(float a, int lane) {
+  a += row_shl<1>(a);
+  a += row_shl<2>(a);
+  a += row_shl<4>(a);
+  a += row_shl<8>(a);
+  const float r1 = lane_value<16>(a), r2 = lane_value<32>(a), r3 = lane_value<48>(a);
+  return a + (lane < 48 ? r3 : 0.0f) + (lane < 32 ? r2 : 0.0f) + (lane < 16 ? r1 : 0.0f);
+}
+
+// The value of v[m] for the lanes m < 4 of a row that store one of four row sums.
+__device__ __forceinline__ float pick4(const float (&v)[4], int m) {
+  return m == 0 ? v[0] : m == 1 ? v[1] : m == 2 ? v[2] : v[3];
 }
 
 // Eight consecutive elements of dy (float32 or bf16) as float32.
@@ -180,19 +204,22 @@ __device__ __forceinline__ void chunk_steps(const SsdBwdParams &p, int64_t b, in
 
 // ---- state passes -------------------------------------------------------------
 // REV = false: S_in of every chunk from h0 (U = B, V = x, weight dt_t e^{a_last - a_t}),
-//   stored as S_in[n][p] (and S_in[p][n] with a gate, for the chunk kernel's Y).
+//   stored as S_in[p][n].
 // REV = true: dS of every chunk from dh_last, walking the chunks backwards
-//   (U = C, V = dyhat, weight e^{a_t}), stored as dS[p][n], with
-//   phi_c = <dS, S_in> per chunk, and dh0 at the end.
+//   (U = C, V = dyhat, weight e^{a_t}), stored as dS[p][n]; dh0 at the end.
 // State tiles as in the forward: rows n = 16 ni + 4q + r, column p = 16 w + i.
+// The next chunk's inputs are loaded into registers while the current one
+// is computed.
 template <int N, bool REV, typename Tdy, bool HAS_Z>
 __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p) {
-  constexpr int NT = N / 16, NPC = N + 8;
+  constexpr int NT = N / 16, NPC = N + 24;
+  constexpr int UJ = Q * (N / 8) / 256;  // U jobs (8 elements) per thread
+  constexpr int VJ = Q * (P / 8) / 256;  // V jobs per thread
+  constexpr int DW = sizeof(Tdy) / 2;    // dy: 16-byte words per 8 elements
   __shared__ __attribute__((aligned(16))) uint16_t sU[Q * NPC];
   __shared__ __attribute__((aligned(16))) uint16_t sV[Q * PP];
   __shared__ __attribute__((aligned(16))) float sOm[Q];
   __shared__ float sDec;
-  __shared__ float sRed[4];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -213,63 +240,103 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
     S[ni] = init ? *reinterpret_cast<const floatx4 *>(init + (bh * P + pcol) * N + 16 * ni + 4 * q)
                  : floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t ci = 0; ci < nC; ++ci) {
-    const int64_t c = REV ? nC - 1 - ci : ci;
+  struct Regs {
+    uint4 u[UJ];
+    uint4 v[VJ][REV ? DW : 1];
+    uint4 z[HAS_Z && REV ? VJ : 1];
+    uint32_t dt;  // raw bf16 bits of this lane's step (wavefront 0)
+  };
+  // Rows past the end are loaded from the last valid step (branch-free) and
+  // zeroed when staged.
+  auto load = [&](int64_t c, Regs &R) __attribute__((always_inline)) {
     const int64_t c0 = c * Q;
-    const int Lc = static_cast<int>(min(static_cast<int64_t>(Q), L - c0));
-    for (int e = tid; e < Q * (N / 8); e += 256) {
-      const int t = e / (N / 8), nv = (e % (N / 8)) * 8;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (t < Lc) v = *reinterpret_cast<const uint4 *>(gU + ((b * L + c0 + t) * G + g) * N + nv);
-      *reinterpret_cast<uint4 *>(&sU[t * NPC + nv]) = v;
+    const int last = static_cast<int>(min(static_cast<int64_t>(Q), L - c0)) - 1;
+#pragma unroll
+    for (int k = 0; k < UJ; ++k) {
+      const int e = tid + 256 * k, t = min(e / (N / 8), last), nv = (e % (N / 8)) * 8;
+      R.u[k] = *reinterpret_cast<const uint4 *>(gU + ((b * L + c0 + t) * G + g) * N + nv);
     }
-    for (int e = tid; e < Q * (P / 8); e += 256) {
-      const int t = e / (P / 8), pv = (e % (P / 8)) * 8;
+#pragma unroll
+    for (int k = 0; k < VJ; ++k) {
+      const int e = tid + 256 * k, t = min(e / (P / 8), last), pv = (e % (P / 8)) * 8;
       const int64_t o = ((b * L + c0 + t) * H + h) * P + pv;
-      uint4 v = {0u, 0u, 0u, 0u};
       if constexpr (!REV) {
-        if (t < Lc) v = *reinterpret_cast<const uint4 *>(gx + o);
+        R.v[k][0] = *reinterpret_cast<const uint4 *>(gx + o);
       } else {
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const Tdy *>(p.dy) + o);
+#pragma unroll
+        for (int w = 0; w < DW; ++w) R.v[k][w] = src[w];
+        if constexpr (HAS_Z) R.z[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.z) + o);
+      }
+    }
+    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, last)) * H + h];
+  };
+  auto stage = [&](int64_t c, const Regs &R) __attribute__((always_inline)) {
+    const int Lc = static_cast<int>(min(static_cast<int64_t>(Q), L - c * Q));
+#pragma unroll
+    for (int k = 0; k < UJ; ++k) {
+      const int e = tid + 256 * k, t = e / (N / 8), nv = (e % (N / 8)) * 8;
+      *reinterpret_cast<uint4 *>(&sU[t * NPC + nv]) = t < Lc ? R.u[k] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < VJ; ++k) {
+      const int e = tid + 256 * k, t = e / (P / 8), pv = (e % (P / 8)) * 8;
+      uint4 v = R.v[k][0];
+      if constexpr (REV) {
         float dv[8];
-        load_dyhat<Tdy, HAS_Z>(p, o, t < Lc, dv);
+        if constexpr (DW == 2) {
+          const float4 a = __builtin_bit_cast(float4, R.v[k][0]), bq = __builtin_bit_cast(float4, R.v[k][1]);
+          dv[0] = a.x; dv[1] = a.y; dv[2] = a.z; dv[3] = a.w; dv[4] = bq.x; dv[5] = bq.y; dv[6] = bq.z; dv[7] = bq.w;
+        } else {
+          const uint32_t w4[4] = {R.v[k][0].x, R.v[k][0].y, R.v[k][0].z, R.v[k][0].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            dv[2 * j] = __uint_as_float(w4[j] << 16);
+            dv[2 * j + 1] = __uint_as_float(w4[j] & 0xffff0000u);
+          }
+        }
+        if constexpr (HAS_Z) {
+          const uint32_t z4[4] = {R.z[k].x, R.z[k].y, R.z[k].z, R.z[k].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float z0 = __uint_as_float(z4[j] << 16), z1 = __uint_as_float(z4[j] & 0xffff0000u);
+            dv[2 * j] *= z0 * sigm(z0);
+            dv[2 * j + 1] *= z1 * sigm(z1);
+          }
+        }
         v = pack8(dv);
       }
-      *reinterpret_cast<uint4 *>(&sV[t * PP + pv]) = v;
+      *reinterpret_cast<uint4 *>(&sV[t * PP + pv]) = t < Lc ? v : uint4{0u, 0u, 0u, 0u};
     }
     if (wave == 0) {
-      float dtv, a;
-      chunk_steps(p, b, h, c0, Lc, Ah, bias, lane, dtv, a);
+      float dtv = 0.0f;
+      if (lane < Lc) {
+        dtv = bf2f(static_cast<uint16_t>(R.dt));
+        if (p.dt_softplus) dtv = dt_softplus(dtv + bias);
+      }
+      const float a = wave_prefix(dtv * Ah, lane);
       const float alast = lane_value<63>(a);
       sOm[lane] = REV ? fast_exp(a) : dtv * fast_exp(alast - a);
       if (lane == 0) sDec = fast_exp(alast);
     }
-    __syncthreads();
+  };
 
-    // The state of this chunk before its update: S_in (forward) or dS (reverse).
+  Regs R;
+  if (nC > 0) load(REV ? nC - 1 : 0, R);
+  for (int64_t ci = 0; ci < nC; ++ci) {
+    const int64_t c = REV ? nC - 1 - ci : ci;
+    stage(c, R);
+    __syncthreads();
+    if (ci + 1 < nC) load(REV ? c - 1 : c + 1, R);
+
+    // The state of this chunk before its update, [p][n]: S_in (forward) or dS (reverse).
     const int64_t wb = (bh * nC + c) * static_cast<int64_t>(N * P);
-    if constexpr (!REV) {
+    uint16_t *wdst = (REV ? p.ws_dSp : p.ws_Sp) + wb + pcol * N + 4 * q;
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p.ws_Sn[wb + (16 * ni + 4 * q + r) * P + pcol] = f2bf(S[ni][r]);
-        if constexpr (HAS_Z) {
-          const uint32_t lo = static_cast<uint32_t>(f2bf(S[ni][0])) | (static_cast<uint32_t>(f2bf(S[ni][1])) << 16);
-          const uint32_t hi = static_cast<uint32_t>(f2bf(S[ni][2])) | (static_cast<uint32_t>(f2bf(S[ni][3])) << 16);
-          *reinterpret_cast<uint2 *>(p.ws_Sp + wb + pcol * N + 16 * ni + 4 * q) = uint2{lo, hi};
-        }
-      }
-    } else {
-      float ph = 0.0f;
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        const uint32_t lo = static_cast<uint32_t>(f2bf(S[ni][0])) | (static_cast<uint32_t>(f2bf(S[ni][1])) << 16);
-        const uint32_t hi = static_cast<uint32_t>(f2bf(S[ni][2])) | (static_cast<uint32_t>(f2bf(S[ni][3])) << 16);
-        *reinterpret_cast<uint2 *>(p.ws_dSp + wb + pcol * N + 16 * ni + 4 * q) = uint2{lo, hi};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ph = fmaf(S[ni][r], bf2f(p.ws_Sn[wb + (16 * ni + 4 * q + r) * P + pcol]), ph);
-      }
-      ph = wave_sum(ph);
-      if (lane == 0) sRed[wave] = ph;
+    for (int ni = 0; ni < NT; ++ni) {
+      const uint32_t lo = static_cast<uint32_t>(f2bf(S[ni][0])) | (static_cast<uint32_t>(f2bf(S[ni][1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f2bf(S[ni][2])) | (static_cast<uint32_t>(f2bf(S[ni][3])) << 16);
+      *reinterpret_cast<uint2 *>(wdst + 16 * ni) = uint2{lo, hi};
     }
 
     // S <- e^{a_last} S + U^T diag(omega) V  (K = the chunk's steps).
@@ -292,7 +359,6 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
       for (int ni = 0; ni < NT; ++ni) S[ni] = mfma(frag_t<NPC>(sU, 32 * kk, 16 * ni, q, m), bfrag, S[ni]);
     }
     __syncthreads();
-    if (REV && tid == 0) p.ws_phi[bh * nC + c] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
   }
   if constexpr (REV) {
     if (p.dh0) {
@@ -303,15 +369,22 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
 }
 
 // ---- chunk kernel ---------------------------------------------------------------
-// Workgroup: one (batch, chunk) and HPW heads of one group, 4 wavefronts.
+// Workgroup: one (batch, chunk) and HPW heads of one group, 16 wavefronts
+// (four per SIMD: the LDS holds one workgroup per CU).
 // Q x Q tiles (s-tile si, t-tile ti): the 10 with si <= ti plus the zero
 // tiles (1, 0) and (3, 2) that the K = 32 steps of the causal products read;
-// wavefront w takes tiles w, w + 4, w + 8.  Wavefront w owns headdim columns
-// [16 w, 16 w + 16) of dX (and Y) and dstate columns [N/4 w, N/4 (w + 1)) of
-// dB and dC.
+// wavefront w < 12 takes tile w.  Output tiles of the other products: dX and
+// Y (16 x 16 in (step, headdim)): headdim tile w % 4, step tile w / 4; dB and
+// dC (step, dstate): dstate tile w % NT and the step tiles w / NT + k (16 / NT),
+// k < NT / 4.
+constexpr int kBwdWaves = 16;
 template <int N, typename Tdy, bool HAS_Z>
-__global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p) {
-  constexpr int NPC = N + 8, NK = N / 32, NTW = N / 64;  // n-tiles per wavefront
+__global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const SsdBwdParams p) {
+  constexpr int NW = kBwdWaves, NTH = 64 * NW;
+  constexpr int NPC = N + 24, NK = N / 32, NT = N / 16;
+  constexpr int TPW = NT * 4 / NW;     // (step tile, dstate tile) pairs per wavefront in dB and dC
+  constexpr int TSTEP = NW / NT;       // step-tile stride of those pairs
+  static_assert(TPW >= 1 && Q * (P / 8) <= NTH, "work split");
   __shared__ __attribute__((aligned(16))) uint16_t sC[Q * NPC];
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NPC];
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * PP];
@@ -319,18 +392,19 @@ __global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p
   __shared__ __attribute__((aligned(16))) uint16_t sW[Q * QPp];
   __shared__ __attribute__((aligned(16))) uint16_t sDG[Q * QPp];
   __shared__ __attribute__((aligned(16))) uint16_t sM[HAS_Z ? Q * QPp : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sDS[P * NPC];
-  __shared__ float sR[Q * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[P * NPC];   // dS[p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sSp[P * NPC];   // S_in[p][n]
   __shared__ __attribute__((aligned(16))) float sA[Q];
   __shared__ __attribute__((aligned(16))) float sEa[Q];
   __shared__ __attribute__((aligned(16))) float sWl[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
-  __shared__ float sDdt[4][Q], sDaC[4][Q], sDaB[4][Q], sDaR[4][Q];
-  __shared__ float sRed[4];
+  __shared__ float sRow[12][4][16], sCol[12][16];  // per tile: sums of R over s (per lane group, per t) and over t (per s)
+  __shared__ float sDdt[4][Q], sDaC[NT][Q], sDaB[NT][Q];
+  __shared__ float sRed[NW], sPhi[NW];
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int lane = tid % 64, q = lane / 16, m = lane % 16;
+  int lane = tid % 64, q = lane / 16, m = lane % 16;
   const int64_t H = p.nheads, L = p.seqlen, G = p.ngroups, nC = p.nchunks;
   const int HPW = p.hpw;
   const int64_t HB = H / HPW;
@@ -346,9 +420,53 @@ __global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p
   const uint16_t *gC = static_cast<const uint16_t *>(p.C);
   uint16_t *gdx = static_cast<uint16_t *>(p.dx);
   uint16_t *gddt = static_cast<uint16_t *>(p.ddt);
+  const int HP = static_cast<int>(H * P);  // step stride of x, dx, z, dz (below 2^25)
+  const int pt = wave % 4;             // headdim tile of dX and Y
+  const int st = wave / 4;             // step tile of dX and Y
+  const int nt = wave % NT;            // dstate tile of dB and dC
+  const bool xjob = tid < Q * (P / 8);  // this thread stages x and dy (whole wavefronts)
+
+  // One head's global inputs in registers, loaded a head ahead: x and dy
+  // (and z) of one 8-element job, dS[p][n] and S_in[p][n] jobs, and this
+  // lane's raw dt (wavefront 0).  Rows past the end load the last valid step
+  // and are zeroed when staged.
+  constexpr int DW = sizeof(Tdy) / 2;           // dy: 16-byte words per job
+  constexpr int SJOBS = P * (N / 8);              // dS (and S_in) staging jobs
+  constexpr int SJ = (SJOBS + NTH - 1) / NTH;     // per thread
+  struct HeadRegs {
+    u32x4 x, dy[DW], z;
+    u32x4 ds[SJ], sn[SJ];
+    uint32_t dt;
+  };
+  auto load_head = [&](int64_t h, HeadRegs &R) __attribute__((always_inline)) {
+    const int64_t bhc = (b * H + h) * nC + c;
+    if (xjob) {
+      const int t = min(tid / (P / 8), Lc - 1), pv = (tid % (P / 8)) * 8;
+      const int64_t o = ((b * L + c0 + t) * H + h) * P + pv;
+      R.x = *reinterpret_cast<const u32x4 *>(gx + o);
+      const u32x4 *dsrc = reinterpret_cast<const u32x4 *>(static_cast<const Tdy *>(p.dy) + o);
+#pragma unroll
+      for (int w = 0; w < DW; ++w) R.dy[w] = dsrc[w];
+      if constexpr (HAS_Z) R.z = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.z) + o);
+    }
+    const uint16_t *gds = p.ws_dSp + bhc * static_cast<int64_t>(P * N);
+    const uint16_t *gsp = p.ws_Sp + bhc * static_cast<int64_t>(P * N);
+#pragma unroll
+    for (int k = 0; k < SJ; ++k) {
+      const int e = tid + NTH * k;
+      if (SJOBS % NTH == 0 || e < SJOBS) {
+        R.ds[k] = *reinterpret_cast<const u32x4 *>(gds + (e / (N / 8)) * N + (e % (N / 8)) * 8);
+        R.sn[k] = *reinterpret_cast<const u32x4 *>(gsp + (e / (N / 8)) * N + (e % (N / 8)) * 8);
+      }
+    }
+    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, Lc - 1)) * H + h];
+  };
+
+  HeadRegs R;
+  load_head(hb * HPW, R);   // overlaps the staging of C and B and the G tiles
 
   // C and B of the chunk (shared by the heads).
-  for (int e = tid; e < 2 * Q * (N / 8); e += 256) {
+  for (int e = tid; e < 2 * Q * (N / 8); e += NTH) {
     const int ee = e % (Q * (N / 8));
     const int t = ee / (N / 8), nv = (ee % (N / 8)) * 8;
     const bool isb = e >= Q * (N / 8);
@@ -362,81 +480,119 @@ __global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p
   constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 | 0xAull << 20 |
                               0xCull << 24 | 0xDull << 28 | 0xEull << 32 | 0xFull << 36 | 0x1ull << 40 |
                               0xBull << 44;
-  // G^T tiles, G^T[s][t] = B_s . C_t: lane holds s = 16 si + 4q + r, t = 16 ti + m.
-  floatx4 Gt[3];
+  // G^T tile of wavefront w < 12, G^T[s][t] = B_s . C_t: lane holds s =
+  // 16 si + 4q + r, t = 16 ti + m.
+  const int gcode = static_cast<int>((kTiles >> (4 * (wave % 12))) & 0xF);
+  const int gsi = gcode & 3, gti = gcode >> 2;
+  floatx4 Gt = {0.f, 0.f, 0.f, 0.f};
+  if (wave < 12 && gsi <= gti) {
 #pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int code = static_cast<int>((kTiles >> (4 * (wave + 4 * u))) & 0xF);
-    const int si = code & 3, ti = code >> 2;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (si <= ti) {
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        acc = mfma(ld8(&sB[(16 * si + m) * NPC + 32 * kk + 8 * q]), ld8(&sC[(16 * ti + m) * NPC + 32 * kk + 8 * q]), acc);
-    }
-    Gt[u] = acc;
+    for (int kk = 0; kk < NK; ++kk)
+      Gt = mfma(ld8(&sB[(16 * gsi + m) * NPC + 32 * kk + 8 * q]), ld8(&sC[(16 * gti + m) * NPC + 32 * kk + 8 * q]), Gt);
   }
 
-  floatx4 aB[4][NTW], aC[4][NTW];
+  floatx4 aB[TPW], aC[TPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      aB[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-      aC[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int u = 0; u < TPW; ++u) {
+    aB[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+    aC[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   for (int k = 0; k < HPW; ++k) {
+    // The lane indices pass through an empty asm each head, so the LDS
+    // addresses derived from them are recomputed (a few VALU operations)
+    // instead of being held, or spilled, across the loop.
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(q), "+v"(m));
     const int64_t h = hb * HPW + k;
     const int64_t bh = b * H + h, bhc = bh * nC + c;
     const float Ah = p.A[h], Dh = p.D ? p.D[h] : 0.0f;
     const float bias = (p.dt_softplus && p.dt_bias) ? p.dt_bias[h] : 0.0f;
 
     if (wave == 0) {
-      float dtv, a;
-      chunk_steps(p, b, h, c0, Lc, Ah, bias, lane, dtv, a);
+      float dtv = 0.0f;
+      if (lane < Lc) {
+        dtv = bf2f(static_cast<uint16_t>(R.dt));
+        if (p.dt_softplus) dtv = dt_softplus(dtv + bias);
+      }
+      const float a = wave_prefix(dtv * Ah, lane);
       const float alast = lane_value<63>(a);
       sA[lane] = a;
       sEa[lane] = fast_exp(a);
       sWl[lane] = fast_exp(alast - a);
       sDt[lane] = dtv;
     }
-    // x and dyhat of the head's chunk, and its dD term.
-    float dDp = 0.0f;
-    for (int e = tid; e < Q * (P / 8); e += 256) {
-      const int t = e / (P / 8), pv = (e % (P / 8)) * 8;
-      const int64_t o = ((b * L + c0 + t) * H + h) * P + pv;
-      uint4 xv = {0u, 0u, 0u, 0u};
-      if (t < Lc) xv = *reinterpret_cast<const uint4 *>(gx + o);
-      float dv[8], xf[8];
-      load_dyhat<Tdy, HAS_Z>(p, o, t < Lc, dv);
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    // x and dyhat of the head's chunk (one 8-element job per thread of the
+    // first Q P / 8), its dD term, dS[p][n] and S_in[p][n].
+    float dDw = 0.0f;  // this wavefront's dD term
+    if (xjob) {
+      const int t = tid / (P / 8), pv = (tid % (P / 8)) * 8;
+      const bool in = t < Lc;
+      float dv[8];
+      if constexpr (DW == 2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dv[j] = __uint_as_float(R.dy[0][j]);
+          dv[j + 4] = __uint_as_float(R.dy[DW - 1][j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dv[2 * j] = __uint_as_float(R.dy[0][j] << 16);
+          dv[2 * j + 1] = __uint_as_float(R.dy[0][j] & 0xffff0000u);
+        }
+      }
+      if constexpr (HAS_Z) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float z0 = __uint_as_float(R.z[j] << 16), z1 = __uint_as_float(R.z[j] & 0xffff0000u);
+          dv[2 * j] *= z0 * sigm(z0);
+          dv[2 * j + 1] *= z1 * sigm(z1);
+        }
+      }
+      const u32x4 xv = in ? R.x : u32x4{0u, 0u, 0u, 0u};
+      if (!in) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dv[j] = 0.0f;
+      }
+      float dDp = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xf[2 * j] = __uint_as_float(xw[j] << 16);
-        xf[2 * j + 1] = __uint_as_float(xw[j] & 0xffff0000u);
+        dDp = fmaf(dv[2 * j], __uint_as_float(xv[j] << 16), dDp);
+        dDp = fmaf(dv[2 * j + 1], __uint_as_float(xv[j] & 0xffff0000u), dDp);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dDp = fmaf(dv[j], xf[j], dDp);
-      *reinterpret_cast<uint4 *>(&sX[t * PP + pv]) = xv;
+      *reinterpret_cast<u32x4 *>(&sX[t * PP + pv]) = xv;
       *reinterpret_cast<uint4 *>(&sDY[t * PP + pv]) = pack8(dv);
+      dDw = wave_sum(dDp);
     }
-    dDp = wave_sum(dDp);
-    if (lane == 0) sRed[wave] = dDp;
-    // dS of the chunk, [p][n].
-    const uint16_t *gds = p.ws_dSp + bhc * static_cast<int64_t>(P * N);
-    for (int e = tid; e < P * (N / 8); e += 256) {
-      const int pr = e / (N / 8), nv = (e % (N / 8)) * 8;
-      *reinterpret_cast<uint4 *>(&sDS[pr * NPC + nv]) = *reinterpret_cast<const uint4 *>(gds + pr * N + nv);
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) {
+      const int e = tid + NTH * j;
+      if (SJOBS % NTH == 0 || e < SJOBS) {
+        *reinterpret_cast<u32x4 *>(&sDS[(e / (N / 8)) * NPC + (e % (N / 8)) * 8]) = R.ds[j];
+        *reinterpret_cast<u32x4 *>(&sSp[(e / (N / 8)) * NPC + (e % (N / 8)) * 8]) = R.sn[j];
+      }
     }
     __syncthreads();
+    if (k + 1 < HPW) load_head(h + 1, R);
+    // (Written after the barrier: wavefront 0 may still be reading the
+    // previous head's terms before it.)
+    if (lane == 0) sRed[wave] = dDw;
 
-    // D2^T tiles (D2^T[s][t] = x_s . dyhat_t) and the masked matrices:
-    // W[t][s], dG[t][s], M[t][s] = W dt_s (bf16) and R[t][s] (float32).
+    // <dS, S_in>: thread (p = tid / (NTH / P), a part of N / (NTH / P) states).
+    {
+      constexpr int PER = N * P / NTH;
+      const int pr = tid / (NTH / P), n0 = (tid % (NTH / P)) * PER;
+      float ph = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int code = static_cast<int>((kTiles >> (4 * (wave + 4 * u))) & 0xF);
-      const int si = code & 3, ti = code >> 2;
+      for (int j = 0; j < PER; ++j) ph = fmaf(bf2f(sDS[pr * NPC + n0 + j]), bf2f(sSp[pr * NPC + n0 + j]), ph);
+      ph = wave_sum(ph);
+      if (lane == 0) sPhi[wave] = ph;
+    }
+
+    // D2^T tiles (D2^T[s][t] = x_s . dyhat_t) and the masked matrices W[t][s],
+    // dG[t][s], M[t][s] = W dt_s (bf16); R[t][s] = dG G summed over s and over t.
+    if (wave < 12) {
+      const int kt = wave, si = gsi, ti = gti;
       floatx4 d2 = {0.f, 0.f, 0.f, 0.f};
       if (si <= ti) {
 #pragma unroll
@@ -448,202 +604,195 @@ __global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p
       const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sA[sb]);
       const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
       uint16_t wv[4], gv[4], mv[4];
+      float rr[4], rrow = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = sb + r;
         const float e = s <= t ? fast_exp(fminf(at - as4[r], 0.0f)) : 0.0f;
-        const float w = Gt[u][r] * e;
+        const float w = Gt[r] * e;
         const float dg = dt4[r] * d2[r] * e;
         wv[r] = f2bf(w);
         gv[r] = f2bf(dg);
         mv[r] = f2bf(w * dt4[r]);
-        sR[t * RP + s] = dg * Gt[u][r];
+        rr[r] = dg * Gt[r];
+        rrow += rr[r];
       }
       *reinterpret_cast<uint2 *>(&sW[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(wv);
       *reinterpret_cast<uint2 *>(&sDG[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(gv);
       if constexpr (HAS_Z) *reinterpret_cast<uint2 *>(&sM[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(mv);
+      // Sum over s of the tile: this lane's rows 4q + r here, the four lane
+      // groups q when the step's gradient is assembled.
+      sRow[kt][q][m] = rrow;
+      // Sum over t of the tile (the 16 lanes of a DPP row).
+      float cs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[r] = row_sum(rr[r]);
+      if (m < 4) sCol[kt][4 * q + m] = pick4(cs, m);
     }
     __syncthreads();
 
-    // Row and column sums of R (s <= t only): thread (u, part) takes a
-    // quarter of the row u and of the column u.
-    {
-      const int u = tid % 64, part = tid / 64;
-      float v = 0.0f;
-      for (int s = 16 * part; s < 16 * part + 16 && s <= u; ++s) v += sR[u * RP + s];
-      for (int t = max(16 * part, u); t < 16 * part + 16; ++t) v -= sR[t * RP + u];
-      sDaR[part][u] = v;
-    }
-
     // dXd = W^T dyhat + diag(e^{a_last - a}) B dS^T; dx, and x . dXd per step.
     {
-      const int pc = 16 * wave + m;
+      const int pc = 16 * pt + m, si = st;
+      floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int si = 0; si < 4; ++si) {
-        floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk == 1 || si < 2)
+          a1 = mfma(frag_t<QPp>(sW, 32 * kk, 16 * si, q, m), frag_t<PP>(sDY, 32 * kk, 16 * pt, q, m), a1);
 #pragma unroll
-        for (int kk = (si >= 2 ? 1 : 0); kk < 2; ++kk)
-          a1 = mfma(frag_t<QPp>(sW, 32 * kk, 16 * si, q, m), frag_t<PP>(sDY, 32 * kk, 16 * wave, q, m), a1);
+      for (int kk = 0; kk < NK; ++kk)
+        a2 = mfma(ld8(&sB[(16 * si + m) * NPC + 32 * kk + 8 * q]), ld8(&sDS[pc * NPC + 32 * kk + 8 * q]), a2);
+      const int sb = 16 * si + 4 * q;
+      const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[sb]);
+      const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
+      uint16_t *dxh = gdx + ((b * L + c0) * H + h) * P + pc;
+      float part[4];
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-          a2 = mfma(ld8(&sB[(16 * si + m) * NPC + 32 * kk + 8 * q]), ld8(&sDS[pc * NPC + 32 * kk + 8 * q]), a2);
-        const int sb = 16 * si + 4 * q;
-        const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[sb]);
-        const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = sb + r;
-          const float dxd = fmaf(wl4[r], a2[r], a1[r]);
-          const float xs = bf2f(sX[s * PP + pc]);
-          const float dys = bf2f(sDY[s * PP + pc]);
-          if (s < Lc) gdx[((b * L + c0 + s) * H + h) * P + pc] = f2bf(fmaf(dt4[r], dxd, Dh * dys));
-          const float part = row_sum(xs * dxd);
-          if (m == r) sDdt[wave][s] = part;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int s = sb + r;
+        const float dxd = fmaf(wl4[r], a2[r], a1[r]);
+        const float xs = bf2f(sX[s * PP + pc]);
+        const float dys = bf2f(sDY[s * PP + pc]);
+        if (s < Lc) dxh[s * HP] = f2bf(fmaf(dt4[r], dxd, Dh * dys));
+        part[r] = row_sum(xs * dxd);
       }
+      if (m < 4) sDdt[pt][sb + m] = pick4(part, m);
     }
 
     // dz = dy yhat silu'(z), yhat = M x + diag(e^a) C S_in^T + D x.
     if constexpr (HAS_Z) {
-      const int pc = 16 * wave + m;
-      const uint16_t *gsp = p.ws_Sp + bhc * static_cast<int64_t>(P * N) + pc * N;
+      const int pc = 16 * pt + m, ti = st;
       const Tdy *gdy = static_cast<const Tdy *>(p.dy);
       const uint16_t *gz = static_cast<const uint16_t *>(p.z);
       uint16_t *gdz = static_cast<uint16_t *>(p.dz);
+      floatx4 y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        floatx4 y1 = {0.f, 0.f, 0.f, 0.f}, y2 = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk == 0 || ti >= 2)
+          y1 = mfma(ld8(&sM[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<PP>(sX, 32 * kk, 16 * pt, q, m), y1);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          if (32 * kk < 16 * (ti + 1))
-            y1 = mfma(ld8(&sM[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<PP>(sX, 32 * kk, 16 * wave, q, m), y1);
+      for (int kk = 0; kk < NK; ++kk)
+        y2 = mfma(ld8(&sC[(16 * ti + m) * NPC + 32 * kk + 8 * q]), ld8(&sSp[pc * NPC + 32 * kk + 8 * q]), y2);
+      const floatx4 ea4 = *reinterpret_cast<const floatx4 *>(&sEa[16 * ti + 4 * q]);
+      const int64_t xb = ((b * L + c0) * H + h) * P + pc;
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-          y2 = mfma(ld8(&sC[(16 * ti + m) * NPC + 32 * kk + 8 * q]), ld8(gsp + 32 * kk + 8 * q), y2);
-        const floatx4 ea4 = *reinterpret_cast<const floatx4 *>(&sEa[16 * ti + 4 * q]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * ti + 4 * q + r;
-          if (t < Lc) {
-            const int64_t o = ((b * L + c0 + t) * H + h) * P + pc;
-            const float yh = fmaf(ea4[r], y2[r], y1[r]) + Dh * bf2f(sX[t * PP + pc]);
-            const float zv = bf2f(gz[o]);
-            const float sg = sigm(zv);
-            gdz[o] = f2bf(ld1(gdy, o) * yh * sg * (1.0f + zv * (1.0f - sg)));
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * q + r;
+        if (t < Lc) {
+          const float yh = fmaf(ea4[r], y2[r], y1[r]) + Dh * bf2f(sX[t * PP + pc]);
+          const float zv = bf2f(gz[xb + t * HP]);
+          const float sg = sigm(zv);
+          gdz[xb + t * HP] = f2bf(ld1(gdy, xb + t * HP) * yh * sg * (1.0f + zv * (1.0f - sg)));
         }
       }
     }
 
-    // dC += dG B + diag(e^a) dyhat S_in; and e^{a_t} (dyhat S_in)_t . C_t per step.
-    {
-      const uint16_t *gsn = p.ws_Sn + bhc * static_cast<int64_t>(N * P);
+    // dC += dG B + diag(e^a) dyhat S_in, and (dyhat S_in)_t . C_t per step.
+    // (A scheduling barrier after each tile keeps the compiler from hoisting
+    // every tile's fragment reads at once, which would exceed the registers.)
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        float rd[4] = {0.f, 0.f, 0.f, 0.f};
-        const floatx4 ea4 = *reinterpret_cast<const floatx4 *>(&sEa[16 * ti + 4 * q]);
+    for (int u = 0; u < TPW; ++u) {
+      const int ti = wave / NT + TSTEP * u;
+      const floatx4 ea4 = *reinterpret_cast<const floatx4 *>(&sEa[16 * ti + 4 * q]);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const int nt = NTW * wave + j;
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk == 0 || ti >= 2)
+          aC[u] = mfma(ld8(&sDG[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<NPC>(sB, 32 * kk, 16 * nt, q, m), aC[u]);
+      floatx4 tc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            if (32 * kk < 16 * (ti + 1))
-              aC[ti][j] = mfma(ld8(&sDG[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<NPC>(sB, 32 * kk, 16 * nt, q, m), aC[ti][j]);
-          floatx4 tmp = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 2; ++kk)
+        tc = mfma(ld8(&sDY[(16 * ti + m) * PP + 32 * kk + 8 * q]), frag_t<NPC>(sSp, 32 * kk, 16 * nt, q, m), tc);
+      float vc[4];
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-            tmp = mfma(ld8(&sDY[(16 * ti + m) * PP + 32 * kk + 8 * q]), ld8(gsn + (16 * nt + m) * P + 32 * kk + 8 * q), tmp);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * ti + 4 * q + r;
-            rd[r] = fmaf(tmp[r], bf2f(sC[t * NPC + 16 * nt + m]), rd[r]);
-            aC[ti][j][r] = fmaf(ea4[r], tmp[r], aC[ti][j][r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = row_sum(rd[r]);
-          if (m == r) sDaC[wave][16 * ti + 4 * q + r] = v * ea4[r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * q + r;
+        vc[r] = row_sum(tc[r] * bf2f(sC[t * NPC + 16 * nt + m])) * ea4[r];
+        aC[u][r] = fmaf(ea4[r], tc[r], aC[u][r]);
       }
+      if (m < 4) sDaC[nt][16 * ti + 4 * q + m] = pick4(vc, m);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // dB += dG^T C + diag(dt e^{a_last - a}) X dS; and (X dS)_s . B_s per step.
+    // dB += dG^T C + diag(dt e^{a_last - a}) X dS, and (X dS)_s . B_s per step.
 #pragma unroll
-    for (int si = 0; si < 4; ++si) {
-      float rq[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < TPW; ++u) {
+      const int si = wave / NT + TSTEP * u;
       const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[16 * si + 4 * q]);
       const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[16 * si + 4 * q]);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int nt = NTW * wave + j;
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk == 1 || si < 2)
+          aB[u] = mfma(frag_t<QPp>(sDG, 32 * kk, 16 * si, q, m), frag_t<NPC>(sC, 32 * kk, 16 * nt, q, m), aB[u]);
+      floatx4 tb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = (si >= 2 ? 1 : 0); kk < 2; ++kk)
-          aB[si][j] = mfma(frag_t<QPp>(sDG, 32 * kk, 16 * si, q, m), frag_t<NPC>(sC, 32 * kk, 16 * nt, q, m), aB[si][j]);
-        floatx4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          tmp = mfma(ld8(&sX[(16 * si + m) * PP + 32 * kk + 8 * q]), frag_t<NPC>(sDS, 32 * kk, 16 * nt, q, m), tmp);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = 16 * si + 4 * q + r;
-          const float ws = dt4[r] * wl4[r];
-          rq[r] = fmaf(tmp[r], bf2f(sB[s * NPC + 16 * nt + m]), rq[r]);
-          aB[si][j][r] = fmaf(ws, tmp[r], aB[si][j][r]);
-        }
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        tb = mfma(ld8(&sX[(16 * si + m) * PP + 32 * kk + 8 * q]), frag_t<NPC>(sDS, 32 * kk, 16 * nt, q, m), tb);
+      float vb[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = row_sum(rq[r]);
-        if (m == r) sDaB[wave][16 * si + 4 * q + r] = v * dt4[r] * wl4[r];
+        const int s = 16 * si + 4 * q + r;
+        const float ws = dt4[r] * wl4[r];
+        vb[r] = row_sum(tb[r] * bf2f(sB[s * NPC + 16 * nt + m])) * ws;
+        aB[u][r] = fmaf(ws, tb[r], aB[u][r]);
       }
+      if (m < 4) sDaB[nt][16 * si + 4 * q + m] = pick4(vb, m);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
     // da per step, its suffix sums, ddt and the dA and dD terms (wavefront 0).
     if (wave == 0) {
-      const int u = lane;
-      float da = (sDaR[0][u] + sDaR[1][u]) + (sDaR[2][u] + sDaR[3][u]);
-      da += (sDaC[0][u] + sDaC[1][u]) + (sDaC[2][u] + sDaC[3][u]);
-      const float qu = (sDaB[0][u] + sDaB[1][u]) + (sDaB[2][u] + sDaB[3][u]);
+      const int u = lane, ut = u / 16, um = u % 16;
+      float da = 0.0f, qu = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 12; ++kt) {
+        const int code = static_cast<int>((kTiles >> (4 * kt)) & 0xF);
+        if ((code >> 2) == ut) da += (sRow[kt][0][um] + sRow[kt][1][um]) + (sRow[kt][2][um] + sRow[kt][3][um]);
+        if ((code & 3) == ut) da -= sCol[kt][um];
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        da += sDaC[j][u];
+        qu += sDaB[j][u];
+      }
       da -= qu;
       const float qtot = wave_sum(qu);
-      if (u == Q - 1) da += qtot + sEa[Q - 1] * p.ws_phi[bhc];
-      // Suffix sums: rc_u = sum_{t >= u} da_t.
-      float rc = da;
+      float phi = 0.0f;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_down(rc, off, 64);
-        if (u + off < 64) rc += o;
-      }
+      for (int w = 0; w < NW; ++w) phi += sPhi[w];
+      if (u == Q - 1) da += qtot + sEa[Q - 1] * phi;
+      // Suffix sums: rc_u = sum_{t >= u} da_t.
+      const float rc = wave_suffix(da, u);
       const float dtv = sDt[u];
       float ddt = (sDdt[0][u] + sDdt[1][u]) + (sDdt[2][u] + sDdt[3][u]);
       ddt = fmaf(Ah, rc, ddt);
       if (p.dt_softplus) ddt *= 1.0f - __builtin_amdgcn_exp2f(-dtv * kLog2e);  // sigmoid(raw + bias) = 1 - e^{-dt}
-      if (u < Lc) gddt[(b * L + c0 + u) * H + h] = f2bf(ddt);
+      if (u < Lc) gddt[(b * L + c0) * H + h + u * H] = f2bf(ddt);
       const float dap = wave_sum(dtv * rc);
       if (u == 0) {
+        float dd = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) dd += sRed[w];
         p.ws_dApart[bhc] = dap;
-        p.ws_dDpart[bhc] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+        p.ws_dDpart[bhc] = dd;
       }
     }
-    __syncthreads();
+    // No barrier here: the next head writes nothing that this step reads
+    // before its own first barrier, which wavefront 0 reaches after it.
   }
 
   // The head block's dB and dC terms.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int u = 0; u < TPW; ++u) {
+    const int ti = wave / NT + TSTEP * u;
+    const int n = 16 * nt + m;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int n = 16 * (NTW * wave + j) + m;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * i + 4 * q + r;
-        if (t < Lc) {
-          const int64_t o = ((b * L + c0 + t) * HB + hb) * N + n;
-          p.ws_dBp[o] = aB[i][j][r];
-          p.ws_dCp[o] = aC[i][j][r];
-        }
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * ti + 4 * q + r;
+      if (t < Lc) {
+        const int64_t o = ((b * L + c0 + t) * HB + hb) * N + n;
+        p.ws_dBp[o] = aB[u][r];
+        p.ws_dCp[o] = aC[u][r];
       }
     }
   }
@@ -651,20 +800,22 @@ __global__ void __launch_bounds__(256) ssd_bwd_chunk_kernel(const SsdBwdParams p
 
 // ---- sums over head blocks, batch rows and chunks ------------------------------------
 __global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams p) {
+  // Thread i: four consecutive states of one (batch, step, group) for dB and dC.
   const int64_t H = p.nheads, G = p.ngroups, N = p.dstate, HB = H / p.hpw, bpg = HB / G;
-  const int64_t total = p.batch * p.seqlen * G * N;
+  const int64_t total4 = p.batch * p.seqlen * G * N / 4;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < total) {
-    const int64_t n = i % N, bt_g = i / N, g = bt_g % G, bt = bt_g / G;
-    const float *sb = p.ws_dBp + (bt * HB + g * bpg) * N + n;
-    const float *sc = p.ws_dCp + (bt * HB + g * bpg) * N + n;
-    float vb = 0.0f, vc = 0.0f;
+  if (i < total4) {
+    const int64_t e = 4 * i, n = e % N, bt_g = e / N, g = bt_g % G, bt = bt_g / G;
+    const float4 *sb = reinterpret_cast<const float4 *>(p.ws_dBp + (bt * HB + g * bpg) * N + n);
+    const float4 *sc = reinterpret_cast<const float4 *>(p.ws_dCp + (bt * HB + g * bpg) * N + n);
+    float4 vb = {0.f, 0.f, 0.f, 0.f}, vc = {0.f, 0.f, 0.f, 0.f};
     for (int64_t k = 0; k < bpg; ++k) {
-      vb += sb[k * N];
-      vc += sc[k * N];
+      const float4 xb = sb[k * N / 4], xc = sc[k * N / 4];
+      vb.x += xb.x; vb.y += xb.y; vb.z += xb.z; vb.w += xb.w;
+      vc.x += xc.x; vc.y += xc.y; vc.z += xc.z; vc.w += xc.w;
     }
-    p.dB[i] = vb;
-    p.dC[i] = vc;
+    p.dB[e] = vb.x; p.dB[e + 1] = vb.y; p.dB[e + 2] = vb.z; p.dB[e + 3] = vb.w;
+    p.dC[e] = vc.x; p.dC[e + 1] = vc.y; p.dC[e + 2] = vc.z; p.dC[e + 3] = vc.w;
   }
   if (i < H) {
     float va = 0.0f, vd = 0.0f;
@@ -686,7 +837,7 @@ hipError_t launch_all(const SsdBwdParams &p, hipStream_t stream) {
   hipLaunchKernelGGL((ssd_bwd_state_kernel<N, true, Tdy, HAS_Z>), grid_bh, dim3(256), 0, stream, p);
   if (p.nchunks > 0) {
     const dim3 grid(static_cast<uint32_t>(p.batch * p.nchunks * (p.nheads / p.hpw)));
-    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<N, Tdy, HAS_Z>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<N, Tdy, HAS_Z>), grid, dim3(64 * kBwdWaves), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -716,7 +867,7 @@ hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream
       e = dy_bf16 ? launch_z<64, uint16_t>(p, stream) : launch_z<64, float>(p, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t total = p.batch * p.seqlen * p.ngroups * p.dstate;
+  const int64_t total = p.batch * p.seqlen * p.ngroups * p.dstate / 4;
   const int64_t work = total > p.nheads ? total : p.nheads;
   if (work > 0) {
     hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>((work + 255) / 256)), dim3(256), 0, stream, p);

@@ -589,15 +589,15 @@ int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const f
 // Scalar-decay SSD backward
 // ---------------------------------------------------------------------------
 
-// Backward workspace: per (batch, head, chunk) three bf16 state matrices
-// (S_in twice, dS once) and three floats; per (batch, step, head block) the
-// float32 dB and dC terms.  Each region starts on a 256-byte boundary.
+// Backward workspace: per (batch, head, chunk) two bf16 state matrices
+// (S_in and dS) and two floats; per (batch, step, head block) the float32 dB
+// and dC terms.  Each region starts on a 256-byte boundary.
 struct SsdBwdWorkspace {
   int64_t nchunks;
   int32_t hpw;
   size_t state, per_bhc, bp;  // elements of one region
   static size_t up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
-  size_t bytes() const { return 3 * up(2 * state) + 3 * up(4 * per_bhc) + 2 * up(4 * bp); }
+  size_t bytes() const { return 2 * up(2 * state) + 2 * up(4 * per_bhc) + 2 * up(4 * bp); }
 };
 
 static SsdBwdWorkspace ssd_bwd_layout(const ssd_dims_t *d) {
@@ -694,14 +694,12 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   p.dh0 = dh0;
   uint8_t *ws = static_cast<uint8_t *>(d.workspace);
   const size_t st = SsdBwdWorkspace::up(2 * wl.state), sc = SsdBwdWorkspace::up(4 * wl.per_bhc);
-  p.ws_Sn = reinterpret_cast<uint16_t *>(ws);
-  p.ws_Sp = reinterpret_cast<uint16_t *>(ws + st);
-  p.ws_dSp = reinterpret_cast<uint16_t *>(ws + 2 * st);
-  p.ws_phi = reinterpret_cast<float *>(ws + 3 * st);
-  p.ws_dApart = reinterpret_cast<float *>(ws + 3 * st + sc);
-  p.ws_dDpart = reinterpret_cast<float *>(ws + 3 * st + 2 * sc);
-  p.ws_dBp = reinterpret_cast<float *>(ws + 3 * st + 3 * sc);
-  p.ws_dCp = reinterpret_cast<float *>(ws + 3 * st + 3 * sc + SsdBwdWorkspace::up(4 * wl.bp));
+  p.ws_Sp = reinterpret_cast<uint16_t *>(ws);
+  p.ws_dSp = reinterpret_cast<uint16_t *>(ws + st);
+  p.ws_dApart = reinterpret_cast<float *>(ws + 2 * st);
+  p.ws_dDpart = reinterpret_cast<float *>(ws + 2 * st + sc);
+  p.ws_dBp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc);
+  p.ws_dCp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + SsdBwdWorkspace::up(4 * wl.bp));
   p.nchunks = wl.nchunks;
   p.hpw = wl.hpw;
   p.batch = d.batch;

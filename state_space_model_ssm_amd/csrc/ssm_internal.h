@@ -110,13 +110,12 @@ struct SsdBwdParams {
   int32_t dt_softplus;
   void *dx, *ddt, *dz;                // bf16; dz only with z
   float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
-  // Workspace, per (batch, head, chunk): the chunk's entering state S_in as
-  // [dstate][headdim] (ws_Sn) and, with a gate, [headdim][dstate] (ws_Sp),
-  // the gradient of its leaving state as [headdim][dstate] (ws_dSp), all
-  // bf16; <dS, S_in>, the dA and dD terms (float32).  Per (batch, step, head
-  // block), the dB and dC terms [batch][seqlen][nheads / hpw][dstate].
-  uint16_t *ws_Sn, *ws_Sp, *ws_dSp;
-  float *ws_phi, *ws_dApart, *ws_dDpart, *ws_dBp, *ws_dCp;
+  // Workspace, per (batch, head, chunk): the chunk's entering state S_in
+  // (ws_Sp) and the gradient of its leaving state (ws_dSp), both
+  // [headdim][dstate] bf16; the dA and dD terms (float32).  Per (batch, step,
+  // head block), the dB and dC terms [batch][seqlen][nheads / hpw][dstate].
+  uint16_t *ws_Sp, *ws_dSp;
+  float *ws_dApart, *ws_dDpart, *ws_dBp, *ws_dCp;
   int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
   int32_t hpw;                        // heads per chunk-kernel workgroup
 };
