@@ -22,10 +22,9 @@
 // (dY here is dyhat = dy silu(z); dz = dy yhat silu'(z) with yhat = Y + D x.)
 //
 // Kernels:
-//   * state pass, forward: per (batch, head), the chunk states S_in from h0
-//     (the forward's state update, MFMA over the chunk's steps), stored bf16;
-//   * state pass, reverse: per (batch, head), dS of every chunk from dh_last,
-//     stored bf16, and dh0;
+//   * state passes (one launch): per (batch, head), the chunk states S_in
+//     from h0 (the forward's state update, MFMA over the chunk's steps) and,
+//     independently, dS of every chunk from dh_last (and dh0), stored bf16;
 //   * chunk kernel: every (batch, chunk, block of heads) at once: the products
 //     above on matrix cores (v_mfma_f32_16x16x32_bf16), dx, ddt, dz directly,
 //     dB and dC summed over the block's heads in registers, dA and dD terms;
@@ -210,23 +209,31 @@ __device__ __forceinline__ void chunk_steps(const SsdBwdParams &p, int64_t b, in
 // State tiles as in the forward: rows n = 16 ni + 4q + r, column p = 16 w + i.
 // The next chunk's inputs are loaded into registers while the current one
 // is computed.
+template <int N>
+struct StateSmem {
+  uint16_t U[Q * (N + 24)];
+  uint16_t V[Q * PP];
+  float om[Q];
+  float dec;
+};
+
 template <int N, bool REV, typename Tdy, bool HAS_Z>
-__global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p) {
+__device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, StateSmem<N> &sm) {
   constexpr int NT = N / 16, NPC = N + 24;
   constexpr int UJ = Q * (N / 8) / 256;  // U jobs (8 elements) per thread
   constexpr int VJ = Q * (P / 8) / 256;  // V jobs per thread
   constexpr int DW = sizeof(Tdy) / 2;    // dy: 16-byte words per 8 elements
-  __shared__ __attribute__((aligned(16))) uint16_t sU[Q * NPC];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[Q * PP];
-  __shared__ __attribute__((aligned(16))) float sOm[Q];
-  __shared__ float sDec;
+  uint16_t *const sU = sm.U;
+  uint16_t *const sV = sm.V;
+  float *const sOm = sm.om;
+  float &sDec = sm.dec;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, q = lane / 16, m = lane % 16;
   const int pcol = 16 * wave + m;
   const int64_t H = p.nheads, L = p.seqlen, G = p.ngroups;
-  const int64_t bh = blockIdx.x, b = bh / H, h = bh % H, g = h / (H / G);
+  const int64_t b = bh / H, h = bh % H, g = h / (H / G);
   const int64_t nC = p.nchunks;
   const float Ah = p.A[h];
   const float bias = (p.dt_softplus && p.dt_bias) ? p.dt_bias[h] : 0.0f;
@@ -248,28 +255,33 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
   };
   // Rows past the end are loaded from the last valid step (branch-free) and
   // zeroed when staged.
+  // Global addresses: a uniform base at the chunk's first step plus 32-bit
+  // lane offsets (the host keeps nheads * headdim and ngroups * dstate below 2^25).
+  const int GN = static_cast<int>(G * N), HP = static_cast<int>(H * P), Hi = static_cast<int>(H);
   auto load = [&](int64_t c, Regs &R) __attribute__((always_inline)) {
     const int64_t c0 = c * Q;
     const int last = static_cast<int>(min(static_cast<int64_t>(Q), L - c0)) - 1;
+    const uint16_t *ub = gU + ((b * L + c0) * G + g) * N;
+    const int64_t vb = ((b * L + c0) * H + h) * P;
 #pragma unroll
     for (int k = 0; k < UJ; ++k) {
       const int e = tid + 256 * k, t = min(e / (N / 8), last), nv = (e % (N / 8)) * 8;
-      R.u[k] = *reinterpret_cast<const uint4 *>(gU + ((b * L + c0 + t) * G + g) * N + nv);
+      R.u[k] = *reinterpret_cast<const uint4 *>(ub + t * GN + nv);
     }
 #pragma unroll
     for (int k = 0; k < VJ; ++k) {
       const int e = tid + 256 * k, t = min(e / (P / 8), last), pv = (e % (P / 8)) * 8;
-      const int64_t o = ((b * L + c0 + t) * H + h) * P + pv;
+      const int o = t * HP + pv;
       if constexpr (!REV) {
-        R.v[k][0] = *reinterpret_cast<const uint4 *>(gx + o);
+        R.v[k][0] = *reinterpret_cast<const uint4 *>(gx + vb + o);
       } else {
-        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const Tdy *>(p.dy) + o);
+        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const Tdy *>(p.dy) + vb + o);
 #pragma unroll
         for (int w = 0; w < DW; ++w) R.v[k][w] = src[w];
-        if constexpr (HAS_Z) R.z[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.z) + o);
+        if constexpr (HAS_Z) R.z[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.z) + vb + o);
       }
     }
-    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, last)) * H + h];
+    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0) * H + h + min(lane, last) * Hi];
   };
   auto stage = [&](int64_t c, const Regs &R) __attribute__((always_inline)) {
     const int Lc = static_cast<int>(min(static_cast<int64_t>(Q), L - c * Q));
@@ -329,14 +341,22 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
     __syncthreads();
     if (ci + 1 < nC) load(REV ? c - 1 : c + 1, R);
 
-    // The state of this chunk before its update, [p][n]: S_in (forward) or dS (reverse).
+    // The state of this chunk before its update (S_in forward, dS reverse),
+    // in the lane-blocked layout: 16-byte piece (wave, j, lane) holds tiles
+    // 2j and 2j + 1 of the lane, so every store writes 1 KB of a wavefront
+    // contiguously.
     const int64_t wb = (bh * nC + c) * static_cast<int64_t>(N * P);
-    uint16_t *wdst = (REV ? p.ws_dSp : p.ws_Sp) + wb + pcol * N + 4 * q;
+    uint16_t *wdst = (REV ? p.ws_dSp : p.ws_Sp) + wb + 8 * (wave * (NT / 2) * 64 + lane);
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      const uint32_t lo = static_cast<uint32_t>(f2bf(S[ni][0])) | (static_cast<uint32_t>(f2bf(S[ni][1])) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f2bf(S[ni][2])) | (static_cast<uint32_t>(f2bf(S[ni][3])) << 16);
-      *reinterpret_cast<uint2 *>(wdst + 16 * ni) = uint2{lo, hi};
+    for (int j = 0; j < NT / 2; ++j) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const floatx4 t = S[2 * j + e];
+        v[2 * e] = static_cast<uint32_t>(f2bf(t[0])) | (static_cast<uint32_t>(f2bf(t[1])) << 16);
+        v[2 * e + 1] = static_cast<uint32_t>(f2bf(t[2])) | (static_cast<uint32_t>(f2bf(t[3])) << 16);
+      }
+      *reinterpret_cast<u32x4 *>(wdst + 8 * 64 * j) = v;
     }
 
     // S <- e^{a_last} S + U^T diag(omega) V  (K = the chunk's steps).
@@ -368,6 +388,21 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
   }
 }
 
+// Both state passes in one launch (they are independent): even workgroups
+// run the forward pass of (batch, head) blockIdx / 2, odd ones the reverse.
+// FWD = false launches the reverse passes alone (an empty sequence).
+template <int N, typename Tdy, bool HAS_Z, bool FWD>
+__global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p) {
+  __shared__ __attribute__((aligned(16))) StateSmem<N> sm;
+  if (!FWD) {
+    state_pass<N, true, Tdy, HAS_Z>(p, blockIdx.x, sm);
+  } else if (blockIdx.x % 2 == 0) {
+    state_pass<N, false, Tdy, HAS_Z>(p, blockIdx.x / 2, sm);
+  } else {
+    state_pass<N, true, Tdy, HAS_Z>(p, blockIdx.x / 2, sm);
+  }
+}
+
 // ---- chunk kernel ---------------------------------------------------------------
 // Workgroup: one (batch, chunk) and HPW heads of one group, 16 wavefronts
 // (four per SIMD: the LDS holds one workgroup per CU).
@@ -393,6 +428,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
   __shared__ __attribute__((aligned(16))) uint16_t sDG[Q * QPp];
   __shared__ __attribute__((aligned(16))) uint16_t sM[HAS_Z ? Q * QPp : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sDS[P * NPC];   // dS[p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sDX[Q * PP];    // dx[t][p], stored as rows
   __shared__ __attribute__((aligned(16))) uint16_t sSp[P * NPC];   // S_in[p][n]
   __shared__ __attribute__((aligned(16))) float sA[Q];
   __shared__ __attribute__((aligned(16))) float sEa[Q];
@@ -455,8 +491,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     for (int k = 0; k < SJ; ++k) {
       const int e = tid + NTH * k;
       if (SJOBS % NTH == 0 || e < SJOBS) {
-        R.ds[k] = *reinterpret_cast<const u32x4 *>(gds + (e / (N / 8)) * N + (e % (N / 8)) * 8);
-        R.sn[k] = *reinterpret_cast<const u32x4 *>(gsp + (e / (N / 8)) * N + (e % (N / 8)) * 8);
+        R.ds[k] = *reinterpret_cast<const u32x4 *>(gds + 8 * e);
+        R.sn[k] = *reinterpret_cast<const u32x4 *>(gsp + 8 * e);
       }
     }
     R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, Lc - 1)) * H + h];
@@ -568,8 +604,14 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     for (int j = 0; j < SJ; ++j) {
       const int e = tid + NTH * j;
       if (SJOBS % NTH == 0 || e < SJOBS) {
-        *reinterpret_cast<u32x4 *>(&sDS[(e / (N / 8)) * NPC + (e % (N / 8)) * 8]) = R.ds[j];
-        *reinterpret_cast<u32x4 *>(&sSp[(e / (N / 8)) * NPC + (e % (N / 8)) * 8]) = R.sn[j];
+        // Piece e of the lane-blocked layout: wave w, tile pair jj, lane (qq, mm)
+        // holds rows n = 16 (2 jj + e') + 4 qq + 0..3 of column p = 16 w + mm.
+        const int el = e % 64, wj = e / 64, w = wj / (N / 32), jj = wj % (N / 32);
+        const int o = (16 * w + el % 16) * NPC + 32 * jj + 4 * (el / 16);
+        *reinterpret_cast<uint2 *>(&sDS[o]) = uint2{R.ds[j][0], R.ds[j][1]};
+        *reinterpret_cast<uint2 *>(&sDS[o + 16]) = uint2{R.ds[j][2], R.ds[j][3]};
+        *reinterpret_cast<uint2 *>(&sSp[o]) = uint2{R.sn[j][0], R.sn[j][1]};
+        *reinterpret_cast<uint2 *>(&sSp[o + 16]) = uint2{R.sn[j][2], R.sn[j][3]};
       }
     }
     __syncthreads();
@@ -645,7 +687,6 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       const int sb = 16 * si + 4 * q;
       const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[sb]);
       const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
-      uint16_t *dxh = gdx + ((b * L + c0) * H + h) * P + pc;
       float part[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -653,7 +694,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
         const float dxd = fmaf(wl4[r], a2[r], a1[r]);
         const float xs = bf2f(sX[s * PP + pc]);
         const float dys = bf2f(sDY[s * PP + pc]);
-        if (s < Lc) dxh[s * HP] = f2bf(fmaf(dt4[r], dxd, Dh * dys));
+        sDX[s * PP + pc] = f2bf(fmaf(dt4[r], dxd, Dh * dys));
         part[r] = row_sum(xs * dxd);
       }
       if (m < 4) sDdt[pt][sb + m] = pick4(part, m);
@@ -740,6 +781,14 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     }
     __syncthreads();
 
+    // dx rows of the head's chunk as 16-byte vectors.
+    if (xjob) {
+      const int t = tid / (P / 8), pv = (tid % (P / 8)) * 8;
+      if (t < Lc)
+        *reinterpret_cast<uint4 *>(gdx + ((b * L + c0) * H + h) * P + t * HP + pv) =
+            *reinterpret_cast<const uint4 *>(&sDX[t * PP + pv]);
+    }
+
     // da per step, its suffix sums, ddt and the dA and dD terms (wavefront 0).
     if (wave == 0) {
       const int u = lane, ut = u / 16, um = u % 16;
@@ -799,7 +848,41 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
 }
 
 // ---- sums over head blocks, batch rows and chunks ------------------------------------
-__global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams p) {
+// dA and dD: one workgroup per head sums its (batch, chunk) terms, thread k
+// taking the terms k, k + 256, ... and a fixed-order tree joining the threads.
+__device__ __forceinline__ void reduce_head(const SsdBwdParams &p, int64_t h) {
+  __shared__ float sa[256], sd[256];
+  const int64_t H = p.nheads, K = p.batch * p.nchunks;
+  const int tid = threadIdx.x;
+  float va = 0.0f, vd = 0.0f;
+  for (int64_t k = tid; k < K; k += 256) {
+    const int64_t bb = k / p.nchunks, c = k % p.nchunks;
+    va += p.ws_dApart[(bb * H + h) * p.nchunks + c];
+    vd += p.ws_dDpart[(bb * H + h) * p.nchunks + c];
+  }
+  sa[tid] = va;
+  sd[tid] = vd;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) {
+      sa[tid] += sa[tid + w];
+      sd[tid] += sd[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.dA[h] = sa[0];
+    if (p.dD) p.dD[h] = sd[0];
+  }
+}
+
+// Workgroups below `nbc` sum the dB and dC terms; the next nheads workgroups
+// sum dA and dD (reduce_head).
+__global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams p, int64_t nbc) {
+  if (static_cast<int64_t>(blockIdx.x) >= nbc) {
+    reduce_head(p, blockIdx.x - nbc);
+    return;
+  }
   // Thread i: four consecutive states of one (batch, step, group) for dB and dC.
   const int64_t H = p.nheads, G = p.ngroups, N = p.dstate, HB = H / p.hpw, bpg = HB / G;
   const int64_t total4 = p.batch * p.seqlen * G * N / 4;
@@ -809,32 +892,38 @@ __global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams 
     const float4 *sb = reinterpret_cast<const float4 *>(p.ws_dBp + (bt * HB + g * bpg) * N + n);
     const float4 *sc = reinterpret_cast<const float4 *>(p.ws_dCp + (bt * HB + g * bpg) * N + n);
     float4 vb = {0.f, 0.f, 0.f, 0.f}, vc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t k = 0; k < bpg; ++k) {
-      const float4 xb = sb[k * N / 4], xc = sc[k * N / 4];
-      vb.x += xb.x; vb.y += xb.y; vb.z += xb.z; vb.w += xb.w;
-      vc.x += xc.x; vc.y += xc.y; vc.z += xc.z; vc.w += xc.w;
-    }
-    p.dB[e] = vb.x; p.dB[e + 1] = vb.y; p.dB[e + 2] = vb.z; p.dB[e + 3] = vb.w;
-    p.dC[e] = vc.x; p.dC[e + 1] = vc.y; p.dC[e + 2] = vc.z; p.dC[e + 3] = vc.w;
-  }
-  if (i < H) {
-    float va = 0.0f, vd = 0.0f;
-    for (int64_t bb = 0; bb < p.batch; ++bb)
-      for (int64_t c = 0; c < p.nchunks; ++c) {
-        va += p.ws_dApart[(bb * H + i) * p.nchunks + c];
-        vd += p.ws_dDpart[(bb * H + i) * p.nchunks + c];
+    // Eight head blocks at a time: all their loads in flight together.
+    for (int64_t k0 = 0; k0 < bpg; k0 += 8) {
+      float4 xb[8], xc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = k0 + j < bpg;
+        xb[j] = in ? sb[(k0 + j) * N / 4] : float4{0.f, 0.f, 0.f, 0.f};
+        xc[j] = in ? sc[(k0 + j) * N / 4] : float4{0.f, 0.f, 0.f, 0.f};
       }
-    p.dA[i] = va;
-    if (p.dD) p.dD[i] = vd;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vb.x += xb[j].x; vb.y += xb[j].y; vb.z += xb[j].z; vb.w += xb[j].w;
+        vc.x += xc[j].x; vc.y += xc[j].y; vc.z += xc[j].z; vc.w += xc[j].w;
+      }
+    }
+    if (((reinterpret_cast<uintptr_t>(p.dB) | reinterpret_cast<uintptr_t>(p.dC)) & 15) == 0) {
+      *reinterpret_cast<float4 *>(p.dB + e) = vb;
+      *reinterpret_cast<float4 *>(p.dC + e) = vc;
+    } else {
+      p.dB[e] = vb.x; p.dB[e + 1] = vb.y; p.dB[e + 2] = vb.z; p.dB[e + 3] = vb.w;
+      p.dC[e] = vc.x; p.dC[e + 1] = vc.y; p.dC[e + 2] = vc.z; p.dC[e + 3] = vc.w;
+    }
   }
 }
 
 template <int N, typename Tdy, bool HAS_Z>
 hipError_t launch_all(const SsdBwdParams &p, hipStream_t stream) {
-  const dim3 grid_bh(static_cast<uint32_t>(p.batch * p.nheads));
+  const uint32_t nbh = static_cast<uint32_t>(p.batch * p.nheads);
   if (p.nchunks > 0)
-    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, false, Tdy, HAS_Z>), grid_bh, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((ssd_bwd_state_kernel<N, true, Tdy, HAS_Z>), grid_bh, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, true>), dim3(2 * nbh), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, false>), dim3(nbh), dim3(256), 0, stream, p);
   if (p.nchunks > 0) {
     const dim3 grid(static_cast<uint32_t>(p.batch * p.nchunks * (p.nheads / p.hpw)));
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<N, Tdy, HAS_Z>), grid, dim3(64 * kBwdWaves), 0, stream, p);
@@ -859,21 +948,18 @@ int ssd_bwd_heads_per_block(int64_t batch, int64_t seqlen, int64_t nheads, int64
 }
 
 hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream) {
-  hipError_t e = hipSuccess;
   if (p.batch * p.nheads > 0) {
+    hipError_t e;
     if (p.dstate == 128)
       e = dy_bf16 ? launch_z<128, uint16_t>(p, stream) : launch_z<128, float>(p, stream);
     else
       e = dy_bf16 ? launch_z<64, uint16_t>(p, stream) : launch_z<64, float>(p, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t total = p.batch * p.seqlen * p.ngroups * p.dstate / 4;
-  const int64_t work = total > p.nheads ? total : p.nheads;
-  if (work > 0) {
-    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>((work + 255) / 256)), dim3(256), 0, stream, p);
-    e = hipGetLastError();
-  }
-  return e;
+  const int64_t nbc = (p.batch * p.seqlen * p.ngroups * p.dstate / 4 + 255) / 256;
+  if (nbc + p.nheads > 0)
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>(nbc + p.nheads)), dim3(256), 0, stream, p, nbc);
+  return hipGetLastError();
 }
 
 }  // namespace ssm

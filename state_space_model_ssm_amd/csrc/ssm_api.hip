@@ -658,6 +658,9 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   }
   if (n_bc / 256 >= kMaxGridX) return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * ngroups * dstate exceeds the grid limit");
   const SsdBwdWorkspace wl = ssd_bwd_layout(&d);
+  if (d.batch * d.nheads > kMaxGridX / 2 ||
+      (d.batch > 0 && wl.nchunks > 0 && d.nheads / wl.hpw > kMaxGridX / d.batch / wl.nchunks))
+    return fail(SSM_ERR_UNSUPPORTED, "batch * nheads * chunks exceeds the grid limit");
   const size_t need = wl.bytes();
   if (need > 0) {
     if (!d.workspace || d.workspace_bytes < need)

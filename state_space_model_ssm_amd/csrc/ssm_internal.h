@@ -111,8 +111,9 @@ struct SsdBwdParams {
   void *dx, *ddt, *dz;                // bf16; dz only with z
   float *dA, *dB, *dC, *dD, *dh0;     // float32; dD only with D; dh0 nullable
   // Workspace, per (batch, head, chunk): the chunk's entering state S_in
-  // (ws_Sp) and the gradient of its leaving state (ws_dSp), both
-  // [headdim][dstate] bf16; the dA and dD terms (float32).  Per (batch, step,
+  // (ws_Sp) and the gradient of its leaving state (ws_dSp), headdim x dstate
+  // bf16 in the state passes' lane-blocked order; the dA and dD terms
+  // (float32).  Per (batch, step,
   // head block), the dB and dC terms [batch][seqlen][nheads / hpw][dstate].
   uint16_t *ws_Sp, *ws_dSp;
   float *ws_dApart, *ws_dDpart, *ws_dBp, *ws_dCp;

@@ -1148,3 +1148,45 @@ def test_ssd_backward_named_workload_full_size():
     dhl = make_state((s.batch, s.nheads, s.headdim, s.dstate), seed=8401, scale=0.5)
     g = _ssd_bwd_pair(inp, dy, None, dhl)
     _check_ssd_bwd(g, ref_ssd_bwd_rows(inp, dy, dhl), "ssd_32x256_h32p64n128_bf16 backward")
+
+
+# The chunk kernel sums dB and dC over blocks of 2, 4 or 8 heads of a group
+# when the grid has enough workgroups (batch * chunks * nheads / hpw >= 1024).
+SSD_BWD_HEAD_BLOCK_CASES = [
+    # (batch, L, H, N, G, has_z, h0 and dh_last, dy dtype, dt_softplus)    heads per block
+    (16, 130, 64, 128, 2, True, True, "bf16", False),    # 2, groups, ragged last chunk
+    (16, 100, 64, 64, 4, False, True, "f32", True),      # 2, dstate 64, raw dt with bias
+    (128, 64, 64, 128, 1, True, True, "bf16", False),    # 8, one chunk
+    (128, 64, 32, 64, 1, False, False, "f32", False),    # 4, dstate 64
+]
+
+
+@pytest.mark.parametrize("case", SSD_BWD_HEAD_BLOCK_CASES, ids=lambda c: "b{}l{}h{}n{}g{}_z{}_h0{}_{}_sp{}".format(*c))
+def test_ssd_backward_head_blocks(case):
+    batch, L, H, N, G, has_z, with_h, dyt, softplus = case
+    seed = 8500 + zlib.crc32(repr(case).encode()) % 1000
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip="normal", seed=seed)
+    inp = make_ssd_inputs(s)
+    h0 = make_state((batch, H, 64, N), seed=seed + 1, scale=0.5) if with_h else None
+    dhl = make_state((batch, H, 64, N), seed=seed + 2, scale=0.5) if with_h else None
+    dy = make_state((batch, L, H, 64), seed=seed + 3).to(DT[dyt])
+    kw = {}
+    if softplus:
+        raw, bias = make_raw_step((batch, L, H), H, seed + 4, "bf16")
+        inp = dict(inp, dt=raw)
+        kw = dict(dt_softplus=True, dt_bias=bias)
+    g = _ssd_bwd_pair(inp, dy, h0, dhl, **kw)
+
+    def one(b):
+        r = {k: (None if v is None else (v[b:b + 1] if k in ("x", "dt", "B", "C", "z") else v)) for k, v in inp.items()}
+        return oracle.ssd_bwd(r["x"], r["dt"], r["A"], r["B"], r["C"], r["D"], r["z"],
+                              None if h0 is None else h0[b:b + 1], dy[b:b + 1],
+                              None if dhl is None else dhl[b:b + 1], **kw)
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        parts = list(ex.map(one, range(batch)))
+    ref = {k: (None if parts[0][k] is None else np.concatenate([q[k] for q in parts]))
+           for k in ("dx", "ddt", "dB", "dC", "dz", "dh0")}
+    for k in ("dA", "dD"):
+        ref[k] = None if parts[0][k] is None else np.sum([q[k] for q in parts], axis=0)
+    _check_ssd_bwd(g, ref, "head blocks " + repr(case[:5]))
