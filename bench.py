@@ -80,6 +80,22 @@ def scan_alu_slots_per_element(N: int, has_z: bool, has_d: bool) -> float:
     return full + TRANS_SLOTS * trans
 
 
+def scan_bwd_alu_slots_per_element(N: int, has_z: bool, has_d: bool) -> float:
+    """VALU slots the selective-scan backward needs per element.
+
+    Per state and step: the forward rebuilt from the checkpoint (dt*A, exp,
+    (dt u) B, the update: 3 full + 1 transcendental), the readout C h for the
+    gate's yhat (1), the adjoint lam = a lam + dyhat C (2), and the sums it
+    feeds: du (lam B, 1), ddelta (lam (A (h - bx) + B u): 4), dA (lam dt (h - bx):
+    2), dB (lam dt u, 1) and dC (dyhat h, 1).  Per element: dt*u, the gate and
+    its derivative (exp, rcp and ~6 mul/add), the D terms (2), du and ddelta
+    scaling (2).
+    """
+    full = 16 * N + 2 + (6 if has_z else 0) + (2 if has_d else 0) + 2
+    trans = N + (2 if has_z else 0)
+    return full + TRANS_SLOTS * trans
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,8 +329,11 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
         ws = torch.empty(max(ssm.scan_bwd_workspace_size(dims), 1), dtype=torch.uint8, device=dev)
         ms, _ = time_calls(lambda: ssm.scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"],
                                                 dy=dy, workspace=ws, stream=stream), 5, 1)
+        # ALU model: the backward's own VALU work at the fp32 VALU peak.
+        t_alu = scan_bwd_alu_slots_per_element(w.dstate, w.has_z, w.dskip != "none") * w.elements / VALU_SLOTS_PER_S
         out["backward_" + name] = {"ms": round(ms, 4), "Gelem/s": round(w.elements / ms / 1e6, 2),
-                                   "workspace_MB": round(ws.numel() / 1e6, 1)}
+                                   "workspace_MB": round(ws.numel() / 1e6, 1),
+                                   "alu_model_us": round(t_alu * 1e6, 1), "alu_frac": round(t_alu * 1e3 / ms, 4)}
         del d, dy, ws
     w = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
     d = {k: (None if v is None else v.to(dev)) for k, v in make_ssd_inputs(w).items()}
@@ -336,8 +355,19 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
     ms, _ = time_calls(lambda: ssm.ssd_bwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy,
                                            workspace=ws, stream=stream), 20, 3)
     nbytes = (2 * d["x"].numel() + 2 * d["dt"].numel()) * 2 + 2 * d["B"].numel() * (2 + 4) + dy.numel() * 2
+    # MFMA model: per (batch, head, 64-step chunk) the two state updates
+    # (2 P N Q each), the shared B C^T tile (2 Q Q N over the 4 heads of a
+    # block), dyhat X^T (2 Q Q P), W^T dyhat (half of 2 Q Q P: causal), the
+    # three products over headdim or dstate with S_in and dS (2 Q N P each)
+    # and dG B, dG^T C (half of 2 Q Q N each): about 7.3 MFLOP for headdim
+    # 64, dstate 128, at the bf16 dense peak (without a gate).
+    Q, P, N = 64, w.headdim, w.dstate
+    chunks = w.batch * w.nheads * ((w.seqlen + Q - 1) // Q)
+    flops = chunks * 2.0 * (2 * P * N * Q + Q * Q * N / 4 + Q * Q * P + Q * Q * P / 2 + 3 * Q * N * P + Q * Q * N)
     out["ssd_backward_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
                                                   "hbm_GB/s_min_bytes": round(nbytes / ms / 1e6, 1),
+                                                  "mfma_model_us": round(flops / (BF16_MFMA_TFLOPS * 1e12) * 1e6, 2),
+                                                  "min_bytes_model_us": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                                                   "workspace_MB": round(ws.numel() / 1e6, 1)}
     del dy, ws
     # The rotary step on the same shapes (one set of angles for all heads),
