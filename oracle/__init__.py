@@ -46,6 +46,8 @@ class Oracle:
         lib.oracle_ssd_f64.restype = ctypes.c_int
         lib.oracle_ssd_bwd_f64.argtypes = [i64] * 6 + [dp] * 18
         lib.oracle_ssd_bwd_f64.restype = ctypes.c_int
+        lib.oracle_ssd_trap_bwd_f64.argtypes = [i64] * 6 + [dp] * 24
+        lib.oracle_ssd_trap_bwd_f64.restype = ctypes.c_int
         lib.oracle_softplus_f64.argtypes = [i64] * 3 + [dp] * 3
         lib.oracle_softplus_f64.restype = None
         lib.oracle_softplus_grad_f64.argtypes = [i64] * 3 + [dp] * 4
@@ -195,6 +197,36 @@ class Oracle:
             raise ValueError("oracle_ssd_bwd_f64 rejected the shapes")
         return g
 
+    def ssd_trap_bwd(self, x, dt, lam, A, B, C, D=None, z=None, h0=None, x_prev=None, B_prev=None, dy=None,
+                     dh_last=None):
+        """Gradients of the trapezoidal SSD in float64 for upstream gradients
+        dy (batch, L, H, P) and dh_last (batch, H, P, N; None = zero).  Returns a
+        dict: dx, ddt, dlam, dA, dB, dC, dh0, and dD / dz / dx_prev / dB_prev
+        (None when D / z / the previous token are None)."""
+        x, dt, lam, A, B, C, D, z, h0, dy, dh_last = map(f64, (x, dt, lam, A, B, C, D, z, h0, dy, dh_last))
+        x_prev, B_prev = f64(x_prev), f64(B_prev)
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        assert dt.shape == (batch, L, H) and lam.shape == dt.shape and A.shape == (H,)
+        assert B.shape == (batch, L, G, N) and C.shape == B.shape and dy.shape == x.shape
+        assert h0 is None or h0.shape == (batch, H, P, N)
+        assert dh_last is None or dh_last.shape == (batch, H, P, N)
+        assert (x_prev is None) == (B_prev is None)
+        g = {"dx": np.zeros_like(x), "ddt": np.zeros_like(dt), "dlam": np.zeros_like(dt), "dA": np.zeros(H),
+             "dB": np.zeros_like(B), "dC": np.zeros_like(C), "dD": None if D is None else np.zeros(H),
+             "dz": None if z is None else np.zeros_like(x), "dh0": np.zeros((batch, H, P, N)),
+             "dx_prev": None if x_prev is None else np.zeros((batch, H, P)),
+             "dB_prev": None if B_prev is None else np.zeros((batch, G, N))}
+        rc = self.lib.oracle_ssd_trap_bwd_f64(batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B),
+                                              _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(x_prev), _ptr(B_prev),
+                                              _ptr(dy), _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]),
+                                              _ptr(g["dlam"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                              _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(g["dx_prev"]),
+                                              _ptr(g["dB_prev"]))
+        if rc != 0:
+            raise ValueError("oracle_ssd_trap_bwd_f64 rejected the shapes")
+        return g
+
     def ssd(self, x, dt, A, B, C, D=None, z=None, h0=None):
         """Scalar-decay SSD recurrence in float64. Returns (y, h_last).
 
@@ -300,6 +332,23 @@ def ssd_bwd(x, dt, A, B, C, D=None, z=None, h0=None, dy=None, dh_last=None, dt_s
     step = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
     g = o.ssd_bwd(x, step, A, B, C, D, z, h0, dy, dh_last)
     g["ddt"] = o.softplus_grad(dt, dt_bias, 1, g["ddt"]).reshape(step.shape)
+    return g
+
+
+def ssd_trap_bwd(x, dt, lam, A, B, C, D=None, z=None, h0=None, x_prev=None, B_prev=None, dy=None, dh_last=None,
+                 dt_softplus=False, dt_bias=None, lam_sigmoid=False):
+    """Trapezoidal SSD gradients in float64 with the default build; see
+    ``Oracle.ssd_trap_bwd``.  With dt_softplus / lam_sigmoid the forward maps
+    the raw dt and lam, and ddt / dlam are the gradients of the raw values
+    (times sigmoid(dt + dt_bias[h]), and sigmoid'(lam) = s (1 - s))."""
+    o = _load()
+    step = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape) if dt_softplus else dt
+    weight = o.sigmoid(lam).reshape(f64(lam).shape) if lam_sigmoid else lam
+    g = o.ssd_trap_bwd(x, step, weight, A, B, C, D, z, h0, x_prev, B_prev, dy, dh_last)
+    if dt_softplus:
+        g["ddt"] = o.softplus_grad(dt, dt_bias, 1, g["ddt"]).reshape(step.shape)
+    if lam_sigmoid:
+        g["dlam"] = g["dlam"] * weight * (1.0 - weight)
     return g
 
 

@@ -443,6 +443,166 @@ int oracle_ssd_trap_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t h
 }
 
 /*
+ * Gradients of the trapezoidal SSD above (reverse mode), float64.
+ *
+ * Upstream gradients dy on y and dh_last (nullable = zero) on h_last; returns
+ * dx, dz (dz only with z), ddt, dlam (batch, seqlen, nheads), dA, dD (dD only
+ * with Dskip), dB, dC, dh0, and with the token before the sequence dx_prev
+ * (batch, nheads, headdim) and dB_prev (batch, ngroups, dstate) (NULL without
+ * it).  As for oracle_ssd_bwd_f64, "Mamba-3 NKI Kernels for AWS Neuron",
+ * section "Correctness", reports backward parity but prints no formulas: this
+ * is the chain rule on the three-term recurrence of oracle_ssd_trap_f64 (its
+ * Eq. 9 with alpha, beta, gamma of Phase 0), walked backwards.  With
+ * Q_t = x_t B_t^T (P x N), P_{t-1} = Q_{t-1} (P_{-1} = x_prev B_prev^T or 0) and
+ * Lam_t = dL/dH_t:
+ *   Lam_t  = dyhat_t C_t^T + alpha_{t+1} Lam_{t+1}        (Lam_{L-1} also receives dh_last)
+ *   dQ_t   = gamma_t Lam_t + beta_{t+1} Lam_{t+1}          (beta_L = 0)
+ *   dx_t   = dQ_t B_t + D dyhat_t;   dB_t += dQ_t^T x_t;   dC_t += H_t^T dyhat_t
+ *   dalpha_t = <Lam_t, H_{t-1}>,  dbeta_t = <Lam_t, P_{t-1}>,  dgamma_t = <Lam_t, Q_t>
+ * and through alpha = exp(dt A), beta = dt (1 - lam) alpha, gamma = lam dt:
+ *   ddt_t  = A alpha_t dalpha_t + (1 - lam_t) alpha_t (1 + dt_t A) dbeta_t + lam_t dgamma_t
+ *   dlam_t = dt_t (dgamma_t - alpha_t dbeta_t),   dA += dt_t (alpha_t dalpha_t + beta_t dbeta_t)
+ *   dh0 = alpha_0 Lam_0;   dP_{-1} = beta_0 Lam_0 gives dx_prev = dP_{-1} B_prev and
+ *   dB_prev = sum over the group's heads of dP_{-1}^T x_prev.
+ * Returns 0, -1 on a bad shape, -2 if memory runs out.
+ */
+int oracle_ssd_trap_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                            int64_t dstate, int64_t ngroups, const double *x, const double *dt,
+                            const double *lam, const double *A, const double *B, const double *C,
+                            const double *Dskip, const double *z, const double *h0,
+                            const double *x_prev, const double *B_prev,
+                            const double *dy, const double *dh_last,
+                            double *dx, double *ddt, double *dlam, double *dA, double *dB, double *dC,
+                            double *dD, double *dz, double *dh0, double *dx_prev, double *dB_prev)
+{
+    if (batch < 0 || seqlen < 0 || nheads < 0 || headdim < 1 || dstate < 1 ||
+        ngroups < 1 || nheads % ngroups != 0 || (x_prev == NULL) != (B_prev == NULL))
+        return -1;
+    const int64_t PN = headdim * dstate, hpg = nheads / ngroups;
+    double *Hs = malloc(sizeof(double) * (size_t)((seqlen + 1) * PN));
+    double *yhat = malloc(sizeof(double) * (size_t)((seqlen > 0 ? seqlen : 1) * headdim));
+    double *Lm = malloc(sizeof(double) * (size_t)PN);      /* Lam_t */
+    double *Ln = malloc(sizeof(double) * (size_t)PN);      /* Lam_{t+1} */
+    double *dyh = malloc(sizeof(double) * (size_t)headdim);
+    if (!Hs || !yhat || !Lm || !Ln || !dyh) {
+        free(Hs); free(yhat); free(Lm); free(Ln); free(dyh);
+        return -2;
+    }
+    for (int64_t k = 0; k < nheads; ++k) dA[k] = 0.0;
+    if (Dskip)
+        for (int64_t k = 0; k < nheads; ++k) dD[k] = 0.0;
+    for (int64_t k = 0; k < batch * seqlen * ngroups * dstate; ++k) {
+        dB[k] = 0.0;
+        dC[k] = 0.0;
+    }
+    if (B_prev)
+        for (int64_t k = 0; k < batch * ngroups * dstate; ++k) dB_prev[k] = 0.0;
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t hd = 0; hd < nheads; ++hd) {
+            const int64_t g = hd / hpg;
+            const double *xp = x_prev ? x_prev + (b * nheads + hd) * headdim : NULL;
+            const double *bp = B_prev ? B_prev + (b * ngroups + g) * dstate : NULL;
+            /* forward, keeping every state: Hs[t + 1] is H_t */
+            for (int64_t k = 0; k < PN; ++k) Hs[k] = h0 ? h0[(b * nheads + hd) * PN + k] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t it = (b * seqlen + t) * nheads + hd;
+                const double d = dt[it], alpha = exp(d * A[hd]), gamma = lam[it] * d;
+                const double beta = (d - gamma) * alpha;
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Bq = t > 0 ? B + ((b * seqlen + t - 1) * ngroups + g) * dstate : bp;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = it * headdim + p;
+                    const double xq = t > 0 ? x[i - nheads * headdim] : (xp ? xp[p] : 0.0);
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const int64_t k = p * dstate + n;
+                        const double prev = Bq ? Bq[n] * xq : 0.0;
+                        Hs[(t + 1) * PN + k] = alpha * Hs[t * PN + k] + beta * prev + gamma * Bt[n] * x[i];
+                        acc += Ct[n] * Hs[(t + 1) * PN + k];
+                    }
+                    if (Dskip) acc += Dskip[hd] * x[i];
+                    yhat[t * headdim + p] = acc;
+                }
+            }
+            /* backward */
+            for (int64_t k = 0; k < PN; ++k) {
+                Ln[k] = 0.0;  /* Lam_L: nothing after the sequence */
+                Lm[k] = 0.0;
+            }
+            double beta_next = 0.0, alpha_next = 0.0;
+            for (int64_t t = seqlen - 1; t >= 0; --t) {
+                const int64_t it = (b * seqlen + t) * nheads + hd;
+                const double d = dt[it], lm = lam[it], alpha = exp(d * A[hd]), gamma = lm * d;
+                const double beta = (d - gamma) * alpha;
+                const double *Bt = B + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Ct = C + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double *Bq = t > 0 ? B + ((b * seqlen + t - 1) * ngroups + g) * dstate : bp;
+                double *dBt = dB + ((b * seqlen + t) * ngroups + g) * dstate;
+                double *dCt = dC + ((b * seqlen + t) * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = it * headdim + p;
+                    dyh[p] = dy[i];
+                    if (z) {
+                        const double sg = 1.0 / (1.0 + exp(-z[i]));
+                        dyh[p] = dy[i] * z[i] * sg;
+                        dz[i] = dy[i] * yhat[t * headdim + p] * sg * (1.0 + z[i] * (1.0 - sg));
+                    }
+                    if (Dskip) dD[hd] += dyh[p] * x[i];
+                }
+                double dal = 0.0, dbe = 0.0, dga = 0.0;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    const int64_t i = it * headdim + p;
+                    const double xq = t > 0 ? x[i - nheads * headdim] : (xp ? xp[p] : 0.0);
+                    double dxp = Dskip ? Dskip[hd] * dyh[p] : 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const int64_t k = p * dstate + n;
+                        /* Lam_t = dyhat_t C_t^T + alpha_{t+1} Lam_{t+1} (+ dh_last at the end) */
+                        double l = dyh[p] * Ct[n] + alpha_next * Ln[k];
+                        if (t == seqlen - 1 && dh_last) l += dh_last[(b * nheads + hd) * PN + k];
+                        Lm[k] = l;
+                        const double dq = gamma * l + beta_next * Ln[k];
+                        dxp += dq * Bt[n];
+                        dBt[n] += dq * x[i];
+                        dCt[n] += Hs[(t + 1) * PN + k] * dyh[p];
+                        dal += l * Hs[t * PN + k];
+                        dbe += l * (Bq ? Bq[n] * xq : 0.0);
+                        dga += l * Bt[n] * x[i];
+                    }
+                    dx[i] = dxp;
+                }
+                ddt[it] = A[hd] * alpha * dal + (1.0 - lm) * alpha * (1.0 + d * A[hd]) * dbe + lm * dga;
+                dlam[it] = d * (dga - alpha * dbe);
+                dA[hd] += d * (alpha * dal + beta * dbe);
+                for (int64_t k = 0; k < PN; ++k) Ln[k] = Lm[k];
+                alpha_next = alpha;
+                beta_next = beta;
+            }
+            /* the state before the first step, and the previous token's input */
+            for (int64_t k = 0; k < PN; ++k) {
+                double l = seqlen > 0 ? Ln[k] : (dh_last ? dh_last[(b * nheads + hd) * PN + k] : 0.0);
+                dh0[(b * nheads + hd) * PN + k] = seqlen > 0 ? alpha_next * l : l;
+            }
+            if (xp) {
+                double *dxq = dx_prev + (b * nheads + hd) * headdim;
+                double *dbq = dB_prev + (b * ngroups + g) * dstate;
+                for (int64_t p = 0; p < headdim; ++p) {
+                    double v = 0.0;
+                    for (int64_t n = 0; n < dstate; ++n) {
+                        const double dp = seqlen > 0 ? beta_next * Ln[p * dstate + n] : 0.0;
+                        v += dp * bp[n];
+                        dbq[n] += dp * xp[p];
+                    }
+                    dxq[p] = v;
+                }
+            }
+        }
+    }
+    free(Hs); free(yhat); free(Lm); free(Ln); free(dyh);
+    return 0;
+}
+
+/*
  * Phase-0 maps of the raw step and trapezoid inputs ("Mamba-3 NKI Kernels for
  * AWS Neuron", section "How it works", Phase 0: dt_softplus = softplus(dt +
  * dt_bias), lam_sigmoid = sigmoid(lam)).

@@ -464,6 +464,53 @@ def _trap_inputs(rng, b, L, H, P, N, G):
             "h0": rng.standard_normal((b, H, P, N))}
 
 
+def check_ssd_trap_bwd_finite_differences(orc):
+    """The trapezoidal SSD backward against central finite differences of the
+    trapezoidal forward, every optional input present, the token before the
+    sequence given (two group counts): the gradient of L = sum(dy * y) +
+    sum(dh_last * h_last) with respect to each element of x, dt, lam, A, B, C,
+    D, z, h0, x_prev and B_prev."""
+    names = {"x": "dx", "dt": "ddt", "lam": "dlam", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "z": "dz",
+             "h0": "dh0", "x_prev": "dx_prev", "B_prev": "dB_prev"}
+    for seed, (b, L, H, P, N, G) in ((71, (2, 5, 2, 3, 4, 1)), (72, (1, 4, 4, 2, 3, 2))):
+        rng = np.random.default_rng(seed)
+        inp = _trap_inputs(rng, b, L, H, P, N, G)
+        inp["x_prev"], inp["B_prev"] = rng.standard_normal((b, H, P)), rng.standard_normal((b, G, N))
+        dy, dhl = rng.standard_normal((b, L, H, P)), rng.standard_normal((b, H, P, N))
+
+        def loss(v):
+            y, h = orc.ssd_trap(v["x"], v["dt"], v["lam"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"],
+                                v["x_prev"], v["B_prev"])
+            return float(np.sum(dy * y) + np.sum(dhl * h))
+
+        g = orc.ssd_trap_bwd(inp["x"], inp["dt"], inp["lam"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"],
+                             inp["h0"], inp["x_prev"], inp["B_prev"], dy, dhl)
+        for k, gk in names.items():
+            fd = np.zeros_like(inp[k])
+            for idx in np.ndindex(inp[k].shape):
+                e = 1e-6 * max(1.0, abs(inp[k][idx]))
+                lo, hi = dict(inp), dict(inp)
+                lo[k], hi[k] = inp[k].copy(), inp[k].copy()
+                lo[k][idx] -= e
+                hi[k][idx] += e
+                fd[idx] = (loss(hi) - loss(lo)) / (2 * e)
+            _close(g[gk], fd, rtol=1e-7, what=f"trapezoidal d{k} against finite differences (seed {seed})")
+
+
+def check_ssd_trap_bwd_lam_one_is_ssd_bwd(orc):
+    """lam = 1 and no previous token: the trapezoid is the plain SSD, so every
+    gradient but dlam equals the SSD backward's."""
+    rng = np.random.default_rng(73)
+    v = _trap_inputs(rng, 2, 9, 3, 4, 5, 1)
+    one = np.ones_like(v["lam"])
+    dy, dhl = rng.standard_normal(v["x"].shape), rng.standard_normal(v["h0"].shape)
+    g = orc.ssd_trap_bwd(v["x"], v["dt"], one, v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"], None, None,
+                         dy, dhl)
+    r = orc.ssd_bwd(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["z"], v["h0"], dy, dhl)
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        _close(g[k], r[k], rtol=1e-12, what=f"trapezoidal {k} at lam = 1 vs SSD backward")
+
+
 def check_ssd_trap_lam_one_is_ssd(orc):
     """lam = 1: gamma = dt and beta = 0, so the three-term recurrence is the
     plain scalar-decay SSD (equal up to the order of one product's rounding)."""
@@ -712,6 +759,8 @@ ALL_CHECKS = [
     check_ssd_trap_lam_one_is_ssd,
     check_ssd_trap_single_ssd_form,
     check_ssd_trap_previous_token,
+    check_ssd_trap_bwd_finite_differences,
+    check_ssd_trap_bwd_lam_one_is_ssd_bwd,
     check_phase0_softplus,
     check_phase0_sigmoid_and_softplus_grad,
     check_rope_closed_form,

@@ -4,7 +4,8 @@ the definition: the decay and its sign, the dt on the input, the readout order,
 B versus C, the D skip, the gate and its order, the group index, the B/C
 layout, the initial state and the final state; and each term of the backward
 (the adjoint's decay, the state each gradient uses, the gate derivative, the
-upstream state gradient); the trapezoid's previous-token term; and the rotary step on B and C (the angle's sign
+upstream state gradient); the trapezoid's previous-token term and each
+term of its backward; and the rotary step on B and C (the angle's sign
 and running sum, the rotation, the pairing of states, the group, the per-head
 angles, the starting angle, C's rotation)."""
 import os
@@ -74,6 +75,16 @@ MUTANTS = [
     ("ssd_bwd_dh_last_ignored", [("lam[k] = dh_last ? dh_last[(b * nheads + hd) * PN + k] : 0.0;", "lam[k] = 0.0;")]),
     ("ssd_bwd_group_index", [("            const int64_t g = hd / hpg;\n            /* forward, keeping every state",
                               "            const int64_t g = hd % ngroups;\n            /* forward, keeping every state")]),
+    ("trap_bwd_no_next_beta", [("const double dq = gamma * l + beta_next * Ln[k];", "const double dq = gamma * l;")]),
+    ("trap_bwd_dlam_sign", [("dlam[it] = d * (dga - alpha * dbe);", "dlam[it] = d * (dga + alpha * dbe);")]),
+    ("trap_bwd_ddt_no_gamma_term", [(" + lm * dga;", ";")]),
+    ("trap_bwd_ddt_beta_decay_dropped", [("(1.0 - lm) * alpha * (1.0 + d * A[hd]) * dbe", "(1.0 - lm) * alpha * dbe")]),
+    ("trap_bwd_dA_no_beta", [("dA[hd] += d * (alpha * dal + beta * dbe);", "dA[hd] += d * alpha * dal;")]),
+    ("trap_bwd_prev_uses_alpha", [("const double dp = seqlen > 0 ? beta_next * Ln[p * dstate + n] : 0.0;",
+                                   "const double dp = seqlen > 0 ? alpha_next * Ln[p * dstate + n] : 0.0;")]),
+    ("trap_bwd_dB_prev_not_summed", [("dbq[n] += dp * xp[p];", "dbq[n] = dp * xp[p];")]),
+    ("trap_bwd_adjoint_no_decay", [("double l = dyh[p] * Ct[n] + alpha_next * Ln[k];", "double l = dyh[p] * Ct[n] + Ln[k];")]),
+    ("trap_bwd_dbeta_uses_current_input", [("dbe += l * (Bq ? Bq[n] * xq : 0.0);", "dbe += l * Bt[n] * x[i];")]),
     ("softplus_overflows", [("return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v));", "return log1p(exp(v));")]),
     ("softplus_bias_dropped", [("out[i] = softplus(raw[i] + bv);", "out[i] = softplus(raw[i]);")]),
     ("softplus_bias_index", [("bias[(i / inner) % nb]", "bias[i % nb]")]),
