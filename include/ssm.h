@@ -328,12 +328,14 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
                          float *h_last, const ssd_dims_t *dims, void *stream);
 
 /*
- * Workspace ssd_bwd needs for `dims`.  With K = ceil(seqlen / 64) chunks and
- * the chunk kernel's hpw heads per workgroup (a function of the sizes, up to
- * 8): two bf16 state matrices per (batch, head, chunk) (2 * batch * nheads
- * * K * headdim * dstate * 2 bytes), two floats per (batch, head, chunk),
- * and two float32 (batch, seqlen, nheads / hpw, dstate) arrays of dB and dC
- * terms; each region rounded up to 256 bytes.
+ * Workspace ssd_bwd and ssd_trap_bwd need for `dims`.  With K =
+ * ceil(seqlen / 64) chunks and the chunk kernel's hpw heads per workgroup (a
+ * function of the sizes, up to 8): two bf16 state matrices per (batch, head,
+ * chunk) (2 * batch * nheads * K * headdim * dstate * 2 bytes), two floats
+ * per (batch, head, chunk), two float32 (batch, seqlen, nheads / hpw,
+ * dstate) arrays of dB and dC terms, three floats per (batch, step, head),
+ * one per (batch, head) and (batch, nheads, dstate) floats; each region
+ * rounded up to 256 bytes.
  */
 SSM_API int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes);
 
@@ -379,6 +381,41 @@ SSM_API int ssd_bwd(const void *x, const void *dt, const float *A, const void *B
             const float *D, const void *z, const float *h0, const void *dy, const float *dh_last,
             void *dx, void *ddt, float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0,
             const ssd_dims_t *dims, void *stream);
+
+/*
+ * Backward of the trapezoidal SSD (ssd_trap_chunked_fwd): gradients of a loss
+ * L with respect to every input, given dy = dL/dy and dh_last = dL/dh_last.
+ *
+ * The chain rule on the three-term recurrence of ssd_trap_chunked_fwd
+ * ([Mamba-3 NKI], "How it works": Eq. 9, H_t = alpha_t H_{t-1} +
+ * beta_t B_{t-1} x_{t-1} + gamma_t B_t x_t with alpha = exp(dt A),
+ * beta = dt (1 - lam) alpha, gamma = lam dt; "Correctness" reports backward
+ * parity and prints no formulas).  With Lam_t = dL/dH_t:
+ *   Lam_t  = dyhat_t C_t^T + alpha_{t+1} Lam_{t+1},   dQ_t = gamma_t Lam_t + beta_{t+1} Lam_{t+1}
+ *   dx_t   = dQ_t B_t + D dyhat_t,   dB_t = sum over heads of dQ_t^T x_t,   dC_t as ssd_bwd
+ *   ddt, dlam and dA through alpha, beta and gamma (the chain rule on each);
+ *   dx_prev, dB_prev: the token before the sequence, through beta_0.
+ * computed chunk by chunk as ssd_bwd, the input of step s weighted by
+ * scale_s = gamma_s + dt_{s+1} (1 - lam_{s+1}) where it reaches a later step
+ * and by gamma_s at its own step, as in the forward.
+ *
+ * Inputs: as ssd_trap_chunked_fwd (dims, x, dt, lam, A, B, C, D, z, h0,
+ * x_prev, B_prev), plus dy and dh_last as ssd_bwd.
+ * Outputs (overwritten): as ssd_bwd, plus
+ *   dlam    : (batch, seqlen, nheads) bf16 (with SSM_LAM_SIGMOID: the gradient
+ *             of the raw lam, i.e. times s (1 - s), s = sigmoid(lam))
+ *   dx_prev : (batch, nheads, headdim) bf16 and dB_prev : (batch, ngroups,
+ *             dstate) float32, required with x_prev and B_prev (ignored
+ *             without them).
+ * Workspace: ssd_bwd_workspace_size() bytes (one size serves both forms).
+ * Flags: SSM_DT_SOFTPLUS and SSM_LAM_SIGMOID.  Alignment, overlap and size
+ * rules as ssd_bwd; x_prev, B_prev and dx_prev element aligned.
+ */
+SSM_API int ssd_trap_bwd(const void *x, const void *dt, const void *lam, const float *A, const void *B,
+                 const void *C, const float *D, const void *z, const float *h0, const void *x_prev,
+                 const void *B_prev, const void *dy, const float *dh_last, void *dx, void *ddt, void *dlam,
+                 float *dA, float *dB, float *dC, float *dD, void *dz, float *dh0, void *dx_prev,
+                 float *dB_prev, const ssd_dims_t *dims, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Rotary step on B and C (Mamba-3 complex-valued state)                     */

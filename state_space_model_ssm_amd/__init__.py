@@ -111,6 +111,8 @@ def lib():
         L.ssd_bwd_workspace_size.restype = i32
         L.ssd_bwd.argtypes = [vp] * 18 + [ctypes.POINTER(SsdDims), vp]
         L.ssd_bwd.restype = i32
+        L.ssd_trap_bwd.argtypes = [vp] * 24 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_trap_bwd.restype = i32
         L.ssm_scan_bwd.argtypes = [vp] * 18 + [ctypes.POINTER(ScanDims), vp]
         L.ssm_scan_bwd.restype = i32
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanDims), ctypes.POINTER(ctypes.c_size_t)]
@@ -462,6 +464,22 @@ def ssd_bwd(x, dt, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, worksp
     dh_last (float32, optional).  Returns a dict dx, ddt, dz (bf16; dz when z is
     given), dA, dB, dC, dD (float32; dD when D is given) and dh0 (float32).
     With dt_softplus, ddt is the gradient of the raw dt."""
+    return _ssd_bwd_call(x, dt, None, A, B, C, D, z, dy=dy, h0=h0, dh_last=dh_last, workspace=workspace,
+                         stream=stream, dt_softplus=dt_softplus, dt_bias=dt_bias)
+
+
+def ssd_trap_bwd(x, dt, lam, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, x_prev=None, B_prev=None,
+                 workspace=None, stream=None, dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False):
+    """Trapezoidal SSD backward (``ssd_trap_bwd``): as ``ssd_bwd`` plus dlam
+    (bf16) and, with x_prev and B_prev, dx_prev (bf16) and dB_prev (float32).
+    With lam_sigmoid, dlam is the gradient of the raw lam."""
+    return _ssd_bwd_call(x, dt, lam, A, B, C, D, z, dy=dy, h0=h0, dh_last=dh_last, workspace=workspace,
+                         stream=stream, dt_softplus=dt_softplus, dt_bias=dt_bias, lam_sigmoid=lam_sigmoid,
+                         x_prev=x_prev, B_prev=B_prev)
+
+
+def _ssd_bwd_call(x, dt, lam, A, B, C, D, z, *, dy, h0, dh_last, workspace, stream, dt_softplus, dt_bias,
+                  lam_sigmoid=False, x_prev=None, B_prev=None):
     torch = _torch()
     in_code = _dtype_code(x.dtype)
     out_code = _dtype_code(dy.dtype)
@@ -469,13 +487,19 @@ def ssd_bwd(x, dt, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, worksp
     G, N = B.shape[2], B.shape[3]
     if dy.shape != x.shape or (z is not None and z.shape != x.shape) or dt.shape != (batch, L, H):
         raise ValueError("dy and z must be shaped like x, dt (batch, L, H)")
+    if lam is not None and lam.shape != dt.shape:
+        raise ValueError("lam must be shaped like dt")
     if B.shape != (batch, L, G, N) or C.shape != B.shape or A.shape != (H,) or (D is not None and D.shape != (H,)):
         raise ValueError("B, C must be (batch, L, ngroups, dstate) and A, D (nheads,)")
     for name, t in (("h0", h0), ("dh_last", dh_last)):
         if t is not None and (t.dtype != torch.float32 or t.shape != (batch, H, P, N)):
             raise ValueError(f"{name} must be float32 (batch, nheads, headdim, dstate)")
+    if (x_prev is None) != (B_prev is None):
+        raise ValueError("x_prev and B_prev are given together or not at all")
+    if x_prev is not None and (x_prev.shape != (batch, H, P) or B_prev.shape != (batch, G, N)):
+        raise ValueError("x_prev must be (batch, nheads, headdim) and B_prev (batch, ngroups, dstate)")
     dims = _ssd_dims(x, B, 64, in_code, out_code)
-    _phase0(dims, H, dt_softplus, dt_bias)
+    _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
     need = ssd_bwd_workspace_size(dims)
     f32 = torch.float32
     with _alloc_on(stream):
@@ -491,9 +515,21 @@ def ssd_bwd(x, dt, A, B, C, D=None, z=None, *, dy, h0=None, dh_last=None, worksp
              "dD": None if D is None else torch.empty((H,), dtype=f32, device=x.device),
              "dz": None if z is None else torch.empty_like(x),
              "dh0": torch.empty((batch, H, P, N), dtype=f32, device=x.device)}
-    _check(lib().ssd_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
-                         _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                         _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), ctypes.byref(dims), _stream(stream)))
+        if lam is not None:
+            g["dlam"] = torch.empty_like(lam)
+            g["dx_prev"] = None if x_prev is None else torch.empty_like(x_prev)
+            g["dB_prev"] = None if B_prev is None else torch.empty((batch, G, N), dtype=f32, device=x.device)
+    if lam is None:
+        _check(lib().ssd_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(dy),
+                             _ptr(dh_last), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                             _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), ctypes.byref(dims),
+                             _stream(stream)))
+    else:
+        _check(lib().ssd_trap_bwd(_ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(h0), _ptr(x_prev), _ptr(B_prev), _ptr(dy), _ptr(dh_last), _ptr(g["dx"]),
+                                  _ptr(g["ddt"]), _ptr(g["dlam"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                  _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["dh0"]), _ptr(g["dx_prev"]),
+                                  _ptr(g["dB_prev"]), ctypes.byref(dims), _stream(stream)))
     return g
 
 

@@ -215,9 +215,10 @@ struct StateSmem {
   uint16_t V[Q * PP];
   float om[Q];
   float dec;
+  float part[4];
 };
 
-template <int N, bool REV, typename Tdy, bool HAS_Z>
+template <int N, bool REV, typename Tdy, bool HAS_Z, bool TRAP>
 __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, StateSmem<N> &sm) {
   constexpr int NT = N / 16, NPC = N + 24;
   constexpr int UJ = Q * (N / 8) / 256;  // U jobs (8 elements) per thread
@@ -239,6 +240,16 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
   const float bias = (p.dt_softplus && p.dt_bias) ? p.dt_bias[h] : 0.0f;
   const uint16_t *gU = static_cast<const uint16_t *>(REV ? p.C : p.B);
   const uint16_t *gx = static_cast<const uint16_t *>(p.x);
+  const uint16_t *gdt = static_cast<const uint16_t *>(p.dt);
+  const uint16_t *glam = static_cast<const uint16_t *>(p.lam);
+  auto step_of = [&](uint32_t raw) __attribute__((always_inline)) {
+    const float v = bf2f(static_cast<uint16_t>(raw));
+    return p.dt_softplus ? dt_softplus(v + bias) : v;
+  };
+  auto lam_of = [&](uint32_t raw) __attribute__((always_inline)) {
+    const float v = bf2f(static_cast<uint16_t>(raw));
+    return p.lam_sigmoid ? 1.0f / (1.0f + expf(-v)) : v;
+  };
 
   floatx4 S[NT];
   const float *init = REV ? p.dh_last : p.h0;
@@ -246,12 +257,28 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
   for (int ni = 0; ni < NT; ++ni)
     S[ni] = init ? *reinterpret_cast<const floatx4 *>(init + (bh * P + pcol) * N + 16 * ni + 4 * q)
                  : floatx4{0.f, 0.f, 0.f, 0.f};
+  // Trapezoid: the token before the sequence enters the state before the
+  // first step with weight w0 = dt_0 (1 - lam_0) (its decay alpha_0 is the
+  // first chunk's); the reverse pass returns the gradients of that term.
+  const bool prev_tok = TRAP && p.x_prev != nullptr && L > 0;
+  const float w0 = prev_tok ? step_of(gdt[b * L * H + h]) * (1.0f - lam_of(glam[b * L * H + h])) : 0.0f;
+  if constexpr (TRAP && !REV) {
+    if (prev_tok) {
+      const float xw = w0 * bf2f(static_cast<const uint16_t *>(p.x_prev)[(b * H + h) * P + pcol]);
+      const uint16_t *bp = static_cast<const uint16_t *>(p.B_prev) + (b * G + g) * N + 4 * q;
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[ni][r] = fmaf(xw, bf2f(bp[16 * ni + r]), S[ni][r]);
+    }
+  }
 
   struct Regs {
     uint4 u[UJ];
     uint4 v[VJ][REV ? DW : 1];
     uint4 z[HAS_Z && REV ? VJ : 1];
     uint32_t dt;  // raw bf16 bits of this lane's step (wavefront 0)
+    uint32_t lam, dtn, lamn;  // trapezoid (forward): lam at this lane's step, dt and lam one step later
   };
   // Rows past the end are loaded from the last valid step (branch-free) and
   // zeroed when staged.
@@ -281,7 +308,13 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
         if constexpr (HAS_Z) R.z[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.z) + vb + o);
       }
     }
-    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0) * H + h + min(lane, last) * Hi];
+    R.dt = gdt[(b * L + c0) * H + h + min(lane, last) * Hi];
+    if constexpr (TRAP && !REV) {
+      const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
+      R.lam = glam[(b * L + c0) * H + h + min(lane, last) * Hi];
+      R.dtn = gdt[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
+      R.lamn = glam[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
+    }
   };
   auto stage = [&](int64_t c, const Regs &R) __attribute__((always_inline)) {
     const int Lc = static_cast<int>(min(static_cast<int64_t>(Q), L - c * Q));
@@ -321,14 +354,16 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
       *reinterpret_cast<uint4 *>(&sV[t * PP + pv]) = t < Lc ? v : uint4{0u, 0u, 0u, 0u};
     }
     if (wave == 0) {
-      float dtv = 0.0f;
-      if (lane < Lc) {
-        dtv = bf2f(static_cast<uint16_t>(R.dt));
-        if (p.dt_softplus) dtv = dt_softplus(dtv + bias);
-      }
+      const float dtv = lane < Lc ? step_of(R.dt) : 0.0f;
       const float a = wave_prefix(dtv * Ah, lane);
       const float alast = lane_value<63>(a);
-      sOm[lane] = REV ? fast_exp(a) : dtv * fast_exp(alast - a);
+      float w = dtv;  // the input's weight where it reaches the state
+      if constexpr (TRAP && !REV) {
+        // scale_s = gamma_s + dt_{s+1} (1 - lam_{s+1}); after the sequence dt = 0.
+        const bool nx = c * Q + lane + 1 < L;
+        w = (lane < Lc ? lam_of(R.lam) * dtv : 0.0f) + (nx ? step_of(R.dtn) * (1.0f - lam_of(R.lamn)) : 0.0f);
+      }
+      sOm[lane] = REV ? fast_exp(a) : w * fast_exp(alast - a);
       if (lane == 0) sDec = fast_exp(alast);
     }
   };
@@ -385,21 +420,53 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni) *reinterpret_cast<floatx4 *>(p.dh0 + (bh * P + pcol) * N + 16 * ni + 4 * q) = S[ni];
     }
+    if constexpr (TRAP) {
+      // S is now dh0 = dL/d(state before the first step), which the folded
+      // term w0 x_prev B_prev^T shares: dw0 = <dh0, x_prev B_prev^T>,
+      // dx_prev = w0 dh0 B_prev, dB_prev = w0 dh0^T x_prev (summed over heads later).
+      if (p.x_prev != nullptr) {
+        float *red = reinterpret_cast<float *>(sm.U);   // [4][N] after the last chunk
+        const float xp = bf2f(static_cast<const uint16_t *>(p.x_prev)[(b * H + h) * P + pcol]);
+        const uint16_t *bp = static_cast<const uint16_t *>(p.B_prev) + (b * G + g) * N + 4 * q;
+        float dxp = 0.0f, dwp = 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < NT; ++ni) {
+          float cs[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float bv = bf2f(bp[16 * ni + r]);
+            dxp = fmaf(S[ni][r], bv, dxp);
+            cs[r] = row_sum(S[ni][r] * xp);
+          }
+          if (m < 4) red[wave * N + 16 * ni + 4 * q + m] = pick4(cs, m);
+        }
+        // dw0 = sum over p of x_prev[p] (dh0 B_prev)[p].
+        dwp = wave_sum(dxp * xp);
+        dxp += __shfl_xor(dxp, 16);
+        dxp += __shfl_xor(dxp, 32);
+        if (q == 0) static_cast<uint16_t *>(p.dx_prev)[(b * H + h) * P + pcol] = f2bf(prev_tok ? w0 * dxp : 0.0f);
+        if (lane == 0) sm.part[wave] = dwp;
+        __syncthreads();
+        if (tid < N)
+          p.ws_dBpp[bh * N + tid] = prev_tok ? w0 * ((red[tid] + red[N + tid]) + (red[2 * N + tid] + red[3 * N + tid])) : 0.0f;
+        if (tid == 0) p.ws_dw0[bh] = prev_tok ? (sm.part[0] + sm.part[1]) + (sm.part[2] + sm.part[3]) : 0.0f;
+      }
+    }
   }
 }
 
 // Both state passes in one launch (they are independent): even workgroups
 // run the forward pass of (batch, head) blockIdx / 2, odd ones the reverse.
 // FWD = false launches the reverse passes alone (an empty sequence).
-template <int N, typename Tdy, bool HAS_Z, bool FWD>
+template <int N, typename Tdy, bool HAS_Z, bool FWD, bool TRAP>
 __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p) {
   __shared__ __attribute__((aligned(16))) StateSmem<N> sm;
   if (!FWD) {
-    state_pass<N, true, Tdy, HAS_Z>(p, blockIdx.x, sm);
+    state_pass<N, true, Tdy, HAS_Z, TRAP>(p, blockIdx.x, sm);
   } else if (blockIdx.x % 2 == 0) {
-    state_pass<N, false, Tdy, HAS_Z>(p, blockIdx.x / 2, sm);
+    state_pass<N, false, Tdy, HAS_Z, TRAP>(p, blockIdx.x / 2, sm);
   } else {
-    state_pass<N, true, Tdy, HAS_Z>(p, blockIdx.x / 2, sm);
+    state_pass<N, true, Tdy, HAS_Z, TRAP>(p, blockIdx.x / 2, sm);
   }
 }
 
@@ -412,8 +479,17 @@ __global__ void __launch_bounds__(256) ssd_bwd_state_kernel(const SsdBwdParams p
 // Y (16 x 16 in (step, headdim)): headdim tile w % 4, step tile w / 4; dB and
 // dC (step, dstate): dstate tile w % NT and the step tiles w / NT + k (16 / NT),
 // k < NT / 4.
+//
+// The masked products carry the input weights: M[t][s] = (C_t . B_s)
+// e^{a_t - a_s} w_ts with w_ts = dt_s (scalar decay) or, trapezoid, scale_s =
+// gamma_s + dt_{s+1} (1 - lam_{s+1}) below the diagonal and gamma_s on it; the
+// state terms use dt_s or scale_s.  The gradients of those weights are the
+// sums over t of U[t][s] = (C_t . B_s) e^{a_t - a_s} (x_s . dyhat_t) (below the
+// diagonal and on it) plus the state term's x_s . (B dS^T)_s e^{a_last - a_s}:
+// their total is the input part of ddt for the scalar decay; the trapezoid
+// stores them per step for the weights' chain rule (ssd_bwd_trap_steps_kernel).
 constexpr int kBwdWaves = 16;
-template <int N, typename Tdy, bool HAS_Z>
+template <int N, typename Tdy, bool HAS_Z, bool TRAP>
 __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const SsdBwdParams p) {
   constexpr int NW = kBwdWaves, NTH = 64 * NW;
   constexpr int NPC = N + 24, NK = N / 32, NT = N / 16;
@@ -424,9 +500,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
   __shared__ __attribute__((aligned(16))) uint16_t sB[Q * NPC];
   __shared__ __attribute__((aligned(16))) uint16_t sX[Q * PP];
   __shared__ __attribute__((aligned(16))) uint16_t sDY[Q * PP];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[Q * QPp];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[Q * QPp];    // M[t][s]
   __shared__ __attribute__((aligned(16))) uint16_t sDG[Q * QPp];
-  __shared__ __attribute__((aligned(16))) uint16_t sM[HAS_Z ? Q * QPp : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sDS[P * NPC];   // dS[p][n]
   __shared__ __attribute__((aligned(16))) uint16_t sDX[Q * PP];    // dx[t][p], stored as rows
   __shared__ __attribute__((aligned(16))) uint16_t sSp[P * NPC];   // S_in[p][n]
@@ -434,7 +509,10 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
   __shared__ __attribute__((aligned(16))) float sEa[Q];
   __shared__ __attribute__((aligned(16))) float sWl[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sWo[Q];   // weight below the diagonal and in the state: dt or scale
+  __shared__ __attribute__((aligned(16))) float sWd[Q];   // weight on the diagonal: dt or gamma
   __shared__ float sRow[12][4][16], sCol[12][16];  // per tile: sums of R over s (per lane group, per t) and over t (per s)
+  __shared__ float sOffC[12][16], sDiag[Q];       // per tile: sums of U over t > s (per s); U on the diagonal
   __shared__ float sDdt[4][Q], sDaC[NT][Q], sDaB[NT][Q];
   __shared__ float sRed[NW], sPhi[NW];
 
@@ -473,6 +551,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     u32x4 x, dy[DW], z;
     u32x4 ds[SJ], sn[SJ];
     uint32_t dt;
+    uint32_t lam, dtn, lamn;  // trapezoid: lam at this lane's step, dt and lam one step later
   };
   auto load_head = [&](int64_t h, HeadRegs &R) __attribute__((always_inline)) {
     const int64_t bhc = (b * H + h) * nC + c;
@@ -496,6 +575,13 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       }
     }
     R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, Lc - 1)) * H + h];
+    if constexpr (TRAP) {
+      const uint16_t *glam = static_cast<const uint16_t *>(p.lam);
+      const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
+      R.lam = glam[(b * L + c0 + min(lane, Lc - 1)) * H + h];
+      R.dtn = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane + 1, lastn)) * H + h];
+      R.lamn = glam[(b * L + c0 + min(lane + 1, lastn)) * H + h];
+    }
   };
 
   HeadRegs R;
@@ -545,17 +631,29 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     const float bias = (p.dt_softplus && p.dt_bias) ? p.dt_bias[h] : 0.0f;
 
     if (wave == 0) {
-      float dtv = 0.0f;
-      if (lane < Lc) {
-        dtv = bf2f(static_cast<uint16_t>(R.dt));
-        if (p.dt_softplus) dtv = dt_softplus(dtv + bias);
-      }
+      auto step_of = [&](uint32_t raw) __attribute__((always_inline)) {
+        const float v = bf2f(static_cast<uint16_t>(raw));
+        return p.dt_softplus ? dt_softplus(v + bias) : v;
+      };
+      const float dtv = lane < Lc ? step_of(R.dt) : 0.0f;
       const float a = wave_prefix(dtv * Ah, lane);
       const float alast = lane_value<63>(a);
       sA[lane] = a;
       sEa[lane] = fast_exp(a);
       sWl[lane] = fast_exp(alast - a);
       sDt[lane] = dtv;
+      float wo = dtv, wd = dtv;
+      if constexpr (TRAP) {
+        auto lam_of = [&](uint32_t raw) __attribute__((always_inline)) {
+          const float v = bf2f(static_cast<uint16_t>(raw));
+          return p.lam_sigmoid ? 1.0f / (1.0f + expf(-v)) : v;
+        };
+        const bool nx = c0 + lane + 1 < L;  // after the sequence dt = 0
+        wd = lane < Lc ? lam_of(R.lam) * dtv : 0.0f;
+        wo = wd + (nx ? step_of(R.dtn) * (1.0f - lam_of(R.lamn)) : 0.0f);
+      }
+      sWo[lane] = wo;
+      sWd[lane] = wd;
     }
     // x and dyhat of the head's chunk (one 8-element job per thread of the
     // first Q P / 8), its dD term, dS[p][n] and S_in[p][n].
@@ -631,8 +729,9 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       if (lane == 0) sPhi[wave] = ph;
     }
 
-    // D2^T tiles (D2^T[s][t] = x_s . dyhat_t) and the masked matrices W[t][s],
-    // dG[t][s], M[t][s] = W dt_s (bf16); R[t][s] = dG G summed over s and over t.
+    // D2^T tiles (D2^T[s][t] = x_s . dyhat_t) and the masked matrices M[t][s]
+    // and dG[t][s] = w_ts e^{a_t - a_s} D2 (bf16); R = M o D2 summed over s and
+    // over t; U = M o D2 / w_ts summed over t below the diagonal, and on it.
     if (wave < 12) {
       const int kt = wave, si = gsi, ti = gti;
       floatx4 d2 = {0.f, 0.f, 0.f, 0.f};
@@ -644,36 +743,45 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       const int t = 16 * ti + m, sb = 16 * si + 4 * q;
       const float at = sA[t];
       const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sA[sb]);
-      const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
-      uint16_t wv[4], gv[4], mv[4];
-      float rr[4], rrow = 0.0f;
+      const floatx4 wo4 = *reinterpret_cast<const floatx4 *>(&sWo[sb]);
+      const floatx4 wd4 = *reinterpret_cast<const floatx4 *>(&sWd[sb]);
+      uint16_t wv[4], gv[4];
+      float rr[4], off[4], rrow = 0.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = sb + r;
         const float e = s <= t ? fast_exp(fminf(at - as4[r], 0.0f)) : 0.0f;
-        const float w = Gt[r] * e;
-        const float dg = dt4[r] * d2[r] * e;
-        wv[r] = f2bf(w);
-        gv[r] = f2bf(dg);
-        mv[r] = f2bf(w * dt4[r]);
-        rr[r] = dg * Gt[r];
+        const float om = s < t ? wo4[r] : wd4[r];
+        const float ge = Gt[r] * e;
+        const float uu = ge * d2[r];
+        wv[r] = f2bf(ge * om);
+        gv[r] = f2bf(om * d2[r] * e);
+        rr[r] = om * uu;
+        off[r] = s < t ? uu : 0.0f;
+        if (s == t) sDiag[s] = uu;
         rrow += rr[r];
       }
       *reinterpret_cast<uint2 *>(&sW[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(wv);
       *reinterpret_cast<uint2 *>(&sDG[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(gv);
-      if constexpr (HAS_Z) *reinterpret_cast<uint2 *>(&sM[t * QPp + sb]) = *reinterpret_cast<const uint2 *>(mv);
       // Sum over s of the tile: this lane's rows 4q + r here, the four lane
       // groups q when the step's gradient is assembled.
       sRow[kt][q][m] = rrow;
-      // Sum over t of the tile (the 16 lanes of a DPP row).
-      float cs[4];
+      // Sums over t of the tile (the 16 lanes of a DPP row).
+      float cs[4], co[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cs[r] = row_sum(rr[r]);
-      if (m < 4) sCol[kt][4 * q + m] = pick4(cs, m);
+      for (int r = 0; r < 4; ++r) {
+        cs[r] = row_sum(rr[r]);
+        co[r] = row_sum(off[r]);
+      }
+      if (m < 4) {
+        sCol[kt][4 * q + m] = pick4(cs, m);
+        sOffC[kt][4 * q + m] = pick4(co, m);
+      }
     }
     __syncthreads();
 
-    // dXd = W^T dyhat + diag(e^{a_last - a}) B dS^T; dx, and x . dXd per step.
+    // dx = M^T dyhat + diag(w e^{a_last - a}) B dS^T + D dyhat, and the state
+    // term x . (B dS^T) e^{a_last - a} per step.
     {
       const int pc = 16 * pt + m, si = st;
       floatx4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
@@ -686,16 +794,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
         a2 = mfma(ld8(&sB[(16 * si + m) * NPC + 32 * kk + 8 * q]), ld8(&sDS[pc * NPC + 32 * kk + 8 * q]), a2);
       const int sb = 16 * si + 4 * q;
       const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[sb]);
-      const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[sb]);
+      const floatx4 wo4 = *reinterpret_cast<const floatx4 *>(&sWo[sb]);
       float part[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = sb + r;
-        const float dxd = fmaf(wl4[r], a2[r], a1[r]);
         const float xs = bf2f(sX[s * PP + pc]);
         const float dys = bf2f(sDY[s * PP + pc]);
-        sDX[s * PP + pc] = f2bf(fmaf(dt4[r], dxd, Dh * dys));
-        part[r] = row_sum(xs * dxd);
+        sDX[s * PP + pc] = f2bf(fmaf(wo4[r] * wl4[r], a2[r], fmaf(Dh, dys, a1[r])));
+        part[r] = row_sum(xs * a2[r]) * wl4[r];
       }
       if (m < 4) sDdt[pt][sb + m] = pick4(part, m);
     }
@@ -710,7 +817,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         if (kk == 0 || ti >= 2)
-          y1 = mfma(ld8(&sM[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<PP>(sX, 32 * kk, 16 * pt, q, m), y1);
+          y1 = mfma(ld8(&sW[(16 * ti + m) * QPp + 32 * kk + 8 * q]), frag_t<PP>(sX, 32 * kk, 16 * pt, q, m), y1);
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
         y2 = mfma(ld8(&sC[(16 * ti + m) * NPC + 32 * kk + 8 * q]), ld8(&sSp[pc * NPC + 32 * kk + 8 * q]), y2);
@@ -754,12 +861,12 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // dB += dG^T C + diag(dt e^{a_last - a}) X dS, and (X dS)_s . B_s per step.
+    // dB += dG^T C + diag(w e^{a_last - a}) X dS, and (X dS)_s . B_s per step.
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int si = wave / NT + TSTEP * u;
       const floatx4 wl4 = *reinterpret_cast<const floatx4 *>(&sWl[16 * si + 4 * q]);
-      const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDt[16 * si + 4 * q]);
+      const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sWo[16 * si + 4 * q]);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         if (kk == 1 || si < 2)
@@ -792,12 +899,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
     // da per step, its suffix sums, ddt and the dA and dD terms (wavefront 0).
     if (wave == 0) {
       const int u = lane, ut = u / 16, um = u % 16;
-      float da = 0.0f, qu = 0.0f;
+      float da = 0.0f, qu = 0.0f, offs = 0.0f;
 #pragma unroll
       for (int kt = 0; kt < 12; ++kt) {
         const int code = static_cast<int>((kTiles >> (4 * kt)) & 0xF);
         if ((code >> 2) == ut) da += (sRow[kt][0][um] + sRow[kt][1][um]) + (sRow[kt][2][um] + sRow[kt][3][um]);
-        if ((code & 3) == ut) da -= sCol[kt][um];
+        if ((code & 3) == ut) {
+          da -= sCol[kt][um];
+          offs += sOffC[kt][um];
+        }
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -813,10 +923,22 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
       // Suffix sums: rc_u = sum_{t >= u} da_t.
       const float rc = wave_suffix(da, u);
       const float dtv = sDt[u];
-      float ddt = (sDdt[0][u] + sDdt[1][u]) + (sDdt[2][u] + sDdt[3][u]);
-      ddt = fmaf(Ah, rc, ddt);
-      if (p.dt_softplus) ddt *= 1.0f - __builtin_amdgcn_exp2f(-dtv * kLog2e);  // sigmoid(raw + bias) = 1 - e^{-dt}
-      if (u < Lc) gddt[(b * L + c0) * H + h + u * H] = f2bf(ddt);
+      // Gradient of the step's input weight below the diagonal and in the
+      // state, and on the diagonal.
+      const float dwo = offs + ((sDdt[0][u] + sDdt[1][u]) + (sDdt[2][u] + sDdt[3][u]));
+      const float dwd = sDiag[u];
+      if constexpr (TRAP) {
+        if (u < Lc) {
+          const int64_t o = (b * L + c0 + u) * H + h;
+          p.ws_dsc[o] = dwo;
+          p.ws_dga[o] = dwd;
+          p.ws_rc[o] = rc;
+        }
+      } else {
+        float ddt = fmaf(Ah, rc, dwo + dwd);
+        if (p.dt_softplus) ddt *= 1.0f - __builtin_amdgcn_exp2f(-dtv * kLog2e);  // sigmoid(raw + bias) = 1 - e^{-dt}
+        if (u < Lc) gddt[(b * L + c0) * H + h + u * H] = f2bf(ddt);
+      }
       const float dap = wave_sum(dtv * rc);
       if (u == 0) {
         float dd = 0.0f;
@@ -877,10 +999,23 @@ __device__ __forceinline__ void reduce_head(const SsdBwdParams &p, int64_t h) {
 }
 
 // Workgroups below `nbc` sum the dB and dC terms; the next nheads workgroups
-// sum dA and dD (reduce_head).
+// sum dA and dD (reduce_head); any after those sum the trapezoid's dB_prev
+// terms over the heads of each group.
 __global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams p, int64_t nbc) {
-  if (static_cast<int64_t>(blockIdx.x) >= nbc) {
-    reduce_head(p, blockIdx.x - nbc);
+  const int64_t blk = blockIdx.x;
+  if (blk >= nbc + p.nheads) {
+    const int64_t i = (blk - nbc - p.nheads) * 256 + threadIdx.x;
+    const int64_t N = p.dstate, hpg = p.nheads / p.ngroups;
+    if (i < p.batch * p.ngroups * N) {
+      const int64_t n = i % N, bg = i / N, g = bg % p.ngroups, b = bg / p.ngroups;
+      float v = 0.0f;
+      for (int64_t k = 0; k < hpg; ++k) v += p.ws_dBpp[(b * p.nheads + g * hpg + k) * N + n];
+      p.dB_prev[i] = v;
+    }
+    return;
+  }
+  if (blk >= nbc) {
+    reduce_head(p, blk - nbc);
     return;
   }
   // Thread i: four consecutive states of one (batch, step, group) for dB and dC.
@@ -917,23 +1052,59 @@ __global__ void __launch_bounds__(256) ssd_bwd_reduce_kernel(const SsdBwdParams 
   }
 }
 
-template <int N, typename Tdy, bool HAS_Z>
+// Trapezoid: ddt and dlam of every (batch, step, head) from the gradients of
+// the step's input weights (scale_t = gamma_t + dt_{t+1} (1 - lam_{t+1}) and
+// gamma_t = lam_t dt_t) and the suffix sums of the log-decay gradient:
+//   ddt_t  = A rc_t + lam_t (dscale_t + dgamma_t) + (1 - lam_t) dscale_{t-1}
+//   dlam_t = dt_t (dscale_t + dgamma_t - dscale_{t-1})
+// where dscale_{-1} is the gradient of the previous token's weight w0 (zero
+// without that token); then the Phase-0 maps' derivatives.
+__global__ void __launch_bounds__(256) ssd_bwd_trap_steps_kernel(const SsdBwdParams p) {
+  const int64_t H = p.nheads, L = p.seqlen;
+  const int64_t o = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (o >= p.batch * L * H) return;
+  const int64_t h = o % H, t = (o / H) % L, b = o / (H * L);
+  const float bias = (p.dt_softplus && p.dt_bias) ? p.dt_bias[h] : 0.0f;
+  float dtv = bf2f(static_cast<const uint16_t *>(p.dt)[o]);
+  if (p.dt_softplus) dtv = dt_softplus(dtv + bias);
+  float lam = bf2f(static_cast<const uint16_t *>(p.lam)[o]);
+  if (p.lam_sigmoid) lam = 1.0f / (1.0f + expf(-lam));
+  const float dsc = p.ws_dsc[o], dga = p.ws_dga[o];
+  const float dprev = t > 0 ? p.ws_dsc[o - H] : (p.x_prev != nullptr ? p.ws_dw0[b * H + h] : 0.0f);
+  float ddt = fmaf(p.A[h], p.ws_rc[o], fmaf(lam, dsc + dga, (1.0f - lam) * dprev));
+  float dlam = dtv * (dsc + dga - dprev);
+  if (p.dt_softplus) ddt *= 1.0f - __builtin_amdgcn_exp2f(-dtv * kLog2e);  // sigmoid(raw + bias) = 1 - e^{-dt}
+  if (p.lam_sigmoid) dlam *= lam * (1.0f - lam);
+  static_cast<uint16_t *>(p.ddt)[o] = f2bf(ddt);
+  static_cast<uint16_t *>(p.dlam)[o] = f2bf(dlam);
+}
+
+template <int N, typename Tdy, bool HAS_Z, bool TRAP>
 hipError_t launch_all(const SsdBwdParams &p, hipStream_t stream) {
   const uint32_t nbh = static_cast<uint32_t>(p.batch * p.nheads);
   if (p.nchunks > 0)
-    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, true>), dim3(2 * nbh), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, true, TRAP>), dim3(2 * nbh), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, false>), dim3(nbh), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ssd_bwd_state_kernel<N, Tdy, HAS_Z, false, TRAP>), dim3(nbh), dim3(256), 0, stream, p);
   if (p.nchunks > 0) {
     const dim3 grid(static_cast<uint32_t>(p.batch * p.nchunks * (p.nheads / p.hpw)));
-    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<N, Tdy, HAS_Z>), grid, dim3(64 * kBwdWaves), 0, stream, p);
+    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<N, Tdy, HAS_Z, TRAP>), grid, dim3(64 * kBwdWaves), 0, stream, p);
+    if constexpr (TRAP) {
+      const int64_t n = p.batch * p.seqlen * p.nheads;
+      hipLaunchKernelGGL(ssd_bwd_trap_steps_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }
 
-template <int N, typename Tdy>
+template <int N, typename Tdy, bool TRAP>
 hipError_t launch_z(const SsdBwdParams &p, hipStream_t stream) {
-  return p.z != nullptr ? launch_all<N, Tdy, true>(p, stream) : launch_all<N, Tdy, false>(p, stream);
+  return p.z != nullptr ? launch_all<N, Tdy, true, TRAP>(p, stream) : launch_all<N, Tdy, false, TRAP>(p, stream);
+}
+
+template <int N, typename Tdy>
+hipError_t launch_form(const SsdBwdParams &p, hipStream_t stream) {
+  return p.lam != nullptr ? launch_z<N, Tdy, true>(p, stream) : launch_z<N, Tdy, false>(p, stream);
 }
 
 }  // namespace
@@ -951,14 +1122,16 @@ hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream
   if (p.batch * p.nheads > 0) {
     hipError_t e;
     if (p.dstate == 128)
-      e = dy_bf16 ? launch_z<128, uint16_t>(p, stream) : launch_z<128, float>(p, stream);
+      e = dy_bf16 ? launch_form<128, uint16_t>(p, stream) : launch_form<128, float>(p, stream);
     else
-      e = dy_bf16 ? launch_z<64, uint16_t>(p, stream) : launch_z<64, float>(p, stream);
+      e = dy_bf16 ? launch_form<64, uint16_t>(p, stream) : launch_form<64, float>(p, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t nbc = (p.batch * p.seqlen * p.ngroups * p.dstate / 4 + 255) / 256;
-  if (nbc + p.nheads > 0)
-    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>(nbc + p.nheads)), dim3(256), 0, stream, p, nbc);
+  const int64_t nprev = (p.lam != nullptr && p.x_prev != nullptr) ? (p.batch * p.ngroups * p.dstate + 255) / 256 : 0;
+  if (nbc + p.nheads + nprev > 0)
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>(nbc + p.nheads + nprev)), dim3(256), 0,
+                       stream, p, nbc);
   return hipGetLastError();
 }
 

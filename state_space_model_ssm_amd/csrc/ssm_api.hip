@@ -591,13 +591,18 @@ int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const f
 
 // Backward workspace: per (batch, head, chunk) two bf16 state matrices
 // (S_in and dS) and two floats; per (batch, step, head block) the float32 dB
-// and dC terms.  Each region starts on a 256-byte boundary.
+// and dC terms; for the trapezoidal form three floats per (batch, step, head),
+// one per (batch, head) and dstate per (batch, head).  Each region starts on a
+// 256-byte boundary.  One size serves both forms.
 struct SsdBwdWorkspace {
   int64_t nchunks;
   int32_t hpw;
-  size_t state, per_bhc, bp;  // elements of one region
+  size_t state, per_bhc, bp, steps, bh;  // elements of one region
   static size_t up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
-  size_t bytes() const { return 2 * up(2 * state) + 2 * up(4 * per_bhc) + 2 * up(4 * bp); }
+  size_t bytes() const {
+    return 2 * up(2 * state) + 2 * up(4 * per_bhc) + 2 * up(4 * bp) + 3 * up(4 * steps) + up(4 * bh) + up(4 * bp_prev);
+  }
+  size_t bp_prev;
 };
 
 static SsdBwdWorkspace ssd_bwd_layout(const ssd_dims_t *d) {
@@ -607,6 +612,9 @@ static SsdBwdWorkspace ssd_bwd_layout(const ssd_dims_t *d) {
   w.per_bhc = static_cast<size_t>(d->batch * d->nheads * w.nchunks);
   w.state = w.per_bhc * static_cast<size_t>(d->headdim * d->dstate);
   w.bp = static_cast<size_t>(d->batch * d->seqlen * (d->nheads / w.hpw) * d->dstate);
+  w.steps = static_cast<size_t>(d->batch * d->seqlen * d->nheads);
+  w.bh = static_cast<size_t>(d->batch * d->nheads);
+  w.bp_prev = w.bh * static_cast<size_t>(d->dstate);
   return w;
 }
 
@@ -618,45 +626,64 @@ int ssd_bwd_workspace_size(const ssd_dims_t *dims, size_t *bytes) {
   return ok();
 }
 
-int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
-            const void *z, const float *h0, const void *dy, const float *dh_last, void *dx, void *ddt, float *dA,
-            float *dB, float *dC, float *dD, void *dz, float *dh0, const ssd_dims_t *dims, void *stream) {
+// Checks and launch shared by ssd_bwd and ssd_trap_bwd (trap: lam non-null).
+static int ssd_bwd_run(const void *x, const void *dt, const void *lam, const float *A, const void *B, const void *C,
+                       const float *D, const void *z, const float *h0, const void *x_prev, const void *B_prev,
+                       const void *dy, const float *dh_last, void *dx, void *ddt, void *dlam, float *dA, float *dB,
+                       float *dC, float *dD, void *dz, float *dh0, void *dx_prev, float *dB_prev,
+                       const ssd_dims_t *dims, void *stream, bool trap) {
   int rc = check_ssd_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssd_dims_t &d = *dims;
-  if (d.flags & SSM_LAM_SIGMOID) return fail(SSM_ERR_SHAPE, "SSM_LAM_SIGMOID applies to the trapezoidal form only");
+  if (!trap && (d.flags & SSM_LAM_SIGMOID))
+    return fail(SSM_ERR_SHAPE, "SSM_LAM_SIGMOID applies to the trapezoidal form only");
   const int64_t n_x = d.batch * d.seqlen * d.nheads * d.headdim;
   const int64_t n_dt = d.batch * d.seqlen * d.nheads;
   const int64_t n_bc = d.batch * d.seqlen * d.ngroups * d.dstate;
   const int64_t n_h = d.batch * d.nheads * d.headdim * d.dstate;
+  const int64_t n_xp = d.batch * d.nheads * d.headdim, n_bp = d.batch * d.ngroups * d.dstate;
   if (n_x > 0 && (!x || !dt || !dy || !dx || !ddt)) return fail(SSM_ERR_NULL, "x, dt, dy, dx and ddt are required");
   if (n_bc > 0 && (!B || !C || !dB || !dC)) return fail(SSM_ERR_NULL, "B, C, dB and dC are required");
   if (d.nheads > 0 && (!A || !dA)) return fail(SSM_ERR_NULL, "A and dA are required");
   if (n_x > 0 && z && !dz) return fail(SSM_ERR_NULL, "dz is required when z is given");
   if (d.nheads > 0 && D && !dD) return fail(SSM_ERR_NULL, "dD is required when D is given");
+  if (trap && n_dt > 0 && (!lam || !dlam)) return fail(SSM_ERR_NULL, "lam and dlam are required");
+  if ((x_prev == nullptr) != (B_prev == nullptr))
+    return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
+  if (x_prev && n_xp > 0 && (!dx_prev || !dB_prev))
+    return fail(SSM_ERR_NULL, "dx_prev and dB_prev are required with x_prev and B_prev");
   if (!z) dz = nullptr;
   if (!D) dD = nullptr;
+  if (!x_prev) {
+    dx_prev = nullptr;
+    dB_prev = nullptr;
+  }
   const size_t eo = dtype_size(d.out_dtype);
   if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(z, 16) || !aligned(dy, 16))
     return fail(SSM_ERR_ALIGN, "x, z, B, C and dy must be 16-byte aligned");
-  if (!aligned(dt, 2) || !aligned(dx, 2) || !aligned(ddt, 2) || !aligned(dz, 2))
-    return fail(SSM_ERR_ALIGN, "dt, dx, ddt and dz must be 2-byte aligned");
-  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4))
-    return fail(SSM_ERR_ALIGN, "A, D, dA, dB, dC and dD must be 4-byte aligned");
+  if (!aligned(dt, 2) || !aligned(lam, 2) || !aligned(x_prev, 2) || !aligned(B_prev, 2) || !aligned(dx, 2) ||
+      !aligned(ddt, 2) || !aligned(dlam, 2) || !aligned(dz, 2) || !aligned(dx_prev, 2))
+    return fail(SSM_ERR_ALIGN, "bf16 pointers must be 2-byte aligned");
+  if (!aligned(A, 4) || !aligned(D, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dC, 4) || !aligned(dD, 4) ||
+      !aligned(dB_prev, 4))
+    return fail(SSM_ERR_ALIGN, "A, D, dA, dB, dC, dD and dB_prev must be 4-byte aligned");
   if (!aligned(h0, 16) || !aligned(dh_last, 16) || !aligned(dh0, 16))
     return fail(SSM_ERR_ALIGN, "h0, dh_last and dh0 must be 16-byte aligned");
-  const Span ins[] = {{x, n_x * 2ull},       {dt, n_dt * 2ull},   {z, n_x * 2ull},        {B, n_bc * 2ull},
-                      {C, n_bc * 2ull},      {A, d.nheads * 4ull}, {D, d.nheads * 4ull}, {h0, n_h * 4ull},
-                      {dy, n_x * eo},        {dh_last, n_h * 4ull}, {d.dt_bias, d.nheads * 4ull}};
-  const Span outs[] = {{dx, n_x * 2ull},     {ddt, n_dt * 2ull},  {dz, n_x * 2ull},       {dA, d.nheads * 4ull},
-                       {dB, n_bc * 4ull},    {dC, n_bc * 4ull},   {dD, d.nheads * 4ull},  {dh0, n_h * 4ull}};
+  const Span ins[] = {{x, n_x * 2ull},       {dt, n_dt * 2ull},    {z, n_x * 2ull},        {B, n_bc * 2ull},
+                      {C, n_bc * 2ull},      {A, d.nheads * 4ull}, {D, d.nheads * 4ull},  {h0, n_h * 4ull},
+                      {dy, n_x * eo},        {dh_last, n_h * 4ull}, {d.dt_bias, d.nheads * 4ull},
+                      {lam, n_dt * 2ull},    {x_prev, n_xp * 2ull}, {B_prev, n_bp * 2ull}};
+  const Span outs[] = {{dx, n_x * 2ull},     {ddt, n_dt * 2ull},   {dz, n_x * 2ull},       {dA, d.nheads * 4ull},
+                       {dB, n_bc * 4ull},    {dC, n_bc * 4ull},    {dD, d.nheads * 4ull},  {dh0, n_h * 4ull},
+                       {dlam, n_dt * 2ull},  {dx_prev, n_xp * 2ull}, {dB_prev, n_bp * 4ull}};
   for (const Span &o : outs) {
     for (const Span &i : ins)
       if (overlap(o, i)) return fail(SSM_ERR_SHAPE, "a gradient output overlaps an input");
     for (const Span &o2 : outs)
       if (&o != &o2 && overlap(o, o2)) return fail(SSM_ERR_SHAPE, "two gradient outputs overlap");
   }
-  if (n_bc / 256 >= kMaxGridX) return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * ngroups * dstate exceeds the grid limit");
+  if (n_bc / 256 >= kMaxGridX || n_dt / 256 >= kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * (ngroups * dstate or nheads) exceeds the grid limit");
   const SsdBwdWorkspace wl = ssd_bwd_layout(&d);
   if (d.batch * d.nheads > kMaxGridX / 2 ||
       (d.batch > 0 && wl.nchunks > 0 && d.nheads / wl.hpw > kMaxGridX / d.batch / wl.nchunks))
@@ -687,6 +714,7 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   p.dh_last = dh_last;
   p.dt_bias = d.dt_bias;
   p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.lam_sigmoid = (d.flags & SSM_LAM_SIGMOID) ? 1 : 0;
   p.dx = dx;
   p.ddt = ddt;
   p.dz = dz;
@@ -695,14 +723,27 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   p.dC = dC;
   p.dD = dD;
   p.dh0 = dh0;
+  p.lam = trap ? lam : nullptr;
+  p.x_prev = trap ? x_prev : nullptr;
+  p.B_prev = trap ? B_prev : nullptr;
+  p.dlam = dlam;
+  p.dx_prev = dx_prev;
+  p.dB_prev = dB_prev;
   uint8_t *ws = static_cast<uint8_t *>(d.workspace);
   const size_t st = SsdBwdWorkspace::up(2 * wl.state), sc = SsdBwdWorkspace::up(4 * wl.per_bhc);
+  const size_t sb = SsdBwdWorkspace::up(4 * wl.bp), ss = SsdBwdWorkspace::up(4 * wl.steps);
+  const size_t sh = SsdBwdWorkspace::up(4 * wl.bh);
   p.ws_Sp = reinterpret_cast<uint16_t *>(ws);
   p.ws_dSp = reinterpret_cast<uint16_t *>(ws + st);
   p.ws_dApart = reinterpret_cast<float *>(ws + 2 * st);
   p.ws_dDpart = reinterpret_cast<float *>(ws + 2 * st + sc);
   p.ws_dBp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc);
-  p.ws_dCp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + SsdBwdWorkspace::up(4 * wl.bp));
+  p.ws_dCp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + sb);
+  p.ws_dsc = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + 2 * sb);
+  p.ws_dga = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + 2 * sb + ss);
+  p.ws_rc = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + 2 * sb + 2 * ss);
+  p.ws_dw0 = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + 2 * sb + 3 * ss);
+  p.ws_dBpp = reinterpret_cast<float *>(ws + 2 * st + 2 * sc + 2 * sb + 3 * ss + sh);
   p.nchunks = wl.nchunks;
   p.hpw = wl.hpw;
   p.batch = d.batch;
@@ -713,6 +754,22 @@ int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const 
   const hipError_t e = ssm::launch_ssd_bwd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssd backward launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int ssd_bwd(const void *x, const void *dt, const float *A, const void *B, const void *C, const float *D,
+            const void *z, const float *h0, const void *dy, const float *dh_last, void *dx, void *ddt, float *dA,
+            float *dB, float *dC, float *dD, void *dz, float *dh0, const ssd_dims_t *dims, void *stream) {
+  return ssd_bwd_run(x, dt, nullptr, A, B, C, D, z, h0, nullptr, nullptr, dy, dh_last, dx, ddt, nullptr, dA, dB, dC,
+                     dD, dz, dh0, nullptr, nullptr, dims, stream, false);
+}
+
+int ssd_trap_bwd(const void *x, const void *dt, const void *lam, const float *A, const void *B, const void *C,
+                 const float *D, const void *z, const float *h0, const void *x_prev, const void *B_prev,
+                 const void *dy, const float *dh_last, void *dx, void *ddt, void *dlam, float *dA, float *dB,
+                 float *dC, float *dD, void *dz, float *dh0, void *dx_prev, float *dB_prev, const ssd_dims_t *dims,
+                 void *stream) {
+  return ssd_bwd_run(x, dt, lam, A, B, C, D, z, h0, x_prev, B_prev, dy, dh_last, dx, ddt, dlam, dA, dB, dC, dD, dz,
+                     dh0, dx_prev, dB_prev, dims, stream, true);
 }
 
 // ---------------------------------------------------------------------------

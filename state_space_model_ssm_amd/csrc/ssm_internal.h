@@ -117,6 +117,18 @@ struct SsdBwdParams {
   // head block), the dB and dC terms [batch][seqlen][nheads / hpw][dstate].
   uint16_t *ws_Sp, *ws_dSp;
   float *ws_dApart, *ws_dDpart, *ws_dBp, *ws_dCp;
+  // Trapezoidal form (lam non-null): lam (batch, seqlen, nheads) and the
+  // token before the sequence x_prev (batch, nheads, headdim), B_prev (batch,
+  // ngroups, dstate), bf16, nullable together; outputs dlam (bf16), dx_prev
+  // (bf16) and dB_prev (float32) with them.  Workspace per (batch, step,
+  // head): the gradients of the step's two input weights (scale_s and
+  // gamma_s) and the suffix sum of the log-decay gradient; per (batch, head)
+  // the gradient of the previous-token weight and the dB_prev terms.
+  const void *lam, *x_prev, *B_prev;
+  int32_t lam_sigmoid;
+  void *dlam, *dx_prev;
+  float *dB_prev;
+  float *ws_dsc, *ws_dga, *ws_rc, *ws_dw0, *ws_dBpp;
   int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
   int32_t hpw;                        // heads per chunk-kernel workgroup
 };

@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 21, declared
+    assert len(declared) == 22, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -462,7 +462,8 @@ def test_ssd_bwd_rules():
     b, L, H, N, P = d.batch, d.seqlen, d.nheads, d.dstate, d.headdim
     up = lambda v: (v + 255) // 256 * 256
     K, hpw = (L + 63) // 64, 1   # 2 x 2 x 4 heads: too few workgroups to share heads
-    assert need.value == 2 * up(2 * b * H * K * P * N) + 2 * up(4 * b * H * K) + 2 * up(4 * b * L * (H // hpw) * N)
+    assert need.value == (2 * up(2 * b * H * K * P * N) + 2 * up(4 * b * H * K) + 2 * up(4 * b * L * (H // hpw) * N)
+                          + 3 * up(4 * b * L * H) + up(4 * b * H) + up(4 * b * H * N))
     assert call(d) == -6                                        # workspace missing
     d.workspace, d.workspace_bytes = ptr(11), need.value
     assert call(d, dx=None) == -1
@@ -476,5 +477,39 @@ def test_ssd_bwd_rules():
     d2 = _sdims(flags=2)
     d2.workspace, d2.workspace_bytes = ptr(11), need.value
     assert call(d2) == -2                                       # no trapezoid flag here
+    d3 = _sdims(headdim=32)
+    assert call(d3) == -5
+
+
+def test_ssd_trap_bwd_rules():
+    """ssd_trap_bwd: the backward's checks plus lam, the previous token and
+    its gradients, before any HIP call."""
+    lib = ssm.lib()
+    G = 1 << 28
+    ptr = lambda k: FAKE + k * G
+
+    def call(d, **kw):
+        a = dict(x=ptr(0), dt=ptr(1), lam=ptr(2), A=ptr(3), B=ptr(4), C=ptr(5), D=None, z=None, h0=None, xp=None,
+                 bp=None, dy=ptr(6), dhl=None, dx=ptr(7), ddt=ptr(8), dlam=ptr(9), dA=ptr(10), dB=ptr(11),
+                 dC=ptr(12), dD=None, dz=None, dh0=None, dxp=None, dbp=None)
+        a.update(kw)
+        return lib.ssd_trap_bwd(a["x"], a["dt"], a["lam"], a["A"], a["B"], a["C"], a["D"], a["z"], a["h0"], a["xp"],
+                                a["bp"], a["dy"], a["dhl"], a["dx"], a["ddt"], a["dlam"], a["dA"], a["dB"], a["dC"],
+                                a["dD"], a["dz"], a["dh0"], a["dxp"], a["dbp"], ctypes.byref(d), None)
+
+    d = _sdims()
+    need = ctypes.c_size_t(0)
+    assert lib.ssd_bwd_workspace_size(ctypes.byref(d), ctypes.byref(need)) == 0
+    d.workspace, d.workspace_bytes = ptr(13), need.value
+    assert call(d, lam=None) == -1                              # lam required
+    assert call(d, dlam=None) == -1                             # dlam required
+    assert call(d, xp=ptr(14)) == -1                            # x_prev without B_prev
+    assert call(d, xp=ptr(14), bp=ptr(15)) == -1                # previous token without its gradients
+    assert call(d, xp=ptr(14), bp=ptr(15), dxp=ptr(16), dbp=ptr(2)) == -2   # dB_prev overlaps lam
+    assert call(d, lam=ptr(2) + 1) == -4                        # lam alignment
+    d2 = _sdims(flags=2)                                        # SSM_LAM_SIGMOID is accepted here
+    d2.workspace, d2.workspace_bytes = ptr(13), need.value
+    assert lib.ssd_bwd(ptr(0), ptr(1), ptr(3), ptr(4), ptr(5), None, None, None, ptr(6), None, ptr(7), ptr(8),
+                       ptr(10), ptr(11), ptr(12), None, None, None, ctypes.byref(d2), None) == -2
     d3 = _sdims(headdim=32)
     assert call(d3) == -5

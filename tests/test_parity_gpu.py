@@ -1190,3 +1190,113 @@ def test_ssd_backward_head_blocks(case):
     for k in ("dA", "dD"):
         ref[k] = None if parts[0][k] is None else np.sum([q[k] for q in parts], axis=0)
     _check_ssd_bwd(g, ref, "head blocks " + repr(case[:5]))
+
+
+# ---------------------------------------------------------------------------
+# Trapezoidal SSD backward
+# ---------------------------------------------------------------------------
+
+TRAP_BWD_KEYS = SSD_BWD_KEYS + ("dlam", "dx_prev", "dB_prev")
+
+TRAP_BWD_CASES = [
+    # (batch, L, H, N, G, has_z, h0 and dh_last, previous token, dy dtype, raw dt and lam)
+    (1, 64, 1, 128, 1, False, False, False, "bf16", False),
+    (2, 203, 4, 128, 2, True, True, True, "bf16", False),     # ragged chunk, groups, gate, previous token
+    (1, 1, 2, 128, 1, True, True, True, "f32", False),        # L = 1 with a previous token
+    (3, 130, 3, 64, 1, False, False, True, "f32", True),      # dstate 64, softplus and sigmoid
+    (2, 67, 4, 64, 4, True, True, False, "bf16", True),
+    (16, 130, 64, 128, 2, True, True, True, "bf16", False),   # two heads per block
+]
+
+
+def _trap_bwd_case(case, seed):
+    batch, L, H, N, G, has_z, with_h, prev, dyt, raw = case
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip="normal", seed=seed)
+    inp = make_ssd_inputs(s)
+    lam = make_lam((batch, L, H), seed=seed + 1)
+    kw, okw = {}, {}
+    if raw:
+        dtr, bias = make_raw_step((batch, L, H), H, seed + 2, "bf16")
+        inp = dict(inp, dt=dtr)
+        lam = make_state((batch, L, H), seed=seed + 3).to(torch.bfloat16)
+        kw = dict(dt_softplus=True, dt_bias=bias, lam_sigmoid=True)
+    h0 = make_state((batch, H, 64, N), seed=seed + 4, scale=0.5) if with_h else None
+    dhl = make_state((batch, H, 64, N), seed=seed + 5, scale=0.5) if with_h else None
+    xp = make_state((batch, H, 64), seed=seed + 6).to(torch.bfloat16) if prev else None
+    bp = (make_state((batch, G, N), seed=seed + 7) / math.sqrt(N)).to(torch.bfloat16) if prev else None
+    dy = make_state((batch, L, H, 64), seed=seed + 8).to(DT[dyt])
+    return inp, lam, h0, dhl, xp, bp, dy, kw
+
+
+def _trap_bwd_gpu(inp, lam, h0, dhl, xp, bp, dy, kw):
+    g = ssm.ssd_trap_bwd(_dev(inp["x"]), _dev(inp["dt"]), _dev(lam), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                         _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy), h0=_dev(h0), dh_last=_dev(dhl), x_prev=_dev(xp),
+                         B_prev=_dev(bp), **{k: (_dev(v) if torch.is_tensor(v) else v) for k, v in kw.items()})
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.float().cpu()) for k, v in g.items()}
+
+
+def _trap_bwd_ref(inp, lam, h0, dhl, xp, bp, dy, kw):
+    batch = inp["x"].shape[0]
+    sl = lambda t, b: None if t is None else t[b:b + 1]
+
+    def one(b):
+        r = {k: (None if v is None else (v[b:b + 1] if k in ("x", "dt", "B", "C", "z") else v)) for k, v in inp.items()}
+        return oracle.ssd_trap_bwd(r["x"], r["dt"], sl(lam, b), r["A"], r["B"], r["C"], r["D"], r["z"], sl(h0, b),
+                                   sl(xp, b), sl(bp, b), sl(dy, b), sl(dhl, b), **kw)
+
+    with ThreadPoolExecutor(max_workers=min(batch, 16)) as ex:
+        parts = list(ex.map(one, range(batch)))
+    ref = {k: (None if parts[0][k] is None else np.concatenate([q[k] for q in parts]))
+           for k in ("dx", "ddt", "dlam", "dB", "dC", "dz", "dh0", "dx_prev", "dB_prev")}
+    for k in ("dA", "dD"):
+        ref[k] = None if parts[0][k] is None else np.sum([q[k] for q in parts], axis=0)
+    return ref
+
+
+def _check_trap_bwd(g, ref, label=""):
+    errs = {}
+    for k in TRAP_BWD_KEYS:
+        if ref[k] is None:
+            assert g.get(k) is None, k
+            continue
+        errs[k] = rel_err(g[k], ref[k])
+    if label:
+        print(f"{label}: whole-tensor rel err " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    for k, err in errs.items():
+        assert err <= TOL_BF16, (k, err)
+
+
+@pytest.mark.parametrize("case", TRAP_BWD_CASES, ids=lambda c: "b{}l{}h{}n{}g{}_z{}_h{}_prev{}_{}_raw{}".format(*c))
+def test_ssd_trap_backward(case):
+    args = _trap_bwd_case(case, 8700 + zlib.crc32(repr(case).encode()) % 1000)
+    _check_trap_bwd(_trap_bwd_gpu(*args), _trap_bwd_ref(*args), "trapezoidal backward " + repr(case[:5]))
+
+
+def test_ssd_trap_backward_lam_one_matches_ssd_backward():
+    """lam = 1, no previous token: the trapezoidal backward's gradients equal
+    the scalar-decay backward's (the kernels take the same products)."""
+    s = SsdShape(2, 150, 4, 64, 128, 2, 64, "bf16", has_z=True, dskip="normal", seed=8800)
+    inp = make_ssd_inputs(s)
+    dy = make_state((2, 150, 4, 64), seed=8801).to(torch.bfloat16)
+    dhl = make_state((2, 4, 64, 128), seed=8802, scale=0.5)
+    one = torch.ones((2, 150, 4), dtype=torch.bfloat16)
+    gt = _trap_bwd_gpu(inp, one, None, dhl, None, None, dy, {})
+    gs = _ssd_bwd_pair(inp, dy, None, dhl)
+    for k in SSD_BWD_KEYS:
+        assert rel_err(gt[k], gs[k].numpy()) <= 1e-5, k
+
+
+def test_ssd_trap_backward_named_workload_full_size():
+    """The trapezoidal SSD on the SSD workload's shapes (batch 32, 256 steps,
+    32 heads x 64, dstate 128) with a previous token, every gradient over the
+    whole tensor against the oracle."""
+    w = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(w)
+    lam = make_lam((w.batch, w.seqlen, w.nheads), seed=8900)
+    xp = make_state((w.batch, w.nheads, w.headdim), seed=8901).to(torch.bfloat16)
+    bp = (make_state((w.batch, w.ngroups, w.dstate), seed=8902) / math.sqrt(w.dstate)).to(torch.bfloat16)
+    dy = make_state((w.batch, w.seqlen, w.nheads, w.headdim), seed=8903).to(torch.bfloat16)
+    dhl = make_state((w.batch, w.nheads, w.headdim, w.dstate), seed=8904, scale=0.5)
+    args = (inp, lam, None, dhl, xp, bp, dy, {})
+    _check_trap_bwd(_trap_bwd_gpu(*args), _trap_bwd_ref(*args), "ssd_trap_32x256_h32p64n128_bf16 backward")
