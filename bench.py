@@ -315,7 +315,7 @@ def main():
 
 def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, make_ssd_inputs):
     """The scan backward on the long-prefill and large-channel workloads; the
-    trapezoidal SSD, the SSD backward, the rotary step on B and C and the SSD on the rotated
+    trapezoidal SSD, both SSD backwards, the rotary step on B and C and the SSD on the rotated
     (per-head) B and C, on the SSD workload's shapes."""
     import torch
     from state_space_model_ssm_amd.synth import make_lam
@@ -369,7 +369,15 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
                                                   "mfma_model_us": round(flops / (BF16_MFMA_TFLOPS * 1e12) * 1e6, 2),
                                                   "min_bytes_model_us": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                                                   "workspace_MB": round(ws.numel() / 1e6, 1)}
-    del dy, ws
+    # The trapezoidal backward on the same shapes (with the token before the
+    # sequence).
+    xp = torch.randn(w.batch, w.nheads, w.headdim, generator=g).to(torch.bfloat16).to(dev)
+    bp = (torch.randn(w.batch, w.ngroups, w.dstate, generator=g) / w.dstate ** 0.5).to(torch.bfloat16).to(dev)
+    ms, _ = time_calls(lambda: ssm.ssd_trap_bwd(d["x"], d["dt"], lam, d["A"], d["B"], d["C"], d["D"], d["z"], dy=dy,
+                                                x_prev=xp, B_prev=bp, workspace=ws, stream=stream), 20, 3)
+    out["ssd_trap_backward_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                                       "mfma_model_us": round(flops / (BF16_MFMA_TFLOPS * 1e12) * 1e6, 2)}
+    del dy, ws, xp, bp
     # The rotary step on the same shapes (one set of angles for all heads),
     # then the SSD on the rotated, per-head B and C.
     from state_space_model_ssm_amd.synth import make_theta
