@@ -398,6 +398,21 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
                                                    h_last=h, stream=stream), 50, 5)
     out["ssd_rotated_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
                                                  "ngroups": w.nheads}
+    unfused = out["rope_bc_32x256_h32n128_bf16"]["ms"] + ms
+    # The same rotated prefill fused in one kernel (the rotated B and C stay in
+    # LDS): bytes are the plain SSD's plus theta and the angles.
+    nbytes = w.metric_bytes() + w.hlast_bytes() + theta.numel() * 2 + ang.numel() * 4
+    ms, _ = time_calls(lambda: ssm.ssd_rope_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], theta, d["D"],
+                                                        d["z"], angle_last=ang, y=y, h_last=h, stream=stream), 50, 5)
+    out["ssd_rope_fused_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),
+                                                    "hbm_GB/s": round(nbytes / ms / 1e6, 1),
+                                                    "unfused_ms": round(unfused, 5)}
+    bl = torch.empty((w.batch, w.nheads, w.dstate), dtype=torch.bfloat16, device=dev)
+    ms, _ = time_calls(lambda: ssm.ssd_rope_trap_chunked_fwd(d["x"], d["dt"], lam, d["A"], d["B"], d["C"], theta,
+                                                             d["D"], d["z"], angle_last=ang, B_last=bl, y=y,
+                                                             h_last=h, stream=stream), 50, 5)
+    out["ssd_rope_trap_fused_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5),
+                                                         "Gelem/s": round(w.elements / ms / 1e6, 2)}
     return out
 
 

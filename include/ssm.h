@@ -328,6 +328,57 @@ SSM_API int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam,
                          float *h_last, const ssd_dims_t *dims, void *stream);
 
 /*
+ * The SSD with the rotary step on B and C fused in (Mamba-3's complex-valued
+ * state): the same result as ssm_rope_bc (per-head rotated B and C, bf16)
+ * followed by ssd_chunked_fwd on them, without the rotated B and C ever being
+ * stored.  For every batch b, head h and state pair k < N/2
+ *   phi_t[k] = angle0[b,h,k] - sum_{s <= t} dt_s theta_s[b,h',k]
+ *   (B_rot[k], B_rot[k + N/2]) = (B[k] cos phi - B[k + N/2] sin phi,
+ *                                 B[k] sin phi + B[k + N/2] cos phi),  C alike,
+ * and the SSD of ssd_chunked_fwd runs on B_rot, C_rot (rounded to bf16) of
+ * head h.
+ *   [Mamba-3 NKI], "How it works", Phase 1 (the rotation) then Phase 2 (the
+ *     chunked SSD); the pairing (k, k + N/2) and the direction are this
+ *     library's reading, as for ssm_rope_bc.
+ * Arguments, layouts and supported sizes are those of ssd_chunked_fwd, plus
+ *   theta       : (batch, seqlen, theta_heads, dstate / 2) bf16, 16-byte
+ *                 aligned; theta_heads is 1 (shared by every head, h' = 0)
+ *                 or nheads (h' = h);
+ *   angle0      : (batch, nheads, dstate / 2) float32, nullable (zero);
+ *   angle_last  : (batch, nheads, dstate / 2) float32, nullable; the angle
+ *                 after the last step reduced to [-pi, pi]; may be exactly
+ *                 angle0 (updated in place);
+ *   B_last      : (batch, nheads, dstate) bf16, 16-byte aligned, nullable:
+ *                 the rotated B of the last step (the previous-token input of
+ *                 a trapezoidal continuation); untouched when seqlen is 0.
+ * The angle is carried from chunk to chunk in float64 and summed within a
+ * chunk in float32, in revolutions.  The SSD (dt_softplus included) is
+ * computed as in ssd_chunked_fwd; with SSM_DT_SOFTPLUS the angles use the
+ * mapped step.  Outputs must not overlap inputs or each other (angle_last ==
+ * angle0, h_last == h0 excepted).
+ */
+SSM_API int ssd_rope_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                                 const void *theta, int64_t theta_heads, const float *angle0, const float *D,
+                                 const void *z, const float *h0, void *y, float *h_last, float *angle_last,
+                                 void *B_last, const ssd_dims_t *dims, void *stream);
+
+/*
+ * The trapezoidal form of ssd_rope_chunked_fwd: ssm_rope_bc followed by
+ * ssd_trap_chunked_fwd on the per-head rotated B and C, fused.
+ *   [Mamba-3 NKI], "How it works", Phases 0-2, and "Kernel details",
+ *     mamba3_siso_ssd_kernel (the single-SSD form, as ssd_trap_chunked_fwd).
+ * Arguments as ssd_rope_chunked_fwd plus lam, x_prev and B_prev as
+ * ssd_trap_chunked_fwd, except that B_prev is per head, (batch, nheads,
+ * dstate) bf16, and already rotated (the B_last of the call before, or the
+ * rotated B that ssm_rope_bc gave for the previous token).
+ */
+SSM_API int ssd_rope_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A,
+                                      const void *B, const void *C, const void *theta, int64_t theta_heads,
+                                      const float *angle0, const float *D, const void *z, const float *h0,
+                                      const void *x_prev, const void *B_prev, void *y, float *h_last,
+                                      float *angle_last, void *B_last, const ssd_dims_t *dims, void *stream);
+
+/*
  * Workspace ssd_bwd and ssd_trap_bwd need for `dims`.  With K =
  * ceil(seqlen / 64) chunks and the chunk kernel's hpw heads per workgroup (a
  * function of the sizes, up to 8): two bf16 state matrices per (batch, head,

@@ -17,7 +17,8 @@ from typing import Optional
 
 __all__ = [
     "SSM_F32", "SSM_BF16", "SSM_DT_SOFTPLUS", "SSM_LAM_SIGMOID", "SsmError", "ScanDims", "SsdDims", "lib", "library_path",
-    "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "scan_step", "ssd_step",
+    "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "ssd_rope_chunked_fwd",
+    "ssd_rope_trap_chunked_fwd", "scan_step", "ssd_step",
     "ssd_trap_step", "ssd_bwd", "ssd_bwd_workspace_size",
     "rope_bc", "RopeDims",
     "scan_workspace_size",
@@ -104,6 +105,11 @@ def lib():
         L.ssd_chunked_fwd.argtypes = [vp] * 10 + [ctypes.POINTER(SsdDims), vp]
         L.ssd_trap_chunked_fwd.argtypes = [vp] * 13 + [ctypes.POINTER(SsdDims), vp]
         L.ssd_trap_chunked_fwd.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        L.ssd_rope_chunked_fwd.argtypes = [vp] * 6 + [i64] + [vp] * 8 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_rope_chunked_fwd.restype = i32
+        L.ssd_rope_trap_chunked_fwd.argtypes = [vp] * 7 + [i64] + [vp] * 10 + [ctypes.POINTER(SsdDims), vp]
+        L.ssd_rope_trap_chunked_fwd.restype = i32
         L.ssd_chunked_fwd.restype = i32
         L.ssd_workspace_size.argtypes = [ctypes.POINTER(SsdDims), ctypes.POINTER(ctypes.c_size_t)]
         L.ssd_workspace_size.restype = i32
@@ -394,9 +400,12 @@ def ssd_workspace_size(dims: SsdDims) -> int:
 def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, out_dtype=None,
                     return_h_last: bool = True, y=None, h_last=None, stream=None,
                     dt_softplus: bool = False, dt_bias=None, lam_sigmoid: bool = False,
-                    x_prev=None, B_prev=None):
+                    x_prev=None, B_prev=None, rope=None):
     """Scalar-decay chunked SSD forward, plain (lam None: ``ssd_chunked_fwd``)
     or trapezoidal (``ssd_trap_chunked_fwd``). Returns ``(y, h_last)``.
+    With ``rope`` (a dict: theta, angle0, angle_last, return_angle_last,
+    B_last, return_B_last) the fused rotary forms ``ssd_rope_chunked_fwd`` /
+    ``ssd_rope_trap_chunked_fwd``; returns ``(y, h_last, angle_last, B_last)``.
 
     x, z: (batch, L, H, P) bf16; dt: (batch, L, H) bf16; A, D: (H,) float32;
     B, C: (batch, L, G, N) bf16; h0: (batch, H, P, N) float32 initial state
@@ -429,17 +438,44 @@ def _ssd_call(x, dt, lam, A, B, C, D=None, z=None, *, h0=None, chunk: int = 64, 
     if x_prev is not None:
         if lam is None:
             raise ValueError("x_prev and B_prev belong to the trapezoidal form")
-        G = B.shape[2]
+        G = H if rope is not None else B.shape[2]  # the rotary forms take the rotated B per head
         if x_prev.shape != (batch, H, P) or B_prev.shape != (batch, G, N) or x_prev.dtype != x.dtype or \
                 B_prev.dtype != x.dtype:
-            raise ValueError("x_prev must be (batch, nheads, headdim) and B_prev (batch, ngroups, dstate), "
-                             "in the dtype of x")
+            raise ValueError("x_prev must be (batch, nheads, headdim) and B_prev (batch, %s, dstate), "
+                             "in the dtype of x" % ("nheads" if rope is not None else "ngroups"))
     dims = _ssd_dims(x, B, chunk, in_code, out_code)
     _phase0(dims, H, dt_softplus, dt_bias, lam_sigmoid)
+    if rope is not None:
+        theta = rope["theta"]
+        TH = theta.shape[2] if theta.dim() == 4 else -1
+        if theta.dtype != x.dtype or theta.shape != (batch, L, TH, N // 2) or TH not in (1, H):
+            raise ValueError("theta must be (batch, L, 1 or nheads, dstate / 2) in the dtype of x")
+        angle0 = rope.get("angle0")
+        if angle0 is not None and (angle0.dtype != torch.float32 or angle0.shape != (batch, H, N // 2)):
+            raise ValueError("angle0 must be float32 (batch, nheads, dstate / 2)")
     with _alloc_on(stream):
         y = _out(y, (batch, L, H, P), out_dt, x, "y")
         if h_last is not None or return_h_last:
             h_last = _out(h_last, (batch, H, P, N), torch.float32, x, "h_last")
+        if rope is not None:
+            angle_last, B_last = rope.get("angle_last"), rope.get("B_last")
+            if angle_last is not None or rope.get("return_angle_last", True):
+                angle_last = _out(angle_last, (batch, H, N // 2), torch.float32, x, "angle_last")
+            if B_last is not None or rope.get("return_B_last", False):
+                B_last = _out(B_last, (batch, H, N), x.dtype, x, "B_last")
+    if rope is not None:
+        if lam is None:
+            rc = lib().ssd_rope_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(theta), TH,
+                                            _ptr(angle0), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
+                                            _ptr(angle_last), _ptr(B_last), ctypes.byref(dims), _stream(stream))
+        else:
+            rc = lib().ssd_rope_trap_chunked_fwd(_ptr(x), _ptr(dt), _ptr(lam), _ptr(A), _ptr(B), _ptr(C),
+                                                 _ptr(theta), TH, _ptr(angle0), _ptr(D), _ptr(z), _ptr(h0),
+                                                 _ptr(x_prev), _ptr(B_prev), _ptr(y), _ptr(h_last),
+                                                 _ptr(angle_last), _ptr(B_last), ctypes.byref(dims),
+                                                 _stream(stream))
+        _check(rc)
+        return y, h_last, angle_last, B_last
     if lam is None:
         rc = lib().ssd_chunked_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                    _ptr(h0), _ptr(y), _ptr(h_last), ctypes.byref(dims), _stream(stream))
@@ -553,6 +589,31 @@ def ssd_trap_chunked_fwd(x, dt, lam, A, B, C, D=None, z=None, **kw):
     the token before the sequence, when the call continues one.  Otherwise as
     ``ssd_chunked_fwd``. Returns ``(y, h_last)``."""
     return _ssd_call(x, dt, lam, A, B, C, D, z, **kw)
+
+
+def ssd_rope_chunked_fwd(x, dt, A, B, C, theta, D=None, z=None, *, angle0=None, angle_last=None,
+                         return_angle_last: bool = True, B_last=None, return_B_last: bool = False, **kw):
+    """The SSD with the rotary step on B and C fused in
+    (``ssd_rope_chunked_fwd``): ``rope_bc`` then ``ssd_chunked_fwd`` on the
+    per-head rotated B and C, which are never stored.  theta: (batch, L, TH,
+    N / 2) bf16 with TH 1 or H; angle0, angle_last: (batch, H, N / 2) float32
+    (angle_last may be angle0, updated in place); B_last: (batch, H, N) bf16,
+    the last step's rotated B.  Other arguments as ``ssd_chunked_fwd``.
+    Returns ``(y, h_last, angle_last, B_last)`` (None for what was not asked for)."""
+    rope = {"theta": theta, "angle0": angle0, "angle_last": angle_last, "return_angle_last": return_angle_last,
+            "B_last": B_last, "return_B_last": return_B_last}
+    return _ssd_call(x, dt, None, A, B, C, D, z, rope=rope, **kw)
+
+
+def ssd_rope_trap_chunked_fwd(x, dt, lam, A, B, C, theta, D=None, z=None, *, angle0=None, angle_last=None,
+                              return_angle_last: bool = True, B_last=None, return_B_last: bool = False, **kw):
+    """The trapezoidal form of ``ssd_rope_chunked_fwd``
+    (``ssd_rope_trap_chunked_fwd``): x_prev (batch, H, P) and B_prev (batch, H,
+    N, the previous token's rotated B, e.g. the B_last of the call before).
+    Returns ``(y, h_last, angle_last, B_last)``."""
+    rope = {"theta": theta, "angle0": angle0, "angle_last": angle_last, "return_angle_last": return_angle_last,
+            "B_last": B_last, "return_B_last": return_B_last}
+    return _ssd_call(x, dt, lam, A, B, C, D, z, rope=rope, **kw)
 
 
 def scan_step(u, delta, A, B, C, D=None, z=None, *, state, out_dtype=None, y=None, stream=None,

@@ -501,9 +501,20 @@ size_t ssd_workspace_bytes(const ssd_dims_t *dims) {
   return ssd_workspace_size(dims, &bytes) == SSM_OK ? bytes : SIZE_MAX;
 }
 
+// The rotary step's arguments of the fused forms (ssd_rope_chunked_fwd,
+// ssd_rope_trap_chunked_fwd).
+struct SsdRopeArgs {
+  const void *theta;
+  int64_t theta_heads;
+  const float *angle0;
+  float *angle_last;
+  void *B_last;
+};
+
 static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, const float *A, const void *B,
                    const void *C, const float *D, const void *z, const float *h0, const void *x_prev,
-                   const void *B_prev, void *y, float *h_last, const ssd_dims_t *dims, void *stream) {
+                   const void *B_prev, void *y, float *h_last, const ssd_dims_t *dims, void *stream,
+                   const SsdRopeArgs *rope = nullptr) {
   const int rc = check_ssd_dims(dims);
   if (rc != SSM_OK) return rc;
   const ssd_dims_t &d = *dims;
@@ -529,16 +540,40 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
     return fail(SSM_ERR_NULL, "x_prev and B_prev are given together or not at all");
   if (!aligned(x_prev, 16) || !aligned(B_prev, 16))
     return fail(SSM_ERR_ALIGN, "x_prev and B_prev must be 16-byte aligned");
-  const int64_t n_xp = d.batch * d.nheads * d.headdim, n_bp = d.batch * d.ngroups * d.dstate;
+  // With the rotary step B_prev is per head (rotated by that head's angle).
+  const int64_t n_xp = d.batch * d.nheads * d.headdim;
+  const int64_t n_bp = d.batch * (rope ? d.nheads : d.ngroups) * d.dstate;
+  const int64_t n_ang = d.batch * d.nheads * (d.dstate / 2);
+  const int64_t th_heads = rope ? rope->theta_heads : 0;
+  const void *theta = rope ? rope->theta : nullptr;
+  const float *angle0 = rope ? rope->angle0 : nullptr;
+  float *angle_last = rope ? rope->angle_last : nullptr;
+  void *B_last = rope ? rope->B_last : nullptr;
+  if (rope) {
+    if (th_heads != 1 && th_heads != d.nheads)
+      return fail(SSM_ERR_SHAPE, "theta_heads must be 1 or nheads (got %lld)", (long long)th_heads);
+    if (d.batch * d.seqlen > 0 && !theta) return fail(SSM_ERR_NULL, "theta is required");
+    if (!aligned(theta, 16) || !aligned(B_last, 16)) return fail(SSM_ERR_ALIGN, "theta and B_last must be 16-byte aligned");
+    if (!aligned(angle0, 4) || !aligned(angle_last, 4)) return fail(SSM_ERR_ALIGN, "angles must be 4-byte aligned");
+  }
   const Span ins[] = {{x, n_x * 2ull},  {dt, n_dt * 2ull},     {z, n_x * 2ull},
                       {B, n_bc * 2ull}, {C, n_bc * 2ull},     {A, d.nheads * 4ull},
                       {D, d.nheads * 4ull}, {lam, n_dt * 2ull}, {d.dt_bias, d.nheads * 4ull},
-                      {x_prev, n_xp * 2ull}, {B_prev, n_bp * 2ull}};
+                      {x_prev, n_xp * 2ull}, {B_prev, n_bp * 2ull},
+                      {theta, d.batch * d.seqlen * th_heads * (d.dstate / 2) * 2ull}, {angle0, n_ang * 4ull}};
   const Span sy{y, n_x * eo}, sh{h_last, n_h * 4ull}, s0{h0, n_h * 4ull};
-  for (const Span &s : ins)
-    if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0))
+  const Span sa{angle_last, n_ang * 4ull}, sbl{B_last, d.batch * d.nheads * d.dstate * 2ull};
+  for (const Span &s : ins) {
+    if (overlap(s, sy) || overlap(s, sh) || overlap(s, s0) || overlap(s, sbl))
       return fail(SSM_ERR_SHAPE, "an output or h0 overlaps an input");
+    // angle_last may be exactly angle0 (each is read before it is written).
+    if (overlap(s, sa) && !(s.p == angle0 && angle_last == angle0))
+      return fail(SSM_ERR_SHAPE, "angle_last overlaps an input (only angle_last == angle0 is allowed)");
+  }
   if (overlap(sy, sh) || overlap(sy, s0)) return fail(SSM_ERR_SHAPE, "y overlaps h_last or h0");
+  if (overlap(sa, sy) || overlap(sa, sh) || overlap(sa, s0) || overlap(sa, sbl) || overlap(sbl, sy) ||
+      overlap(sbl, sh) || overlap(sbl, s0))
+    return fail(SSM_ERR_SHAPE, "outputs overlap each other");
   // One workgroup per (batch, head) reads its state first and writes it last.
   if (overlap(s0, sh) && h0 != h_last)
     return fail(SSM_ERR_SHAPE, "h_last overlaps h0 (only h_last == h0 is allowed)");
@@ -568,7 +603,19 @@ static int ssd_run(const void *x, const void *dt, const void *lam, bool trap, co
   p.dstate = d.dstate;
   p.ngroups = d.ngroups;
   p.chunk = d.chunk;
-  const hipError_t e = ssm::launch_ssd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (rope) {
+    ssm::SsdRopeParams rp{};
+    rp.ssd = p;
+    rp.theta = theta;
+    rp.angle0 = angle0;
+    rp.angle_last = angle_last;
+    rp.B_last = B_last;
+    rp.theta_heads = th_heads;
+    e = ssm::launch_ssd_rope(rp, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  } else {
+    e = ssm::launch_ssd(p, d.out_dtype == SSM_BF16, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "ssd launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -583,6 +630,23 @@ int ssd_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const f
                          const void *C, const float *D, const void *z, const float *h0, const void *x_prev,
                          const void *B_prev, void *y, float *h_last, const ssd_dims_t *dims, void *stream) {
   return ssd_run(x, dt, lam, true, A, B, C, D, z, h0, x_prev, B_prev, y, h_last, dims, stream);
+}
+
+int ssd_rope_chunked_fwd(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                         const void *theta, int64_t theta_heads, const float *angle0, const float *D,
+                         const void *z, const float *h0, void *y, float *h_last, float *angle_last,
+                         void *B_last, const ssd_dims_t *dims, void *stream) {
+  const SsdRopeArgs r{theta, theta_heads, angle0, angle_last, B_last};
+  return ssd_run(x, dt, nullptr, false, A, B, C, D, z, h0, nullptr, nullptr, y, h_last, dims, stream, &r);
+}
+
+int ssd_rope_trap_chunked_fwd(const void *x, const void *dt, const void *lam, const float *A, const void *B,
+                              const void *C, const void *theta, int64_t theta_heads, const float *angle0,
+                              const float *D, const void *z, const float *h0, const void *x_prev,
+                              const void *B_prev, void *y, float *h_last, float *angle_last, void *B_last,
+                              const ssd_dims_t *dims, void *stream) {
+  const SsdRopeArgs r{theta, theta_heads, angle0, angle_last, B_last};
+  return ssd_run(x, dt, lam, true, A, B, C, D, z, h0, x_prev, B_prev, y, h_last, dims, stream, &r);
 }
 
 // ---------------------------------------------------------------------------

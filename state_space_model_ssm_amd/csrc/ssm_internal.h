@@ -93,6 +93,20 @@ struct SsdParams {
 };
 
 hipError_t launch_ssd(const SsdParams &p, int out_bf16, hipStream_t stream);
+
+// The chunked SSD with the rotary step on B and C fused in (see
+// ssd_rope_chunked_fwd in include/ssm.h): one workgroup per (batch, head).
+// ssd.B_prev is per head here (batch, nheads, dstate), already rotated.
+struct SsdRopeParams {
+  SsdParams ssd;
+  const void *theta;                  // bf16 (batch, seqlen, theta_heads, dstate / 2)
+  const float *angle0;                // nullable (batch, nheads, dstate / 2)
+  float *angle_last;                  // nullable; may be angle0 itself
+  void *B_last;                       // nullable: bf16 (batch, nheads, dstate), the last step's rotated B
+  int64_t theta_heads;                // 1 or nheads
+};
+
+hipError_t launch_ssd_rope(const SsdRopeParams &p, int out_bf16, hipStream_t stream);
 // Heads one SSD workgroup takes (1, 2 or 4, at most max_hpb; they share a
 // group), and the grid size below which fewer heads per workgroup are taken
 // (the CU count).

@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 22, declared
+    assert len(declared) == 24, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -249,6 +249,44 @@ def test_ssd_trap_rules():
     assert call(lam, bp=FAKE + 0x800000) == -1      # B_prev without x_prev
     assert call(lam, xp=FAKE + 0x700008, bp=FAKE + 0x800000) == -4   # 16-byte alignment
     assert call(lam, xp=FAKE + 0x700000, bp=FAKE + 0x10000000) == -2  # B_prev inside y
+
+
+def test_ssd_rope_rules():
+    """The fused rotary SSD forms: the SSD's checks plus theta, theta_heads,
+    the angles, B_last and (trapezoidal) a per-head B_prev."""
+    d = _sdims()  # 2 x 128 steps, 4 heads, dstate 128: theta (2, 128, TH, 64) bf16
+    f = ssm.lib().ssd_rope_chunked_fwd
+    ft = ssm.lib().ssd_rope_trap_chunked_fwd
+
+    def call(theta=FAKE + 0x500000, th=1, a0=None, al=None, bl=None, dims=d, y=FAKE + 0x10000000):
+        return f(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, theta, th, a0, None,
+                 None, None, y, None, al, bl, ctypes.byref(dims), None)
+
+    assert call(th=2) == -2 and "theta_heads" in ssm.last_error()    # 1 or nheads
+    assert call(th=0) == -2
+    assert call(theta=None) == -1                                      # theta is required
+    assert call(theta=FAKE + 0x500008) == -4                           # 16-byte aligned
+    assert call(a0=FAKE + 0x600002) == -4                              # angles 4-byte aligned
+    assert call(al=FAKE + 0x600002) == -4
+    assert call(bl=FAKE + 0x700008) == -4                              # B_last 16-byte aligned
+    assert call(al=FAKE + 0x10000000 + 64) == -2                       # angle_last inside y
+    assert call(al=FAKE + 0x500000 + 64) == -2                         # angle_last inside theta
+    assert call(a0=FAKE + 0x600000, al=FAKE + 0x600000 + 8) == -2      # overlaps angle0 without being it
+    assert call(bl=FAKE + 0x300000 + 256) == -2                        # B_last inside B
+    assert call(bl=FAKE + 0x10000000) == -2                            # B_last is y
+    assert call(dims=_sdims(dstate=96)) == -5                          # the SSD's own checks still apply
+    assert call(dims=_sdims(in_dtype=0)) == -5
+
+    def tcall(lam=FAKE + 0xA00000, xp=None, bp=None):
+        return ft(FAKE, FAKE + 0x100000, lam, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000,
+                  4, None, None, None, None, xp, bp, FAKE + 0x10000000, None, None, None, ctypes.byref(d), None)
+
+    assert tcall(lam=None) == -1                                       # lam is required
+    assert tcall(xp=FAKE + 0xB00000) == -1                             # x_prev without B_prev
+    # B_prev is per head here: (2, 4, 128) bf16 = 2048 bytes, so a B_prev that
+    # starts 1024 bytes before y would fit there only as a per-group array.
+    assert tcall(xp=FAKE + 0xB00000, bp=FAKE + 0x10000000 - 1024) == -2
+    assert tcall(xp=FAKE + 0xB00000, bp=FAKE + 0xC00008) == -4         # 16-byte aligned
 
 
 def test_ssd_trap_step_rules():

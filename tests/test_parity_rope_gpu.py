@@ -267,3 +267,150 @@ def test_rope_trap_prefill_then_128_decode_steps():
     got = torch.cat(ys, dim=1).cpu()
     assert rel_err(got, ry) <= TOL_BF16, rel_err(got, ry)
     assert rel_err(state.cpu(), rh) <= TOL_BF16, rel_err(state.cpu(), rh)
+
+
+# ---------------------------------------------------------------------------
+# The fused forms: ssd_rope_chunked_fwd / ssd_rope_trap_chunked_fwd against
+# the oracle's rotary step followed by the oracle's SSD on the rotated B and
+# C (rounded to bf16, as the SSD reads them).
+# ---------------------------------------------------------------------------
+
+# (batch, L, H, G, N, theta_heads, has_z, out dtype, trap, angle0, theta scale, seed)
+FUSED_CASES = [
+    (2, 192, 8, 1, 128, 1, True, "bf16", False, False, 20.0, 201),   # three whole chunks
+    (2, 130, 4, 2, 128, 4, False, "f32", False, True, 20.0, 202),    # ragged tail of 2 steps, per-head theta
+    (3, 100, 6, 3, 64, 1, True, "bf16", False, True, 5.0, 203),      # dstate 64, ragged
+    (1, 64, 2, 1, 64, 2, False, "f32", False, False, 50.0, 204),     # one whole chunk
+    (2, 1, 4, 1, 128, 1, True, "bf16", False, True, 20.0, 205),      # a single step
+    (2, 192, 8, 1, 128, 1, True, "bf16", True, False, 20.0, 206),    # trapezoidal
+    (2, 77, 4, 2, 64, 4, False, "f32", True, True, 10.0, 207),       # trapezoidal, ragged, dstate 64
+    (1, 2048, 2, 1, 128, 1, False, "f32", False, True, 30.0, 208),   # 32 chunks: the angle carry
+]
+
+
+def _fused_inputs(batch, L, H, G, N, TH, has_z, trap, a0, scale, seed):
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip="normal", seed=seed)
+    inp = make_ssd_inputs(s)
+    inp["theta"] = make_theta((batch, L, TH, N // 2), seed + 1000, "bf16", scale)
+    inp["lam"] = make_lam((batch, L, H), seed + 2000) if trap else None
+    inp["h0"] = make_state((batch, H, 64, N), seed + 3000, 0.5)
+    rng = np.random.default_rng(seed + 4000)
+    inp["angle0"] = torch.from_numpy(rng.uniform(-4.0, 4.0, (batch, H, N // 2)).astype(np.float32)) if a0 else None
+    return inp
+
+
+def _fused_oracle(inp, trap, dt_bias=None, lam_sigmoid=False):
+    """The oracle's rotary step, then its SSD on the rotated B and C rounded to
+    bf16; dt_bias given: dt holds raw values (the step is softplus(dt + bias))."""
+    sp = dict(dt_softplus=dt_bias is not None, dt_bias=dt_bias)
+    rb, rc, ra = oracle.rope_bc(inp["dt"], inp["theta"], inp["B"], inp["C"], inp["angle0"], **sp)
+    rb16 = torch.from_numpy(rb).to(torch.bfloat16)
+    rc16 = torch.from_numpy(rc).to(torch.bfloat16)
+    if trap:
+        ry, rh = oracle.ssd_trap(inp["x"], inp["dt"], inp["lam"], inp["A"], rb16, rc16, inp["D"], inp["z"],
+                                 inp["h0"], lam_sigmoid=lam_sigmoid, **sp)
+    else:
+        ry, rh = oracle.ssd(inp["x"], inp["dt"], inp["A"], rb16, rc16, inp["D"], inp["z"], inp["h0"], **sp)
+    return ry, rh, ra, rb16
+
+
+def _fused_run(inp, trap, out_dtype, **kw):
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    batch, L, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    y = torch.full((batch, L, H, P), float("nan"), dtype=out_dtype, device="cuda")
+    hl = torch.full((batch, H, P, N), float("nan"), dtype=torch.float32, device="cuda")
+    al = torch.full((batch, H, N // 2), float("nan"), dtype=torch.float32, device="cuda")
+    bl = torch.full((batch, H, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    common = dict(angle0=d["angle0"], angle_last=al, B_last=bl, h0=d["h0"], y=y, h_last=hl, out_dtype=out_dtype)
+    common.update(kw)
+    if trap:
+        out = ssm.ssd_rope_trap_chunked_fwd(d["x"], d["dt"], d["lam"], d["A"], d["B"], d["C"], d["theta"], d["D"],
+                                            d["z"], **common)
+    else:
+        out = ssm.ssd_rope_chunked_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["theta"], d["D"], d["z"], **common)
+    torch.cuda.synchronize()
+    return [None if t is None else t.float().cpu() for t in out]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "b{}l{}h{}g{}n{}th{}_z{}_{}_trap{}_a0{}".format(*c[:10]))
+def test_fused_rope_ssd_matches_oracle(case):
+    batch, L, H, G, N, TH, has_z, out, trap, a0, scale, seed = case
+    print(f"fused rope ssd case {case}", flush=True)
+    inp = _fused_inputs(batch, L, H, G, N, TH, has_z, trap, a0, scale, seed)
+    y, hl, al, bl = _fused_run(inp, trap, DT[out])
+    ry, rh, ra, rb16 = _fused_oracle(inp, trap)
+    errs = (rel_err(y, ry), rel_err(hl, rh), angle_err(al, ra))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
+    # The last step's rotated B (bf16): within one bf16 rounding of the oracle's.
+    assert rel_err(bl, rb16[:, L - 1].float()) <= 1e-2
+
+
+def test_fused_rope_ssd_empty_sequence():
+    """seqlen 0: h_last is h0, angle_last is angle0 reduced to [-pi, pi], and
+    B_last is left untouched."""
+    inp = _fused_inputs(2, 0, 4, 1, 128, 1, False, False, True, 1.0, 209)
+    inp["angle0"] = inp["angle0"] * 3.0  # beyond [-pi, pi]
+    y, hl, al, bl = _fused_run(inp, False, torch.bfloat16)
+    assert y.numel() == 0 and torch.isnan(bl).all()
+    assert torch.equal(hl, inp["h0"])
+    assert angle_err(al, inp["angle0"].double().numpy()) <= TOL_F32
+
+
+@pytest.mark.parametrize("trap", [False, True])
+def test_fused_rope_ssd_dt_softplus(trap):
+    """Raw dt with dt_bias (and raw lam): the angles and the SSD use the mapped
+    step."""
+    inp = _fused_inputs(2, 150, 4, 1, 128, 1, True, trap, True, 10.0, 210)
+    raw, bias = make_raw_step((2, 150, 4), 4, 211, "bf16")
+    inp["dt"] = raw
+    kw = dict(dt_softplus=True, dt_bias=bias.cuda())
+    if trap:
+        inp["lam"] = torch.from_numpy(np.random.default_rng(212).standard_normal((2, 150, 4))).to(torch.bfloat16)
+        kw["lam_sigmoid"] = True
+    y, hl, al, _ = _fused_run(inp, trap, torch.bfloat16, **kw)
+    ry, rh, ra, _ = _fused_oracle(inp, trap, dt_bias=bias, lam_sigmoid=trap)
+    errs = (rel_err(y, ry), rel_err(hl, rh), angle_err(al, ra))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
+
+
+def test_fused_rope_trap_chained_in_place():
+    """A trapezoidal sequence in two fused calls: the second starts from the
+    first's h_last, angle_last (updated in place: angle_last is angle0) and
+    B_last with x of the first call's last step, and continues the oracle's
+    single pass exactly."""
+    batch, L, H, N, T1 = 2, 200, 4, 128, 120
+    inp = _fused_inputs(batch, L, H, 1, N, 1, True, True, True, 20.0, 213)
+    ry, rh, ra, _ = _fused_oracle(inp, True)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    cut = lambda t, a, b: t[:, a:b].contiguous()
+    ang = d["angle0"].clone()
+    y1, h1, _, b1 = ssm.ssd_rope_trap_chunked_fwd(
+        cut(d["x"], 0, T1), cut(d["dt"], 0, T1), cut(d["lam"], 0, T1), d["A"], cut(d["B"], 0, T1),
+        cut(d["C"], 0, T1), cut(d["theta"], 0, T1), d["D"], cut(d["z"], 0, T1), h0=d["h0"], angle0=ang,
+        angle_last=ang, return_B_last=True)
+    y2, h2, _, _ = ssm.ssd_rope_trap_chunked_fwd(
+        cut(d["x"], T1, L), cut(d["dt"], T1, L), cut(d["lam"], T1, L), d["A"], cut(d["B"], T1, L),
+        cut(d["C"], T1, L), cut(d["theta"], T1, L), d["D"], cut(d["z"], T1, L), h0=h1, angle0=ang,
+        angle_last=ang, x_prev=d["x"][:, T1 - 1].contiguous(), B_prev=b1)
+    torch.cuda.synchronize()
+    got = torch.cat([y1, y2], dim=1).float().cpu()
+    errs = (rel_err(got, ry), rel_err(h2.cpu(), rh), angle_err(ang.cpu(), ra))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
+
+
+@pytest.mark.parametrize("trap", [False, True])
+def test_fused_rope_ssd_named_workload_full_size(trap):
+    """The fused rotary SSD at the SSD workload's full size (32 x 256, 32
+    heads, headdim 64, dstate 128, bf16, one set of angles for every head),
+    every output against the oracle."""
+    s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(s)
+    inp["theta"] = make_theta((s.batch, s.seqlen, 1, s.dstate // 2), 71, "bf16", 1.0)
+    inp["lam"] = make_lam((s.batch, s.seqlen, s.nheads), 72) if trap else None
+    inp["h0"] = None
+    inp["angle0"] = None
+    y, hl, al, bl = _fused_run(inp, trap, torch.bfloat16, h0=None)
+    ry, rh, ra, rb16 = _fused_oracle(inp, trap)
+    errs = (rel_err(y, ry), rel_err(hl, rh), angle_err(al, ra), rel_err(bl, rb16[:, -1].float()))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32 and errs[3] <= 1e-2, errs
