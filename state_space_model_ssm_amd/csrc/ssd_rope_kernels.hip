@@ -8,22 +8,25 @@
 // per-head B and C.  For state pair k < N/2 (states k and k + N/2):
 //   B_rot[k]       = B[k] cos phi[k] - B[k + N/2] sin phi[k]
 //   B_rot[k + N/2] = B[k] sin phi[k] + B[k + N/2] cos phi[k],   C alike.
-// The SSD part is the chunk kernel of ssd_kernels.hip at one head per
-// workgroup; see there for the chunk products.
+// The SSD part follows the chunk kernel of ssd_kernels.hip (see there for
+// the chunk products), at one head per workgroup.
 //
-// The rotated B and C never reach HBM: each workgroup (one batch row b and
-// head h, four wavefronts) reads the group's shared B and C rows (and theta)
-// once and rotates them while it stages a chunk into LDS.  For the rotation
-// wavefront w owns the pairs k in [w N/8, (w + 1) N/8) and lane t the
-// chunk's step t: the in-chunk angle sums are prefix sums over the lanes (DPP
-// row shifts plus the row totals), in float32 revolutions, on top of the
-// angle at the chunk's start, which is carried from chunk to chunk in float64
-// (lane j of wavefront w holds pair w N/8 + j) and reduced to [-1/2, 1/2]
-// revolutions after every chunk.  The hardware sine and cosine take
-// revolutions.  Only the transposed copy of B that the state update reads is
-// dropped: that MFMA operand comes from the natural [s][n] layout through the
-// transposing LDS read (ds_read_b64_tr_b16), which keeps the LDS at ~60 KB, two
-// workgroups per CU.
+// The rotated B and C never reach HBM.  Each workgroup (batch row b, head h,
+// eight wavefronts) reads the group's shared B and C rows and theta, and per
+// chunk:
+//   - an angle pass (for the next chunk, during this one) fills a table of
+//     phi_t[k] for the chunk's 64 steps: the increments dt_t theta_t[k] are
+//     written lane-per-step as loaded, read back lane-per-(pair, 8-step
+//     segment), summed in registers and combined over the segments with a DPP
+//     scan, in float32 revolutions on top of the angle at the chunk's start,
+//     which is carried from chunk to chunk in float64 and reduced to
+//     [-1/2, 1/2] revolutions after every chunk;
+//   - the staging rotates one 16-byte piece of B and of C per thread (8 pairs
+//     of one step, both halves, loaded coalesced) with the hardware sine and
+//     cosine (which take revolutions) and writes the rotated rows to LDS.
+// The state update's B operand comes from the natural [s][n] rows through
+// the transposing LDS read (ds_read_b64_tr_b16), so no transposed copy is
+// kept: ~77 KB of LDS, two workgroups per CU.
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -104,19 +107,6 @@ __device__ __forceinline__ float wave_prefix(float a, int lane) {
   return a + (lane >= 16 ? r0 : 0.0f) + (lane >= 32 ? r1 : 0.0f) + (lane >= 48 ? r2 : 0.0f);
 }
 
-// The same scan with the rows combined by DPP broadcasts: row_bcast:15 adds
-// lane 15 of the row below to rows 1 and 3, then row_bcast:31 adds lane 31 to
-// rows 2 and 3 (rows outside the row mask add 0, the `old` operand).
-__device__ __forceinline__ float wave_prefix_bcast(float a) {
-  a += row_shr<1>(a);
-  a += row_shr<2>(a);
-  a += row_shr<4>(a);
-  a += row_shr<8>(a);
-  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x142, 0xA, 0xF, false));
-  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x143, 0xC, 0xF, false));
-  return a;
-}
-
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Two float32 rounded to bf16 (nearest even) in one 32-bit word, lo first.
@@ -137,10 +127,11 @@ __device__ __forceinline__ int tidx(int col, int t) { return col * QP + 2 * ((t 
 
 // One workgroup per (batch row, head) of eight wavefronts (two workgroups,
 // four wavefronts per SIMD, per CU).  Wavefront w owns the headdim columns
-// [16 (w % 4), 16 (w % 4) + 16) of the state for all dstate rows, and the
-// output rows [32 (w / 4), 32 (w / 4) + 32) of each chunk: the two
-// wavefronts of a column block both keep (and update) that block's state, so
-// each computes its half of the chunk's rows with no exchange between them.
+// [16 (w % 4), 16 (w % 4) + 16) and the dstate rows [(w / 4) N/2, (w / 4) N/2
+// + N/2) of the state, and the output rows [32 (w / 4), 32 (w / 4) + 32) of
+// each chunk: the two wavefronts of a column block each take Y_off over their
+// half of dstate for all rows, and swap the partial sums of each other's rows
+// through LDS.
 template <typename Tout, int N, bool HAS_Z, bool TRAP>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4)))
 ssd_rope_kernel(const SsdRopeParams rp) {
@@ -150,9 +141,13 @@ ssd_rope_kernel(const SsdRopeParams rp) {
   constexpr int PG = KP / 8;      // groups of 8 pairs (one 16-byte vector of each half row)
   constexpr int NJOB = Q * PG;    // rotation jobs (step, pair group) per chunk
   constexpr int PPW = KP / 8;     // pairs per wavefront in the angle pass
-  constexpr int KA = KP + 4;      // padded row of the angle table (floats)
+  constexpr int SEGS = 64 / PPW;  // angle pass: step segments (lanes per pair)
+  constexpr int SLEN = Q / SEGS;  // angle pass: steps per segment
+  constexpr int KA = KP + 1;      // row of the angle table (floats): conflict-free by rows and by columns
   constexpr int NP = N + 24;      // padded LDS row of [.][n] arrays
   constexpr int NT = N / 16;      // dstate tiles of S^T
+  constexpr int NT2 = NT / 2;     // dstate tiles of this wavefront's half
+  constexpr int NK2 = N / 64;     // K steps over this wavefront's half of dstate
   constexpr int NK = N / 32;      // K steps over dstate
   static_assert(NJOB <= NTH && NTH % NJOB == 0 && PPW % 4 == 0, "rotation map");
   constexpr bool kStageY = sizeof(Tout) == 2;
@@ -161,8 +156,8 @@ ssd_rope_kernel(const SsdRopeParams rp) {
   static_assert(Q * (P / YV) == NTH, "one y vector per thread per chunk");
   constexpr int SM = (kStageY && Q * YP > Q * QP) ? Q * YP : Q * QP;  // M (or y) buffer
   // One LDS block: the small per-step arrays first (a_t, exp(a_t),
-  // exp(a_last - a_s) w_s, w_s, gamma_s when TRAP, exp(a_last)), the angle
-  // then the tiles and the angle table.
+  // exp(a_last - a_s) w_s, w_s, gamma_s when TRAP, exp(a_last)), then the
+  // tiles and the angle table.
   constexpr int kF = Q * 4;
   constexpr int kOffA = 0, kOffEa = kOffA + kF, kOffW = kOffEa + kF, kOffDt = kOffW + kF;
   constexpr int kOffGam = kOffDt + kF;
@@ -172,7 +167,10 @@ ssd_rope_kernel(const SsdRopeParams rp) {
   constexpr int kOffXt = kOffB + Q * NP * 2;                // x[p][s]
   constexpr int kOffM = kOffXt + P * QP * 2;                // M[t][s], then y[t][p]
   constexpr int kOffAng = kOffM + SM * 2;                   // angle[t][k] (revolutions, in [0, 1))
-  constexpr int kLds = kOffAng + Q * KA * 4;
+  // The angle table's space also carries the Y_off halves (8 wavefronts x 2
+  // tiles x 64 lanes x 4 floats) between the angle passes.
+  constexpr int kAngF = Q * KA > 8 * 2 * 64 * 4 ? Q * KA : 8 * 2 * 64 * 4;
+  constexpr int kLds = kOffAng + kAngF * 4;
   static_assert(kOffC % 16 == 0 && kOffB % 16 == 0 && kOffXt % 16 == 0 && kOffM % 16 == 0 && kOffAng % 16 == 0,
                 "LDS layout");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
@@ -216,12 +214,15 @@ ssd_rope_kernel(const SsdRopeParams rp) {
   int q = lane / 16;
   int r16 = lane % 16;
   int pcol = (wave % 4) * 16 + r16;  // this lane's headdim column in S^T and Y
-  const int tr = wave / 4;                 // this wavefront's output rows: tiles 2 tr, 2 tr + 1
+  const int tr = wave / 4;   // this wavefront's output rows (tiles 2 tr, 2 tr + 1) and dstate half
+  const int nb = tr * (N / 2);  // first dstate row of the half
   // Rotation job (the last NJOB threads) and x staging job (the first 256).
   const int jv = tid - (NTH - NJOB);
   const bool has_job = jv >= 0;
   int jt = max(jv, 0) / PG, jk0 = 8 * (max(jv, 0) % PG);
   const int kw = wave * PPW;  // the angle pass's first pair for this wavefront
+  // Angle pass, second half: this lane's pair kw + aj and step segment ag.
+  const int aj = lane / SEGS, ag = lane % SEGS;
 
   const float Ah = p.A[h];
   const float Dh = p.D ? p.D[h] : 0.0f;
@@ -233,21 +234,20 @@ ssd_rope_kernel(const SsdRopeParams rp) {
     return p.lam_sigmoid ? 1.0f / (1.0f + expf(-raw)) : raw;
   };
 
-  // The angle of pair kw + lane (lane < PPW) at the start of the next chunk
-  // whose angles are to be computed, in revolutions reduced to [-1/2, 1/2],
-  // float64.  angle0 is read here, before anything is written, so
-  // angle_last may be angle0 itself.
-  double base = 0.0;
-  if (rp.angle0 != nullptr && lane < PPW) base = static_cast<double>(rp.angle0[(b * H + h) * KP + kw + lane]) * kInvTwoPi;
+  // The angle of pair kw + aj at the start of the next chunk whose angles
+  // are to be computed, in revolutions reduced to [-1/2, 1/2], float64 (the
+  // SEGS lanes of a pair hold the same value).  angle0 is read here, before
+  // anything is written, so angle_last may be angle0 itself.
+  double base = rp.angle0 != nullptr ? static_cast<double>(rp.angle0[(b * H + h) * KP + kw + aj]) * kInvTwoPi : 0.0;
   base -= rint(base);
 
-  floatx4 S[NT];  // S^T tiles: rows n = 16 ni + 4q + r, column p = pcol
+  floatx4 S[NT2];  // S^T tiles: rows n = nb + 16 i + 4q + r, column p = pcol
 #pragma unroll
-  for (int i = 0; i < NT; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NT2; ++i) S[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (p.h0) {
-    const float *h0 = p.h0 + ((b * H + h) * P + pcol) * N;
+    const float *h0 = p.h0 + ((b * H + h) * P + pcol) * N + nb;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
+    for (int i = 0; i < NT2; ++i) S[i] = *reinterpret_cast<const floatx4 *>(h0 + i * 16 + 4 * q);
   }
   if constexpr (TRAP) {
     // The token before the sequence (its B already rotated, per head) enters
@@ -256,9 +256,9 @@ ssd_rope_kernel(const SsdRopeParams rp) {
       const int64_t i0 = b * L * H + h;
       const float w0 = step_of(bf2f(gdt[i0])) * (1.0f - lam_of(bf2f(glam[i0])));
       const float xw = w0 * bf2f(static_cast<const uint16_t *>(p.x_prev)[(b * H + h) * P + pcol]);
-      const uint16_t *bp = static_cast<const uint16_t *>(p.B_prev) + (b * H + h) * N + 4 * q;
+      const uint16_t *bp = static_cast<const uint16_t *>(p.B_prev) + (b * H + h) * N + nb + 4 * q;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
+      for (int i = 0; i < NT2; ++i) {
         const u32x2 v = *reinterpret_cast<const u32x2 *>(bp + 16 * i);
         S[i][0] = fmaf(xw, lo_bf(v.x), S[i][0]);
         S[i][1] = fmaf(xw, hi_bf(v.x), S[i][1]);
@@ -334,40 +334,71 @@ ssd_rope_kernel(const SsdRopeParams rp) {
     }
   };
 
-  // ---- angle pass (lane = step, this wavefront's PPW pairs) ---------------
+  // ---- angle pass (this wavefront's PPW pairs, every step of a chunk) -----
   // phi_t = base - sum_{s <= t} dt_s theta_s as a fraction of a revolution,
-  // for every step of the chunk at c0, into the table; then the base moves to
-  // the next chunk's start.
+  // into the table; then the base moves to the next chunk's start.  The
+  // table first takes the increments dt_t theta_t (lane = step, as loaded);
+  // the wavefront then reads back its own columns with lane = (pair aj,
+  // segment ag of SLEN steps), sums each segment in registers, combines the
+  // segments with a scan over the SEGS lanes of the pair and writes the
+  // angles over the increments.  Only this wavefront touches these columns.
   auto angle_pass = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
     const float sr = (c0 + lane < L) ? step_of(bf2f(R.dt)) * kInvTwoPiF : 0.0f;  // revolutions per unit theta
-    const float bf = static_cast<float>(base);
-    float tot = 0.0f;  // lane j: this chunk's turn of pair kw + j
-    float ang[PPW];
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const uint32_t tw = R.th[j / 2];
-      const float pre = wave_prefix_bcast(sr * ((j & 1) ? hi_bf(tw) : lo_bf(tw)));
-      const float pj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bf), j));
-      const float tj = lane_value<63>(pre);
-      tot = lane == j ? tj : tot;
-      ang[j] = __builtin_amdgcn_fractf(pj - pre);
+      sAng[lane * KA + kw + j] = sr * ((j & 1) ? hi_bf(tw) : lo_bf(tw));
     }
+    __builtin_amdgcn_wave_barrier();
+    float part[SLEN];
+    float acc = 0.0f;
 #pragma unroll
-    for (int v = 0; v < PPW / 4; ++v)
-      *reinterpret_cast<floatx4 *>(&sAng[lane * KA + kw + 4 * v]) =
-          floatx4{ang[4 * v], ang[4 * v + 1], ang[4 * v + 2], ang[4 * v + 3]};
+    for (int i = 0; i < SLEN; ++i) {
+      acc += sAng[(ag * SLEN + i) * KA + kw + aj];
+      part[i] = acc;
+    }
+    // Inclusive scan of the segment sums over the pair's SEGS consecutive
+    // lanes (within a 16-lane row; with SEGS = 8 a row holds two pairs, and
+    // the lanes of the other pair are masked off).
+    float incl = acc;
+#pragma unroll
+    for (int sh = 1; sh < SEGS; sh *= 2) {
+      float v;
+      if (sh == 1) v = row_shr<1>(incl);
+      else if (sh == 2) v = row_shr<2>(incl);
+      else if (sh == 4) v = row_shr<4>(incl);
+      else v = row_shr<8>(incl);
+      if constexpr (SEGS < 16) v = ag >= sh ? v : 0.0f;
+      incl += v;
+    }
+    const float excl = incl - acc;
+    // The chunk's turn of the pair: the inclusive sum of its last segment
+    // (lane 15, or lanes 7 and 15 of the row), broadcast within the row.
+    float tot;
+    if constexpr (SEGS == 16) {
+      tot = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, incl), 0x15F, 0xF, 0xF, true));
+    } else {
+      const float t7 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, incl), 0x157, 0xF, 0xF, true));
+      const float t15 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, incl), 0x15F, 0xF, 0xF, true));
+      tot = (lane & 8) ? t15 : t7;
+    }
+    const float bf = static_cast<float>(base);
+#pragma unroll
+    for (int i = 0; i < SLEN; ++i)
+      sAng[(ag * SLEN + i) * KA + kw + aj] = __builtin_amdgcn_fractf(bf - (excl + part[i]));
     base -= static_cast<double>(tot);
     base -= rint(base);
-    if (c0 + Q >= L && rp.angle_last != nullptr && lane < PPW)  // after the last chunk
-      rp.angle_last[(b * H + h) * KP + kw + lane] = static_cast<float>(base * kTwoPi);
+    if (c0 + Q >= L && rp.angle_last != nullptr && ag == 0)  // after the last chunk
+      rp.angle_last[(b * H + h) * KP + kw + aj] = static_cast<float>(base * kTwoPi);
   };
 
   auto stage_chunk = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
     // ---- rotary step: the job's 8 pairs at its step ------------------------
     if (has_job) {
       const int t = jt, k0 = jk0;
-      const floatx4 a0 = *reinterpret_cast<const floatx4 *>(&sAng[t * KA + k0]);
-      const floatx4 a1 = *reinterpret_cast<const floatx4 *>(&sAng[t * KA + k0 + 4]);
+      float ang[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ang[i] = sAng[t * KA + k0 + i];
       u32x4 ob[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -375,7 +406,7 @@ ssd_rope_kernel(const SsdRopeParams rp) {
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
           const int i = 2 * e + hw;
-          const float rev = i < 4 ? a0[i] : a1[i - 4];
+          const float rev = ang[i];
           const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {  // B, then C
@@ -410,8 +441,9 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         sXt32[(c + 1) * (QP / 2) + (tp ^ tswz(c + 1))] = pair_hi(R.xv[0][i], R.xv[1][i]);
       }
     }
-    // dt and the in-chunk cumulative decay (the first wavefront: one lane per step).
-    if (wave == 0) {
+    // dt and the in-chunk cumulative decay (one lane per step; on a
+    // wavefront that stages no x).
+    if (wave == 4) {
       const float dtv = (c0 + lane < L) ? step_of(bf2f(R.dt)) : 0.0f;
       const float a = wave_prefix(dtv * Ah, lane);
       const float alast = lane_value<63>(a);
@@ -446,7 +478,6 @@ ssd_rope_kernel(const SsdRopeParams rp) {
     const bool more = c0 + Q < L;
     stage_chunk(R, c0);
     __syncthreads();
-    if (more) load_chunk(c0 + Q, R);
 
     // ---- M = mask(G^T) into LDS: 12 tiles (si, ti) over the 8 wavefronts ----
     // (the two all-zero tiles listed last go to the second round)
@@ -488,39 +519,43 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         *reinterpret_cast<u32x2 *>(&sM[t * QP + si * 16 + 4 * q]) = *reinterpret_cast<const u32x2 *>(m);
       }
     }
-    __syncthreads();
-
-    // ---- Y_off = diag(exp(a_t)) C S_prev^T ---------------------------------
-    // (this wavefront's two row tiles, ti = 2 tr + i)
+    // ---- Y_off = diag(exp(a_t)) C S_prev^T over this half of dstate --------
+    // (all four row tiles; the partner wavefront's two go to it through LDS,
+    // in the angle table's space, which is free until the next angle pass)
+    float *const sX = sAng;
     floatx4 Y[2];
+    {
+      floatx4 Yp[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) Y[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ti = 0; ti < 4; ++ti) Yp[ti] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const floatx8 sf = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
-                          S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
-      const bf16x8 bfrag = __builtin_convertvector(sf, bf16x8);
+      for (int kk = 0; kk < NK2; ++kk) {
+        const floatx8 sf = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
+                            S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
+        const bf16x8 bfrag = __builtin_convertvector(sf, bf16x8);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          const uint16_t *crow = &sC[(ti * 16 + r16) * NP + nb + 32 * kk + 4 * q];
+          const bf16x4 lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(crow));
+          const bf16x4 hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(crow + 16));
+          const bf16x8 afrag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          Yp[ti] = mfma(afrag, bfrag, Yp[ti]);
+        }
+      }
+      // Selected with a wave-uniform condition, not a run-time register
+      // index (which would compile to indexed register moves).
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint16_t *crow = &sC[((2 * tr + i) * 16 + r16) * NP + 32 * kk + 4 * q];
-        const bf16x4 lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(crow));
-        const bf16x4 hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(crow + 16));
-        const bf16x8 afrag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        Y[i] = mfma(afrag, bfrag, Y[i]);
+        *reinterpret_cast<floatx4 *>(&sX[((wave * 2 + i) * 64 + lane) * 4]) = tr ? Yp[i] : Yp[2 + i];
+        Y[i] = tr ? Yp[2 + i] : Yp[i];
       }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const floatx4 ea = *reinterpret_cast<const floatx4 *>(&sEa[(2 * tr + i) * 16 + 4 * q]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Y[i][r] *= ea[r];
-    }
 
-    // ---- S_new = exp(a_last) S_prev + B^T (w x) ----------------------------
+    // ---- S_new = exp(a_last) S_prev + B^T (w x) over this half of dstate ---
     {
       const float decay = sDecay[0];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) S[i] *= decay;
+      for (int i = 0; i < NT2; ++i) S[i] *= decay;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int s0 = 32 * kk + 8 * q;
@@ -535,13 +570,25 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         }
         const bf16x8 bfrag = __builtin_convertvector(wx, bf16x8);
 #pragma unroll
-        for (int ni = 0; ni < NT; ++ni) S[ni] = mfma(frag_t<NP>(sB, 32 * kk, 16 * ni, q, r16), bfrag, S[ni]);
+        for (int i = 0; i < NT2; ++i) S[i] = mfma(frag_t<NP>(sB, 32 * kk, nb + 16 * i, q, r16), bfrag, S[i]);
       }
     }
-    if (p.h_last != nullptr && !more && tr == 0) {
-      float *hl = p.h_last + ((b * H + h) * P + pcol) * N;
+    if (p.h_last != nullptr && !more) {
+      float *hl = p.h_last + ((b * H + h) * P + pcol) * N + nb;
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) *reinterpret_cast<floatx4 *>(hl + ni * 16 + 4 * q) = S[ni];
+      for (int i = 0; i < NT2; ++i) *reinterpret_cast<floatx4 *>(hl + i * 16 + 4 * q) = S[i];
+    }
+    // The next chunk's inputs.
+    if (more) load_chunk(c0 + Q, R);
+    __syncthreads();
+
+    // The partner's half of Y_off for this wavefront's rows, then exp(a_t).
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      Y[i] += *reinterpret_cast<const floatx4 *>(&sX[(((wave ^ 4) * 2 + i) * 64 + lane) * 4]);
+      const floatx4 ea = *reinterpret_cast<const floatx4 *>(&sEa[(2 * tr + i) * 16 + 4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[i][r] *= ea[r];
     }
 
     // ---- Y += M X (causal: K steps at or below the diagonal) ---------------
@@ -557,9 +604,6 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         }
       }
     }
-    // The next chunk's angles (its theta and dt were loaded during this
-    // chunk's products; this chunk's table was read before the first barrier).
-    if (more) angle_pass(R, c0 + Q);
 
     // ---- epilogue: D skip and gate in the MFMA layout ------------------------
     // Element e of this lane: step t = (2 tr + e / 4) 16 + 4q + e % 4.
@@ -581,9 +625,12 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         yv[i * 4 + r] = v;
       }
     }
-    // Every wavefront is done reading M and x, and the next chunk's angles
-    // are written: the M buffer takes y, and the next chunk may be staged.
+    // Every wavefront is done reading M, x and the Y_off halves: the M buffer
+    // takes y, and the angle table the next chunk's angles (its theta and dt
+    // were loaded during this chunk's products; this chunk's table was read
+    // before the first barrier).
     __syncthreads();
+    if (more) angle_pass(R, c0 + Q);
     if constexpr (kStageY) {
       Tout *sY = reinterpret_cast<Tout *>(sM);
 #pragma unroll
@@ -601,17 +648,18 @@ ssd_rope_kernel(const SsdRopeParams rp) {
         const int t = (2 * tr + e / 4) * 16 + 4 * q + (e % 4);
         if (c0 + t < L) st(gy + ybase, t * rx + pcol, yv[e]);
       }
+      if (more) __syncthreads();  // the angle table is complete before the next staging
     }
   }
 
   if (L == 0) {  // an empty sequence: h_last is the initial state, angle_last the initial angle
-    if (p.h_last != nullptr && tr == 0) {
-      float *hl = p.h_last + ((b * H + h) * P + pcol) * N;
+    if (p.h_last != nullptr) {
+      float *hl = p.h_last + ((b * H + h) * P + pcol) * N + nb;
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) *reinterpret_cast<floatx4 *>(hl + ni * 16 + 4 * q) = S[ni];
+      for (int i = 0; i < NT2; ++i) *reinterpret_cast<floatx4 *>(hl + i * 16 + 4 * q) = S[i];
     }
-    if (rp.angle_last != nullptr && lane < PPW)
-      rp.angle_last[(b * H + h) * KP + kw + lane] = static_cast<float>(base * kTwoPi);
+    if (rp.angle_last != nullptr && ag == 0)
+      rp.angle_last[(b * H + h) * KP + kw + aj] = static_cast<float>(base * kTwoPi);
   }
 }
 
