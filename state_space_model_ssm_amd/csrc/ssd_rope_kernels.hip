@@ -301,7 +301,7 @@ ssd_rope_kernel(const SsdRopeParams rp) {
     const int64_t dbase = (b * L + c0) * H + h;
     const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0) - 1);  // the next chunk's first step too
     R.dt = gdt[dbase + min(lane, last) * rdt];
-    if constexpr (TRAP) {
+    if (TRAP && wave == 4) {  // the weights are built by the decay wavefront only
       R.lam = glam[dbase + min(lane, last) * rdt];
       R.dtn = gdt[dbase + min(lane + 1, lastn) * rdt];
       R.lamn = glam[dbase + min(lane + 1, lastn) * rdt];
