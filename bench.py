@@ -335,6 +335,28 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
                                    "workspace_MB": round(ws.numel() / 1e6, 1),
                                    "alu_model_us": round(t_alu * 1e6, 1), "alu_frac": round(t_alu * 1e3 / ms, 4)}
         del d, dy, ws
+    # The chunked carry on the shape it is for: one long sequence with too few
+    # channels to fill the GPU (1 x 1536 channels x 4096 steps, 16 states,
+    # float32: 96 channel blocks of 16 channels).  The library's own chunk
+    # count against one chunk and two forced counts.
+    from state_space_model_ssm_amd.synth import ScanShape
+    w = ScanShape(1, 1536, 16, 4096, 1, "f32", has_z=True, dskip="normal", seed=12)
+    d = {k: (None if v is None else v.to(dev)) for k, v in make_scan_inputs(w).items()}
+    y = torch.empty_like(d["u"])
+    dims = ssm._scan_dims(d["u"], d["B"], ssm._dtype_code(d["u"].dtype), ssm._dtype_code(d["u"].dtype), 0)
+    auto = ssm.scan_resolved_chunks(dims)
+    entry = {"resolved_chunks": auto}
+    for k in (1, auto, 4, 32):
+        ws = torch.empty(max(ssm.scan_workspace_size(ssm._scan_dims(d["u"], d["B"], ssm._dtype_code(d["u"].dtype),
+                                                                     ssm._dtype_code(d["u"].dtype), k)), 1),
+                         dtype=torch.uint8, device=dev)
+        ms, _ = time_calls(lambda: ssm.scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["z"], y=y,
+                                                n_chunks=k, workspace=ws, stream=stream), 20, 3)
+        entry[f"ms_{k}_chunks"] = round(ms, 5)
+    entry["hbm_GB/s_auto"] = round(w.metric_bytes() / entry[f"ms_{auto}_chunks"] / 1e6, 1)
+    out["chunked_carry_1x1536x4096_f32"] = entry
+    del d, y
+
     w = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
     d = {k: (None if v is None else v.to(dev)) for k, v in make_ssd_inputs(w).items()}
     lam = make_lam((w.batch, w.seqlen, w.nheads), seed=10).to(dev)
