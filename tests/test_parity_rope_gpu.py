@@ -413,6 +413,8 @@ def test_fused_rope_ssd_named_workload_full_size(trap):
     y, hl, al, bl = _fused_run(inp, trap, torch.bfloat16, h0=None)
     ry, rh, ra, rb16 = _fused_oracle(inp, trap)
     errs = (rel_err(y, ry), rel_err(hl, rh), angle_err(al, ra), rel_err(bl, rb16[:, -1].float()))
+    print(f"fused rotary SSD full size (trap={trap}): y {errs[0]:.2e} h_last {errs[1]:.2e} "
+          f"angle_last {errs[2]:.2e} B_last {errs[3]:.2e}", flush=True)
     assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32 and errs[3] <= 1e-2, errs
 
 
