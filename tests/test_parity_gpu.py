@@ -542,6 +542,61 @@ def test_decode_steps_at_bench_state_sizes():
     assert rel_err(state.cpu(), hr) <= TOL_BF16
 
 
+def _offset_copy(t, elems=1):
+    """A device copy of t whose data starts `elems` elements into its buffer
+    (element-aligned, not 16-byte aligned)."""
+    buf = torch.empty(t.numel() + elems, dtype=t.dtype, device="cuda")
+    v = buf[elems:].view(t.shape)
+    v.copy_(t.cuda())
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps_unaligned_bc(dtype):
+    """B, C (and B_prev) that are only element-aligned take the element-load
+    path of the decode steps: one scan step, one SSD step and one trapezoidal
+    step against the oracle, and equal to the same calls on aligned copies."""
+    g = torch.Generator().manual_seed(5995)
+    cast = torch.float32 if dtype == "f32" else torch.bfloat16
+    rnd = lambda *sh: torch.randn(*sh, generator=g).to(cast)
+    pos = lambda *sh: (torch.rand(*sh, generator=g) * 0.1 + 1e-3).to(cast)
+    b, d, n = 2, 48, 16
+    u, dl, z, Bm, Cm = rnd(b, d), pos(b, d), rnd(b, d), rnd(b, 1, n), rnd(b, 1, n)
+    A = -torch.rand(d, n, generator=g) - 0.5
+    D = torch.randn(d, generator=g)
+    S = make_state((b, d, n), seed=5996)
+    outs = []
+    for mk in (_dev, _offset_copy):
+        state = S.cuda().clone()
+        y = ssm.scan_step(_dev(u), _dev(dl), _dev(A), mk(Bm), mk(Cm), _dev(D), _dev(z), state=state)
+        outs.append((y.float().cpu(), state.cpu()))
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_step(u, dl, A, Bm, Cm, D, z, state=S)
+    tol = tol_for(dtype)
+    assert rel_err(outs[1][0], yr) <= tol and rel_err(outs[1][1], hr) <= tol
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    b, H, P, n = 2, 4, 16, 64
+    x, dt, lam, xp = rnd(b, H, P), pos(b, H), torch.rand(b, H, generator=g).to(cast), rnd(b, H, P)
+    Bm, Cm, Bp = rnd(b, 1, n), rnd(b, 1, n), rnd(b, 1, n)
+    Ah = -torch.rand(H, generator=g) - 0.5
+    Dh = torch.randn(H, generator=g)
+    S = make_state((b, H, P, n), seed=5997, scale=0.1)
+    outs = []
+    for mk in (_dev, _offset_copy):
+        st1, st2 = S.cuda().clone(), S.cuda().clone()
+        y1 = ssm.ssd_step(_dev(x), _dev(dt), _dev(Ah), mk(Bm), mk(Cm), _dev(Dh), None, state=st1)
+        y2 = ssm.ssd_trap_step(_dev(x), _dev(dt), _dev(lam), _dev(Ah), mk(Bm), mk(Cm), _dev(Dh), None, state=st2,
+                               x_prev=_dev(xp), B_prev=mk(Bp))
+        outs.append([t.float().cpu() for t in (y1, st1, y2, st2)])
+    torch.cuda.synchronize()
+    yr, hr = oracle.ssd_step(x, dt, Ah, Bm, Cm, Dh, None, state=S)
+    ytr, htr = oracle.ssd_trap_step(x, dt, lam, Ah, Bm, Cm, Dh, None, state=S, x_prev=xp, B_prev=Bp)
+    for got, ref in zip(outs[1], (yr, hr, ytr, htr)):
+        assert rel_err(got, ref) <= tol
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a, b_)
+
+
 def test_ssd_prefill_then_128_decode_steps():
     """A 64-token chunked prefill leaves its state in a cache; 128 decode steps
     continue from it in place.  Every step's y and the final state match one
