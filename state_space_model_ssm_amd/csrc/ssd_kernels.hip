@@ -378,59 +378,9 @@ ssd_chunk_kernel(const SsdParams p) {
     __syncthreads();
     if (c0 + Q < L) load_chunk(c0 + Q, R);
 
-    // ---- M = mask(G^T) into LDS, for every head of the workgroup -----------
-    // 12 tiles (si, ti): the lower-triangular tiles plus the two upper tiles
-    // (1,0) and (3,2) that the K = 32 steps of Y_diag read; those are written
-    // as zeros.  Tile k goes to wavefront k mod (4 HPB).
-    {
-      // (si, ti) pairs, four bits each: si | ti << 2, in the order listed above.
-      constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 |
-                                  0xAull << 20 | 0xCull << 24 | 0xDull << 28 | 0xEull << 32 |
-                                  0xFull << 36 | 0x1ull << 40 | 0xBull << 44;
-      constexpr int kRounds = (12 + 4 * HPB - 1) / (4 * HPB);
-#pragma unroll
-      for (int u = 0; u < kRounds; ++u) {
-        const int k = wave + 4 * HPB * u;
-        if (12 % (4 * HPB) == 0 || k < 12) {
-          const int code = static_cast<int>((kTiles >> (4 * k)) & 0xF);
-          const int si = code & 3;
-          const int ti = code >> 2;
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          if (si <= ti) {
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-              const bf16x8 afrag = lds8(&sB[(si * 16 + r16) * NP + 32 * kk + 8 * q]);
-              const bf16x8 bfrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
-              acc = mfma(afrag, bfrag, acc);
-            }
-          }
-          const int t = ti * 16 + r16;
-          const int sb = si * 16 + 4 * q;
-#pragma unroll
-          for (int j = 0; j < HPB; ++j) {
-            const float at = sAH[j * Q + t];
-            const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sAH[j * Q + sb]);
-            const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDtH[j * Q + sb]);
-            floatx4 gm4 = dt4;
-            if constexpr (TRAP) gm4 = *reinterpret_cast<const floatx4 *>(&sGamH[j * Q + sb]);
-            uint16_t m[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              // Branch-free: above the diagonal the exponent is clamped to 0
-              // (a_t - a_s > 0 there) and the product is multiplied by 0.
-              const int s = sb + r;
-              const float ws = s < t ? dt4[r] : gm4[r];
-              const float keep = s <= t ? 1.0f : 0.0f;
-              m[r] = f2bf(acc[r] * fast_exp(fminf(at - as4[r], 0.0f)) * ws * keep);
-            }
-            *reinterpret_cast<uint2 *>(&sMH[j * SM + t * QP + si * 16 + 4 * q]) =
-                *reinterpret_cast<const uint2 *>(m);
-          }
-        }
-      }
-    }
-    __syncthreads();
-
+    // Y_off and the state update need only what the staging wrote (not M),
+    // so they come before the mask tiles: the wavefronts without a tile work
+    // while the others build M (4-6% faster than after the M barrier).
     // ---- Y_off = diag(exp(a_t)) C S_prev^T ---------------------------------
     floatx4 Y[4];
 #pragma unroll
@@ -489,6 +439,59 @@ ssd_chunk_kernel(const SsdParams p) {
       for (int ni = 0; ni < NT; ++ni)
         *reinterpret_cast<floatx4 *>(hl + ni * 16 + 4 * q) = S[ni];
     }
+
+    // ---- M = mask(G^T) into LDS, for every head of the workgroup -----------
+    // 12 tiles (si, ti): the lower-triangular tiles plus the two upper tiles
+    // (1,0) and (3,2) that the K = 32 steps of Y_diag read; those are written
+    // as zeros.  Tile k goes to wavefront k mod (4 HPB).
+    {
+      // (si, ti) pairs, four bits each: si | ti << 2, in the order listed above.
+      constexpr uint64_t kTiles = 0x0 | 0x4ull << 4 | 0x5ull << 8 | 0x8ull << 12 | 0x9ull << 16 |
+                                  0xAull << 20 | 0xCull << 24 | 0xDull << 28 | 0xEull << 32 |
+                                  0xFull << 36 | 0x1ull << 40 | 0xBull << 44;
+      constexpr int kRounds = (12 + 4 * HPB - 1) / (4 * HPB);
+#pragma unroll
+      for (int u = 0; u < kRounds; ++u) {
+        const int k = wave + 4 * HPB * u;
+        if (12 % (4 * HPB) == 0 || k < 12) {
+          const int code = static_cast<int>((kTiles >> (4 * k)) & 0xF);
+          const int si = code & 3;
+          const int ti = code >> 2;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (si <= ti) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+              const bf16x8 afrag = lds8(&sB[(si * 16 + r16) * NP + 32 * kk + 8 * q]);
+              const bf16x8 bfrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
+              acc = mfma(afrag, bfrag, acc);
+            }
+          }
+          const int t = ti * 16 + r16;
+          const int sb = si * 16 + 4 * q;
+#pragma unroll
+          for (int j = 0; j < HPB; ++j) {
+            const float at = sAH[j * Q + t];
+            const floatx4 as4 = *reinterpret_cast<const floatx4 *>(&sAH[j * Q + sb]);
+            const floatx4 dt4 = *reinterpret_cast<const floatx4 *>(&sDtH[j * Q + sb]);
+            floatx4 gm4 = dt4;
+            if constexpr (TRAP) gm4 = *reinterpret_cast<const floatx4 *>(&sGamH[j * Q + sb]);
+            uint16_t m[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              // Branch-free: above the diagonal the exponent is clamped to 0
+              // (a_t - a_s > 0 there) and the product is multiplied by 0.
+              const int s = sb + r;
+              const float ws = s < t ? dt4[r] : gm4[r];
+              const float keep = s <= t ? 1.0f : 0.0f;
+              m[r] = f2bf(acc[r] * fast_exp(fminf(at - as4[r], 0.0f)) * ws * keep);
+            }
+            *reinterpret_cast<uint2 *>(&sMH[j * SM + t * QP + si * 16 + 4 * q]) =
+                *reinterpret_cast<const uint2 *>(m);
+          }
+        }
+      }
+    }
+    __syncthreads();
 
     // ---- Y += M X (causal: K steps at or below the diagonal) ---------------
 #pragma unroll
