@@ -135,7 +135,7 @@ ssd_chunk_kernel(const SsdParams p) {
   constexpr int kOffGam = kOffDt + kHeadF;
   constexpr int kOffDecay = kOffGam + (TRAP ? kHeadF : 16);
   constexpr int kOffC = kOffDecay + 16 * ((HPB * 4 + 15) / 16);
-  constexpr int kOffB = kOffC + Q * NP * 2;                 // C[t][n], then B[s][n]
+  constexpr int kOffB = kOffC + Q * NP * 2;                 // C[t][n], then B[s][n] (n reordered)
   constexpr int kOffBt = kOffB + Q * NP * 2;                // B[n][s]
   constexpr int kOffXt = kOffBt + N * QP * 2;               // per head: x[p][s]
   constexpr int kOffM = kOffXt + HPB * P * QP * 2;          // per head: M[t][s], then y[t][p]
@@ -313,7 +313,7 @@ ssd_chunk_kernel(const SsdParams p) {
     }
   };
   auto stage_chunk = [&](const ChunkRegs &R, int64_t c0) __attribute__((always_inline)) {
-    // B and C: natural layout [t][n] for both, B also transposed to [n][t].
+    // B and C: [t][n] rows (n reordered, below), B also transposed to [n][t].
 #pragma unroll
     for (int k = 0; k < BJ; ++k) {
       const int v = tid + NTH * k;
@@ -323,8 +323,19 @@ ssd_chunk_kernel(const SsdParams p) {
         const int nv = (vv % (N / 8)) * 8;
         const bool is_b = v < BC_JOBS / 2;  // uniform over a wavefront
         uint16_t *dst = is_b ? sB : sC;
+        // Within each block of 32 dstate columns, slot 8i + j (i < 4, j < 8)
+        // holds n = 4i + j for j < 4 and n = 16 + 4i + (j - 4) for j >= 4:
+        // the order in which the state tiles pair n in the K slots of Y_off,
+        // so that a lane's C fragment there is one 16-byte read.  The mask
+        // tiles contract B and C over n, which any common order leaves alone.
+        const int o = nv % 32;  // 0, 8, 16 or 24: this vector's n = nv .. nv + 7
+        const int slot = (nv - o) + 8 * ((o % 16) / 4) + 4 * (o / 16);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<uint4 *>(&dst[(2 * tp + e) * NP + nv]) = R.bc[k][e];
+        for (int e = 0; e < 2; ++e) {
+          uint16_t *row = &dst[(2 * tp + e) * NP + slot];
+          *reinterpret_cast<uint2 *>(row) = uint2{R.bc[k][e].x, R.bc[k][e].y};
+          *reinterpret_cast<uint2 *>(row + 8) = uint2{R.bc[k][e].z, R.bc[k][e].w};
+        }
         if (is_b) put_t(sBt32, nv, tp, R.bc[k][0], R.bc[k][1], std::integral_constant<int, N>{});
       }
     }
@@ -392,10 +403,7 @@ ssd_chunk_kernel(const SsdParams p) {
       const bf16x8 bfrag = __builtin_convertvector(sf, bf16x8);
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const uint16_t *crow = &sC[(ti * 16 + r16) * NP + 32 * kk + 4 * q];
-        const bf16x4 lo = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(crow));
-        const bf16x4 hi = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2 *>(crow + 16));
-        const bf16x8 afrag = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 afrag = lds8(&sC[(ti * 16 + r16) * NP + 32 * kk + 8 * q]);
         Y[ti] = mfma(afrag, bfrag, Y[ti]);
       }
     }
