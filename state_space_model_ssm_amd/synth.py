@@ -11,6 +11,11 @@ Recipe (one definition for every workload):
   * scan order: u, delta, B, C, z, Dskip, then A when A is random.
     SSD order: x, dt, B, C, z, Dskip, A.
   * the stored values (not the float64 draws) are what both sides consume.
+  * shapes too large to draw on the host in reasonable time (tensors of more
+    than 2^31 elements) use ``make_scan_inputs_on`` / ``make_ssd_inputs_on``:
+    the same distributions drawn by torch's seeded generator on the device
+    (other values than the host recipe's, equally seeded); a test copies the
+    slices it checks to the host, so both sides again consume stored values.
 
 The named workloads reproduce the shapes and value distributions of the pages'
 own measurements: the 1536-channel, L=128 Mamba state of "We brought Mamba to
@@ -30,7 +35,7 @@ import torch
 
 __all__ = [
     "ScanShape", "SsdShape", "WORKLOADS", "make_scan_inputs", "make_ssd_inputs",
-    "inv_softplus", "make_raw_step",
+    "inv_softplus", "make_raw_step", "make_scan_inputs_on", "make_ssd_inputs_on",
 ]
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -236,3 +241,65 @@ def make_ssd_inputs(s: SsdShape) -> dict:
         "D": None if Dk is None else torch.from_numpy(Dk.astype(np.float32)),
         "z": None if z is None else _store(z, s.dtype),
     }
+
+
+def _dev_gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _dev_normal(shape, g, device, dtype, scale: float = 1.0) -> torch.Tensor:
+    """N(0, scale^2) stored in dtype, drawn a leading-index slice at a time so
+    that no float32 copy of a whole huge tensor is needed."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    for i in range(shape[0]):
+        out[i] = (torch.randn(shape[1:], generator=g, device=device) * scale).to(dtype)
+    return out
+
+
+def make_scan_inputs_on(s: ScanShape, device="cuda") -> dict:
+    """``make_scan_inputs``'s distributions drawn on the device (torch's
+    generator, seed ``s.seed``), in the same order and layouts."""
+    g = _dev_gen(s.seed, device)
+    dt = _TORCH_DTYPES[s.dtype]
+    bdl = (s.batch, s.dim, s.seqlen)
+    bgnl = (s.batch, s.ngroups, s.dstate, s.seqlen)
+    u = _dev_normal(bdl, g, device, dt)
+    delta = torch.empty(bdl, dtype=dt, device=device)
+    for i in range(s.batch):
+        r = torch.empty(bdl[1:], device=device).uniform_(math.log(s.delta_lo), math.log(s.delta_hi), generator=g)
+        delta[i] = r.exp_().to(dt)
+    B = _dev_normal(bgnl, g, device, dt)
+    C = _dev_normal(bgnl, g, device, dt)
+    z = _dev_normal(bdl, g, device, dt) if s.has_z else None
+    Dk = {"normal": lambda: torch.randn(s.dim, generator=g, device=device),
+          "ones": lambda: torch.ones(s.dim, device=device), "none": lambda: None}[s.dskip]()
+    if s.a_kind == "neg_n1":
+        A = -torch.arange(1, s.dstate + 1, dtype=torch.float32, device=device).repeat(s.dim, 1)
+    elif s.a_kind == "zero":
+        A = torch.zeros((s.dim, s.dstate), device=device)
+    elif s.a_kind == "loguniform":
+        A = -torch.empty((s.dim, s.dstate), device=device).uniform_(math.log(0.5), math.log(16.0), generator=g).exp_()
+    else:
+        raise ValueError(f"unknown a_kind {s.a_kind!r}")
+    return {"u": u, "delta": delta, "A": A.contiguous(), "B": B, "C": C, "D": Dk, "z": z}
+
+
+def make_ssd_inputs_on(s: SsdShape, device="cuda") -> dict:
+    """``make_ssd_inputs``'s distributions drawn on the device (torch's
+    generator, seed ``s.seed``), in the same order and layouts."""
+    g = _dev_gen(s.seed, device)
+    dt_ = _TORCH_DTYPES[s.dtype]
+    xs = (s.batch, s.seqlen, s.nheads, s.headdim)
+    x = _dev_normal(xs, g, device, dt_)
+    pre = torch.randn((s.batch, s.seqlen, s.nheads), generator=g, device=device) + inv_softplus(0.01)
+    dt = torch.nn.functional.softplus(pre).to(dt_)
+    bcs = (s.batch, s.seqlen, s.ngroups, s.dstate)
+    B = _dev_normal(bcs, g, device, dt_, 1.0 / math.sqrt(s.dstate))
+    C = _dev_normal(bcs, g, device, dt_, 1.0 / math.sqrt(s.dstate))
+    z = _dev_normal(xs, g, device, dt_) if s.has_z else None
+    Dk = {"ones": lambda: torch.ones(s.nheads, device=device),
+          "normal": lambda: torch.randn(s.nheads, generator=g, device=device), "none": lambda: None}[s.dskip]()
+    A = -torch.empty(s.nheads, device=device).uniform_(math.log(1.0), math.log(16.0), generator=g).exp_()
+    return {"x": x, "dt": dt, "A": A, "B": B, "C": C, "D": Dk, "z": z}

@@ -399,6 +399,39 @@ def test_fused_rope_trap_chained_in_place():
     assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
 
 
+def test_fused_rope_trap_prefill_then_128_decode_steps():
+    """The serving order with the fused prefill: a 64-token fused rotary
+    trapezoidal prefill returns h_last, angle_last and B_last (the last
+    token's rotated B); 128 decode tokens follow, each a one-token rotary step
+    from the cached angle and an ssd_trap_step that passes the previous
+    token's x and rotated B.  Every output against the oracle (rotary step,
+    then the trapezoidal SSD) over all 192 tokens."""
+    batch, L, H, N, T = 2, 192, 8, 128, 64
+    inp = _fused_inputs(batch, L, H, 1, N, 1, True, True, True, 5.0, 215)
+    ry, rh, ra, _ = _fused_oracle(inp, True)
+    d = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    pre = lambda t: t[:, :T].contiguous()
+    ang = d["angle0"].clone()
+    y0, state, _, bp = ssm.ssd_rope_trap_chunked_fwd(
+        pre(d["x"]), pre(d["dt"]), pre(d["lam"]), d["A"], pre(d["B"]), pre(d["C"]), pre(d["theta"]), d["D"],
+        pre(d["z"]), h0=d["h0"], angle0=ang, angle_last=ang, return_B_last=True)
+    ys = [y0.float()]
+    xp = d["x"][:, T - 1].contiguous()
+    for t in range(T, L):
+        one = lambda a: a[:, t:t + 1].contiguous()
+        b1, c1, _ = ssm.rope_bc(one(d["dt"]), one(d["theta"]), one(d["B"]), one(d["C"]), angle0=ang, angle_last=ang)
+        xt = d["x"][:, t].contiguous()
+        y = ssm.ssd_trap_step(xt, d["dt"][:, t].contiguous(), d["lam"][:, t].contiguous(), d["A"],
+                              b1[:, 0].contiguous(), c1[:, 0].contiguous(), d["D"], d["z"][:, t].contiguous(),
+                              state=state, x_prev=xp, B_prev=bp)
+        ys.append(y.float()[:, None])
+        xp, bp = xt, b1[:, 0].contiguous()
+    torch.cuda.synchronize()
+    got = torch.cat(ys, dim=1).cpu()
+    errs = (rel_err(got, ry), rel_err(state.cpu(), rh), angle_err(ang.cpu(), ra))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
+
+
 @pytest.mark.parametrize("trap", [False, True])
 def test_fused_rope_ssd_named_workload_full_size(trap):
     """The fused rotary SSD at the SSD workload's full size (32 x 256, 32
