@@ -308,12 +308,14 @@ __device__ __forceinline__ void state_pass(const SsdBwdParams &p, int64_t bh, St
         if constexpr (HAS_Z) R.z[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.z) + vb + o);
       }
     }
-    R.dt = gdt[(b * L + c0) * H + h + min(lane, last) * Hi];
-    if constexpr (TRAP && !REV) {
-      const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
-      R.lam = glam[(b * L + c0) * H + h + min(lane, last) * Hi];
-      R.dtn = gdt[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
-      R.lamn = glam[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
+    if (wave == 0) {  // the per-step gathers, for the wavefront that forms the decays
+      R.dt = gdt[(b * L + c0) * H + h + min(lane, last) * Hi];
+      if constexpr (TRAP && !REV) {
+        const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
+        R.lam = glam[(b * L + c0) * H + h + min(lane, last) * Hi];
+        R.dtn = gdt[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
+        R.lamn = glam[(b * L + c0) * H + h + min(lane + 1, lastn) * Hi];
+      }
     }
   };
   auto stage = [&](int64_t c, const Regs &R) __attribute__((always_inline)) {
@@ -574,13 +576,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves) ssd_bwd_chunk_kernel(const Ssd
         R.sn[k] = *reinterpret_cast<const u32x4 *>(gsp + 8 * e);
       }
     }
-    R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, Lc - 1)) * H + h];
-    if constexpr (TRAP) {
-      const uint16_t *glam = static_cast<const uint16_t *>(p.lam);
-      const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
-      R.lam = glam[(b * L + c0 + min(lane, Lc - 1)) * H + h];
-      R.dtn = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane + 1, lastn)) * H + h];
-      R.lamn = glam[(b * L + c0 + min(lane + 1, lastn)) * H + h];
+    if (wave == 0) {  // the per-step gathers, for the wavefront that forms the decays
+      R.dt = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane, Lc - 1)) * H + h];
+      if constexpr (TRAP) {
+        const uint16_t *glam = static_cast<const uint16_t *>(p.lam);
+        const int lastn = static_cast<int>(min(static_cast<int64_t>(Q) + 1, L - c0)) - 1;  // the next chunk's first step too
+        R.lam = glam[(b * L + c0 + min(lane, Lc - 1)) * H + h];
+        R.dtn = static_cast<const uint16_t *>(p.dt)[(b * L + c0 + min(lane + 1, lastn)) * H + h];
+        R.lamn = glam[(b * L + c0 + min(lane + 1, lastn)) * H + h];
+      }
     }
   };
 
