@@ -444,6 +444,28 @@ def test_rope_empty_inputs_launch_nothing():
     assert _rope(_ropedims(seqlen=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
 
 
+def test_last_error_is_per_thread():
+    """ssm_last_error() is thread-local: two host threads that fail different
+    checks at the same time each read their own message."""
+    import threading
+    gate = threading.Barrier(2)
+    seen = {}
+
+    def fail_and_read(name, call):
+        for _ in range(50):
+            rc = call()
+            gate.wait()          # both threads have failed
+            seen.setdefault(name, []).append((rc, ssm.last_error()))
+            gate.wait()          # both have read before either fails again
+
+    a = threading.Thread(target=fail_and_read, args=("scan", lambda: _scan(_dims(dstate=12))))
+    b = threading.Thread(target=fail_and_read, args=("ssd", lambda: _ssd(_sdims(headdim=32))))
+    a.start(), b.start()
+    a.join(), b.join()
+    assert all(rc == -5 and "dstate" in msg for rc, msg in seen["scan"]), seen["scan"][:2]
+    assert all(rc == -5 and "headdim" in msg for rc, msg in seen["ssd"]), seen["ssd"][:2]
+
+
 def test_size_returning_workspace_queries_and_error_message():
     """ssm_scan_workspace_bytes / ssd_workspace_bytes return what the
     status-returning queries write, SIZE_MAX on a failed check, and
