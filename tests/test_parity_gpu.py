@@ -1355,3 +1355,73 @@ def test_ssd_trap_backward_named_workload_full_size():
     dhl = make_state((w.batch, w.nheads, w.headdim, w.dstate), seed=8904, scale=0.5)
     args = (inp, lam, None, dhl, xp, bp, dy, {})
     _check_trap_bwd(_trap_bwd_gpu(*args), _trap_bwd_ref(*args), "ssd_trap_32x256_h32p64n128_bf16 backward")
+
+
+# ---------------------------------------------------------------------------
+# Seeded random sweep over the supported shape space: shapes, group counts,
+# dtypes, chunk counts and optional inputs in combinations the hand-picked
+# cases above do not list.  The cases are drawn once, from a fixed seed, so
+# every run (and every test id) is the same; each is checked against the
+# oracle over the whole outputs.
+# ---------------------------------------------------------------------------
+
+def _sweep_scan_cases(n=24, seed=20261):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 4, 8, 16, 16, 16, 32, 64]))
+        G = int(rng.choice([1, 1, 2, 3]))
+        dim = G * int(rng.integers(1, 90))
+        L = int(rng.integers(1, 600))
+        cases.append((int(rng.integers(1, 4)), dim, N, L, G, str(rng.choice(["f32", "bf16"])),
+                      str(rng.choice(["f32", "bf16"])), bool(rng.integers(0, 2)),
+                      str(rng.choice(["ones", "normal", "none"])),
+                      int(rng.choice([0, 1, 1, 2, 3, max(1, L // 40)])), bool(rng.integers(0, 2)), 7000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_scan_cases(),
+                         ids=lambda c: "b{}d{}n{}l{}g{}_{}to{}_z{}_{}_k{}_h0{}".format(*c[:11]))
+def test_scan_random_sweep(case):
+    batch, dim, N, L, G, dtype, out, has_z, dskip, k, with_h0, seed = case
+    print(f"scan sweep case {case}", flush=True)
+    s = ScanShape(batch, dim, N, L, G, dtype, has_z=has_z, dskip=dskip, a_kind="loguniform", seed=seed)
+    inp = make_scan_inputs(s)
+    h0 = make_state((batch, dim, N), seed + 1, 0.5) if with_h0 else None
+    y, h = run_scan(inp, out_dtype=DT[out], n_chunks=k, h0=h0)
+    yr, hr = ref_scan(inp, h0=h0)
+    tol = tol_for(dtype, out)
+    assert rel_err(y, yr) <= tol, (rel_err(y, yr), tol)
+    assert rel_err(h, hr) <= tol, (rel_err(h, hr), tol)
+
+
+def _sweep_ssd_cases(n=16, seed=20262):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        G = int(rng.choice([1, 1, 2, 4]))
+        H = G * int(rng.choice([1, 1, 2, 3, 4]))
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 300)), H, int(rng.choice([64, 128])), G,
+                      bool(rng.integers(0, 2)), str(rng.choice(["ones", "normal", "none"])),
+                      bool(rng.integers(0, 2)), str(rng.choice(["f32", "bf16"])), bool(rng.integers(0, 2)),
+                      8000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_ssd_cases(),
+                         ids=lambda c: "b{}l{}h{}n{}g{}_z{}_{}_h0{}_{}_trap{}".format(*c[:10]))
+def test_ssd_random_sweep(case):
+    batch, L, H, N, G, has_z, dskip, with_h0, out, trap, seed = case
+    print(f"ssd sweep case {case}", flush=True)
+    s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=has_z, dskip=dskip, seed=seed)
+    inp = make_ssd_inputs(s)
+    h0 = make_state((batch, H, 64, N), seed + 1, 0.5) if with_h0 else None
+    if trap:
+        lam = make_lam((batch, L, H), seed + 2)
+        y, h = run_trap(inp, lam, h0, out_dtype=DT[out])
+        yr, hr = oracle.ssd_trap(inp["x"], inp["dt"], lam, inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0)
+    else:
+        y, h = run_ssd(inp, out_dtype=DT[out], h0=h0)
+        yr, hr = ref_ssd(inp, h0=h0)
+    assert rel_err(y, yr) <= TOL_BF16, rel_err(y, yr)
+    assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)

@@ -461,3 +461,33 @@ def test_fused_rope_ssd_repeat_runs_identical(N):
         again = _fused_run(inp, False, torch.bfloat16)
         for a, b_ in zip(first, again):
             assert torch.equal(a, b_)
+
+
+def _sweep_fused_cases(n=10, seed=20263):
+    """A seeded random draw of fused-call shapes (the same every run)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        G = int(rng.choice([1, 1, 2]))
+        H = G * int(rng.choice([1, 2, 3, 4]))
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 300)), H, G, int(rng.choice([64, 128])),
+                      int(rng.choice([1, H])), bool(rng.integers(0, 2)), str(rng.choice(["f32", "bf16"])),
+                      bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), float(rng.choice([1.0, 5.0, 20.0])),
+                      9000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_fused_cases(),
+                         ids=lambda c: "b{}l{}h{}g{}n{}th{}_z{}_{}_trap{}_a0{}".format(*c[:10]))
+def test_fused_rope_ssd_random_sweep(case):
+    """Seeded random shapes of the fused calls (groups, per-head or shared
+    theta, gate, output dtype, trapezoid, starting angle) against the
+    oracle's rotary step followed by its SSD."""
+    batch, L, H, G, N, TH, has_z, out, trap, a0, scale, seed = case
+    print(f"fused sweep case {case}", flush=True)
+    inp = _fused_inputs(batch, L, H, G, N, TH, has_z, trap, a0, scale, seed)
+    y, hl, al, bl = _fused_run(inp, trap, DT[out])
+    ry, rh, ra, rb16 = _fused_oracle(inp, trap)
+    errs = (rel_err(y, ry), rel_err(hl, rh), angle_err(al, ra))
+    assert errs[0] <= TOL_BF16 and errs[1] <= TOL_BF16 and errs[2] <= TOL_F32, errs
+    assert rel_err(bl, rb16[:, L - 1].float()) <= 1e-2
