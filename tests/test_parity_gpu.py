@@ -1425,3 +1425,115 @@ def test_ssd_random_sweep(case):
         yr, hr = ref_ssd(inp, h0=h0)
     assert rel_err(y, yr) <= TOL_BF16, rel_err(y, yr)
     assert rel_err(h, hr) <= TOL_BF16, rel_err(h, hr)
+
+
+def _sweep_scan_bwd_cases(n=12, seed=20264):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.choice([1, 2, 4, 8, 16, 16, 32, 64]))
+        G = int(rng.choice([1, 1, 2, 3]))
+        cases.append((int(rng.integers(1, 3)), G * int(rng.integers(1, 60)), N, int(rng.integers(1, 300)), G,
+                      str(rng.choice(["f32", "bf16"])), bool(rng.integers(0, 2)),
+                      str(rng.choice(["ones", "normal", "none"])), bool(rng.integers(0, 2)),
+                      bool(rng.integers(0, 2)), 9500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_scan_bwd_cases(),
+                         ids=lambda c: "b{}d{}n{}l{}g{}_{}_z{}_{}_h0{}_dh{}".format(*c[:10]))
+def test_scan_backward_random_sweep(case):
+    batch, dim, N, L, G, dtype, has_z, dskip, with_h0, with_dhl, seed = case
+    print(f"scan backward sweep case {case}", flush=True)
+    s = ScanShape(batch, dim, N, L, G, dtype, has_z=has_z, dskip=dskip, a_kind="loguniform", seed=seed)
+    inp = make_scan_inputs(s)
+    h0 = make_state((batch, dim, N), seed + 1) if with_h0 else None
+    dhl = make_state((batch, dim, N), seed + 2) if with_dhl else None
+    dy = make_state((batch, dim, L), seed + 3).to(DT[dtype])
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0, dy, dhl)
+    g = ssm.scan_bwd(_dev(inp["u"]), _dev(inp["delta"]), _dev(inp["A"]), _dev(inp["B"]), _dev(inp["C"]),
+                     _dev(inp["D"]), _dev(inp["z"]), dy=_dev(dy), h0=_dev(h0), dh_last=_dev(dhl))
+    torch.cuda.synchronize()
+    tol = TOL_BF16 if dtype == "bf16" else TOL_BWD_F32
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dh0"):
+        if ref[k] is None:
+            assert g[k] is None
+            continue
+        err = rel_err(g[k].float().cpu(), ref[k])
+        assert err <= tol, (k, err)
+
+
+def _sweep_ssd_bwd_cases(n=10, seed=20265):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        G = int(rng.choice([1, 1, 2, 4]))
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 260)), G * int(rng.choice([1, 2, 3, 4])),
+                      int(rng.choice([64, 128])), G, bool(rng.integers(0, 2)), bool(rng.integers(0, 2)),
+                      bool(rng.integers(0, 2)), str(rng.choice(["f32", "bf16"])), bool(rng.integers(0, 2)),
+                      bool(rng.integers(0, 2)), 9600 + i))
+    return cases
+
+
+def _dA_spread(args, trap, draws=3, seed=0):
+    """How far the float64 oracle's dA moves when x, B, C and dy are perturbed
+    by up to half a bf16 step (three seeded draws).  dA sums every step's
+    log-decay gradient over the batch; where those terms cancel, this spread
+    is a sizeable part of dA itself, and no bf16 computation can resolve dA
+    more finely."""
+    inp, lam, h0, dhl, xp, bp, dy, kw = args
+    rng = np.random.default_rng(seed)
+    pert = lambda t: torch.from_numpy(t.double().numpy() * (1.0 + rng.uniform(-2.0 ** -9, 2.0 ** -9, tuple(t.shape))))
+    ref = None
+    out = 0.0
+    for k in range(draws + 1):
+        q = dict(inp)
+        dyq = dy
+        if k > 0:
+            q["x"], q["B"], q["C"], dyq = pert(inp["x"]), pert(inp["B"]), pert(inp["C"]), pert(dy)
+        if trap:
+            dA = oracle.ssd_trap_bwd(q["x"], q["dt"], lam, q["A"], q["B"], q["C"], q["D"], q["z"], h0, xp, bp, dyq,
+                                     dhl, **kw)["dA"]
+        else:
+            kw2 = {a: v for a, v in kw.items() if a != "lam_sigmoid"}
+            dA = oracle.ssd_bwd(q["x"], q["dt"], q["A"], q["B"], q["C"], q["D"], q["z"], h0, dyq, dhl, **kw2)["dA"]
+        dA = np.asarray(dA, dtype=np.float64)
+        if ref is None:
+            ref = dA
+        else:
+            out = max(out, float(np.abs(dA - ref).max()))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_ssd_bwd_cases(),
+                         ids=lambda c: "b{}l{}h{}n{}g{}_z{}_h{}_prev{}_{}_raw{}_trap{}".format(*c[:11]))
+def test_ssd_backward_random_sweep(case):
+    """Seeded random shapes of the scalar-decay and trapezoidal backwards
+    (groups, gate, h0 and dh_last, the previous token, dy dtype, raw dt and
+    lam through their maps) against the oracle backward.  Every gradient at
+    the usual bar, except dA: one number per head summed over every step,
+    whose bar is the larger of 2e-2 of its largest value and twice the spread
+    that bf16-resolution perturbations of the inputs cause in the oracle's
+    own dA (the kernel also rounds the chunk states to bf16)."""
+    batch, L, H, N, G, has_z, with_h, prev, dyt, raw, trap, seed = case
+    print(f"ssd backward sweep case {case}", flush=True)
+    args = _trap_bwd_case((batch, L, H, N, G, has_z, with_h, prev and trap, dyt, raw), seed)
+    inp, lam, h0, dhl, xp, bp, dy, kw = args
+    if trap:
+        g, ref, keys = _trap_bwd_gpu(*args), _trap_bwd_ref(*args), TRAP_BWD_KEYS
+    else:
+        kw2 = {k: v for k, v in kw.items() if k != "lam_sigmoid"}
+        g = _ssd_bwd_pair(inp, dy, h0, dhl, **kw2)
+        ref = oracle.ssd_bwd(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["z"], h0, dy, dhl,
+                             **kw2)
+        keys = SSD_BWD_KEYS
+    for k in keys:
+        if ref[k] is None:
+            assert g.get(k) is None, k
+            continue
+        err = float(np.abs(np.asarray(g[k], dtype=np.float64) - np.asarray(ref[k], dtype=np.float64)).max())
+        scale = float(np.abs(np.asarray(ref[k], dtype=np.float64)).max())
+        bar = TOL_BF16 * scale
+        if k == "dA":
+            bar = max(bar, 2.0 * _dA_spread(args, trap, seed=seed))
+        assert err <= bar, (k, err, bar, scale)
