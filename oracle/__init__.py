@@ -56,6 +56,8 @@ class Oracle:
         lib.oracle_sigmoid_f64.restype = None
         lib.oracle_rope_bc_f64.argtypes = [i64] * 6 + [dp] * 8
         lib.oracle_rope_bc_f64.restype = ctypes.c_int
+        lib.oracle_rope_bc_bwd_f64.argtypes = [i64] * 6 + [dp] * 13
+        lib.oracle_rope_bc_bwd_f64.restype = ctypes.c_int
         self.lib = lib
 
     def rope_bc(self, dt, theta, B, C, angle0=None):
@@ -80,6 +82,32 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_rope_bc_f64 rejected the shapes")
         return b_rot, c_rot, last
+
+    def rope_bc_bwd(self, dt, theta, B, C, angle0=None, dB_rot=None, dC_rot=None, dangle_last=None):
+        """Gradients of ``rope_bc`` in float64 for upstream dB_rot, dC_rot
+        (batch, L, H, N; None = zero) and dangle_last (batch, H, N / 2; None =
+        zero).  Returns a dict: ddt (batch, L, H), dtheta (like theta), dB, dC
+        (like B, C), dangle0 (batch, H, N / 2)."""
+        dt, theta, B, C, angle0, dB_rot, dC_rot, dangle_last = map(
+            f64, (dt, theta, B, C, angle0, dB_rot, dC_rot, dangle_last))
+        batch, L, H = dt.shape
+        G, N = B.shape[2], B.shape[3]
+        TH = theta.shape[2]
+        assert B.shape == (batch, L, G, N) and C.shape == B.shape
+        assert theta.shape == (batch, L, TH, N // 2)
+        zeros_rot = np.zeros((batch, L, H, N))
+        dB_rot = zeros_rot if dB_rot is None else dB_rot
+        dC_rot = zeros_rot if dC_rot is None else dC_rot
+        assert dB_rot.shape == (batch, L, H, N) and dC_rot.shape == dB_rot.shape
+        g = {"ddt": np.zeros((batch, L, H)), "dtheta": np.zeros(theta.shape), "dB": np.zeros(B.shape),
+             "dC": np.zeros(C.shape), "dangle0": np.zeros((batch, H, N // 2))}
+        rc = self.lib.oracle_rope_bc_bwd_f64(batch, L, H, G, N, TH, _ptr(dt), _ptr(theta), _ptr(B), _ptr(C),
+                                             _ptr(angle0), _ptr(dB_rot), _ptr(dC_rot), _ptr(dangle_last),
+                                             _ptr(g["ddt"]), _ptr(g["dtheta"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                                             _ptr(g["dangle0"]))
+        if rc != 0:
+            raise ValueError("oracle_rope_bc_bwd_f64 rejected the shapes")
+        return g
 
     def softplus(self, raw, bias, inner):
         """Phase-0 step: softplus(raw + bias[(i / inner) % len(bias)]) elementwise
@@ -388,3 +416,17 @@ def rope_bc(dt, theta, B, C, angle0=None, dt_softplus=False, dt_bias=None):
     if dt_softplus:
         dt = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
     return o.rope_bc(dt, theta, B, C, angle0)
+
+
+def rope_bc_bwd(dt, theta, B, C, angle0=None, dB_rot=None, dC_rot=None, dangle_last=None, dt_softplus=False,
+                dt_bias=None):
+    """Gradients of the rotary step in float64 with the default build; see
+    ``Oracle.rope_bc_bwd``.  With dt_softplus the forward steps with
+    softplus(dt + dt_bias[h]) and ddt is the gradient of the raw dt."""
+    o = _load()
+    if not dt_softplus:
+        return o.rope_bc_bwd(dt, theta, B, C, angle0, dB_rot, dC_rot, dangle_last)
+    step = o.softplus(dt, dt_bias, 1).reshape(f64(dt).shape)
+    g = o.rope_bc_bwd(step, theta, B, C, angle0, dB_rot, dC_rot, dangle_last)
+    g["ddt"] = o.softplus_grad(dt, dt_bias, 1, g["ddt"]).reshape(step.shape)
+    return g

@@ -694,3 +694,87 @@ int oracle_rope_bc_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ng
   }
   return 0;
 }
+
+/*
+ * Gradients of the rotary step (oracle_rope_bc_f64) for upstream gradients
+ * dB_rot, dC_rot (batch, seqlen, nheads, dstate) and dangle_last (batch,
+ * nheads, dstate / 2; nullable: 0).  The pages print no backward; this is
+ * the chain rule on the forward written above ("Mamba-3 NKI Kernels for AWS
+ * Neuron", section "How it works", Phase 1, as read there):
+ *   B and C: the rotation by phi_t is orthogonal, so each pair's gradient is
+ *     the upstream gradient turned back by -phi_t, summed over the heads that
+ *     read the group;
+ *   phi_t: d(v1 cos - v2 sin)/dphi = -(rotated v2) and d(v1 sin + v2 cos)/dphi
+ *     = rotated v1, so dL/dphi_t, per pair, is the sum over B and C of
+ *     -dRot1 * rot2 + dRot2 * rot1;
+ *   phi_t = angle0 - sum_{s <= t} dt_s theta_s: with R_s = dangle_last +
+ *     sum_{t >= s} dL/dphi_t, dtheta_s += -dt_s R_s (summed over heads when
+ *     theta is shared), ddt_s += -sum_k theta_s[k] R_s[k], dangle0 = R_0.
+ * ddt is the gradient of the step (the caller chains any softplus).
+ * Outputs: ddt (batch, seqlen, nheads), dtheta like theta, dB and dC like B
+ * and C, dangle0 like angle0; all are written (zeroed first).
+ */
+int oracle_rope_bc_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t ngroups, int64_t dstate,
+                           int64_t theta_heads, const double *dt, const double *theta, const double *B,
+                           const double *C, const double *angle0, const double *dB_rot, const double *dC_rot,
+                           const double *dangle_last, double *ddt, double *dtheta, double *dB, double *dC,
+                           double *dangle0) {
+  if (batch < 0 || seqlen < 0 || nheads < 1 || ngroups < 1 || nheads % ngroups != 0 || dstate < 2 ||
+      dstate % 2 != 0 || (theta_heads != 1 && theta_heads != nheads))
+    return -1;
+  const int64_t half = dstate / 2, hpg = nheads / ngroups;
+  for (int64_t i = 0; i < batch * seqlen * nheads; ++i) ddt[i] = 0.0;
+  for (int64_t i = 0; i < batch * seqlen * theta_heads * half; ++i) dtheta[i] = 0.0;
+  for (int64_t i = 0; i < batch * seqlen * ngroups * dstate; ++i) dB[i] = dC[i] = 0.0;
+  double *phis = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+  double *dphi = malloc(sizeof(double) * (size_t)(seqlen > 0 ? seqlen : 1));
+  if (!phis || !dphi) {
+    free(phis); free(dphi);
+    return -2;
+  }
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t h = 0; h < nheads; ++h) {
+      const int64_t g = h / hpg;
+      const int64_t th = theta_heads == 1 ? 0 : h;
+      for (int64_t k = 0; k < half; ++k) {
+        /* The forward angles. */
+        double phi = angle0 ? angle0[(b * nheads + h) * half + k] : 0.0;
+        for (int64_t t = 0; t < seqlen; ++t) {
+          phi -= dt[(b * seqlen + t) * nheads + h] * theta[((b * seqlen + t) * theta_heads + th) * half + k];
+          phis[t] = phi;
+        }
+        /* Each step: B and C turned back, and the gradient of its angle. */
+        for (int64_t t = 0; t < seqlen; ++t) {
+          const double c = cos(phis[t]), s = sin(phis[t]);
+          const int64_t src = ((b * seqlen + t) * ngroups + g) * dstate;
+          const int64_t dst = ((b * seqlen + t) * nheads + h) * dstate;
+          const double b1 = B[src + k], b2 = B[src + k + half];
+          const double c1 = C[src + k], c2 = C[src + k + half];
+          const double gb1 = dB_rot[dst + k], gb2 = dB_rot[dst + k + half];
+          const double gc1 = dC_rot[dst + k], gc2 = dC_rot[dst + k + half];
+          dB[src + k] += gb1 * c + gb2 * s;
+          dB[src + k + half] += -gb1 * s + gb2 * c;
+          dC[src + k] += gc1 * c + gc2 * s;
+          dC[src + k + half] += -gc1 * s + gc2 * c;
+          /* rotated pair (r1, r2) = (v1 c - v2 s, v1 s + v2 c): dr1/dphi = -r2, dr2/dphi = r1 */
+          const double rb1 = b1 * c - b2 * s, rb2 = b1 * s + b2 * c;
+          const double rc1 = c1 * c - c2 * s, rc2 = c1 * s + c2 * c;
+          dphi[t] = -gb1 * rb2 + gb2 * rb1 - gc1 * rc2 + gc2 * rc1;
+        }
+        /* The running sum, walked backwards. */
+        double R = dangle_last ? dangle_last[(b * nheads + h) * half + k] : 0.0;
+        for (int64_t t = seqlen - 1; t >= 0; --t) {
+          R += dphi[t];
+          const int64_t it = (b * seqlen + t) * nheads + h;
+          const int64_t ith = ((b * seqlen + t) * theta_heads + th) * half + k;
+          dtheta[ith] += -dt[it] * R;
+          ddt[it] += -theta[ith] * R;
+        }
+        dangle0[(b * nheads + h) * half + k] = R;
+      }
+    }
+  }
+  free(phis);
+  free(dphi);
+  return 0;
+}

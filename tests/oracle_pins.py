@@ -741,6 +741,58 @@ def check_rope_chaining_and_identities(orc):
     _close(last, np.zeros_like(last), rtol=0.0, what="rope theta = 0, angle_last")
 
 
+def check_rope_bwd_finite_differences(orc):
+    """The rotary step's backward against central finite differences of the
+    forward: the gradient of L = sum(wB * B_rot) + sum(wC * C_rot) +
+    sum(wA * angle_last) with respect to each element of dt, theta, B, C and
+    angle0; shared and per-head theta, two group counts."""
+    for seed, (b, L, H, G, N, TH) in ((31, (2, 5, 4, 2, 6, 1)), (32, (1, 6, 2, 1, 4, 2)), (33, (1, 4, 3, 3, 8, 3))):
+        rng = np.random.default_rng(seed)
+        inp = {"dt": np.exp(rng.uniform(-3, 0, (b, L, H))), "theta": rng.standard_normal((b, L, TH, N // 2)),
+               "B": rng.standard_normal((b, L, G, N)), "C": rng.standard_normal((b, L, G, N)),
+               "angle0": rng.uniform(-3, 3, (b, H, N // 2))}
+        wb, wc = rng.standard_normal((b, L, H, N)), rng.standard_normal((b, L, H, N))
+        wa = rng.standard_normal((b, H, N // 2))
+
+        def loss(v):
+            br, cr, last = orc.rope_bc(v["dt"], v["theta"], v["B"], v["C"], v["angle0"])
+            return float(np.sum(wb * br) + np.sum(wc * cr) + np.sum(wa * last))
+
+        g = orc.rope_bc_bwd(inp["dt"], inp["theta"], inp["B"], inp["C"], inp["angle0"], wb, wc, wa)
+        for k, gk in (("dt", "ddt"), ("theta", "dtheta"), ("B", "dB"), ("C", "dC"), ("angle0", "dangle0")):
+            fd = np.zeros_like(inp[k])
+            for idx in np.ndindex(inp[k].shape):
+                e = 1e-6 * max(1.0, abs(inp[k][idx]))
+                lo, hi = dict(inp), dict(inp)
+                lo[k], hi[k] = inp[k].copy(), inp[k].copy()
+                lo[k][idx] -= e
+                hi[k][idx] += e
+                fd[idx] = (loss(hi) - loss(lo)) / (2 * e)
+            _close(g[gk], fd, rtol=1e-7, what=f"rope d{k} against finite differences (seed {seed})")
+
+
+def check_rope_bwd_orthogonality(orc):
+    """With one group per head the rotation of B (and of C) at fixed angles is
+    orthogonal, so its transpose preserves inner products:
+    <dB, B> = <dB_rot, B_rot> and <dC, C> = <dC_rot, C_rot>; and with theta = 0
+    and no starting angle nothing turns: dB = dB_rot, dC = dC_rot, ddt = 0."""
+    rng = np.random.default_rng(34)
+    b, L, H, N = 2, 9, 3, 10
+    dt = np.exp(rng.uniform(-3, 0, (b, L, H)))
+    theta = rng.standard_normal((b, L, H, N // 2))
+    B, C = rng.standard_normal((b, L, H, N)), rng.standard_normal((b, L, H, N))
+    a0 = rng.uniform(-3, 3, (b, H, N // 2))
+    wb, wc = rng.standard_normal((b, L, H, N)), rng.standard_normal((b, L, H, N))
+    br, cr, _ = orc.rope_bc(dt, theta, B, C, a0)
+    g = orc.rope_bc_bwd(dt, theta, B, C, a0, wb, wc, None)
+    _close(np.sum(g["dB"] * B), np.sum(wb * br), what="rope <dB, B> = <dB_rot, B_rot>")
+    _close(np.sum(g["dC"] * C), np.sum(wc * cr), what="rope <dC, C> = <dC_rot, C_rot>")
+    g0 = orc.rope_bc_bwd(dt, np.zeros_like(theta), B, C, None, wb, wc, None)
+    _close(g0["dB"], wb, rtol=0.0, what="rope theta = 0: dB = dB_rot")
+    _close(g0["dC"], wc, rtol=0.0, what="rope theta = 0: dC = dC_rot")
+    _close(g0["ddt"], np.zeros_like(dt), rtol=0.0, what="rope theta = 0: ddt = 0")
+
+
 ALL_CHECKS = [
     check_scan_hand_example,
     check_scan_a_zero_prefix_sum,
@@ -766,4 +818,6 @@ ALL_CHECKS = [
     check_rope_closed_form,
     check_rope_complex_state,
     check_rope_chaining_and_identities,
+    check_rope_bwd_finite_differences,
+    check_rope_bwd_orthogonality,
 ]

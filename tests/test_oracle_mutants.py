@@ -110,6 +110,18 @@ MUTANTS = [
     ("rope_angle0_ignored", [("double phi = angle0 ? angle0[(b * nheads + h) * half + k] : 0.0;", "double phi = 0.0;")]),
     ("rope_c_unrotated", [("C_rot[dst + k] = c1 * c - c2 * s;", "C_rot[dst + k] = c1;"),
                           ("C_rot[dst + k + half] = c1 * s + c2 * c;", "C_rot[dst + k + half] = c2;")]),
+    # the rotary step's backward
+    ("rope_bwd_angle_grad_sign", [("dphi[t] = -gb1 * rb2 + gb2 * rb1", "dphi[t] = gb1 * rb2 - gb2 * rb1")]),
+    ("rope_bwd_not_transposed", [("dB[src + k + half] += -gb1 * s + gb2 * c;", "dB[src + k + half] += gb1 * s + gb2 * c;"),
+                                 ("dB[src + k] += gb1 * c + gb2 * s;", "dB[src + k] += gb1 * c - gb2 * s;")]),
+    ("rope_bwd_exclusive_suffix", [(
+        "R += dphi[t];\n          const int64_t it = (b * seqlen + t) * nheads + h;",
+        "const int64_t it = (b * seqlen + t) * nheads + h;"),
+        ("ddt[it] += -theta[ith] * R;\n        }", "ddt[it] += -theta[ith] * R;\n          R += dphi[t];\n        }")]),
+    ("rope_bwd_dangle_last_ignored", [("double R = dangle_last ? dangle_last[(b * nheads + h) * half + k] : 0.0;",
+                                       "double R = 0.0;")]),
+    ("rope_bwd_dtheta_without_dt", [("dtheta[ith] += -dt[it] * R;", "dtheta[ith] += -R;")]),
+    ("rope_bwd_c_angle_term_dropped", [("- gc1 * rc2 + gc2 * rc1;", ";")]),
 ]
 
 
