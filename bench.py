@@ -416,6 +416,26 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
     out["rope_bc_32x256_h32n128_bf16"] = {"ms": round(ms, 5), "hbm_GB/s": round(nbytes / ms / 1e6, 1),
                                           "hbm_frac": round(nbytes / ms / 1e6 / 8000.0, 4),
                                           "rows": rows, "traffic": measured_traffic("rope_bc_32x256_h32n128_bf16")}
+    # The rotary step's backward on the same shapes, for float32 upstream
+    # gradients of B_rot and C_rot (as the SSD backward writes dB and dC).
+    # Least bytes: dt, theta, B, C and the two upstream gradients read once;
+    # ddt, dtheta, dB, dC and dangle0 (float32) written once.
+    gdev = torch.Generator(device=dev)
+    gdev.manual_seed(13)
+    gbr = torch.randn(br.shape, generator=gdev, device=dev)
+    gcr = torch.randn(br.shape, generator=gdev, device=dev)
+    rdims = ssm.RopeDims(batch=w.batch, seqlen=w.seqlen, nheads=w.nheads, ngroups=w.ngroups, dstate=w.dstate,
+                         theta_heads=1, in_dtype=ssm.SSM_BF16, out_dtype=ssm.SSM_F32, flags=0, reserved=0)
+    rws = torch.empty(max(ssm.rope_bc_bwd_workspace_size(rdims), 1), dtype=torch.uint8, device=dev)
+    ms, _ = time_calls(lambda: ssm.rope_bc_bwd(d["dt"], theta, d["B"], d["C"], dB_rot=gbr, dC_rot=gcr,
+                                               angle0=ang, workspace=rws, stream=stream), 20, 3)
+    nbytes = (d["dt"].numel() + theta.numel() + d["B"].numel() + d["C"].numel()) * 2 + \
+        (gbr.numel() + gcr.numel()) * 4 + (d["dt"].numel() + theta.numel() + d["B"].numel() + d["C"].numel()) * 4 + \
+        2 * ang.numel() * 4
+    out["rope_bc_backward_32x256_h32n128_bf16"] = {"ms": round(ms, 5), "hbm_GB/s_min_bytes": round(nbytes / ms / 1e6, 1),
+                                                   "min_bytes_MB": round(nbytes / 1e6, 1),
+                                                   "workspace_MB": round(rws.numel() / 1e6, 1)}
+    del gbr, gcr, rws
     ms, _ = time_calls(lambda: ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], y=y,
                                                    h_last=h, stream=stream), 50, 5)
     out["ssd_rotated_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),

@@ -529,6 +529,58 @@ SSM_API int ssm_rope_bc(const void *dt, const void *theta, const void *B, const 
                         const float *angle0, void *B_rot, void *C_rot, float *angle_last,
                         const ssm_rope_dims_t *dims, void *stream);
 
+/*
+ * Workspace ssm_rope_bc_bwd needs for `dims`: two float32 (batch, seqlen,
+ * nheads, dstate) arrays when ngroups < nheads (per-head dB and dC terms) and
+ * one float32 (batch, seqlen, nheads, dstate / 2) array when theta_heads = 1
+ * < nheads (per-head dtheta terms), each rounded up to 256 bytes; 0 when
+ * ngroups = theta_heads = nheads.
+ */
+SSM_API int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *bytes);
+
+/*
+ * Backward of the rotary step (ssm_rope_bc): gradients of a loss with respect
+ * to dt, theta, B, C and angle0, given dB_rot = dL/dB_rot, dC_rot = dL/dC_rot
+ * and dangle_last = dL/dangle_last.  The chain rule on the forward's formula
+ * ([Mamba-3 NKI], "How it works", Phase 1, as read above; the page prints no
+ * backward): with c, s = cos, sin phi_t[k] and the pair (g1, g2) of dB_rot
+ * (states k, k + N/2),
+ *   dB_t[k] += g1 c + g2 s,   dB_t[k + N/2] += -g1 s + g2 c   (C alike),
+ *   dphi_t[k] = B_rot x dB_rot + C_rot x dC_rot   (x: the 2-D cross
+ *               product r1 g2 - r2 g1),
+ *   R_t[k]    = dangle_last[k] + sum_{s >= t} dphi_s[k],
+ *   dtheta_t[k] += -dt_t R_t[k],   ddt_t = -sum_k theta_t[k] R_t[k],
+ *   dangle0[k] = R_0[k]   (dangle_last when seqlen = 0),
+ * summed over the heads of a group for dB and dC and over the heads for
+ * dtheta when theta_heads = 1.
+ *
+ * Inputs: dims, dt, theta, B, C, angle0 as ssm_rope_bc (the same forward
+ *   call), and
+ *   dB_rot, dC_rot : (batch, seqlen, nheads, dstate) in dims->out_dtype (the
+ *                    forward's B_rot dtype; float32 as ssd_bwd writes dB, dC)
+ *   dangle_last    : (batch, nheads, dstate / 2) float32, nullable (zero)
+ * Outputs (overwritten, all float32):
+ *   ddt     : (batch, seqlen, nheads) (with SSM_DT_SOFTPLUS the gradient of
+ *             the raw dt, i.e. times sigmoid(dt + dt_bias[h]))
+ *   dtheta  : (batch, seqlen, theta_heads, dstate / 2)
+ *   dB, dC  : (batch, seqlen, ngroups, dstate)
+ *   dangle0 : (batch, nheads, dstate / 2), nullable
+ * Workspace: caller-owned device memory of at least
+ * ssm_rope_bc_bwd_workspace_size() bytes, 16-byte aligned (NULL when that is
+ * 0).  The angle is rebuilt in float64 as in the forward; the sum R runs in
+ * float64 and the rotations in float32.  Sums over heads run in head order,
+ * so every output is deterministic.  theta, B, C, dB_rot, dC_rot, dtheta, dB
+ * and dC must be 16-byte aligned, ddt and the angle arrays 4-byte aligned,
+ * dt element aligned.  No output may overlap an input, another output or the
+ * workspace.  Supported sizes: those of ssm_rope_bc, with
+ * batch * seqlen * nheads * dstate / 256 < 2^31.
+ */
+SSM_API int ssm_rope_bc_bwd(const void *dt, const void *theta, const void *B, const void *C,
+                            const float *angle0, const void *dB_rot, const void *dC_rot,
+                            const float *dangle_last, float *ddt, float *dtheta, float *dB, float *dC,
+                            float *dangle0, void *workspace, size_t workspace_bytes,
+                            const ssm_rope_dims_t *dims, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Single-token decode steps (state cache updated in place)                  */
 /* ------------------------------------------------------------------------ */

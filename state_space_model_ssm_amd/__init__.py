@@ -20,7 +20,7 @@ __all__ = [
     "scan_fwd", "scan_fwd_noalloc", "scan_bwd", "ssd_chunked_fwd", "ssd_trap_chunked_fwd", "ssd_rope_chunked_fwd",
     "ssd_rope_trap_chunked_fwd", "scan_step", "ssd_step",
     "ssd_trap_step", "ssd_bwd", "ssd_bwd_workspace_size",
-    "rope_bc", "RopeDims",
+    "rope_bc", "rope_bc_bwd", "rope_bc_bwd_workspace_size", "RopeDims",
     "scan_workspace_size",
     "scan_resolved_chunks", "ssd_workspace_size", "status_string", "last_error", "version",
 ]
@@ -131,6 +131,10 @@ def lib():
         L.ssd_trap_step.restype = i32
         L.ssm_rope_bc.argtypes = [vp] * 8 + [ctypes.POINTER(RopeDims), vp]
         L.ssm_rope_bc.restype = i32
+        L.ssm_rope_bc_bwd_workspace_size.argtypes = [ctypes.POINTER(RopeDims), ctypes.POINTER(ctypes.c_size_t)]
+        L.ssm_rope_bc_bwd_workspace_size.restype = i32
+        L.ssm_rope_bc_bwd.argtypes = [vp] * 14 + [ctypes.c_size_t, ctypes.POINTER(RopeDims), vp]
+        L.ssm_rope_bc_bwd.restype = i32
         L.ssm_status_string.argtypes = [i32]
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_last_error.argtypes = []
@@ -761,3 +765,61 @@ def rope_bc(dt, theta, B, C, *, angle0=None, out_dtype=None, B_rot=None, C_rot=N
     _check(lib().ssm_rope_bc(_ptr(dt), _ptr(theta), _ptr(B), _ptr(C), _ptr(angle0), _ptr(B_rot), _ptr(C_rot),
                              _ptr(angle_last), ctypes.byref(dims), _stream(stream)))
     return B_rot, C_rot, angle_last
+
+
+def rope_bc_bwd_workspace_size(dims: RopeDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ssm_rope_bc_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def rope_bc_bwd(dt, theta, B, C, *, dB_rot, dC_rot, angle0=None, dangle_last=None, workspace=None,
+                return_dangle0: bool = True, stream=None, dt_softplus: bool = False, dt_bias=None):
+    """Backward of the rotary step (``ssm_rope_bc_bwd``): gradients of a loss
+    with upstream dB_rot, dC_rot ((batch, L, H, N), float32 or bf16: the
+    forward's B_rot dtype) and dangle_last ((batch, H, N / 2) float32,
+    optional).  dt, theta, B, C, angle0 as given to ``rope_bc``.  Returns a
+    dict of float32 tensors: ddt (batch, L, H), dtheta (like theta), dB, dC
+    (like B, C) and dangle0 (batch, H, N / 2; None with return_dangle0
+    False).  With dt_softplus, ddt is the gradient of the raw dt."""
+    torch = _torch()
+    in_code = _dtype_code(B.dtype)
+    g_code = _dtype_code(dB_rot.dtype)
+    for name, t in (("dt", dt), ("theta", theta), ("C", C)):
+        if t.dtype != B.dtype:
+            raise TypeError(f"{name} must have dtype {B.dtype}")
+    if dC_rot.dtype != dB_rot.dtype:
+        raise TypeError("dC_rot must have the dtype of dB_rot")
+    batch, L, G, N = B.shape
+    H = dt.shape[2]
+    TH = theta.shape[2]
+    if dt.shape != (batch, L, H) or C.shape != B.shape or N % 2 != 0:
+        raise ValueError("dt must be (batch, L, H), C shaped like B, dstate even")
+    if theta.shape != (batch, L, TH, N // 2):
+        raise ValueError("theta must be (batch, L, 1 or H, dstate / 2)")
+    if dB_rot.shape != (batch, L, H, N) or dC_rot.shape != dB_rot.shape:
+        raise ValueError("dB_rot and dC_rot must be (batch, L, nheads, dstate)")
+    for name, t in (("angle0", angle0), ("dangle_last", dangle_last)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (batch, H, N // 2)):
+            raise ValueError(f"{name} must be float32 (batch, nheads, dstate / 2)")
+    dims = RopeDims(batch=batch, seqlen=L, nheads=H, ngroups=G, dstate=N, theta_heads=TH, in_dtype=in_code,
+                    out_dtype=g_code, flags=0, reserved=0)
+    _phase0(dims, H, dt_softplus, dt_bias)
+    need = rope_bc_bwd_workspace_size(dims)
+    f32 = torch.float32
+    dev = B.device
+    with _alloc_on(stream):
+        if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        g = {"ddt": torch.empty((batch, L, H), dtype=f32, device=dev),
+             "dtheta": torch.empty(theta.shape, dtype=f32, device=dev),
+             "dB": torch.empty(B.shape, dtype=f32, device=dev),
+             "dC": torch.empty(C.shape, dtype=f32, device=dev),
+             "dangle0": torch.empty((batch, H, N // 2), dtype=f32, device=dev) if return_dangle0 else None}
+    ws_bytes = 0 if (need == 0 or workspace is None) else workspace.numel() * workspace.element_size()
+    _check(lib().ssm_rope_bc_bwd(_ptr(dt), _ptr(theta), _ptr(B), _ptr(C), _ptr(angle0), _ptr(dB_rot),
+                                 _ptr(dC_rot), _ptr(dangle_last), _ptr(g["ddt"]), _ptr(g["dtheta"]),
+                                 _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dangle0"]),
+                                 _ptr(workspace) if need > 0 else None, ws_bytes, ctypes.byref(dims),
+                                 _stream(stream)))
+    return g

@@ -981,8 +981,8 @@ int ssd_step(const void *x, const void *dt, const float *A, const void *B, const
 // Rotary step on B and C
 // ---------------------------------------------------------------------------
 
-int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C, const float *angle0,
-                void *B_rot, void *C_rot, float *angle_last, const ssm_rope_dims_t *dims, void *stream) {
+// Checks shared by the rotary step and its backward.
+static int check_rope_dims(const ssm_rope_dims_t *dims) {
   if (!dims) return fail(SSM_ERR_NULL, "dims is NULL");
   const ssm_rope_dims_t &d = *dims;
   if (d.batch < 0 || d.seqlen < 0) return fail(SSM_ERR_SHAPE, "negative size");
@@ -996,6 +996,14 @@ int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,
   if (d.dstate < 2 || !step_dstate_ok(d.dstate))
     return fail(SSM_ERR_UNSUPPORTED, "dstate %lld not supported (a power of two from 2 to 256)", (long long)d.dstate);
   if (d.batch > 0 && d.nheads > kMaxGridX / d.batch) return fail(SSM_ERR_UNSUPPORTED, "batch * nheads exceeds the grid limit");
+  return SSM_OK;
+}
+
+int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C, const float *angle0,
+                void *B_rot, void *C_rot, float *angle_last, const ssm_rope_dims_t *dims, void *stream) {
+  const int rc = check_rope_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssm_rope_dims_t &d = *dims;
   const int64_t rows = d.batch * d.seqlen;
   const int64_t half = d.dstate / 2;
   if (rows > 0 && (!dt || !theta || !B || !C || !B_rot || !C_rot))
@@ -1043,6 +1051,120 @@ int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,
   const hipError_t e = ssm::launch_rope(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SSM_ERR_HIP, "rope launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Workspace of the rotary backward: per-head dB and dC terms when heads share
+// a group, per-head dtheta terms when they share theta.
+static size_t rope_bwd_workspace(const ssm_rope_dims_t &d) {
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t bl = static_cast<size_t>(d.batch) * static_cast<size_t>(d.seqlen);
+  size_t w = 0;
+  if (d.ngroups < d.nheads) w += 2 * up(bl * d.nheads * d.dstate * 4);
+  if (d.theta_heads < d.nheads) w += up(bl * d.nheads * (d.dstate / 2) * 4);
+  return w;
+}
+
+int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *bytes) {
+  if (!bytes) return fail(SSM_ERR_NULL, "bytes is NULL");
+  const int rc = check_rope_dims(dims);
+  if (rc != SSM_OK) return rc;
+  *bytes = rope_bwd_workspace(*dims);
+  return ok();
+}
+
+int ssm_rope_bc_bwd(const void *dt, const void *theta, const void *B, const void *C, const float *angle0,
+                    const void *dB_rot, const void *dC_rot, const float *dangle_last, float *ddt, float *dtheta,
+                    float *dB, float *dC, float *dangle0, void *workspace, size_t workspace_bytes,
+                    const ssm_rope_dims_t *dims, void *stream) {
+  int rc = check_rope_dims(dims);
+  if (rc != SSM_OK) return rc;
+  const ssm_rope_dims_t &d = *dims;
+  const int64_t rows = d.batch * d.seqlen;
+  const int64_t half = d.dstate / 2;
+  if (rows > 0 && (!dt || !theta || !B || !C || !dB_rot || !dC_rot))
+    return fail(SSM_ERR_NULL, "dt, theta, B, C, dB_rot and dC_rot are required");
+  if (rows > 0 && (!ddt || !dtheta || !dB || !dC)) return fail(SSM_ERR_NULL, "ddt, dtheta, dB and dC are required");
+  const size_t ei = dtype_size(d.in_dtype), eg = dtype_size(d.out_dtype);
+  if (!aligned(dt, ei)) return fail(SSM_ERR_ALIGN, "dt must be aligned to %zu bytes", ei);
+  if (!aligned(theta, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dB_rot, 16) || !aligned(dC_rot, 16) ||
+      !aligned(dtheta, 16) || !aligned(dB, 16) || !aligned(dC, 16))
+    return fail(SSM_ERR_ALIGN, "theta, B, C, dB_rot, dC_rot, dtheta, dB and dC must be 16-byte aligned");
+  if (!aligned(ddt, 4) || !aligned(angle0, 4) || !aligned(dangle_last, 4) || !aligned(dangle0, 4))
+    return fail(SSM_ERR_ALIGN, "ddt and the angle arrays must be 4-byte aligned");
+  const int64_t n_ang = d.batch * d.nheads * half;
+  const Span ins[] = {{dt, rows * d.nheads * ei},
+                      {theta, rows * d.theta_heads * half * ei},
+                      {B, rows * d.ngroups * d.dstate * ei},
+                      {C, rows * d.ngroups * d.dstate * ei},
+                      {dB_rot, rows * d.nheads * d.dstate * eg},
+                      {dC_rot, rows * d.nheads * d.dstate * eg},
+                      {d.dt_bias, d.nheads * 4ull},
+                      {angle0, n_ang * 4ull},
+                      {dangle_last, n_ang * 4ull}};
+  const Span outs[] = {{ddt, rows * d.nheads * 4ull},
+                       {dtheta, rows * d.theta_heads * half * 4ull},
+                       {dB, rows * d.ngroups * d.dstate * 4ull},
+                       {dC, rows * d.ngroups * d.dstate * 4ull},
+                       {dangle0, n_ang * 4ull}};
+  for (const Span &o : outs) {
+    for (const Span &i : ins)
+      if (overlap(o, i)) return fail(SSM_ERR_SHAPE, "a gradient output overlaps an input");
+    for (const Span &o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return fail(SSM_ERR_SHAPE, "two gradient outputs overlap");
+  }
+  const size_t need = rope_bwd_workspace(d);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(SSM_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(SSM_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const Span sw{workspace, need};
+    for (const Span &s : ins)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an input");
+    for (const Span &s : outs)
+      if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
+  }
+  // The head sums run over rows of ngroups * dstate or dstate / 2 floats.
+  if (rows * d.nheads * d.dstate / 256 >= kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * nheads * dstate exceeds the grid limit");
+  if (d.batch * d.nheads == 0 || (rows == 0 && dangle0 == nullptr)) return ok();
+
+  ssm::RopeBwdParams p{};
+  p.dt = dt;
+  p.theta = theta;
+  p.B = B;
+  p.C = C;
+  p.dB_rot = dB_rot;
+  p.dC_rot = dC_rot;
+  p.angle0 = angle0;
+  p.dangle_last = dangle_last;
+  p.dt_bias = d.dt_bias;
+  p.ddt = ddt;
+  p.dtheta = dtheta;
+  p.dB = dB;
+  p.dC = dC;
+  p.dangle0 = dangle0;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  const size_t bl = static_cast<size_t>(rows);
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  if (d.ngroups < d.nheads) {
+    const size_t one = up(bl * d.nheads * d.dstate * 4);
+    p.ws_dB = reinterpret_cast<float *>(ws);
+    p.ws_dC = reinterpret_cast<float *>(ws + one);
+    ws += 2 * one;
+  }
+  if (d.theta_heads < d.nheads) p.ws_dth = reinterpret_cast<float *>(ws);
+  p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
+  p.dstate = static_cast<int32_t>(d.dstate);
+  p.batch = d.batch;
+  p.seqlen = d.seqlen;
+  p.nheads = d.nheads;
+  p.ngroups = d.ngroups;
+  p.theta_heads = d.theta_heads;
+  const hipError_t e = ssm::launch_rope_bwd(p, d.in_dtype == SSM_BF16, d.out_dtype == SSM_BF16,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SSM_ERR_HIP, "rope backward launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

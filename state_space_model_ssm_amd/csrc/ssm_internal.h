@@ -186,4 +186,24 @@ struct RopeParams {
 
 hipError_t launch_rope(const RopeParams &p, int in_bf16, int out_bf16, hipStream_t stream);
 
+// Backward of the rotary step (ssm_rope_bc_bwd).  The per-head terms go to the
+// outputs when they are per head already (ngroups = nheads for dB and dC,
+// theta_heads = nheads for dtheta), else to the workspace arrays, which a
+// second kernel then sums over heads in a fixed order.
+struct RopeBwdParams {
+  const void *dt, *theta, *B, *C;     // in_dtype
+  const void *dB_rot, *dC_rot;        // g_dtype (the forward's out_dtype)
+  const float *angle0, *dangle_last;  // nullable
+  const float *dt_bias;               // nullable
+  float *ddt, *dtheta, *dB, *dC;      // float32 outputs
+  float *dangle0;                     // nullable
+  float *ws_dB, *ws_dC;               // (batch, seqlen, nheads, dstate) when ngroups < nheads
+  float *ws_dth;                      // (batch, seqlen, nheads, dstate / 2) when theta_heads < nheads
+  int32_t dt_softplus;
+  int32_t dstate;
+  int64_t batch, seqlen, nheads, ngroups, theta_heads;
+};
+
+hipError_t launch_rope_bwd(const RopeBwdParams &p, int in_bf16, int g_bf16, hipStream_t stream);
+
 }  // namespace ssm

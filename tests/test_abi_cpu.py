@@ -45,7 +45,7 @@ def _exported():
 def test_library_loads_and_exports_exactly_the_header():
     lib = ssm.lib()
     declared = _declared()
-    assert len(declared) == 24, declared
+    assert len(declared) == 26, declared
     for name in declared:
         assert hasattr(lib, name), name
     assert _exported() == declared
@@ -442,6 +442,71 @@ def test_rope_rejects_null_misaligned_overlap():
 def test_rope_empty_inputs_launch_nothing():
     assert _rope(_ropedims(batch=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
     assert _rope(_ropedims(seqlen=0), dt=None, theta=None, B=None, C=None, B_rot=None, C_rot=None) == 0
+
+
+def _rope_bwd(dims, dt=FAKE, theta=FAKE + 0x100000, B=FAKE + 0x200000, C=FAKE + 0x300000, angle0=None,
+              dB_rot=FAKE + 0x10000000, dC_rot=FAKE + 0x11000000, dangle_last=None, ddt=FAKE + 0x20000000,
+              dtheta=FAKE + 0x21000000, dB=FAKE + 0x22000000, dC=FAKE + 0x23000000, dangle0=None,
+              ws=FAKE + 0x30000000, ws_bytes=1 << 20):
+    return ssm.lib().ssm_rope_bc_bwd(dt, theta, B, C, angle0, dB_rot, dC_rot, dangle_last, ddt, dtheta, dB, dC,
+                                     dangle0, ws, ws_bytes, ctypes.byref(dims), None)
+
+
+def _rope_bwd_ws(dims):
+    n = ctypes.c_size_t(0)
+    rc = ssm.lib().ssm_rope_bc_bwd_workspace_size(ctypes.byref(dims), ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), -2), (dict(seqlen=-1), -2), (dict(nheads=0), -2), (dict(nheads=6, ngroups=4), -2),
+    (dict(theta_heads=3), -2), (dict(dstate=12), -5), (dict(dstate=512), -5), (dict(in_dtype=5), -3),
+    (dict(out_dtype=-1), -3), (dict(flags=2), -2), (dict(reserved=1), -2), (dict(dt_bias=FAKE + 0x800000), -2),
+])
+def test_rope_bwd_rejects_bad_dims(kw, code):
+    assert _rope_bwd(_ropedims(**kw)) == code, ssm.last_error()
+    assert _rope_bwd_ws(_ropedims(**kw))[0] == code
+
+
+def test_rope_bwd_workspace_size():
+    """Per-head dB and dC terms (2 x 128 rows x 4 heads x 16 floats) when the
+    heads share a group, per-head dtheta terms (128 x 4 x 8 floats) when they
+    share theta; nothing when both are per head."""
+    assert _rope_bwd_ws(_ropedims()) == (0, 2 * 32768 + 16384)
+    assert _rope_bwd_ws(_ropedims(ngroups=4, theta_heads=4)) == (0, 0)
+    assert _rope_bwd_ws(_ropedims(theta_heads=4)) == (0, 2 * 32768)
+    assert _rope_bwd_ws(_ropedims(ngroups=4)) == (0, 16384)
+    assert _rope_bwd_ws(_ropedims(seqlen=3, nheads=2, dstate=2)) == (0, 2 * 256 + 256)   # rounded up to 256 bytes
+    assert ssm.lib().ssm_rope_bc_bwd_workspace_size(ctypes.byref(_ropedims()), None) == -1
+
+
+def test_rope_bwd_rejects_null_misaligned_overlap_workspace():
+    d = _ropedims()
+    assert _rope_bwd(d, dt=None) == -1
+    assert _rope_bwd(d, dC_rot=None) == -1
+    assert _rope_bwd(d, ddt=None) == -1
+    assert _rope_bwd(d, dB=None) == -1
+    assert _rope_bwd(d, dt=FAKE + 1) == -4                        # bf16 dt needs 2-byte alignment
+    assert _rope_bwd(d, dB_rot=FAKE + 0x10000008) == -4           # vector operands need 16
+    assert _rope_bwd(d, dtheta=FAKE + 0x21000004) == -4
+    assert _rope_bwd(d, ddt=FAKE + 0x20000002) == -4
+    assert _rope_bwd(d, dangle0=FAKE + 0x24000002) == -4
+    assert _rope_bwd(d, ws=FAKE + 0x30000008) == -4
+    assert _rope_bwd(d, dB=FAKE + 0x10000000) == -2               # dB is dB_rot
+    assert _rope_bwd(d, dC=FAKE + 0x22000000 + 64) == -2          # dC inside dB
+    assert _rope_bwd(d, dangle0=FAKE + 0x100000 + 16) == -2       # dangle0 inside theta
+    assert _rope_bwd(d, dangle_last=FAKE + 0x24000000, dangle0=FAKE + 0x24000000) == -2   # no in-place
+    assert _rope_bwd(d, ws=FAKE + 0x22000000 - 0x1000) == -2       # workspace runs into dB
+    assert _rope_bwd(d, ws=FAKE + 0x300000) == -2                 # workspace is C
+    assert _rope_bwd(d, ws=None) == -6
+    assert _rope_bwd(d, ws_bytes=2 * 32768 + 16384 - 1) == -6
+
+
+def test_rope_bwd_empty_inputs_launch_nothing():
+    nulls = dict(dt=None, theta=None, B=None, C=None, dB_rot=None, dC_rot=None, ddt=None, dtheta=None, dB=None,
+                 dC=None, ws=None, ws_bytes=0)
+    assert _rope_bwd(_ropedims(batch=0), **nulls) == 0
+    assert _rope_bwd(_ropedims(seqlen=0), **nulls) == 0
 
 
 def test_last_error_is_per_thread():
