@@ -530,11 +530,11 @@ SSM_API int ssm_rope_bc(const void *dt, const void *theta, const void *B, const 
                         const ssm_rope_dims_t *dims, void *stream);
 
 /*
- * Workspace ssm_rope_bc_bwd needs for `dims`: two float32 (batch, seqlen,
- * nheads, dstate) arrays when ngroups < nheads (per-head dB and dC terms) and
- * one float32 (batch, seqlen, nheads, dstate / 2) array when theta_heads = 1
- * < nheads (per-head dtheta terms), each rounded up to 256 bytes; 0 when
- * ngroups = theta_heads = nheads.
+ * Workspace ssm_rope_bc_bwd needs for `dims`: two float32 arrays of
+ * (batch, nheads, ceil(seqlen / T), dstate / 2), where T, the steps of one
+ * tile, is 8 for dstate >= 64, 16 for 32, 32 for 16 and 64 below; and for
+ * dstate 128 or 256 one float32 array of (batch, seqlen, nheads, P) with
+ * P = 2 or 4 (the parts of ddt).  Each is rounded up to 256 bytes.
  */
 SSM_API int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *bytes);
 
@@ -567,9 +567,10 @@ SSM_API int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *
  *   dangle0 : (batch, nheads, dstate / 2), nullable
  * Workspace: caller-owned device memory of at least
  * ssm_rope_bc_bwd_workspace_size() bytes, 16-byte aligned (NULL when that is
- * 0).  The angle is rebuilt in float64 as in the forward; the sum R runs in
- * float64 and the rotations in float32.  Sums over heads run in head order,
- * so every output is deterministic.  theta, B, C, dB_rot, dC_rot, dtheta, dB
+ * 0).  The angle before every tile of T steps is rebuilt in float64 as in the
+ * forward, the angles within a tile and the rotations are float32, and R is
+ * summed in float32 within a tile and in float64 across tiles.  Every sum
+ * runs in a fixed order, so every output is deterministic.  theta, B, C, dB_rot, dC_rot, dtheta, dB
  * and dC must be 16-byte aligned, ddt and the angle arrays 4-byte aligned,
  * dt element aligned.  No output may overlap an input, another output or the
  * workspace.  Supported sizes: those of ssm_rope_bc, with

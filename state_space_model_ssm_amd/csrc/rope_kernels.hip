@@ -258,79 +258,105 @@ hipError_t launch_typed(const RopeParams &p, hipStream_t stream) {
 // R_t = dangle_last + sum_{s >= t} dphi_s:
 //   dtheta_t[k] = -dt_t R_t[k],   ddt_t = -sum_k theta_t[k] R_t[k],   dangle0 = R_0.
 //
-// One workgroup per (b, h) in the forward's layout.  Pass 1 sums each time
-// segment's dt theta and combines the sums through LDS, which gives every
-// segment its starting angle (as the forward does).  Pass 2 walks each
-// segment backwards from its last angle: it undoes the rotation (per-head dB
-// and dC), sums dphi from the segment's end (R local to the segment, float64),
-// and writes dtheta and ddt as if nothing came after the segment.  The
-// segment totals of dphi are combined through LDS, and pass 3 adds what the
-// later segments and dangle_last contribute (R_end, constant over the
-// segment): -dt_t R_end to dtheta and -theta_t . R_end to ddt.  Pass 3 reads
-// only dt and theta again, and the dtheta and ddt values the same thread
-// wrote in pass 2.  Every output element is written by one thread, so the
-// result does not depend on timing; sums over the heads that share a group
-// (dB, dC) or theta (dtheta) run afterwards in rope_bwd_reduce_kernel.
+// dB and dC sum over the heads that share a group, and dtheta over all heads
+// when they share theta, so the work is tiled over time with every head of a
+// tile in one workgroup and the head sums kept in registers:
+//   1. rope_bwd_angle_kernel, per (b, h): the angle before each tile of T
+//      steps (float64 running sum as in the forward; stored as float32
+//      revolutions reduced to [-1/2, 1/2]).
+//   2. rope_bwd_tile_kernel, per (b, tile): each wavefront holds the tile's T
+//      steps (rows) for one part of the pairs and one head slot, and loops
+//      over its slot's heads.  Per head, a scan over the rows gives the angle
+//      within the tile (float32 revolutions, reduced after every addition)
+//      and a reverse scan the sum of dphi from the tile's end (R local to the
+//      tile); both stay inside the wavefront (lane shuffles), so the head
+//      loop has no barrier.  The undone rotations add into registers and
+//      are summed over slots through LDS when a group ends.  It writes dB,
+//      dC, the local parts of dtheta and ddt, and each (head, tile)'s total
+//      of dphi.
+//   3. rope_bwd_suffix_kernel, per (b, h): R at each tile's end (dangle_last
+//      plus the later tiles' totals, float64) and dangle0.
+//   4. rope_bwd_fix_kernel, per step: adds R_end's share, -dt R_end to dtheta
+//      and -theta . R_end to ddt, then the chain rule through the step's
+//      softplus.
+// Every output element is written by one thread and every sum runs in a
+// fixed order, so results do not depend on timing.
 
-// Sum over the TPR consecutive lanes that hold one row's pairs (every lane of
-// the row is active wherever this is called: lanes of a row share their
-// segment and so every branch).
-template <int TPR>
+constexpr int kBwdThreads = 512;
+// Tile kernel layout for N / 2 = KP pairs: a row (one step) takes TPR
+// threads of VEC pairs (as the forward), split over KS wavefronts of TPRW
+// (at most 8) lanes each; a wavefront holds T = 64 / TPRW rows; the 8
+// wavefronts are HS = 8 / KS head slots.  T is 8 from KP = 32 up.  (Two
+// pairs per thread, with fewer registers but twice the head rounds, measured
+// 10% slower on 32 x 256 x 32 heads x 128 states.)
+template <int KP>
+struct BwdCfg {
+  static constexpr int VEC = RopeCfg<KP>::VEC;
+  static constexpr int TPR = RopeCfg<KP>::TPR;
+  static constexpr int KS = TPR >= 32 ? 4 : (TPR >= 16 ? 2 : 1);
+  static constexpr int TPRW = TPR / KS;
+  static constexpr int T = 64 / TPRW;
+  static constexpr int HS = 8 / KS;
+  static_assert(T * TPRW == 64 && HS * KS == 8, "rows tile a wavefront");
+};
+// Fix-up kernel layout: rows (steps) of TPR threads of VEC pairs.
+template <int KP>
+struct FixCfg {
+  static constexpr int VEC = RopeCfg<KP>::VEC;
+  static constexpr int TPR = RopeCfg<KP>::TPR;
+  static constexpr int ROWS = kBwdThreads / 4 / TPR;  // steps per workgroup
+};
+
+// Sum over the W consecutive lanes that hold one row's pairs.  Called by
+// every lane of the wavefront (no enclosing branch).
+template <int W>
 __device__ __forceinline__ float row_sum(float v) {
 #pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) v += __shfl_xor(v, m);
+  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-// Steps per batch of loads in the backward's rotation pass.
-#ifndef SSM_ROPE_BWD_BATCH
-#define SSM_ROPE_BWD_BATCH 1
-#endif
-#ifndef SSM_ROPE_BWD_WAVES
-#define SSM_ROPE_BWD_WAVES 4
-#endif
-constexpr int kBwdBatch = SSM_ROPE_BWD_BATCH;
+__device__ __forceinline__ float wrap_rev(float v) { return v - rintf(v); }
 
-template <typename Tin, typename Tg, int KP>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SSM_ROPE_BWD_WAVES))) rope_bc_bwd_kernel(const RopeBwdParams p) {
-  using Cfg = RopeCfg<KP>;
+// Pass 1: the angle before every tile.  The forward's layout (segments of
+// consecutive steps, combined through LDS) with half its segments per
+// workgroup (256 threads), so that every workgroup of the SSD-sized problems
+// is resident at once.
+template <int KP>
+struct AngleCfg {
+  static constexpr int VEC = RopeCfg<KP>::VEC;
+  static constexpr int TPR = RopeCfg<KP>::TPR;
+  static constexpr int NSEG = 256 / TPR < 64 ? 256 / TPR : 64;
+  static constexpr int THREADS = TPR * NSEG;
+};
+
+template <typename Tin, int KP>
+__global__ void __launch_bounds__(256) rope_bwd_angle_kernel(const RopeBwdParams p) {
+  using Cfg = AngleCfg<KP>;
   constexpr int VEC = Cfg::VEC, TPR = Cfg::TPR, NSEG = Cfg::NSEG;
-  constexpr int N = 2 * KP;
+  constexpr int NB = 8;  // steps whose loads are issued together
   __shared__ double sPart[NSEG * KP];
-  __shared__ double sTot[NSEG * KP];
 
   const int seg = threadIdx.x / TPR;
   const int k0 = (threadIdx.x % TPR) * VEC;
   const int64_t H = p.nheads, L = p.seqlen;
   const int64_t nblk = p.batch * H;
   int64_t id = blockIdx.x;
-  if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;  // a batch row's heads on one XCD (shared B, C, theta)
+  if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;  // a batch row's heads on one XCD (shared theta)
   const int64_t b = id / H, h = id % H;
-  const int64_t g = h / (H / p.ngroups);
   const int64_t th = p.theta_heads == 1 ? 0 : h;
   const int64_t seglen = (L + NSEG - 1) / NSEG;
   const int64_t t0 = min(L, seg * seglen), t1 = min(L, t0 + seglen);
   const int n = static_cast<int>(t1 - t0);
   const float bias = (p.dt_softplus && p.dt_bias != nullptr) ? p.dt_bias[h] : 0.0f;
-
   const int64_t row0 = b * L + t0;
   const Tin *dtp = static_cast<const Tin *>(p.dt) + row0 * H + h;
   const Tin *thp = static_cast<const Tin *>(p.theta) + (row0 * p.theta_heads + th) * KP + k0;
-  const Tin *bp = static_cast<const Tin *>(p.B) + (row0 * p.ngroups + g) * N + k0;
-  const Tin *cp = static_cast<const Tin *>(p.C) + (row0 * p.ngroups + g) * N + k0;
-  const Tg *gbp = static_cast<const Tg *>(p.dB_rot) + (row0 * H + h) * N + k0;
-  const Tg *gcp = static_cast<const Tg *>(p.dC_rot) + (row0 * H + h) * N + k0;
-  float *dbp = (p.ngroups == H ? p.dB : p.ws_dB) + (row0 * H + h) * N + k0;
-  float *dcp = (p.ngroups == H ? p.dC : p.ws_dC) + (row0 * H + h) * N + k0;
-  float *dthp = (p.theta_heads == H ? p.dtheta : p.ws_dth) + (row0 * H + h) * KP + k0;
-  float *ddtp = p.ddt + row0 * H + h;
-  const int64_t s_dt = H, s_th = p.theta_heads * KP, s_bc = p.ngroups * N, s_g = H * N, s_dth = H * KP;
+  const int64_t s_dt = H, s_th = p.theta_heads * KP;
   auto step = [&](int i) __attribute__((always_inline)) {
     const float dt = ld(dtp, i * s_dt);
     return p.dt_softplus ? dt_softplus(dt + bias) : dt;
   };
-
-  // Pass 1: the angle before this segment's first step.
   const int64_t ai = (b * H + h) * KP + k0;
   double phi[VEC], part[VEC];
 #pragma unroll
@@ -338,16 +364,33 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SSM_RO
     phi[j] = p.angle0 != nullptr ? static_cast<double>(p.angle0[ai + j]) : 0.0;
     part[j] = 0.0;
   }
-  for (int i0 = 0; i0 < n; i0 += kSumBatch) {
-    float dv[kSumBatch], tv[kSumBatch][VEC];
+  // The first NB steps stay in registers for the second pass (all of a
+  // segment's steps when the sequence has at most NSEG * NB steps).
+  float dv0[NB], tv0[NB][VEC];
 #pragma unroll
-    for (int q = 0; q < kSumBatch; ++q) {
+  for (int q = 0; q < NB; ++q) {
+    dv0[q] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) tv0[q][j] = 0.0f;
+    if (q < n) {
+      dv0[q] = step(q);
+      vload<VEC>(thp + q * s_th, tv0[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) part[j] += static_cast<double>(dv0[q]) * static_cast<double>(tv0[q][j]);
+  for (int i0 = NB; i0 < n; i0 += NB) {
+    float dv[NB], tv[NB][VEC];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
       const int i = min(i0 + q, n - 1);
       dv[q] = step(i);
       vload<VEC>(thp + i * s_th, tv[q]);
     }
 #pragma unroll
-    for (int q = 0; q < kSumBatch; ++q)
+    for (int q = 0; q < NB; ++q)
       if (i0 + q < n) {
 #pragma unroll
         for (int j = 0; j < VEC; ++j) part[j] += static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]);
@@ -360,160 +403,394 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SSM_RO
 #pragma unroll
     for (int j = 0; j < VEC; ++j) phi[j] -= sPart[s * KP + k0 + j];
   }
-
-  // Pass 2: backwards over the segment, from the angle after its last step
-  // (in revolutions; each step then adds its dt theta back).
-  double rev[VEC], R[VEC];
+  double rev[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    rev[j] = (phi[j] - part[j]) * kInvTwoPi;
-    R[j] = 0.0;
-  }
-  for (int i0 = n - 1; i0 >= 0; i0 -= kBwdBatch) {
-    float dv[kBwdBatch], tv[kBwdBatch][VEC], b1[kBwdBatch][VEC], b2[kBwdBatch][VEC], c1[kBwdBatch][VEC],
-        c2[kBwdBatch][VEC];
-    float gb1[kBwdBatch][VEC], gb2[kBwdBatch][VEC], gc1[kBwdBatch][VEC], gc2[kBwdBatch][VEC];
+  for (int j = 0; j < VEC; ++j) rev[j] = phi[j] * kInvTwoPi;
+  constexpr int T = BwdCfg<KP>::T;  // a power of two
+  float *angp = p.ws_ang + ((b * H + h) * p.ntile) * KP + k0;
+  for (int i0 = 0; i0 < n; i0 += NB) {
+    float dv[NB], tv[NB][VEC];
+    if (i0 == 0) {
 #pragma unroll
-    for (int q = 0; q < kBwdBatch; ++q) {
-      const int i = max(i0 - q, 0);
-      dv[q] = step(i);
-      vload<VEC>(thp + i * s_th, tv[q]);
-      vload<VEC>(bp + i * s_bc, b1[q]);
-      vload<VEC>(bp + i * s_bc + KP, b2[q]);
-      vload<VEC>(cp + i * s_bc, c1[q]);
-      vload<VEC>(cp + i * s_bc + KP, c2[q]);
-      vload<VEC>(gbp + i * s_g, gb1[q]);
-      vload<VEC>(gbp + i * s_g + KP, gb2[q]);
-      vload<VEC>(gcp + i * s_g, gc1[q]);
-      vload<VEC>(gcp + i * s_g + KP, gc2[q]);
-    }
+      for (int q = 0; q < NB; ++q) {
+        dv[q] = dv0[q];
 #pragma unroll
-    for (int q = 0; q < kBwdBatch; ++q) {
-      if (i0 - q >= 0) {
-        const int i = i0 - q;
-        float db1[VEC], db2[VEC], dc1[VEC], dc2[VEC], dth[VEC];
-        float dd = 0.0f;
+        for (int j = 0; j < VEC; ++j) tv[q][j] = tv0[q][j];
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          const float fr = static_cast<float>(rev[j] - rint(rev[j]));
-          const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
-          db1[j] = gb1[q][j] * cs + gb2[q][j] * sn;
-          db2[j] = gb2[q][j] * cs - gb1[q][j] * sn;
-          dc1[j] = gc1[q][j] * cs + gc2[q][j] * sn;
-          dc2[j] = gc2[q][j] * cs - gc1[q][j] * sn;
-          R[j] += static_cast<double>(b1[q][j] * db2[j] - b2[q][j] * db1[j] + c1[q][j] * dc2[j] - c2[q][j] * dc1[j]);
-          const float rf = static_cast<float>(R[j]);
-          dth[j] = -dv[q] * rf;
-          dd += tv[q][j] * rf;
-          rev[j] += static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]) * kInvTwoPi;
-        }
-        dd = row_sum<TPR>(dd);
-        vstore<VEC>(dbp + i * s_g, db1);
-        vstore<VEC>(dbp + i * s_g + KP, db2);
-        vstore<VEC>(dcp + i * s_g, dc1);
-        vstore<VEC>(dcp + i * s_g + KP, dc2);
-        vstore<VEC>(dthp + i * s_dth, dth);
-        if (k0 == 0) ddtp[i * s_dt] = -dd;
+      for (int q = 0; q < NB; ++q) {
+        const int i = min(i0 + q, n - 1);
+        dv[q] = step(i);
+        vload<VEC>(thp + i * s_th, tv[q]);
       }
     }
-  }
-
-  // The later segments' dphi and dangle_last: R_end of this segment.
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) sTot[seg * KP + k0 + j] = R[j];
-  __syncthreads();
-  double rend[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) rend[j] = p.dangle_last != nullptr ? static_cast<double>(p.dangle_last[ai + j]) : 0.0;
-  for (int s = seg + 1; s < NSEG; ++s) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) rend[j] += sTot[s * KP + k0 + j];
-  }
-  if (seg == 0 && p.dangle0 != nullptr) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) p.dangle0[ai + j] = static_cast<float>(rend[j] + R[j]);
-  }
-
-  // Pass 3: R_end's share of dtheta and ddt, and the chain rule through the
-  // step's softplus (d softplus(v) / dv = sigmoid(v) = 1 - exp(-softplus(v))).
-  float re[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) re[j] = static_cast<float>(rend[j]);
-  for (int i0 = 0; i0 < n; i0 += kSumBatch) {
-    float dv[kSumBatch], tv[kSumBatch][VEC], old[kSumBatch][VEC];
-#pragma unroll
-    for (int q = 0; q < kSumBatch; ++q) {
-      const int i = min(i0 + q, n - 1);
-      dv[q] = step(i);
-      vload<VEC>(thp + i * s_th, tv[q]);
-      vload<VEC>(dthp + i * s_dth, old[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < kSumBatch; ++q)
+    for (int q = 0; q < NB; ++q)
       if (i0 + q < n) {
-        const int i = i0 + q;
-        float dth[VEC];
-        float dd = 0.0f;
+        const int64_t t = t0 + i0 + q;
+        if ((t & (T - 1)) == 0) {
+          float a[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          dth[j] = old[q][j] - dv[q] * re[j];
-          dd += tv[q][j] * re[j];
+          for (int j = 0; j < VEC; ++j) a[j] = static_cast<float>(rev[j] - rint(rev[j]));
+          vstore<VEC>(angp + (t / T) * KP, a);
         }
-        vstore<VEC>(dthp + i * s_dth, dth);
-        dd = row_sum<TPR>(dd);
-        if (k0 == 0) {
-          float v = ddtp[i * s_dt] - dd;
-          if (p.dt_softplus) v *= 1.0f - expf(-dv[q]);
-          ddtp[i * s_dt] = v;
-        }
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) rev[j] -= static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]) * kInvTwoPi;
       }
   }
 }
 
-// Sums of per-head terms over heads, in head order: for job j,
-//   out[r][c] = sum_{i < cnt} in[(r / per) * nheads + (r % per) * cnt + i][c]
-// over rows r < rows and columns c < width (blockIdx.y picks the job).
-struct RopeReduceJob {
-  const float *in;
-  float *out;
-  int64_t rows, per, cnt, width;
-};
-struct RopeReduceJobs {
-  RopeReduceJob job[3];
-  int64_t nheads;
-};
+// Pass 2: one tile of T steps of one batch row, every head (see above).
+// Wavefront w: pair part ks = w % KS, head slot w / KS; lane: row (step) r =
+// lane / TPRW, pairs k0 .. k0 + VEC - 1 of part ks.
+// Registers held to 128 (two workgroups per CU; a few spill): unbounded
+// (~140 registers, one workgroup per CU) measured 16% slower, and loading the
+// next head's operands a round ahead (160 registers) slower still.
+template <typename Tin, typename Tg, int KP>
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(4)))
+rope_bwd_tile_kernel(const RopeBwdParams p) {
+  using Cfg = BwdCfg<KP>;
+  constexpr int VEC = Cfg::VEC, TPRW = Cfg::TPRW, T = Cfg::T, KS = Cfg::KS;
+  constexpr int N = 2 * KP;
+  constexpr int NACC = 4 * VEC;
+  __shared__ float sRed[NACC * kBwdThreads];  // [component][thread]: lanes consecutive
 
-template <int W>
-__device__ __forceinline__ void reduce_unit(const RopeReduceJob &jb, int64_t H, int64_t u) {
-  const int64_t wu = jb.width / W;
-  const int64_t r = u / wu, c = (u % wu) * W;
-  const float *src = jb.in + ((r / jb.per) * H + (r % jb.per) * jb.cnt) * jb.width + c;
-  float acc[W];
-  vload<W>(src, acc);
-  for (int64_t i = 1; i < jb.cnt; ++i) {
-    float v[W];
-    vload<W>(src + i * jb.width, v);
+  const int tid = threadIdx.x;
+  const int lane = tid % 64, wave = tid / 64;
+  const int ks = wave % KS, slot = wave / KS;
+  const int r = lane / TPRW;
+  const int k0 = (ks * TPRW + lane % TPRW) * VEC;
+  const int64_t H = p.nheads, L = p.seqlen, G = p.ngroups, hpg = H / G;
+  const int US = p.slots;                    // slots in use
+  const int64_t b = blockIdx.x / p.ntile, tile = blockIdx.x % p.ntile;
+  const int64_t t = tile * T + r;
+  const bool act_t = t < L;
+  const int64_t bt = b * L + (act_t ? t : 0);
+  const int rounds = static_cast<int>((H + US - 1) / US);
+  const int64_t span = hpg < US ? hpg : US;  // slots that share a group in one round
+
+  const Tin *dtp = static_cast<const Tin *>(p.dt) + bt * H;
+  const Tin *thp = static_cast<const Tin *>(p.theta) + bt * p.theta_heads * KP + k0;
+  const Tg *gbp = static_cast<const Tg *>(p.dB_rot) + bt * H * N + k0;
+  const Tg *gcp = static_cast<const Tg *>(p.dC_rot) + bt * H * N + k0;
+  const bool shared_theta = p.theta_heads == 1 && H > 1;
+  float th[VEC], aTh[VEC];
 #pragma unroll
-    for (int e = 0; e < W; ++e) acc[e] += v[e];
+  for (int j = 0; j < VEC; ++j) th[j] = aTh[j] = 0.0f;
+  if (act_t && p.theta_heads == 1) vload<VEC>(thp, th);
+  float b1[VEC], b2[VEC], c1[VEC], c2[VEC], acc[NACC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) b1[j] = b2[j] = c1[j] = c2[j] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) acc[q] = 0.0f;
+  int64_t gcur = -1;
+
+  for (int it = 0; it < rounds; ++it) {
+    const int64_t hh = static_cast<int64_t>(it) * US + slot;
+    const bool hv = slot < US && hh < H;  // wavefront-uniform
+    const bool act = act_t && hv;
+    const int64_t h = hv ? hh : 0;
+    const int64_t g = h / hpg;
+    if (hv && g != gcur) {
+      gcur = g;
+      if (act_t) {
+        const Tin *bp = static_cast<const Tin *>(p.B) + (bt * G + g) * N + k0;
+        const Tin *cp = static_cast<const Tin *>(p.C) + (bt * G + g) * N + k0;
+        vload<VEC>(bp, b1);
+        vload<VEC>(bp + KP, b2);
+        vload<VEC>(cp, c1);
+        vload<VEC>(cp + KP, c2);
+      }
+    }
+    float dv = 0.0f, a0[VEC], gb1[VEC], gb2[VEC], gc1[VEC], gc2[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) a0[j] = gb1[j] = gb2[j] = gc1[j] = gc2[j] = 0.0f;
+    if (hv) vload<VEC>(p.ws_ang + ((b * H + h) * p.ntile + tile) * KP + k0, a0);
+    if (act) {
+      const float raw = ld(dtp, h);
+      dv = p.dt_softplus ? dt_softplus(raw + (p.dt_bias != nullptr ? p.dt_bias[h] : 0.0f)) : raw;
+      if (p.theta_heads != 1) vload<VEC>(thp + h * KP, th);
+      vload<VEC>(gbp + h * N, gb1);
+      vload<VEC>(gbp + h * N + KP, gb2);
+      vload<VEC>(gcp + h * N, gc1);
+      vload<VEC>(gcp + h * N + KP, gc2);
+    }
+    // The angle within the tile: inclusive prefix over the rows of dt theta
+    // in revolutions (each term formed in float64 and reduced, then the
+    // float32 partial sums reduced after every addition).
+    float pre[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const double a = static_cast<double>(dv) * static_cast<double>(th[j]) * kInvTwoPi;
+      pre[j] = act ? static_cast<float>(a - rint(a)) : 0.0f;
+    }
+#pragma unroll
+    for (int d = 1; d < T; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float u = __shfl_up(pre[j], d * TPRW);
+        if (r >= d) pre[j] = wrap_rev(pre[j] + u);
+      }
+    }
+    // Undo the rotation; dphi.
+    float R[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const float fr = wrap_rev(a0[j] - pre[j]);
+      const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
+      const float db1 = gb1[j] * cs + gb2[j] * sn, db2 = gb2[j] * cs - gb1[j] * sn;
+      const float dc1 = gc1[j] * cs + gc2[j] * sn, dc2 = gc2[j] * cs - gc1[j] * sn;
+      acc[j] += db1;
+      acc[VEC + j] += db2;
+      acc[2 * VEC + j] += dc1;
+      acc[3 * VEC + j] += dc2;
+      R[j] = b1[j] * db2 - b2[j] * db1 + c1[j] * dc2 - c2[j] * dc1;
+    }
+    // R local to the tile: inclusive suffix over the rows.
+#pragma unroll
+    for (int d = 1; d < T; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float u = __shfl_down(R[j], d * TPRW);
+        if (r + d < T) R[j] += u;
+      }
+    }
+    if (r == 0 && hv) vstore<VEC>(p.ws_tot + ((b * H + h) * p.ntile + tile) * KP + k0, R);
+    float dd = 0.0f;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      dd += th[j] * R[j];
+      if (shared_theta) aTh[j] -= dv * R[j];
+    }
+    if (act && !shared_theta) {
+      float o[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) o[j] = -dv * R[j];
+      vstore<VEC>(p.dtheta + (bt * H + h) * KP + k0, o);
+    }
+    dd = row_sum<TPRW>(dd);
+    if (act && lane % TPRW == 0) {
+      if (KS == 1) p.ddt[bt * H + h] = -dd;
+      else p.ws_ddt[(bt * H + h) * KS + ks] = -dd;
+    }
+
+    // A group ends with this round: its slots' sums of dB, dC, added in slot
+    // order by the first slot of the group.
+    if (((static_cast<int64_t>(it) + 1) * US) % hpg == 0 || it == rounds - 1) {
+      if (span == 1) {
+        if (act) {
+          float *dbp = p.dB + (bt * G + g) * N + k0;
+          float *dcp = p.dC + (bt * G + g) * N + k0;
+          vstore<VEC>(dbp, *reinterpret_cast<float(*)[VEC]>(&acc[0]));
+          vstore<VEC>(dbp + KP, *reinterpret_cast<float(*)[VEC]>(&acc[VEC]));
+          vstore<VEC>(dcp, *reinterpret_cast<float(*)[VEC]>(&acc[2 * VEC]));
+          vstore<VEC>(dcp + KP, *reinterpret_cast<float(*)[VEC]>(&acc[3 * VEC]));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NACC; ++q) sRed[q * kBwdThreads + tid] = acc[q];
+        __syncthreads();
+        if (act && slot % span == 0) {
+          for (int s = 1; s < span; ++s) {
+            const int src = tid + s * KS * 64;  // same part and lane, slot + s
+#pragma unroll
+            for (int q = 0; q < NACC; ++q) acc[q] += sRed[q * kBwdThreads + src];
+          }
+          float *dbp = p.dB + (bt * G + g) * N + k0;
+          float *dcp = p.dC + (bt * G + g) * N + k0;
+          vstore<VEC>(dbp, *reinterpret_cast<float(*)[VEC]>(&acc[0]));
+          vstore<VEC>(dbp + KP, *reinterpret_cast<float(*)[VEC]>(&acc[VEC]));
+          vstore<VEC>(dcp, *reinterpret_cast<float(*)[VEC]>(&acc[2 * VEC]));
+          vstore<VEC>(dcp + KP, *reinterpret_cast<float(*)[VEC]>(&acc[3 * VEC]));
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int q = 0; q < NACC; ++q) acc[q] = 0.0f;
+    }
   }
-  vstore<W>(jb.out + r * jb.width + c, acc);
+
+  // The local dtheta of a theta shared by all heads: the slots' sums.
+  if (shared_theta) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) sRed[j * kBwdThreads + tid] = aTh[j];
+    __syncthreads();
+    if (slot == 0 && act_t) {
+      for (int s = 1; s < US; ++s) {
+        const int src = tid + s * KS * 64;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) aTh[j] += sRed[j * kBwdThreads + src];
+      }
+      vstore<VEC>(p.dtheta + bt * KP + k0, aTh);
+    }
+  }
 }
 
-__global__ void __launch_bounds__(256) rope_bwd_reduce_kernel(const RopeReduceJobs jobs) {
-  const RopeReduceJob jb = blockIdx.y == 0 ? jobs.job[0] : (blockIdx.y == 1 ? jobs.job[1] : jobs.job[2]);
-  if (jb.out == nullptr) return;
-  const int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (jb.width % 4 == 0) {
-    if (u < jb.rows * (jb.width / 4)) reduce_unit<4>(jb, jobs.nheads, u);
-  } else {
-    if (u < jb.rows * jb.width) reduce_unit<1>(jb, jobs.nheads, u);
+// Pass 3: R at the end of every tile (in place of the tile totals) and
+// dangle0.  One workgroup per (b, h): threads (pair k, segment of tiles),
+// segment sums combined through LDS.
+template <int KP>
+__global__ void __launch_bounds__(256) rope_bwd_suffix_kernel(const RopeBwdParams p) {
+  constexpr int NS = 256 / KP < 1 ? 1 : 256 / KP;  // segments (KP <= 128: at least 2)
+  constexpr int NB = 8;
+  __shared__ double sSeg[NS * KP];
+  const int k = threadIdx.x % KP, seg = threadIdx.x / KP;
+  const int64_t bh = blockIdx.x;
+  const int64_t nt = p.ntile, per = (nt + NS - 1) / NS;
+  const int64_t i0 = min(nt, seg * per), i1 = min(nt, i0 + per);
+  float *tot = p.ws_tot + bh * nt * KP + k;
+  double s = 0.0;
+  for (int64_t a = i0; a < i1; a += NB) {
+    float v[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v[q] = a + q < i1 ? tot[(a + q) * KP] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) s += static_cast<double>(v[q]);
+  }
+  sSeg[seg * KP + k] = s;
+  __syncthreads();
+  double R = p.dangle_last != nullptr ? static_cast<double>(p.dangle_last[bh * KP + k]) : 0.0;
+  for (int q = seg + 1; q < NS; ++q) R += sSeg[q * KP + k];
+  if (seg == 0 && p.dangle0 != nullptr) p.dangle0[bh * KP + k] = static_cast<float>(R + s);
+  // Walk the segment from its end; every load of a batch precedes its stores.
+  for (int64_t e = i1; e > i0; e -= NB) {
+    float v[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) v[q] = e - 1 - q >= i0 ? tot[(e - 1 - q) * KP] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+      if (e - 1 - q >= i0) {
+        tot[(e - 1 - q) * KP] = static_cast<float>(R);
+        R += static_cast<double>(v[q]);
+      }
+  }
+}
+
+// Pass 4: R_end's share of dtheta and ddt.  A row (one step) takes TPR
+// threads of VEC pairs in each of NHG head groups (128 threads per group);
+// group g takes heads in blocks of HB, g * HB + NHG * HB * i + q, whose loads
+// are issued together.  With a theta shared by all heads the groups' sums of
+// -dt R_end are added in group order through LDS.
+template <typename Tin, int KP>
+__global__ void __launch_bounds__(kBwdThreads) rope_bwd_fix_kernel(const RopeBwdParams p) {
+  using Cfg = FixCfg<KP>;
+  constexpr int VEC = Cfg::VEC, TPR = Cfg::TPR, KS = BwdCfg<KP>::KS;
+  constexpr int NHG = 4, GT = kBwdThreads / NHG, HB = 4;
+  constexpr int RPG = GT / TPR;  // rows (steps) per workgroup
+  __shared__ float sAcc[VEC * kBwdThreads];
+  const int hg = threadIdx.x / GT, tl = threadIdx.x % GT;
+  const int kb = tl % TPR, k0 = kb * VEC;
+  const int64_t H = p.nheads, L = p.seqlen;
+  const int64_t flat = static_cast<int64_t>(blockIdx.x) * RPG + tl / TPR;  // (b, t)
+  const bool act = flat < p.batch * L;
+  const int64_t bt = act ? flat : 0;
+  const int64_t b = bt / L, t = bt % L, tile = t / BwdCfg<KP>::T;
+  const Tin *dtp = static_cast<const Tin *>(p.dt) + bt * H;
+  const Tin *thp = static_cast<const Tin *>(p.theta) + bt * p.theta_heads * KP + k0;
+  const float *rep = p.ws_tot + (b * H * p.ntile + tile) * KP + k0;
+  const int64_t s_re = p.ntile * KP;
+  const bool shared_theta = p.theta_heads == 1 && H > 1;
+  float th[HB][VEC], acc[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < HB; ++q)
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) th[q][j] = 0.0f;
+  // Loads that precede every store (a load after a store waits for it).
+  float thold[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) thold[j] = 0.0f;
+  if (act && p.theta_heads == 1) {
+    vload<VEC>(thp, th[0]);
+    if (shared_theta && hg == 0) vload<VEC>(p.dtheta + bt * KP + k0, thold);
+#pragma unroll
+    for (int q = 1; q < HB; ++q)
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) th[q][j] = th[0][j];
+  }
+  for (int64_t h0 = static_cast<int64_t>(hg) * HB; h0 < H; h0 += NHG * HB) {
+    float re[HB][VEC], dv[HB], part[HB], old[HB][VEC];
+#pragma unroll
+    for (int q = 0; q < HB; ++q) {
+      const int64_t h = min(h0 + q, H - 1);
+      dv[q] = part[q] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) re[q][j] = old[q][j] = 0.0f;
+      if (act) {
+        vload<VEC>(rep + h * s_re, re[q]);
+        const float raw = ld(dtp, h);
+        dv[q] = p.dt_softplus ? dt_softplus(raw + (p.dt_bias != nullptr ? p.dt_bias[h] : 0.0f)) : raw;
+        if (p.theta_heads != 1) vload<VEC>(thp + h * KP, th[q]);
+        if (!shared_theta) vload<VEC>(p.dtheta + (bt * H + h) * KP + k0, old[q]);
+        if (kb == 0) {
+          if (KS == 1) {
+            part[q] = p.ddt[bt * H + h];
+          } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) part[q] += p.ws_ddt[(bt * H + h) * KS + s];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < HB; ++q) {
+      const int64_t h = h0 + q;
+      float dd = 0.0f;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) dd += th[q][j] * re[q][j];
+      dd = row_sum<TPR>(dd);
+      if (h < H) {
+        if (shared_theta) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) acc[j] -= dv[q] * re[q][j];
+        } else if (act) {
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) old[q][j] -= dv[q] * re[q][j];
+          vstore<VEC>(p.dtheta + (bt * H + h) * KP + k0, old[q]);
+        }
+        if (act && kb == 0) {
+          float v = part[q] - dd;
+          if (p.dt_softplus) v *= 1.0f - expf(-dv[q]);  // d softplus(x) / dx = sigmoid(x) = 1 - exp(-softplus(x))
+          p.ddt[bt * H + h] = v;
+        }
+      }
+    }
+  }
+  if (shared_theta) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) sAcc[j * kBwdThreads + threadIdx.x] = acc[j];
+    __syncthreads();
+    if (hg == 0 && act) {
+      for (int g = 1; g < NHG; ++g) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc[j] += sAcc[j * kBwdThreads + g * GT + tl];
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) thold[j] += acc[j];
+      vstore<VEC>(p.dtheta + bt * KP + k0, thold);
+    }
   }
 }
 
 template <typename Tin, typename Tg, int KP>
 hipError_t launch_bwd_kp(const RopeBwdParams &p, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(p.batch * p.nheads));
-  hipLaunchKernelGGL((rope_bc_bwd_kernel<Tin, Tg, KP>), grid, dim3(RopeCfg<KP>::THREADS), 0, stream, p);
+  using Cfg = BwdCfg<KP>;
+  if (p.tile_len != Cfg::T || p.slots < 1 || p.slots > Cfg::HS || p.ws_parts != Cfg::KS) return hipErrorInvalidValue;
+  const int64_t bl = p.batch * p.seqlen;
+  if (bl > 0) {
+    hipLaunchKernelGGL((rope_bwd_angle_kernel<Tin, KP>), dim3(static_cast<uint32_t>(p.batch * p.nheads)),
+                       dim3(AngleCfg<KP>::THREADS), 0, stream, p);
+    hipLaunchKernelGGL((rope_bwd_tile_kernel<Tin, Tg, KP>), dim3(static_cast<uint32_t>(p.batch * p.ntile)),
+                       dim3(kBwdThreads), 0, stream, p);
+  }
+  hipLaunchKernelGGL((rope_bwd_suffix_kernel<KP>), dim3(static_cast<uint32_t>(p.batch * p.nheads)), dim3(256), 0,
+                     stream, p);
+  if (bl > 0)
+    hipLaunchKernelGGL((rope_bwd_fix_kernel<Tin, KP>),
+                       dim3(static_cast<uint32_t>((bl + FixCfg<KP>::ROWS - 1) / FixCfg<KP>::ROWS)), dim3(kBwdThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -536,31 +813,10 @@ hipError_t launch_bwd_typed(const RopeBwdParams &p, hipStream_t stream) {
 
 hipError_t launch_rope_bwd(const RopeBwdParams &p, int in_bf16, int g_bf16, hipStream_t stream) {
   if (p.batch * p.nheads == 0) return hipSuccess;
-  hipError_t e;
-  if (!in_bf16 && !g_bf16) e = launch_bwd_typed<float, float>(p, stream);
-  else if (!in_bf16 && g_bf16) e = launch_bwd_typed<float, uint16_t>(p, stream);
-  else if (in_bf16 && !g_bf16) e = launch_bwd_typed<uint16_t, float>(p, stream);
-  else e = launch_bwd_typed<uint16_t, uint16_t>(p, stream);
-  if (e != hipSuccess) return e;
-  // Head sums of the per-head terms that went to the workspace.
-  const int64_t H = p.nheads, half = p.dstate / 2, bl = p.batch * p.seqlen;
-  RopeReduceJobs jobs{};
-  jobs.nheads = H;
-  int64_t units = 0;
-  if (p.ngroups < H && bl > 0) {
-    const int64_t rows = bl * p.ngroups;
-    jobs.job[0] = RopeReduceJob{p.ws_dB, p.dB, rows, p.ngroups, H / p.ngroups, p.dstate};
-    jobs.job[1] = RopeReduceJob{p.ws_dC, p.dC, rows, p.ngroups, H / p.ngroups, p.dstate};
-    units = max(units, rows * p.dstate / (p.dstate % 4 == 0 ? 4 : 1));
-  }
-  if (p.theta_heads < H && bl > 0) {
-    jobs.job[2] = RopeReduceJob{p.ws_dth, p.dtheta, bl, 1, H, half};
-    units = max(units, bl * half / (half % 4 == 0 ? 4 : 1));
-  }
-  if (units == 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>((units + 255) / 256), 3);
-  hipLaunchKernelGGL(rope_bwd_reduce_kernel, grid, dim3(256), 0, stream, jobs);
-  return hipGetLastError();
+  if (!in_bf16 && !g_bf16) return launch_bwd_typed<float, float>(p, stream);
+  if (!in_bf16 && g_bf16) return launch_bwd_typed<float, uint16_t>(p, stream);
+  if (in_bf16 && !g_bf16) return launch_bwd_typed<uint16_t, float>(p, stream);
+  return launch_bwd_typed<uint16_t, uint16_t>(p, stream);
 }
 
 hipError_t launch_rope(const RopeParams &p, int in_bf16, int out_bf16, hipStream_t stream) {

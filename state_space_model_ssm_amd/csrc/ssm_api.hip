@@ -1054,15 +1054,27 @@ int ssm_rope_bc(const void *dt, const void *theta, const void *B, const void *C,
   return ok();
 }
 
-// Workspace of the rotary backward: per-head dB and dC terms when heads share
-// a group, per-head dtheta terms when they share theta.
-static size_t rope_bwd_workspace(const ssm_rope_dims_t &d) {
+// Workspace of the rotary backward: the angle before every tile and the
+// tiles' sums of the angle gradient, (batch, nheads, ntile, dstate / 2)
+// float32 each, and the parts of ddt when a step's pairs span several
+// wavefronts; each rounded up to 256 bytes.
+struct RopeBwdTiling {
+  ssm::RopeBwdTilingCfg c;
+  int64_t ntile;
+  size_t one, ddt;  // bytes of one angle array, of the ddt parts
+};
+static RopeBwdTiling rope_bwd_tiling(const ssm_rope_dims_t &d) {
+  RopeBwdTiling t{};
+  t.c = ssm::rope_bwd_tiling(d.dstate, d.nheads, d.ngroups);
+  t.ntile = (d.seqlen + t.c.tile_len - 1) / t.c.tile_len;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t bl = static_cast<size_t>(d.batch) * static_cast<size_t>(d.seqlen);
-  size_t w = 0;
-  if (d.ngroups < d.nheads) w += 2 * up(bl * d.nheads * d.dstate * 4);
-  if (d.theta_heads < d.nheads) w += up(bl * d.nheads * (d.dstate / 2) * 4);
-  return w;
+  t.one = up(static_cast<size_t>(d.batch) * d.nheads * t.ntile * (d.dstate / 2) * 4);
+  t.ddt = t.c.parts > 1 ? up(static_cast<size_t>(d.batch) * d.seqlen * d.nheads * t.c.parts * 4) : 0;
+  return t;
+}
+static size_t rope_bwd_workspace(const ssm_rope_dims_t &d) {
+  const RopeBwdTiling t = rope_bwd_tiling(d);
+  return 2 * t.one + t.ddt;
 }
 
 int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *bytes) {
@@ -1125,9 +1137,9 @@ int ssm_rope_bc_bwd(const void *dt, const void *theta, const void *B, const void
     for (const Span &s : outs)
       if (overlap(s, sw)) return fail(SSM_ERR_SHAPE, "workspace overlaps an output");
   }
-  // The head sums run over rows of ngroups * dstate or dstate / 2 floats.
-  if (rows * d.nheads * d.dstate / 256 >= kMaxGridX)
-    return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen * nheads * dstate exceeds the grid limit");
+  const RopeBwdTiling tl = rope_bwd_tiling(d);
+  if (d.batch * tl.ntile >= kMaxGridX || rows / 4 >= kMaxGridX)
+    return fail(SSM_ERR_UNSUPPORTED, "batch * seqlen exceeds the grid limit");
   if (d.batch * d.nheads == 0 || (rows == 0 && dangle0 == nullptr)) return ok();
 
   ssm::RopeBwdParams p{};
@@ -1146,15 +1158,13 @@ int ssm_rope_bc_bwd(const void *dt, const void *theta, const void *B, const void
   p.dC = dC;
   p.dangle0 = dangle0;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  const size_t bl = static_cast<size_t>(rows);
-  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-  if (d.ngroups < d.nheads) {
-    const size_t one = up(bl * d.nheads * d.dstate * 4);
-    p.ws_dB = reinterpret_cast<float *>(ws);
-    p.ws_dC = reinterpret_cast<float *>(ws + one);
-    ws += 2 * one;
-  }
-  if (d.theta_heads < d.nheads) p.ws_dth = reinterpret_cast<float *>(ws);
+  p.ws_ang = reinterpret_cast<float *>(ws);
+  p.ws_tot = reinterpret_cast<float *>(ws + tl.one);
+  p.ws_ddt = tl.ddt > 0 ? reinterpret_cast<float *>(ws + 2 * tl.one) : nullptr;
+  p.tile_len = tl.c.tile_len;
+  p.slots = tl.c.slots;
+  p.ws_parts = tl.c.parts;
+  p.ntile = tl.ntile;
   p.dt_softplus = (d.flags & SSM_DT_SOFTPLUS) ? 1 : 0;
   p.dstate = static_cast<int32_t>(d.dstate);
   p.batch = d.batch;

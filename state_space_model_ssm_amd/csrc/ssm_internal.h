@@ -186,10 +186,12 @@ struct RopeParams {
 
 hipError_t launch_rope(const RopeParams &p, int in_bf16, int out_bf16, hipStream_t stream);
 
-// Backward of the rotary step (ssm_rope_bc_bwd).  The per-head terms go to the
-// outputs when they are per head already (ngroups = nheads for dB and dC,
-// theta_heads = nheads for dtheta), else to the workspace arrays, which a
-// second kernel then sums over heads in a fixed order.
+// Backward of the rotary step (ssm_rope_bc_bwd): tiles of tile_len steps, a
+// workgroup per (batch row, tile) holding every head of the tile in `slots`
+// head slots, a row's pairs split over ws_parts wavefronts.  Workspace: the
+// angle before every tile and the tiles' sums of the angle gradient,
+// (batch, nheads, ntile, dstate / 2) float32 each, and with ws_parts > 1 the
+// parts of ddt, (batch, seqlen, nheads, ws_parts) float32.
 struct RopeBwdParams {
   const void *dt, *theta, *B, *C;     // in_dtype
   const void *dB_rot, *dC_rot;        // g_dtype (the forward's out_dtype)
@@ -197,12 +199,34 @@ struct RopeBwdParams {
   const float *dt_bias;               // nullable
   float *ddt, *dtheta, *dB, *dC;      // float32 outputs
   float *dangle0;                     // nullable
-  float *ws_dB, *ws_dC;               // (batch, seqlen, nheads, dstate) when ngroups < nheads
-  float *ws_dth;                      // (batch, seqlen, nheads, dstate / 2) when theta_heads < nheads
+  float *ws_ang, *ws_tot, *ws_ddt;
   int32_t dt_softplus;
   int32_t dstate;
+  int32_t tile_len, slots, ws_parts;
+  int64_t ntile;
   int64_t batch, seqlen, nheads, ngroups, theta_heads;
 };
+
+// Tiling of the rotary backward for `dstate`, nheads and ngroups (it must
+// match the tile kernel's layout): threads per step tpr = max(1, dstate / 8)
+// split over parts = 4, 2 or 1 wavefronts as tpr >= 32, >= 16 or less; steps
+// per tile = 64 * parts / tpr; head slots: up to 8 / parts, a power of two
+// that divides nheads and divides or is a multiple of the heads per group.
+struct RopeBwdTilingCfg {
+  int32_t tile_len, slots, parts;
+};
+inline RopeBwdTilingCfg rope_bwd_tiling(int64_t dstate, int64_t nheads, int64_t ngroups) {
+  const int64_t kp = dstate / 2, tpr = kp < 4 ? 1 : kp / 4;
+  const int64_t parts = tpr >= 32 ? 4 : (tpr >= 16 ? 2 : 1);
+  const int64_t hpg = nheads / ngroups;
+  int64_t use = 8 / parts;
+  while (use > 1 && (nheads % use != 0 || (use % hpg != 0 && hpg % use != 0))) use /= 2;
+  RopeBwdTilingCfg c;
+  c.tile_len = static_cast<int32_t>(64 * parts / tpr);
+  c.slots = static_cast<int32_t>(use);
+  c.parts = static_cast<int32_t>(parts);
+  return c;
+}
 
 hipError_t launch_rope_bwd(const RopeBwdParams &p, int in_bf16, int g_bf16, hipStream_t stream);
 

@@ -469,14 +469,25 @@ def test_rope_bwd_rejects_bad_dims(kw, code):
 
 
 def test_rope_bwd_workspace_size():
-    """Per-head dB and dC terms (2 x 128 rows x 4 heads x 16 floats) when the
-    heads share a group, per-head dtheta terms (128 x 4 x 8 floats) when they
-    share theta; nothing when both are per head."""
-    assert _rope_bwd_ws(_ropedims()) == (0, 2 * 32768 + 16384)
-    assert _rope_bwd_ws(_ropedims(ngroups=4, theta_heads=4)) == (0, 0)
-    assert _rope_bwd_ws(_ropedims(theta_heads=4)) == (0, 2 * 32768)
-    assert _rope_bwd_ws(_ropedims(ngroups=4)) == (0, 16384)
-    assert _rope_bwd_ws(_ropedims(seqlen=3, nheads=2, dstate=2)) == (0, 2 * 256 + 256)   # rounded up to 256 bytes
+    """Two float32 arrays of (batch, heads, tiles, dstate / 2), tiles of 8
+    steps from dstate 64 up (16, 32, 64 below), plus the (batch, L, heads, P)
+    float32 parts of ddt for dstate 128 (P = 2) and 256 (P = 4); each rounded
+    up to 256 bytes."""
+    up = lambda v: -(-v // 256) * 256
+
+    def want(batch, L, H, N):
+        T = {2: 64, 4: 64, 8: 64, 16: 32, 32: 16}.get(N, 8)
+        P = {128: 2, 256: 4}.get(N, 1)
+        return 2 * up(batch * H * (-(-L // T)) * (N // 2) * 4) + (up(batch * L * H * P * 4) if P > 1 else 0)
+    assert _rope_bwd_ws(_ropedims()) == (0, want(2, 64, 4, 16))          # 32-step tiles: 2 tiles
+    assert want(2, 64, 4, 16) == 2 * 2 * 4 * 2 * 8 * 4
+    for kw in (dict(ngroups=4, theta_heads=4), dict(ngroups=2), dict(seqlen=1000, dstate=128),
+               dict(seqlen=1000, dstate=256, nheads=32), dict(seqlen=3, nheads=2, dstate=2), dict(seqlen=0),
+               dict(dstate=64), dict(dstate=32, seqlen=17)):
+        d = _ropedims(**kw)
+        assert _rope_bwd_ws(d) == (0, want(d.batch, d.seqlen, d.nheads, d.dstate)), kw
+    # The SSD shapes: 32 tiles of 8 steps, and the two parts of ddt.
+    assert want(32, 256, 32, 128) == 2 * 32 * 32 * 32 * 64 * 4 + 32 * 256 * 32 * 2 * 4
     assert ssm.lib().ssm_rope_bc_bwd_workspace_size(ctypes.byref(_ropedims()), None) == -1
 
 
@@ -496,10 +507,10 @@ def test_rope_bwd_rejects_null_misaligned_overlap_workspace():
     assert _rope_bwd(d, dC=FAKE + 0x22000000 + 64) == -2          # dC inside dB
     assert _rope_bwd(d, dangle0=FAKE + 0x100000 + 16) == -2       # dangle0 inside theta
     assert _rope_bwd(d, dangle_last=FAKE + 0x24000000, dangle0=FAKE + 0x24000000) == -2   # no in-place
-    assert _rope_bwd(d, ws=FAKE + 0x22000000 - 0x1000) == -2       # workspace runs into dB
+    assert _rope_bwd(d, ws=FAKE + 0x22000000 - 0x100) == -2        # workspace runs into dB
     assert _rope_bwd(d, ws=FAKE + 0x300000) == -2                 # workspace is C
     assert _rope_bwd(d, ws=None) == -6
-    assert _rope_bwd(d, ws_bytes=2 * 32768 + 16384 - 1) == -6
+    assert _rope_bwd(d, ws_bytes=_rope_bwd_ws(d)[1] - 1) == -6
 
 
 def test_rope_bwd_empty_inputs_launch_nothing():
