@@ -436,6 +436,24 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
                                                    "min_bytes_MB": round(nbytes / 1e6, 1),
                                                    "workspace_MB": round(rws.numel() / 1e6, 1)}
     del gbr, gcr, rws
+    # The Mamba-3 layer's backward on the same shapes, given the fused rotary
+    # SSD forward: the rotated B and C recomputed, the SSD backward on them
+    # (ngroups = nheads), then the rotary backward on its dB and dC.
+    rdy = torch.randn(w.batch, w.seqlen, w.nheads, w.headdim, generator=gdev, device=dev).to(torch.bfloat16)
+    gdims = ssm._ssd_dims(d["x"], br, 64, ssm._dtype_code(d["x"].dtype), ssm._dtype_code(rdy.dtype))
+    gws = torch.empty(max(ssm.ssd_bwd_workspace_size(gdims), 1), dtype=torch.uint8, device=dev)
+    rws = torch.empty(max(ssm.rope_bc_bwd_workspace_size(rdims), 1), dtype=torch.uint8, device=dev)
+
+    def layer_bwd():
+        ssm.rope_bc(d["dt"], theta, d["B"], d["C"], B_rot=br, C_rot=cr, return_angle_last=False, stream=stream)
+        gs = ssm.ssd_bwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], dy=rdy, workspace=gws, stream=stream)
+        ssm.rope_bc_bwd(d["dt"], theta, d["B"], d["C"], dB_rot=gs["dB"], dC_rot=gs["dC"], workspace=rws,
+                        stream=stream)
+    ms, _ = time_calls(layer_bwd, 10, 2)
+    out["mamba3_layer_backward_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5),
+                                                            "parts": "rope_bc + ssd_bwd (ngroups = nheads) + "
+                                                                     "rope_bc_bwd"}
+    del rdy, gws, rws
     ms, _ = time_calls(lambda: ssm.ssd_chunked_fwd(d["x"], d["dt"], d["A"], br, cr, d["D"], d["z"], y=y,
                                                    h_last=h, stream=stream), 50, 5)
     out["ssd_rotated_32x256_h32p64n128_bf16"] = {"ms": round(ms, 5), "Gelem/s": round(w.elements / ms / 1e6, 2),

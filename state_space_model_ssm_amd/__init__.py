@@ -774,14 +774,15 @@ def rope_bc_bwd_workspace_size(dims: RopeDims) -> int:
 
 
 def rope_bc_bwd(dt, theta, B, C, *, dB_rot, dC_rot, angle0=None, dangle_last=None, workspace=None,
-                return_dangle0: bool = True, stream=None, dt_softplus: bool = False, dt_bias=None):
+                return_dangle0: bool = True, stream=None, dt_softplus: bool = False, dt_bias=None, out=None):
     """Backward of the rotary step (``ssm_rope_bc_bwd``): gradients of a loss
     with upstream dB_rot, dC_rot ((batch, L, H, N), float32 or bf16: the
     forward's B_rot dtype) and dangle_last ((batch, H, N / 2) float32,
     optional).  dt, theta, B, C, angle0 as given to ``rope_bc``.  Returns a
     dict of float32 tensors: ddt (batch, L, H), dtheta (like theta), dB, dC
     (like B, C) and dangle0 (batch, H, N / 2; None with return_dangle0
-    False).  With dt_softplus, ddt is the gradient of the raw dt."""
+    False).  With dt_softplus, ddt is the gradient of the raw dt.  ``out``: an
+    optional dict of preallocated output tensors under those names."""
     torch = _torch()
     in_code = _dtype_code(B.dtype)
     g_code = _dtype_code(dB_rot.dtype)
@@ -811,11 +812,12 @@ def rope_bc_bwd(dt, theta, B, C, *, dB_rot, dC_rot, angle0=None, dangle_last=Non
     with _alloc_on(stream):
         if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        g = {"ddt": torch.empty((batch, L, H), dtype=f32, device=dev),
-             "dtheta": torch.empty(theta.shape, dtype=f32, device=dev),
-             "dB": torch.empty(B.shape, dtype=f32, device=dev),
-             "dC": torch.empty(C.shape, dtype=f32, device=dev),
-             "dangle0": torch.empty((batch, H, N // 2), dtype=f32, device=dev) if return_dangle0 else None}
+        o = out or {}
+        g = {"ddt": _out(o.get("ddt"), (batch, L, H), f32, B, "ddt"),
+             "dtheta": _out(o.get("dtheta"), theta.shape, f32, B, "dtheta"),
+             "dB": _out(o.get("dB"), B.shape, f32, B, "dB"),
+             "dC": _out(o.get("dC"), C.shape, f32, B, "dC"),
+             "dangle0": _out(o.get("dangle0"), (batch, H, N // 2), f32, B, "dangle0") if return_dangle0 else None}
     ws_bytes = 0 if (need == 0 or workspace is None) else workspace.numel() * workspace.element_size()
     _check(lib().ssm_rope_bc_bwd(_ptr(dt), _ptr(theta), _ptr(B), _ptr(C), _ptr(angle0), _ptr(dB_rot),
                                  _ptr(dC_rot), _ptr(dangle_last), _ptr(g["ddt"]), _ptr(g["dtheta"]),

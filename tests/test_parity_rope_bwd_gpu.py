@@ -63,8 +63,12 @@ def _inputs(batch, L, H, G, N, TH, dtype, gdtype, with_a0, with_dal, seed, theta
 
 def _gpu_bwd(inp, **kw):
     cu = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    batch, L, H = inp["dt"].shape
+    nan = lambda shape: torch.full(tuple(shape), float("nan"), dtype=torch.float32, device="cuda")
+    out = {"ddt": nan((batch, L, H)), "dtheta": nan(inp["theta"].shape), "dB": nan(inp["B"].shape),
+           "dC": nan(inp["C"].shape), "dangle0": nan((batch, H, inp["B"].shape[3] // 2))}
     g = ssm.rope_bc_bwd(cu["dt"], cu["theta"], cu["B"], cu["C"], dB_rot=cu["dB_rot"], dC_rot=cu["dC_rot"],
-                        angle0=cu["angle0"], dangle_last=cu["dangle_last"], **kw)
+                        angle0=cu["angle0"], dangle_last=cu["dangle_last"], out=out, **kw)
     torch.cuda.synchronize()
     return {k: (None if v is None else v.cpu()) for k, v in g.items()}
 
@@ -193,3 +197,29 @@ def test_mamba3_gradient_chain(case):
     print(f"chain {case}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for k, e in errs.items():
         assert e <= TOL_BF16, (k, e)
+
+
+def _sweep_cases(n=16, seed=20264):
+    """A seeded random draw of shapes (the same every run): head counts that
+    exercise every head-slot choice (1, 2, 4 or 8 slots, groups that span
+    slots and slots that span groups), every dstate, ragged tiles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        G = int(rng.choice([1, 1, 2, 3]))
+        H = G * int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        N = int(rng.choice([2, 4, 8, 16, 32, 64, 128, 256]))
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 400)), H, G, N, int(rng.choice([1, H])),
+                      str(rng.choice(["f32", "bf16"])), str(rng.choice(["f32", "bf16"])), bool(rng.integers(0, 2)),
+                      bool(rng.integers(0, 2)), float(rng.choice([1.0, 5.0])), 9800 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(),
+                         ids=lambda c: "b{}l{}h{}g{}n{}th{}_{}_{}_a0{}_dal{}".format(*c[:10]))
+def test_rope_bwd_random_sweep(case):
+    """Whole outputs against the oracle on the drawn shapes, at the float32 bar."""
+    *shape, scale, seed = case
+    print(f"rope bwd sweep case {case}", flush=True)
+    inp = _inputs(*shape, seed=seed, theta_scale=scale)
+    _check(_gpu_bwd(inp), _oracle_bwd(inp), TOL_F32, f"sweep {case}")
