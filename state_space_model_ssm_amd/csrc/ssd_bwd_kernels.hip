@@ -1122,7 +1122,17 @@ int ssd_bwd_heads_per_block(int64_t batch, int64_t seqlen, int64_t nheads, int64
   return 1;
 }
 
-hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream) {
+hipError_t launch_ssd_bwd(const SsdBwdParams &pin, int dy_bf16, hipStream_t stream) {
+  // When every head block is a whole group (one block per group, as with one
+  // head per group), a block's dB and dC terms are the gradients themselves:
+  // the chunk kernel writes them to dB and dC, and the sum over blocks (a
+  // copy of 2 * batch * seqlen * ngroups * dstate floats) is skipped.
+  SsdBwdParams p = pin;
+  const bool direct = p.nheads / p.hpw == p.ngroups;
+  if (direct) {
+    p.ws_dBp = p.dB;
+    p.ws_dCp = p.dC;
+  }
   if (p.batch * p.nheads > 0) {
     hipError_t e;
     if (p.dstate == 128)
@@ -1131,7 +1141,7 @@ hipError_t launch_ssd_bwd(const SsdBwdParams &p, int dy_bf16, hipStream_t stream
       e = dy_bf16 ? launch_form<64, uint16_t>(p, stream) : launch_form<64, float>(p, stream);
     if (e != hipSuccess) return e;
   }
-  const int64_t nbc = (p.batch * p.seqlen * p.ngroups * p.dstate / 4 + 255) / 256;
+  const int64_t nbc = direct ? 0 : (p.batch * p.seqlen * p.ngroups * p.dstate / 4 + 255) / 256;
   const int64_t nprev = (p.lam != nullptr && p.x_prev != nullptr) ? (p.batch * p.ngroups * p.dstate + 255) / 256 : 0;
   if (nbc + p.nheads + nprev > 0)
     hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(static_cast<uint32_t>(nbc + p.nheads + nprev)), dim3(256), 0,
