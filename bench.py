@@ -434,7 +434,8 @@ def extra_context(ssm, dev, stream, time_calls, WORKLOADS, make_scan_inputs, mak
         2 * ang.numel() * 4
     out["rope_bc_backward_32x256_h32n128_bf16"] = {"ms": round(ms, 5), "hbm_GB/s_min_bytes": round(nbytes / ms / 1e6, 1),
                                                    "min_bytes_MB": round(nbytes / 1e6, 1),
-                                                   "workspace_MB": round(rws.numel() / 1e6, 1)}
+                                                   "workspace_MB": round(rws.numel() / 1e6, 1),
+                                                   "traffic": measured_traffic("rope_bc_bwd_32x256_h32n128_bf16")}
     del gbr, gcr, rws
     # The Mamba-3 layer's backward on the same shapes, given the fused rotary
     # SSD forward: the rotated B and C recomputed, the SSD backward on them

@@ -223,3 +223,23 @@ def test_rope_bwd_random_sweep(case):
     print(f"rope bwd sweep case {case}", flush=True)
     inp = _inputs(*shape, seed=seed, theta_scale=scale)
     _check(_gpu_bwd(inp), _oracle_bwd(inp), TOL_F32, f"sweep {case}")
+
+
+def test_rope_bwd_side_stream_own_workspace():
+    """On a side stream with no workspace given, the binding allocates the
+    workspace and outputs on that stream; the result equals the default
+    stream's bit for bit."""
+    inp = _inputs(2, 300, 8, 1, 128, 1, "bf16", "f32", True, True, seed=9900)
+    want = _gpu_bwd(inp)
+    cu = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = ssm.rope_bc_bwd(cu["dt"], cu["theta"], cu["B"], cu["C"], dB_rot=cu["dB_rot"], dC_rot=cu["dC_rot"],
+                        angle0=cu["angle0"], dangle_last=cu["dangle_last"], stream=s)
+    # Work queued on the default stream meanwhile must not disturb it.
+    junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda").fill_(255)
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for k in KEYS:
+        assert torch.equal(g[k].cpu(), want[k]), k
