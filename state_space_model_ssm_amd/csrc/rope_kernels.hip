@@ -334,7 +334,9 @@ template <typename Tin, int KP>
 __global__ void __launch_bounds__(256) rope_bwd_angle_kernel(const RopeBwdParams p) {
   using Cfg = AngleCfg<KP>;
   constexpr int VEC = Cfg::VEC, TPR = Cfg::TPR, NSEG = Cfg::NSEG;
-  constexpr int NB = 8;  // steps whose loads are issued together
+  constexpr int NB = 8;                // steps whose loads are issued together
+  constexpr int T = BwdCfg<KP>::T;     // steps per tile, a power of two
+  constexpr bool kShort = T <= 8;      // segments of up to two tiles in one pass
   __shared__ double sPart[NSEG * KP];
 
   const int seg = threadIdx.x / TPR;
@@ -345,7 +347,8 @@ __global__ void __launch_bounds__(256) rope_bwd_angle_kernel(const RopeBwdParams
   if (nblk % 8 == 0) id = (id % 8) * (nblk / 8) + id / 8;  // a batch row's heads on one XCD (shared theta)
   const int64_t b = id / H, h = id % H;
   const int64_t th = p.theta_heads == 1 ? 0 : h;
-  const int64_t seglen = (L + NSEG - 1) / NSEG;
+  // Segments of whole tiles.
+  const int64_t seglen = ((L + NSEG - 1) / NSEG + T - 1) / T * T;
   const int64_t t0 = min(L, seg * seglen), t1 = min(L, t0 + seglen);
   const int n = static_cast<int>(t1 - t0);
   const float bias = (p.dt_softplus && p.dt_bias != nullptr) ? p.dt_bias[h] : 0.0f;
@@ -358,30 +361,74 @@ __global__ void __launch_bounds__(256) rope_bwd_angle_kernel(const RopeBwdParams
     return p.dt_softplus ? dt_softplus(dt + bias) : dt;
   };
   const int64_t ai = (b * H + h) * KP + k0;
-  double phi[VEC], part[VEC];
+  float *angp = p.ws_ang + ((b * H + h) * p.ntile + t0 / T) * KP + k0;
+  double phi[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    phi[j] = p.angle0 != nullptr ? static_cast<double>(p.angle0[ai + j]) : 0.0;
-    part[j] = 0.0;
-  }
-  // The first NB steps stay in registers for the second pass (all of a
-  // segment's steps when the sequence has at most NSEG * NB steps).
-  float dv0[NB], tv0[NB][VEC];
+  for (int j = 0; j < VEC; ++j) phi[j] = p.angle0 != nullptr ? static_cast<double>(p.angle0[ai + j]) : 0.0;
+  auto combine = [&](const double (&part)[VEC]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    dv0[q] = 0.0f;
+    for (int j = 0; j < VEC; ++j) sPart[seg * KP + k0 + j] = part[j];
+    __syncthreads();
+    for (int s = 0; s < seg; ++s) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) tv0[q][j] = 0.0f;
-    if (q < n) {
-      dv0[q] = step(q);
-      vload<VEC>(thp + q * s_th, tv0[q]);
+      for (int j = 0; j < VEC; ++j) phi[j] -= sPart[s * KP + k0 + j];
     }
+  };
+  auto store_angle = [&](int tile_in_seg, const double (&a)[VEC]) __attribute__((always_inline)) {
+    float v[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      const double r = a[j] * kInvTwoPi;
+      v[j] = static_cast<float>(r - rint(r));
+    }
+    vstore<VEC>(angp + tile_in_seg * KP, v);
+  };
+
+  if (kShort && seglen <= 2 * T) {
+    // The segment's (at most two) tiles summed apart, one tile's loads at a
+    // time, so the tile angles follow from the segment's start.
+    double ts[2][VEC];
+#pragma unroll 1
+    for (int u = 0; u < 2; ++u) {
+      float dv[T], tv[T][VEC];
+#pragma unroll
+      for (int q = 0; q < T; ++q) {
+        dv[q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) tv[q][j] = 0.0f;
+        if (u * T + q < n) {
+          dv[q] = step(u * T + q);
+          vload<VEC>(thp + (u * T + q) * s_th, tv[q]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        double a = 0.0;
+#pragma unroll
+        for (int q = 0; q < T; ++q) a += static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]);
+        if (u == 0) ts[0][j] = a;
+        else ts[1][j] = a;
+      }
+    }
+    double part[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) part[j] = ts[0][j] + ts[1][j];
+    combine(part);
+    if (n > 0) store_angle(0, phi);
+    if (n > T) {
+      double a1[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) a1[j] = phi[j] - ts[0][j];
+      store_angle(1, a1);
+    }
+    return;
   }
+
+  // Longer segments: sum, combine, then walk the segment again.
+  double part[VEC];
 #pragma unroll
-  for (int q = 0; q < NB; ++q)
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) part[j] += static_cast<double>(dv0[q]) * static_cast<double>(tv0[q][j]);
-  for (int i0 = NB; i0 < n; i0 += NB) {
+  for (int j = 0; j < VEC; ++j) part[j] = 0.0;
+  for (int i0 = 0; i0 < n; i0 += NB) {
     float dv[NB], tv[NB][VEC];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
@@ -396,47 +443,22 @@ __global__ void __launch_bounds__(256) rope_bwd_angle_kernel(const RopeBwdParams
         for (int j = 0; j < VEC; ++j) part[j] += static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]);
       }
   }
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) sPart[seg * KP + k0 + j] = part[j];
-  __syncthreads();
-  for (int s = 0; s < seg; ++s) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) phi[j] -= sPart[s * KP + k0 + j];
-  }
-  double rev[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) rev[j] = phi[j] * kInvTwoPi;
-  constexpr int T = BwdCfg<KP>::T;  // a power of two
-  float *angp = p.ws_ang + ((b * H + h) * p.ntile) * KP + k0;
+  combine(part);
   for (int i0 = 0; i0 < n; i0 += NB) {
     float dv[NB], tv[NB][VEC];
-    if (i0 == 0) {
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        dv[q] = dv0[q];
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) tv[q][j] = tv0[q][j];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const int i = min(i0 + q, n - 1);
-        dv[q] = step(i);
-        vload<VEC>(thp + i * s_th, tv[q]);
-      }
+    for (int q = 0; q < NB; ++q) {
+      const int i = min(i0 + q, n - 1);
+      dv[q] = step(i);
+      vload<VEC>(thp + i * s_th, tv[q]);
     }
 #pragma unroll
     for (int q = 0; q < NB; ++q)
       if (i0 + q < n) {
-        const int64_t t = t0 + i0 + q;
-        if ((t & (T - 1)) == 0) {
-          float a[VEC];
+        const int i = i0 + q;  // t0 is a multiple of T
+        if ((i & (T - 1)) == 0) store_angle(i / T, phi);
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) a[j] = static_cast<float>(rev[j] - rint(rev[j]));
-          vstore<VEC>(angp + (t / T) * KP, a);
-        }
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) rev[j] -= static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]) * kInvTwoPi;
+        for (int j = 0; j < VEC; ++j) phi[j] -= static_cast<double>(dv[q]) * static_cast<double>(tv[q][j]);
       }
   }
 }
@@ -670,15 +692,18 @@ __global__ void __launch_bounds__(256) rope_bwd_suffix_kernel(const RopeBwdParam
 // Pass 4: R_end's share of dtheta and ddt.  A row (one step) takes TPR
 // threads of VEC pairs in each of NHG head groups (128 threads per group);
 // group g takes heads in blocks of HB, g * HB + NHG * HB * i + q, whose loads
-// are issued together.  With a theta shared by all heads the groups' sums of
-// -dt R_end are added in group order through LDS.
-template <typename Tin, int KP>
+// are issued together (HB = 8 with a theta shared by all heads, whose dtheta
+// is one row per step; 4 with theta per head, which also reads and writes a
+// dtheta row per head).  With a shared theta the groups' sums of -dt R_end
+// are added in group order through LDS.
+template <typename Tin, int KP, bool SHARED>
 __global__ void __launch_bounds__(kBwdThreads) rope_bwd_fix_kernel(const RopeBwdParams p) {
   using Cfg = FixCfg<KP>;
   constexpr int VEC = Cfg::VEC, TPR = Cfg::TPR, KS = BwdCfg<KP>::KS;
-  constexpr int NHG = 4, GT = kBwdThreads / NHG, HB = 4;
+  constexpr int NHG = 4, GT = kBwdThreads / NHG, HB = SHARED ? 8 : 4;
+  constexpr int NTH = SHARED ? 1 : HB;  // theta rows held
   constexpr int RPG = GT / TPR;  // rows (steps) per workgroup
-  __shared__ float sAcc[VEC * kBwdThreads];
+  __shared__ float sAcc[SHARED ? VEC * kBwdThreads : 1];
   const int hg = threadIdx.x / GT, tl = threadIdx.x % GT;
   const int kb = tl % TPR, k0 = kb * VEC;
   const int64_t H = p.nheads, L = p.seqlen;
@@ -690,40 +715,38 @@ __global__ void __launch_bounds__(kBwdThreads) rope_bwd_fix_kernel(const RopeBwd
   const Tin *thp = static_cast<const Tin *>(p.theta) + bt * p.theta_heads * KP + k0;
   const float *rep = p.ws_tot + (b * H * p.ntile + tile) * KP + k0;
   const int64_t s_re = p.ntile * KP;
-  const bool shared_theta = p.theta_heads == 1 && H > 1;
-  float th[HB][VEC], acc[VEC];
+  float th[NTH][VEC], acc[VEC], thold[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
+  for (int j = 0; j < VEC; ++j) acc[j] = thold[j] = 0.0f;
 #pragma unroll
-  for (int q = 0; q < HB; ++q)
+  for (int q = 0; q < NTH; ++q)
 #pragma unroll
     for (int j = 0; j < VEC; ++j) th[q][j] = 0.0f;
   // Loads that precede every store (a load after a store waits for it).
-  float thold[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) thold[j] = 0.0f;
-  if (act && p.theta_heads == 1) {
+  if (act && SHARED) {
     vload<VEC>(thp, th[0]);
-    if (shared_theta && hg == 0) vload<VEC>(p.dtheta + bt * KP + k0, thold);
-#pragma unroll
-    for (int q = 1; q < HB; ++q)
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) th[q][j] = th[0][j];
+    if (hg == 0) vload<VEC>(p.dtheta + bt * KP + k0, thold);
   }
   for (int64_t h0 = static_cast<int64_t>(hg) * HB; h0 < H; h0 += NHG * HB) {
-    float re[HB][VEC], dv[HB], part[HB], old[HB][VEC];
+    float re[HB][VEC], dv[HB], part[HB], old[SHARED ? 1 : HB][VEC];
 #pragma unroll
     for (int q = 0; q < HB; ++q) {
       const int64_t h = min(h0 + q, H - 1);
       dv[q] = part[q] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) re[q][j] = old[q][j] = 0.0f;
+      for (int j = 0; j < VEC; ++j) re[q][j] = 0.0f;
+      if (!SHARED) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) old[SHARED ? 0 : q][j] = 0.0f;
+      }
       if (act) {
         vload<VEC>(rep + h * s_re, re[q]);
         const float raw = ld(dtp, h);
         dv[q] = p.dt_softplus ? dt_softplus(raw + (p.dt_bias != nullptr ? p.dt_bias[h] : 0.0f)) : raw;
-        if (p.theta_heads != 1) vload<VEC>(thp + h * KP, th[q]);
-        if (!shared_theta) vload<VEC>(p.dtheta + (bt * H + h) * KP + k0, old[q]);
+        if (!SHARED) {
+          vload<VEC>(thp + (p.theta_heads != 1 ? h * KP : 0), th[SHARED ? 0 : q]);
+          vload<VEC>(p.dtheta + (bt * H + h) * KP + k0, old[SHARED ? 0 : q]);
+        }
         if (kb == 0) {
           if (KS == 1) {
             part[q] = p.ddt[bt * H + h];
@@ -737,18 +760,20 @@ __global__ void __launch_bounds__(kBwdThreads) rope_bwd_fix_kernel(const RopeBwd
 #pragma unroll
     for (int q = 0; q < HB; ++q) {
       const int64_t h = h0 + q;
+      const int tq = SHARED ? 0 : q;
       float dd = 0.0f;
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) dd += th[q][j] * re[q][j];
+      for (int j = 0; j < VEC; ++j) dd += th[tq][j] * re[q][j];
       dd = row_sum<TPR>(dd);
       if (h < H) {
-        if (shared_theta) {
+        if (SHARED) {
 #pragma unroll
           for (int j = 0; j < VEC; ++j) acc[j] -= dv[q] * re[q][j];
         } else if (act) {
+          float o[VEC];
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) old[q][j] -= dv[q] * re[q][j];
-          vstore<VEC>(p.dtheta + (bt * H + h) * KP + k0, old[q]);
+          for (int j = 0; j < VEC; ++j) o[j] = old[tq][j] - dv[q] * re[q][j];
+          vstore<VEC>(p.dtheta + (bt * H + h) * KP + k0, o);
         }
         if (act && kb == 0) {
           float v = part[q] - dd;
@@ -758,7 +783,7 @@ __global__ void __launch_bounds__(kBwdThreads) rope_bwd_fix_kernel(const RopeBwd
       }
     }
   }
-  if (shared_theta) {
+  if (SHARED) {
 #pragma unroll
     for (int j = 0; j < VEC; ++j) sAcc[j * kBwdThreads + threadIdx.x] = acc[j];
     __syncthreads();
@@ -787,10 +812,13 @@ hipError_t launch_bwd_kp(const RopeBwdParams &p, hipStream_t stream) {
   }
   hipLaunchKernelGGL((rope_bwd_suffix_kernel<KP>), dim3(static_cast<uint32_t>(p.batch * p.nheads)), dim3(256), 0,
                      stream, p);
-  if (bl > 0)
-    hipLaunchKernelGGL((rope_bwd_fix_kernel<Tin, KP>),
-                       dim3(static_cast<uint32_t>((bl + FixCfg<KP>::ROWS - 1) / FixCfg<KP>::ROWS)), dim3(kBwdThreads), 0,
-                       stream, p);
+  if (bl > 0) {
+    const dim3 grid(static_cast<uint32_t>((bl + FixCfg<KP>::ROWS - 1) / FixCfg<KP>::ROWS));
+    if (p.theta_heads == 1 && p.nheads > 1)
+      hipLaunchKernelGGL((rope_bwd_fix_kernel<Tin, KP, true>), grid, dim3(kBwdThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((rope_bwd_fix_kernel<Tin, KP, false>), grid, dim3(kBwdThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
