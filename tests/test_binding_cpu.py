@@ -53,3 +53,22 @@ def test_rope_rejects_bad_outputs():
         ssm.rope_bc(dt, theta, B, B, angle_last=torch.empty(1, 2, 16))
     with pytest.raises(ValueError, match="angle0 must be"):
         ssm.rope_bc(dt, theta, B, B, angle0=torch.empty(1, 2, 16))
+
+
+def test_rope_bwd_rejects_bad_arguments():
+    dt = torch.zeros(1, 5, 2)
+    theta = torch.zeros(1, 5, 1, 8)
+    B = torch.zeros(1, 5, 1, 16)
+    g = torch.zeros(1, 5, 2, 16)
+    with pytest.raises(ValueError, match="dB_rot and dC_rot must be"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=torch.zeros(1, 5, 1, 16), dC_rot=torch.zeros(1, 5, 1, 16))
+    with pytest.raises(TypeError, match="dC_rot must have"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=g, dC_rot=g.to(torch.bfloat16))
+    with pytest.raises(ValueError, match="dangle_last must be"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=g, dC_rot=g, dangle_last=torch.zeros(1, 2, 16))
+    with pytest.raises(ValueError, match="ddt must be"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=g, dC_rot=g, out={"ddt": torch.empty(1, 5, 3)})
+    with pytest.raises(ValueError, match="dB must be"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=g, dC_rot=g, out={"dB": torch.empty(1, 5, 1, 16, dtype=torch.bfloat16)})
+    with pytest.raises(ValueError, match="dtheta must be"):
+        ssm.rope_bc_bwd(dt, theta, B, B, dB_rot=g, dC_rot=g, out={"dtheta": torch.empty(1, 5, 2, 8)})
