@@ -9,6 +9,7 @@ chain through the bf16 SSD is held to 2e-2 as the SSD backward is.  Outputs
 are NaN-poisoned before each call.
 """
 import zlib
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -16,7 +17,8 @@ import torch
 
 import oracle
 import state_space_model_ssm_amd as ssm
-from state_space_model_ssm_amd.synth import SsdShape, make_raw_step, make_ssd_inputs, make_state, make_theta
+from state_space_model_ssm_amd.synth import (WORKLOADS, SsdShape, make_raw_step, make_ssd_inputs, make_state,
+                                             make_theta)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +160,60 @@ def test_rope_bwd_workload_full_size():
     _check(_gpu_bwd(inp), _oracle_bwd(inp), TOL_F32, "full size")
 
 
+def _chain_gpu(inp, theta, dy, dhl):
+    """The GPU chain: rotary step (per-head B, C), SSD backward on them, rotary
+    backward on its dB, dC; dt's two shares summed."""
+    cu = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    th_c, dy_c, dhl_c = theta.cuda(), dy.cuda(), dhl.cuda()
+    br, cr, _ = ssm.rope_bc(cu["dt"], th_c, cu["B"], cu["C"], return_angle_last=False)
+    gs = ssm.ssd_bwd(cu["x"], cu["dt"], cu["A"], br, cr, cu["D"], cu["z"], dy=dy_c, dh_last=dhl_c)
+    gr = ssm.rope_bc_bwd(cu["dt"], th_c, cu["B"], cu["C"], dB_rot=gs["dB"], dC_rot=gs["dC"])
+    torch.cuda.synchronize()
+    got = {"dx": gs["dx"], "ddt": gs["ddt"].float() + gr["ddt"], "dtheta": gr["dtheta"], "dB": gr["dB"],
+           "dC": gr["dC"], "dA": gs["dA"], "dD": gs["dD"], "dz": gs["dz"]}
+    return {k: (None if v is None else v.float().cpu()) for k, v in got.items()}
+
+
+def _chain_oracle(inp, theta, dy, dhl):
+    """The oracle's same chain in float64, one host thread per batch row (dA
+    and dD sum over rows; the oracle's rotary step and backwards keep no
+    state between calls)."""
+    batch = inp["x"].shape[0]
+
+    def one(b):
+        r = {k: (None if v is None else (v[b:b + 1] if k in ("x", "dt", "B", "C", "z") else v))
+             for k, v in inp.items()}
+        rb, rc, _ = oracle.rope_bc(r["dt"], theta[b:b + 1], r["B"], r["C"])
+        rs = oracle.ssd_bwd(r["x"], r["dt"], r["A"], rb, rc, r["D"], r["z"], None, dy[b:b + 1], dhl[b:b + 1])
+        rr = oracle.rope_bc_bwd(r["dt"], theta[b:b + 1], r["B"], r["C"], None, rs["dB"], rs["dC"], None)
+        return {"dx": rs["dx"], "ddt": rs["ddt"] + rr["ddt"], "dtheta": rr["dtheta"], "dB": rr["dB"],
+                "dC": rr["dC"], "dA": rs["dA"], "dD": rs["dD"], "dz": rs["dz"]}
+
+    with ThreadPoolExecutor(max_workers=min(batch, 16)) as ex:
+        parts = list(ex.map(one, range(batch)))
+    out = {}
+    for k in parts[0]:
+        if parts[0][k] is None:
+            out[k] = None
+        elif k in ("dA", "dD"):
+            out[k] = np.sum([q[k] for q in parts], axis=0)
+        else:
+            out[k] = np.concatenate([q[k] for q in parts])
+    return out
+
+
+def _check_chain(got, want, label):
+    errs = {}
+    for k in got:
+        if want[k] is None:
+            assert got[k] is None, k
+            continue
+        errs[k] = rel_err(got[k], want[k])
+    print(f"{label}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= TOL_BF16, (k, e)
+
+
 @pytest.mark.parametrize("case", [(2, 192, 4, 1, 64, 1), (1, 130, 4, 2, 128, 4)],
                          ids=lambda c: "b{}l{}h{}g{}n{}th{}".format(*c))
 def test_mamba3_gradient_chain(case):
@@ -165,7 +221,7 @@ def test_mamba3_gradient_chain(case):
     rotary step, the SSD on the rotated B, C (ngroups = nheads), the SSD
     backward for dy and dh_last, then the rotary backward on the SSD's dB, dC.
     Gradients of x, dt (the SSD's and the rotary step's shares summed),
-    theta, B, C, A and D against the oracle's same chain in float64."""
+    theta, B, C, A, D and z against the oracle's same chain in float64."""
     batch, L, H, G, N, TH = case
     seed = 9700 + zlib.crc32(repr(case).encode()) % 1000
     s = SsdShape(batch, L, H, 64, N, G, 64, "bf16", has_z=True, dskip="normal", seed=seed)
@@ -173,26 +229,19 @@ def test_mamba3_gradient_chain(case):
     theta = make_theta((batch, L, TH, N // 2), seed + 1, "bf16", 1.0)
     dy = make_state((batch, L, H, 64), seed=seed + 2).to(torch.bfloat16)
     dhl = make_state((batch, H, 64, N), seed=seed + 3, scale=0.5)
-    cu = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
-    th_c, dy_c, dhl_c = theta.cuda(), dy.cuda(), dhl.cuda()
+    _check_chain(_chain_gpu(inp, theta, dy, dhl), _chain_oracle(inp, theta, dy, dhl), f"chain {case}")
 
-    br, cr, _ = ssm.rope_bc(cu["dt"], th_c, cu["B"], cu["C"], return_angle_last=False)
-    gs = ssm.ssd_bwd(cu["x"], cu["dt"], cu["A"], br, cr, cu["D"], cu["z"], dy=dy_c, dh_last=dhl_c)
-    gr = ssm.rope_bc_bwd(cu["dt"], th_c, cu["B"], cu["C"], dB_rot=gs["dB"], dC_rot=gs["dC"])
-    torch.cuda.synchronize()
-    got = {"dx": gs["dx"], "ddt": gs["ddt"].float() + gr["ddt"], "dtheta": gr["dtheta"], "dB": gr["dB"],
-           "dC": gr["dC"], "dA": gs["dA"], "dD": gs["dD"], "dz": gs["dz"]}
-    got = {k: v.float().cpu() for k, v in got.items()}
 
-    rb, rc, _ = oracle.rope_bc(inp["dt"], theta, inp["B"], inp["C"])
-    rs = oracle.ssd_bwd(inp["x"], inp["dt"], inp["A"], rb, rc, inp["D"], inp["z"], None, dy, dhl)
-    rr = oracle.rope_bc_bwd(inp["dt"], theta, inp["B"], inp["C"], None, rs["dB"], rs["dC"], None)
-    want = {"dx": rs["dx"], "ddt": rs["ddt"] + rr["ddt"], "dtheta": rr["dtheta"], "dB": rr["dB"], "dC": rr["dC"],
-            "dA": rs["dA"], "dD": rs["dD"], "dz": rs["dz"]}
-    errs = {k: rel_err(got[k], want[k]) for k in got}
-    print(f"chain {case}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-    for k, e in errs.items():
-        assert e <= TOL_BF16, (k, e)
+def test_mamba3_gradient_chain_full_size():
+    """The same chain at the SSD workload's shapes (batch 32, 256 steps, 32
+    heads x 64 sharing one group of B, C with dstate 128, one theta, D skip):
+    every gradient, whole tensors, against the oracle's chain."""
+    s = WORKLOADS["ssd_32x256_h32p64n128_bf16"]
+    inp = make_ssd_inputs(s)
+    theta = make_theta((s.batch, s.seqlen, 1, s.dstate // 2), 9750, "bf16", 1.0)
+    dy = make_state((s.batch, s.seqlen, s.nheads, s.headdim), seed=9751).to(torch.bfloat16)
+    dhl = make_state((s.batch, s.nheads, s.headdim, s.dstate), seed=9752, scale=0.5)
+    _check_chain(_chain_gpu(inp, theta, dy, dhl), _chain_oracle(inp, theta, dy, dhl), "chain full size")
 
 
 def _sweep_cases(n=16, seed=20264):
