@@ -574,7 +574,7 @@ SSM_API int ssm_rope_bc_bwd_workspace_size(const ssm_rope_dims_t *dims, size_t *
  * and dC must be 16-byte aligned, ddt and the angle arrays 4-byte aligned,
  * dt element aligned.  No output may overlap an input, another output or the
  * workspace.  Supported sizes: those of ssm_rope_bc, with
- * batch * seqlen * nheads * dstate / 256 < 2^31.
+ * batch * seqlen / 4 < 2^31 - 1 (the grids of the tiled kernels).
  */
 SSM_API int ssm_rope_bc_bwd(const void *dt, const void *theta, const void *B, const void *C,
                             const float *angle0, const void *dB_rot, const void *dC_rot,
