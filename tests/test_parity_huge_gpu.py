@@ -8,7 +8,8 @@ input module (the host generator would take minutes at this size); the oracle
 then checks, row by row, the channel rows or heads that lie past element 2^31,
 the one that straddles it, and one near the start, on copies of exactly those
 input slices.  Bars as everywhere else: max|y - y_ref| / max|y_ref| <= 2e-2
-with bf16 storage, the same for the final state.
+with bf16 storage, the same for the final state; the rotary backward's
+float32 gradients at 1e-5.
 """
 import gc
 from concurrent.futures import ThreadPoolExecutor
@@ -152,5 +153,48 @@ def test_ssd_beyond_2pow31_elements(kind):
         print(f"  batch row {b} head {hh}: y {ey:.2e} (steps {t_past}.. {ep:.2e}) h_last {eh:.2e}", flush=True)
         assert ey <= TOL_BF16 and eh <= TOL_BF16 and ep <= TOL_BF16, (b, hh, ey, eh, ep)
     del inp, y, h, theta
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_rope_bwd_beyond_2pow31_elements():
+    """The rotary backward with float32 upstream gradients of 8 x 65600
+    steps x 64 heads x 128 states (4.3e9 elements each), one head per group
+    and theta per head (so every (batch row, head) is independent): heads 0
+    and 63 of the last batch row (steps past element 2^31) and head 5 of the
+    first, against the oracle on exactly those slices.  Bar: float32 outputs
+    from the same stored inputs, 1e-5 of the largest magnitude."""
+    batch, L, H, N = 8, 65600, 64, 128
+    assert batch * L * H * N > 2 ** 31
+    print(f"rope backward {batch}x{L}x{H}x{N}: {batch * L * H * N} elements per gradient", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(44)
+
+    def normal(shape, scale=1.0, dtype=torch.float32):
+        return (scale * torch.randn(shape, generator=g, device="cuda")).to(dtype)
+
+    dt = torch.nn.functional.softplus(normal((batch, L, H)) - 4.6).to(torch.bfloat16)
+    theta = normal((batch, L, H, N // 2), dtype=torch.bfloat16)
+    B = normal((batch, L, H, N), N ** -0.5, torch.bfloat16)
+    C = normal((batch, L, H, N), N ** -0.5, torch.bfloat16)
+    dB_rot = normal((batch, L, H, N))
+    dC_rot = normal((batch, L, H, N))
+    angle0 = normal((batch, H, N // 2))
+    dal = normal((batch, H, N // 2))
+    out = ssm.rope_bc_bwd(dt, theta, B, C, dB_rot=dB_rot, dC_rot=dC_rot, angle0=angle0, dangle_last=dal)
+    torch.cuda.synchronize()
+    pairs = [(batch - 1, 0), (batch - 1, H - 1), (0, 5)]
+    for b, h in pairs:
+        s = slice(h, h + 1)
+        ref = oracle.rope_bc_bwd(_cpu(dt[b:b + 1, :, s]), _cpu(theta[b:b + 1, :, s]), _cpu(B[b:b + 1, :, s]),
+                                 _cpu(C[b:b + 1, :, s]), _cpu(angle0[b:b + 1, s]), _cpu(dB_rot[b:b + 1, :, s]),
+                                 _cpu(dC_rot[b:b + 1, :, s]), _cpu(dal[b:b + 1, s]))
+        got = {"ddt": out["ddt"][b:b + 1, :, s], "dtheta": out["dtheta"][b:b + 1, :, s],
+               "dB": out["dB"][b:b + 1, :, s], "dC": out["dC"][b:b + 1, :, s], "dangle0": out["dangle0"][b:b + 1, s]}
+        errs = {k: rel_err(_cpu(v), ref[k]) for k, v in got.items()}
+        print(f"  batch row {b} head {h}: " + ", ".join(f"{k} {e:.2e}" for k, e in errs.items()), flush=True)
+        for k, e in errs.items():
+            assert e <= 1e-5, (b, h, k, e)
+    del dt, theta, B, C, dB_rot, dC_rot, angle0, dal, out
     gc.collect()
     torch.cuda.empty_cache()
